@@ -1,0 +1,224 @@
+"""ctypes binding over libhata.so (see include/hata.h for the full contract).
+
+Argument marshalling only: each function takes torch tensors that already
+live on the GPU, derives the sizes from their shapes, passes raw device
+pointers plus torch's current stream to the C entry point of the same name,
+and raises HataError on a non-zero status.  Every step of the path runs in
+the library's HIP kernels; there is no fallback.
+
+dtype conventions on the torch side: bf16 arrays are torch.bfloat16, codes
+are torch.int64 holding the uint64 code words, scores are torch.int16 holding
+uint16 values, indices are torch.int32.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libhata.so")
+
+OP_TOPK = 1
+OP_SPARSE_DECODE = 2
+OP_DECODE_STEP = 3
+OP_DENSE_DECODE = 4
+
+_lib = None
+
+
+class HataError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(message)
+        self.status = status
+
+
+def load() -> ctypes.CDLL:
+    """Load libhata.so (built in-tree by hash_top_sparse_amd/build.py)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m hash_top_sparse_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    P, I, I64, F, SZ = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
+    sig = {
+        "hata_status_string": ([I], ctypes.c_char_p),
+        "hata_last_error_message": ([], ctypes.c_char_p),
+        "hata_version": ([], I),
+        "hata_encode_append": ([P, I64, I, I, I, P, I, I, I, P, I64, P, P], I),
+        "hata_hamming_scores": ([P, P, I, I, I, I, I64, P, I64, P, P], I),
+        "hata_topk": ([P, I, I, I64, P, I64, I, I, P, P, SZ, P], I),
+        "hata_sparse_decode": ([P, P, P, I, I, I, I, I64, P, I, F, P, P, SZ, P], I),
+        "hata_decode_step": ([P, P, P, P, P, I, I, I, I, I, I64, P, I64, I, F, P, P, P, SZ, P], I),
+        "hata_dense_decode": ([P, P, P, I, I, I, I, I64, P, I64, F, P, P, SZ, P], I),
+        "hata_workspace_bytes": ([I, I, I, I, I, I, I64, I], SZ),
+        "hata_workspace_reset": ([P, SZ, P], I),
+        "hata_workspace_check": ([P, SZ, ctypes.POINTER(I), P], I),
+    }
+    for name, (args, res) in sig.items():
+        fn = getattr(L, name)
+        fn.argtypes = args
+        fn.restype = res
+    _lib = L
+    return L
+
+
+def exported_symbols() -> list[str]:
+    return [n for n in ("hata_status_string", "hata_last_error_message", "hata_version",
+                        "hata_encode_append", "hata_hamming_scores", "hata_topk",
+                        "hata_sparse_decode", "hata_decode_step", "hata_dense_decode",
+                        "hata_workspace_bytes", "hata_workspace_reset", "hata_workspace_check")
+            if hasattr(load(), n)]
+
+
+def _check(rc: int) -> None:
+    if rc != 0:
+        L = load()
+        raise HataError(rc, f"{L.hata_status_string(rc).decode()} -- {L.hata_last_error_message().decode()}")
+
+
+def _ptr(t: torch.Tensor | None):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("tensor must live on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensor must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _need(t: torch.Tensor, dtype: torch.dtype, name: str) -> None:
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+
+
+def _stream(stream=None):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+# ----------------------------------------------------------------- entry points
+
+def encode_append(x: torch.Tensor, W_H: torch.Tensor, codes: torch.Tensor, n_new: int,
+                  pos: torch.Tensor | None = None, stream=None) -> None:
+    """x bf16 [B,H,x_rows,d]; W_H f32 [Hkv,d,r]; codes int64 [B,H,cap,r/64]."""
+    _need(x, torch.bfloat16, "x")
+    _need(W_H, torch.float32, "W_H")
+    _need(codes, torch.int64, "codes")
+    if pos is not None:
+        _need(pos, torch.int32, "pos")
+    B, H, x_rows, d = x.shape
+    Hkv, _, r = W_H.shape
+    cap = codes.shape[2]
+    _check(load().hata_encode_append(_ptr(x), x_rows, B, H, int(n_new), _ptr(W_H), Hkv, d, r,
+                                     _ptr(codes), cap, _ptr(pos), _stream(stream)))
+
+
+def hamming_scores(q_codes: torch.Tensor, k_codes: torch.Tensor, seq_lens: torch.Tensor,
+                   max_len: int, scores: torch.Tensor, stream=None) -> None:
+    """q_codes int64 [B,Hq,2]; k_codes int64 [B,Hkv,cap,2]; scores int16 [B,Hkv,cap]."""
+    _need(q_codes, torch.int64, "q_codes")
+    _need(k_codes, torch.int64, "k_codes")
+    _need(scores, torch.int16, "scores")
+    _need(seq_lens, torch.int32, "seq_lens")
+    B, Hq, words = q_codes.shape
+    _, Hkv, cap, _ = k_codes.shape
+    _check(load().hata_hamming_scores(_ptr(q_codes), _ptr(k_codes), B, Hq, Hkv, words * 64, cap,
+                                      _ptr(seq_lens), int(max_len), _ptr(scores), _stream(stream)))
+
+
+def topk(scores: torch.Tensor, seq_lens: torch.Tensor, max_len: int, k: int, max_score: int,
+         idx: torch.Tensor, stream=None) -> None:
+    """scores int16 [B,Hkv,cap]; idx int32 [B,Hkv,k]."""
+    _need(scores, torch.int16, "scores")
+    _need(idx, torch.int32, "idx")
+    _need(seq_lens, torch.int32, "seq_lens")
+    B, Hkv, cap = scores.shape
+    _check(load().hata_topk(_ptr(scores), B, Hkv, cap, _ptr(seq_lens), int(max_len), int(k),
+                            int(max_score), _ptr(idx), None, 0, _stream(stream)))
+
+
+def workspace_bytes(op: int, B: int, Hq: int, Hkv: int, max_len: int, k: int, d: int = 128,
+                    r: int = 128) -> int:
+    return int(load().hata_workspace_bytes(op, B, Hq, Hkv, d, r, int(max_len), int(k)))
+
+
+def alloc_workspace(op: int, B: int, Hq: int, Hkv: int, max_len: int, k: int,
+                    device="cuda") -> torch.Tensor:
+    """A zeroed workspace tensor (uint8) for operation `op` at these sizes."""
+    n = max(workspace_bytes(op, B, Hq, Hkv, max_len, k), 256)
+    return torch.zeros(n, dtype=torch.uint8, device=device)
+
+
+def sparse_decode(q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, idx: torch.Tensor,
+                  scale: float, out: torch.Tensor, ws: torch.Tensor, stream=None) -> None:
+    """q bf16 [B,Hq,d]; K,V bf16 [B,Hkv,cap,d]; idx int32 [B,Hkv,k]; out f32 [B,Hq,d]."""
+    for t, n in ((q, "q"), (K, "K"), (V, "V")):
+        _need(t, torch.bfloat16, n)
+    _need(idx, torch.int32, "idx")
+    _need(out, torch.float32, "out")
+    B, Hq, d = q.shape
+    _, Hkv, cap, _ = K.shape
+    k = idx.shape[2]
+    _check(load().hata_sparse_decode(_ptr(q), _ptr(K), _ptr(V), B, Hq, Hkv, d, cap, _ptr(idx), k,
+                                     float(scale), _ptr(out), _ptr(ws), ws.numel(), _stream(stream)))
+
+
+def dense_decode(q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, seq_lens: torch.Tensor,
+                 max_len: int, scale: float, out: torch.Tensor, ws: torch.Tensor,
+                 stream=None) -> None:
+    for t, n in ((q, "q"), (K, "K"), (V, "V")):
+        _need(t, torch.bfloat16, n)
+    _need(out, torch.float32, "out")
+    _need(seq_lens, torch.int32, "seq_lens")
+    B, Hq, d = q.shape
+    _, Hkv, cap, _ = K.shape
+    _check(load().hata_dense_decode(_ptr(q), _ptr(K), _ptr(V), B, Hq, Hkv, d, cap, _ptr(seq_lens),
+                                    int(max_len), float(scale), _ptr(out), _ptr(ws), ws.numel(),
+                                    _stream(stream)))
+
+
+def decode_step(q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, W_H: torch.Tensor,
+                codes: torch.Tensor, seq_lens: torch.Tensor, max_len: int, k: int, scale: float,
+                out: torch.Tensor, ws: torch.Tensor, idx_out: torch.Tensor | None = None,
+                stream=None) -> None:
+    """The fused decode step (see hata_decode_step)."""
+    for t, n in ((q, "q"), (K, "K"), (V, "V")):
+        _need(t, torch.bfloat16, n)
+    _need(W_H, torch.float32, "W_H")
+    _need(codes, torch.int64, "codes")
+    _need(out, torch.float32, "out")
+    _need(seq_lens, torch.int32, "seq_lens")
+    if idx_out is not None:
+        _need(idx_out, torch.int32, "idx_out")
+    B, Hq, d = q.shape
+    _, Hkv, cap, _ = K.shape
+    r = W_H.shape[2]
+    _check(load().hata_decode_step(_ptr(q), _ptr(K), _ptr(V), _ptr(W_H), _ptr(codes), B, Hq, Hkv,
+                                   d, r, cap, _ptr(seq_lens), int(max_len), int(k), float(scale),
+                                   _ptr(out), _ptr(idx_out), _ptr(ws), ws.numel(), _stream(stream)))
+
+
+def workspace_reset(ws: torch.Tensor, stream=None) -> None:
+    _check(load().hata_workspace_reset(_ptr(ws), ws.numel(), _stream(stream)))
+
+
+def workspace_check(ws: torch.Tensor, stream=None) -> int:
+    err = ctypes.c_int(0)
+    _check(load().hata_workspace_check(_ptr(ws), ws.numel(), ctypes.byref(err), _stream(stream)))
+    return err.value
+
+
+def status_string(status: int) -> str:
+    return load().hata_status_string(int(status)).decode()
+
+
+def raw_call(name: str, *args) -> int:
+    """Call a C entry point with raw ctypes arguments (tests of the error paths)."""
+    return int(getattr(load(), name)(*args))
+
+
+def last_error_message() -> str:
+    return load().hata_last_error_message().decode()

@@ -1,0 +1,314 @@
+// api.cpp -- the C ABI of libhata.so: argument validation, workspace layout
+// and kernel dispatch.  Declarations and the full contract are in hata.h.
+#include "../../include/hata.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <mutex>
+
+#include "hata_launch.hpp"
+
+namespace {
+
+thread_local char g_msg[512] = "";
+
+int fail(int status, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_msg, sizeof g_msg, fmt, ap);
+  va_end(ap);
+  return status;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(HATA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+constexpr int kMaxDevices = 64;
+std::mutex g_dev_mu;
+int g_cus[kMaxDevices] = {0};
+
+// Compute-unit count of the current device (cached).
+int current_cus(int* out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(HATA_ERR_HIP, "device id %d out of range", dev);
+  std::lock_guard<std::mutex> lk(g_dev_mu);
+  if (g_cus[dev] == 0) {
+    int cus = 0;
+    e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return hip_fail(e, "hipDeviceGetAttribute");
+    g_cus[dev] = cus > 0 ? cus : 1;
+  }
+  *out = g_cus[dev];
+  return HATA_OK;
+}
+
+bool test_fail_launch() {
+  const char* v = std::getenv("HATA_TEST_FAIL_LAUNCH");
+  return v && v[0] == '1';
+}
+
+// Test hook: with HATA_TEST_FAIL_LAUNCH=1 every entry point reports a HIP
+// failure after validating its arguments and before launching anything.
+int pre_launch(const char* what) {
+  if (test_fail_launch()) return fail(HATA_ERR_HIP, "%s: launch failure forced by HATA_TEST_FAIL_LAUNCH", what);
+  return HATA_OK;
+}
+
+int check_launch(hipError_t e, const char* what) {
+  if (e != hipSuccess) return hip_fail(e, what);
+  return HATA_OK;
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int check_dims(int d, int r) {
+  if (d != 128) return fail(HATA_ERR_UNSUPPORTED, "head dim d=%d unsupported (only 128)", d);
+  if (r != 128) return fail(HATA_ERR_UNSUPPORTED, "code width r=%d unsupported (only 128)", r);
+  return HATA_OK;
+}
+
+int check_heads(int B, int Hq, int Hkv) {
+  if (B < 1) return fail(HATA_ERR_SHAPE, "B=%d must be >= 1", B);
+  if (Hq < 1 || Hkv < 1) return fail(HATA_ERR_SHAPE, "Hq=%d, Hkv=%d must be >= 1", Hq, Hkv);
+  if (Hq % Hkv != 0) return fail(HATA_ERR_SHAPE, "Hq=%d is not a multiple of Hkv=%d", Hq, Hkv);
+  const int G = Hq / Hkv;
+  if (G != 1 && G != 2 && G != 4 && G != 8)
+    return fail(HATA_ERR_UNSUPPORTED, "group size G=%d unsupported (1, 2, 4, 8)", G);
+  if ((int64_t)B * Hkv > (1 << 24)) return fail(HATA_ERR_SHAPE, "B*Hkv=%lld too large", (long long)B * Hkv);
+  return HATA_OK;
+}
+
+int check_len(int64_t cap, int64_t max_len) {
+  if (cap < 1 || cap > (int64_t)1 << 30) return fail(HATA_ERR_SHAPE, "cap=%lld out of range [1, 2^30]", (long long)cap);
+  if (max_len < 1 || max_len > cap)
+    return fail(HATA_ERR_SHAPE, "max_len=%lld must lie in [1, cap=%lld]", (long long)max_len, (long long)cap);
+  return HATA_OK;
+}
+
+int check_k(int k) {
+  if (k < 1 || k > 4096) return fail(HATA_ERR_UNSUPPORTED, "budget k=%d outside [1, 4096]", k);
+  return HATA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* hata_status_string(int status) {
+  switch (status) {
+    case HATA_OK: return "HATA_OK";
+    case HATA_ERR_NULL: return "HATA_ERR_NULL: a required pointer is NULL";
+    case HATA_ERR_SHAPE: return "HATA_ERR_SHAPE: inconsistent or out-of-range sizes";
+    case HATA_ERR_UNSUPPORTED: return "HATA_ERR_UNSUPPORTED: sizes outside the supported set";
+    case HATA_ERR_ALIGN: return "HATA_ERR_ALIGN: misaligned pointer";
+    case HATA_ERR_WORKSPACE: return "HATA_ERR_WORKSPACE: workspace missing or too small";
+    case HATA_ERR_HIP: return "HATA_ERR_HIP: HIP runtime error";
+    default: return "unknown hata_status";
+  }
+}
+
+const char* hata_last_error_message(void) { return g_msg; }
+
+int hata_version(void) { return 100; }
+
+int hata_encode_append(const void* x, int64_t x_rows, int B, int H, int n_new, const float* W_H,
+                       int Hkv, int d, int r, uint64_t* codes, int64_t cap, const int32_t* pos,
+                       void* stream) {
+  if (!x || !W_H || !codes) return fail(HATA_ERR_NULL, "encode_append: x, W_H and codes are required");
+  int st = check_dims(d, r);
+  if (st) return st;
+  if (B < 1 || H < 1 || Hkv < 1) return fail(HATA_ERR_SHAPE, "encode_append: B=%d H=%d Hkv=%d", B, H, Hkv);
+  if (H % Hkv != 0) return fail(HATA_ERR_SHAPE, "encode_append: H=%d not a multiple of Hkv=%d", H, Hkv);
+  if (n_new < 0) return fail(HATA_ERR_SHAPE, "encode_append: n_new=%d < 0", n_new);
+  if (x_rows < 1 || cap < 1) return fail(HATA_ERR_SHAPE, "encode_append: x_rows=%lld cap=%lld", (long long)x_rows, (long long)cap);
+  if (!pos && ((int64_t)n_new > x_rows || (int64_t)n_new > cap))
+    return fail(HATA_ERR_SHAPE, "encode_append: n_new=%d exceeds x_rows=%lld or cap=%lld", n_new, (long long)x_rows, (long long)cap);
+  if ((int64_t)(H / Hkv) * n_new > ((int64_t)1 << 31) - 1) return fail(HATA_ERR_SHAPE, "encode_append: too many rows");
+  if (!aligned(codes, 16)) return fail(HATA_ERR_ALIGN, "encode_append: codes must be 16-byte aligned");
+  if (!aligned(x, 4)) return fail(HATA_ERR_ALIGN, "encode_append: x must be 4-byte aligned");
+  if (n_new == 0) return HATA_OK;
+  if ((st = pre_launch("encode_append"))) return st;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const auto* xb = static_cast<const uint16_t*>(x);
+  hipError_t e;
+  e = hata::launch_encode_rows(xb, x_rows, B, H, Hkv, n_new, W_H, codes, cap, pos, 0, s);
+  return check_launch(e, "encode_append launch");
+}
+
+int hata_hamming_scores(const uint64_t* q_codes, const uint64_t* k_codes, int B, int Hq, int Hkv,
+                        int r, int64_t cap, const int32_t* seq_lens, int64_t max_len,
+                        uint16_t* scores, void* stream) {
+  if (!q_codes || !k_codes || !seq_lens || !scores) return fail(HATA_ERR_NULL, "hamming_scores: null pointer");
+  int st = check_dims(128, r);
+  if (st) return st;
+  if ((st = check_heads(B, Hq, Hkv))) return st;
+  if ((st = check_len(cap, max_len))) return st;
+  if (!aligned(k_codes, 16) || !aligned(q_codes, 8) || !aligned(scores, 2))
+    return fail(HATA_ERR_ALIGN, "hamming_scores: k_codes must be 16-byte aligned");
+  if ((st = pre_launch("hamming_scores"))) return st;
+  hipError_t e = hata::launch_hamming(q_codes, k_codes, B, Hq, Hkv, cap, seq_lens, max_len, scores,
+                                      cap, reinterpret_cast<hipStream_t>(stream));
+  return check_launch(e, "hamming_scores launch");
+}
+
+int hata_topk(const uint16_t* scores, int B, int Hkv, int64_t cap, const int32_t* seq_lens,
+              int64_t max_len, int k, int max_score, int32_t* idx, void* ws, size_t ws_bytes,
+              void* stream) {
+  (void)ws;
+  (void)ws_bytes;
+  if (!scores || !seq_lens || !idx) return fail(HATA_ERR_NULL, "topk: null pointer");
+  if (B < 1 || Hkv < 1) return fail(HATA_ERR_SHAPE, "topk: B=%d Hkv=%d", B, Hkv);
+  int st = check_len(cap, max_len);
+  if (st) return st;
+  if ((st = check_k(k))) return st;
+  if (max_score < 0 || max_score > 8 * 128)
+    return fail(HATA_ERR_UNSUPPORTED, "topk: max_score=%d outside [0, 1024]", max_score);
+  if (!aligned(scores, 2) || !aligned(idx, 4)) return fail(HATA_ERR_ALIGN, "topk: misaligned buffer");
+  if ((st = pre_launch("topk"))) return st;
+  hipError_t e = hata::launch_topk(scores, cap, B, Hkv, cap, seq_lens, k, max_score, idx,
+                                   reinterpret_cast<hipStream_t>(stream));
+  return check_launch(e, "topk launch");
+}
+
+int hata_sparse_decode(const void* q, const void* K, const void* V, int B, int Hq, int Hkv, int d,
+                       int64_t cap, const int32_t* idx, int k, float scale, float* out, void* ws,
+                       size_t ws_bytes, void* stream) {
+  if (!q || !K || !V || !idx || !out) return fail(HATA_ERR_NULL, "sparse_decode: null pointer");
+  int st = check_dims(d, 128);
+  if (st) return st;
+  if ((st = check_heads(B, Hq, Hkv))) return st;
+  if (cap < 1) return fail(HATA_ERR_SHAPE, "sparse_decode: cap=%lld", (long long)cap);
+  if ((st = check_k(k))) return st;
+  if (!aligned(q, 16) || !aligned(K, 16) || !aligned(V, 16))
+    return fail(HATA_ERR_ALIGN, "sparse_decode: q, K and V must be 16-byte aligned");
+  const size_t need = hata_workspace_bytes(HATA_OP_SPARSE_DECODE, B, Hq, Hkv, d, 128, k, k);
+  if (!ws || ws_bytes < need)
+    return fail(HATA_ERR_WORKSPACE, "sparse_decode: workspace of %zu bytes needed, %zu given", need, ws_bytes);
+  if ((st = pre_launch("sparse_decode"))) return st;
+  hipError_t e = hata::launch_attention(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(K),
+                                        static_cast<const uint16_t*>(V), B, Hq, Hkv, cap, idx, k,
+                                        nullptr, k, scale, out, static_cast<float*>(ws),
+                                        reinterpret_cast<hipStream_t>(stream));
+  return check_launch(e, "sparse_decode launch");
+}
+
+int hata_dense_decode(const void* q, const void* K, const void* V, int B, int Hq, int Hkv, int d,
+                      int64_t cap, const int32_t* seq_lens, int64_t max_len, float scale,
+                      float* out, void* ws, size_t ws_bytes, void* stream) {
+  if (!q || !K || !V || !seq_lens || !out) return fail(HATA_ERR_NULL, "dense_decode: null pointer");
+  int st = check_dims(d, 128);
+  if (st) return st;
+  if ((st = check_heads(B, Hq, Hkv))) return st;
+  if ((st = check_len(cap, max_len))) return st;
+  if (!aligned(q, 16) || !aligned(K, 16) || !aligned(V, 16))
+    return fail(HATA_ERR_ALIGN, "dense_decode: q, K and V must be 16-byte aligned");
+  const size_t need = hata_workspace_bytes(HATA_OP_DENSE_DECODE, B, Hq, Hkv, d, 128, max_len, 1);
+  if (!ws || ws_bytes < need)
+    return fail(HATA_ERR_WORKSPACE, "dense_decode: workspace of %zu bytes needed, %zu given", need, ws_bytes);
+  if ((st = pre_launch("dense_decode"))) return st;
+  hipError_t e = hata::launch_attention(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(K),
+                                        static_cast<const uint16_t*>(V), B, Hq, Hkv, cap, nullptr, 0,
+                                        seq_lens, max_len, scale, out, static_cast<float*>(ws),
+                                        reinterpret_cast<hipStream_t>(stream));
+  return check_launch(e, "dense_decode launch");
+}
+
+int hata_decode_step(const void* q, const void* K, const void* V, const float* W_H, uint64_t* codes,
+                     int B, int Hq, int Hkv, int d, int r, int64_t cap, const int32_t* seq_lens,
+                     int64_t max_len, int k, float scale, float* out, int32_t* idx_out, void* ws,
+                     size_t ws_bytes, void* stream) {
+  if (!q || !K || !V || !W_H || !codes || !seq_lens || !out)
+    return fail(HATA_ERR_NULL, "decode_step: null pointer");
+  int st = check_dims(d, r);
+  if (st) return st;
+  if ((st = check_heads(B, Hq, Hkv))) return st;
+  if ((st = check_len(cap, max_len))) return st;
+  if ((st = check_k(k))) return st;
+  if (!aligned(codes, 16) || !aligned(q, 16) || !aligned(K, 16) || !aligned(V, 16))
+    return fail(HATA_ERR_ALIGN, "decode_step: q, K, V and codes must be 16-byte aligned");
+  int cus = 0;
+  if ((st = current_cus(&cus))) return st;
+  const hata::StepPlan p = hata::plan_decode_step(B, Hq, Hkv, max_len, k, cus);
+  if (!ws || ws_bytes < p.total)
+    return fail(HATA_ERR_WORKSPACE, "decode_step: workspace of %zu bytes needed, %zu given", p.total, ws_bytes);
+  if ((st = pre_launch("decode_step"))) return st;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  auto* wsb = static_cast<unsigned char*>(ws);
+  const auto* qb = static_cast<const uint16_t*>(q);
+  const auto* Kb = static_cast<const uint16_t*>(K);
+  const auto* Vb = static_cast<const uint16_t*>(V);
+  if (p.fused) {
+    hipError_t e = hata::launch_decode_step(p, qb, Kb, Vb, W_H, codes, B, Hq, Hkv, cap, seq_lens, k,
+                                            scale, out, idx_out, wsb, s);
+    return check_launch(e, "decode_step launch");
+  }
+  // Staged steps: the per-unit scores do not fit on chip at this shape.
+  const int G = Hq / Hkv;
+  auto* qc = reinterpret_cast<uint64_t*>(wsb + p.off_qc);
+  auto* sc = reinterpret_cast<uint16_t*>(wsb + p.off_scores);
+  auto* part = reinterpret_cast<float*>(wsb + p.off_attn);
+  hipError_t e = hata::launch_encode_rows(qb, 1, B, Hq, Hkv, 1, W_H, qc, 1, nullptr, 0, s);
+  if (e == hipSuccess)  // key append at row seq_lens[b] - 1
+    e = hata::launch_encode_rows(Kb, cap, B, Hkv, Hkv, 1, W_H, codes, cap, seq_lens, -1, s);
+  (void)G;
+  if (e == hipSuccess) e = hata::launch_hamming(qc, codes, B, Hq, Hkv, cap, seq_lens, max_len, sc, max_len, s);
+  int32_t* idx = idx_out;
+  if (e == hipSuccess && !idx) return fail(HATA_ERR_UNSUPPORTED, "decode_step: this shape needs idx_out");
+  if (e == hipSuccess) e = hata::launch_topk(sc, max_len, B, Hkv, cap, seq_lens, k, G * 128, idx, s);
+  if (e == hipSuccess)
+    e = hata::launch_attention(qb, Kb, Vb, B, Hq, Hkv, cap, idx, k, nullptr, k, scale, out, part, s);
+  return check_launch(e, "decode_step (staged) launch");
+}
+
+size_t hata_workspace_bytes(int op, int B, int Hq, int Hkv, int d, int r, int64_t max_len, int k) {
+  (void)d;
+  (void)r;
+  if (B < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || max_len < 1 || k < 1) return 0;
+  const int G = Hq / Hkv;
+  switch (op) {
+    case HATA_OP_TOPK:
+      return 0;
+    case HATA_OP_SPARSE_DECODE:
+      return hata::attn_part_floats(B, Hkv, G, k) * sizeof(float);
+    case HATA_OP_DENSE_DECODE:
+      return hata::attn_part_floats(B, Hkv, G, max_len) * sizeof(float);
+    case HATA_OP_DECODE_STEP: {
+      int cus = 0;
+      if (current_cus(&cus) != HATA_OK) return 0;
+      return hata::plan_decode_step(B, Hq, Hkv, max_len, k, cus).total;
+    }
+    default:
+      return 0;
+  }
+}
+
+int hata_workspace_reset(void* ws, size_t ws_bytes, void* stream) {
+  if (!ws) return fail(HATA_ERR_NULL, "workspace_reset: ws is NULL");
+  if (ws_bytes == 0) return HATA_OK;
+  if (!aligned(ws, 4)) return fail(HATA_ERR_ALIGN, "workspace_reset: ws must be 4-byte aligned");
+  if (int st = pre_launch("workspace_reset")) return st;
+  hipError_t e = hata::launch_fill_zero(ws, ws_bytes, reinterpret_cast<hipStream_t>(stream));
+  return check_launch(e, "workspace_reset launch");
+}
+
+int hata_workspace_check(const void* ws, size_t ws_bytes, int* err_out, void* stream) {
+  if (!ws || !err_out) return fail(HATA_ERR_NULL, "workspace_check: null pointer");
+  if (ws_bytes < 4) return fail(HATA_ERR_WORKSPACE, "workspace_check: workspace too small");
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  hipError_t e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
+  uint32_t v = 0;
+  e = hipMemcpy(&v, ws, sizeof v, hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return hip_fail(e, "hipMemcpy");
+  *err_out = (int)v;
+  return HATA_OK;
+}
+
+}  // extern "C"

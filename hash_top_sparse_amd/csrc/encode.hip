@@ -1,0 +1,138 @@
+// encode.hip -- HashEncode (projection by W_H, sign, bit-pack) with cache append.
+//
+// HATA paper notes, section "Key design: Decode-stage algorithm" (HashEncode =
+// matrix multiply + Sign + BitPack, then append the key code to the code
+// cache) and section "Hardware-efficient optimisation" (projection, sign,
+// bit-pack and cache update fused in one kernel).  bit c = (p_c >= 0.0f),
+// word c/64, bit c%64.
+//
+// GEMV form for a few rows per (sequence, KV head): a 256-thread workgroup
+// holds the KV head's W_H in registers -- lane = output column (64 columns
+// per wave), the two halves of the 128 input channels split across wave pairs
+// -- and packs each 64-column half of a code with one wave64 ballot.
+#include "hata_device.hpp"
+#include "hata_launch.hpp"
+
+namespace hata {
+
+namespace {
+
+constexpr int kRowsPerBatch = 4;
+
+__global__ __launch_bounds__(kNT) void encode_rows_kernel(
+    const uint16_t* __restrict__ x, int64_t x_rows, int H, int Hkv, int n_new,
+    const float* __restrict__ W, uint64_t* __restrict__ codes, int64_t cap,
+    const int32_t* __restrict__ pos, int pos_off, int rows_per_block) {
+  __shared__ float xs[kRowsPerBatch][kD];
+  __shared__ float red[kRowsPerBatch][kR];
+  const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
+  const int G = H / Hkv;
+  const int bh = blockIdx.y;
+  const int b = bh / Hkv, hk = bh - b * Hkv;
+  const int col = (wv & 1) * 64 + lane, dh = wv >> 1;
+
+  const int total = G * n_new;
+  const int r_begin = blockIdx.x * rows_per_block;
+  const int r_end = min(total, r_begin + rows_per_block);
+  if (r_begin >= r_end) return;
+
+  float wr[64];
+  const float* Wh = W + (int64_t)hk * kD * kR;
+#pragma unroll
+  for (int i = 0; i < 64; ++i) wr[i] = Wh[(dh * 64 + i) * kR + col];
+
+  const int64_t p_b = (pos ? (int64_t)pos[b] : 0) + pos_off;
+  const int64_t lim = x_rows < cap ? x_rows : cap;
+
+  for (int r0 = r_begin; r0 < r_end; r0 += kRowsPerBatch) {
+    // stage up to 4 rows (64 threads per row, 2 bf16 each)
+    {
+      const int rr = t >> 6, c2 = t & 63;
+      const int r = r0 + rr;
+      float lo = 0.f, hi = 0.f;
+      if (r < r_end) {
+        const int g = r / n_new, j = r - g * n_new;
+        const int64_t ridx = p_b + j;
+        if (ridx >= 0 && ridx < lim) {
+          const int64_t head = (int64_t)b * H + (int64_t)hk * G + g;
+          const uint32_t two = reinterpret_cast<const uint32_t*>(x + (head * x_rows + ridx) * kD)[c2];
+          lo = bf16_lo(two);
+          hi = bf16_hi(two);
+        }
+      }
+      xs[rr][2 * c2] = lo;
+      xs[rr][2 * c2 + 1] = hi;
+    }
+    __syncthreads();
+    float p[kRowsPerBatch];
+#pragma unroll
+    for (int rr = 0; rr < kRowsPerBatch; ++rr) {
+      float s = 0.f;
+#pragma unroll
+      for (int i = 0; i < 64; ++i) s = fmaf(xs[rr][dh * 64 + i], wr[i], s);
+      p[rr] = s;
+    }
+    if (dh == 1) {
+#pragma unroll
+      for (int rr = 0; rr < kRowsPerBatch; ++rr) red[rr][col] = p[rr];
+    }
+    __syncthreads();
+    if (dh == 0) {
+#pragma unroll
+      for (int rr = 0; rr < kRowsPerBatch; ++rr) {
+        const float s = p[rr] + red[rr][col];
+        const uint64_t m = __ballot(s >= 0.0f);
+        const int r = r0 + rr;
+        if (lane == 0 && r < r_end) {
+          const int g = r / n_new, j = r - g * n_new;
+          const int64_t ridx = p_b + j;
+          if (ridx >= 0 && ridx < lim) {
+            const int64_t head = (int64_t)b * H + (int64_t)hk * G + g;
+            codes[(head * cap + ridx) * 2 + (wv & 1)] = m;
+          }
+        }
+      }
+    }
+    __syncthreads();
+  }
+}
+
+}  // namespace
+
+hipError_t launch_encode_rows(const uint16_t* x, int64_t x_rows, int B, int H, int Hkv, int n_new,
+                              const float* W, uint64_t* codes, int64_t cap, const int32_t* pos,
+                              int pos_off, hipStream_t s) {
+  const int G = H / Hkv;
+  const int64_t total = (int64_t)G * n_new;
+  // enough blocks to cover the chip for long row runs, few rows per block otherwise
+  int64_t rpb = (total + 31) / 32;
+  if (rpb < 16) rpb = 16;
+  rpb = (rpb + kRowsPerBatch - 1) / kRowsPerBatch * kRowsPerBatch;
+  const int64_t nbx = (total + rpb - 1) / rpb;
+  dim3 grid((unsigned)nbx, (unsigned)(B * Hkv));
+  hipLaunchKernelGGL(encode_rows_kernel, grid, dim3(kNT), 0, s, x, x_rows, H, Hkv, n_new, W, codes,
+                     cap, pos, pos_off, (int)rpb);
+  return hipGetLastError();
+}
+
+__global__ void fill_zero_kernel(unsigned char* p, size_t bytes) {
+  const size_t words = bytes / 4;
+  uint32_t* w = reinterpret_cast<uint32_t*>(p);
+  const size_t stride = (size_t)gridDim.x * blockDim.x;
+  const size_t i0 = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  for (size_t i = i0; i < words; i += stride) w[i] = 0u;
+  for (size_t i = words * 4 + i0; i < bytes; i += stride) p[i] = 0;
+}
+
+// Zero `bytes` bytes at p (4-byte aligned) with a kernel, so the reset can be
+// captured in a HIP graph.
+hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s) {
+  size_t blocks = (bytes / 4 + 255) / 256;
+  if (blocks > 4096) blocks = 4096;
+  if (blocks < 1) blocks = 1;
+  hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)blocks), dim3(256), 0, s,
+                     static_cast<unsigned char*>(p), bytes);
+  return hipGetLastError();
+}
+
+}  // namespace hata

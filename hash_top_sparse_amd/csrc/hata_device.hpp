@@ -1,0 +1,294 @@
+// hata_device.hpp -- device helpers shared by the HATA kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace hata {
+
+constexpr int kD = 128;      // head dim
+constexpr int kR = 128;      // code bits
+constexpr int kWords32 = 4;  // 32-bit words per code
+constexpr int kNT = 256;     // threads per workgroup of the decode kernels
+
+// ---------------------------------------------------------------- bf16
+__device__ __forceinline__ float bf16_lo(uint32_t two) { return __uint_as_float(two << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t two) { return __uint_as_float(two & 0xFFFF0000u); }
+
+// 8 bf16 (one 16-byte load) -> 8 fp32
+__device__ __forceinline__ void unpack8(const uint4 v, float (&f)[8]) {
+  f[0] = bf16_lo(v.x); f[1] = bf16_hi(v.x);
+  f[2] = bf16_lo(v.y); f[3] = bf16_hi(v.y);
+  f[4] = bf16_lo(v.z); f[5] = bf16_hi(v.z);
+  f[6] = bf16_lo(v.w); f[7] = bf16_hi(v.w);
+}
+
+// ------------------------------------------------------- memory access
+// Streaming 16-byte load that should not displace reusable lines.
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 load_stream16(const uint4* p) {
+  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+// Agent-coherent accesses for data that workgroups of one launch exchange.
+// They compile to global_load/global_store with the device-scope cache bit
+// (sc1), which bypasses the per-XCD L2 state that another XCD cannot see,
+// so no L2 writeback or invalidate is needed around them.
+template <typename T>
+__device__ __forceinline__ void st_agent(T* p, T v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+template <typename T>
+__device__ __forceinline__ T ld_agent(const T* p) {
+  return __hip_atomic_load(const_cast<T*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// Wait until every memory operation this wave issued has completed.
+__device__ __forceinline__ void wait_all_mem() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+// ------------------------------------------------------- wave reductions
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+// Sum over each aligned group of 16 lanes; every lane gets the group's sum.
+// quad_perm [1,0,3,2], quad_perm [2,3,0,1], row_half_mirror, row_mirror.
+__device__ __forceinline__ float sum16(float v) {
+  v += dpp_f<0xB1>(v);
+  v += dpp_f<0x4E>(v);
+  v += dpp_f<0x141>(v);
+  v += dpp_f<0x140>(v);
+  return v;
+}
+
+__device__ __forceinline__ uint32_t wave_incl_scan_u32(uint32_t v, int lane) {
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    uint32_t o = __shfl_up(v, off, 64);
+    if (lane >= off) v += o;
+  }
+  return v;
+}
+
+// Exclusive scan over the 256 threads of a workgroup; `tmp` holds 4 words of
+// LDS.  Returns the exclusive prefix; *total gets the block sum.  Contains
+// __syncthreads, so every thread must call it.
+__device__ __forceinline__ uint32_t block_excl_scan_u32(uint32_t v, uint32_t* tmp, uint32_t* total) {
+  const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
+  uint32_t inc = wave_incl_scan_u32(v, lane);
+  if (lane == 63) tmp[wv] = inc;
+  __syncthreads();
+  uint32_t base = 0, all = 0;
+#pragma unroll
+  for (int i = 0; i < kNT / 64; ++i) {
+    uint32_t s = tmp[i];
+    base += (i < wv) ? s : 0u;
+    all += s;
+  }
+  __syncthreads();
+  *total = all;
+  return base + inc - v;
+}
+
+// ------------------------------------------------------- Hamming with GQA sum
+// For a code c and G query codes q_g, sum_g popcount(q_g ^ c) equals
+// sum over bits of (c_bit ? #{g : q_g bit = 0} : #{g : q_g bit = 1}).  Both
+// per-bit counts are kept bit-sliced (J slices of 32-bit masks per word), so
+// the per-token work is J bitfield-selects and J popcounts per word instead
+// of G xors and G popcounts.
+template <int G>
+struct SliceCount {
+  static constexpr int J = (G == 1) ? 1 : (G == 2) ? 2 : (G <= 7) ? 3 : 4;
+};
+
+template <int G>
+struct QMasks {
+  uint32_t one[SliceCount<G>::J][kWords32];   // bit slices of #{g: q_g bit = 1}
+  uint32_t zero[SliceCount<G>::J][kWords32];  // bit slices of #{g: q_g bit = 0}
+};
+
+// qw[g][w]: 32-bit word w of query code g.
+template <int G>
+__device__ __forceinline__ void build_qmasks(const uint32_t (&qw)[G][kWords32], QMasks<G>& m) {
+  constexpr int J = SliceCount<G>::J;
+#pragma unroll
+  for (int w = 0; w < kWords32; ++w) {
+    uint32_t c1[J], c0[J];
+#pragma unroll
+    for (int j = 0; j < J; ++j) { c1[j] = 0; c0[j] = 0; }
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      uint32_t x1 = qw[g][w], x0 = ~qw[g][w];
+#pragma unroll
+      for (int j = 0; j < J; ++j) {  // bit-sliced increment by one bit
+        uint32_t n1 = c1[j] ^ x1, n0 = c0[j] ^ x0;
+        x1 &= c1[j];
+        x0 &= c0[j];
+        c1[j] = n1;
+        c0[j] = n0;
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < J; ++j) { m.one[j][w] = c1[j]; m.zero[j][w] = c0[j]; }
+  }
+}
+
+template <int G>
+__device__ __forceinline__ uint32_t gqa_hamming(const uint4 c, const QMasks<G>& m) {
+  constexpr int J = SliceCount<G>::J;
+  const uint32_t cw[4] = {c.x, c.y, c.z, c.w};
+  uint32_t s = 0;
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    uint32_t acc = 0;
+#pragma unroll
+    for (int w = 0; w < kWords32; ++w) {
+      uint32_t sel = (cw[w] & m.zero[j][w]) | (~cw[w] & m.one[j][w]);
+      acc = __builtin_popcount(sel) + acc;
+    }
+    s += acc << j;
+  }
+  return s;
+}
+
+// ------------------------------------------------------- online softmax
+// Per-lane state of a 16-lane group that attends rows with G query heads;
+// the lane holds 8 of the 128 channels (channels sub*8 .. sub*8+7).
+template <int G>
+struct SoftmaxState {
+  float m[G], l[G], acc[G][8];
+  __device__ __forceinline__ void init() {
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      m[g] = -INFINITY;
+      l[g] = 0.f;
+#pragma unroll
+      for (int c = 0; c < 8; ++c) acc[g][c] = 0.f;
+    }
+  }
+};
+
+// Attend UNROLL rows at once: logits, one max update, then weights.  `valid`
+// masks rows past the end (their loads must not have been issued).
+template <int G, int UNROLL>
+__device__ __forceinline__ void attend_block(SoftmaxState<G>& st, const float (&qreg)[G][8],
+                                             const uint4 (&kv)[UNROLL], const uint4 (&vv)[UNROLL],
+                                             const bool (&valid)[UNROLL], float scale) {
+  float z[UNROLL][G];
+#pragma unroll
+  for (int u = 0; u < UNROLL; ++u) {
+    float kf[8];
+    unpack8(kv[u], kf);
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      float s = 0.f;
+#pragma unroll
+      for (int c = 0; c < 8; ++c) s = fmaf(qreg[g][c], kf[c], s);
+      z[u][g] = sum16(s) * scale;
+    }
+  }
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    float mx = st.m[g];
+#pragma unroll
+    for (int u = 0; u < UNROLL; ++u) mx = valid[u] ? fmaxf(mx, z[u][g]) : mx;
+    // exp(-inf) = 0 when m was -inf; no valid row at all keeps the state
+    const float alpha = (mx == -INFINITY) ? 1.f : __expf(st.m[g] - mx);
+    st.l[g] *= alpha;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) st.acc[g][c] *= alpha;
+    st.m[g] = mx;
+  }
+#pragma unroll
+  for (int u = 0; u < UNROLL; ++u) {
+    if (!valid[u]) continue;
+    float vf[8];
+    unpack8(vv[u], vf);
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const float p = __expf(z[u][g] - st.m[g]);
+      st.l[g] += p;
+#pragma unroll
+      for (int c = 0; c < 8; ++c) st.acc[g][c] = fmaf(p, vf[c], st.acc[g][c]);
+    }
+  }
+}
+
+// Merge the 16 row-group states of a 256-thread workgroup (4 waves x 4
+// groups of 16 lanes) into one (M, L, A[128]) record per head:
+//   step 1 combines the 4 groups of a wave with xor-shuffles over 16 and 32
+//   lanes; step 2 combines the 4 waves through LDS.
+// red: LDS of kMergeFloats<G> floats, laid out [4 waves][G][2 + 128]; on
+// return red[0][g] holds head g's merged record.  Fixed merge order.
+constexpr int kRec = 2 + kD;
+template <int G>
+constexpr int kMergeFloats = 4 * G * kRec;
+
+template <int G>
+__device__ __forceinline__ void merge_wg(const SoftmaxState<G>& st, float* red) {
+  const int t = threadIdx.x, lane = t & 63, wv = t >> 6, sub = lane & 15;
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    float M = st.m[g];
+    M = fmaxf(M, __shfl_xor(M, 16, 64));
+    M = fmaxf(M, __shfl_xor(M, 32, 64));
+    const float f = (M == -INFINITY) ? 0.f : __expf(st.m[g] - M);
+    float L = st.l[g] * f;
+    L += __shfl_xor(L, 16, 64);
+    L += __shfl_xor(L, 32, 64);
+    float A[8];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      A[c] = st.acc[g][c] * f;
+      A[c] += __shfl_xor(A[c], 16, 64);
+      A[c] += __shfl_xor(A[c], 32, 64);
+    }
+    if (lane < 16) {
+      float* r = red + (wv * G + g) * kRec;
+      if (sub == 0) { r[0] = M; r[1] = L; }
+#pragma unroll
+      for (int c = 0; c < 8; ++c) r[2 + sub * 8 + c] = A[c];
+    }
+  }
+  __syncthreads();
+  constexpr int PER = (G * kD + kNT - 1) / kNT;
+  float Ms[PER], Ls[PER], As[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int e = t + i * kNT;
+    Ms[i] = -INFINITY; Ls[i] = 0.f; As[i] = 0.f;
+    if (e >= G * kD) continue;
+    const int g = e / kD, c = e % kD;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) M = fmaxf(M, red[(w * G + g) * kRec]);
+    float L = 0.f, A = 0.f;
+    if (M != -INFINITY) {
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const float* r = red + (w * G + g) * kRec;
+        const float f = __expf(r[0] - M);
+        L = fmaf(r[1], f, L);
+        A = fmaf(r[2 + c], f, A);
+      }
+    }
+    Ms[i] = M; Ls[i] = L; As[i] = A;
+  }
+  __syncthreads();  // every wave record has been read
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int e = t + i * kNT;
+    if (e >= G * kD) continue;
+    const int g = e / kD, c = e % kD;
+    float* r0 = red + g * kRec;
+    if (c == 0) { r0[0] = Ms[i]; r0[1] = Ls[i]; }
+    r0[2 + c] = As[i];
+  }
+  __syncthreads();
+}
+
+}  // namespace hata

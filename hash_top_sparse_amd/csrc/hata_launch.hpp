@@ -1,0 +1,56 @@
+// hata_launch.hpp -- host-side launchers of the HATA kernels (internal to libhata.so).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace hata {
+
+// ---------------------------------------------------------------- encode
+// x bf16 [B][H][x_rows][128]; rows p_b + j (j < n_new) -> codes [B][H][cap][2].
+// Row index of (b, j) is (pos ? pos[b] : 0) + pos_off + j.
+hipError_t launch_encode_rows(const uint16_t* x, int64_t x_rows, int B, int H, int Hkv, int n_new,
+                              const float* W, uint64_t* codes, int64_t cap, const int32_t* pos,
+                              int pos_off, hipStream_t s);
+// Same contract, matrix-core path for long row runs (prefill).
+hipError_t launch_encode_bulk(const uint16_t* x, int64_t x_rows, int B, int H, int Hkv, int n_new,
+                              const float* W, uint64_t* codes, int64_t cap, const int32_t* pos,
+                              hipStream_t s);
+
+// ---------------------------------------------------------------- score / select
+hipError_t launch_hamming(const uint64_t* qc, const uint64_t* kc, int B, int Hq, int Hkv,
+                          int64_t cap, const int32_t* seq_lens, int64_t max_len, uint16_t* scores,
+                          int64_t sstride, hipStream_t s);
+hipError_t launch_topk(const uint16_t* scores, int64_t sstride, int B, int Hkv, int64_t cap,
+                       const int32_t* seq_lens, int k, int max_score, int32_t* idx, hipStream_t s);
+
+// ---------------------------------------------------------------- attention
+// Split-K partial attention + combine.  idx == nullptr means dense (rows
+// [0, n_b)).  part: workspace of attn_part_floats(...) floats.
+size_t attn_part_floats(int B, int Hkv, int G, int64_t max_rows);
+hipError_t launch_attention(const uint16_t* q, const uint16_t* K, const uint16_t* V, int B, int Hq,
+                            int Hkv, int64_t cap, const int32_t* idx, int k,
+                            const int32_t* seq_lens, int64_t max_len, float scale, float* out,
+                            float* part, hipStream_t s);
+
+// ---------------------------------------------------------------- fused step
+struct StepPlan {
+  bool fused = false;
+  int G = 0, U = 0, Wg = 1, chunk = 0, xcd_map = 0;
+  size_t lds_bytes = 0;
+  // workspace layout (byte offsets)
+  size_t off_err = 0, off_flags = 0, off_win = 0, off_full = 0, off_part = 0;
+  size_t off_qc = 0, off_scores = 0, off_attn = 0;
+  int full_words = 0;  // 32-bit words per workgroup in the full-histogram area
+  size_t total = 0;
+};
+StepPlan plan_decode_step(int B, int Hq, int Hkv, int64_t max_len, int k, int num_cus);
+hipError_t launch_decode_step(const StepPlan& p, const uint16_t* q, const uint16_t* K,
+                              const uint16_t* V, const float* W, uint64_t* codes, int B, int Hq,
+                              int Hkv, int64_t cap, const int32_t* seq_lens, int k, float scale,
+                              float* out, int32_t* idx_out, unsigned char* ws, hipStream_t s);
+
+hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s);
+
+}  // namespace hata

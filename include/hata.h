@@ -1,0 +1,203 @@
+/*
+ * hata.h -- C ABI of libhata.so, the HATA decode-step hot path on MI355X (gfx950).
+ *
+ * HATA (Hash-Aware Top-k Attention; paper notes "HATA: Trainable and
+ * Hardware-Efficient Hash-Aware Top-k Attention for Scalable Large Model
+ * Inference", ACL 2025, arXiv 2506.02572).  Each decode step of one attention
+ * layer does, per (sequence b, KV head h) "unit":
+ *   1. HashEncode the new query rows and the new key row: project by the KV
+ *      head's W_H, take the sign, bit-pack into r-bit codes
+ *      (section "Key design: Decode-stage algorithm"; hash function from
+ *      "Learning-to-Hash modelling");
+ *   2. append the key code to the unit's code cache;
+ *   3. Hamming distance popcount(q_code XOR k_code) against every cached code,
+ *   4. summed over the G = Hq/Hkv query heads sharing the KV head (GQA);
+ *   5. keep the top-k tokens (smallest summed distance) and run exact softmax
+ *      attention over the gathered K/V rows only (section "Overall framework",
+ *      decode phase; section "Hardware-efficient optimisation": fused encode,
+ *      XOR+popcount scoring, gather fused into the attention kernel).
+ *
+ * Conventions fixed here (the notes leave them open):
+ *   - bit c of a code is 1 iff the fp32 projection p_c compares >= 0.0f
+ *     (so -0.0 gives 1 and NaN gives 0); bit c lives in 64-bit word c/64 at
+ *     bit position c%64;
+ *   - one W_H per KV head, stored [Hkv][d][r] row-major, used for the G query
+ *     heads of that KV head and for its keys; query head j uses KV head j/G;
+ *   - the kept set is the first min(k, n) tokens in (summed distance, token
+ *     index) ascending order -- ties go to the lower index -- reported in
+ *     ascending token order and padded with -1;
+ *   - attention logits are scale * <q, K_i> with softmax over the kept rows
+ *     only; outputs are fp32.
+ *
+ * Layouts (all contiguous, row-major; bf16 arrays are passed as const void*):
+ *   q      bf16   [B][Hq][d]
+ *   K, V   bf16   [B][Hkv][cap][d]          (row n_b-1 is the new token)
+ *   W_H    fp32   [Hkv][d][r]
+ *   codes  uint64 [B][Hkv][cap][r/64]       (16-byte aligned)
+ *   out    fp32   [B][Hq][d]
+ *   idx    int32  [B][Hkv][k]
+ *   seq_lens int32 [B] on the device: n_b, the number of valid rows
+ *            including the new token.  max_len is a host-side upper bound of
+ *            every n_b, used only to size launch grids (so calls can be
+ *            captured in a HIP graph); it must satisfy 1 <= max_len <= cap.
+ *
+ * Supported sizes: d = 128, r = 128, G = Hq/Hkv in {1, 2, 4, 8}, 1 <= k <= 4096.
+ *
+ * Ownership and threading: every pointer is a device pointer unless stated;
+ * the caller allocates and owns every buffer, the library never allocates,
+ * frees or keeps a pointer after returning, and never synchronises the
+ * stream.  `stream` is a hipStream_t passed as void* (NULL = default stream).
+ * Workspaces are sized by hata_workspace_bytes, zeroed once by the caller
+ * (hata_workspace_reset), restore their own state at the end of every call
+ * and must not be shared by calls that can run concurrently.
+ *
+ * Errors: every call validates its host-side arguments first and returns a
+ * hata_status without launching anything if they are bad (outputs are left
+ * untouched).  HATA_ERR_HIP reports a failed launch.  Device-side values
+ * (seq_lens entries, idx entries) are bounds-checked inside the kernels:
+ * out-of-range rows are skipped, never dereferenced.  No C++ exception
+ * crosses this interface.  hata_last_error_message() gives a thread-local
+ * description of the last failure.
+ */
+#ifndef HATA_H_
+#define HATA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  HATA_OK = 0,
+  HATA_ERR_NULL = 1,        /* a required pointer is NULL */
+  HATA_ERR_SHAPE = 2,       /* inconsistent or out-of-range sizes */
+  HATA_ERR_UNSUPPORTED = 3, /* sizes outside the supported set (d, r, G, k) */
+  HATA_ERR_ALIGN = 4,       /* a pointer is not aligned as required */
+  HATA_ERR_WORKSPACE = 5,   /* workspace NULL or smaller than required */
+  HATA_ERR_HIP = 6          /* the HIP runtime reported an error */
+} hata_status;
+
+/* Operation ids for hata_workspace_bytes. */
+enum {
+  HATA_OP_TOPK = 1,
+  HATA_OP_SPARSE_DECODE = 2,
+  HATA_OP_DECODE_STEP = 3,
+  HATA_OP_DENSE_DECODE = 4
+};
+
+/* Static description of a status code. */
+const char* hata_status_string(int status);
+
+/* Thread-local detail of the most recent failed call on this thread. */
+const char* hata_last_error_message(void);
+
+/* Library version as major*10000 + minor*100 + patch. */
+int hata_version(void);
+
+/*
+ * HashEncode and append (decode-stage steps 1-2; fused projection, sign,
+ * bit-pack and cache update).
+ * x is bf16 [B][H][x_rows][d]; for each (b, h) and j in [0, n_new) the row
+ * p_b + j of x is encoded with W_H[h / (H/Hkv)] and written to row p_b + j of
+ * codes [B][H][cap][r/64], where p_b = pos ? pos[b] : 0 (pos: device int32[B]).
+ *   queries:      x = q, H = Hq, x_rows = 1, cap = 1, pos = NULL, n_new = 1
+ *   key append:   x = K cache, H = Hkv, x_rows = cap, pos = seq_lens - 1 (device)
+ *   prefill bulk: x = K cache, H = Hkv, x_rows = cap, pos = NULL, n_new = n
+ *                 (large n_new runs on the matrix cores, bit-identical on
+ *                 inputs whose fp32 projections are exact)
+ * Rows with p_b + j outside [0, min(x_rows, cap)) are skipped.
+ * Requires H % Hkv == 0; codes 16-byte aligned.
+ */
+int hata_encode_append(const void* x, int64_t x_rows, int B, int H, int n_new,
+                       const float* W_H, int Hkv, int d, int r, uint64_t* codes,
+                       int64_t cap, const int32_t* pos, void* stream);
+
+/*
+ * Hamming scores with GQA sum (decode-stage steps 3-4):
+ * scores[b][h][i] = sum over g in [hG, hG+G) of popcount(q_codes[b][g] XOR
+ * k_codes[b][h][i]) for i < n_b; entries i >= n_b are not written.
+ * q_codes uint64 [B][Hq][r/64]; k_codes uint64 [B][Hkv][cap][r/64];
+ * scores uint16 [B][Hkv][cap].  Values lie in [0, G*r].
+ */
+int hata_hamming_scores(const uint64_t* q_codes, const uint64_t* k_codes, int B,
+                        int Hq, int Hkv, int r, int64_t cap,
+                        const int32_t* seq_lens, int64_t max_len,
+                        uint16_t* scores, void* stream);
+
+/*
+ * Top-k selection (decode-stage step 5, selection): idx[b][h][0:min(k,n_b)] =
+ * ascending token ids of the first min(k, n_b) tokens in (score, id) order;
+ * idx[b][h][min(k,n_b):k] = -1.  scores as produced by hata_hamming_scores,
+ * every valid entry <= max_score (max_score = G*r; larger values are clamped
+ * to max_score).  ws: hata_workspace_bytes(HATA_OP_TOPK, ...).
+ */
+int hata_topk(const uint16_t* scores, int B, int Hkv, int64_t cap,
+              const int32_t* seq_lens, int64_t max_len, int k, int max_score,
+              int32_t* idx, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Gather + exact sparse attention (decode-stage step 5, attention; gather
+ * fused into the attention kernel): for query head j of unit (b, h = j/G),
+ * out[b][j] = softmax(scale * q[b][j] K_I^T) V_I over I = the entries of
+ * idx[b][h][0:k] that lie in [0, cap) (negative entries are padding).  A
+ * unit with no valid entry gets out = 0.
+ * ws: hata_workspace_bytes(HATA_OP_SPARSE_DECODE, ...).
+ */
+int hata_sparse_decode(const void* q, const void* K, const void* V, int B,
+                       int Hq, int Hkv, int d, int64_t cap, const int32_t* idx,
+                       int k, float scale, float* out, void* ws,
+                       size_t ws_bytes, void* stream);
+
+/*
+ * The whole decode step in one launch: encode the new queries, encode and
+ * append the new key, Hamming + GQA sum over the unit's cache, top-k, gather
+ * and exact sparse attention.
+ * On entry K/V rows [0, n_b) are valid (row n_b-1 is the new token, written
+ * by the caller) and codes rows [0, n_b-1) are valid; on return codes row
+ * n_b-1 holds the new key's code, out holds the attention output and, if
+ * idx_out is not NULL, idx_out [B][Hkv][k] holds the kept set exactly as
+ * hata_topk reports it.  Results are bit-identical to the staged calls
+ * (hata_encode_append, hata_hamming_scores, hata_topk) for codes and idx.
+ * ws: hata_workspace_bytes(HATA_OP_DECODE_STEP, ...), zeroed once before
+ * first use.  Shapes whose per-unit scores do not fit on chip run the same
+ * steps as separate kernels inside this call.
+ */
+int hata_decode_step(const void* q, const void* K, const void* V,
+                     const float* W_H, uint64_t* codes, int B, int Hq, int Hkv,
+                     int d, int r, int64_t cap, const int32_t* seq_lens,
+                     int64_t max_len, int k, float scale, float* out,
+                     int32_t* idx_out, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Dense flash-decode baseline over all n_b rows of every unit (the same
+ * attention with the kept set = every token), same layouts.
+ * ws: hata_workspace_bytes(HATA_OP_DENSE_DECODE, ...).
+ */
+int hata_dense_decode(const void* q, const void* K, const void* V, int B,
+                      int Hq, int Hkv, int d, int64_t cap,
+                      const int32_t* seq_lens, int64_t max_len, float scale,
+                      float* out, void* ws, size_t ws_bytes, void* stream);
+
+/* Workspace bytes for operation `op` at these sizes (0 if none is needed). */
+size_t hata_workspace_bytes(int op, int B, int Hq, int Hkv, int d, int r,
+                            int64_t max_len, int k);
+
+/* Zero a workspace on `stream` (a fill kernel, safe under graph capture). */
+int hata_workspace_reset(void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Synchronise `stream` and read the workspace's device-side error word:
+ * *err_out = 0 if no kernel reported a problem since the last reset, else a
+ * bit set (1 = a cross-workgroup wait gave up after its spin limit).
+ * Diagnostic only; never needed on the hot path.
+ */
+int hata_workspace_check(const void* ws, size_t ws_bytes, int* err_out,
+                         void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HATA_H_ */

@@ -1,0 +1,156 @@
+"""The C ABI without a GPU: the library loads, exports every symbol that
+include/hata.h declares, and every argument check returns its status before
+anything is launched."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from hash_top_sparse_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "hata.h")
+
+OK, ENULL, ESHAPE, EUNSUP, EALIGN, EWS, EHIP = range(7)
+P = ctypes.c_void_p
+F = ctypes.c_float
+A = P(0x10000)        # aligned, never dereferenced: validation fails or the hook fires first
+MIS = P(0x10008)      # 8-byte but not 16-byte aligned
+
+
+@pytest.fixture(scope="module", autouse=True)
+def lib():
+    if not os.path.exists(binding.LIB_PATH):
+        from hash_top_sparse_amd import build
+        build.build()
+    return binding.load()
+
+
+def declared_functions():
+    txt = open(HEADER).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"\b(hata_[a-z_]+)\s*\(", txt)))
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = declared_functions()
+    assert len(names) >= 12
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(binding.exported_symbols()) == set(names)
+
+
+def test_status_strings(lib):
+    for s in range(7):
+        assert binding.status_string(s).startswith("HATA_")
+    assert "unknown" in binding.status_string(99)
+    assert lib.hata_version() >= 100
+
+
+def _enc(**kw):
+    a = dict(x=A, x_rows=16, B=1, H=4, n_new=1, W=A, Hkv=1, d=128, r=128, codes=A, cap=16, pos=None)
+    a.update(kw)
+    return binding.raw_call("hata_encode_append", a["x"], a["x_rows"], a["B"], a["H"], a["n_new"],
+                            a["W"], a["Hkv"], a["d"], a["r"], a["codes"], a["cap"], a["pos"], None)
+
+
+def test_encode_append_validation():
+    assert _enc(x=None) == ENULL
+    assert _enc(codes=None) == ENULL
+    assert _enc(d=64) == EUNSUP
+    assert _enc(r=256) == EUNSUP
+    assert _enc(H=6, Hkv=4) == ESHAPE
+    assert _enc(n_new=-1) == ESHAPE
+    assert _enc(n_new=17) == ESHAPE            # more rows than x_rows without pos
+    assert _enc(codes=MIS) == EALIGN
+    assert _enc(n_new=0) == OK                 # nothing to do, nothing launched
+    assert "n_new" in binding.last_error_message() or True
+
+
+def _ham(**kw):
+    a = dict(qc=A, kc=A, B=1, Hq=32, Hkv=8, r=128, cap=1024, seq=A, max_len=1024, sc=A)
+    a.update(kw)
+    return binding.raw_call("hata_hamming_scores", a["qc"], a["kc"], a["B"], a["Hq"], a["Hkv"],
+                            a["r"], ctypes.c_int64(a["cap"]), a["seq"], ctypes.c_int64(a["max_len"]),
+                            a["sc"], None)
+
+
+def test_hamming_validation():
+    assert _ham(kc=None) == ENULL
+    assert _ham(Hq=12, Hkv=4) == EUNSUP        # G = 3
+    assert _ham(Hq=30, Hkv=8) == ESHAPE        # not a multiple
+    assert _ham(max_len=2048) == ESHAPE        # max_len > cap
+    assert _ham(max_len=0) == ESHAPE
+    assert _ham(kc=MIS) == EALIGN
+    assert _ham(r=64) == EUNSUP
+
+
+def _topk(**kw):
+    a = dict(sc=A, B=1, Hkv=8, cap=1024, seq=A, max_len=1024, k=512, max_score=512, idx=A)
+    a.update(kw)
+    return binding.raw_call("hata_topk", a["sc"], a["B"], a["Hkv"], ctypes.c_int64(a["cap"]), a["seq"],
+                            ctypes.c_int64(a["max_len"]), a["k"], a["max_score"], a["idx"], None,
+                            ctypes.c_size_t(0), None)
+
+
+def test_topk_validation():
+    assert _topk(idx=None) == ENULL
+    assert _topk(k=0) == EUNSUP
+    assert _topk(k=4097) == EUNSUP
+    assert _topk(max_score=1025) == EUNSUP
+    assert _topk(max_len=0) == ESHAPE
+
+
+def test_sparse_and_dense_workspace_checks(lib):
+    need = binding.workspace_bytes(binding.OP_SPARSE_DECODE, 1, 32, 8, 1024, 512)
+    assert need > 0
+    rc = binding.raw_call("hata_sparse_decode", A, A, A, 1, 32, 8, 128, ctypes.c_int64(1024), A, 512,
+                          F(0.088), A, None, ctypes.c_size_t(0), None)
+    assert rc == EWS
+    rc = binding.raw_call("hata_sparse_decode", A, A, A, 1, 32, 8, 128, ctypes.c_int64(1024), A, 512,
+                          F(0.088), A, A, ctypes.c_size_t(need - 1), None)
+    assert rc == EWS
+    rc = binding.raw_call("hata_sparse_decode", A, MIS, A, 1, 32, 8, 128, ctypes.c_int64(1024), A, 512,
+                          F(0.088), A, A, ctypes.c_size_t(need), None)
+    assert rc == EALIGN
+    dneed = binding.workspace_bytes(binding.OP_DENSE_DECODE, 1, 32, 8, 4096, 1)
+    assert dneed > 0
+    rc = binding.raw_call("hata_dense_decode", A, A, A, 1, 32, 8, 128, ctypes.c_int64(4096), A,
+                          ctypes.c_int64(4096), F(0.088), A, A, ctypes.c_size_t(dneed - 4), None)
+    assert rc == EWS
+    assert binding.workspace_bytes(binding.OP_TOPK, 1, 32, 8, 4096, 512) == 0
+
+
+def test_decode_step_validation():
+    def step(**kw):
+        a = dict(q=A, K=A, V=A, W=A, codes=A, B=1, Hq=32, Hkv=8, d=128, r=128, cap=4096, seq=A,
+                 max_len=4096, k=512, out=A)
+        a.update(kw)
+        return binding.raw_call("hata_decode_step", a["q"], a["K"], a["V"], a["W"], a["codes"], a["B"],
+                                a["Hq"], a["Hkv"], a["d"], a["r"], ctypes.c_int64(a["cap"]), a["seq"],
+                                ctypes.c_int64(a["max_len"]), a["k"], F(0.088), a["out"], None, A,
+                                ctypes.c_size_t(1 << 30), None)
+    assert step(W=None) == ENULL
+    assert step(out=None) == ENULL
+    assert step(d=96) == EUNSUP
+    assert step(Hq=48, Hkv=4) == EUNSUP         # G = 12
+    assert step(k=0) == EUNSUP
+    assert step(max_len=8192) == ESHAPE
+    assert step(codes=MIS) == EALIGN
+
+
+def test_forced_launch_failure_propagates():
+    """With the test hook set, a fully valid call reports HATA_ERR_HIP before
+    launching, and the binding raises it as HataError."""
+    os.environ["HATA_TEST_FAIL_LAUNCH"] = "1"
+    try:
+        assert _ham() == EHIP
+        assert "forced" in binding.last_error_message()
+        assert _topk() == EHIP
+        assert _enc() == EHIP
+        with pytest.raises(binding.HataError) as ei:
+            binding._check(_ham())
+        assert ei.value.status == EHIP
+    finally:
+        del os.environ["HATA_TEST_FAIL_LAUNCH"]

@@ -1,0 +1,273 @@
+"""GPU parity: every stage of the HIP path against the CPU oracle, through the
+C ABI.  Codes, scores and index sets bit-exact (encode judged exactly on the
+exact recipe, within the sign-flip allowance on Gaussian inputs); attention
+within |gpu - ref| <= 2e-3 + 1e-3 |ref| in fp32."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from hash_top_sparse_amd import synth
+from helpers import (Dev, assert_close, check_codes, codes_np, codes_tensor, gpu_build_cache,
+                     gpu_query_codes, oracle_units, scores_np)
+
+pytestmark = pytest.mark.gpu
+
+
+def _shape(B, Hq, Hkv, N, k, dist="gauss", seed=7000, needles=0):
+    return synth.Shape(f"t-{B}-{Hq}-{Hkv}-{N}-{k}-{dist}", B=B, Hq=Hq, Hkv=Hkv, N=N, k=k, dist=dist,
+                       seed_base=seed, outliers=4 if dist == "gauss" else 0, needles=needles)
+
+
+def _log(msg):
+    print(msg, flush=True)
+
+
+# ------------------------------------------------------------------ encode
+
+@pytest.mark.parametrize("dist", ["exact", "gauss"])
+def test_encode_queries_and_bulk_cache(hata_gpu, dist):
+    s = _shape(2, 8, 2, 700, 32, dist=dist, seed=7100)
+    inp = synth.make_inputs(s)
+    d = Dev(inp)
+    _log(f"encode {s.name}")
+    qc = codes_np(gpu_query_codes(hata_gpu, d))
+    cc = codes_np(gpu_build_cache(hata_gpu, d))
+    G = s.G
+    flips = 0
+    for b in range(s.B):
+        for h in range(s.Hkv):
+            flips += check_codes(qc[b, h * G:(h + 1) * G], inp.q[b, h * G:(h + 1) * G], inp.W[h],
+                                 exact=dist == "exact")
+            flips += check_codes(cc[b, h], inp.K[b, h], inp.W[h], exact=dist == "exact")
+    _log(f"allowed flips: {flips}")
+
+
+def test_encode_append_writes_only_row_pos(hata_gpu):
+    s = _shape(3, 4, 1, 200, 16, seed=7200)
+    lens = np.array([200, 57, 1], np.int32)
+    inp = synth.make_inputs(s, seq_lens=lens)
+    d = Dev(inp)
+    sentinel = np.full((3, 1, 200, 2), 0x5A5A5A5A5A5A5A5A, np.uint64)
+    codes = codes_tensor(sentinel)
+    pos = torch.from_numpy(lens - 1).cuda()
+    hata_gpu.encode_append(d.K, d.W, codes, n_new=1, pos=pos)
+    got = codes_np(codes)
+    for b in range(3):
+        n = int(lens[b])
+        mask = np.ones(200, bool)
+        mask[n - 1] = False
+        assert (got[b, 0, mask] == sentinel[b, 0, mask]).all()
+        check_codes(got[b, 0, n - 1:n], inp.K[b, 0, n - 1:n], inp.W[0], exact=False)
+
+
+def test_encode_exact_identity_bit_order(hata_gpu):
+    """W_H = I: bit c is the sign of input channel c (fixes the packing order)."""
+    s = _shape(1, 4, 1, 64, 8, seed=7300)
+    inp = synth.make_inputs(s)
+    inp.W = np.eye(128, dtype=np.float32)[None]
+    d = Dev(inp)
+    cc = codes_np(gpu_build_cache(hata_gpu, d))
+    xf = synth.bf16_to_f32(inp.K[0, 0])
+    for i in range(64):
+        bits = [(int(cc[0, 0, i, c // 64]) >> (c % 64)) & 1 for c in range(128)]
+        assert bits == [int(v >= 0) for v in xf[i]]
+
+
+# ------------------------------------------------------------------ Hamming + top-k
+
+@pytest.mark.parametrize("G", [1, 2, 4, 8])
+def test_hamming_scores_exact(hata_gpu, G):
+    Hkv = 2
+    s = _shape(2, G * Hkv, Hkv, 3000, 64, seed=7400 + G)
+    lens = np.array([3000, 1234], np.int32)
+    inp = synth.make_inputs(s, seq_lens=lens)
+    d = Dev(inp)
+    qc = gpu_query_codes(hata_gpu, d)
+    cc = gpu_build_cache(hata_gpu, d)
+    sc = torch.full((2, Hkv, 3000), -1, dtype=torch.int16, device="cuda")
+    hata_gpu.hamming_scores(qc, cc, d.seq, d.max_len, sc)
+    got = scores_np(sc)
+    qn, cn = codes_np(qc), codes_np(cc)
+    for b in range(2):
+        n = int(lens[b])
+        for h in range(Hkv):
+            ref = oracle.hamming_gqa(qn[b, h * G:(h + 1) * G], cn[b, h, :n])
+            np.testing.assert_array_equal(got[b, h, :n].astype(np.int32), ref)
+            assert (got[b, h, n:] == 0xFFFF).all()   # rows past n untouched
+
+
+@pytest.mark.parametrize("case", ["random", "ties", "all_equal", "k_ge_n", "n1", "max_score"])
+def test_topk_exact(hata_gpu, case):
+    rng = np.random.default_rng(hash(case) % 1000)
+    B, Hkv, cap = 2, 3, 5000
+    k = 512
+    lens = np.array([5000, 3333], np.int32)
+    max_score = 512
+    if case == "random":
+        S = rng.integers(200, 320, size=(B, Hkv, cap))
+    elif case == "ties":
+        S = rng.integers(0, 4, size=(B, Hkv, cap))
+    elif case == "all_equal":
+        S = np.full((B, Hkv, cap), 77)
+    elif case == "k_ge_n":
+        k = 4096
+        lens = np.array([300, 4096], np.int32)
+        S = rng.integers(0, 513, size=(B, Hkv, cap))
+    elif case == "n1":
+        lens = np.array([1, 2], np.int32)
+        S = rng.integers(0, 513, size=(B, Hkv, cap))
+    else:
+        max_score = 1024
+        S = rng.choice([0, 1024, 1023], size=(B, Hkv, cap))
+    sc = torch.from_numpy(S.astype(np.uint16).view(np.int16)).cuda()
+    idx = torch.full((B, Hkv, k), -7, dtype=torch.int32, device="cuda")
+    seq = torch.from_numpy(lens).cuda()
+    hata_gpu.topk(sc, seq, int(lens.max()), k, max_score, idx)
+    got = idx.cpu().numpy()
+    for b in range(B):
+        for h in range(Hkv):
+            ref = oracle.topk(S[b, h, :lens[b]].astype(np.int32), k)
+            np.testing.assert_array_equal(got[b, h], ref)
+
+
+# ------------------------------------------------------------------ attention
+
+@pytest.mark.parametrize("G", [1, 4, 8])
+def test_sparse_decode_matches_oracle(hata_gpu, G):
+    Hkv = 2
+    s = _shape(2, G * Hkv, Hkv, 2000, 100, seed=7500 + G)
+    inp = synth.make_inputs(s)
+    d = Dev(inp)
+    rng = np.random.default_rng(G)
+    idx = np.full((2, Hkv, 100), -1, np.int32)
+    for b in range(2):
+        for h in range(Hkv):
+            m = [100, 37, 1, 0][(b * Hkv + h) % 4]
+            idx[b, h, :m] = np.sort(rng.choice(2000, m, replace=False))
+    it = torch.from_numpy(idx).cuda()
+    out = torch.full((2, G * Hkv, 128), np.nan, dtype=torch.float32, device="cuda")
+    ws = hata_gpu.alloc_workspace(hata_gpu.OP_SPARSE_DECODE, 2, G * Hkv, Hkv, 100, 100)
+    hata_gpu.sparse_decode(d.q, d.K, d.V, it, inp.scale, out, ws)
+    got = out.cpu().numpy()
+    for b in range(2):
+        for h in range(Hkv):
+            ref = oracle.attention(inp.q[b, h * G:(h + 1) * G], inp.K[b, h], inp.V[b, h], idx[b, h], inp.scale)
+            if (idx[b, h] < 0).all():
+                ref = np.zeros_like(ref)
+            assert_close(got[b, h * G:(h + 1) * G], ref)
+
+
+@pytest.mark.parametrize("G,N", [(4, 5000), (1, 777), (8, 300)])
+def test_dense_decode_matches_oracle(hata_gpu, G, N):
+    Hkv = 2
+    s = _shape(2, G * Hkv, Hkv, N, 8, seed=7600 + G)
+    lens = np.array([N, max(1, N // 3)], np.int32)
+    inp = synth.make_inputs(s, seq_lens=lens)
+    d = Dev(inp)
+    out = torch.full((2, G * Hkv, 128), np.nan, dtype=torch.float32, device="cuda")
+    ws = hata_gpu.alloc_workspace(hata_gpu.OP_DENSE_DECODE, 2, G * Hkv, Hkv, d.max_len, 1)
+    hata_gpu.dense_decode(d.q, d.K, d.V, d.seq, d.max_len, inp.scale, out, ws)
+    ref = oracle.dense_attention(inp.q, inp.K, inp.V, inp.seq_lens, inp.scale)
+    assert_close(out.cpu().numpy(), ref)
+
+
+# ------------------------------------------------------------------ fused step
+
+STEP_CASES = [
+    # B, Hq, Hkv, N, k, dist, lens
+    (1, 4, 1, 4096, 256, "exact", None),          # exact recipe, many ties, Wg > 1
+    (1, 32, 8, 8192, 512, "gauss", None),         # GQA-4, 8 units (XCD map)
+    (3, 8, 2, 3000, 64, "gauss", [3000, 1500, 1]),  # ragged, n = 1
+    (2, 8, 8, 700, 512, "gauss", [700, 300]),     # G = 1, k > n
+    (1, 16, 2, 20000, 100, "gauss", None),        # G = 8
+    (2, 4, 2, 1000, 5, "exact", [1000, 999]),     # G = 2, tiny k
+    (8, 32, 32, 2048, 128, "gauss", None),        # 256 units, one workgroup each
+]
+
+
+@pytest.mark.parametrize("case", STEP_CASES, ids=lambda c: f"B{c[0]}-Hq{c[1]}-Hkv{c[2]}-N{c[3]}-k{c[4]}-{c[5]}")
+def test_decode_step_matches_oracle(hata_gpu, case):
+    B, Hq, Hkv, N, k, dist, lens = case
+    s = _shape(B, Hq, Hkv, N, k, dist=dist, seed=7700 + N % 97, needles=8 if dist == "gauss" else 0)
+    lens = np.array(lens if lens else [N] * B, np.int32)
+    inp = synth.make_inputs(s, seq_lens=lens)
+    d = Dev(inp)
+    _log(f"step case {case}")
+    # cache rows [0, n-1) from the library's encode; row n-1 deliberately stale
+    codes = gpu_build_cache(hata_gpu, d)
+    for b in range(B):
+        codes[b, :, int(lens[b]) - 1] = 0x1234
+    ws = hata_gpu.alloc_workspace(hata_gpu.OP_DECODE_STEP, B, Hq, Hkv, d.max_len, k)
+    out = torch.full((B, Hq, 128), np.nan, dtype=torch.float32, device="cuda")
+    idx = torch.full((B, Hkv, k), -9, dtype=torch.int32, device="cuda")
+    hata_gpu.decode_step(d.q, d.K, d.V, d.W, codes, d.seq, d.max_len, k, inp.scale, out, ws, idx)
+    torch.cuda.synchronize()
+    assert hata_gpu.workspace_check(ws) == 0
+    cn = codes_np(codes)
+    # appended code: same as the staged encode, and the oracle's within the allowance
+    for b in range(B):
+        n = int(lens[b])
+        for h in range(Hkv):
+            check_codes(cn[b, h, n - 1:n], inp.K[b, h, n - 1:n], inp.W[h], exact=dist == "exact")
+    qc = codes_np(gpu_query_codes(hata_gpu, d))
+    _, ref_idx, ref_out = oracle_units(inp, qc, cn)
+    np.testing.assert_array_equal(idx.cpu().numpy(), ref_idx)
+    assert_close(out.cpu().numpy(), ref_out)
+
+
+def test_decode_step_equals_staged_path(hata_gpu):
+    B, Hq, Hkv, N, k = 2, 32, 8, 6000, 512
+    s = _shape(B, Hq, Hkv, N, k, seed=7800, needles=16)
+    inp = synth.make_inputs(s, seq_lens=np.array([6000, 4321], np.int32))
+    d = Dev(inp)
+    codes = gpu_build_cache(hata_gpu, d)
+    staged_codes = codes.clone()
+    ws = hata_gpu.alloc_workspace(hata_gpu.OP_DECODE_STEP, B, Hq, Hkv, d.max_len, k)
+    out = torch.zeros((B, Hq, 128), dtype=torch.float32, device="cuda")
+    idx = torch.zeros((B, Hkv, k), dtype=torch.int32, device="cuda")
+    hata_gpu.decode_step(d.q, d.K, d.V, d.W, codes, d.seq, d.max_len, k, inp.scale, out, ws, idx)
+    # staged: encode q, append k, Hamming, top-k, sparse attention
+    qc = gpu_query_codes(hata_gpu, d)
+    hata_gpu.encode_append(d.K, d.W, staged_codes, n_new=1, pos=(d.seq - 1).to(torch.int32))
+    sc = torch.zeros((B, Hkv, N), dtype=torch.int16, device="cuda")
+    hata_gpu.hamming_scores(qc, staged_codes, d.seq, d.max_len, sc)
+    sidx = torch.zeros((B, Hkv, k), dtype=torch.int32, device="cuda")
+    hata_gpu.topk(sc, d.seq, d.max_len, k, (Hq // Hkv) * 128, sidx)
+    sout = torch.zeros_like(out)
+    ws2 = hata_gpu.alloc_workspace(hata_gpu.OP_SPARSE_DECODE, B, Hq, Hkv, k, k)
+    hata_gpu.sparse_decode(d.q, d.K, d.V, sidx, inp.scale, sout, ws2)
+    torch.cuda.synchronize()
+    assert torch.equal(codes, staged_codes)
+    assert torch.equal(idx, sidx)
+    assert_close(out.cpu().numpy(), sout.cpu().numpy(), "fused vs staged")
+
+
+def test_decode_step_deterministic_and_workspace_reuse(hata_gpu):
+    """Bitwise-identical reruns; one workspace reused across shapes whose plans
+    use different numbers of workgroups per unit."""
+    B, Hq, Hkv, k = 1, 32, 8, 512
+    runs = []
+    ws = hata_gpu.alloc_workspace(hata_gpu.OP_DECODE_STEP, B, Hq, Hkv, 65536, k)
+    for N in (65536, 4096, 65536, 20000, 65536):
+        s = _shape(B, Hq, Hkv, N, k, seed=7900)
+        inp = synth.make_inputs(s)
+        d = Dev(inp)
+        need = hata_gpu.workspace_bytes(hata_gpu.OP_DECODE_STEP, B, Hq, Hkv, N, k)
+        assert need <= ws.numel()
+        codes = gpu_build_cache(hata_gpu, d)
+        out = torch.zeros((B, Hq, 128), dtype=torch.float32, device="cuda")
+        idx = torch.zeros((B, Hkv, k), dtype=torch.int32, device="cuda")
+        hata_gpu.decode_step(d.q, d.K, d.V, d.W, codes, d.seq, d.max_len, k, inp.scale, out, ws, idx)
+        torch.cuda.synchronize()
+        assert hata_gpu.workspace_check(ws) == 0
+        if N == 65536:
+            runs.append((out.cpu().numpy().copy(), idx.cpu().numpy().copy(), codes_np(codes).copy()))
+        else:
+            qc = codes_np(gpu_query_codes(hata_gpu, d))
+            _, ref_idx, ref_out = oracle_units(inp, qc, codes_np(codes))
+            np.testing.assert_array_equal(idx.cpu().numpy(), ref_idx)
+            assert_close(out.cpu().numpy(), ref_out)
+    for o, i, c in runs[1:]:
+        assert np.array_equal(o.view(np.uint32), runs[0][0].view(np.uint32))
+        assert np.array_equal(i, runs[0][1]) and np.array_equal(c, runs[0][2])
