@@ -1,0 +1,258 @@
+"""Benchmark of the fused HATA decode step on one MI355X.
+
+Workload: one decode step of a Llama-3.1-8B-shaped attention layer at 128K
+context -- batch 1, 32 query heads over 8 KV heads (GQA 4), head dim 128,
+N = 131072 cached tokens, 128-bit codes, budget k = 512 -- on seeded
+synthetic inputs (bf16 q/K/V ~ N(0,1) with 4 outlier key channels x8 per KV
+head, W_H ~ N(0, 1/128) per KV head).
+
+A step is one hata_decode_step call: encode the 32 new queries, encode and
+append the 8 new keys, Hamming + GQA sum over the 8 x 131072 cached codes,
+top-512 per KV head, gather + exact attention.  The caches of `--layers`
+distinct layers live in HBM and consecutive steps walk through them, as a
+model's layers would, so no step finds its working set in the 256 MB
+Infinity Cache.  The K timed steps are captured in one HIP graph and timed
+with HIP events on the stream they run on.
+
+Printed: one JSON line (steps/s, the roofline object of the fused kernel,
+the oracle's CPU baseline, the dense flash-decode baseline on the same
+caches and the prefill bulk encode).
+"""
+from __future__ import annotations
+
+import argparse
+import concurrent.futures as cf
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0  # MI355X HBM3E peak, GB/s
+
+
+def log(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def step_bytes(B: int, Hq: int, Hkv: int, N: int, k: int, d: int = 128, r: int = 128) -> int:
+    """Algorithmic HBM bytes of one step: per unit N*r/8 code bytes plus
+    2*k*d*2 gathered K/V bytes, plus q (bf16) and out (fp32)."""
+    units = B * Hkv
+    return units * (N * r // 8 + 2 * min(k, N) * d * 2) + B * Hq * d * 2 + B * Hq * d * 4
+
+
+def dense_bytes(B: int, Hq: int, Hkv: int, N: int, d: int = 128) -> int:
+    return B * Hkv * 2 * N * d * 2 + B * Hq * d * 2 + B * Hq * d * 4
+
+
+def bulk_bytes(B: int, Hkv: int, N: int, d: int = 128, r: int = 128) -> int:
+    return B * Hkv * N * (d * 2 + r // 8) + Hkv * d * r * 4
+
+
+def cpu_baseline(inp, budget_s: float) -> dict:
+    """Time the oracle's whole decode step on the host (OpenMP over units)."""
+    import oracle
+
+    oracle.build()
+    B, Hq, d = inp.q.shape
+    _, Hkv, cap, _ = inp.K.shape
+    threads = oracle.max_threads()
+    log(f"oracle: building the code cache on {threads} host threads (not timed)")
+    codes = np.zeros((B, Hkv, cap, 2), np.uint64)
+    jobs = [(b, h) for b in range(B) for h in range(Hkv)]
+
+    def enc(bh):
+        b, h = bh
+        n = int(inp.seq_lens[b])
+        codes[b, h, :n - 1] = oracle.encode(inp.K[b, h, :n - 1], inp.W[h])
+
+    with cf.ThreadPoolExecutor(max_workers=max(1, min(threads, len(jobs)))) as ex:
+        list(ex.map(enc, jobs))
+    times = []
+    t_start = time.perf_counter()
+    while True:
+        t0 = time.perf_counter()
+        oracle.decode_step(inp.q, inp.K, inp.V, inp.W, codes, inp.seq_lens, inp.k, inp.scale,
+                           nthreads=threads)
+        times.append(time.perf_counter() - t0)
+        if time.perf_counter() - t_start > budget_s or len(times) >= 50:
+            break
+    med = float(np.median(times))
+    return {"value": 1.0 / med, "unit": "steps/s", "cores": threads, "kind": "oracle",
+            "sample": (f"the whole step of this workload (all {B * Hkv} units, N={cap}, k={inp.k}); "
+                       f"median of {len(times)} runs, {med * 1e3:.1f} ms each; code cache prebuilt "
+                       f"by the oracle outside the timing")}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=4096)
+    ap.add_argument("--warmup", type=int, default=64)
+    ap.add_argument("--config", type=int, default=4, help="workload id in hash_top_sparse_amd.synth.CONFIGS")
+    ap.add_argument("--layers", type=int, default=0, help="distinct layer caches to rotate through (0 = auto)")
+    ap.add_argument("--dense-steps", type=int, default=256)
+    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle timing")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--no-graph", action="store_true", help="launch the timed steps eagerly")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (this build has no multi-GPU path); got --gpus {args.gpus}",
+              file=sys.stderr)
+        return 2
+
+    import torch
+
+    from hash_top_sparse_amd import binding, synth
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    binding.load()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    shape = synth.CONFIGS[args.config]
+    B, Hq, Hkv, N, k = shape.B, shape.Hq, shape.Hkv, shape.N, shape.k
+    per_step = step_bytes(B, Hq, Hkv, N, k)
+    L = args.layers or max(2, min(64, int(np.ceil(1.5e9 / per_step))))
+    log(f"workload {shape.name}: B={B} Hq={Hq} Hkv={Hkv} N={N} k={k}; {L} layer caches")
+
+    t0 = time.perf_counter()
+    inp = synth.make_inputs(shape)
+    log(f"inputs drawn in {time.perf_counter() - t0:.1f} s")
+    bf = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+    q0, K0, V0 = bf(inp.q), bf(inp.K), bf(inp.V)
+    W = torch.from_numpy(inp.W).to(dev)
+    seq = torch.from_numpy(inp.seq_lens).to(dev)
+    codes0 = torch.zeros((B, Hkv, N, 2), dtype=torch.int64, device=dev)
+
+    # ---- prefill bulk encode (timed on its own), builds layer 0's code cache
+    binding.encode_append(K0, W, codes0, n_new=N)
+    torch.cuda.synchronize()
+    layers = []
+    for l in range(L):
+        layers.append((K0.clone() if l else K0, V0.clone() if l else V0, codes0.clone() if l else codes0))
+    torch.cuda.synchronize()
+    nb = min(L, 16)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    scratch_codes = [torch.empty_like(codes0) for _ in range(2)]
+    for i in range(4):
+        binding.encode_append(layers[i % L][0], W, scratch_codes[i % 2], n_new=N)
+    ev0.record()
+    for i in range(nb):
+        binding.encode_append(layers[i][0], W, scratch_codes[i % 2], n_new=N)
+    ev1.record()
+    torch.cuda.synchronize()
+    bulk_ms = ev0.elapsed_time(ev1) / nb
+    bulk = {"ms": bulk_ms, "keys_per_s": B * Hkv * N / (bulk_ms * 1e-3),
+            "GBs": bulk_bytes(B, Hkv, N) / (bulk_ms * 1e-3) / 1e9,
+            "TFLOPs": 2.0 * B * Hkv * N * 128 * 128 / (bulk_ms * 1e-3) / 1e12}
+    del scratch_codes
+    log(f"bulk encode: {bulk_ms * 1e3:.1f} us per layer")
+
+    # ---- fused decode step
+    ws = binding.alloc_workspace(binding.OP_DECODE_STEP, B, Hq, Hkv, N, k, device=dev)
+    out = torch.zeros((B, Hq, 128), dtype=torch.float32, device=dev)
+    idx = torch.zeros((B, Hkv, k), dtype=torch.int32, device=dev)
+
+    def step(i):
+        Kl, Vl, cl = layers[i % L]
+        binding.decode_step(q0, Kl, Vl, W, cl, seq, N, k, inp.scale, out, ws, idx)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    K_steps = args.steps
+    if args.no_graph:
+        ev0.record()
+        for i in range(K_steps):
+            step(i)
+        ev1.record()
+        torch.cuda.synchronize()
+    else:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(K_steps):
+                step(i)
+        torch.cuda.synchronize()
+        g.replay()  # warm replay
+        torch.cuda.synchronize()
+        ev0.record()
+        g.replay()
+        ev1.record()
+        torch.cuda.synchronize()
+    ms_total = ev0.elapsed_time(ev1)
+    ms_step = ms_total / K_steps
+    err = binding.workspace_check(ws)
+    if err:
+        log(f"workspace error word {err}: a cross-workgroup wait timed out")
+        return 1
+    achieved = per_step / (ms_step * 1e-3) / 1e9
+    log(f"fused step: {ms_step * 1e3:.2f} us/step, {achieved:.0f} GB/s")
+
+    # ---- dense flash-decode baseline on the same caches
+    dense = None
+    if not args.no_dense:
+        dws = binding.alloc_workspace(binding.OP_DENSE_DECODE, B, Hq, Hkv, N, 1, device=dev)
+        dout = torch.zeros_like(out)
+        nd = max(1, args.dense_steps)
+
+        def dstep(i):
+            Kl, Vl, _ = layers[i % L]
+            binding.dense_decode(q0, Kl, Vl, seq, N, inp.scale, dout, dws)
+
+        for i in range(8):
+            dstep(i)
+        torch.cuda.synchronize()
+        ev0.record()
+        for i in range(nd):
+            dstep(i)
+        ev1.record()
+        torch.cuda.synchronize()
+        d_ms = ev0.elapsed_time(ev1) / nd
+        dgb = dense_bytes(B, Hq, Hkv, N) / (d_ms * 1e-3) / 1e9
+        dense = {"ms_per_step": d_ms, "GBs": dgb, "frac_of_peak": dgb / PEAK_HBM_GBS,
+                 "speedup_of_hata": d_ms / ms_step}
+        log(f"dense: {d_ms * 1e3:.1f} us/step, {dgb:.0f} GB/s, hata speedup {d_ms / ms_step:.2f}x")
+
+    cpu = None
+    if not args.no_cpu:
+        cpu = cpu_baseline(inp, args.cpu_budget)
+        log(f"oracle: {cpu['value']:.2f} steps/s on {cpu['cores']} threads")
+
+    res = {
+        "metric": "decode steps/s and HBM GB/s (% of peak) for hata_decode_step at 128K ctx",
+        "value": 1000.0 / ms_step,
+        "unit": "steps/s",
+        "n_gpus": 1,
+        "steps": K_steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int32+fp32 (bf16 K/V, fp32 W_H)",
+        "data": "synthetic",
+        "config": {"workload": f"{shape.name}: one decode step of one attention layer",
+                   "batch": B, "q_heads": Hq, "kv_heads": Hkv, "head_dim": 128, "context": N,
+                   "code_bits": 128, "budget_k": k, "layer_caches_rotated": L,
+                   "timing": "graph of K steps, HIP events" if not args.no_graph else "eager, HIP events"},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": achieved / PEAK_HBM_GBS, "traffic": None,
+                     "kernel": "decode_step_kernel<4>", "bytes_per_launch": per_step},
+        "cpu_baseline": cpu,
+        "dense_baseline": dense,
+        "bulk_encode": bulk,
+    }
+    print(json.dumps(res), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,6 +1,6 @@
 // api.cpp -- the C ABI of libhata.so: argument validation, workspace layout
 // and kernel dispatch.  Declarations and the full contract are in hata.h.
-#include "../../include/hata.h"
+#include "hata.h"
 
 #include <hip/hip_runtime.h>
 

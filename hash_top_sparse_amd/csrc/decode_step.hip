@@ -36,6 +36,8 @@
 // own slots plus one monotonically increasing flag per workgroup; there is
 // no same-address read-modify-write (those serialise at the memory side).
 // Every wait is bounded; a timeout sets bit 0 of the workspace error word.
+#include <atomic>
+
 #include "hata_device.hpp"
 #include "hata_launch.hpp"
 
@@ -44,12 +46,37 @@ namespace hata {
 namespace {
 
 constexpr int kMaxWg = 64;         // workgroups per unit (one polling wave)
-constexpr int kWinWords = 64;      // 32-bit words per published window (128 uint16)
+constexpr int kWinBytes = 256;     // published window record per workgroup
+constexpr int kWinWords = kWinBytes / 4;
 constexpr int kWinHdr = 8;         // uint16 header entries
-constexpr int kWinCap = 2 * kWinWords - kWinHdr;  // histogram bins a window holds
+constexpr int kWinCap = kWinBytes / 2 - kWinHdr;  // histogram bins a window holds
 constexpr int kMaxChunk = 32768;   // tokens per workgroup (uint16 scores in LDS)
-constexpr int kPF = 16;            // code loads in flight per thread
 constexpr uint32_t kSpinLimit = 1u << 22;
+
+template <int G>
+struct Cfg {
+  static constexpr int NB = G * kR + 1;           // histogram bins
+  static constexpr int NBP = (NB + 63) / 64 * 64;
+  static constexpr int PF = (G >= 8) ? 8 : 16;    // code loads in flight per thread
+  static constexpr int HDRP = (2 * G + 3) / 4 * 4; // partial record header floats (M[G], L[G])
+  static constexpr int RECP = HDRP + G * kD;       // partial record floats
+  static constexpr int PROJ = 4 * (G + 1) * kR;    // projection reduction floats
+  static constexpr int RED = (kMergeFloats<G> > PROJ) ? kMergeFloats<G> : PROJ;
+  // LDS offsets in bytes
+  static constexpr int o_hist = 0;                               // NBP uint32
+  static constexpr int o_qf = o_hist + NBP * 4;                  // (G+1)*128 float
+  static constexpr int o_red = o_qf + (G + 1) * kD * 4;          // RED float
+  static constexpr int o_qcode = o_red + RED * 4;                // (G+1)*2 uint64
+  static constexpr int o_misc = o_qcode + (G + 1) * 16;          // 64 uint32
+  static constexpr int o_whdr = o_misc + 64 * 4;                 // 6 x kMaxWg int32
+  static constexpr int o_win = o_whdr + 6 * kMaxWg * 4;          // kMaxWg*kWinBytes (also combine staging)
+  static constexpr int o_sel = o_win + kMaxWg * kWinBytes;       // k int32
+  static size_t lds_bytes(int k, int chunk) {
+    size_t s = (size_t)o_sel + (size_t)(k + 1) * 4;
+    s = (s + 15) / 16 * 16;
+    return s + (size_t)chunk * 2;
+  }
+};
 
 struct StepArgs {
   const uint16_t* q;
@@ -68,31 +95,8 @@ struct StepArgs {
   uint32_t* flags;  // [U][kMaxWg]
   uint32_t* win;    // [U][kMaxWg][kWinWords]
   uint32_t* full;   // [U][kMaxWg][full_words]  (only for overflowing windows)
-  float* part;      // [U][kMaxWg][G][kRec]
+  float* part;      // [U][kMaxWg][RECP]
   int full_words;
-};
-
-template <int G>
-struct Lds {
-  static constexpr int NB = G * kR + 1;           // histogram bins
-  static constexpr int NBP = (NB + 63) / 64 * 64;
-  static constexpr int RED = (kMergeFloats<G> > (G + 1) * kD) ? kMergeFloats<G> : (G + 1) * kD;
-  // offsets in bytes
-  static constexpr int o_hist = 0;                               // NBP uint32
-  static constexpr int o_qf = o_hist + NBP * 4;                  // (G+1)*128 float
-  static constexpr int o_red = o_qf + (G + 1) * kD * 4;          // RED float
-  static constexpr int o_qcode = o_red + RED * 4;                // (G+1)*2 uint64
-  static constexpr int o_misc = o_qcode + (G + 1) * 16;          // 64 uint32
-  static constexpr int o_wlt = o_misc + 64 * 4;                  // kMaxWg uint32
-  static constexpr int o_weq = o_wlt + kMaxWg * 4;               // kMaxWg uint32
-  static constexpr int o_win = o_weq + kMaxWg * 4;               // kMaxWg*kWinWords uint32
-  static constexpr int o_sel = o_win + kMaxWg * kWinWords * 4;   // k int32
-  static constexpr int fixed = o_sel;
-  static size_t bytes(int k, int chunk) {
-    size_t s = (size_t)fixed + (size_t)k * 4;
-    s = (s + 15) / 16 * 16;
-    return s + (size_t)chunk * 2;
-  }
 };
 
 __device__ __forceinline__ void map_block(const StepArgs& a, int* unit, int* w) {
@@ -112,10 +116,10 @@ __device__ __forceinline__ void map_block(const StepArgs& a, int* unit, int* w) 
 __device__ __forceinline__ void wait_unit(const StepArgs& a, int unit, uint32_t target) {
   const int lane = threadIdx.x & 63;
   if ((threadIdx.x >> 6) == 0) {
-    const uint32_t* f = a.flags + (int64_t)unit * kMaxWg;
+    const CohBuf fb(a.flags + (int64_t)unit * kMaxWg, kMaxWg * 4);
     uint32_t it = 0;
     while (true) {
-      const uint32_t v = (lane < a.Wg) ? ld_agent(f + lane) : target;
+      const uint32_t v = (lane < a.Wg) ? fb.ld4(lane * 4) : target;
       const bool ok = (int32_t)(v - target) >= 0;
       if (__all(ok)) break;
       if (++it > kSpinLimit) {
@@ -128,12 +132,13 @@ __device__ __forceinline__ void wait_unit(const StepArgs& a, int unit, uint32_t 
   __syncthreads();
 }
 
-// In-place inclusive scan of hist[0, nb) with 256 threads; returns nothing,
-// leaves cum in hist.  Also accumulates three counts into misc[0..2]:
-// #bins with cum == 0, #bins with cum < cnt, #bins with cum < k.
+// In-place inclusive scan of hist[0, NB) with 256 threads.  Also records the
+// first bin where the running count becomes > 0, >= cnt and >= k in misc[0],
+// misc[1], misc[2] (each written by the one thread that sees the transition;
+// the caller presets them to NB).  Ends with __syncthreads.
 template <int NB>
-__device__ __forceinline__ void cum_hist(uint32_t* hist, uint32_t* misc, uint32_t* tmp, uint32_t cnt,
-                                         uint32_t k) {
+__device__ __forceinline__ void cum_hist(uint32_t* hist, uint32_t* misc, uint32_t* tmp,
+                                         uint32_t cnt, uint32_t k) {
   constexpr int BPT = (NB + kNT - 1) / kNT;
   const int t = threadIdx.x;
   uint32_t v[BPT];
@@ -145,40 +150,37 @@ __device__ __forceinline__ void cum_hist(uint32_t* hist, uint32_t* misc, uint32_
     loc += v[j];
   }
   uint32_t tot;
-  uint32_t run = block_excl_scan_u32(loc, tmp, &tot);
-  uint32_t zero = 0, below_cnt = 0, below_k = 0;
+  uint32_t prev = block_excl_scan_u32(loc, tmp, &tot);
 #pragma unroll
   for (int j = 0; j < BPT; ++j) {
     const int s = t * BPT + j;
     if (s < NB) {
-      run += v[j];
+      const uint32_t run = prev + v[j];
       hist[s] = run;
-      zero += (run == 0);
-      below_cnt += (run < cnt);
-      below_k += (run < k);
+      if (prev == 0 && run > 0) misc[0] = s;
+      if (prev < cnt && run >= cnt) misc[1] = s;
+      if (prev < k && run >= k) misc[2] = s;
+      prev = run;
     }
   }
-  if (zero) atomicAdd(&misc[0], zero);
-  if (below_cnt) atomicAdd(&misc[1], below_cnt);
-  if (below_k) atomicAdd(&misc[2], below_k);
   __syncthreads();
 }
 
 template <int G>
 __global__ __launch_bounds__(kNT) void decode_step_kernel(const StepArgs a) {
-  using L = Lds<G>;
-  constexpr int NB = L::NB;
+  using C = Cfg<G>;
+  constexpr int NB = C::NB;
+  constexpr int PF = C::PF;
   extern __shared__ __align__(16) unsigned char smem[];
-  uint32_t* hist = reinterpret_cast<uint32_t*>(smem + L::o_hist);
-  float* qf = reinterpret_cast<float*>(smem + L::o_qf);
-  float* red = reinterpret_cast<float*>(smem + L::o_red);
-  uint64_t* qcode = reinterpret_cast<uint64_t*>(smem + L::o_qcode);
-  uint32_t* misc = reinterpret_cast<uint32_t*>(smem + L::o_misc);
-  uint32_t* wlt = reinterpret_cast<uint32_t*>(smem + L::o_wlt);
-  uint32_t* weq = reinterpret_cast<uint32_t*>(smem + L::o_weq);
-  uint32_t* winl = reinterpret_cast<uint32_t*>(smem + L::o_win);
-  int32_t* sel = reinterpret_cast<int32_t*>(smem + L::o_sel);
-  uint16_t* sc = reinterpret_cast<uint16_t*>(smem + ((L::o_sel + a.k * 4 + 15) / 16 * 16));
+  uint32_t* hist = reinterpret_cast<uint32_t*>(smem + C::o_hist);
+  float* qf = reinterpret_cast<float*>(smem + C::o_qf);
+  float* red = reinterpret_cast<float*>(smem + C::o_red);
+  uint64_t* qcode = reinterpret_cast<uint64_t*>(smem + C::o_qcode);
+  uint32_t* misc = reinterpret_cast<uint32_t*>(smem + C::o_misc);
+  int32_t* whdr = reinterpret_cast<int32_t*>(smem + C::o_whdr);  // [6][kMaxWg]
+  unsigned char* winb = smem + C::o_win;
+  int32_t* sel = reinterpret_cast<int32_t*>(smem + C::o_sel);
+  uint16_t* sc = reinterpret_cast<uint16_t*>(smem + ((C::o_sel + (a.k + 1) * 4 + 15) / 16 * 16));
 
   const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
   int unit, w;
@@ -204,65 +206,51 @@ __global__ __launch_bounds__(kNT) void decode_step_kernel(const StepArgs a) {
   const bool owns_new = (n - 1 >= lo) && (n - 1 < lo + cnt);
   const int new_li = n - 1 - lo;
 
-  uint32_t epoch = 0;
-  if (a.Wg > 1 && wv == 0) epoch = ld_agent(a.flags + (int64_t)unit * kMaxWg + w);
-
-  // ---- 1. first group of code-cache loads
-  const uint4* cbase = reinterpret_cast<const uint4*>(a.codes) + row0 + lo;
-  uint4 cbuf[kPF];
+  // ---- 1. loads: W_H and the new rows first, then the code-cache prefetch
+  WRegs wr;
+  load_w_regs(a.W + (int64_t)h * kD * kR, wr);
+  const int nrows = G + (owns_new ? 1 : 0);
+  uint32_t xrow[(G + 1 + 3) / 4];
 #pragma unroll
-  for (int j = 0; j < kPF; ++j) {
+  for (int i = 0; i < (G + 1 + 3) / 4; ++i) {
+    const int e = t + i * kNT;
+    const int r = e >> 6, c2 = e & 63;
+    xrow[i] = 0;
+    if (r < nrows) {
+      const uint32_t* src = (r < G)
+          ? reinterpret_cast<const uint32_t*>(a.q + ((int64_t)b * a.Hq + (int64_t)h * G + r) * kD)
+          : reinterpret_cast<const uint32_t*>(a.K + (row0 + n - 1) * kD);
+      xrow[i] = src[c2];
+    }
+  }
+  uint32_t epoch = 0;
+  if (a.Wg > 1 && wv == 0) {
+    const CohBuf fb(a.flags + (int64_t)unit * kMaxWg, kMaxWg * 4);
+    epoch = fb.ld4(w * 4);
+  }
+  const uint4* cbase = reinterpret_cast<const uint4*>(a.codes) + row0 + lo;
+  uint4 cbuf[PF];
+#pragma unroll
+  for (int j = 0; j < PF; ++j) {
     const int li = j * kNT + t;
     cbuf[j] = make_uint4(0, 0, 0, 0);
     if (li < cnt) cbuf[j] = load_stream16(cbase + li);
   }
 
-  // ---- 2. encode q rows (+ new key row)
-  const int col = (wv & 1) * 64 + lane, dh = wv >> 1;
-  const float* Wh = a.W + (int64_t)h * kD * kR;
-  float wr[64];
+  // ---- 2. encode the query rows (+ the new key row)
 #pragma unroll
-  for (int i = 0; i < 64; ++i) wr[i] = Wh[(dh * 64 + i) * kR + col];
-  const int nrows = G + (owns_new ? 1 : 0);
-  for (int e = t; e < nrows * 64; e += kNT) {
+  for (int i = 0; i < (G + 1 + 3) / 4; ++i) {
+    const int e = t + i * kNT;
     const int r = e >> 6, c2 = e & 63;
-    const uint32_t* src = (r < G)
-        ? reinterpret_cast<const uint32_t*>(a.q + ((int64_t)b * a.Hq + (int64_t)h * G + r) * kD)
-        : reinterpret_cast<const uint32_t*>(a.K + (row0 + n - 1) * kD);
-    const uint32_t two = src[c2];
-    qf[r * kD + 2 * c2] = bf16_lo(two);
-    qf[r * kD + 2 * c2 + 1] = bf16_hi(two);
-  }
-  for (int i = t; i < L::NBP; i += kNT) hist[i] = 0;
-  if (t < 64) misc[t] = 0;
-  __syncthreads();
-  float p[G + 1];
-#pragma unroll
-  for (int r = 0; r <= G; ++r) {
-    float s = 0.f;
-    if (r < nrows) {
-#pragma unroll
-      for (int i = 0; i < 64; ++i) s = fmaf(qf[r * kD + dh * 64 + i], wr[i], s);
-    }
-    p[r] = s;
-  }
-  if (dh == 1) {
-#pragma unroll
-    for (int r = 0; r <= G; ++r)
-      if (r < nrows) red[r * kD + col] = p[r];
-  }
-  __syncthreads();
-  if (dh == 0) {
-#pragma unroll
-    for (int r = 0; r <= G; ++r) {
-      if (r < nrows) {
-        const float s = p[r] + red[r * kD + col];
-        const uint64_t m = __ballot(s >= 0.0f);
-        if (lane == 0) qcode[r * 2 + (wv & 1)] = m;
-      }
+    if (r <= G) {
+      qf[r * kD + 2 * c2] = bf16_lo(xrow[i]);
+      qf[r * kD + 2 * c2 + 1] = bf16_hi(xrow[i]);
     }
   }
+  for (int i = t; i < C::NBP; i += kNT) hist[i] = 0;
+  if (t < 64) misc[t] = (t < 3) ? (uint32_t)NB : 0u;
   __syncthreads();
+  project_pack<G + 1>(wr, qf, red, qcode, nrows);
   uint4 newc = make_uint4(0, 0, 0, 0);
   if (owns_new) {
     const uint64_t k0 = qcode[G * 2], k1 = qcode[G * 2 + 1];
@@ -280,17 +268,17 @@ __global__ __launch_bounds__(kNT) void decode_step_kernel(const StepArgs a) {
   build_qmasks<G>(qw, qm);
 
   // ---- 3. score the owned tokens
-  for (int base = 0; base < cnt; base += kPF * kNT) {
-    uint4 nbuf[kPF];
-    const int nbase = base + kPF * kNT;
+  for (int base = 0; base < cnt; base += PF * kNT) {
+    uint4 nbuf[PF];
+    const int nbase = base + PF * kNT;
 #pragma unroll
-    for (int j = 0; j < kPF; ++j) {
+    for (int j = 0; j < PF; ++j) {
       const int li = nbase + j * kNT + t;
       nbuf[j] = make_uint4(0, 0, 0, 0);
       if (li < cnt) nbuf[j] = load_stream16(cbase + li);
     }
 #pragma unroll
-    for (int j = 0; j < kPF; ++j) {
+    for (int j = 0; j < PF; ++j) {
       const int li = base + j * kNT + t;
       if (li < cnt) {
         const uint4 c = (li == new_li) ? newc : cbuf[j];
@@ -300,17 +288,15 @@ __global__ __launch_bounds__(kNT) void decode_step_kernel(const StepArgs a) {
       }
     }
 #pragma unroll
-    for (int j = 0; j < kPF; ++j) cbuf[j] = nbuf[j];
+    for (int j = 0; j < PF; ++j) cbuf[j] = nbuf[j];
   }
   __syncthreads();
 
   // ---- 4. threshold
   cum_hist<NB>(hist, misc, misc + 8, (uint32_t)cnt, (uint32_t)k);
-  // local stats: lo_w = first nonempty bin, hi_w = last nonempty bin,
-  // tk = own k-th smallest score (if cnt >= k)
-  const int lo_w = (int)misc[0];
-  const int hi_w = (int)misc[1];
-  const int tk = (int)misc[2];
+  const int lo_w = (int)misc[0];   // first nonempty bin (NB if none)
+  const int hi_w = (int)misc[1];   // last nonempty bin
+  const int tk = (int)misc[2];     // own k-th smallest score (NB if cnt < k)
   int T;
   uint32_t lt_all, quota, sel_before = 0, take_self;
   if (a.Wg == 1) {
@@ -320,44 +306,45 @@ __global__ __launch_bounds__(kNT) void decode_step_kernel(const StepArgs a) {
     const uint32_t eq_self = hist[T] - lt_all;
     take_self = eq_self < quota ? eq_self : quota;
   } else {
-    // publish the window [lo_w, top] of this workgroup's histogram
+    const CohBuf wbuf(a.win + (int64_t)unit * kMaxWg * kWinWords, kMaxWg * kWinBytes);
+    // publish the window [wlo, top] of this workgroup's histogram
     const bool has_k = cnt >= k;
     const int top = (cnt == 0) ? -1 : (has_k ? tk : hi_w);
     const int wlo = (cnt == 0) ? 0 : lo_w;
     const int len = top - wlo + 1;
     const bool ovf = len > kWinCap;
-    uint32_t* mywin = a.win + ((int64_t)unit * kMaxWg + w) * kWinWords;
-    if (t < kWinWords) {
-      uint32_t word;
-      if (t < kWinHdr / 2) {
-        const uint32_t hv[kWinHdr] = {(uint32_t)wlo, (uint32_t)(top + 1), has_k ? 1u : 0u,
-                                      ovf ? 1u : 0u, (uint32_t)cnt & 0xFFFFu, (uint32_t)cnt >> 16,
-                                      0u, 0u};
-        word = hv[2 * t] | (hv[2 * t + 1] << 16);
+    if (t < kWinBytes / 16) {
+      uint32_t e16[8];
+      if (t == 0) {
+        e16[0] = (uint32_t)wlo; e16[1] = (uint32_t)(top + 1);
+        e16[2] = has_k ? 1u : 0u; e16[3] = ovf ? 1u : 0u;
+        e16[4] = (uint32_t)cnt & 0xFFFFu; e16[5] = (uint32_t)cnt >> 16;
+        e16[6] = 0; e16[7] = 0;
       } else {
-        uint32_t two[2];
 #pragma unroll
-        for (int e = 0; e < 2; ++e) {
-          const int j = 2 * t + e - kWinHdr;
-          const int s = wlo + j;
-          uint32_t c = 0;
-          if (j < len && j < kWinCap) c = hist[s] - (s > 0 ? hist[s - 1] : 0u);
-          two[e] = c;
+        for (int e = 0; e < 8; ++e) {
+          const int j = 8 * t + e - kWinHdr;
+          const int s2 = wlo + j;
+          // cumulative count (tokens with score <= s2); past the window's
+          // end the count at its last bin
+          e16[e] = (j < kWinCap && len > 0) ? hist[min(s2, top)] : 0u;
         }
-        word = two[0] | (two[1] << 16);
       }
-      st_agent(mywin + t, word);
+      u32x4 v;
+      v.x = e16[0] | (e16[1] << 16); v.y = e16[2] | (e16[3] << 16);
+      v.z = e16[4] | (e16[5] << 16); v.w = e16[6] | (e16[7] << 16);
+      wbuf.st16(w * kWinBytes + t * 16, v);
     }
     if (ovf) {
-      uint32_t* myfull = a.full + ((int64_t)unit * kMaxWg + w) * a.full_words;
+      const CohBuf fbuf(a.full + ((int64_t)unit * kMaxWg + w) * a.full_words, a.full_words * 4);
       for (int i = t; i < a.full_words; i += kNT) {
         uint32_t two[2];
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
-          const int s = 2 * i + e;
-          two[e] = (s < NB) ? hist[s] - (s > 0 ? hist[s - 1] : 0u) : 0u;
+          const int s2 = 2 * i + e;
+          two[e] = (s2 < NB) ? hist[s2] : (uint32_t)cnt;
         }
-        st_agent(myfull + i, two[0] | (two[1] << 16));
+        fbuf.st4(i * 4, two[0] | (two[1] << 16));
       }
     }
     wait_all_mem();
@@ -365,118 +352,119 @@ __global__ __launch_bounds__(kNT) void decode_step_kernel(const StepArgs a) {
     if (t == 0) st_agent(a.flags + (int64_t)unit * kMaxWg + w, epoch + 1);
     wait_unit(a, unit, epoch + 1);
 
-    // read every window of the unit
-    const uint32_t* uwin = a.win + (int64_t)unit * kMaxWg * kWinWords;
-    for (int i = t; i < a.Wg * kWinWords; i += kNT) winl[i] = ld_agent(uwin + i);
-    __syncthreads();
-    // bound on T: the smallest own-k-th score among workgroups that have one
-    if (t < 16) misc[t] = 0;
-    __syncthreads();
-    if (t < a.Wg) {
-      const uint32_t h0 = winl[t * kWinWords], h1 = winl[t * kWinWords + 1];
-      const bool whas = (h1 & 0xFFFFu) != 0;
-      const int wtop = (int)(h0 >> 16) - 1;
-      if (whas) atomicMax(&misc[4], (uint32_t)(NB - wtop));  // NB - (min top)
-    }
-    __syncthreads();
-    const int tmin = misc[4] ? NB - (int)misc[4] : NB - 1;
-    // global histogram over [0, tmin]
-    for (int i = t; i < L::NBP; i += kNT) hist[i] = 0;
-    __syncthreads();
-    for (int ww = 0; ww < a.Wg; ++ww) {
-      const uint32_t* wr16 = winl + ww * kWinWords;
-      const uint32_t h0 = wr16[0], h1 = wr16[1];
-      const int wlo2 = min((int)(h0 & 0xFFFF), NB);
-      const int wtop = min((int)(h0 >> 16) - 1, NB - 1);
-      const bool wovf = (h1 >> 16) & 1u;
-      int hi2 = min(wtop, tmin);
-      if (!wovf) {
-        hi2 = min(hi2, wlo2 + kWinCap - 1);
-        for (int s = wlo2 + t; s <= hi2; s += kNT) {
-          const int j = s - wlo2 + kWinHdr;
-          const uint32_t c = (wr16[j >> 1] >> ((j & 1) * 16)) & 0xFFFFu;
-          if (c) atomicAdd(&hist[s], c);
-        }
-      } else {
-        const uint32_t* wf = a.full + ((int64_t)unit * kMaxWg + ww) * a.full_words;
-        for (int s = wlo2 + t; s <= hi2; s += kNT) {
-          const uint32_t c = (ld_agent(wf + (s >> 1)) >> ((s & 1) * 16)) & 0xFFFFu;
-          if (c) atomicAdd(&hist[s], c);
-        }
+    // read every window of the unit: Wg*16 chunks of 16 bytes, all in flight
+    {
+      const int nchunks = a.Wg * (kWinBytes / 16);
+      u32x4 v[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int c = t + i * kNT;
+        if (c < nchunks) v[i] = wbuf.ld16(c * 16);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int c = t + i * kNT;
+        if (c < nchunks) *reinterpret_cast<u32x4*>(winb + c * 16) = v[i];
       }
     }
-    if (t < 16) misc[t] = 0;
     __syncthreads();
-    cum_hist<NB>(hist, misc, misc + 8, 0xFFFFFFFFu, (uint32_t)k);
-    // bins beyond tmin hold cum == C(tmin); T = #bins with C < k, capped at tmin
+    // The threshold and the per-writer counts are computed by wave 0 with
+    // lane = writer: C(s) = sum over lanes of the writer's cumulative count
+    // at s (a register-held header plus one LDS read), summed with DPP.
+    if (wv == 0) {
+      int lw = NB, tw = NB - 1, ln = 0, topc = 0;
+      bool hw = false, ow = false;
+      const uint16_t* ent = reinterpret_cast<const uint16_t*>(winb + lane * kWinBytes) + kWinHdr;
+      if (lane < a.Wg) {
+        const uint32_t* hdr = reinterpret_cast<const uint32_t*>(winb + lane * kWinBytes);
+        lw = min((int)(hdr[0] & 0xFFFFu), NB);
+        tw = min((int)(hdr[0] >> 16) - 1, NB - 1);
+        hw = (hdr[1] & 0xFFFFu) != 0;
+        ow = ((hdr[1] >> 16) & 1u) != 0;
+        ln = max(0, min(tw - lw + 1, kWinCap));
+        topc = ln > 0 ? ent[ln - 1] : 0;
+      }
+      // cumulative count of this lane's writer at bin s2
+      auto cumw = [&](int s2) -> uint32_t {
+        if (lane >= a.Wg || s2 < lw) return 0u;
+        if (ow) {
+          const CohBuf fbuf(a.full + ((int64_t)unit * kMaxWg + lane) * a.full_words, a.full_words * 4);
+          return (fbuf.ld4((s2 >> 1) * 4) >> ((s2 & 1) * 16)) & 0xFFFFu;
+        }
+        const int j = s2 - lw;
+        return j >= ln ? (uint32_t)topc : (uint32_t)ent[j];
+      };
+      // T cannot exceed any workgroup's own k-th smallest score
+      const int tmin = wave_min_i((lane < a.Wg && hw) ? tw : NB - 1);
+      const int glo = min(wave_min_i(lw), tmin);
+      // binary search: C(lo2) < k <= C(hi2)
+      int lo2 = glo - 1, hi2 = tmin;
+      if (wave_sum_u32(cumw(tmin)) >= (uint32_t)k) {
+        while (hi2 - lo2 > 1) {
+          const int mid = (lo2 + hi2) >> 1;
+          if (wave_sum_u32(cumw(mid)) >= (uint32_t)k) hi2 = mid; else lo2 = mid;
+        }
+      }
+      const int Tw = hi2;
+      const uint32_t l1 = Tw > 0 ? cumw(Tw - 1) : 0u;
+      const uint32_t e1 = cumw(Tw) - l1;
+      const uint32_t il = wave_incl_scan_u32(l1);
+      const uint32_t ie = wave_incl_scan_u32(e1);
+      if (lane == w) { misc[6] = il - l1; misc[7] = ie - e1; misc[3] = e1; }
+      if (lane == 63) { misc[5] = il; misc[2] = (uint32_t)Tw; }
+    }
+    __syncthreads();
     T = (int)misc[2];
-    if (T > tmin) T = tmin;
-    lt_all = T > 0 ? hist[T - 1] : 0u;
+    lt_all = misc[5];
     quota = (uint32_t)k - lt_all;
-    // per-workgroup counts below and at T
-    if (t < a.Wg) {
-      const uint32_t* wr16 = winl + t * kWinWords;
-      const uint32_t h0 = wr16[0], h1 = wr16[1];
-      const int wlo2 = min((int)(h0 & 0xFFFF), NB);
-      const int wtop = min((int)(h0 >> 16) - 1, NB - 1);
-      const bool wovf = (h1 >> 16) & 1u;
-      const uint32_t* wf = a.full + ((int64_t)unit * kMaxWg + t) * a.full_words;
-      uint32_t lt = 0, eq = 0;
-      const int last = wovf ? min(wtop, T) : min(min(wtop, T), wlo2 + kWinCap - 1);
-      for (int s = wlo2; s <= last; ++s) {
-        uint32_t c;
-        if (!wovf) {
-          const int j = s - wlo2 + kWinHdr;
-          c = (wr16[j >> 1] >> ((j & 1) * 16)) & 0xFFFFu;
-        } else {
-          c = (ld_agent(wf + (s >> 1)) >> ((s & 1) * 16)) & 0xFFFFu;
-        }
-        if (s < T) lt += c; else eq += c;
-      }
-      wlt[t] = lt;
-      weq[t] = eq;
-    }
-    __syncthreads();
-    uint32_t pre_lt = 0, pre_eq = 0;
-    for (int ww = 0; ww < w; ++ww) { pre_lt += wlt[ww]; pre_eq += weq[ww]; }
-    const uint32_t eq_self = weq[w];
+    const uint32_t pre_lt = misc[6], pre_eq = misc[7];
+    const uint32_t eq_self = misc[3];
     const uint32_t left = quota > pre_eq ? quota - pre_eq : 0u;
     take_self = eq_self < left ? eq_self : left;
     sel_before = pre_lt + (pre_eq < quota ? pre_eq : quota);
   }
 
-  // ---- 5. ordered compaction of the kept tokens
-  const int per = (cnt + kNT - 1) / kNT;
-  const int i_begin = min(cnt, t * per), i_end = min(cnt, i_begin + per);
+  // ---- 5. ordered compaction of the kept tokens (index order); each
+  // thread owns a contiguous run of 8*per8 scores, read 8 at a time
+  const int per8 = (cnt + 8 * kNT - 1) / (8 * kNT);
+  const int i_begin = min(cnt, t * per8 * 8), i_end = min(cnt, i_begin + per8 * 8);
+  const uint32_t Tu = (uint32_t)T;
   uint32_t lt = 0, eq = 0;
-  for (int i = i_begin; i < i_end; ++i) {
-    const int s = sc[i];
-    lt += (s < T);
-    eq += (s == T);
+  for (int i8 = i_begin; i8 < i_end; i8 += 8) {
+    const uint4 v = *reinterpret_cast<const uint4*>(sc + i8);
+    const uint32_t wds[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const uint32_t s2 = (wds[e >> 1] >> ((e & 1) * 16)) & 0xFFFFu;
+      const bool in = i8 + e < i_end;
+      lt += (in && s2 < Tu);
+      eq += (in && s2 == Tu);
+    }
   }
   uint32_t tot_lt, tot_eq;
   uint32_t lt_before = block_excl_scan_u32(lt, misc + 8, &tot_lt);
   uint32_t eq_before = block_excl_scan_u32(eq, misc + 12, &tot_eq);
-  int32_t* idx_unit = a.idx_out ? a.idx_out + (int64_t)unit * k : nullptr;
-  for (int i = i_begin; i < i_end; ++i) {
-    const int s = sc[i];
-    int pos = -1;
-    if (s < T) {
-      pos = (int)(lt_before + min(eq_before, take_self));
-      ++lt_before;
-    } else if (s == T) {
-      if (eq_before < take_self) pos = (int)(lt_before + eq_before);
-      ++eq_before;
-    }
-    // pos < m_self <= k and sel_before + m_self <= min(k, n) by construction;
-    // the bounds are re-checked so a broken invariant cannot write outside
-    if (pos >= 0 && pos < k) {
-      sel[pos] = lo + i;
-      if (idx_unit && sel_before + (uint32_t)pos < (uint32_t)k) idx_unit[sel_before + pos] = lo + i;
+  // Branch-free emission: a kept token's position among this workgroup's
+  // kept tokens is lt_before + min(eq_before, take_self) (strict and tied
+  // alike); tokens that are not kept write to the spare slot sel[k].
+  if (lt | eq) {
+    for (int i8 = i_begin; i8 < i_end; i8 += 8) {
+      const uint4 v = *reinterpret_cast<const uint4*>(sc + i8);
+      const uint32_t wds[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const uint32_t s2 = (wds[e >> 1] >> ((e & 1) * 16)) & 0xFFFFu;
+        const bool in = i8 + e < i_end;
+        const bool islt = in && s2 < Tu;
+        const bool iseq = in && s2 == Tu;
+        const bool keep = islt || (iseq && eq_before < take_self);
+        const uint32_t pos = lt_before + min(eq_before, take_self);
+        sel[keep ? min(pos, (uint32_t)k) : (uint32_t)k] = lo + i8 + e;
+        lt_before += islt;
+        eq_before += iseq;
+      }
     }
   }
-  if (idx_unit && w == 0)
-    for (int j = min(k, n) + t; j < k; j += kNT) idx_unit[j] = -1;
   const int m_self = min(k, (int)(tot_lt + min(tot_eq, take_self)));
   __syncthreads();
 
@@ -511,8 +499,19 @@ __global__ __launch_bounds__(kNT) void decode_step_kernel(const StepArgs a) {
   }
   merge_wg<G>(st, red);
 
+  // kept indices, written once the attention no longer needs the LDS list
+  // (coalesced, and no barrier waits on these stores)
+  auto write_idx = [&]() {
+    if (!a.idx_out) return;
+    int32_t* idx_unit = a.idx_out + (int64_t)unit * k;
+    for (int j = t; j < m_self; j += kNT)
+      if (sel_before + (uint32_t)j < (uint32_t)k) idx_unit[sel_before + j] = sel[j];
+    if (w == 0)
+      for (int j = min(k, n) + t; j < k; j += kNT) idx_unit[j] = -1;
+  };
   float* outp = a.out + ((int64_t)b * a.Hq + (int64_t)h * G) * kD;
   if (a.Wg == 1) {
+    write_idx();
     for (int e = t; e < G * kD; e += kNT) {
       const int g = e / kD, c = e % kD;
       const float* r = red + g * kRec;
@@ -521,27 +520,67 @@ __global__ __launch_bounds__(kNT) void decode_step_kernel(const StepArgs a) {
     return;
   }
 
-  // ---- 7. publish this workgroup's records, wait, merge a slice
-  float* mypart = a.part + ((int64_t)unit * kMaxWg + w) * (G * kRec);
-  for (int e = t; e < G * kRec; e += kNT) st_agent(mypart + e, red[e]);
+  // ---- 7. publish this workgroup's record, wait, merge a slice of the outputs
+  const CohBuf pbuf(a.part + (int64_t)unit * kMaxWg * C::RECP, kMaxWg * C::RECP * 4);
+  for (int c = t; c < C::RECP / 4; c += kNT) {
+    float f[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int i = 4 * c + e;
+      float v = 0.f;
+      if (i < C::HDRP) {
+        if (i < G) v = red[i * kRec];
+        else if (i < 2 * G) v = red[(i - G) * kRec + 1];
+      } else {
+        const int j = i - C::HDRP, g = j / kD, cc = j % kD;
+        v = red[g * kRec + 2 + cc];
+      }
+      f[e] = v;
+    }
+    u32x4 v4;
+    v4.x = __float_as_uint(f[0]); v4.y = __float_as_uint(f[1]);
+    v4.z = __float_as_uint(f[2]); v4.w = __float_as_uint(f[3]);
+    pbuf.st16((w * C::RECP + 4 * c) * 4, v4);
+  }
   wait_all_mem();
   __syncthreads();
   if (t == 0) st_agent(a.flags + (int64_t)unit * kMaxWg + w, epoch + 2);
   wait_unit(a, unit, epoch + 2);
-  const int per_wg = (G * kD + a.Wg - 1) / a.Wg;
-  const int e0 = w * per_wg, e1 = min(G * kD, e0 + per_wg);
-  const float* upart = a.part + (int64_t)unit * kMaxWg * (G * kRec);
+
+  // slice [e0, e1) of the G*128 outputs, a multiple of 4 wide
+  const int per_wg = ((G * kD + a.Wg - 1) / a.Wg + 3) / 4 * 4;
+  const int e0 = min(G * kD, w * per_wg), e1 = min(G * kD, e0 + per_wg);
+  const int hch = C::HDRP / 4, sch = (e1 - e0) / 4, nch = hch + sch;
+  {
+    u32x4 v[3];
+#pragma unroll
+    for (int i = 0; i < 3; ++i) {
+      const int f = t + i * kNT;
+      if (f < a.Wg * nch) {
+        const int ww = f / nch, c = f - ww * nch;
+        const int off = (c < hch) ? 4 * c : C::HDRP + e0 + 4 * (c - hch);
+        v[i] = pbuf.ld16((ww * C::RECP + off) * 4);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 3; ++i) {
+      const int f = t + i * kNT;
+      if (f < a.Wg * nch) *reinterpret_cast<u32x4*>(winb + f * 16) = v[i];
+    }
+  }
+  __syncthreads();
+  const float* stage = reinterpret_cast<const float*>(winb);
   for (int e = e0 + t; e < e1; e += kNT) {
-    const int g = e / kD, c = e % kD;
+    const int g = e / kD;
     float M = -INFINITY;
-    for (int ww = 0; ww < a.Wg; ++ww) M = fmaxf(M, ld_agent(upart + ww * (G * kRec) + g * kRec));
+    for (int ww = 0; ww < a.Wg; ++ww) M = fmaxf(M, stage[ww * nch * 4 + g]);
     float Ls = 0.f, A = 0.f;
     if (M != -INFINITY) {
       for (int ww = 0; ww < a.Wg; ++ww) {
-        const float* r = upart + ww * (G * kRec) + g * kRec;
-        const float f = __expf(ld_agent(r) - M);
-        Ls = fmaf(ld_agent(r + 1), f, Ls);
-        A = fmaf(ld_agent(r + 2 + c), f, A);
+        const float* r = stage + ww * nch * 4;
+        const float f = __expf(r[g] - M);
+        Ls = fmaf(r[G + g], f, Ls);
+        A = fmaf(r[C::HDRP + (e - e0)], f, A);
       }
     }
     outp[e] = (Ls > 0.f) ? A / Ls : 0.f;
@@ -550,6 +589,7 @@ __global__ __launch_bounds__(kNT) void decode_step_kernel(const StepArgs a) {
   // use a different number of workgroups per unit)
   if (w == 0 && t >= a.Wg && t < kMaxWg)
     st_agent(a.flags + (int64_t)unit * kMaxWg + t, epoch + 2);
+  write_idx();
 }
 
 }  // namespace
@@ -587,18 +627,19 @@ StepPlan plan_decode_step(int B, int Hq, int Hkv, int64_t max_len, int k, int nu
   size_t off = 0;
   p.off_err = off;   off = align(off + 256);
   if (p.fused) {
+    size_t recp;
     switch (G) {
-      case 1: p.lds_bytes = Lds<1>::bytes(k, p.chunk); break;
-      case 2: p.lds_bytes = Lds<2>::bytes(k, p.chunk); break;
-      case 4: p.lds_bytes = Lds<4>::bytes(k, p.chunk); break;
-      default: p.lds_bytes = Lds<8>::bytes(k, p.chunk); break;
+      case 1: p.lds_bytes = Cfg<1>::lds_bytes(k, p.chunk); recp = Cfg<1>::RECP; break;
+      case 2: p.lds_bytes = Cfg<2>::lds_bytes(k, p.chunk); recp = Cfg<2>::RECP; break;
+      case 4: p.lds_bytes = Cfg<4>::lds_bytes(k, p.chunk); recp = Cfg<4>::RECP; break;
+      default: p.lds_bytes = Cfg<8>::lds_bytes(k, p.chunk); recp = Cfg<8>::RECP; break;
     }
     const size_t slots = (size_t)U * kMaxWg;
     p.off_flags = off; off = align(off + slots * 4);
     if (Wg > 1) {
       p.off_win = off;  off = align(off + slots * kWinWords * 4);
       p.off_full = off; off = align(off + slots * (size_t)p.full_words * 4);
-      p.off_part = off; off = align(off + slots * (size_t)G * kRec * 4);
+      p.off_part = off; off = align(off + slots * recp * 4);
     }
   } else {
     // staged steps inside hata_decode_step
@@ -613,12 +654,13 @@ StepPlan plan_decode_step(int B, int Hq, int Hkv, int64_t max_len, int k, int nu
 template <int G>
 static hipError_t launch_step_g(const StepPlan& p, const StepArgs& a, hipStream_t s) {
   const size_t lds = p.lds_bytes;
-  static bool configured = false;  // raise the dynamic-LDS limit once per instantiation
-  if (!configured) {
+  // raise the kernel's dynamic-LDS limit when a plan needs more than 64 KiB
+  static std::atomic<size_t> configured{64 * 1024};
+  if (lds > configured.load()) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&decode_step_kernel<G>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
-    configured = true;
+    configured.store(lds);
   }
   hipLaunchKernelGGL(decode_step_kernel<G>, dim3(p.U * p.Wg), dim3(kNT), lds, s, a);
   return hipGetLastError();

@@ -7,9 +7,9 @@
 // word c/64, bit c%64.
 //
 // GEMV form for a few rows per (sequence, KV head): a 256-thread workgroup
-// holds the KV head's W_H in registers -- lane = output column (64 columns
-// per wave), the two halves of the 128 input channels split across wave pairs
-// -- and packs each 64-column half of a code with one wave64 ballot.
+// holds the KV head's W_H in registers (16 float4 per thread) and packs each
+// 64-column half of a code with one wave64 ballot (project_pack); the fused
+// decode step uses the same routine, so both produce identical codes.
 #include "hata_device.hpp"
 #include "hata_launch.hpp"
 
@@ -23,23 +23,21 @@ __global__ __launch_bounds__(kNT) void encode_rows_kernel(
     const uint16_t* __restrict__ x, int64_t x_rows, int H, int Hkv, int n_new,
     const float* __restrict__ W, uint64_t* __restrict__ codes, int64_t cap,
     const int32_t* __restrict__ pos, int pos_off, int rows_per_block) {
-  __shared__ float xs[kRowsPerBatch][kD];
-  __shared__ float red[kRowsPerBatch][kR];
-  const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
+  __shared__ __align__(16) float xs[kRowsPerBatch * kD];
+  __shared__ __align__(16) float red[4 * kRowsPerBatch * kR];
+  __shared__ uint64_t cw[kRowsPerBatch * 2];
+  const int t = threadIdx.x;
   const int G = H / Hkv;
   const int bh = blockIdx.y;
   const int b = bh / Hkv, hk = bh - b * Hkv;
-  const int col = (wv & 1) * 64 + lane, dh = wv >> 1;
 
   const int total = G * n_new;
   const int r_begin = blockIdx.x * rows_per_block;
   const int r_end = min(total, r_begin + rows_per_block);
   if (r_begin >= r_end) return;
 
-  float wr[64];
-  const float* Wh = W + (int64_t)hk * kD * kR;
-#pragma unroll
-  for (int i = 0; i < 64; ++i) wr[i] = Wh[(dh * 64 + i) * kR + col];
+  WRegs wr;
+  load_w_regs(W + (int64_t)hk * kD * kR, wr);
 
   const int64_t p_b = (pos ? (int64_t)pos[b] : 0) + pos_off;
   const int64_t lim = x_rows < cap ? x_rows : cap;
@@ -60,40 +58,21 @@ __global__ __launch_bounds__(kNT) void encode_rows_kernel(
           hi = bf16_hi(two);
         }
       }
-      xs[rr][2 * c2] = lo;
-      xs[rr][2 * c2 + 1] = hi;
+      xs[rr * kD + 2 * c2] = lo;
+      xs[rr * kD + 2 * c2 + 1] = hi;
     }
     __syncthreads();
-    float p[kRowsPerBatch];
-#pragma unroll
-    for (int rr = 0; rr < kRowsPerBatch; ++rr) {
-      float s = 0.f;
-#pragma unroll
-      for (int i = 0; i < 64; ++i) s = fmaf(xs[rr][dh * 64 + i], wr[i], s);
-      p[rr] = s;
-    }
-    if (dh == 1) {
-#pragma unroll
-      for (int rr = 0; rr < kRowsPerBatch; ++rr) red[rr][col] = p[rr];
-    }
-    __syncthreads();
-    if (dh == 0) {
-#pragma unroll
-      for (int rr = 0; rr < kRowsPerBatch; ++rr) {
-        const float s = p[rr] + red[rr][col];
-        const uint64_t m = __ballot(s >= 0.0f);
-        const int r = r0 + rr;
-        if (lane == 0 && r < r_end) {
-          const int g = r / n_new, j = r - g * n_new;
-          const int64_t ridx = p_b + j;
-          if (ridx >= 0 && ridx < lim) {
-            const int64_t head = (int64_t)b * H + (int64_t)hk * G + g;
-            codes[(head * cap + ridx) * 2 + (wv & 1)] = m;
-          }
-        }
+    const int nr = min(kRowsPerBatch, r_end - r0);
+    project_pack<kRowsPerBatch>(wr, xs, red, cw, nr);
+    if (t < nr * 2) {
+      const int r = r0 + (t >> 1);
+      const int g = r / n_new, j = r - g * n_new;
+      const int64_t ridx = p_b + j;
+      if (ridx >= 0 && ridx < lim) {
+        const int64_t head = (int64_t)b * H + (int64_t)hk * G + g;
+        codes[(head * cap + ridx) * 2 + (t & 1)] = cw[t];
       }
     }
-    __syncthreads();
   }
 }
 

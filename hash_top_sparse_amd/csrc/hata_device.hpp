@@ -43,6 +43,28 @@ template <typename T>
 __device__ __forceinline__ T ld_agent(const T* p) {
   return __hip_atomic_load(const_cast<T*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+// Wide agent-coherent access to a workspace exchange area through a buffer
+// resource: 16-byte loads/stores with the device-scope bit, bounds-checked by
+// the hardware against `bytes` (out-of-range loads return 0, stores drop).
+constexpr int kSC1 = 16;  // cache-policy bit: device-scope coherence
+struct CohBuf {
+  __amdgpu_buffer_rsrc_t r;
+  __device__ __forceinline__ CohBuf(const void* base, uint32_t bytes)
+      : r(__builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000)) {}
+  __device__ __forceinline__ u32x4 ld16(uint32_t off) const {
+    return __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, kSC1);
+  }
+  __device__ __forceinline__ void st16(uint32_t off, u32x4 v) const {
+    __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)off, 0, kSC1);
+  }
+  __device__ __forceinline__ uint32_t ld4(uint32_t off) const {
+    return __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, kSC1);
+  }
+  __device__ __forceinline__ void st4(uint32_t off, uint32_t v) const {
+    __builtin_amdgcn_raw_buffer_store_b32(v, r, (int)off, 0, kSC1);
+  }
+};
+
 // Wait until every memory operation this wave issued has completed.
 __device__ __forceinline__ void wait_all_mem() {
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
@@ -65,13 +87,63 @@ __device__ __forceinline__ float sum16(float v) {
   return v;
 }
 
-__device__ __forceinline__ uint32_t wave_incl_scan_u32(uint32_t v, int lane) {
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    uint32_t o = __shfl_up(v, off, 64);
-    if (lane >= off) v += o;
-  }
+template <int CTRL, int ROW_MASK, bool BOUND_ZERO>
+__device__ __forceinline__ uint32_t dpp_u(uint32_t v) {
+  return __builtin_amdgcn_update_dpp(0u, v, CTRL, ROW_MASK, 0xF, BOUND_ZERO);
+}
+// Inclusive prefix sum over the 64 lanes of a wave: row_shr 1/2/4/8 within
+// each row of 16 lanes, then row_bcast15 and row_bcast31 carry the row totals.
+__device__ __forceinline__ uint32_t wave_incl_scan_u32(uint32_t v) {
+  v += dpp_u<0x111, 0xF, true>(v);
+  v += dpp_u<0x112, 0xF, true>(v);
+  v += dpp_u<0x114, 0xF, true>(v);
+  v += dpp_u<0x118, 0xF, true>(v);
+  v += dpp_u<0x142, 0xA, false>(v);
+  v += dpp_u<0x143, 0xC, false>(v);
   return v;
+}
+// Sum over the 64 lanes of a wave (every lane gets the total).
+__device__ __forceinline__ uint32_t wave_sum_u32(uint32_t v) {
+  return __builtin_amdgcn_readlane(wave_incl_scan_u32(v), 63);
+}
+// Values of lanes l and l^32 (resp. l^16), as (bit clear, bit set); both
+// lanes of a pair see the same two values, so pair results are identical.
+__device__ __forceinline__ float pair32_sum(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float pair16_sum(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float pair32_max(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair16_max(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ int pair32_min_i(int v) {
+  const auto r = __builtin_amdgcn_permlane32_swap((uint32_t)v, (uint32_t)v, false, false);
+  return min((int)r[0], (int)r[1]);
+}
+__device__ __forceinline__ int pair16_min_i(int v) {
+  const auto r = __builtin_amdgcn_permlane16_swap((uint32_t)v, (uint32_t)v, false, false);
+  return min((int)r[0], (int)r[1]);
+}
+template <int CTRL>
+__device__ __forceinline__ int dpp_i(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
+}
+// Minimum over the 64 lanes of a wave (every lane gets it).
+__device__ __forceinline__ int wave_min_i(int v) {
+  v = min(v, dpp_i<0xB1>(v));
+  v = min(v, dpp_i<0x4E>(v));
+  v = min(v, dpp_i<0x141>(v));
+  v = min(v, dpp_i<0x140>(v));
+  v = pair16_min_i(v);
+  return pair32_min_i(v);
 }
 
 // Exclusive scan over the 256 threads of a workgroup; `tmp` holds 4 words of
@@ -79,7 +151,8 @@ __device__ __forceinline__ uint32_t wave_incl_scan_u32(uint32_t v, int lane) {
 // __syncthreads, so every thread must call it.
 __device__ __forceinline__ uint32_t block_excl_scan_u32(uint32_t v, uint32_t* tmp, uint32_t* total) {
   const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
-  uint32_t inc = wave_incl_scan_u32(v, lane);
+  (void)lane;
+  uint32_t inc = wave_incl_scan_u32(v);
   if (lane == 63) tmp[wv] = inc;
   __syncthreads();
   uint32_t base = 0, all = 0;
@@ -92,6 +165,74 @@ __device__ __forceinline__ uint32_t block_excl_scan_u32(uint32_t v, uint32_t* tm
   __syncthreads();
   *total = all;
   return base + inc - v;
+}
+
+// ------------------------------------------------------- HashEncode projection
+// Projection of R staged rows by one KV head's W_H ([128][128] fp32,
+// row-major) with a 256-thread workgroup, then sign + bit-pack:
+//   thread t owns columns 4*(t&31) .. +3 and input channels 16*(t>>5) .. +15
+//   (16 float4 loads of W per thread); partial sums over its 16 channels are
+//   added pairwise across the two channel groups of a wave (lanes l, l^32),
+//   then over the 4 waves in fixed order through LDS; each 64-column half of
+//   a code is one wave64 ballot of (p >= 0).
+// The summation order is fixed, so every kernel that uses this function
+// produces identical codes.
+struct WRegs {
+  float4 w[16];
+};
+__device__ __forceinline__ void load_w_regs(const float* __restrict__ Wh, WRegs& wr) {
+  const int t = threadIdx.x, cg = t & 31, rg = t >> 5;
+  const float4* src = reinterpret_cast<const float4*>(Wh + (rg * 16) * kR) + cg;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) wr.w[i] = src[i * (kR / 4)];
+}
+// xs: LDS rows [R][128] fp32; red: LDS [4][R][128] fp32; out: LDS [R][2] uint64.
+// Rows >= nrows are skipped.  Ends with __syncthreads.
+template <int R>
+__device__ __forceinline__ void project_pack(const WRegs& wr, const float* xs, float* red,
+                                             uint64_t* out, int nrows) {
+  const int t = threadIdx.x, lane = t & 63, wv = t >> 6, cg = t & 31, rg = t >> 5;
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    if (r >= nrows) break;
+    const float4* xr = reinterpret_cast<const float4*>(xs + r * kD + rg * 16);
+    float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
+#pragma unroll
+    for (int i4 = 0; i4 < 4; ++i4) {
+      const float4 x = xr[i4];
+      const float xv[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float4 w = wr.w[i4 * 4 + j];
+        a0 = fmaf(xv[j], w.x, a0);
+        a1 = fmaf(xv[j], w.y, a1);
+        a2 = fmaf(xv[j], w.z, a2);
+        a3 = fmaf(xv[j], w.w, a3);
+      }
+    }
+    a0 = pair32_sum(a0);
+    a1 = pair32_sum(a1);
+    a2 = pair32_sum(a2);
+    a3 = pair32_sum(a3);
+    if (lane < 32) {
+      float* dst = red + (wv * R + r) * kR + cg * 4;
+      *reinterpret_cast<float4*>(dst) = make_float4(a0, a1, a2, a3);
+    }
+  }
+  __syncthreads();
+  // wave wv: column half (wv & 1), rows r with r % 2 == wv >> 1
+  const int col = (wv & 1) * 64 + lane;
+#pragma unroll
+  for (int r = (wv >> 1); r < R; r += 2) {
+    if (r >= nrows) break;
+    float s = red[(0 * R + r) * kR + col];
+    s += red[(1 * R + r) * kR + col];
+    s += red[(2 * R + r) * kR + col];
+    s += red[(3 * R + r) * kR + col];
+    const uint64_t m = __ballot(s >= 0.0f);
+    if (lane == 0) out[r * 2 + (wv & 1)] = m;
+  }
+  __syncthreads();
 }
 
 // ------------------------------------------------------- Hamming with GQA sum
@@ -233,20 +374,12 @@ __device__ __forceinline__ void merge_wg(const SoftmaxState<G>& st, float* red) 
   const int t = threadIdx.x, lane = t & 63, wv = t >> 6, sub = lane & 15;
 #pragma unroll
   for (int g = 0; g < G; ++g) {
-    float M = st.m[g];
-    M = fmaxf(M, __shfl_xor(M, 16, 64));
-    M = fmaxf(M, __shfl_xor(M, 32, 64));
+    const float M = pair32_max(pair16_max(st.m[g]));
     const float f = (M == -INFINITY) ? 0.f : __expf(st.m[g] - M);
-    float L = st.l[g] * f;
-    L += __shfl_xor(L, 16, 64);
-    L += __shfl_xor(L, 32, 64);
+    const float L = pair32_sum(pair16_sum(st.l[g] * f));
     float A[8];
 #pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      A[c] = st.acc[g][c] * f;
-      A[c] += __shfl_xor(A[c], 16, 64);
-      A[c] += __shfl_xor(A[c], 32, 64);
-    }
+    for (int c = 0; c < 8; ++c) A[c] = pair32_sum(pair16_sum(st.acc[g][c] * f));
     if (lane < 16) {
       float* r = red + (wv * G + g) * kRec;
       if (sub == 0) { r[0] = M; r[1] = L; }

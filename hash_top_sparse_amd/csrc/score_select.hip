@@ -66,7 +66,8 @@ constexpr int kMaxBins = 8 * kR + 1;
 
 __device__ __forceinline__ uint32_t block_excl_scan_1024(uint32_t v, uint32_t* tmp, uint32_t* total) {
   const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
-  const uint32_t inc = wave_incl_scan_u32(v, lane);
+  (void)lane;
+  const uint32_t inc = wave_incl_scan_u32(v);
   if (lane == 63) tmp[wv] = inc;
   __syncthreads();
   uint32_t base = 0, all = 0;
