@@ -90,6 +90,120 @@ def cpu_baseline(inp, budget_s: float) -> dict:
                        f"by the oracle outside the timing")}
 
 
+def measure(cfg_id: int, steps: int, warmup: int, dense_steps: int, layers: int, use_graph: bool,
+            with_bulk: bool):
+    """Time the fused step (and the dense baseline) on one workload; returns
+    (result dict, inputs)."""
+    import torch
+
+    from hash_top_sparse_amd import binding, synth
+
+    dev = torch.device("cuda:0")
+    shape = synth.CONFIGS[cfg_id]
+    B, Hq, Hkv, N, k = shape.B, shape.Hq, shape.Hkv, shape.N, shape.k
+    per_step = step_bytes(B, Hq, Hkv, N, k)
+    L = layers or max(2, min(64, int(np.ceil(1.5e9 / per_step))))
+    log(f"workload {shape.name}: B={B} Hq={Hq} Hkv={Hkv} N={N} k={k}; {L} layer caches")
+    t0 = time.perf_counter()
+    inp = synth.make_inputs(shape)
+    log(f"inputs drawn in {time.perf_counter() - t0:.1f} s")
+    bf = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+    q0, K0, V0 = bf(inp.q), bf(inp.K), bf(inp.V)
+    W = torch.from_numpy(inp.W).to(dev)
+    seq = torch.from_numpy(inp.seq_lens).to(dev)
+    codes0 = torch.zeros((B, Hkv, N, 2), dtype=torch.int64, device=dev)
+    binding.encode_append(K0, W, codes0, n_new=N)
+    torch.cuda.synchronize()
+    layer_bufs = []
+    for l in range(L):
+        layer_bufs.append((K0.clone() if l else K0, V0.clone() if l else V0,
+                           codes0.clone() if l else codes0))
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    bulk = None
+    if with_bulk:
+        nb = min(L, 16)
+        scratch = [torch.empty_like(codes0) for _ in range(2)]
+        for i in range(4):
+            binding.encode_append(layer_bufs[i % L][0], W, scratch[i % 2], n_new=N)
+        ev0.record()
+        for i in range(nb):
+            binding.encode_append(layer_bufs[i][0], W, scratch[i % 2], n_new=N)
+        ev1.record()
+        torch.cuda.synchronize()
+        bulk_ms = ev0.elapsed_time(ev1) / nb
+        bulk = {"ms": bulk_ms, "keys_per_s": B * Hkv * N / (bulk_ms * 1e-3),
+                "GBs": bulk_bytes(B, Hkv, N) / (bulk_ms * 1e-3) / 1e9,
+                "TFLOPs": 2.0 * B * Hkv * N * 128 * 128 / (bulk_ms * 1e-3) / 1e12}
+        del scratch
+        log(f"bulk encode: {bulk_ms * 1e3:.1f} us per layer")
+
+    ws = binding.alloc_workspace(binding.OP_DECODE_STEP, B, Hq, Hkv, N, k, device=dev)
+    out = torch.zeros((B, Hq, 128), dtype=torch.float32, device=dev)
+
+    def step(i):
+        Kl, Vl, cl = layer_bufs[i % L]
+        binding.decode_step(q0, Kl, Vl, W, cl, seq, N, k, inp.scale, out, ws)
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    if not use_graph:
+        ev0.record()
+        for i in range(steps):
+            step(i)
+        ev1.record()
+        torch.cuda.synchronize()
+    else:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(steps):
+                step(i)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        ev0.record()
+        g.replay()
+        ev1.record()
+        torch.cuda.synchronize()
+    ms_step = ev0.elapsed_time(ev1) / steps
+    err = binding.workspace_check(ws)
+    if err:
+        raise RuntimeError(f"workspace error word {err}: a cross-workgroup wait timed out")
+    achieved = per_step / (ms_step * 1e-3) / 1e9
+    log(f"fused step: {ms_step * 1e3:.2f} us/step, {achieved:.0f} GB/s ({achieved / PEAK_HBM_GBS:.1%})")
+
+    dense = None
+    if dense_steps > 0:
+        dws = binding.alloc_workspace(binding.OP_DENSE_DECODE, B, Hq, Hkv, N, 1, device=dev)
+        dout = torch.zeros_like(out)
+
+        def dstep(i):
+            Kl, Vl, _ = layer_bufs[i % L]
+            binding.dense_decode(q0, Kl, Vl, seq, N, inp.scale, dout, dws)
+
+        for i in range(4):
+            dstep(i)
+        torch.cuda.synchronize()
+        ev0.record()
+        for i in range(dense_steps):
+            dstep(i)
+        ev1.record()
+        torch.cuda.synchronize()
+        d_ms = ev0.elapsed_time(ev1) / dense_steps
+        dgb = dense_bytes(B, Hq, Hkv, N) / (d_ms * 1e-3) / 1e9
+        dense = {"ms_per_step": d_ms, "GBs": dgb, "frac_of_peak": dgb / PEAK_HBM_GBS,
+                 "speedup_of_hata": d_ms / ms_step}
+        log(f"dense: {d_ms * 1e3:.1f} us/step, {dgb:.0f} GB/s, hata speedup {d_ms / ms_step:.2f}x")
+    res = {"workload": shape.name, "ms_per_step": ms_step, "steps_per_s": 1000.0 / ms_step,
+           "GBs": achieved, "frac_of_peak": achieved / PEAK_HBM_GBS, "bytes_per_step": per_step,
+           "layers": L, "dense": dense, "bulk_encode": bulk}
+    del layer_bufs
+    torch.cuda.empty_cache()
+    return res, inp
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -102,6 +216,7 @@ def main() -> int:
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="launch the timed steps eagerly")
+    ap.add_argument("--sweep", action="store_true", help="also time the other workloads (2, 3, 5)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -111,127 +226,36 @@ def main() -> int:
 
     import torch
 
-    from hash_top_sparse_amd import binding, synth
+    from hash_top_sparse_amd import binding
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     binding.load()
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
-    shape = synth.CONFIGS[args.config]
-    B, Hq, Hkv, N, k = shape.B, shape.Hq, shape.Hkv, shape.N, shape.k
-    per_step = step_bytes(B, Hq, Hkv, N, k)
-    L = args.layers or max(2, min(64, int(np.ceil(1.5e9 / per_step))))
-    log(f"workload {shape.name}: B={B} Hq={Hq} Hkv={Hkv} N={N} k={k}; {L} layer caches")
-
-    t0 = time.perf_counter()
-    inp = synth.make_inputs(shape)
-    log(f"inputs drawn in {time.perf_counter() - t0:.1f} s")
-    bf = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
-    q0, K0, V0 = bf(inp.q), bf(inp.K), bf(inp.V)
-    W = torch.from_numpy(inp.W).to(dev)
-    seq = torch.from_numpy(inp.seq_lens).to(dev)
-    codes0 = torch.zeros((B, Hkv, N, 2), dtype=torch.int64, device=dev)
-
-    # ---- prefill bulk encode (timed on its own), builds layer 0's code cache
-    binding.encode_append(K0, W, codes0, n_new=N)
-    torch.cuda.synchronize()
-    layers = []
-    for l in range(L):
-        layers.append((K0.clone() if l else K0, V0.clone() if l else V0, codes0.clone() if l else codes0))
-    torch.cuda.synchronize()
-    nb = min(L, 16)
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    scratch_codes = [torch.empty_like(codes0) for _ in range(2)]
-    for i in range(4):
-        binding.encode_append(layers[i % L][0], W, scratch_codes[i % 2], n_new=N)
-    ev0.record()
-    for i in range(nb):
-        binding.encode_append(layers[i][0], W, scratch_codes[i % 2], n_new=N)
-    ev1.record()
-    torch.cuda.synchronize()
-    bulk_ms = ev0.elapsed_time(ev1) / nb
-    bulk = {"ms": bulk_ms, "keys_per_s": B * Hkv * N / (bulk_ms * 1e-3),
-            "GBs": bulk_bytes(B, Hkv, N) / (bulk_ms * 1e-3) / 1e9,
-            "TFLOPs": 2.0 * B * Hkv * N * 128 * 128 / (bulk_ms * 1e-3) / 1e12}
-    del scratch_codes
-    log(f"bulk encode: {bulk_ms * 1e3:.1f} us per layer")
-
-    # ---- fused decode step
-    ws = binding.alloc_workspace(binding.OP_DECODE_STEP, B, Hq, Hkv, N, k, device=dev)
-    out = torch.zeros((B, Hq, 128), dtype=torch.float32, device=dev)
-    idx = torch.zeros((B, Hkv, k), dtype=torch.int32, device=dev)
-
-    def step(i):
-        Kl, Vl, cl = layers[i % L]
-        binding.decode_step(q0, Kl, Vl, W, cl, seq, N, k, inp.scale, out, ws, idx)
-
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-    K_steps = args.steps
-    if args.no_graph:
-        ev0.record()
-        for i in range(K_steps):
-            step(i)
-        ev1.record()
-        torch.cuda.synchronize()
-    else:
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            for i in range(K_steps):
-                step(i)
-        torch.cuda.synchronize()
-        g.replay()  # warm replay
-        torch.cuda.synchronize()
-        ev0.record()
-        g.replay()
-        ev1.record()
-        torch.cuda.synchronize()
-    ms_total = ev0.elapsed_time(ev1)
-    ms_step = ms_total / K_steps
-    err = binding.workspace_check(ws)
-    if err:
-        log(f"workspace error word {err}: a cross-workgroup wait timed out")
-        return 1
-    achieved = per_step / (ms_step * 1e-3) / 1e9
-    log(f"fused step: {ms_step * 1e3:.2f} us/step, {achieved:.0f} GB/s")
-
-    # ---- dense flash-decode baseline on the same caches
-    dense = None
-    if not args.no_dense:
-        dws = binding.alloc_workspace(binding.OP_DENSE_DECODE, B, Hq, Hkv, N, 1, device=dev)
-        dout = torch.zeros_like(out)
-        nd = max(1, args.dense_steps)
-
-        def dstep(i):
-            Kl, Vl, _ = layers[i % L]
-            binding.dense_decode(q0, Kl, Vl, seq, N, inp.scale, dout, dws)
-
-        for i in range(8):
-            dstep(i)
-        torch.cuda.synchronize()
-        ev0.record()
-        for i in range(nd):
-            dstep(i)
-        ev1.record()
-        torch.cuda.synchronize()
-        d_ms = ev0.elapsed_time(ev1) / nd
-        dgb = dense_bytes(B, Hq, Hkv, N) / (d_ms * 1e-3) / 1e9
-        dense = {"ms_per_step": d_ms, "GBs": dgb, "frac_of_peak": dgb / PEAK_HBM_GBS,
-                 "speedup_of_hata": d_ms / ms_step}
-        log(f"dense: {d_ms * 1e3:.1f} us/step, {dgb:.0f} GB/s, hata speedup {d_ms / ms_step:.2f}x")
+    torch.cuda.set_device(0)
+    head, inp = measure(args.config, args.steps, args.warmup, 0 if args.no_dense else args.dense_steps,
+                        args.layers, not args.no_graph, with_bulk=True)
+    shape = inp.shape
+    sweep = None
+    if args.sweep:
+        sweep = {}
+        for c in (2, 3, 5, 1):
+            if c == args.config:
+                continue
+            r, _ = measure(c, max(256, args.steps // 8), 16, 0 if args.no_dense else 32, 0,
+                           not args.no_graph, with_bulk=False)
+            sweep[str(c)] = r
 
     cpu = None
     if not args.no_cpu:
         cpu = cpu_baseline(inp, args.cpu_budget)
         log(f"oracle: {cpu['value']:.2f} steps/s on {cpu['cores']} threads")
 
+    ms_step = head["ms_per_step"]
     res = {
         "metric": "decode steps/s and HBM GB/s (% of peak) for hata_decode_step at 128K ctx",
         "value": 1000.0 / ms_step,
         "unit": "steps/s",
         "n_gpus": 1,
-        "steps": K_steps,
+        "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": ms_step,
         "higher_is_better": True,
@@ -240,16 +264,19 @@ def main() -> int:
         "dtype": "int32+fp32 (bf16 K/V, fp32 W_H)",
         "data": "synthetic",
         "config": {"workload": f"{shape.name}: one decode step of one attention layer",
-                   "batch": B, "q_heads": Hq, "kv_heads": Hkv, "head_dim": 128, "context": N,
-                   "code_bits": 128, "budget_k": k, "layer_caches_rotated": L,
+                   "batch": shape.B, "q_heads": shape.Hq, "kv_heads": shape.Hkv, "head_dim": 128,
+                   "context": shape.N, "code_bits": 128, "budget_k": shape.k,
+                   "layer_caches_rotated": head["layers"],
                    "timing": "graph of K steps, HIP events" if not args.no_graph else "eager, HIP events"},
-        "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": achieved / PEAK_HBM_GBS, "traffic": None,
-                     "kernel": "decode_step_kernel<4>", "bytes_per_launch": per_step},
+        "roofline": {"bound": "hbm", "achieved": head["GBs"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": head["GBs"] / PEAK_HBM_GBS, "traffic": None,
+                     "kernel": f"decode_step_kernel<{shape.G}>", "bytes_per_launch": head["bytes_per_step"]},
         "cpu_baseline": cpu,
-        "dense_baseline": dense,
-        "bulk_encode": bulk,
+        "dense_baseline": head["dense"],
+        "bulk_encode": head["bulk_encode"],
     }
+    if sweep is not None:
+        res["sweep"] = sweep
     print(json.dumps(res), flush=True)
     return 0
 

@@ -96,27 +96,48 @@ __global__ __launch_bounds__(kNT) void attn_partial_kernel(
   for (int e = t; e < G * kRec; e += kNT) dst[e] = red[e];
 }
 
+// Log-sum-exp merge of a unit's split records.  One workgroup per (unit,
+// head, 16-channel slice); lane (s16, ch) = (t / 16, t % 16) walks splits
+// s16, s16+16, ... so each thread issues only a few independent loads, and
+// the 16 split lanes are merged through LDS in fixed order.
 template <int G>
 __global__ __launch_bounds__(kNT) void attn_combine_kernel(const float* __restrict__ part,
                                                            int splits, int Hq, int Hkv,
                                                            float* __restrict__ out) {
-  const int t = threadIdx.x, unit = blockIdx.x;
+  __shared__ float sm[16][16];
+  __shared__ float sl[16][16];
+  __shared__ float sa[16][16];
+  const int t = threadIdx.x, s16 = t >> 4, ch = t & 15;
+  const int unit = blockIdx.x, g = blockIdx.y, c = blockIdx.z * 16 + ch;
   const int b = unit / Hkv, h = unit - b * Hkv;
-  const float* src = part + (int64_t)unit * splits * (G * kRec);
-  for (int e = t; e < G * kD; e += kNT) {
-    const int g = e / kD, c = e % kD;
-    float M = -INFINITY;
-    for (int s = 0; s < splits; ++s) M = fmaxf(M, src[(int64_t)s * G * kRec + g * kRec]);
-    float L = 0.f, A = 0.f;
-    if (M != -INFINITY) {
-      for (int s = 0; s < splits; ++s) {
-        const float* r = src + (int64_t)s * G * kRec + g * kRec;
-        const float f = __expf(r[0] - M);
-        L = fmaf(r[1], f, L);
-        A = fmaf(r[2 + c], f, A);
+  const float* src = part + (int64_t)unit * splits * (G * kRec) + g * kRec;
+  float M = -INFINITY;
+  for (int s = s16; s < splits; s += 16) M = fmaxf(M, src[(int64_t)s * G * kRec]);
+  float L = 0.f, A = 0.f;
+  if (M != -INFINITY) {
+    for (int s = s16; s < splits; s += 16) {
+      const float* r = src + (int64_t)s * G * kRec;
+      const float f = __expf(r[0] - M);
+      L = fmaf(r[1], f, L);
+      A = fmaf(r[2 + c], f, A);
+    }
+  }
+  sm[s16][ch] = M;
+  sl[s16][ch] = L;
+  sa[s16][ch] = A;
+  __syncthreads();
+  if (s16 == 0) {
+    float Mg = -INFINITY;
+    for (int i = 0; i < 16; ++i) Mg = fmaxf(Mg, sm[i][ch]);
+    float Lg = 0.f, Ag = 0.f;
+    if (Mg != -INFINITY) {
+      for (int i = 0; i < 16; ++i) {
+        const float f = (sm[i][ch] == -INFINITY) ? 0.f : __expf(sm[i][ch] - Mg);
+        Lg = fmaf(sl[i][ch], f, Lg);
+        Ag = fmaf(sa[i][ch], f, Ag);
       }
     }
-    out[((int64_t)b * Hq + (int64_t)h * G + g) * kD + c] = (L > 0.f) ? A / L : 0.f;
+    out[((int64_t)b * Hq + (int64_t)h * G + g) * kD + c] = (Lg > 0.f) ? Ag / Lg : 0.f;
   }
 }
 
@@ -130,7 +151,8 @@ hipError_t launch_attention_g(const uint16_t* q, const uint16_t* K, const uint16
   const int splits = splits_for(U, idx ? (int64_t)k : max_len, idx == nullptr, &rps);
   hipLaunchKernelGGL(attn_partial_kernel<G>, dim3(splits, U), dim3(kNT), 0, s, q, K, V, Hq, Hkv,
                      cap, idx, k, seq_lens, rps, splits, scale, part);
-  hipLaunchKernelGGL(attn_combine_kernel<G>, dim3(U), dim3(kNT), 0, s, part, splits, Hq, Hkv, out);
+  hipLaunchKernelGGL(attn_combine_kernel<G>, dim3(U, G, kD / 16), dim3(kNT), 0, s, part, splits, Hq,
+                     Hkv, out);
   return hipGetLastError();
 }
 

@@ -57,7 +57,7 @@ template <int G>
 struct Cfg {
   static constexpr int NB = G * kR + 1;           // histogram bins
   static constexpr int NBP = (NB + 63) / 64 * 64;
-  static constexpr int PF = (G >= 8) ? 8 : 16;    // code loads in flight per thread
+  static constexpr int PF = 8;  // code loads in flight per thread (32 KiB per workgroup)
   static constexpr int HDRP = (2 * G + 3) / 4 * 4; // partial record header floats (M[G], L[G])
   static constexpr int RECP = HDRP + G * kD;       // partial record floats
   static constexpr int PROJ = 4 * (G + 1) * kR;    // projection reduction floats
