@@ -138,7 +138,10 @@ int hata_encode_append(const void* x, int64_t x_rows, int B, int H, int n_new, c
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const auto* xb = static_cast<const uint16_t*>(x);
   hipError_t e;
-  e = hata::launch_encode_rows(xb, x_rows, B, H, Hkv, n_new, W_H, codes, cap, pos, 0, s);
+  if (n_new >= hata::kBulkMinRows)
+    e = hata::launch_encode_bulk(xb, x_rows, B, H, Hkv, n_new, W_H, codes, cap, pos, 0, s);
+  else
+    e = hata::launch_encode_rows(xb, x_rows, B, H, Hkv, n_new, W_H, codes, cap, pos, 0, s);
   return check_launch(e, "encode_append launch");
 }
 

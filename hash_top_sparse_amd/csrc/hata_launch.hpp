@@ -16,7 +16,9 @@ hipError_t launch_encode_rows(const uint16_t* x, int64_t x_rows, int B, int H, i
 // Same contract, matrix-core path for long row runs (prefill).
 hipError_t launch_encode_bulk(const uint16_t* x, int64_t x_rows, int B, int H, int Hkv, int n_new,
                               const float* W, uint64_t* codes, int64_t cap, const int32_t* pos,
-                              hipStream_t s);
+                              int pos_off, hipStream_t s);
+// Row-run length from which hata_encode_append uses the matrix-core path.
+constexpr int kBulkMinRows = 512;
 
 // ---------------------------------------------------------------- score / select
 hipError_t launch_hamming(const uint64_t* qc, const uint64_t* kc, int B, int Hq, int Hkv,

@@ -271,3 +271,28 @@ def test_decode_step_deterministic_and_workspace_reuse(hata_gpu):
     for o, i, c in runs[1:]:
         assert np.array_equal(o.view(np.uint32), runs[0][0].view(np.uint32))
         assert np.array_equal(i, runs[0][1]) and np.array_equal(c, runs[0][2])
+
+
+@pytest.mark.parametrize("dist", ["exact", "gauss"])
+def test_bulk_encode_matches_row_encode(hata_gpu, dist):
+    """The matrix-core bulk path and the per-row path agree: bit-identical on
+    the exact recipe, within the flip allowance of each other otherwise."""
+    s = _shape(2, 4, 2, 3000, 16, dist=dist, seed=7950)
+    inp = synth.make_inputs(s, cap=3100)
+    d = Dev(inp)
+    bulk = torch.zeros((2, 2, 3100, 2), dtype=torch.int64, device="cuda")
+    hata_gpu.encode_append(d.K, d.W, bulk, n_new=3000)       # matrix cores
+    rows = torch.zeros_like(bulk)
+    for start in range(0, 3000, 500):                      # per-row path, 500 rows at a time
+        pos = torch.full((2,), start, dtype=torch.int32, device="cuda")
+        hata_gpu.encode_append(d.K, d.W, rows, n_new=min(500, 3000 - start), pos=pos)
+    torch.cuda.synchronize()
+    a, b_ = codes_np(bulk), codes_np(rows)
+    assert (a[:, :, 3000:] == 0).all()
+    if dist == "exact":
+        np.testing.assert_array_equal(a, b_)
+    else:
+        for b in range(2):
+            for h in range(2):
+                check_codes(a[b, h, :3000], inp.K[b, h, :3000], inp.W[h], exact=False)
+                check_codes(b_[b, h, :3000], inp.K[b, h, :3000], inp.W[h], exact=False)
