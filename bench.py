@@ -55,6 +55,30 @@ def bulk_bytes(B: int, Hkv: int, N: int, d: int = 128, r: int = 128) -> int:
     return B * Hkv * N * (d * 2 + r // 8) + Hkv * d * r * 4
 
 
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "decode_step_128k_hbm_traffic.md")
+KERNEL_SOURCES = ("hash_top_sparse_amd/csrc/decode_step.hip", "hash_top_sparse_amd/csrc/hata_device.hpp")
+
+
+def profiled_traffic():
+    """HBM bytes per fused-step launch from the committed counter summary,
+    or None when the kernel sources changed since the counters were taken."""
+    import hashlib
+    try:
+        txt = open(TRAFFIC_PROFILE).read()
+    except OSError:
+        return None
+    fields = dict(line.split(": ", 1) for line in txt.splitlines() if ": " in line and line[:1].isalpha())
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        h.update(open(os.path.join(ROOT, f), "rb").read())
+    if fields.get("kernel_source_sha256_16", "").strip() != h.hexdigest()[:16]:
+        return None
+    try:
+        return int(fields["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
 def cpu_baseline(inp, budget_s: float) -> dict:
     """Time the oracle's whole decode step on the host (OpenMP over units)."""
     import oracle
@@ -217,6 +241,9 @@ def main() -> int:
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="launch the timed steps eagerly")
     ap.add_argument("--sweep", action="store_true", help="also time the other workloads (2, 3, 5)")
+    ap.add_argument("--pmc-run", action="store_true",
+                    help="short run for hardware-counter passes: 32 eager fused steps over the layer "
+                         "caches, then one plain device copy of 1 GiB as the byte-counter reference")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -231,6 +258,16 @@ def main() -> int:
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     binding.load()
     torch.cuda.set_device(0)
+    if args.pmc_run:
+        measure(args.config, 32, 8, 0, args.layers, False, with_bulk=False)
+        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        src.fill_(1)
+        torch.cuda.synchronize()
+        dst.copy_(src)  # reference: reads and writes exactly 1 GiB
+        torch.cuda.synchronize()
+        log("pmc run done: reference copy of 1073741824 bytes")
+        return 0
     head, inp = measure(args.config, args.steps, args.warmup, 0 if args.no_dense else args.dense_steps,
                         args.layers, not args.no_graph, with_bulk=True)
     shape = inp.shape
@@ -269,7 +306,8 @@ def main() -> int:
                    "layer_caches_rotated": head["layers"],
                    "timing": "graph of K steps, HIP events" if not args.no_graph else "eager, HIP events"},
         "roofline": {"bound": "hbm", "achieved": head["GBs"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": head["GBs"] / PEAK_HBM_GBS, "traffic": None,
+                     "frac": head["GBs"] / PEAK_HBM_GBS,
+                     "traffic": profiled_traffic() if args.config == 4 else None,
                      "kernel": f"decode_step_kernel<{shape.G}>", "bytes_per_launch": head["bytes_per_step"]},
         "cpu_baseline": cpu,
         "dense_baseline": head["dense"],
