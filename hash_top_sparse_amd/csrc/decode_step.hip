@@ -52,6 +52,7 @@ constexpr int kWinHdr = 8;         // uint16 header entries
 constexpr int kWinCap = kWinBytes / 2 - kWinHdr;  // histogram bins a window holds
 constexpr int kMaxChunk = 32768;   // tokens per workgroup (uint16 scores in LDS)
 constexpr uint32_t kSpinLimit = 1u << 22;
+constexpr int kShortList = 64;     // kept rows staged in LDS, waves assigned to heads
 
 template <int G>
 struct Cfg {
@@ -61,7 +62,8 @@ struct Cfg {
   static constexpr int HDRP = (2 * G + 3) / 4 * 4; // partial record header floats (M[G], L[G])
   static constexpr int RECP = HDRP + G * kD;       // partial record floats
   static constexpr int PROJ = 4 * (G + 1) * kR;    // projection reduction floats
-  static constexpr int RED = (kMergeFloats<G> > PROJ) ? kMergeFloats<G> : PROJ;
+  static constexpr int RED0 = (kMergeFloats<G> > PROJ) ? kMergeFloats<G> : PROJ;
+  static constexpr int RED = (RED0 > (G + 4) * kRec) ? RED0 : (G + 4) * kRec;
   // LDS offsets in bytes
   static constexpr int o_hist = 0;                               // NBP uint32
   static constexpr int o_qf = o_hist + NBP * 4;                  // (G+1)*128 float
@@ -70,7 +72,8 @@ struct Cfg {
   static constexpr int o_misc = o_qcode + (G + 1) * 16;          // 64 uint32
   static constexpr int o_whdr = o_misc + 64 * 4;                 // 6 x kMaxWg int32
   static constexpr int o_win = o_whdr + 6 * kMaxWg * 4;          // kMaxWg*kWinBytes (also combine staging)
-  static constexpr int o_sel = o_win + kMaxWg * kWinBytes;       // k int32
+  static constexpr int o_kvs = o_win + kMaxWg * kWinBytes;       // kShortList K/V rows
+  static constexpr int o_sel = o_kvs + kShortList * 512;         // k + 1 int32
   static size_t lds_bytes(int k, int chunk) {
     size_t s = (size_t)o_sel + (size_t)(k + 1) * 4;
     s = (s + 15) / 16 * 16;
@@ -179,6 +182,7 @@ __global__ __launch_bounds__(kNT) void decode_step_kernel(const StepArgs a) {
   uint32_t* misc = reinterpret_cast<uint32_t*>(smem + C::o_misc);
   int32_t* whdr = reinterpret_cast<int32_t*>(smem + C::o_whdr);  // [6][kMaxWg]
   unsigned char* winb = smem + C::o_win;
+  unsigned char* kvs = smem + C::o_kvs;
   int32_t* sel = reinterpret_cast<int32_t*>(smem + C::o_sel);
   uint16_t* sc = reinterpret_cast<uint16_t*>(smem + ((C::o_sel + (a.k + 1) * 4 + 15) / 16 * 16));
 
@@ -468,36 +472,44 @@ __global__ __launch_bounds__(kNT) void decode_step_kernel(const StepArgs a) {
   const int m_self = min(k, (int)(tot_lt + min(tot_eq, take_self)));
   __syncthreads();
 
-  // ---- 6. gather-fused attention over the kept rows
-  const int slot = t >> 4, sub = t & 15;
-  float qreg[G][8];
-#pragma unroll
-  for (int g = 0; g < G; ++g)
-#pragma unroll
-    for (int c = 0; c < 8; ++c) qreg[g][c] = qf[g * kD + sub * 8 + c];
+  // ---- 6. gather-fused attention over the kept rows; a short list is
+  // processed with waves assigned to heads (no cross-wave merge), a long one
+  // with row groups spread over all waves
+  const int sub = t & 15;
   const uint16_t* Kb = a.K + row0 * kD + sub * 8;
   const uint16_t* Vb = a.V + row0 * kD + sub * 8;
-  SoftmaxState<G> st;
-  st.init();
-  constexpr int UN = 2;
-  for (int r0 = slot; r0 < m_self; r0 += 16 * UN) {
-    uint4 kv[UN], vv[UN];
-    bool valid[UN];
+  if (m_self <= kShortList) {
+    attend_heads<G, kShortList>(qf, sel, m_self, n, a.K + row0 * kD, a.V + row0 * kD, a.scale, red,
+                                reinterpret_cast<uint4*>(kvs));
+  } else {
+    const int slot = t >> 4;
+    float qreg[G][8];
 #pragma unroll
-    for (int u = 0; u < UN; ++u) {
-      const int r = r0 + 16 * u;
-      valid[u] = r < m_self;
-      kv[u] = make_uint4(0, 0, 0, 0);
-      vv[u] = make_uint4(0, 0, 0, 0);
-      if (valid[u]) {
-        const int64_t tok = min(max(sel[r], 0), n - 1);
-        kv[u] = *reinterpret_cast<const uint4*>(Kb + tok * kD);
-        vv[u] = *reinterpret_cast<const uint4*>(Vb + tok * kD);
+    for (int g = 0; g < G; ++g)
+#pragma unroll
+      for (int c = 0; c < 8; ++c) qreg[g][c] = qf[g * kD + sub * 8 + c];
+    SoftmaxState<G> st;
+    st.init();
+    constexpr int UN = 2;
+    for (int r0 = slot; r0 < m_self; r0 += 16 * UN) {
+      uint4 kv[UN], vv[UN];
+      bool valid[UN];
+#pragma unroll
+      for (int u = 0; u < UN; ++u) {
+        const int r = r0 + 16 * u;
+        valid[u] = r < m_self;
+        kv[u] = make_uint4(0, 0, 0, 0);
+        vv[u] = make_uint4(0, 0, 0, 0);
+        if (valid[u]) {
+          const int64_t tok = min(max(sel[r], 0), n - 1);
+          kv[u] = *reinterpret_cast<const uint4*>(Kb + tok * kD);
+          vv[u] = *reinterpret_cast<const uint4*>(Vb + tok * kD);
+        }
       }
+      attend_block<G, UN>(st, qreg, kv, vv, valid, a.scale);
     }
-    attend_block<G, UN>(st, qreg, kv, vv, valid, a.scale);
+    merge_wg<G>(st, red);
   }
-  merge_wg<G>(st, red);
 
   // kept indices, written once the attention no longer needs the LDS list
   // (coalesced, and no barrier waits on these stores)
@@ -570,18 +582,25 @@ __global__ __launch_bounds__(kNT) void decode_step_kernel(const StepArgs a) {
   }
   __syncthreads();
   const float* stage = reinterpret_cast<const float*>(winb);
+  // rescale factor of every writer for the (at most two) heads of the slice,
+  // computed once: fac[h2][ww] = exp(M_ww - M) with M the max over writers
+  float* fac = red;  // [2][kMaxWg], red is free again
+  const int ga = e0 / kD, gb = (e1 - 1) / kD;  // first and last head of the slice
+  if (wv < 2 && e0 < e1) {
+    const int g = wv == 0 ? ga : gb;
+    const float Mw = (lane < a.Wg) ? stage[lane * nch * 4 + g] : -INFINITY;
+    const float M = pair32_max(pair16_max(row16_max_f(Mw)));
+    fac[wv * kMaxWg + lane] = (lane < a.Wg && M != -INFINITY) ? __expf(Mw - M) : 0.f;
+  }
+  __syncthreads();
   for (int e = e0 + t; e < e1; e += kNT) {
     const int g = e / kD;
-    float M = -INFINITY;
-    for (int ww = 0; ww < a.Wg; ++ww) M = fmaxf(M, stage[ww * nch * 4 + g]);
+    const float* f = fac + (g == ga ? 0 : kMaxWg);
     float Ls = 0.f, A = 0.f;
-    if (M != -INFINITY) {
-      for (int ww = 0; ww < a.Wg; ++ww) {
-        const float* r = stage + ww * nch * 4;
-        const float f = __expf(r[g] - M);
-        Ls = fmaf(r[G + g], f, Ls);
-        A = fmaf(r[C::HDRP + (e - e0)], f, A);
-      }
+    for (int ww = 0; ww < a.Wg; ++ww) {
+      const float* r = stage + ww * nch * 4;
+      Ls = fmaf(r[G + g], f[ww], Ls);
+      A = fmaf(r[C::HDRP + (e - e0)], f[ww], A);
     }
     outp[e] = (Ls > 0.f) ? A / Ls : 0.f;
   }
@@ -624,16 +643,20 @@ StepPlan plan_decode_step(int B, int Hq, int Hkv, int64_t max_len, int k, int nu
   const int G = p.G;
   const int NB = G * kR + 1;
   p.full_words = (NB + 1) / 2;
-  size_t off = 0;
-  p.off_err = off;   off = align(off + 256);
+  size_t recp = 0;
   if (p.fused) {
-    size_t recp;
     switch (G) {
       case 1: p.lds_bytes = Cfg<1>::lds_bytes(k, p.chunk); recp = Cfg<1>::RECP; break;
       case 2: p.lds_bytes = Cfg<2>::lds_bytes(k, p.chunk); recp = Cfg<2>::RECP; break;
       case 4: p.lds_bytes = Cfg<4>::lds_bytes(k, p.chunk); recp = Cfg<4>::RECP; break;
       default: p.lds_bytes = Cfg<8>::lds_bytes(k, p.chunk); recp = Cfg<8>::RECP; break;
     }
+    // 160 KiB of LDS per CU, less the kernel's static LDS and a margin
+    if (p.lds_bytes > 159 * 1024) p.fused = false;
+  }
+  size_t off = 0;
+  p.off_err = off;   off = align(off + 256);
+  if (p.fused) {
     const size_t slots = (size_t)U * kMaxWg;
     p.off_flags = off; off = align(off + slots * 4);
     if (Wg > 1) {

@@ -136,6 +136,18 @@ template <int CTRL>
 __device__ __forceinline__ int dpp_i(int v) {
   return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
 }
+template <int CTRL>
+__device__ __forceinline__ float dpp_fm(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(-INFINITY), __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+// Maximum within each row of 16 lanes (every lane of the row gets it).
+__device__ __forceinline__ float row16_max_f(float v) {
+  v = fmaxf(v, dpp_fm<0xB1>(v));
+  v = fmaxf(v, dpp_fm<0x4E>(v));
+  v = fmaxf(v, dpp_fm<0x141>(v));
+  v = fmaxf(v, dpp_fm<0x140>(v));
+  return v;
+}
 // Minimum over the 64 lanes of a wave (every lane gets it).
 __device__ __forceinline__ int wave_min_i(int v) {
   v = min(v, dpp_i<0xB1>(v));
@@ -422,6 +434,110 @@ __device__ __forceinline__ void merge_wg(const SoftmaxState<G>& st, float* red) 
     r0[2 + c] = As[i];
   }
   __syncthreads();
+}
+
+// Attention over a short list of kept rows (m <= MAXR) with waves assigned
+// to heads.  The m K/V rows are first staged in LDS by the whole workgroup
+// (one round of 16-byte loads, at most MAXR*32/256 per thread); then for
+// G >= 4 wave wv owns heads [wv*G/4, (wv+1)*G/4) over every row, and for
+// G < 4 the 4/G waves of a head split the rows.  Within a wave the 4 groups
+// of 16 lanes take rows in turn (8 channels per lane).  Each wave merges only
+// its own heads (permlane swaps), so no cross-wave merge is needed for G >= 4.
+// kvs: LDS of MAXR * 512 bytes.  Writes red[g*kRec + {M, L, A[128]}] (red
+// holds at least (G + 4) * kRec floats); ends with __syncthreads.
+template <int G, int MAXR>
+__device__ __forceinline__ void attend_heads(const float* qf, const int32_t* sel, int m, int n,
+                                             const uint16_t* K, const uint16_t* V, float scale,
+                                             float* red, uint4* kvs) {
+  constexpr int HPW = (G >= 4) ? G / 4 : 1;  // heads per wave
+  constexpr int WPH = (G >= 4) ? 1 : 4 / G;  // waves per head
+  constexpr int LPT = MAXR * 32 / kNT;       // staging loads per thread
+  const int t = threadIdx.x, lane = t & 63, wv = t >> 6, rg = lane >> 4, sub = lane & 15;
+  // stage: row r occupies 32 chunks of 16 bytes (16 of K, then 16 of V)
+  {
+    uint4 v[LPT];
+#pragma unroll
+    for (int i = 0; i < LPT; ++i) {
+      const int c = t + i * kNT, r = c >> 5, part16 = c & 31;
+      v[i] = make_uint4(0, 0, 0, 0);
+      if (r < m) {
+        const int64_t tok = min(max(sel[r], 0), n - 1);
+        const uint16_t* src = (part16 < 16 ? K : V) + tok * kD + (part16 & 15) * 8;
+        v[i] = *reinterpret_cast<const uint4*>(src);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < LPT; ++i) {
+      const int c = t + i * kNT;
+      if ((c >> 5) < m) kvs[c] = v[i];
+    }
+  }
+  __syncthreads();
+  const int hg = wv / WPH, part = wv - hg * WPH;
+  const int g0 = hg * HPW;
+  float qreg[HPW][8];
+#pragma unroll
+  for (int i = 0; i < HPW; ++i)
+#pragma unroll
+    for (int c = 0; c < 8; ++c) qreg[i][c] = qf[(g0 + i) * kD + sub * 8 + c];
+  SoftmaxState<HPW> st;
+  st.init();
+  constexpr int UN = 4;
+  const int stride = 4 * WPH;
+  for (int r0 = part * 4 + rg; r0 < m; r0 += stride * UN) {
+    uint4 kv[UN], vv[UN];
+    bool valid[UN];
+#pragma unroll
+    for (int u = 0; u < UN; ++u) {
+      const int r = r0 + u * stride;
+      valid[u] = r < m;
+      kv[u] = make_uint4(0, 0, 0, 0);
+      vv[u] = make_uint4(0, 0, 0, 0);
+      if (valid[u]) {
+        kv[u] = kvs[r * 32 + sub];
+        vv[u] = kvs[r * 32 + 16 + sub];
+      }
+    }
+    attend_block<HPW, UN>(st, qreg, kv, vv, valid, scale);
+  }
+  float* tmp = red + G * kRec;  // [4 waves][kRec] when several waves share a head
+#pragma unroll
+  for (int i = 0; i < HPW; ++i) {
+    const float M = pair32_max(pair16_max(st.m[i]));
+    const float f = (M == -INFINITY) ? 0.f : __expf(st.m[i] - M);
+    const float L = pair32_sum(pair16_sum(st.l[i] * f));
+    float A[8];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) A[c] = pair32_sum(pair16_sum(st.acc[i][c] * f));
+    if (rg == 0) {
+      float* r = (WPH == 1) ? red + (g0 + i) * kRec : tmp + wv * kRec;
+      if (sub == 0) { r[0] = M; r[1] = L; }
+#pragma unroll
+      for (int c = 0; c < 8; ++c) r[2 + sub * 8 + c] = A[c];
+    }
+  }
+  __syncthreads();
+  if (WPH > 1) {
+    // merge the WPH row partitions of each head in fixed order
+    for (int e = t; e < G * kD; e += kNT) {
+      const int g = e / kD, c = e % kD;
+      float M = -INFINITY;
+      for (int p = 0; p < WPH; ++p) M = fmaxf(M, tmp[(g * WPH + p) * kRec]);
+      float L = 0.f, A = 0.f;
+      if (M != -INFINITY) {
+        for (int p = 0; p < WPH; ++p) {
+          const float* r = tmp + (g * WPH + p) * kRec;
+          const float f = __expf(r[0] - M);
+          L = fmaf(r[1], f, L);
+          A = fmaf(r[2 + c], f, A);
+        }
+      }
+      float* o = red + g * kRec;
+      if (c == 0) { o[0] = M; o[1] = L; }
+      o[2 + c] = A;
+    }
+    __syncthreads();
+  }
 }
 
 }  // namespace hata
