@@ -58,7 +58,9 @@ template <int G>
 struct Cfg {
   static constexpr int NB = G * kR + 1;           // histogram bins
   static constexpr int NBP = (NB + 63) / 64 * 64;
-  static constexpr int PF = 8;  // code loads in flight per thread (32 KiB per workgroup)
+  // code loads in flight per thread (a ring: 32 KiB per workgroup); deeper
+  // rings delay W_H, which shares the CU's vector-memory path
+  static constexpr int PF = 8;
   static constexpr int HDRP = (2 * G + 3) / 4 * 4; // partial record header floats (M[G], L[G])
   static constexpr int RECP = HDRP + G * kD;       // partial record floats
   static constexpr int PROJ = 4 * (G + 1) * kR;    // projection reduction floats
@@ -77,7 +79,8 @@ struct Cfg {
   static size_t lds_bytes(int k, int chunk) {
     size_t s = (size_t)o_sel + (size_t)(k + 1) * 4;
     s = (s + 15) / 16 * 16;
-    return s + (size_t)chunk * 2;
+    // scores, padded to a multiple of 8 slabs of 256 tokens
+    return s + (size_t)((chunk + 8 * kNT - 1) / (8 * kNT) * (8 * kNT)) * 2;
   }
 };
 
@@ -210,9 +213,7 @@ __global__ __launch_bounds__(kNT) void decode_step_kernel(const StepArgs a) {
   const bool owns_new = (n - 1 >= lo) && (n - 1 < lo + cnt);
   const int new_li = n - 1 - lo;
 
-  // ---- 1. loads: W_H and the new rows first, then the code-cache prefetch
-  WRegs wr;
-  load_w_regs(a.W + (int64_t)h * kD * kR, wr);
+  // ---- 1. loads: the new rows, W_H, then the code-cache ring
   const int nrows = G + (owns_new ? 1 : 0);
   uint32_t xrow[(G + 1 + 3) / 4];
 #pragma unroll
@@ -227,6 +228,8 @@ __global__ __launch_bounds__(kNT) void decode_step_kernel(const StepArgs a) {
       xrow[i] = src[c2];
     }
   }
+  WRegs wr;
+  load_w_regs(a.W + (int64_t)h * kD * kR, wr);
   uint32_t epoch = 0;
   if (a.Wg > 1 && wv == 0) {
     const CohBuf fb(a.flags + (int64_t)unit * kMaxWg, kMaxWg * 4);
@@ -271,28 +274,46 @@ __global__ __launch_bounds__(kNT) void decode_step_kernel(const StepArgs a) {
   QMasks<G> qm;
   build_qmasks<G>(qw, qm);
 
-  // ---- 3. score the owned tokens
-  for (int base = 0; base < cnt; base += PF * kNT) {
-    uint4 nbuf[PF];
-    const int nbase = base + PF * kNT;
-#pragma unroll
-    for (int j = 0; j < PF; ++j) {
-      const int li = nbase + j * kNT + t;
-      nbuf[j] = make_uint4(0, 0, 0, 0);
-      if (li < cnt) nbuf[j] = load_stream16(cbase + li);
-    }
+  // ---- 3. score the owned tokens.  Each ring slot is scored, then refilled
+  // with the load PF*256 tokens ahead.  Row n-1 is scored from the cache
+  // like the others and corrected afterwards by the thread that scored it.
+  auto score_one = [&](const uint4 c, int li) {
+    const uint32_t s = gqa_hamming<G>(c, qm);
+    sc[li] = (uint16_t)s;
+    atomicAdd(&hist[s], 1u);
+  };
+  constexpr int BATCH = PF * kNT;
+  int base = 0;
+  for (; base + 2 * BATCH <= cnt; base += BATCH) {  // this batch and the next are full
 #pragma unroll
     for (int j = 0; j < PF; ++j) {
       const int li = base + j * kNT + t;
-      if (li < cnt) {
-        const uint4 c = (li == new_li) ? newc : cbuf[j];
-        const uint32_t s = gqa_hamming<G>(c, qm);
-        sc[li] = (uint16_t)s;
-        atomicAdd(&hist[s], 1u);
-      }
+      score_one(cbuf[j], li);
+      cbuf[j] = load_stream16(cbase + li + BATCH);
     }
+  }
+  if (base + BATCH <= cnt) {  // a full batch, the next one partial or empty
 #pragma unroll
-    for (int j = 0; j < PF; ++j) cbuf[j] = nbuf[j];
+    for (int j = 0; j < PF; ++j) {
+      const int li = base + j * kNT + t;
+      score_one(cbuf[j], li);
+      if (li + BATCH < cnt) cbuf[j] = load_stream16(cbase + li + BATCH);
+    }
+    base += BATCH;
+  }
+  if (base < cnt) {  // the last, partial batch
+#pragma unroll
+    for (int j = 0; j < PF; ++j) {
+      const int li = base + j * kNT + t;
+      if (li < cnt) score_one(cbuf[j], li);
+    }
+  }
+  if (owns_new && t == new_li % kNT) {
+    const uint32_t s_old = sc[new_li];
+    const uint32_t s_new = gqa_hamming<G>(newc, qm);
+    atomicSub(&hist[s_old], 1u);
+    atomicAdd(&hist[s_new], 1u);
+    sc[new_li] = (uint16_t)s_new;
   }
   __syncthreads();
 
@@ -428,44 +449,73 @@ __global__ __launch_bounds__(kNT) void decode_step_kernel(const StepArgs a) {
     sel_before = pre_lt + (pre_eq < quota ? pre_eq : quota);
   }
 
-  // ---- 5. ordered compaction of the kept tokens (index order); each
-  // thread owns a contiguous run of 8*per8 scores, read 8 at a time
-  const int per8 = (cnt + 8 * kNT - 1) / (8 * kNT);
-  const int i_begin = min(cnt, t * per8 * 8), i_end = min(cnt, i_begin + per8 * 8);
+  // ---- 5. ordered compaction of the kept tokens (index order).  Thread t
+  // owns the run of `run` consecutive tokens from t*run and records, per 32
+  // of them, which are strict (score < T) and which tied (score == T) as bit
+  // masks with token p of the word at bit 31-p.  A token's rank among the
+  // workgroup's strict (resp. tied) tokens is the block prefix of the
+  // per-thread counts plus the set bits above it; it is kept if strict, or
+  // tied with tied-rank < take_self, at position
+  // strict-rank + min(tied-rank, take_self).  Only set bits are visited.
+  constexpr int kRunWords = kMaxChunk / kNT / 32;  // mask words per thread
+  const int per8 = (cnt + 8 * kNT - 1) / (8 * kNT);  // 16-byte score reads per thread
+  const int run = per8 * 8;
+  const int i_begin = t * run;  // the padded score area covers 256 * run tokens
+  const int nvalid = max(0, min(cnt - i_begin, run));
   const uint32_t Tu = (uint32_t)T;
-  uint32_t lt = 0, eq = 0;
-  for (int i8 = i_begin; i8 < i_end; i8 += 8) {
-    const uint4 v = *reinterpret_cast<const uint4*>(sc + i8);
-    const uint32_t wds[4] = {v.x, v.y, v.z, v.w};
+  uint32_t mlt[kRunWords], meq[kRunWords];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const uint32_t s2 = (wds[e >> 1] >> ((e & 1) * 16)) & 0xFFFFu;
-      const bool in = i8 + e < i_end;
-      lt += (in && s2 < Tu);
-      eq += (in && s2 == Tu);
+  for (int wi = 0; wi < kRunWords; ++wi) {
+    uint32_t ml = 0, me = 0;
+    if (wi * 4 < per8) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        if (wi * 4 + c < per8) {
+          const uint4 v = *reinterpret_cast<const uint4*>(sc + i_begin + wi * 32 + c * 8);
+          const uint32_t wds[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const uint32_t s2 = (wds[e >> 1] >> ((e & 1) * 16)) & 0xFFFFu;
+            ml = ml + ml + (s2 < Tu ? 1u : 0u);
+            me = me + me + (s2 == Tu ? 1u : 0u);
+          }
+        }
+      }
+      // left-align (token p at bit 31-p) and drop tokens past cnt
+      const int ntok = min(32, run - wi * 32);
+      const int nv = max(0, min(32, nvalid - wi * 32));
+      const uint32_t keep = nv == 0 ? 0u : (~0u << (32 - nv));
+      ml = (ml << (32 - ntok)) & keep;
+      me = (me << (32 - ntok)) & keep;
     }
+    mlt[wi] = ml;
+    meq[wi] = me;
   }
-  uint32_t tot_lt, tot_eq;
-  uint32_t lt_before = block_excl_scan_u32(lt, misc + 8, &tot_lt);
-  uint32_t eq_before = block_excl_scan_u32(eq, misc + 12, &tot_eq);
-  // Branch-free emission: a kept token's position among this workgroup's
-  // kept tokens is lt_before + min(eq_before, take_self) (strict and tied
-  // alike); tokens that are not kept write to the spare slot sel[k].
-  if (lt | eq) {
-    for (int i8 = i_begin; i8 < i_end; i8 += 8) {
-      const uint4 v = *reinterpret_cast<const uint4*>(sc + i8);
-      const uint32_t wds[4] = {v.x, v.y, v.z, v.w};
+  uint32_t own_pk = 0;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const uint32_t s2 = (wds[e >> 1] >> ((e & 1) * 16)) & 0xFFFFu;
-        const bool in = i8 + e < i_end;
-        const bool islt = in && s2 < Tu;
-        const bool iseq = in && s2 == Tu;
-        const bool keep = islt || (iseq && eq_before < take_self);
-        const uint32_t pos = lt_before + min(eq_before, take_self);
-        sel[keep ? min(pos, (uint32_t)k) : (uint32_t)k] = lo + i8 + e;
-        lt_before += islt;
-        eq_before += iseq;
+  for (int wi = 0; wi < kRunWords; ++wi)
+    own_pk += (uint32_t)__popc(mlt[wi]) | ((uint32_t)__popc(meq[wi]) << 16);
+  uint32_t tot_pk;  // packed halves never exceed kMaxChunk
+  const uint32_t before_pk = block_excl_scan_u32(own_pk, misc + 8, &tot_pk);
+  const uint32_t tot_lt = tot_pk & 0xFFFFu, tot_eq = tot_pk >> 16;
+  {
+    uint32_t ltb = before_pk & 0xFFFFu, eqb = before_pk >> 16;
+#pragma unroll
+    for (int wi = 0; wi < kRunWords; ++wi) {
+      if (wi * 32 < run) {
+        uint32_t m = mlt[wi] | meq[wi];
+        while (m) {
+          const int bpos = 31 - __clz(m);  // highest set bit: earliest token
+          const uint32_t above = (bpos == 31) ? 0u : (~0u << (bpos + 1));
+          const uint32_t rl = ltb + (uint32_t)__popc(mlt[wi] & above);
+          const uint32_t re = eqb + (uint32_t)__popc(meq[wi] & above);
+          const bool islt = (mlt[wi] >> bpos) & 1u;
+          if (islt || re < take_self)
+            sel[min(rl + min(re, take_self), (uint32_t)k)] = lo + i_begin + wi * 32 + (31 - bpos);
+          m &= ~(1u << bpos);
+        }
+        ltb += (uint32_t)__popc(mlt[wi]);
+        eqb += (uint32_t)__popc(meq[wi]);
       }
     }
   }
@@ -584,25 +634,34 @@ __global__ __launch_bounds__(kNT) void decode_step_kernel(const StepArgs a) {
   const float* stage = reinterpret_cast<const float*>(winb);
   // rescale factor of every writer for the (at most two) heads of the slice,
   // computed once: fac[h2][ww] = exp(M_ww - M) with M the max over writers
-  float* fac = red;  // [2][kMaxWg], red is free again
+  // and the head's rescaled sum of L, Lsum[h2] = sum_ww L_ww * fac[h2][ww]
+  float* fac = red;  // [2][kMaxWg] then Lsum[2]; red is free again
   const int ga = e0 / kD, gb = (e1 - 1) / kD;  // first and last head of the slice
   if (wv < 2 && e0 < e1) {
     const int g = wv == 0 ? ga : gb;
     const float Mw = (lane < a.Wg) ? stage[lane * nch * 4 + g] : -INFINITY;
     const float M = pair32_max(pair16_max(row16_max_f(Mw)));
-    fac[wv * kMaxWg + lane] = (lane < a.Wg && M != -INFINITY) ? __expf(Mw - M) : 0.f;
+    const float f = (lane < a.Wg && M != -INFINITY) ? __expf(Mw - M) : 0.f;
+    fac[wv * kMaxWg + lane] = f;
+    const float Lw = (lane < a.Wg) ? stage[lane * nch * 4 + G + g] * f : 0.f;
+    const float Ls = pair32_sum(pair16_sum(sum16(Lw)));
+    if (lane == 0) fac[2 * kMaxWg + wv] = Ls;
   }
   __syncthreads();
-  for (int e = e0 + t; e < e1; e += kNT) {
-    const int g = e / kD;
-    const float* f = fac + (g == ga ? 0 : kMaxWg);
-    float Ls = 0.f, A = 0.f;
-    for (int ww = 0; ww < a.Wg; ++ww) {
-      const float* r = stage + ww * nch * 4;
-      Ls = fmaf(r[G + g], f[ww], Ls);
-      A = fmaf(r[C::HDRP + (e - e0)], f[ww], A);
+  {
+    // output e0 + eo is summed by the 16 lanes of one row, writer ww by lane
+    // ww % 16, then added across the row in a fixed order
+    const int sub16 = t & 15, nout = e1 - e0;
+    for (int eo = t >> 4; eo < nout; eo += kNT / 16) {
+      const int g = (e0 + eo) / kD, h2 = (g == ga) ? 0 : 1;
+      const float* f = fac + h2 * kMaxWg;
+      float A = 0.f;
+      for (int ww = sub16; ww < a.Wg; ww += 16)
+        A = fmaf(stage[ww * nch * 4 + C::HDRP + eo], f[ww], A);
+      A = sum16(A);
+      const float Ls = fac[2 * kMaxWg + h2];
+      if (sub16 == 0) outp[e0 + eo] = (Ls > 0.f) ? A / Ls : 0.f;
     }
-    outp[e] = (Ls > 0.f) ? A / Ls : 0.f;
   }
   // keep every flag slot of the unit equal for the next launch (which may
   // use a different number of workgroups per unit)
