@@ -9,8 +9,12 @@
 // Work split.  A unit is one (sequence b, KV head h).  Each unit owns Wg
 // workgroups (co-resident: the host keeps units x Wg <= CU count); workgroup
 // w owns tokens [w*chunk, (w+1)*chunk).  When the unit count is a multiple of
-// 8 the block -> unit map keeps a unit's workgroups on one XCD (blocks are
-// dealt round-robin over the 8 XCDs), so their exchanges stay XCD-local.
+// 8 the block -> unit map gives a unit only blocks whose indices agree mod 8;
+// the dispatcher deals blocks round-robin over the 8 XCDs, so (once a probe
+// launch has confirmed that on the device) a unit's workgroups share one XCD
+// and its exchanges use plain stores that land in that XCD's L2, read back
+// with device-coherent loads; every writer stamps its XCD id into its window
+// header and readers check it.  Otherwise the stores are device-coherent.
 //
 // Per workgroup:
 //   1. issue the streaming loads of its code-cache rows (16 bytes per token);
@@ -37,6 +41,8 @@
 // no same-address read-modify-write (those serialise at the memory side).
 // Every wait is bounded; a timeout sets bit 0 of the workspace error word.
 #include <atomic>
+#include <mutex>
+#include <vector>
 
 #include "hata_device.hpp"
 #include "hata_launch.hpp"
@@ -52,6 +58,9 @@ constexpr int kWinHdr = 8;         // uint16 header entries
 constexpr int kWinCap = kWinBytes / 2 - kWinHdr;  // histogram bins a window holds
 constexpr int kMaxChunk = 32768;   // tokens per workgroup (uint16 scores in LDS)
 constexpr uint32_t kSpinLimit = 1u << 22;
+// s_getreg operand for HW_REG_XCC_ID (register 20, bits 0..31): the XCD the
+// wave runs on
+constexpr int kXccIdReg = 20 | (31 << 11);
 constexpr int kShortList = 64;     // kept rows staged in LDS, waves assigned to heads
 
 template <int G>
@@ -72,8 +81,8 @@ struct Cfg {
   static constexpr int o_red = o_qf + (G + 1) * kD * 4;          // RED float
   static constexpr int o_qcode = o_red + RED * 4;                // (G+1)*2 uint64
   static constexpr int o_misc = o_qcode + (G + 1) * 16;          // 64 uint32
-  static constexpr int o_whdr = o_misc + 64 * 4;                 // 6 x kMaxWg int32
-  static constexpr int o_win = o_whdr + 6 * kMaxWg * 4;          // kMaxWg*kWinBytes (also combine staging)
+  static constexpr int o_whdr = o_misc + 64 * 4;                 // kMaxWg int4 + 2*4*64 uint32
+  static constexpr int o_win = o_whdr + 4 * kMaxWg * 4 + 2048;   // kMaxWg*kWinBytes (also combine staging)
   static constexpr int o_kvs = o_win + kMaxWg * kWinBytes;       // kShortList K/V rows
   static constexpr int o_sel = o_kvs + kShortList * 512;         // k + 1 int32
   static size_t lds_bytes(int k, int chunk) {
@@ -97,6 +106,7 @@ struct StepArgs {
   int Hq, Hkv, k;
   float scale;
   int Wg, chunk, xcd_map, U;
+  int xcd_local;    // exchanges stay on one XCD: plain stores (see CohBuf::st16x)
   uint32_t* err;
   uint32_t* flags;  // [U][kMaxWg]
   uint32_t* win;    // [U][kMaxWg][kWinWords]
@@ -183,7 +193,7 @@ __global__ __launch_bounds__(kNT) void decode_step_kernel(const StepArgs a) {
   float* red = reinterpret_cast<float*>(smem + C::o_red);
   uint64_t* qcode = reinterpret_cast<uint64_t*>(smem + C::o_qcode);
   uint32_t* misc = reinterpret_cast<uint32_t*>(smem + C::o_misc);
-  int32_t* whdr = reinterpret_cast<int32_t*>(smem + C::o_whdr);  // [6][kMaxWg]
+  int32_t* whdr = reinterpret_cast<int32_t*>(smem + C::o_whdr);  // writer headers + partial counts
   unsigned char* winb = smem + C::o_win;
   unsigned char* kvs = smem + C::o_kvs;
   int32_t* sel = reinterpret_cast<int32_t*>(smem + C::o_sel);
@@ -344,7 +354,8 @@ __global__ __launch_bounds__(kNT) void decode_step_kernel(const StepArgs a) {
         e16[0] = (uint32_t)wlo; e16[1] = (uint32_t)(top + 1);
         e16[2] = has_k ? 1u : 0u; e16[3] = ovf ? 1u : 0u;
         e16[4] = (uint32_t)cnt & 0xFFFFu; e16[5] = (uint32_t)cnt >> 16;
-        e16[6] = 0; e16[7] = 0;
+        e16[6] = (uint32_t)__builtin_amdgcn_s_getreg(kXccIdReg) & 0xFu;  // this XCD
+        e16[7] = 0;
       } else {
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
@@ -358,7 +369,7 @@ __global__ __launch_bounds__(kNT) void decode_step_kernel(const StepArgs a) {
       u32x4 v;
       v.x = e16[0] | (e16[1] << 16); v.y = e16[2] | (e16[3] << 16);
       v.z = e16[4] | (e16[5] << 16); v.w = e16[6] | (e16[7] << 16);
-      wbuf.st16(w * kWinBytes + t * 16, v);
+      wbuf.st16x(w * kWinBytes + t * 16, v, a.xcd_local);
     }
     if (ovf) {
       const CohBuf fbuf(a.full + ((int64_t)unit * kMaxWg + w) * a.full_words, a.full_words * 4);
@@ -369,12 +380,12 @@ __global__ __launch_bounds__(kNT) void decode_step_kernel(const StepArgs a) {
           const int s2 = 2 * i + e;
           two[e] = (s2 < NB) ? hist[s2] : (uint32_t)cnt;
         }
-        fbuf.st4(i * 4, two[0] | (two[1] << 16));
+        fbuf.st4x(i * 4, two[0] | (two[1] << 16), a.xcd_local);
       }
     }
     wait_all_mem();
     __syncthreads();
-    if (t == 0) st_agent(a.flags + (int64_t)unit * kMaxWg + w, epoch + 1);
+    if (t == 0) CohBuf(a.flags + (int64_t)unit * kMaxWg, kMaxWg * 4).st4x(w * 4, epoch + 1, a.xcd_local);
     wait_unit(a, unit, epoch + 1);
 
     // read every window of the unit: Wg*16 chunks of 16 bytes, all in flight
@@ -393,15 +404,16 @@ __global__ __launch_bounds__(kNT) void decode_step_kernel(const StepArgs a) {
       }
     }
     __syncthreads();
-    // The threshold and the per-writer counts are computed by wave 0 with
-    // lane = writer: C(s) = sum over lanes of the writer's cumulative count
-    // at s (a register-held header plus one LDS read), summed with DPP.
+    // Writer headers, parsed once by wave 0 (lane = writer): first bin lw,
+    // window length ln, count at the window's end topc, overflow flag.
+    int4* hdr4 = reinterpret_cast<int4*>(whdr);                 // [kMaxWg]
+    uint32_t* cpart = reinterpret_cast<uint32_t*>(whdr + 4 * kMaxWg);  // [2][4][64]
     if (wv == 0) {
       int lw = NB, tw = NB - 1, ln = 0, topc = 0;
       bool hw = false, ow = false;
-      const uint16_t* ent = reinterpret_cast<const uint16_t*>(winb + lane * kWinBytes) + kWinHdr;
       if (lane < a.Wg) {
         const uint32_t* hdr = reinterpret_cast<const uint32_t*>(winb + lane * kWinBytes);
+        const uint16_t* ent = reinterpret_cast<const uint16_t*>(hdr) + kWinHdr;
         lw = min((int)(hdr[0] & 0xFFFFu), NB);
         tw = min((int)(hdr[0] >> 16) - 1, NB - 1);
         hw = (hdr[1] & 0xFFFFu) != 0;
@@ -409,30 +421,78 @@ __global__ __launch_bounds__(kNT) void decode_step_kernel(const StepArgs a) {
         ln = max(0, min(tw - lw + 1, kWinCap));
         topc = ln > 0 ? ent[ln - 1] : 0;
       }
-      // cumulative count of this lane's writer at bin s2
-      auto cumw = [&](int s2) -> uint32_t {
-        if (lane >= a.Wg || s2 < lw) return 0u;
-        if (ow) {
-          const CohBuf fbuf(a.full + ((int64_t)unit * kMaxWg + lane) * a.full_words, a.full_words * 4);
-          return (fbuf.ld4((s2 >> 1) * 4) >> ((s2 & 1) * 16)) & 0xFFFFu;
-        }
-        const int j = s2 - lw;
-        return j >= ln ? (uint32_t)topc : (uint32_t)ent[j];
-      };
+      hdr4[lane] = make_int4(lw, ln, topc, ow ? 1 : 0);
+      if (a.xcd_local) {
+        // the plain-store exchange needs every writer on this XCD
+        const uint32_t own = (uint32_t)__builtin_amdgcn_s_getreg(kXccIdReg) & 0xFu;
+        const uint32_t wx = (lane < a.Wg)
+            ? (reinterpret_cast<const uint32_t*>(winb + lane * kWinBytes)[3] & 0xFFFFu) : own;
+        if (__ballot(wx != own) && lane == 0) atomicOr(a.err, 4u);
+      }
       // T cannot exceed any workgroup's own k-th smallest score
       const int tmin = wave_min_i((lane < a.Wg && hw) ? tw : NB - 1);
       const int glo = min(wave_min_i(lw), tmin);
-      // binary search: C(lo2) < k <= C(hi2)
-      int lo2 = glo - 1, hi2 = tmin;
-      if (wave_sum_u32(cumw(tmin)) >= (uint32_t)k) {
-        while (hi2 - lo2 > 1) {
-          const int mid = (lo2 + hi2) >> 1;
-          if (wave_sum_u32(cumw(mid)) >= (uint32_t)k) hi2 = mid; else lo2 = mid;
-        }
+      const bool any_ow = __ballot(ow) != 0;
+      if (lane == 0) { misc[16] = (uint32_t)glo; misc[17] = (uint32_t)tmin; misc[18] = any_ow ? 1u : 0u; }
+    }
+    __syncthreads();
+    const bool any_ow = misc[18] != 0;
+    // cumulative count of writer ww at bin s2 (0 below its window, the
+    // window's last count past its end); an overflowing window is read from
+    // the writer's full cumulative histogram instead
+    auto win_count = [&](const int4 hd, int ww, int s2) -> uint32_t {
+      const int j = s2 - hd.x;
+      const uint16_t* ent = reinterpret_cast<const uint16_t*>(winb + ww * kWinBytes) + kWinHdr;
+      const uint32_t v = ent[min(max(j, 0), kWinCap - 1)];
+      // branch-free select keeps the entry reads of several writers in flight
+      const uint32_t below = (uint32_t)(j >> 31);  // all ones when j < 0
+      const uint32_t past = (uint32_t)((hd.y - 1 - j) >> 31);  // all ones when j >= ln
+      return ((v & ~past) | ((uint32_t)hd.z & past)) & ~below;
+    };
+    auto cumw = [&](int ww, int s2) -> uint32_t {
+      const int4 hd = hdr4[ww];
+      if (any_ow && hd.w) {
+        const CohBuf fbuf(a.full + ((int64_t)unit * kMaxWg + ww) * a.full_words, a.full_words * 4);
+        const int sc2 = min(max(s2, 0), NB - 1);
+        const uint32_t v = (fbuf.ld4((sc2 >> 1) * 4) >> ((sc2 & 1) * 16)) & 0xFFFFu;
+        return s2 < hd.x ? 0u : v;
       }
-      const int Tw = hi2;
-      const uint32_t l1 = Tw > 0 ? cumw(Tw - 1) : 0u;
-      const uint32_t e1 = cumw(Tw) - l1;
+      return win_count(hd, ww, s2);
+    };
+    // T = smallest s in [glo, tmin] with C(s) = sum of the writers' counts
+    // >= k, else tmin.  Bins are tried 64 at a time (lane = bin), each wave
+    // summing every 4th writer; every wave then forms the same totals.
+    const int glo = (int)misc[16], tmin = (int)misc[17];
+    int Tw = tmin;
+    const int nper = (a.Wg + 3) / 4;
+    for (int c0 = glo, rnd = 0; c0 <= tmin; c0 += 64, ++rnd) {
+      const int s2 = c0 + lane;
+      // writers wv, wv+4, ... in groups of 8 (unused header slots count 0)
+      uint32_t part = 0;
+      if (!any_ow) {
+        for (int i0 = 0; i0 < nper; i0 += 8) {
+          int4 hd[8];
+#pragma unroll
+          for (int u = 0; u < 8; ++u) hd[u] = hdr4[wv + 4 * (i0 + u)];
+#pragma unroll
+          for (int u = 0; u < 8; ++u) part += win_count(hd[u], wv + 4 * (i0 + u), s2);
+        }
+      } else {
+        for (int i = 0; i < nper; ++i) part += cumw(wv + 4 * i, s2);
+      }
+      uint32_t* cp = cpart + (rnd & 1) * 256;
+      cp[wv * 64 + lane] = part;
+      __syncthreads();
+      const uint32_t C = cp[lane] + cp[64 + lane] + cp[128 + lane] + cp[192 + lane];
+      const uint64_t hit = __ballot(C >= (uint32_t)k && s2 <= tmin);
+      if (hit) {
+        Tw = c0 + (int)__builtin_ctzll(hit);
+        break;
+      }
+    }
+    if (wv == 0) {
+      const uint32_t l1 = (lane < a.Wg && Tw > 0) ? cumw(lane, Tw - 1) : 0u;
+      const uint32_t e1 = (lane < a.Wg) ? cumw(lane, Tw) - l1 : 0u;
       const uint32_t il = wave_incl_scan_u32(l1);
       const uint32_t ie = wave_incl_scan_u32(e1);
       if (lane == w) { misc[6] = il - l1; misc[7] = ie - e1; misc[3] = e1; }
@@ -602,11 +662,11 @@ __global__ __launch_bounds__(kNT) void decode_step_kernel(const StepArgs a) {
     u32x4 v4;
     v4.x = __float_as_uint(f[0]); v4.y = __float_as_uint(f[1]);
     v4.z = __float_as_uint(f[2]); v4.w = __float_as_uint(f[3]);
-    pbuf.st16((w * C::RECP + 4 * c) * 4, v4);
+    pbuf.st16x((w * C::RECP + 4 * c) * 4, v4, a.xcd_local);
   }
   wait_all_mem();
   __syncthreads();
-  if (t == 0) st_agent(a.flags + (int64_t)unit * kMaxWg + w, epoch + 2);
+  if (t == 0) CohBuf(a.flags + (int64_t)unit * kMaxWg, kMaxWg * 4).st4x(w * 4, epoch + 2, a.xcd_local);
   wait_unit(a, unit, epoch + 2);
 
   // slice [e0, e1) of the G*128 outputs, a multiple of 4 wide
@@ -668,6 +728,56 @@ __global__ __launch_bounds__(kNT) void decode_step_kernel(const StepArgs a) {
   if (w == 0 && t >= a.Wg && t < kMaxWg)
     st_agent(a.flags + (int64_t)unit * kMaxWg + t, epoch + 2);
   write_idx();
+}
+
+__global__ void xcc_probe_kernel(uint32_t* out) {
+  if (threadIdx.x == 0) out[blockIdx.x] = (uint32_t)__builtin_amdgcn_s_getreg(kXccIdReg) & 0xFu;
+}
+
+// Whether the workgroups of a launch whose indices agree mod 8 share an XCD
+// (the 8 classes on 8 different XCDs) on the current device, checked once
+// per device with a 2048-workgroup probe launch (not while `user` is being
+// captured: then the answer is "no" for this call only).  The dispatcher
+// deals workgroups round-robin over the XCDs; where the round starts may
+// differ between launches, so only the classes are relied on.
+bool xcd_round_robin(hipStream_t user) {
+  constexpr int kDevs = 64, kBlocks = 2048;
+  static std::mutex mu;
+  static int state[kDevs] = {0};  // 0 unknown, 1 verified, 2 differs
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kDevs) {
+    (void)hipGetLastError();
+    return false;
+  }
+  std::lock_guard<std::mutex> lk(mu);
+  if (state[dev]) return state[dev] == 1;
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(user, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone) {
+    (void)hipGetLastError();
+    return false;
+  }
+  bool ran = false, ok = true;
+  uint32_t* d = nullptr;
+  hipStream_t ps = nullptr;
+  if (hipStreamCreateWithFlags(&ps, hipStreamNonBlocking) == hipSuccess &&
+      hipMalloc(reinterpret_cast<void**>(&d), kBlocks * sizeof(uint32_t)) == hipSuccess) {
+    hipLaunchKernelGGL(xcc_probe_kernel, dim3(kBlocks), dim3(64), 0, ps, d);
+    std::vector<uint32_t> h(kBlocks);
+    if (hipGetLastError() == hipSuccess &&
+        hipMemcpyAsync(h.data(), d, kBlocks * sizeof(uint32_t), hipMemcpyDeviceToHost, ps) == hipSuccess &&
+        hipStreamSynchronize(ps) == hipSuccess) {
+      ran = true;
+      for (int i = 0; i < kBlocks; ++i) ok = ok && h[i] == h[i & 7];
+      for (int i = 0; i < 8; ++i)
+        for (int j = 0; j < i; ++j) ok = ok && h[i] != h[j];
+    }
+  }
+  if (d) (void)hipFree(d);
+  if (ps) (void)hipStreamDestroy(ps);
+  (void)hipGetLastError();
+  if (!ran) return false;  // not cached: tried again on a later call
+  state[dev] = ok ? 1 : 2;
+  return ok;
 }
 
 }  // namespace
@@ -756,6 +866,7 @@ hipError_t launch_decode_step(const StepPlan& p, const uint16_t* q, const uint16
   a.q = q; a.K = K; a.V = V; a.W = W; a.codes = codes; a.seq_lens = seq_lens;
   a.out = out; a.idx_out = idx_out; a.cap = cap; a.Hq = Hq; a.Hkv = Hkv; a.k = k;
   a.scale = scale; a.Wg = p.Wg; a.chunk = p.chunk; a.xcd_map = p.xcd_map; a.U = p.U;
+  a.xcd_local = (p.xcd_map && p.Wg > 1 && xcd_round_robin(s)) ? 1 : 0;
   a.err = reinterpret_cast<uint32_t*>(ws + p.off_err);
   a.flags = reinterpret_cast<uint32_t*>(ws + p.off_flags);
   a.win = p.Wg > 1 ? reinterpret_cast<uint32_t*>(ws + p.off_win) : nullptr;

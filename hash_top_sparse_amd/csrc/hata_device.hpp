@@ -57,6 +57,17 @@ struct CohBuf {
   __device__ __forceinline__ void st16(uint32_t off, u32x4 v) const {
     __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)off, 0, kSC1);
   }
+  // Stores for an exchange whose readers all run on the writer's XCD: a
+  // plain store lands in that XCD's L2, where the readers' sc1 loads find it
+  // (it is not written through to memory, so the ack comes sooner).
+  __device__ __forceinline__ void st16x(uint32_t off, u32x4 v, bool xcd_local) const {
+    if (xcd_local) __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)off, 0, 0);
+    else __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)off, 0, kSC1);
+  }
+  __device__ __forceinline__ void st4x(uint32_t off, uint32_t v, bool xcd_local) const {
+    if (xcd_local) __builtin_amdgcn_raw_buffer_store_b32(v, r, (int)off, 0, 0);
+    else __builtin_amdgcn_raw_buffer_store_b32(v, r, (int)off, 0, kSC1);
+  }
   __device__ __forceinline__ uint32_t ld4(uint32_t off) const {
     return __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, kSC1);
   }

@@ -190,7 +190,9 @@ int hata_workspace_reset(void* ws, size_t ws_bytes, void* stream);
 /*
  * Synchronise `stream` and read the workspace's device-side error word:
  * *err_out = 0 if no kernel reported a problem since the last reset, else a
- * bit set (1 = a cross-workgroup wait gave up after its spin limit).
+ * bit set (1 = a cross-workgroup wait gave up after its spin limit;
+ * 4 = workgroups of one hata_decode_step unit ran on different XCDs,
+ * against the placement a once-per-device check had shown).
  * Diagnostic only; never needed on the hot path.
  */
 int hata_workspace_check(const void* ws, size_t ws_bytes, int* err_out,
