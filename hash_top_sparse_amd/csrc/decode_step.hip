@@ -77,8 +77,9 @@ struct Cfg {
   static constexpr int RED = (RED0 > (G + 4) * kRec) ? RED0 : (G + 4) * kRec;
   // LDS offsets in bytes
   static constexpr int o_hist = 0;                               // NBP uint32
-  static constexpr int o_qf = o_hist + NBP * 4;                  // (G+1)*128 float
-  static constexpr int o_red = o_qf + (G + 1) * kD * 4;          // RED float
+  static constexpr int NSTG = (G + 1 + 3) / 4;                   // staging loads per thread
+  static constexpr int o_qf = o_hist + NBP * 4;                  // 4*NSTG rows of 128 float (G+1 used)
+  static constexpr int o_red = o_qf + 4 * NSTG * kD * 4;         // RED float
   static constexpr int o_qcode = o_red + RED * 4;                // (G+1)*2 uint64
   static constexpr int o_misc = o_qcode + (G + 1) * 16;          // 64 uint32
   static constexpr int o_whdr = o_misc + 64 * 4;                 // kMaxWg int4 + 2*4*64 uint32
@@ -205,6 +206,28 @@ __global__ __launch_bounds__(kNT) void decode_step_kernel(const StepArgs a) {
   const int b = unit / a.Hkv, h = unit - b * a.Hkv;
   const int64_t cap = a.cap;
   const int k = a.k;
+  const int64_t row0 = ((int64_t)b * a.Hkv + h) * cap;
+
+  // ---- 1. loads.  The query rows, W_H and this workgroup's flag do not
+  // depend on the sequence length, so they are issued before it is read;
+  // then the appended key row, the code-cache ring and the exchange lines.
+  // Every load here is unconditional (clamped to a valid row, or to a
+  // zero-size buffer that returns 0), so the compiler can count the loads in
+  // flight exactly and wait for the early ones without draining the ring.
+  // staging slot i of thread t holds dword (t + 256 i) % 64 of row (t + 256 i) / 64
+  uint32_t xrow[C::NSTG];
+#pragma unroll
+  for (int i = 0; i < C::NSTG; ++i) {
+    const int e = t + i * kNT;
+    const int r = min(e >> 6, G - 1), c2 = e & 63;
+    xrow[i] = 0;
+    if (i * kNT < 64 * G)  // slots that hold query rows (known at compile time)
+      xrow[i] = reinterpret_cast<const uint32_t*>(a.q + ((int64_t)b * a.Hq + (int64_t)h * G + r) * kD)[c2];
+  }
+  WRegs wr;
+  load_w_regs(a.W + (int64_t)h * kD * kR, wr);
+  const uint32_t epoch =
+      CohBuf(a.flags + (int64_t)unit * kMaxWg, a.Wg > 1 ? kMaxWg * 4 : 0).ld4(w * 4);
   const int n = a.seq_lens[b];
   if (n < 1 || (int64_t)n > cap) {
     // invalid length: every workgroup of the unit leaves here, so the unit's
@@ -217,52 +240,52 @@ __global__ __launch_bounds__(kNT) void decode_step_kernel(const StepArgs a) {
     }
     return;
   }
-  const int64_t row0 = ((int64_t)b * a.Hkv + h) * cap;
   const int lo = w * a.chunk;
   const int cnt = max(0, min(n, lo + a.chunk) - lo);
   const bool owns_new = (n - 1 >= lo) && (n - 1 < lo + cnt);
   const int new_li = n - 1 - lo;
-
-  // ---- 1. loads: the new rows, W_H, then the code-cache ring
   const int nrows = G + (owns_new ? 1 : 0);
-  uint32_t xrow[(G + 1 + 3) / 4];
-#pragma unroll
-  for (int i = 0; i < (G + 1 + 3) / 4; ++i) {
-    const int e = t + i * kNT;
-    const int r = e >> 6, c2 = e & 63;
-    xrow[i] = 0;
-    if (r < nrows) {
-      const uint32_t* src = (r < G)
-          ? reinterpret_cast<const uint32_t*>(a.q + ((int64_t)b * a.Hq + (int64_t)h * G + r) * kD)
-          : reinterpret_cast<const uint32_t*>(a.K + (row0 + n - 1) * kD);
-      xrow[i] = src[c2];
-    }
-  }
-  WRegs wr;
-  load_w_regs(a.W + (int64_t)h * kD * kR, wr);
-  uint32_t epoch = 0;
-  if (a.Wg > 1 && wv == 0) {
-    const CohBuf fb(a.flags + (int64_t)unit * kMaxWg, kMaxWg * 4);
-    epoch = fb.ld4(w * 4);
-  }
-  const uint4* cbase = reinterpret_cast<const uint4*>(a.codes) + row0 + lo;
+  // row n-1 of K (row 0 when this workgroup does not own it): dword `lane`
+  const uint32_t krow = reinterpret_cast<const uint32_t*>(a.K + (row0 + (owns_new ? n - 1 : 0)) * kD)[lane];
+  // ring slots past cnt reload this workgroup's last row (row 0 if it has none)
+  const uint4* cbase = reinterpret_cast<const uint4*>(a.codes) + row0 + (cnt > 0 ? lo : 0);
+  const int clast = max(cnt - 1, 0);
   uint4 cbuf[PF];
 #pragma unroll
-  for (int j = 0; j < PF; ++j) {
-    const int li = j * kNT + t;
-    cbuf[j] = make_uint4(0, 0, 0, 0);
-    if (li < cnt) cbuf[j] = load_stream16(cbase + li);
+  for (int j = 0; j < PF; ++j) cbuf[j] = load_stream16(cbase + min(j * kNT + t, clast));
+  // This workgroup's exchange lines (its histogram window and its partial
+  // record) have usually left L2 since the previous step; the unit's first
+  // reads of them after the flag take about 1 us then, against about 0.4 us
+  // when the lines were loaded into L2 before this workgroup stores to them
+  // (measured at 128K), so they are loaded here.  The values are consumed
+  // only at the end of the kernel, so no wait is placed on these loads.
+  uint32_t warm;
+  {
+    // one buffer over [win, end of the partial records); wave 0 touches the
+    // window's 2 lines, the other waves the record's lines.  With one
+    // workgroup per unit there is no exchange: a zero-size buffer.
+    constexpr int plines = (C::RECP * 4 + 127) / 128 + 1;
+    const bool ex = a.Wg > 1;
+    const char* wbase = ex ? reinterpret_cast<const char*>(a.win) : reinterpret_cast<const char*>(a.err);
+    const uint32_t part_off = ex ? (uint32_t)(reinterpret_cast<const char*>(a.part) - wbase) : 0u;
+    const uint32_t span = ex ? part_off + (uint32_t)a.U * kMaxWg * C::RECP * 4 : 0u;
+    const uint32_t woff = (uint32_t)(unit * kMaxWg + w) * kWinBytes + (t & 1) * 128;
+    const uint32_t rec0 = (uint32_t)(unit * kMaxWg + w) * C::RECP * 4;
+    const uint32_t poff = part_off + min(rec0 / 128 * 128 + (uint32_t)(t % plines) * 128,
+                                         (uint32_t)(unit * kMaxWg + kMaxWg) * C::RECP * 4 - 4);
+    warm = CohBuf(wbase, span).ld4(wv == 0 ? woff : poff);
   }
 
-  // ---- 2. encode the query rows (+ the new key row)
+  // ---- 2. encode the query rows (+ the new key row).  Every slot is
+  // stored (rows past G are zero and never read), so no load is consumed
+  // under a branch.
 #pragma unroll
-  for (int i = 0; i < (G + 1 + 3) / 4; ++i) {
+  for (int i = 0; i < C::NSTG; ++i) {
     const int e = t + i * kNT;
     const int r = e >> 6, c2 = e & 63;
-    if (r <= G) {
-      qf[r * kD + 2 * c2] = bf16_lo(xrow[i]);
-      qf[r * kD + 2 * c2 + 1] = bf16_hi(xrow[i]);
-    }
+    const uint32_t v = (r < G) ? xrow[i] : ((r == G) ? krow : 0u);  // lane == c2 for row G
+    qf[r * kD + 2 * c2] = bf16_lo(v);
+    qf[r * kD + 2 * c2 + 1] = bf16_hi(v);
   }
   for (int i = t; i < C::NBP; i += kNT) hist[i] = 0;
   if (t < 64) misc[t] = (t < 3) ? (uint32_t)NB : 0u;
@@ -723,6 +746,7 @@ __global__ __launch_bounds__(kNT) void decode_step_kernel(const StepArgs a) {
       if (sub16 == 0) outp[e0 + eo] = (Ls > 0.f) ? A / Ls : 0.f;
     }
   }
+  if (warm == 0x9E3779B9u && k < 0) a.err[1] = warm;  // keeps the exchange-line loads
   // keep every flag slot of the unit equal for the next launch (which may
   // use a different number of workgroups per unit)
   if (w == 0 && t >= a.Wg && t < kMaxWg)
