@@ -715,34 +715,35 @@ __global__ __launch_bounds__(kNT) void decode_step_kernel(const StepArgs a) {
   }
   __syncthreads();
   const float* stage = reinterpret_cast<const float*>(winb);
-  // rescale factor of every writer for the (at most two) heads of the slice,
-  // computed once: fac[h2][ww] = exp(M_ww - M) with M the max over writers
-  // and the head's rescaled sum of L, Lsum[h2] = sum_ww L_ww * fac[h2][ww]
-  float* fac = red;  // [2][kMaxWg] then Lsum[2]; red is free again
-  const int ga = e0 / kD, gb = (e1 - 1) / kD;  // first and last head of the slice
-  if (wv < 2 && e0 < e1) {
-    const int g = wv == 0 ? ga : gb;
-    const float Mw = (lane < a.Wg) ? stage[lane * nch * 4 + g] : -INFINITY;
-    const float M = pair32_max(pair16_max(row16_max_f(Mw)));
-    const float f = (lane < a.Wg && M != -INFINITY) ? __expf(Mw - M) : 0.f;
-    fac[wv * kMaxWg + lane] = f;
-    const float Lw = (lane < a.Wg) ? stage[lane * nch * 4 + G + g] * f : 0.f;
-    const float Ls = pair32_sum(pair16_sum(sum16(Lw)));
-    if (lane == 0) fac[2 * kMaxWg + wv] = Ls;
-  }
-  __syncthreads();
+  // Output e0 + eo is formed by one row of 16 lanes; lane j takes writers
+  // j, j+16, j+32, j+48.  The row finds its head's maximum M over the
+  // writers, rescales each writer's L and accumulator by exp(M_w - M) and
+  // adds them in a fixed order (per lane, then across the row).
   {
-    // output e0 + eo is summed by the 16 lanes of one row, writer ww by lane
-    // ww % 16, then added across the row in a fixed order
     const int sub16 = t & 15, nout = e1 - e0;
     for (int eo = t >> 4; eo < nout; eo += kNT / 16) {
-      const int g = (e0 + eo) / kD, h2 = (g == ga) ? 0 : 1;
-      const float* f = fac + h2 * kMaxWg;
-      float A = 0.f;
-      for (int ww = sub16; ww < a.Wg; ww += 16)
-        A = fmaf(stage[ww * nch * 4 + C::HDRP + eo], f[ww], A);
+      const int g = (e0 + eo) / kD;
+      float mw[kMaxWg / 16];
+      float Mloc = -INFINITY;
+#pragma unroll
+      for (int q = 0; q < kMaxWg / 16; ++q) {
+        const int ww = sub16 + 16 * q;
+        mw[q] = (ww < a.Wg) ? stage[ww * nch * 4 + g] : -INFINITY;
+        Mloc = fmaxf(Mloc, mw[q]);
+      }
+      const float M = row16_max_f(Mloc);
+      float Ls = 0.f, A = 0.f;
+#pragma unroll
+      for (int q = 0; q < kMaxWg / 16; ++q) {
+        const int ww = sub16 + 16 * q;
+        if (ww < a.Wg && mw[q] != -INFINITY) {
+          const float f = __expf(mw[q] - M);
+          Ls = fmaf(stage[ww * nch * 4 + G + g], f, Ls);
+          A = fmaf(stage[ww * nch * 4 + C::HDRP + eo], f, A);
+        }
+      }
+      Ls = sum16(Ls);
       A = sum16(A);
-      const float Ls = fac[2 * kMaxWg + h2];
       if (sub16 == 0) outp[e0 + eo] = (Ls > 0.f) ? A / Ls : 0.f;
     }
   }
