@@ -228,18 +228,14 @@ __global__ __launch_bounds__(kNT) void decode_step_kernel(const StepArgs a) {
   load_w_regs(a.W + (int64_t)h * kD * kR, wr);
   const uint32_t epoch =
       CohBuf(a.flags + (int64_t)unit * kMaxWg, a.Wg > 1 ? kMaxWg * 4 : 0).ld4(w * 4);
-  const int n = a.seq_lens[b];
-  if (n < 1 || (int64_t)n > cap) {
-    // invalid length: every workgroup of the unit leaves here, so the unit's
-    // flags stay consistent; workgroup 0 clears the outputs
-    if (w == 0) {
-      for (int e = t; e < G * kD; e += kNT)
-        a.out[((int64_t)b * a.Hq + (int64_t)h * G) * kD + e] = 0.f;
-      if (a.idx_out)
-        for (int j = t; j < k; j += kNT) a.idx_out[(int64_t)unit * k + j] = -1;
-    }
-    return;
-  }
+  // An invalid length is handled after the projection (below); until then
+  // the length is clamped into [1, cap] so that every address is valid and
+  // no branch stands between the loads above and their issue.
+  // keep the loads above ahead of the length read in the issued code
+  __builtin_amdgcn_sched_barrier(0);
+  const int n_in = a.seq_lens[b];
+  const bool bad_len = n_in < 1 || (int64_t)n_in > cap;
+  const int n = bad_len ? 1 : n_in;
   const int lo = w * a.chunk;
   const int cnt = max(0, min(n, lo + a.chunk) - lo);
   const bool owns_new = (n - 1 >= lo) && (n - 1 < lo + cnt);
@@ -291,6 +287,18 @@ __global__ __launch_bounds__(kNT) void decode_step_kernel(const StepArgs a) {
   if (t < 64) misc[t] = (t < 3) ? (uint32_t)NB : 0u;
   __syncthreads();
   project_pack<G + 1>(wr, qf, red, qcode, nrows);
+  if (bad_len) {
+    // invalid length: every workgroup of the unit leaves here, before any
+    // exchange, so the unit's flags stay consistent; workgroup 0 clears the
+    // outputs
+    if (w == 0) {
+      for (int e = t; e < G * kD; e += kNT)
+        a.out[((int64_t)b * a.Hq + (int64_t)h * G) * kD + e] = 0.f;
+      if (a.idx_out)
+        for (int j = t; j < k; j += kNT) a.idx_out[(int64_t)unit * k + j] = -1;
+    }
+    return;
+  }
   uint4 newc = make_uint4(0, 0, 0, 0);
   if (owns_new) {
     const uint64_t k0 = qcode[G * 2], k1 = qcode[G * 2 + 1];
