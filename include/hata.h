@@ -160,6 +160,8 @@ int hata_sparse_decode(const void* q, const void* K, const void* V, int B,
  * idx_out is not NULL, idx_out [B][Hkv][k] holds the kept set exactly as
  * hata_topk reports it.  Results are bit-identical to the staged calls
  * (hata_encode_append, hata_hamming_scores, hata_topk) for codes and idx.
+ * A sequence whose length (read on the device) lies outside [1, cap] gets
+ * out = 0 and idx_out = -1 and its code rows are left unchanged.
  * ws: hata_workspace_bytes(HATA_OP_DECODE_STEP, ...), zeroed once before
  * first use.  Shapes whose per-unit scores do not fit on chip run the same
  * steps as separate kernels inside this call.

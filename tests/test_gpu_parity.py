@@ -216,6 +216,42 @@ def test_decode_step_matches_oracle(hata_gpu, case):
     assert_close(out.cpu().numpy(), ref_out)
 
 
+@pytest.mark.parametrize("B,Hq,Hkv,N,k", [(3, 32, 8, 4096, 256), (3, 4, 1, 3000, 64)])
+def test_decode_step_invalid_lengths(hata_gpu, B, Hq, Hkv, N, k):
+    """A sequence whose device-side length lies outside [1, cap] gets a zero
+    output and an all -1 kept set, and its code rows stay untouched; the
+    other sequences of the batch are unaffected (the units of such a sequence
+    leave before any exchange)."""
+    s = _shape(B, Hq, Hkv, N, k, seed=7950 + Hkv)
+    inp = synth.make_inputs(s)
+    d = Dev(inp)
+    _log(f"invalid-length case B{B} Hq{Hq} Hkv{Hkv} N{N} k{k}")
+    codes = gpu_build_cache(hata_gpu, d)
+    before = codes_np(codes).copy()
+    bad = {1: 0, 2: d.cap + 7}
+    seq = d.seq.clone()
+    for b, n in bad.items():
+        seq[b] = n
+    ws = hata_gpu.alloc_workspace(hata_gpu.OP_DECODE_STEP, B, Hq, Hkv, d.max_len, k)
+    out = torch.full((B, Hq, 128), np.nan, dtype=torch.float32, device="cuda")
+    idx = torch.full((B, Hkv, k), -9, dtype=torch.int32, device="cuda")
+    hata_gpu.decode_step(d.q, d.K, d.V, d.W, codes, seq, d.max_len, k, inp.scale, out, ws, idx)
+    torch.cuda.synchronize()
+    assert hata_gpu.workspace_check(ws) == 0
+    got_out, got_idx, cn = out.cpu().numpy(), idx.cpu().numpy(), codes_np(codes)
+    G = Hq // Hkv
+    for b in bad:
+        assert (got_out[b] == 0).all()
+        assert (got_idx[b] == -1).all()
+        np.testing.assert_array_equal(cn[b], before[b])
+    qc = codes_np(gpu_query_codes(hata_gpu, d))
+    units = [(0, h) for h in range(Hkv)]
+    _, ref_idx, ref_out = oracle_units(inp, qc, cn, units=units)
+    np.testing.assert_array_equal(got_idx[0], ref_idx[0])
+    assert_close(got_out[0], ref_out[0])
+    assert G * Hkv == Hq
+
+
 def test_decode_step_equals_staged_path(hata_gpu):
     B, Hq, Hkv, N, k = 2, 32, 8, 6000, 512
     s = _shape(B, Hq, Hkv, N, k, seed=7800, needles=16)
