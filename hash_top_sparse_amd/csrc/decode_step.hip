@@ -61,7 +61,7 @@ constexpr uint32_t kSpinLimit = 1u << 22;
 // s_getreg operand for HW_REG_XCC_ID (register 20, bits 0..31): the XCD the
 // wave runs on
 constexpr int kXccIdReg = 20 | (31 << 11);
-constexpr int kShortList = 64;     // kept rows staged in LDS, waves assigned to heads
+constexpr int kShortList = 64;     // kept rows staged in LDS per attention batch
 
 template <int G>
 struct Cfg {
@@ -613,44 +613,11 @@ __global__ __launch_bounds__(kNT) void decode_step_kernel(const StepArgs a) {
   const int m_self = min(k, (int)(tot_lt + min(tot_eq, take_self)));
   __syncthreads();
 
-  // ---- 6. gather-fused attention over the kept rows; a short list is
-  // processed with waves assigned to heads (no cross-wave merge), a long one
-  // with row groups spread over all waves
-  const int sub = t & 15;
-  const uint16_t* Kb = a.K + row0 * kD + sub * 8;
-  const uint16_t* Vb = a.V + row0 * kD + sub * 8;
-  if (m_self <= kShortList) {
-    attend_heads<G, kShortList>(qf, sel, m_self, n, a.K + row0 * kD, a.V + row0 * kD, a.scale, red,
-                                reinterpret_cast<uint4*>(kvs));
-  } else {
-    const int slot = t >> 4;
-    float qreg[G][8];
-#pragma unroll
-    for (int g = 0; g < G; ++g)
-#pragma unroll
-      for (int c = 0; c < 8; ++c) qreg[g][c] = qf[g * kD + sub * 8 + c];
-    SoftmaxState<G> st;
-    st.init();
-    constexpr int UN = 2;
-    for (int r0 = slot; r0 < m_self; r0 += 16 * UN) {
-      uint4 kv[UN], vv[UN];
-      bool valid[UN];
-#pragma unroll
-      for (int u = 0; u < UN; ++u) {
-        const int r = r0 + 16 * u;
-        valid[u] = r < m_self;
-        kv[u] = make_uint4(0, 0, 0, 0);
-        vv[u] = make_uint4(0, 0, 0, 0);
-        if (valid[u]) {
-          const int64_t tok = min(max(sel[r], 0), n - 1);
-          kv[u] = *reinterpret_cast<const uint4*>(Kb + tok * kD);
-          vv[u] = *reinterpret_cast<const uint4*>(Vb + tok * kD);
-        }
-      }
-      attend_block<G, UN>(st, qreg, kv, vv, valid, a.scale);
-    }
-    merge_wg<G>(st, red);
-  }
+  // ---- 6. gather-fused attention over the kept rows (batches of
+  // kShortList rows staged in LDS, the next batch's loads in flight while a
+  // batch is used; waves assigned to heads)
+  attend_heads<G, kShortList>(qf, sel, m_self, n, a.K + row0 * kD, a.V + row0 * kD, a.scale, red,
+                              reinterpret_cast<uint4*>(kvs));
 
   // kept indices, written once the attention no longer needs the LDS list
   // (coalesced, and no barrier waits on these stores)

@@ -447,43 +447,43 @@ __device__ __forceinline__ void merge_wg(const SoftmaxState<G>& st, float* red) 
   __syncthreads();
 }
 
-// Attention over a short list of kept rows (m <= MAXR) with waves assigned
-// to heads.  The m K/V rows are first staged in LDS by the whole workgroup
-// (one round of 16-byte loads, at most MAXR*32/256 per thread); then for
-// G >= 4 wave wv owns heads [wv*G/4, (wv+1)*G/4) over every row, and for
-// G < 4 the 4/G waves of a head split the rows.  Within a wave the 4 groups
-// of 16 lanes take rows in turn (8 channels per lane).  Each wave merges only
-// its own heads (permlane swaps), so no cross-wave merge is needed for G >= 4.
-// kvs: LDS of MAXR * 512 bytes.  Writes red[g*kRec + {M, L, A[128]}] (red
-// holds at least (G + 4) * kRec floats); ends with __syncthreads.
+// Attention over the kept rows with waves assigned to heads.  Rows are taken
+// in batches of MAXR: a batch's K/V rows are staged in LDS by the whole
+// workgroup (16-byte loads, MAXR*32/256 per thread), and the next batch's
+// loads are issued into registers before the current batch is used, so they
+// are in flight meanwhile.  For G >= 4 wave wv owns heads
+// [wv*G/4, (wv+1)*G/4) over every row, and for G < 4 the 4/G waves of a head
+// split the rows.  Within a wave the 4 groups of 16 lanes take rows in turn
+// (8 channels per lane); the online-softmax state runs over all batches.
+// Each wave merges only its own heads (permlane swaps), so no cross-wave
+// merge is needed for G >= 4.  kvs: LDS of MAXR * 512 bytes.  Writes
+// red[g*kRec + {M, L, A[128]}] (red holds at least (G + 4) * kRec floats);
+// ends with __syncthreads.
 template <int G, int MAXR>
 __device__ __forceinline__ void attend_heads(const float* qf, const int32_t* sel, int m, int n,
                                              const uint16_t* K, const uint16_t* V, float scale,
                                              float* red, uint4* kvs) {
   constexpr int HPW = (G >= 4) ? G / 4 : 1;  // heads per wave
   constexpr int WPH = (G >= 4) ? 1 : 4 / G;  // waves per head
-  constexpr int LPT = MAXR * 32 / kNT;       // staging loads per thread
+  constexpr int LPT = MAXR * 32 / kNT;       // staging loads per thread and batch
   const int t = threadIdx.x, lane = t & 63, wv = t >> 6, rg = lane >> 4, sub = lane & 15;
-  // stage: row r occupies 32 chunks of 16 bytes (16 of K, then 16 of V)
-  {
-    uint4 v[LPT];
+  // row id of staging slot i of batch r0 (clamped into the list) and the load
+  auto gather = [&](int r0, uint4 (&v)[LPT]) {
+    const int mb = min(MAXR, m - r0);
+    int tokv[LPT];
+#pragma unroll
+    for (int i = 0; i < LPT; ++i) tokv[i] = sel[r0 + max(min((t >> 5) + 8 * i, mb - 1), 0)];
 #pragma unroll
     for (int i = 0; i < LPT; ++i) {
       const int c = t + i * kNT, r = c >> 5, part16 = c & 31;
       v[i] = make_uint4(0, 0, 0, 0);
-      if (r < m) {
-        const int64_t tok = min(max(sel[r], 0), n - 1);
+      if (r < mb) {
+        const int64_t tok = min(max(tokv[i], 0), n - 1);
         const uint16_t* src = (part16 < 16 ? K : V) + tok * kD + (part16 & 15) * 8;
         v[i] = *reinterpret_cast<const uint4*>(src);
       }
     }
-#pragma unroll
-    for (int i = 0; i < LPT; ++i) {
-      const int c = t + i * kNT;
-      if ((c >> 5) < m) kvs[c] = v[i];
-    }
-  }
-  __syncthreads();
+  };
   const int hg = wv / WPH, part = wv - hg * WPH;
   const int g0 = hg * HPW;
   float qreg[HPW][8];
@@ -495,21 +495,34 @@ __device__ __forceinline__ void attend_heads(const float* qf, const int32_t* sel
   st.init();
   constexpr int UN = 4;
   const int stride = 4 * WPH;
-  for (int r0 = part * 4 + rg; r0 < m; r0 += stride * UN) {
-    uint4 kv[UN], vv[UN];
-    bool valid[UN];
+  uint4 pv[LPT];
+  gather(0, pv);
+  for (int r0 = 0; r0 < m; r0 += MAXR) {
+    const int mb = min(MAXR, m - r0);
+    if (r0 > 0) __syncthreads();  // the previous batch is no longer read
 #pragma unroll
-    for (int u = 0; u < UN; ++u) {
-      const int r = r0 + u * stride;
-      valid[u] = r < m;
-      kv[u] = make_uint4(0, 0, 0, 0);
-      vv[u] = make_uint4(0, 0, 0, 0);
-      if (valid[u]) {
-        kv[u] = kvs[r * 32 + sub];
-        vv[u] = kvs[r * 32 + 16 + sub];
-      }
+    for (int i = 0; i < LPT; ++i) {
+      const int c = t + i * kNT;
+      if ((c >> 5) < mb) kvs[c] = pv[i];
     }
-    attend_block<HPW, UN>(st, qreg, kv, vv, valid, scale);
+    if (r0 + MAXR < m) gather(r0 + MAXR, pv);  // in flight while this batch is used
+    __syncthreads();
+    for (int rr = part * 4 + rg; rr < mb; rr += stride * UN) {
+      uint4 kv[UN], vv[UN];
+      bool valid[UN];
+#pragma unroll
+      for (int u = 0; u < UN; ++u) {
+        const int r = rr + u * stride;
+        valid[u] = r < mb;
+        kv[u] = make_uint4(0, 0, 0, 0);
+        vv[u] = make_uint4(0, 0, 0, 0);
+        if (valid[u]) {
+          kv[u] = kvs[r * 32 + sub];
+          vv[u] = kvs[r * 32 + 16 + sub];
+        }
+      }
+      attend_block<HPW, UN>(st, qreg, kv, vv, valid, scale);
+    }
   }
   float* tmp = red + G * kRec;  // [4 waves][kRec] when several waves share a head
 #pragma unroll
