@@ -108,10 +108,58 @@ def cpu_baseline(inp, budget_s: float) -> dict:
         if time.perf_counter() - t_start > budget_s or len(times) >= 50:
             break
     med = float(np.median(times))
+    # the same step on one host thread (two runs), and the oracle's encode of
+    # 16384 cached keys of one KV head (the prefill bulk encode's work per row)
+    t1 = []
+    for _ in range(2):
+        t0 = time.perf_counter()
+        oracle.decode_step(inp.q, inp.K, inp.V, inp.W, codes, inp.seq_lens, inp.k, inp.scale,
+                           nthreads=1)
+        t1.append(time.perf_counter() - t0)
+    rows = min(16384, cap)
+    t0 = time.perf_counter()
+    oracle.encode(inp.K[0, 0, :rows], inp.W[0])
+    enc_s = time.perf_counter() - t0
+    cpu_model = ""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                cpu_model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
     return {"value": 1.0 / med, "unit": "steps/s", "cores": threads, "kind": "oracle",
             "sample": (f"the whole step of this workload (all {B * Hkv} units, N={cap}, k={inp.k}); "
                        f"median of {len(times)} runs, {med * 1e3:.1f} ms each; code cache prebuilt "
-                       f"by the oracle outside the timing")}
+                       f"by the oracle outside the timing"),
+            "single_thread_steps_per_s": 1.0 / float(np.median(t1)),
+            "encode_keys_per_s_one_thread": rows / enc_s,
+            "cpu_model": cpu_model}
+
+
+def read_peak(gib: int = 4, reps: int = 5) -> float:
+    """HBM read rate (GB/s) of the library's streaming-read kernel over a
+    `gib` GiB buffer: best of `reps` passes, HIP events on the launch stream."""
+    import torch
+
+    from hash_top_sparse_amd import binding
+
+    src = torch.empty(gib << 30, dtype=torch.uint8, device="cuda")
+    src.fill_(7)
+    sink = torch.zeros(1024, dtype=torch.int64, device="cuda")
+    binding.stream_read(src, sink)
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    best = 0.0
+    for _ in range(reps):
+        ev0.record()
+        binding.stream_read(src, sink)
+        ev1.record()
+        torch.cuda.synchronize()
+        best = max(best, src.numel() / (ev0.elapsed_time(ev1) * 1e-3) / 1e9)
+    del src
+    torch.cuda.empty_cache()
+    return best
 
 
 def measure(cfg_id: int, steps: int, warmup: int, dense_steps: int, layers: int, use_graph: bool,
@@ -192,6 +240,18 @@ def measure(cfg_id: int, steps: int, warmup: int, dense_steps: int, layers: int,
         ev1.record()
         torch.cuda.synchronize()
     ms_step = ev0.elapsed_time(ev1) / steps
+    # spread of single eagerly launched steps (launch gap included), events
+    # around each step on the launch stream
+    nsp = min(200, steps)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(nsp + 1)]
+    evs[0].record()
+    for i in range(nsp):
+        step(i)
+        evs[i + 1].record()
+    torch.cuda.synchronize()
+    per = np.array([evs[i].elapsed_time(evs[i + 1]) * 1e3 for i in range(nsp)])
+    spread = {"steps": nsp, "median_us": float(np.median(per)), "p10_us": float(np.percentile(per, 10)),
+              "p90_us": float(np.percentile(per, 90))}
     err = binding.workspace_check(ws)
     if err:
         raise RuntimeError(f"workspace error word {err}: a cross-workgroup wait timed out")
@@ -221,8 +281,9 @@ def measure(cfg_id: int, steps: int, warmup: int, dense_steps: int, layers: int,
                  "speedup_of_hata": d_ms / ms_step}
         log(f"dense: {d_ms * 1e3:.1f} us/step, {dgb:.0f} GB/s, hata speedup {d_ms / ms_step:.2f}x")
     res = {"workload": shape.name, "ms_per_step": ms_step, "steps_per_s": 1000.0 / ms_step,
+           "tokens_per_s": B * 1000.0 / ms_step,
            "GBs": achieved, "frac_of_peak": achieved / PEAK_HBM_GBS, "bytes_per_step": per_step,
-           "layers": L, "dense": dense, "bulk_encode": bulk}
+           "layers": L, "eager_step_spread": spread, "dense": dense, "bulk_encode": bulk}
     del layer_bufs
     torch.cuda.empty_cache()
     return res, inp
@@ -281,6 +342,8 @@ def main() -> int:
                            not args.no_graph, with_bulk=False)
             sweep[str(c)] = r
 
+    peak_meas = read_peak()
+    log(f"streaming read of 4 GiB: {peak_meas:.0f} GB/s")
     cpu = None
     if not args.no_cpu:
         cpu = cpu_baseline(inp, args.cpu_budget)
@@ -308,7 +371,11 @@ def main() -> int:
         "roofline": {"bound": "hbm", "achieved": head["GBs"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": head["GBs"] / PEAK_HBM_GBS,
                      "traffic": profiled_traffic() if args.config == 4 else None,
-                     "kernel": f"decode_step_kernel<{shape.G}>", "bytes_per_launch": head["bytes_per_step"]},
+                     "kernel": f"decode_step_kernel<{shape.G}>", "bytes_per_launch": head["bytes_per_step"],
+                     "peak_measured": peak_meas, "frac_of_measured": head["GBs"] / peak_meas,
+                     "peak_measured_by": "hata_stream_read over 4 GiB, best of 5"},
+        "tokens_per_s": head["tokens_per_s"],
+        "eager_step_spread": head["eager_step_spread"],
         "cpu_baseline": cpu,
         "dense_baseline": head["dense"],
         "bulk_encode": head["bulk_encode"],

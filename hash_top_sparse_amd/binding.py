@@ -56,6 +56,7 @@ def load() -> ctypes.CDLL:
         "hata_workspace_bytes": ([I, I, I, I, I, I, I64, I], SZ),
         "hata_workspace_reset": ([P, SZ, P], I),
         "hata_workspace_check": ([P, SZ, ctypes.POINTER(I), P], I),
+        "hata_stream_read": ([P, SZ, P, SZ, P], I),
     }
     for name, (args, res) in sig.items():
         fn = getattr(L, name)
@@ -69,7 +70,8 @@ def exported_symbols() -> list[str]:
     return [n for n in ("hata_status_string", "hata_last_error_message", "hata_version",
                         "hata_encode_append", "hata_hamming_scores", "hata_topk",
                         "hata_sparse_decode", "hata_decode_step", "hata_dense_decode",
-                        "hata_workspace_bytes", "hata_workspace_reset", "hata_workspace_check")
+                        "hata_workspace_bytes", "hata_workspace_reset", "hata_workspace_check",
+                        "hata_stream_read")
             if hasattr(load(), n)]
 
 
@@ -178,6 +180,13 @@ def dense_decode(q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, seq_lens: to
     _check(load().hata_dense_decode(_ptr(q), _ptr(K), _ptr(V), B, Hq, Hkv, d, cap, _ptr(seq_lens),
                                     int(max_len), float(scale), _ptr(out), _ptr(ws), ws.numel(),
                                     _stream(stream)))
+
+
+def stream_read(src: torch.Tensor, sink: torch.Tensor, stream=None) -> None:
+    """Read all of `src` once (measurement of the HBM read rate); sink int64 [>= 1024]."""
+    _need(sink, torch.int64, "sink")
+    _check(load().hata_stream_read(_ptr(src), src.numel() * src.element_size(), _ptr(sink),
+                                   sink.numel(), _stream(stream)))
 
 
 def decode_step(q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, W_H: torch.Tensor,

@@ -223,6 +223,23 @@ int hata_dense_decode(const void* q, const void* K, const void* V, int B, int Hq
   return check_launch(e, "dense_decode launch");
 }
 
+int hata_stream_read(const void* src, size_t bytes, uint64_t* sink, size_t sink_words, void* stream) {
+  if (!src || !sink) return fail(HATA_ERR_NULL, "stream_read: null pointer");
+  if (!aligned(src, 16) || bytes % 16 != 0)
+    return fail(HATA_ERR_ALIGN, "stream_read: src must be 16-byte aligned and bytes a multiple of 16");
+  if (sink_words < (size_t)hata::stream_read_blocks())
+    return fail(HATA_ERR_WORKSPACE, "stream_read: sink of %d words needed, %zu given",
+                hata::stream_read_blocks(), sink_words);
+  int st = pre_launch("stream_read");
+  if (st) return st;
+  int cus = 0;
+  if ((st = current_cus(&cus))) return st;
+  // one workgroup per CU (as many as the sink holds)
+  const int blocks = cus < hata::stream_read_blocks() ? cus : hata::stream_read_blocks();
+  hipError_t e = hata::launch_stream_read(src, bytes, sink, blocks, reinterpret_cast<hipStream_t>(stream));
+  return check_launch(e, "stream_read launch");
+}
+
 int hata_decode_step(const void* q, const void* K, const void* V, const float* W_H, uint64_t* codes,
                      int B, int Hq, int Hkv, int d, int r, int64_t cap, const int32_t* seq_lens,
                      int64_t max_len, int k, float scale, float* out, int32_t* idx_out, void* ws,

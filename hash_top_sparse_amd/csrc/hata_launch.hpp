@@ -55,4 +55,8 @@ hipError_t launch_decode_step(const StepPlan& p, const uint16_t* q, const uint16
 
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s);
 
+// read-only streaming reduction (measurement of the device's HBM read rate)
+int stream_read_blocks();
+hipError_t launch_stream_read(const void* src, size_t bytes, uint64_t* sink, int blocks, hipStream_t s);
+
 }  // namespace hata

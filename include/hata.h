@@ -182,6 +182,20 @@ int hata_dense_decode(const void* q, const void* K, const void* V, int B,
                       const int32_t* seq_lens, int64_t max_len, float scale,
                       float* out, void* ws, size_t ws_bytes, void* stream);
 
+/*
+ * Measurement utility, not part of the decode path: read `bytes` of device
+ * memory at `src` once with streaming 16-byte loads (one workgroup per CU,
+ * each over a contiguous segment) and fold them into sink (one word per
+ * workgroup, at most 1024 words written; words past the CU count are left
+ * as they are, so a caller folding sink clears it first).
+ * Timing it gives the HBM read rate a plain kernel reaches on this device,
+ * against which the decode step's bytes/s can be compared besides the
+ * published peak.  src 16-byte aligned, bytes a multiple of 16; sink is a
+ * device buffer of sink_words >= 1024 uint64 (HATA_ERR_WORKSPACE if fewer).
+ */
+int hata_stream_read(const void* src, size_t bytes, uint64_t* sink,
+                     size_t sink_words, void* stream);
+
 /* Workspace bytes for operation `op` at these sizes (0 if none is needed). */
 size_t hata_workspace_bytes(int op, int B, int Hq, int Hkv, int d, int r,
                             int64_t max_len, int k);

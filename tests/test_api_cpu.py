@@ -140,6 +140,20 @@ def test_decode_step_validation():
     assert step(codes=MIS) == EALIGN
 
 
+def lib_stream_read_valid():
+    return binding.load().hata_stream_read(A, ctypes.c_size_t(4096), A, ctypes.c_size_t(1024), P(None))
+
+
+def test_stream_read_validation(lib):
+    SZ = ctypes.c_size_t
+    f = lib.hata_stream_read
+    assert f(P(None), SZ(4096), A, SZ(1024), P(None)) == ENULL
+    assert f(A, SZ(4096), P(None), SZ(1024), P(None)) == ENULL
+    assert f(MIS, SZ(4096), A, SZ(1024), P(None)) == EALIGN
+    assert f(A, SZ(4100), A, SZ(1024), P(None)) == EALIGN
+    assert f(A, SZ(4096), A, SZ(1023), P(None)) == EWS
+
+
 def test_forced_launch_failure_propagates():
     """With the test hook set, a fully valid call reports HATA_ERR_HIP before
     launching, and the binding raises it as HataError."""
@@ -149,6 +163,7 @@ def test_forced_launch_failure_propagates():
         assert "forced" in binding.last_error_message()
         assert _topk() == EHIP
         assert _enc() == EHIP
+        assert lib_stream_read_valid() == EHIP
         with pytest.raises(binding.HataError) as ei:
             binding._check(_ham())
         assert ei.value.status == EHIP

@@ -309,6 +309,19 @@ def test_decode_step_deterministic_and_workspace_reuse(hata_gpu):
         assert np.array_equal(i, runs[0][1]) and np.array_equal(c, runs[0][2])
 
 
+def test_stream_read_reads_every_word(hata_gpu):
+    """The read-stream measurement kernel folds every 32-bit word of the
+    buffer: the XOR of its 1024 workgroup words is the XOR of the buffer."""
+    rng = np.random.default_rng(11)
+    words = rng.integers(0, 2**32, size=(3 << 20) + 4, dtype=np.uint64).astype(np.uint32)
+    src = torch.from_numpy(words.view(np.int32)).cuda()
+    sink = torch.zeros(1024, dtype=torch.int64, device="cuda")
+    hata_gpu.stream_read(src, sink)
+    torch.cuda.synchronize()
+    got = np.bitwise_xor.reduce(sink.cpu().numpy().astype(np.uint64) & 0xFFFFFFFF)
+    assert int(got) == int(np.bitwise_xor.reduce(words))
+
+
 @pytest.mark.parametrize("dist", ["exact", "gauss"])
 def test_bulk_encode_matches_row_encode(hata_gpu, dist):
     """The matrix-core bulk path and the per-row path agree: bit-identical on
