@@ -613,11 +613,15 @@ __global__ __launch_bounds__(kNT) void decode_step_kernel(const StepArgs a) {
   const int m_self = min(k, (int)(tot_lt + min(tot_eq, take_self)));
   __syncthreads();
 
-  // ---- 6. gather-fused attention over the kept rows (batches of
+  // ---- 6. gather-fused attention over the kept rows (G > 1: batches of
   // kShortList rows staged in LDS, the next batch's loads in flight while a
-  // batch is used; waves assigned to heads)
-  attend_heads<G, kShortList>(qf, sel, m_self, n, a.K + row0 * kD, a.V + row0 * kD, a.scale, red,
-                              reinterpret_cast<uint4*>(kvs));
+  // batch is used, waves assigned to heads; G = 1: rows gathered straight
+  // into registers, three steps of 64 rows in flight)
+  if constexpr (G == 1)
+    attend_rows_g1<4, 3>(qf, sel, m_self, n, a.K + row0 * kD, a.V + row0 * kD, a.scale, red);
+  else
+    attend_heads<G, kShortList>(qf, sel, m_self, n, a.K + row0 * kD, a.V + row0 * kD, a.scale, red,
+                                reinterpret_cast<uint4*>(kvs));
 
   // kept indices, written once the attention no longer needs the LDS list
   // (coalesced, and no barrier waits on these stores)

@@ -447,6 +447,107 @@ __device__ __forceinline__ void merge_wg(const SoftmaxState<G>& st, float* red) 
   __syncthreads();
 }
 
+// End of the attention: merge the 4 row groups of each wave (permlane
+// swaps), then, when several waves share a head, the waves in fixed order
+// through LDS.  Writes red[g*kRec + {M, L, A[128]}]; ends with
+// __syncthreads.
+template <int G>
+__device__ __forceinline__ void finish_heads(const SoftmaxState<(G >= 4) ? G / 4 : 1>& st, float* red) {
+  constexpr int HPW = (G >= 4) ? G / 4 : 1;
+  constexpr int WPH = (G >= 4) ? 1 : 4 / G;
+  const int t = threadIdx.x, lane = t & 63, wv = t >> 6, rg = lane >> 4, sub = lane & 15;
+  const int hg = wv / WPH;
+  const int g0 = hg * HPW;
+  float* tmp = red + G * kRec;  // [4 waves][kRec] when several waves share a head
+#pragma unroll
+  for (int i = 0; i < HPW; ++i) {
+    const float M = pair32_max(pair16_max(st.m[i]));
+    const float f = (M == -INFINITY) ? 0.f : __expf(st.m[i] - M);
+    const float L = pair32_sum(pair16_sum(st.l[i] * f));
+    float A[8];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) A[c] = pair32_sum(pair16_sum(st.acc[i][c] * f));
+    if (rg == 0) {
+      float* r = (WPH == 1) ? red + (g0 + i) * kRec : tmp + wv * kRec;
+      if (sub == 0) { r[0] = M; r[1] = L; }
+#pragma unroll
+      for (int c = 0; c < 8; ++c) r[2 + sub * 8 + c] = A[c];
+    }
+  }
+  __syncthreads();
+  if (WPH > 1) {
+    // merge the WPH row partitions of each head in fixed order
+    for (int e = t; e < G * kD; e += kNT) {
+      const int g = e / kD, c = e % kD;
+      float M = -INFINITY;
+      for (int p = 0; p < WPH; ++p) M = fmaxf(M, tmp[(g * WPH + p) * kRec]);
+      float L = 0.f, A = 0.f;
+      if (M != -INFINITY) {
+        for (int p = 0; p < WPH; ++p) {
+          const float* r = tmp + (g * WPH + p) * kRec;
+          const float f = __expf(r[0] - M);
+          L = fmaf(r[1], f, L);
+          A = fmaf(r[2 + c], f, A);
+        }
+      }
+      float* o = red + g * kRec;
+      if (c == 0) { o[0] = M; o[1] = L; }
+      o[2 + c] = A;
+    }
+    __syncthreads();
+  }
+}
+
+
+// One query head per KV head: the 4 waves split the kept rows and no row is
+// used by two waves, so nothing is staged in LDS.  The 16 groups of 16 lanes
+// take rows grp, grp + 16, grp + 32, ... (grp = 4*wave + group within the
+// wave); each step covers UN rows of every group, and the loads of the next
+// NPF steps stay in flight in a register ring (NPF*UN*512 bytes per group).
+// Row ids past the list are clamped to its last row, so every load is issued
+// unconditionally (the compiler can count them exactly) and the extra rows
+// are masked out of the softmax.  Same output as attend_heads<1, ...>.
+template <int UN, int NPF>
+__device__ __forceinline__ void attend_rows_g1(const float* qf, const int32_t* sel, int m, int n,
+                                               const uint16_t* K, const uint16_t* V, float scale,
+                                               float* red) {
+  const int t = threadIdx.x, lane = t & 63, wv = t >> 6, rg = lane >> 4, sub = lane & 15;
+  const int grp = wv * 4 + rg;
+  float qreg[1][8];
+#pragma unroll
+  for (int c = 0; c < 8; ++c) qreg[0][c] = qf[sub * 8 + c];
+  SoftmaxState<1> st;
+  st.init();
+  const int nsteps = (m + 16 * UN - 1) / (16 * UN);
+  auto issue = [&](int step, uint4 (&kk)[UN], uint4 (&vv)[UN]) {
+    int tok[UN];
+#pragma unroll
+    for (int u = 0; u < UN; ++u) tok[u] = sel[max(min((step * UN + u) * 16 + grp, m - 1), 0)];
+#pragma unroll
+    for (int u = 0; u < UN; ++u) {
+      const int64_t off = (int64_t)min(max(tok[u], 0), n - 1) * kD + sub * 8;
+      kk[u] = *reinterpret_cast<const uint4*>(K + off);
+      vv[u] = *reinterpret_cast<const uint4*>(V + off);
+    }
+  };
+  uint4 kr[NPF][UN], vr[NPF][UN];
+#pragma unroll
+  for (int j = 0; j < NPF; ++j) issue(j, kr[j], vr[j]);
+  for (int s0 = 0; s0 < nsteps; s0 += NPF) {
+#pragma unroll
+    for (int j = 0; j < NPF; ++j) {
+      const int step = s0 + j;
+      if (step >= nsteps) break;
+      bool valid[UN];
+#pragma unroll
+      for (int u = 0; u < UN; ++u) valid[u] = (step * UN + u) * 16 + grp < m;
+      attend_block<1, UN>(st, qreg, kr[j], vr[j], valid, scale);
+      issue(step + NPF, kr[j], vr[j]);  // past the list: clamped, never used
+    }
+  }
+  finish_heads<1>(st, red);
+}
+
 // Attention over the kept rows with waves assigned to heads.  Rows are taken
 // in batches of MAXR: a batch's K/V rows are staged in LDS by the whole
 // workgroup (16-byte loads, MAXR*32/256 per thread), and the next batch's
@@ -524,44 +625,7 @@ __device__ __forceinline__ void attend_heads(const float* qf, const int32_t* sel
       attend_block<HPW, UN>(st, qreg, kv, vv, valid, scale);
     }
   }
-  float* tmp = red + G * kRec;  // [4 waves][kRec] when several waves share a head
-#pragma unroll
-  for (int i = 0; i < HPW; ++i) {
-    const float M = pair32_max(pair16_max(st.m[i]));
-    const float f = (M == -INFINITY) ? 0.f : __expf(st.m[i] - M);
-    const float L = pair32_sum(pair16_sum(st.l[i] * f));
-    float A[8];
-#pragma unroll
-    for (int c = 0; c < 8; ++c) A[c] = pair32_sum(pair16_sum(st.acc[i][c] * f));
-    if (rg == 0) {
-      float* r = (WPH == 1) ? red + (g0 + i) * kRec : tmp + wv * kRec;
-      if (sub == 0) { r[0] = M; r[1] = L; }
-#pragma unroll
-      for (int c = 0; c < 8; ++c) r[2 + sub * 8 + c] = A[c];
-    }
-  }
-  __syncthreads();
-  if (WPH > 1) {
-    // merge the WPH row partitions of each head in fixed order
-    for (int e = t; e < G * kD; e += kNT) {
-      const int g = e / kD, c = e % kD;
-      float M = -INFINITY;
-      for (int p = 0; p < WPH; ++p) M = fmaxf(M, tmp[(g * WPH + p) * kRec]);
-      float L = 0.f, A = 0.f;
-      if (M != -INFINITY) {
-        for (int p = 0; p < WPH; ++p) {
-          const float* r = tmp + (g * WPH + p) * kRec;
-          const float f = __expf(r[0] - M);
-          L = fmaf(r[1], f, L);
-          A = fmaf(r[2 + c], f, A);
-        }
-      }
-      float* o = red + g * kRec;
-      if (c == 0) { o[0] = M; o[1] = L; }
-      o[2 + c] = A;
-    }
-    __syncthreads();
-  }
+  finish_heads<G>(st, red);
 }
 
 }  // namespace hata

@@ -183,6 +183,7 @@ STEP_CASES = [
     (1, 16, 2, 20000, 100, "gauss", None),        # G = 8
     (2, 4, 2, 1000, 5, "exact", [1000, 999]),     # G = 2, tiny k
     (8, 32, 32, 2048, 128, "gauss", None),        # 256 units, one workgroup each
+    (1, 4, 4, 30000, 40, "gauss", None),          # G = 1 over many workgroups, most keep no row
 ]
 
 
