@@ -208,12 +208,13 @@ __global__ __launch_bounds__(kNT) void decode_step_kernel(const StepArgs a) {
   const int k = a.k;
   const int64_t row0 = ((int64_t)b * a.Hkv + h) * cap;
 
-  // ---- 1. loads.  The query rows, W_H and this workgroup's flag do not
-  // depend on the sequence length, so they are issued before it is read;
-  // then the appended key row, the code-cache ring and the exchange lines.
-  // Every load here is unconditional (clamped to a valid row, or to a
-  // zero-size buffer that returns 0), so the compiler can count the loads in
-  // flight exactly and wait for the early ones without draining the ring.
+  // ---- 1. loads.  The query rows, W_H, this workgroup's flag, the first
+  // PF*256 rows of its code chunk and its exchange lines do not depend on
+  // the sequence length, so they are issued before it is read; the appended
+  // key row follows (only the workgroup that owns it waits for it, after its
+  // scan).  Every load here is unconditional (clamped to a valid row, or to
+  // a zero-size buffer that returns 0), so the compiler can count the loads
+  // in flight exactly and wait for the early ones without draining the ring.
   // staging slot i of thread t holds dword (t + 256 i) % 64 of row (t + 256 i) / 64
   uint32_t xrow[C::NSTG];
 #pragma unroll
@@ -231,24 +232,13 @@ __global__ __launch_bounds__(kNT) void decode_step_kernel(const StepArgs a) {
   // An invalid length is handled after the projection (below); until then
   // the length is clamped into [1, cap] so that every address is valid and
   // no branch stands between the loads above and their issue.
-  // keep the loads above ahead of the length read in the issued code
-  __builtin_amdgcn_sched_barrier(0);
-  const int n_in = a.seq_lens[b];
-  const bool bad_len = n_in < 1 || (int64_t)n_in > cap;
-  const int n = bad_len ? 1 : n_in;
   const int lo = w * a.chunk;
-  const int cnt = max(0, min(n, lo + a.chunk) - lo);
-  const bool owns_new = (n - 1 >= lo) && (n - 1 < lo + cnt);
-  const int new_li = n - 1 - lo;
-  const int nrows = G + (owns_new ? 1 : 0);
-  // row n-1 of K (row 0 when this workgroup does not own it): dword `lane`
-  const uint32_t krow = reinterpret_cast<const uint32_t*>(a.K + (row0 + (owns_new ? n - 1 : 0)) * kD)[lane];
-  // ring slots past cnt reload this workgroup's last row (row 0 if it has none)
-  const uint4* cbase = reinterpret_cast<const uint4*>(a.codes) + row0 + (cnt > 0 ? lo : 0);
-  const int clast = max(cnt - 1, 0);
+  // the code ring's first PF*256 rows of the chunk, clamped into the cache
+  // (rows past the sequence end are loaded and never scored)
+  const uint4* cunit = reinterpret_cast<const uint4*>(a.codes) + row0;
   uint4 cbuf[PF];
 #pragma unroll
-  for (int j = 0; j < PF; ++j) cbuf[j] = load_stream16(cbase + min(j * kNT + t, clast));
+  for (int j = 0; j < PF; ++j) cbuf[j] = load_stream16(cunit + min((int64_t)lo + j * kNT + t, cap - 1));
   // This workgroup's exchange lines (its histogram window and its partial
   // record) have usually left L2 since the previous step; the unit's first
   // reads of them after the flag take about 1 us then, against about 0.4 us
@@ -271,22 +261,33 @@ __global__ __launch_bounds__(kNT) void decode_step_kernel(const StepArgs a) {
                                          (uint32_t)(unit * kMaxWg + kMaxWg) * C::RECP * 4 - 4);
     warm = CohBuf(wbase, span).ld4(wv == 0 ? woff : poff);
   }
+  // keep the loads above ahead of the length read in the issued code
+  __builtin_amdgcn_sched_barrier(0);
+  const int n_in = a.seq_lens[b];
+  const bool bad_len = n_in < 1 || (int64_t)n_in > cap;
+  const int n = bad_len ? 1 : n_in;
+  const int cnt = max(0, min(n, lo + a.chunk) - lo);
+  const bool owns_new = (n - 1 >= lo) && (n - 1 < lo + cnt);
+  const int new_li = n - 1 - lo;
+  // row n-1 of K (row 0 when this workgroup does not own it): dword `lane`
+  const uint32_t krow = reinterpret_cast<const uint32_t*>(a.K + (row0 + (owns_new ? n - 1 : 0)) * kD)[lane];
+  // ring refills: rows lo + li for li < cnt
+  const uint4* cbase = cunit + (cnt > 0 ? lo : 0);
 
-  // ---- 2. encode the query rows (+ the new key row).  Every slot is
-  // stored (rows past G are zero and never read), so no load is consumed
-  // under a branch.
+  // ---- 2. encode the query rows.  Every staging slot is stored (slots past
+  // the G query rows are zero), so no load is consumed under a branch.
 #pragma unroll
   for (int i = 0; i < C::NSTG; ++i) {
     const int e = t + i * kNT;
     const int r = e >> 6, c2 = e & 63;
-    const uint32_t v = (r < G) ? xrow[i] : ((r == G) ? krow : 0u);  // lane == c2 for row G
+    const uint32_t v = (r < G) ? xrow[i] : 0u;
     qf[r * kD + 2 * c2] = bf16_lo(v);
     qf[r * kD + 2 * c2 + 1] = bf16_hi(v);
   }
   for (int i = t; i < C::NBP; i += kNT) hist[i] = 0;
   if (t < 64) misc[t] = (t < 3) ? (uint32_t)NB : 0u;
   __syncthreads();
-  project_pack<G + 1>(wr, qf, red, qcode, nrows);
+  project_pack<G>(wr, qf, red, qcode, G);
   if (bad_len) {
     // invalid length: every workgroup of the unit leaves here, before any
     // exchange, so the unit's flags stay consistent; workgroup 0 clears the
@@ -298,12 +299,6 @@ __global__ __launch_bounds__(kNT) void decode_step_kernel(const StepArgs a) {
         for (int j = t; j < k; j += kNT) a.idx_out[(int64_t)unit * k + j] = -1;
     }
     return;
-  }
-  uint4 newc = make_uint4(0, 0, 0, 0);
-  if (owns_new) {
-    const uint64_t k0 = qcode[G * 2], k1 = qcode[G * 2 + 1];
-    newc = make_uint4((uint32_t)k0, (uint32_t)(k0 >> 32), (uint32_t)k1, (uint32_t)(k1 >> 32));
-    if (t == 0) reinterpret_cast<uint4*>(a.codes)[row0 + n - 1] = newc;
   }
   uint32_t qw[G][kWords32];
 #pragma unroll
@@ -349,12 +344,27 @@ __global__ __launch_bounds__(kNT) void decode_step_kernel(const StepArgs a) {
       if (li < cnt) score_one(cbuf[j], li);
     }
   }
-  if (owns_new && t == new_li % kNT) {
-    const uint32_t s_old = sc[new_li];
-    const uint32_t s_new = gqa_hamming<G>(newc, qm);
-    atomicSub(&hist[s_old], 1u);
-    atomicAdd(&hist[s_new], 1u);
-    sc[new_li] = (uint16_t)s_new;
+  if (owns_new) {
+    // The appended key row, encoded by the one workgroup that owns it once
+    // its scan is done (its load has long arrived; the other workgroups never
+    // wait for it); its code goes to the cache and its score replaces the
+    // one computed from the stale cache row.
+    if (t < 64) {
+      qf[G * kD + 2 * lane] = bf16_lo(krow);
+      qf[G * kD + 2 * lane + 1] = bf16_hi(krow);
+    }
+    __syncthreads();
+    project_pack<1>(wr, qf + G * kD, red, qcode + G * 2, 1);
+    const uint64_t k0 = qcode[G * 2], k1 = qcode[G * 2 + 1];
+    const uint4 newc = make_uint4((uint32_t)k0, (uint32_t)(k0 >> 32), (uint32_t)k1, (uint32_t)(k1 >> 32));
+    if (t == 0) reinterpret_cast<uint4*>(a.codes)[row0 + n - 1] = newc;
+    if (t == new_li % kNT) {
+      const uint32_t s_old = sc[new_li];
+      const uint32_t s_new = gqa_hamming<G>(newc, qm);
+      atomicSub(&hist[s_old], 1u);
+      atomicAdd(&hist[s_new], 1u);
+      sc[new_li] = (uint16_t)s_new;
+    }
   }
   __syncthreads();
 

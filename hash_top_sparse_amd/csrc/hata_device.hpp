@@ -210,33 +210,45 @@ __device__ __forceinline__ void load_w_regs(const float* __restrict__ Wh, WRegs&
   for (int i = 0; i < 16; ++i) wr.w[i] = src[i * (kR / 4)];
 }
 // xs: LDS rows [R][128] fp32; red: LDS [4][R][128] fp32; out: LDS [R][2] uint64.
-// Rows >= nrows are skipped.  Ends with __syncthreads.
+// Rows >= nrows are not packed (their products are formed and dropped, so
+// they may hold anything).  The FMA loop runs over W's registers in load
+// order, all rows at once, so the products with the first W registers start
+// while the later ones are still arriving; each accumulator still takes its
+// 16 channels in ascending order.  Ends with __syncthreads.
 template <int R>
 __device__ __forceinline__ void project_pack(const WRegs& wr, const float* xs, float* red,
                                              uint64_t* out, int nrows) {
   const int t = threadIdx.x, lane = t & 63, wv = t >> 6, cg = t & 31, rg = t >> 5;
+  float acc[R][4];
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) acc[r][c] = 0.f;
+#pragma unroll
+  for (int i4 = 0; i4 < 4; ++i4) {
+    float4 xq[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) xq[r] = reinterpret_cast<const float4*>(xs + r * kD + rg * 16)[i4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float4 w = wr.w[i4 * 4 + j];
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const float xv = (j == 0) ? xq[r].x : (j == 1) ? xq[r].y : (j == 2) ? xq[r].z : xq[r].w;
+        acc[r][0] = fmaf(xv, w.x, acc[r][0]);
+        acc[r][1] = fmaf(xv, w.y, acc[r][1]);
+        acc[r][2] = fmaf(xv, w.z, acc[r][2]);
+        acc[r][3] = fmaf(xv, w.w, acc[r][3]);
+      }
+    }
+  }
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     if (r >= nrows) break;
-    const float4* xr = reinterpret_cast<const float4*>(xs + r * kD + rg * 16);
-    float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
-#pragma unroll
-    for (int i4 = 0; i4 < 4; ++i4) {
-      const float4 x = xr[i4];
-      const float xv[4] = {x.x, x.y, x.z, x.w};
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const float4 w = wr.w[i4 * 4 + j];
-        a0 = fmaf(xv[j], w.x, a0);
-        a1 = fmaf(xv[j], w.y, a1);
-        a2 = fmaf(xv[j], w.z, a2);
-        a3 = fmaf(xv[j], w.w, a3);
-      }
-    }
-    a0 = pair32_sum(a0);
-    a1 = pair32_sum(a1);
-    a2 = pair32_sum(a2);
-    a3 = pair32_sum(a3);
+    const float a0 = pair32_sum(acc[r][0]);
+    const float a1 = pair32_sum(acc[r][1]);
+    const float a2 = pair32_sum(acc[r][2]);
+    const float a3 = pair32_sum(acc[r][3]);
     if (lane < 32) {
       float* dst = red + (wv * R + r) * kR + cg * 4;
       *reinterpret_cast<float4*>(dst) = make_float4(a0, a1, a2, a3);
