@@ -394,7 +394,8 @@ __global__ __launch_bounds__(kNT) void decode_step_kernel(const StepArgs a) {
       if (t == 0) {
         e16[0] = (uint32_t)wlo; e16[1] = (uint32_t)(top + 1);
         e16[2] = has_k ? 1u : 0u; e16[3] = ovf ? 1u : 0u;
-        e16[4] = (uint32_t)cnt & 0xFFFFu; e16[5] = (uint32_t)cnt >> 16;
+        // cumulative count at the window's last stored bin
+        e16[4] = (len > 0) ? hist[wlo + min(len, kWinCap) - 1] : 0u; e16[5] = 0;
         e16[6] = (uint32_t)__builtin_amdgcn_s_getreg(kXccIdReg) & 0xFu;  // this XCD
         e16[7] = 0;
       } else {
@@ -433,6 +434,9 @@ __global__ __launch_bounds__(kNT) void decode_step_kernel(const StepArgs a) {
     {
       const int nchunks = a.Wg * (kWinBytes / 16);
       u32x4 v[4];
+      // wave 0 also loads writer `lane`'s header chunk into registers
+      u32x4 hv = {0u, 0u, 0u, 0u};
+      if (wv == 0) hv = wbuf.ld16(min(lane, a.Wg - 1) * kWinBytes);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int c = t + i * kNT;
@@ -443,40 +447,37 @@ __global__ __launch_bounds__(kNT) void decode_step_kernel(const StepArgs a) {
         const int c = t + i * kNT;
         if (c < nchunks) *reinterpret_cast<u32x4*>(winb + c * 16) = v[i];
       }
+      // Writer headers, parsed by wave 0 from registers (lane = writer):
+      // first bin lw, window length ln, count at the window's end topc,
+      // overflow flag; published in LDS with the barrier below.
+      if (wv == 0) {
+        int lw = NB, tw = NB - 1, ln = 0, topc = 0;
+        bool hw = false, ow = false;
+        if (lane < a.Wg) {
+          lw = min((int)(hv.x & 0xFFFFu), NB);
+          tw = min((int)(hv.x >> 16) - 1, NB - 1);
+          hw = (hv.y & 0xFFFFu) != 0;
+          ow = ((hv.y >> 16) & 1u) != 0;
+          ln = max(0, min(tw - lw + 1, kWinCap));
+          topc = ln > 0 ? (int)(hv.z & 0xFFFFu) : 0;
+        }
+        reinterpret_cast<int4*>(whdr)[lane] = make_int4(lw, ln, topc, ow ? 1 : 0);
+        if (a.xcd_local) {
+          // the plain-store exchange needs every writer on this XCD
+          const uint32_t own = (uint32_t)__builtin_amdgcn_s_getreg(kXccIdReg) & 0xFu;
+          const uint32_t wx = (lane < a.Wg) ? (hv.w & 0xFFFFu) : own;
+          if (__ballot(wx != own) && lane == 0) atomicOr(a.err, 4u);
+        }
+        // T cannot exceed any workgroup's own k-th smallest score
+        const int tmin = wave_min_i((lane < a.Wg && hw) ? tw : NB - 1);
+        const int glo = min(wave_min_i(lw), tmin);
+        const bool any_ow = __ballot(ow) != 0;
+        if (lane == 0) { misc[16] = (uint32_t)glo; misc[17] = (uint32_t)tmin; misc[18] = any_ow ? 1u : 0u; }
+      }
     }
     __syncthreads();
-    // Writer headers, parsed once by wave 0 (lane = writer): first bin lw,
-    // window length ln, count at the window's end topc, overflow flag.
-    int4* hdr4 = reinterpret_cast<int4*>(whdr);                 // [kMaxWg]
+    const int4* hdr4 = reinterpret_cast<const int4*>(whdr);            // [kMaxWg]
     uint32_t* cpart = reinterpret_cast<uint32_t*>(whdr + 4 * kMaxWg);  // [2][4][64]
-    if (wv == 0) {
-      int lw = NB, tw = NB - 1, ln = 0, topc = 0;
-      bool hw = false, ow = false;
-      if (lane < a.Wg) {
-        const uint32_t* hdr = reinterpret_cast<const uint32_t*>(winb + lane * kWinBytes);
-        const uint16_t* ent = reinterpret_cast<const uint16_t*>(hdr) + kWinHdr;
-        lw = min((int)(hdr[0] & 0xFFFFu), NB);
-        tw = min((int)(hdr[0] >> 16) - 1, NB - 1);
-        hw = (hdr[1] & 0xFFFFu) != 0;
-        ow = ((hdr[1] >> 16) & 1u) != 0;
-        ln = max(0, min(tw - lw + 1, kWinCap));
-        topc = ln > 0 ? ent[ln - 1] : 0;
-      }
-      hdr4[lane] = make_int4(lw, ln, topc, ow ? 1 : 0);
-      if (a.xcd_local) {
-        // the plain-store exchange needs every writer on this XCD
-        const uint32_t own = (uint32_t)__builtin_amdgcn_s_getreg(kXccIdReg) & 0xFu;
-        const uint32_t wx = (lane < a.Wg)
-            ? (reinterpret_cast<const uint32_t*>(winb + lane * kWinBytes)[3] & 0xFFFFu) : own;
-        if (__ballot(wx != own) && lane == 0) atomicOr(a.err, 4u);
-      }
-      // T cannot exceed any workgroup's own k-th smallest score
-      const int tmin = wave_min_i((lane < a.Wg && hw) ? tw : NB - 1);
-      const int glo = min(wave_min_i(lw), tmin);
-      const bool any_ow = __ballot(ow) != 0;
-      if (lane == 0) { misc[16] = (uint32_t)glo; misc[17] = (uint32_t)tmin; misc[18] = any_ow ? 1u : 0u; }
-    }
-    __syncthreads();
     const bool any_ow = misc[18] != 0;
     // cumulative count of writer ww at bin s2 (0 below its window, the
     // window's last count past its end); an overflowing window is read from
@@ -531,20 +532,19 @@ __global__ __launch_bounds__(kNT) void decode_step_kernel(const StepArgs a) {
         break;
       }
     }
-    if (wv == 0) {
-      const uint32_t l1 = (lane < a.Wg && Tw > 0) ? cumw(lane, Tw - 1) : 0u;
-      const uint32_t e1 = (lane < a.Wg) ? cumw(lane, Tw) - l1 : 0u;
-      const uint32_t il = wave_incl_scan_u32(l1);
-      const uint32_t ie = wave_incl_scan_u32(e1);
-      if (lane == w) { misc[6] = il - l1; misc[7] = ie - e1; misc[3] = e1; }
-      if (lane == 63) { misc[5] = il; misc[2] = (uint32_t)Tw; }
-    }
-    __syncthreads();
-    T = (int)misc[2];
-    lt_all = misc[5];
+    // Every wave (lane = writer) forms the writers' below-T and tie counts
+    // and their prefixes itself and takes this workgroup's values by
+    // readlane: no LDS round trip and no barrier.
+    const uint32_t l1 = (lane < a.Wg && Tw > 0) ? cumw(lane, Tw - 1) : 0u;
+    const uint32_t e1 = (lane < a.Wg) ? cumw(lane, Tw) - l1 : 0u;
+    const uint32_t il = wave_incl_scan_u32(l1);
+    const uint32_t ie = wave_incl_scan_u32(e1);
+    T = Tw;
+    lt_all = (uint32_t)__builtin_amdgcn_readlane((int)il, 63);
     quota = (uint32_t)k - lt_all;
-    const uint32_t pre_lt = misc[6], pre_eq = misc[7];
-    const uint32_t eq_self = misc[3];
+    const uint32_t pre_lt = (uint32_t)__builtin_amdgcn_readlane((int)(il - l1), w);
+    const uint32_t pre_eq = (uint32_t)__builtin_amdgcn_readlane((int)(ie - e1), w);
+    const uint32_t eq_self = (uint32_t)__builtin_amdgcn_readlane((int)e1, w);
     const uint32_t left = quota > pre_eq ? quota - pre_eq : 0u;
     take_self = eq_self < left ? eq_self : left;
     sel_before = pre_lt + (pre_eq < quota ? pre_eq : quota);
