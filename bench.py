@@ -289,6 +289,73 @@ def measure(cfg_id: int, steps: int, warmup: int, dense_steps: int, layers: int,
     return res, inp
 
 
+def model_sweep(layers: int = 32, ctxs=(32768, 65536, 131072), reps: int = 10) -> list:
+    """Multi-layer decode: for each context length, `layers` layers of a
+    Llama-3.1-8B-shaped attention (B=1, 32 query / 8 KV heads, d=128, k=512),
+    each with its own q, K, V, W_H and code cache, decoded one token as one
+    captured graph of `layers` fused steps, against a graph of `layers` dense
+    flash-decodes over the same caches.  Attention only (no projections or
+    MLP): the shape of a whole-model decode speed table, not its values."""
+    import torch
+
+    from hash_top_sparse_amd import binding
+
+    dev = torch.device("cuda:0")
+    B, Hq, Hkv, d, k = 1, 32, 8, 128, 512
+    scale = 1.0 / np.sqrt(d)
+    gen = torch.Generator(device=dev)
+    res = []
+    for N in ctxs:
+        gen.manual_seed(6000 + N // 1024)
+        bf = lambda *shp: torch.randn(shp, generator=gen, device=dev).to(torch.bfloat16)
+        qs = [bf(B, Hq, d) for _ in range(layers)]
+        Ks = [bf(B, Hkv, N, d) for _ in range(layers)]
+        Vs = [bf(B, Hkv, N, d) for _ in range(layers)]
+        Ws = [torch.randn((Hkv, d, 128), generator=gen, device=dev) / np.sqrt(128.0) for _ in range(layers)]
+        codes = [torch.zeros((B, Hkv, N, 2), dtype=torch.int64, device=dev) for _ in range(layers)]
+        for l in range(layers):
+            binding.encode_append(Ks[l], Ws[l], codes[l], n_new=N)
+        seq = torch.full((B,), N, dtype=torch.int32, device=dev)
+        outs = [torch.zeros((B, Hq, d), dtype=torch.float32, device=dev) for _ in range(layers)]
+        ws = binding.alloc_workspace(binding.OP_DECODE_STEP, B, Hq, Hkv, N, k, device=dev)
+        dws = binding.alloc_workspace(binding.OP_DENSE_DECODE, B, Hq, Hkv, N, 1, device=dev)
+        torch.cuda.synchronize()
+
+        def timed(one_layer):
+            for l in range(layers):  # warm-up, eager
+                one_layer(l)
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for l in range(layers):
+                    one_layer(l)
+            g.replay()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(reps):
+                g.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) / reps
+
+        h_ms = timed(lambda l: binding.decode_step(qs[l], Ks[l], Vs[l], Ws[l], codes[l], seq, N, k, scale,
+                                                   outs[l], ws))
+        err = binding.workspace_check(ws)
+        if err:
+            raise RuntimeError(f"workspace error word {err}: a cross-workgroup wait timed out")
+        d_ms = timed(lambda l: binding.dense_decode(qs[l], Ks[l], Vs[l], seq, N, scale, outs[l], dws))
+        r = {"ctx": N, "layers": layers, "hata_ms_per_token": h_ms, "dense_ms_per_token": d_ms,
+             "speedup": d_ms / h_ms, "hata_tokens_per_s": 1000.0 / h_ms,
+             "hata_GBs": layers * step_bytes(B, Hq, Hkv, N, k) / (h_ms * 1e-3) / 1e9}
+        log(f"model sweep {N // 1024}K x {layers} layers: hata {h_ms * 1e3:.1f} us/token, dense "
+            f"{d_ms * 1e3:.1f} us/token, speedup {d_ms / h_ms:.2f}x")
+        res.append(r)
+        del qs, Ks, Vs, Ws, codes, outs, ws, dws
+        torch.cuda.empty_cache()
+    return res
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -302,6 +369,8 @@ def main() -> int:
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="launch the timed steps eagerly")
     ap.add_argument("--sweep", action="store_true", help="also time the other workloads (2, 3, 5)")
+    ap.add_argument("--model-sweep", action="store_true",
+                    help="also time 32-layer decode (one graph per token) at 32K/64K/128K against dense")
     ap.add_argument("--pmc-run", action="store_true",
                     help="short run for hardware-counter passes: 32 eager fused steps over the layer "
                          "caches, then one plain device copy of 1 GiB as the byte-counter reference")
@@ -342,6 +411,7 @@ def main() -> int:
                            not args.no_graph, with_bulk=False)
             sweep[str(c)] = r
 
+    msweep = model_sweep() if args.model_sweep else None
     peak_meas = read_peak()
     log(f"streaming read of 4 GiB: {peak_meas:.0f} GB/s")
     cpu = None
@@ -382,6 +452,8 @@ def main() -> int:
     }
     if sweep is not None:
         res["sweep"] = sweep
+    if msweep is not None:
+        res["model_sweep"] = msweep
     print(json.dumps(res), flush=True)
     return 0
 
