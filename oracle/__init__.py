@@ -69,7 +69,7 @@ def lib() -> ctypes.CDLL:
         L.oracle_attention.argtypes = [P, ctypes.c_int, P, P, P, ctypes.c_int, ctypes.c_int,
                                        ctypes.c_float, P]
         L.oracle_attention.restype = None
-        L.oracle_decode_step.argtypes = [P, P, P, P, P, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+        L.oracle_decode_step.argtypes = [P, P, P, P, P, P, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                          ctypes.c_int, ctypes.c_int, i64, P, ctypes.c_int,
                                          ctypes.c_float, P, P, P, P, ctypes.c_int]
         L.oracle_decode_step.restype = ctypes.c_int
@@ -144,12 +144,15 @@ def attention(q_bf16: np.ndarray, K_bf16: np.ndarray, V_bf16: np.ndarray,
 
 
 def decode_step(q, K, V, W, codes, seq_lens, k, scale, nthreads: int = 0,
-                want_scores: bool = False, want_qcodes: bool = False):
+                want_scores: bool = False, want_qcodes: bool = False, Wk=None):
     """Whole decode step over every (sequence, KV head) unit.
 
     q [B,Hq,d] bf16 bits; K, V [B,Hkv,cap,d] bf16 bits; W [Hkv,d,r] fp32;
     codes [B,Hkv,cap,r/64] uint64, rows < n_b-1 valid -- a copy is returned
-    with row n_b-1 appended.  Returns dict(out, idx, codes[, scores][, qcodes]).
+    with row n_b-1 appended.  Wk (optional, like W): a separate key encoder
+    for the appended row (HashAttention summary page, "Approach": independent
+    query and key encoders); None means W encodes both.
+    Returns dict(out, idx, codes[, scores][, qcodes]).
     """
     q = _c(q, np.uint16)
     K = _c(K, np.uint16)
@@ -164,7 +167,10 @@ def decode_step(q, K, V, W, codes, seq_lens, k, scale, nthreads: int = 0,
     idx = np.zeros((B, Hkv, k), np.int32)
     scores = np.full((B, Hkv, cap), -1, np.int32) if want_scores else None
     qcodes = np.zeros((B, Hq, r // 64), np.uint64) if want_qcodes else None
-    rc = lib().oracle_decode_step(_p(q), _p(K), _p(V), _p(W), _p(codes), B, Hq, Hkv, d, r,
+    Wk = None if Wk is None else _c(Wk, np.float32)
+    if Wk is not None and Wk.shape != W.shape:
+        raise ValueError("Wk must have W's shape")
+    rc = lib().oracle_decode_step(_p(q), _p(K), _p(V), _p(W), _p(Wk), _p(codes), B, Hq, Hkv, d, r,
                                   cap, _p(seq), k, ctypes.c_float(scale), _p(out), _p(idx),
                                   _p(scores), _p(qcodes), nthreads)
     if rc != 0:

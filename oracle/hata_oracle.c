@@ -182,11 +182,14 @@ void oracle_attention(const uint16_t* q, int G, const uint16_t* K,
  * Layouts: q [B][Hq][d] bf16; K, V [B][Hkv][cap][d] bf16; W [Hkv][d][r];
  * codes [B][Hkv][cap][r/64] (rows < n_b-1 valid on entry); seq_lens [B]
  * (host); out [B][Hq][d] fp32; idx_out [B][Hkv][k].
+ * Wk (nullable, same layout as W): a separate key encoder, used in step 2
+ * instead of W (independent query and key encoders, as described on the
+ * HashAttention summary page, "Approach"); NULL means W encodes both.
  * Nullable extras: scores_out [B][Hkv][cap] (rows < n_b written), qcodes_out
  * [B][Hq][r/64].  nthreads <= 0 means "all available" (OpenMP over units).
  * Returns 0, or -1 on bad arguments. */
 int oracle_decode_step(const uint16_t* q, const uint16_t* K, const uint16_t* V,
-                       const float* W, uint64_t* codes, int B, int Hq, int Hkv,
+                       const float* W, const float* Wk, uint64_t* codes, int B, int Hq, int Hkv,
                        int d, int r, int64_t cap, const int32_t* seq_lens,
                        int k, float scale, float* out, int32_t* idx_out,
                        int32_t* scores_out, uint64_t* qcodes_out,
@@ -208,6 +211,7 @@ int oracle_decode_step(const uint16_t* q, const uint16_t* K, const uint16_t* V,
     const int64_t n = seq_lens[b];
     const int64_t base = ((int64_t)b * Hkv + h) * cap;
     const float* Wh = W + (int64_t)h * d * r;
+    const float* Wkh = (Wk ? Wk : W) + (int64_t)h * d * r;
     uint64_t* qc = (uint64_t*)malloc((size_t)G * words * sizeof *qc);
     int32_t* S = (int32_t*)malloc((size_t)n * sizeof *S);
     int32_t* idx = idx_out + (int64_t)u * k;
@@ -219,7 +223,7 @@ int oracle_decode_step(const uint16_t* q, const uint16_t* K, const uint16_t* V,
     }
     const uint16_t* qrows = q + ((int64_t)b * Hq + (int64_t)h * G) * d;
     oracle_encode_rows(qrows, G, d, Wh, r, qc, NULL);
-    oracle_encode_rows(K + (base + n - 1) * d, 1, d, Wh, r,
+    oracle_encode_rows(K + (base + n - 1) * d, 1, d, Wkh, r,
                        codes + (base + n - 1) * words, NULL);
     oracle_hamming_gqa(qc, G, codes + base * words, n, words, S);
     int m = oracle_topk(S, n, k, idx);

@@ -375,3 +375,47 @@ def test_decode_step_appended_code_is_encode_of_new_key(oracle_mod):
     stale[:, :, -1] = 0
     res = oracle_mod.decode_step(inp.q, inp.K, inp.V, inp.W, stale, inp.seq_lens, inp.k, inp.scale)
     np.testing.assert_array_equal(res["codes"], codes)
+
+
+# ------------------------------------------- separate query and key encoders
+# (HashAttention summary page, "Approach": independent query and key
+# encoders.)  Pins: the shared case is the special case Wk = W, and with
+# Wk = -W every key bit flips wherever the projection is nonzero (negating W
+# negates every product and so the fp32 sum exactly), which turns each
+# summed distance S into G*r - S.
+
+
+def test_decode_step_key_encoder_equal_to_query_encoder_is_shared_case(oracle_mod):
+    shape = synth.small_shape(B=2, Hq=8, Hkv=2, N=96, k=16, seed_base=9400)
+    inp = synth.make_inputs(shape)
+    codes = oracle_mod.build_cache(inp.K, inp.W)
+    a = oracle_mod.decode_step(inp.q, inp.K, inp.V, inp.W, codes, inp.seq_lens, inp.k, inp.scale,
+                               want_scores=True)
+    b = oracle_mod.decode_step(inp.q, inp.K, inp.V, inp.W, codes, inp.seq_lens, inp.k, inp.scale,
+                               want_scores=True, Wk=inp.W.copy())
+    for key in ("out", "idx", "codes", "scores"):
+        np.testing.assert_array_equal(a[key], b[key])
+
+
+def test_decode_step_negated_key_encoder_complements_scores(oracle_mod):
+    shape = synth.small_shape(B=2, Hq=8, Hkv=2, N=200, k=24, seed_base=9500)
+    inp = synth.make_inputs(shape)
+    G, r = 4, inp.W.shape[2]
+    Wk = -inp.W
+    shared = oracle_mod.decode_step(inp.q, inp.K, inp.V, inp.W, oracle_mod.build_cache(inp.K, inp.W),
+                                    inp.seq_lens, inp.k, inp.scale, want_scores=True)
+    sep = oracle_mod.decode_step(inp.q, inp.K, inp.V, inp.W, oracle_mod.build_cache(inp.K, Wk),
+                                 inp.seq_lens, inp.k, inp.scale, want_scores=True, Wk=Wk)
+    for b in range(2):
+        n = int(inp.seq_lens[b])
+        # Gaussian inputs: no projection is exactly zero, so the identity is exact
+        np.testing.assert_array_equal(sep["scores"][b, :, :n], G * r - shared["scores"][b, :, :n])
+        # the appended row is the key encoder's code of the new key
+        np.testing.assert_array_equal(sep["codes"][b, :, n - 1],
+                                      np.stack([oracle_mod.encode(inp.K[b, h, n - 1], Wk[h])
+                                                for h in range(2)]))
+        # so the kept set is the k tokens of LARGEST shared distance (ties to lower index)
+        for h in range(2):
+            s = shared["scores"][b, h, :n].astype(np.int64)
+            order = np.lexsort((np.arange(n), -s))[: inp.k]
+            assert list(sep["idx"][b, h]) == sorted(order.tolist())
