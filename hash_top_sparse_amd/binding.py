@@ -52,6 +52,7 @@ def load() -> ctypes.CDLL:
         "hata_topk": ([P, I, I, I64, P, I64, I, I, P, P, SZ, P], I),
         "hata_sparse_decode": ([P, P, P, I, I, I, I, I64, P, I, F, P, P, SZ, P], I),
         "hata_decode_step": ([P, P, P, P, P, I, I, I, I, I, I64, P, I64, I, F, P, P, P, SZ, P], I),
+        "hata_decode_step_qk": ([P, P, P, P, P, P, I, I, I, I, I, I64, P, I64, I, F, P, P, P, SZ, P], I),
         "hata_dense_decode": ([P, P, P, I, I, I, I, I64, P, I64, F, P, P, SZ, P], I),
         "hata_workspace_bytes": ([I, I, I, I, I, I, I64, I], SZ),
         "hata_workspace_reset": ([P, SZ, P], I),
@@ -69,7 +70,8 @@ def load() -> ctypes.CDLL:
 def exported_symbols() -> list[str]:
     return [n for n in ("hata_status_string", "hata_last_error_message", "hata_version",
                         "hata_encode_append", "hata_hamming_scores", "hata_topk",
-                        "hata_sparse_decode", "hata_decode_step", "hata_dense_decode",
+                        "hata_sparse_decode", "hata_decode_step", "hata_decode_step_qk",
+                        "hata_dense_decode",
                         "hata_workspace_bytes", "hata_workspace_reset", "hata_workspace_check",
                         "hata_stream_read")
             if hasattr(load(), n)]
@@ -208,6 +210,29 @@ def decode_step(q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, W_H: torch.Te
     _check(load().hata_decode_step(_ptr(q), _ptr(K), _ptr(V), _ptr(W_H), _ptr(codes), B, Hq, Hkv,
                                    d, r, cap, _ptr(seq_lens), int(max_len), int(k), float(scale),
                                    _ptr(out), _ptr(idx_out), _ptr(ws), ws.numel(), _stream(stream)))
+
+
+def decode_step_qk(q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, W_Hq: torch.Tensor,
+                   W_Hk: torch.Tensor, codes: torch.Tensor, seq_lens: torch.Tensor, max_len: int, k: int,
+                   scale: float, out: torch.Tensor, ws: torch.Tensor, idx_out: torch.Tensor | None = None,
+                   stream=None) -> None:
+    """The fused decode step with separate query and key encoders (see
+    hata_decode_step_qk)."""
+    for t, n in ((q, "q"), (K, "K"), (V, "V")):
+        _need(t, torch.bfloat16, n)
+    _need(W_Hq, torch.float32, "W_Hq")
+    _need(W_Hk, torch.float32, "W_Hk")
+    _need(codes, torch.int64, "codes")
+    _need(out, torch.float32, "out")
+    _need(seq_lens, torch.int32, "seq_lens")
+    if idx_out is not None:
+        _need(idx_out, torch.int32, "idx_out")
+    B, Hq, d = q.shape
+    _, Hkv, cap, _ = K.shape
+    r = W_Hq.shape[2]
+    _check(load().hata_decode_step_qk(_ptr(q), _ptr(K), _ptr(V), _ptr(W_Hq), _ptr(W_Hk), _ptr(codes), B, Hq,
+                                      Hkv, d, r, cap, _ptr(seq_lens), int(max_len), int(k), float(scale),
+                                      _ptr(out), _ptr(idx_out), _ptr(ws), ws.numel(), _stream(stream)))
 
 
 def workspace_reset(ws: torch.Tensor, stream=None) -> None:

@@ -240,11 +240,11 @@ int hata_stream_read(const void* src, size_t bytes, uint64_t* sink, size_t sink_
   return check_launch(e, "stream_read launch");
 }
 
-int hata_decode_step(const void* q, const void* K, const void* V, const float* W_H, uint64_t* codes,
-                     int B, int Hq, int Hkv, int d, int r, int64_t cap, const int32_t* seq_lens,
-                     int64_t max_len, int k, float scale, float* out, int32_t* idx_out, void* ws,
-                     size_t ws_bytes, void* stream) {
-  if (!q || !K || !V || !W_H || !codes || !seq_lens || !out)
+static int decode_step_impl(const void* q, const void* K, const void* V, const float* W_H,
+                            const float* W_Hk, uint64_t* codes, int B, int Hq, int Hkv, int d, int r,
+                            int64_t cap, const int32_t* seq_lens, int64_t max_len, int k, float scale,
+                            float* out, int32_t* idx_out, void* ws, size_t ws_bytes, void* stream) {
+  if (!q || !K || !V || !W_H || !W_Hk || !codes || !seq_lens || !out)
     return fail(HATA_ERR_NULL, "decode_step: null pointer");
   int st = check_dims(d, r);
   if (st) return st;
@@ -265,8 +265,8 @@ int hata_decode_step(const void* q, const void* K, const void* V, const float* W
   const auto* Kb = static_cast<const uint16_t*>(K);
   const auto* Vb = static_cast<const uint16_t*>(V);
   if (p.fused) {
-    hipError_t e = hata::launch_decode_step(p, qb, Kb, Vb, W_H, codes, B, Hq, Hkv, cap, seq_lens, k,
-                                            scale, out, idx_out, wsb, s);
+    hipError_t e = hata::launch_decode_step(p, qb, Kb, Vb, W_H, W_Hk, codes, B, Hq, Hkv, cap, seq_lens,
+                                            k, scale, out, idx_out, wsb, s);
     return check_launch(e, "decode_step launch");
   }
   // Staged steps: the per-unit scores do not fit on chip at this shape.
@@ -276,7 +276,7 @@ int hata_decode_step(const void* q, const void* K, const void* V, const float* W
   auto* part = reinterpret_cast<float*>(wsb + p.off_attn);
   hipError_t e = hata::launch_encode_rows(qb, 1, B, Hq, Hkv, 1, W_H, qc, 1, nullptr, 0, s);
   if (e == hipSuccess)  // key append at row seq_lens[b] - 1
-    e = hata::launch_encode_rows(Kb, cap, B, Hkv, Hkv, 1, W_H, codes, cap, seq_lens, -1, s);
+    e = hata::launch_encode_rows(Kb, cap, B, Hkv, Hkv, 1, W_Hk, codes, cap, seq_lens, -1, s);
   (void)G;
   if (e == hipSuccess) e = hata::launch_hamming(qc, codes, B, Hq, Hkv, cap, seq_lens, max_len, sc, max_len, s);
   int32_t* idx = idx_out;
@@ -285,6 +285,22 @@ int hata_decode_step(const void* q, const void* K, const void* V, const float* W
   if (e == hipSuccess)
     e = hata::launch_attention(qb, Kb, Vb, B, Hq, Hkv, cap, idx, k, nullptr, k, scale, out, part, s);
   return check_launch(e, "decode_step (staged) launch");
+}
+
+int hata_decode_step(const void* q, const void* K, const void* V, const float* W_H, uint64_t* codes,
+                     int B, int Hq, int Hkv, int d, int r, int64_t cap, const int32_t* seq_lens,
+                     int64_t max_len, int k, float scale, float* out, int32_t* idx_out, void* ws,
+                     size_t ws_bytes, void* stream) {
+  return decode_step_impl(q, K, V, W_H, W_H, codes, B, Hq, Hkv, d, r, cap, seq_lens, max_len, k, scale,
+                          out, idx_out, ws, ws_bytes, stream);
+}
+
+int hata_decode_step_qk(const void* q, const void* K, const void* V, const float* W_Hq,
+                        const float* W_Hk, uint64_t* codes, int B, int Hq, int Hkv, int d, int r,
+                        int64_t cap, const int32_t* seq_lens, int64_t max_len, int k, float scale,
+                        float* out, int32_t* idx_out, void* ws, size_t ws_bytes, void* stream) {
+  return decode_step_impl(q, K, V, W_Hq, W_Hk, codes, B, Hq, Hkv, d, r, cap, seq_lens, max_len, k, scale,
+                          out, idx_out, ws, ws_bytes, stream);
 }
 
 size_t hata_workspace_bytes(int op, int B, int Hq, int Hkv, int d, int r, int64_t max_len, int k) {

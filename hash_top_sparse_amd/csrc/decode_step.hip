@@ -99,6 +99,7 @@ struct StepArgs {
   const uint16_t* K;
   const uint16_t* V;
   const float* W;
+  const float* Wk;  // key encoder (== W unless a separate one is given)
   uint64_t* codes;
   const int32_t* seq_lens;
   float* out;
@@ -183,7 +184,9 @@ __device__ __forceinline__ void cum_hist(uint32_t* hist, uint32_t* misc, uint32_
   __syncthreads();
 }
 
-template <int G>
+// SEP: the appended key row is encoded with a separate key encoder a.Wk
+// (a separate instance, so the shared-encoder code is unchanged).
+template <int G, bool SEP>
 __global__ __launch_bounds__(kNT) void decode_step_kernel(const StepArgs a) {
   using C = Cfg<G>;
   constexpr int NB = C::NB;
@@ -288,6 +291,13 @@ __global__ __launch_bounds__(kNT) void decode_step_kernel(const StepArgs a) {
   if (t < 64) misc[t] = (t < 3) ? (uint32_t)NB : 0u;
   __syncthreads();
   project_pack<G>(wr, qf, red, qcode, G);
+  if constexpr (SEP) {
+    // Independent query and key encoders (HashAttention summary page,
+    // "Approach"): the workgroup that owns the appended row reloads W's
+    // registers, no longer needed for the queries, with the key encoder's
+    // rows; the loads are in flight during its scan.
+    if (owns_new) load_w_regs(a.Wk + (int64_t)h * kD * kR, wr);
+  }
   if (bad_len) {
     // invalid length: every workgroup of the unit leaves here, before any
     // exchange, so the unit's flags stay consistent; workgroup 0 clears the
@@ -857,27 +867,32 @@ StepPlan plan_decode_step(int B, int Hq, int Hkv, int64_t max_len, int k, int nu
   return p;
 }
 
-template <int G>
-static hipError_t launch_step_g(const StepPlan& p, const StepArgs& a, hipStream_t s) {
+template <int G, bool SEP>
+static hipError_t launch_step_gs(const StepPlan& p, const StepArgs& a, hipStream_t s) {
   const size_t lds = p.lds_bytes;
   // raise the kernel's dynamic-LDS limit when a plan needs more than 64 KiB
   static std::atomic<size_t> configured{64 * 1024};
   if (lds > configured.load()) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&decode_step_kernel<G>),
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&decode_step_kernel<G, SEP>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
     configured.store(lds);
   }
-  hipLaunchKernelGGL(decode_step_kernel<G>, dim3(p.U * p.Wg), dim3(kNT), lds, s, a);
+  hipLaunchKernelGGL((decode_step_kernel<G, SEP>), dim3(p.U * p.Wg), dim3(kNT), lds, s, a);
   return hipGetLastError();
 }
 
+template <int G>
+static hipError_t launch_step_g(const StepPlan& p, const StepArgs& a, hipStream_t s) {
+  return a.Wk == a.W ? launch_step_gs<G, false>(p, a, s) : launch_step_gs<G, true>(p, a, s);
+}
+
 hipError_t launch_decode_step(const StepPlan& p, const uint16_t* q, const uint16_t* K,
-                              const uint16_t* V, const float* W, uint64_t* codes, int B, int Hq,
+                              const uint16_t* V, const float* W, const float* Wk, uint64_t* codes, int B, int Hq,
                               int Hkv, int64_t cap, const int32_t* seq_lens, int k, float scale,
                               float* out, int32_t* idx_out, unsigned char* ws, hipStream_t s) {
   StepArgs a;
-  a.q = q; a.K = K; a.V = V; a.W = W; a.codes = codes; a.seq_lens = seq_lens;
+  a.q = q; a.K = K; a.V = V; a.W = W; a.Wk = Wk ? Wk : W; a.codes = codes; a.seq_lens = seq_lens;
   a.out = out; a.idx_out = idx_out; a.cap = cap; a.Hq = Hq; a.Hkv = Hkv; a.k = k;
   a.scale = scale; a.Wg = p.Wg; a.chunk = p.chunk; a.xcd_map = p.xcd_map; a.U = p.U;
   a.xcd_local = (p.xcd_map && p.Wg > 1 && xcd_round_robin(s)) ? 1 : 0;

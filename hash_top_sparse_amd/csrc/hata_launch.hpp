@@ -49,7 +49,7 @@ struct StepPlan {
 };
 StepPlan plan_decode_step(int B, int Hq, int Hkv, int64_t max_len, int k, int num_cus);
 hipError_t launch_decode_step(const StepPlan& p, const uint16_t* q, const uint16_t* K,
-                              const uint16_t* V, const float* W, uint64_t* codes, int B, int Hq,
+                              const uint16_t* V, const float* W, const float* Wk, uint64_t* codes, int B, int Hq,
                               int Hkv, int64_t cap, const int32_t* seq_lens, int k, float scale,
                               float* out, int32_t* idx_out, unsigned char* ws, hipStream_t s);
 

@@ -173,6 +173,23 @@ int hata_decode_step(const void* q, const void* K, const void* V,
                      int32_t* idx_out, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * hata_decode_step with independent query and key encoders (HashAttention
+ * summary page, "Approach": separate query and key encoders): the G query
+ * rows of KV head h are encoded with W_Hq[h] and the appended key row with
+ * W_Hk[h] (both [Hkv][d][r] fp32, device); the cache rows [0, n_b-1) must
+ * hold W_Hk codes (build them with hata_encode_append and W_Hk).  With
+ * W_Hk == W_Hq this is hata_decode_step.  Same layouts, workspace, errors
+ * (HATA_ERR_NULL also for a NULL W_Hk) and results contract.  In the fused
+ * path only the workgroup that owns the appended row loads W_Hk.
+ */
+int hata_decode_step_qk(const void* q, const void* K, const void* V,
+                        const float* W_Hq, const float* W_Hk, uint64_t* codes,
+                        int B, int Hq, int Hkv, int d, int r, int64_t cap,
+                        const int32_t* seq_lens, int64_t max_len, int k,
+                        float scale, float* out, int32_t* idx_out, void* ws,
+                        size_t ws_bytes, void* stream);
+
+/*
  * Dense flash-decode baseline over all n_b rows of every unit (the same
  * attention with the kept set = every token), same layouts.
  * ws: hata_workspace_bytes(HATA_OP_DENSE_DECODE, ...).

@@ -140,6 +140,23 @@ def test_decode_step_validation():
     assert step(codes=MIS) == EALIGN
 
 
+def test_decode_step_qk_validation():
+    def step(**kw):
+        a = dict(q=A, K=A, V=A, Wq=A, Wk=A, codes=A, B=1, Hq=32, Hkv=8, d=128, r=128, cap=4096, seq=A,
+                 max_len=4096, k=512, out=A)
+        a.update(kw)
+        return binding.raw_call("hata_decode_step_qk", a["q"], a["K"], a["V"], a["Wq"], a["Wk"], a["codes"],
+                                a["B"], a["Hq"], a["Hkv"], a["d"], a["r"], ctypes.c_int64(a["cap"]), a["seq"],
+                                ctypes.c_int64(a["max_len"]), a["k"], F(0.088), a["out"], None, A,
+                                ctypes.c_size_t(1 << 30), None)
+    assert step(Wq=None) == ENULL
+    assert step(Wk=None) == ENULL
+    assert step(d=96) == EUNSUP
+    assert step(k=0) == EUNSUP
+    assert step(max_len=8192) == ESHAPE
+    assert step(codes=MIS) == EALIGN
+
+
 def lib_stream_read_valid():
     return binding.load().hata_stream_read(A, ctypes.c_size_t(4096), A, ctypes.c_size_t(1024), P(None))
 

@@ -346,3 +346,88 @@ def test_bulk_encode_matches_row_encode(hata_gpu, dist):
             for h in range(2):
                 check_codes(a[b, h, :3000], inp.K[b, h, :3000], inp.W[h], exact=False)
                 check_codes(b_[b, h, :3000], inp.K[b, h, :3000], inp.W[h], exact=False)
+
+
+# ------------------------------------- separate query and key encoders
+
+QK_CASES = [
+    # B, Hq, Hkv, N, k, dist, lens
+    (1, 32, 8, 8192, 512, "gauss", None),         # GQA-4, the owner of row n-1 reloads W_Hk
+    (8, 32, 32, 2048, 128, "gauss", None),        # one workgroup per unit: every workgroup owns its row
+    (1, 4, 1, 4096, 256, "exact", None),          # exact recipe: codes bit-exact
+    (2, 8, 2, 3000, 64, "gauss", [3000, 1]),      # ragged, n = 1 (the new key is the only token)
+]
+
+
+@pytest.mark.parametrize("case", QK_CASES, ids=lambda c: f"B{c[0]}-Hq{c[1]}-Hkv{c[2]}-N{c[3]}-k{c[4]}-{c[5]}")
+def test_decode_step_qk_matches_oracle(hata_gpu, case):
+    B, Hq, Hkv, N, k, dist, lens = case
+    s = _shape(B, Hq, Hkv, N, k, dist=dist, seed=7900 + N % 89)
+    lens = np.array(lens if lens else [N] * B, np.int32)
+    inp = synth.make_inputs(s, seq_lens=lens)
+    d = Dev(inp)
+    _log(f"qk step case {case}")
+    rng = np.random.default_rng(7950)
+    if dist == "exact":
+        Wk_np = rng.integers(-1, 2, size=inp.W.shape).astype(np.float32)
+    else:
+        Wk_np = (rng.standard_normal(inp.W.shape) / np.sqrt(128.0)).astype(np.float32)
+    Wk = torch.from_numpy(Wk_np).cuda()
+    # the cache holds key-encoder codes; row n-1 deliberately stale
+    codes = torch.zeros((B, Hkv, d.cap, 2), dtype=torch.int64, device="cuda")
+    hata_gpu.encode_append(d.K, Wk, codes, n_new=d.cap)
+    for b in range(B):
+        codes[b, :, int(lens[b]) - 1] = 0x1234
+    ws = hata_gpu.alloc_workspace(hata_gpu.OP_DECODE_STEP, B, Hq, Hkv, d.max_len, k)
+    out = torch.full((B, Hq, 128), np.nan, dtype=torch.float32, device="cuda")
+    idx = torch.full((B, Hkv, k), -9, dtype=torch.int32, device="cuda")
+    hata_gpu.decode_step_qk(d.q, d.K, d.V, d.W, Wk, codes, d.seq, d.max_len, k, inp.scale, out, ws, idx)
+    torch.cuda.synchronize()
+    assert hata_gpu.workspace_check(ws) == 0
+    cn = codes_np(codes)
+    for b in range(B):
+        n = int(lens[b])
+        for h in range(Hkv):  # the appended row is the key encoder's code
+            check_codes(cn[b, h, n - 1:n], inp.K[b, h, n - 1:n], Wk_np[h], exact=dist == "exact")
+    qc = codes_np(gpu_query_codes(hata_gpu, d))  # query codes from W_Hq
+    _, ref_idx, ref_out = oracle_units(inp, qc, cn)
+    np.testing.assert_array_equal(idx.cpu().numpy(), ref_idx)
+    assert_close(out.cpu().numpy(), ref_out)
+
+
+def test_decode_step_qk_staged_shape(hata_gpu):
+    """A shape whose per-unit chunk cannot stay on chip (130 units of 32,800
+    tokens: two workgroups per unit would need 260 CUs) runs the separate
+    kernels inside the call; the key row is still encoded with W_Hk.  Inputs
+    drawn on the device; a sample of units is checked against the oracle."""
+    B, Hq, Hkv, N, k = 1, 130, 130, 32800, 64
+    g = torch.Generator(device="cuda")
+    g.manual_seed(7990)
+    q = torch.randn((B, Hq, 128), generator=g, device="cuda").to(torch.bfloat16)
+    K = torch.randn((B, Hkv, N, 128), generator=g, device="cuda").to(torch.bfloat16)
+    V = torch.randn((B, Hkv, N, 128), generator=g, device="cuda").to(torch.bfloat16)
+    Wq = torch.randn((Hkv, 128, 128), generator=g, device="cuda") / np.sqrt(128.0)
+    Wk = torch.randn((Hkv, 128, 128), generator=g, device="cuda") / np.sqrt(128.0)
+    seq = torch.full((B,), N, dtype=torch.int32, device="cuda")
+    codes = torch.zeros((B, Hkv, N, 2), dtype=torch.int64, device="cuda")
+    hata_gpu.encode_append(K, Wk, codes, n_new=N)
+    codes[:, :, N - 1] = 0x1234
+    ws = hata_gpu.alloc_workspace(hata_gpu.OP_DECODE_STEP, B, Hq, Hkv, N, k)
+    out = torch.zeros((B, Hq, 128), dtype=torch.float32, device="cuda")
+    idx = torch.zeros((B, Hkv, k), dtype=torch.int32, device="cuda")
+    _log("qk staged shape: 130 units x 32800")
+    hata_gpu.decode_step_qk(q, K, V, Wq, Wk, codes, seq, N, k, 1.0 / np.sqrt(128.0), out, ws, idx)
+    torch.cuda.synchronize()
+    qc = torch.zeros((B, Hq, 1, 2), dtype=torch.int64, device="cuda")
+    hata_gpu.encode_append(q.view(B, Hq, 1, 128), Wq, qc, n_new=1)
+    bits = lambda t: t.view(torch.int16).cpu().numpy().view(np.uint16)
+    qcn = codes_np(qc.view(B, Hq, 2))
+    for h in (0, 1, 77, 129):
+        kb, vb = bits(K[0, h]), bits(V[0, h])
+        cn = codes_np(codes[0, h])
+        check_codes(cn[N - 1:N], kb[N - 1:N], Wk[h].cpu().numpy(), exact=False)
+        S = oracle.hamming_gqa(qcn[0, h:h + 1], cn)
+        ix = oracle.topk(S, k)
+        np.testing.assert_array_equal(idx[0, h].cpu().numpy(), ix)
+        ref = oracle.attention(bits(q[0, h:h + 1]), kb, vb, ix, 1.0 / np.sqrt(128.0))
+        assert_close(out[0, h:h + 1].cpu().numpy(), ref)
