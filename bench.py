@@ -163,7 +163,7 @@ def read_peak(gib: int = 4, reps: int = 5) -> float:
 
 
 def measure(cfg_id: int, steps: int, warmup: int, dense_steps: int, layers: int, use_graph: bool,
-            with_bulk: bool):
+            with_bulk: bool, with_qk: bool = True):
     """Time the fused step (and the dense baseline) on one workload; returns
     (result dict, inputs)."""
     import torch
@@ -252,6 +252,34 @@ def measure(cfg_id: int, steps: int, warmup: int, dense_steps: int, layers: int,
     per = np.array([evs[i].elapsed_time(evs[i + 1]) * 1e3 for i in range(nsp)])
     spread = {"steps": nsp, "median_us": float(np.median(per)), "p10_us": float(np.percentile(per, 10)),
               "p90_us": float(np.percentile(per, 90))}
+    # the same step with a separate key encoder (an equal-valued copy of W_H
+    # at another address, so the separate-encoder kernel instance runs)
+    Wk = W.clone()
+    qk = None
+
+    def step_qk(i):
+        Kl, Vl, cl = layer_bufs[i % L]
+        binding.decode_step_qk(q0, Kl, Vl, W, Wk, cl, seq, N, k, inp.scale, out, ws)
+
+    if with_qk and use_graph:
+        nqk = min(steps, 1024)
+        for i in range(8):
+            step_qk(i)
+        torch.cuda.synchronize()
+        gq = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gq):
+            for i in range(nqk):
+                step_qk(i)
+        gq.replay()
+        torch.cuda.synchronize()
+        ev0.record()
+        gq.replay()
+        ev1.record()
+        torch.cuda.synchronize()
+        qk_ms = ev0.elapsed_time(ev1) / nqk
+        del gq
+        qk = {"ms_per_step": qk_ms, "steps_per_s": 1000.0 / qk_ms}
+        log(f"fused step, separate key encoder: {qk_ms * 1e3:.2f} us/step")
     err = binding.workspace_check(ws)
     if err:
         raise RuntimeError(f"workspace error word {err}: a cross-workgroup wait timed out")
@@ -283,7 +311,8 @@ def measure(cfg_id: int, steps: int, warmup: int, dense_steps: int, layers: int,
     res = {"workload": shape.name, "ms_per_step": ms_step, "steps_per_s": 1000.0 / ms_step,
            "tokens_per_s": B * 1000.0 / ms_step,
            "GBs": achieved, "frac_of_peak": achieved / PEAK_HBM_GBS, "bytes_per_step": per_step,
-           "layers": L, "eager_step_spread": spread, "dense": dense, "bulk_encode": bulk}
+           "layers": L, "eager_step_spread": spread, "separate_key_encoder": qk, "dense": dense,
+           "bulk_encode": bulk}
     del layer_bufs
     torch.cuda.empty_cache()
     return res, inp
@@ -389,7 +418,7 @@ def main() -> int:
     binding.load()
     torch.cuda.set_device(0)
     if args.pmc_run:
-        measure(args.config, 32, 8, 0, args.layers, False, with_bulk=False)
+        measure(args.config, 32, 8, 0, args.layers, False, with_bulk=False, with_qk=False)
         src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
         dst = torch.empty_like(src)
         src.fill_(1)
@@ -408,7 +437,7 @@ def main() -> int:
             if c == args.config:
                 continue
             r, _ = measure(c, max(256, args.steps // 8), 16, 0 if args.no_dense else 32, 0,
-                           not args.no_graph, with_bulk=False)
+                           not args.no_graph, with_bulk=False, with_qk=False)
             sweep[str(c)] = r
 
     msweep = model_sweep() if args.model_sweep else None
@@ -446,6 +475,7 @@ def main() -> int:
                      "peak_measured_by": "hata_stream_read over 4 GiB, best of 5"},
         "tokens_per_s": head["tokens_per_s"],
         "eager_step_spread": head["eager_step_spread"],
+        "separate_key_encoder": head["separate_key_encoder"],
         "cpu_baseline": cpu,
         "dense_baseline": head["dense"],
         "bulk_encode": head["bulk_encode"],
