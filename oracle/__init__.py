@@ -95,9 +95,9 @@ def encode(x_bf16: np.ndarray, W: np.ndarray, return_proj: bool = False):
     x = _c(x_bf16, np.uint16)
     W = _c(W, np.float32)
     d, r = W.shape
-    assert x.shape[-1] == d and r % 64 == 0
+    assert x.shape[-1] == d and r >= 1
     rows = int(np.prod(x.shape[:-1], dtype=np.int64))
-    codes = np.zeros(x.shape[:-1] + (r // 64,), np.uint64)
+    codes = np.zeros(x.shape[:-1] + ((r + 63) // 64,), np.uint64)
     proj = np.zeros(x.shape[:-1] + (r,), np.float32) if return_proj else None
     lib().oracle_encode_rows(_p(x), rows, d, _p(W), r, _p(codes), _p(proj))
     return (codes, proj) if return_proj else codes
@@ -166,7 +166,7 @@ def decode_step(q, K, V, W, codes, seq_lens, k, scale, nthreads: int = 0,
     out = np.zeros((B, Hq, d), np.float32)
     idx = np.zeros((B, Hkv, k), np.int32)
     scores = np.full((B, Hkv, cap), -1, np.int32) if want_scores else None
-    qcodes = np.zeros((B, Hq, r // 64), np.uint64) if want_qcodes else None
+    qcodes = np.zeros((B, Hq, (r + 63) // 64), np.uint64) if want_qcodes else None
     Wk = None if Wk is None else _c(Wk, np.float32)
     if Wk is not None and Wk.shape != W.shape:
         raise ValueError("Wk must have W's shape")
@@ -204,7 +204,7 @@ def build_cache(K, W, seq_lens=None) -> np.ndarray:
     K = _c(K, np.uint16)
     B, Hkv, cap, d = K.shape
     r = W.shape[2]
-    codes = np.zeros((B, Hkv, cap, r // 64), np.uint64)
+    codes = np.zeros((B, Hkv, cap, (r + 63) // 64), np.uint64)
     for b in range(B):
         n = cap if seq_lens is None else int(seq_lens[b])
         for h in range(Hkv):

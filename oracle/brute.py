@@ -41,7 +41,7 @@ def encode(x_bits, W) -> list:
     """List of r/64 Python ints; bit c of the code is bit c%64 of word c//64."""
     p = project(x_bits, W)
     r = len(p)
-    words = [0] * (r // 64)
+    words = [0] * ((r + 63) // 64)
     for c in range(r):
         if p[c] >= 0.0:
             words[c // 64] += 1 << (c % 64)

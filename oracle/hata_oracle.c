@@ -21,7 +21,9 @@
  *   - inference hash = sign(x W_H): for sigma > 0 the sigmoid relaxation and
  *     the sign agree in sign, so sigma drops out;
  *   - bit = 1 iff the fp32 projection compares >= 0.0f (so -0.0 -> 1, NaN -> 0);
- *   - column c of the projection is bit (c mod 64) of 64-bit word c/64;
+ *   - column c of the projection is bit (c mod 64) of 64-bit word c/64; a
+ *     code of r bits takes ceil(r/64) words, bits r..63 of the last word zero
+ *     (r = 32 keeps one 64-bit word per row);
  *   - one W_H per KV head, shared by its G query heads and by q and k;
  *     W_H is stored [d][r] and a row vector x is projected as x * W_H;
  *   - query head j belongs to KV head j / G;
@@ -57,7 +59,7 @@ static float bf16_to_float(uint16_t h) {
  * packed LSB-first into r/64 words per row.  `proj` (nullable) receives p. */
 void oracle_encode_rows(const uint16_t* x, int64_t rows, int d, const float* W,
                         int r, uint64_t* codes, float* proj) {
-  const int words = r / 64;
+  const int words = (r + 63) / 64;
   for (int64_t row = 0; row < rows; ++row) {
     const uint16_t* xr = x + row * (int64_t)d;
     uint64_t* cr = codes + row * (int64_t)words;
@@ -194,12 +196,12 @@ int oracle_decode_step(const uint16_t* q, const uint16_t* K, const uint16_t* V,
                        int k, float scale, float* out, int32_t* idx_out,
                        int32_t* scores_out, uint64_t* qcodes_out,
                        int nthreads) {
-  if (B < 1 || Hkv < 1 || Hq % Hkv != 0 || r % 64 != 0 || d < 1 || k < 1)
+  if (B < 1 || Hkv < 1 || Hq % Hkv != 0 || r < 1 || d < 1 || k < 1)
     return -1;
   for (int b = 0; b < B; ++b)
     if (seq_lens[b] < 1 || seq_lens[b] > cap) return -1;
   const int G = Hq / Hkv;
-  const int words = r / 64;
+  const int words = (r + 63) / 64;
   const int units = B * Hkv;
   int bad = 0;
 #ifdef _OPENMP

@@ -322,6 +322,8 @@ def test_attention_subset_equals_scipy_on_gathered_rows(oracle_mod):
     (1, 4, 1, 40, 6, 16, 64, "gauss"),
     (2, 4, 2, 23, 30, 16, 64, "exact"),   # k > n
     (1, 2, 1, 33, 5, 128, 128, "gauss"),
+    (1, 4, 1, 40, 6, 16, 32, "gauss"),    # 32-bit codes (one word, high half zero)
+    (1, 2, 1, 21, 4, 16, 256, "gauss"),   # 256-bit codes
 ])
 def test_decode_step_matches_pure_python_brute_force(oracle_mod, B, Hq, Hkv, N, k, d, r, dist):
     from oracle import brute
@@ -334,7 +336,7 @@ def test_decode_step_matches_pure_python_brute_force(oracle_mod, B, Hq, Hkv, N, 
     else:
         inp.W = np.random.default_rng(5).standard_normal((Hkv, d, r)).astype(np.float32) / np.float32(np.sqrt(d))
     # the cache rows before the new token come from the pure-Python encoder
-    words = r // 64
+    words = (r + 63) // 64
     codes = np.zeros((B, Hkv, inp.cap, words), np.uint64)
     for b in range(B):
         for h in range(Hkv):
@@ -419,3 +421,50 @@ def test_decode_step_negated_key_encoder_complements_scores(oracle_mod):
             s = shared["scores"][b, h, :n].astype(np.int64)
             order = np.lexsort((np.arange(n), -s))[: inp.k]
             assert list(sep["idx"][b, h]) == sorted(order.tolist())
+
+
+
+# ------------------------------------------------ other code widths r
+# (HATA notes list the code width among the method's knobs; the
+# HashAttention summary page uses 32-bit signatures.)  Closed forms: with W
+# the first r columns of the identity (r <= d) bit c is (x_c >= 0); with
+# W = [I, -I] (r = 2d) bit c is (x_c >= 0) and bit d + c is (x_c <= 0).  The
+# code of r bits occupies ceil(r/64) words with the bits past r zero.
+
+
+@pytest.mark.parametrize("r", [32, 64, 256])
+def test_encode_identity_columns_each_width(oracle_mod, r):
+    d = 128
+    x = synth.bf16_bits(RNG.standard_normal((40, d)).astype(np.float32))
+    x[0, :8] = 0  # exact zeros: bit 1 in both halves of [I, -I]
+    if r <= d:
+        W = np.eye(d, dtype=np.float32)[:, :r]
+    else:
+        W = np.concatenate([np.eye(d, dtype=np.float32), -np.eye(d, dtype=np.float32)], axis=1)
+    codes = oracle_mod.encode(x, W)
+    assert codes.shape == (40, (r + 63) // 64)
+    xf = synth.bf16_to_f32(x)
+    for row in range(40):
+        bits = _bits_of(codes[row], 64 * codes.shape[1])
+        want = np.zeros(64 * codes.shape[1], np.int64)
+        if r <= d:
+            want[:r] = xf[row, :r] >= 0
+        else:
+            want[:d] = xf[row] >= 0
+            want[d:2 * d] = xf[row] <= 0
+        np.testing.assert_array_equal(bits, want)
+
+
+@pytest.mark.parametrize("r", [32, 64, 256])
+def test_hamming_each_width_counts_differing_bits(oracle_mod, r):
+    d = 128
+    x = synth.bf16_bits(RNG.standard_normal((30, d)).astype(np.float32))
+    W = _gauss_W(d, r)
+    c = oracle_mod.encode(x, W)
+    q = c[:3]
+    S = oracle_mod.hamming_gqa(q, c)
+    for i in range(30):
+        want = sum(int(np.sum(_bits_of(q[g], 64 * c.shape[1]) != _bits_of(c[i], 64 * c.shape[1])))
+                   for g in range(3))
+        assert S[i] == want
+        assert 0 <= S[i] <= 3 * r
