@@ -107,7 +107,8 @@ def _stream(stream=None):
 
 def encode_append(x: torch.Tensor, W_H: torch.Tensor, codes: torch.Tensor, n_new: int,
                   pos: torch.Tensor | None = None, stream=None) -> None:
-    """x bf16 [B,H,x_rows,d]; W_H f32 [Hkv,d,r]; codes int64 [B,H,cap,r/64]."""
+    """x bf16 [B,H,x_rows,d]; W_H f32 [Hkv,d,r]; codes int64 [B,H,cap,ceil(r/64)]
+    (r in 32, 64, 128, 256; for r = 32 the high half of each word stays 0)."""
     _need(x, torch.bfloat16, "x")
     _need(W_H, torch.float32, "W_H")
     _need(codes, torch.int64, "codes")
@@ -121,15 +122,16 @@ def encode_append(x: torch.Tensor, W_H: torch.Tensor, codes: torch.Tensor, n_new
 
 
 def hamming_scores(q_codes: torch.Tensor, k_codes: torch.Tensor, seq_lens: torch.Tensor,
-                   max_len: int, scores: torch.Tensor, stream=None) -> None:
-    """q_codes int64 [B,Hq,2]; k_codes int64 [B,Hkv,cap,2]; scores int16 [B,Hkv,cap]."""
+                   max_len: int, scores: torch.Tensor, stream=None, r: int | None = None) -> None:
+    """q_codes int64 [B,Hq,ceil(r/64)]; k_codes int64 [B,Hkv,cap,ceil(r/64)]; scores int16
+    [B,Hkv,cap].  r defaults to 64 bits per code word."""
     _need(q_codes, torch.int64, "q_codes")
     _need(k_codes, torch.int64, "k_codes")
     _need(scores, torch.int16, "scores")
     _need(seq_lens, torch.int32, "seq_lens")
     B, Hq, words = q_codes.shape
     _, Hkv, cap, _ = k_codes.shape
-    _check(load().hata_hamming_scores(_ptr(q_codes), _ptr(k_codes), B, Hq, Hkv, words * 64, cap,
+    _check(load().hata_hamming_scores(_ptr(q_codes), _ptr(k_codes), B, Hq, Hkv, int(r or words * 64), cap,
                                       _ptr(seq_lens), int(max_len), _ptr(scores), _stream(stream)))
 
 
@@ -150,9 +152,10 @@ def workspace_bytes(op: int, B: int, Hq: int, Hkv: int, max_len: int, k: int, d:
 
 
 def alloc_workspace(op: int, B: int, Hq: int, Hkv: int, max_len: int, k: int,
-                    device="cuda") -> torch.Tensor:
-    """A zeroed workspace tensor (uint8) for operation `op` at these sizes."""
-    n = max(workspace_bytes(op, B, Hq, Hkv, max_len, k), 256)
+                    device="cuda", r: int = 128) -> torch.Tensor:
+    """A zeroed workspace tensor (uint8) for operation `op` at these sizes
+    (r: code width in bits)."""
+    n = max(workspace_bytes(op, B, Hq, Hkv, max_len, k, r=r), 256)
     return torch.zeros(n, dtype=torch.uint8, device=device)
 
 

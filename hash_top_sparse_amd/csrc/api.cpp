@@ -70,7 +70,8 @@ bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) %
 
 int check_dims(int d, int r) {
   if (d != 128) return fail(HATA_ERR_UNSUPPORTED, "head dim d=%d unsupported (only 128)", d);
-  if (r != 128) return fail(HATA_ERR_UNSUPPORTED, "code width r=%d unsupported (only 128)", r);
+  if (r != 32 && r != 64 && r != 128 && r != 256)
+    return fail(HATA_ERR_UNSUPPORTED, "code width r=%d unsupported (32, 64, 128, 256)", r);
   return HATA_OK;
 }
 
@@ -138,10 +139,12 @@ int hata_encode_append(const void* x, int64_t x_rows, int B, int H, int n_new, c
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const auto* xb = static_cast<const uint16_t*>(x);
   hipError_t e;
-  if (n_new >= hata::kBulkMinRows)
+  // the matrix-core bulk encode is written for 128-bit codes; other widths
+  // use the row kernel for every row count
+  if (n_new >= hata::kBulkMinRows && r == 128)
     e = hata::launch_encode_bulk(xb, x_rows, B, H, Hkv, n_new, W_H, codes, cap, pos, 0, s);
   else
-    e = hata::launch_encode_rows(xb, x_rows, B, H, Hkv, n_new, W_H, codes, cap, pos, 0, s);
+    e = hata::launch_encode_rows(xb, x_rows, B, H, Hkv, n_new, W_H, codes, cap, pos, 0, s, r);
   return check_launch(e, "encode_append launch");
 }
 
@@ -157,7 +160,7 @@ int hata_hamming_scores(const uint64_t* q_codes, const uint64_t* k_codes, int B,
     return fail(HATA_ERR_ALIGN, "hamming_scores: k_codes must be 16-byte aligned");
   if ((st = pre_launch("hamming_scores"))) return st;
   hipError_t e = hata::launch_hamming(q_codes, k_codes, B, Hq, Hkv, cap, seq_lens, max_len, scores,
-                                      cap, reinterpret_cast<hipStream_t>(stream));
+                                      cap, reinterpret_cast<hipStream_t>(stream), r);
   return check_launch(e, "hamming_scores launch");
 }
 
@@ -171,8 +174,8 @@ int hata_topk(const uint16_t* scores, int B, int Hkv, int64_t cap, const int32_t
   int st = check_len(cap, max_len);
   if (st) return st;
   if ((st = check_k(k))) return st;
-  if (max_score < 0 || max_score > 8 * 128)
-    return fail(HATA_ERR_UNSUPPORTED, "topk: max_score=%d outside [0, 1024]", max_score);
+  if (max_score < 0 || max_score > 8 * 256)
+    return fail(HATA_ERR_UNSUPPORTED, "topk: max_score=%d outside [0, 2048]", max_score);
   if (!aligned(scores, 2) || !aligned(idx, 4)) return fail(HATA_ERR_ALIGN, "topk: misaligned buffer");
   if ((st = pre_launch("topk"))) return st;
   hipError_t e = hata::launch_topk(scores, cap, B, Hkv, cap, seq_lens, k, max_score, idx,
@@ -255,7 +258,7 @@ static int decode_step_impl(const void* q, const void* K, const void* V, const f
     return fail(HATA_ERR_ALIGN, "decode_step: q, K, V and codes must be 16-byte aligned");
   int cus = 0;
   if ((st = current_cus(&cus))) return st;
-  const hata::StepPlan p = hata::plan_decode_step(B, Hq, Hkv, max_len, k, cus);
+  const hata::StepPlan p = hata::plan_decode_step(B, Hq, Hkv, max_len, k, cus, r);
   if (!ws || ws_bytes < p.total)
     return fail(HATA_ERR_WORKSPACE, "decode_step: workspace of %zu bytes needed, %zu given", p.total, ws_bytes);
   if ((st = pre_launch("decode_step"))) return st;
@@ -274,14 +277,14 @@ static int decode_step_impl(const void* q, const void* K, const void* V, const f
   auto* qc = reinterpret_cast<uint64_t*>(wsb + p.off_qc);
   auto* sc = reinterpret_cast<uint16_t*>(wsb + p.off_scores);
   auto* part = reinterpret_cast<float*>(wsb + p.off_attn);
-  hipError_t e = hata::launch_encode_rows(qb, 1, B, Hq, Hkv, 1, W_H, qc, 1, nullptr, 0, s);
+  hipError_t e = hata::launch_encode_rows(qb, 1, B, Hq, Hkv, 1, W_H, qc, 1, nullptr, 0, s, r);
   if (e == hipSuccess)  // key append at row seq_lens[b] - 1
-    e = hata::launch_encode_rows(Kb, cap, B, Hkv, Hkv, 1, W_Hk, codes, cap, seq_lens, -1, s);
+    e = hata::launch_encode_rows(Kb, cap, B, Hkv, Hkv, 1, W_Hk, codes, cap, seq_lens, -1, s, r);
   (void)G;
-  if (e == hipSuccess) e = hata::launch_hamming(qc, codes, B, Hq, Hkv, cap, seq_lens, max_len, sc, max_len, s);
+  if (e == hipSuccess) e = hata::launch_hamming(qc, codes, B, Hq, Hkv, cap, seq_lens, max_len, sc, max_len, s, r);
   int32_t* idx = idx_out;
   if (e == hipSuccess && !idx) return fail(HATA_ERR_UNSUPPORTED, "decode_step: this shape needs idx_out");
-  if (e == hipSuccess) e = hata::launch_topk(sc, max_len, B, Hkv, cap, seq_lens, k, G * 128, idx, s);
+  if (e == hipSuccess) e = hata::launch_topk(sc, max_len, B, Hkv, cap, seq_lens, k, G * r, idx, s);
   if (e == hipSuccess)
     e = hata::launch_attention(qb, Kb, Vb, B, Hq, Hkv, cap, idx, k, nullptr, k, scale, out, part, s);
   return check_launch(e, "decode_step (staged) launch");
@@ -305,8 +308,8 @@ int hata_decode_step_qk(const void* q, const void* K, const void* V, const float
 
 size_t hata_workspace_bytes(int op, int B, int Hq, int Hkv, int d, int r, int64_t max_len, int k) {
   (void)d;
-  (void)r;
   if (B < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || max_len < 1 || k < 1) return 0;
+  if (r != 32 && r != 64 && r != 128 && r != 256) return 0;
   const int G = Hq / Hkv;
   switch (op) {
     case HATA_OP_TOPK:
@@ -318,7 +321,7 @@ size_t hata_workspace_bytes(int op, int B, int Hq, int Hkv, int d, int r, int64_
     case HATA_OP_DECODE_STEP: {
       int cus = 0;
       if (current_cus(&cus) != HATA_OK) return 0;
-      return hata::plan_decode_step(B, Hq, Hkv, max_len, k, cus).total;
+      return hata::plan_decode_step(B, Hq, Hkv, max_len, k, cus, r).total;
     }
     default:
       return 0;

@@ -63,16 +63,18 @@ constexpr uint32_t kSpinLimit = 1u << 22;
 constexpr int kXccIdReg = 20 | (31 << 11);
 constexpr int kShortList = 64;     // kept rows staged in LDS per attention batch
 
-template <int G>
+template <int G, int R = kR>
 struct Cfg {
-  static constexpr int NB = G * kR + 1;           // histogram bins
+  static constexpr int W64 = Width<R>::W64;       // 64-bit words per code row
+  static constexpr int NB = G * R + 1;            // histogram bins
   static constexpr int NBP = (NB + 63) / 64 * 64;
-  // code loads in flight per thread (a ring: 32 KiB per workgroup); deeper
-  // rings delay W_H, which shares the CU's vector-memory path
-  static constexpr int PF = 8;
+  // code rows in flight per thread (a ring of 32 KiB per workgroup: 8 rows of
+  // 16 bytes, 16 of 8 or 4 of 32); deeper rings delay W_H, which shares the
+  // CU's vector-memory path
+  static constexpr int PF = (R <= 64) ? 16 : (R == 128) ? 8 : 4;
   static constexpr int HDRP = (2 * G + 3) / 4 * 4; // partial record header floats (M[G], L[G])
   static constexpr int RECP = HDRP + G * kD;       // partial record floats
-  static constexpr int PROJ = 4 * (G + 1) * kR;    // projection reduction floats
+  static constexpr int PROJ = 4 * (G + 1) * R;     // projection reduction floats
   static constexpr int RED0 = (kMergeFloats<G> > PROJ) ? kMergeFloats<G> : PROJ;
   static constexpr int RED = (RED0 > (G + 4) * kRec) ? RED0 : (G + 4) * kRec;
   // LDS offsets in bytes
@@ -80,8 +82,8 @@ struct Cfg {
   static constexpr int NSTG = (G + 1 + 3) / 4;                   // staging loads per thread
   static constexpr int o_qf = o_hist + NBP * 4;                  // 4*NSTG rows of 128 float (G+1 used)
   static constexpr int o_red = o_qf + 4 * NSTG * kD * 4;         // RED float
-  static constexpr int o_qcode = o_red + RED * 4;                // (G+1)*2 uint64
-  static constexpr int o_misc = o_qcode + (G + 1) * 16;          // 64 uint32
+  static constexpr int o_qcode = o_red + RED * 4;                // (G+1)*W64 uint64
+  static constexpr int o_misc = o_qcode + (G + 1) * W64 * 8;     // 64 uint32
   static constexpr int o_whdr = o_misc + 64 * 4;                 // kMaxWg int4 + 2*4*64 uint32
   static constexpr int o_win = o_whdr + 4 * kMaxWg * 4 + 2048;   // kMaxWg*kWinBytes (also combine staging)
   static constexpr int o_kvs = o_win + kMaxWg * kWinBytes;       // kShortList K/V rows
@@ -185,10 +187,12 @@ __device__ __forceinline__ void cum_hist(uint32_t* hist, uint32_t* misc, uint32_
 }
 
 // SEP: the appended key row is encoded with a separate key encoder a.Wk
-// (a separate instance, so the shared-encoder code is unchanged).
-template <int G, bool SEP>
+// (a separate instance, so the shared-encoder code is unchanged).  R: code
+// width in bits (32, 64, 128, 256).
+template <int G, bool SEP, int R>
 __global__ __launch_bounds__(kNT) void decode_step_kernel(const StepArgs a) {
-  using C = Cfg<G>;
+  using C = Cfg<G, R>;
+  constexpr int W64 = C::W64, W32 = Width<R>::W32;
   constexpr int NB = C::NB;
   constexpr int PF = C::PF;
   extern __shared__ __align__(16) unsigned char smem[];
@@ -228,8 +232,8 @@ __global__ __launch_bounds__(kNT) void decode_step_kernel(const StepArgs a) {
     if (i * kNT < 64 * G)  // slots that hold query rows (known at compile time)
       xrow[i] = reinterpret_cast<const uint32_t*>(a.q + ((int64_t)b * a.Hq + (int64_t)h * G + r) * kD)[c2];
   }
-  WRegs wr;
-  load_w_regs(a.W + (int64_t)h * kD * kR, wr);
+  WRegs<R> wr;
+  load_w_regs<R>(a.W + (int64_t)h * kD * R, wr);
   const uint32_t epoch =
       CohBuf(a.flags + (int64_t)unit * kMaxWg, a.Wg > 1 ? kMaxWg * 4 : 0).ld4(w * 4);
   // An invalid length is handled after the projection (below); until then
@@ -238,10 +242,10 @@ __global__ __launch_bounds__(kNT) void decode_step_kernel(const StepArgs a) {
   const int lo = w * a.chunk;
   // the code ring's first PF*256 rows of the chunk, clamped into the cache
   // (rows past the sequence end are loaded and never scored)
-  const uint4* cunit = reinterpret_cast<const uint4*>(a.codes) + row0;
-  uint4 cbuf[PF];
+  const uint64_t* cunit = a.codes + row0 * W64;
+  CodeRow<R> cbuf[PF];
 #pragma unroll
-  for (int j = 0; j < PF; ++j) cbuf[j] = load_stream16(cunit + min((int64_t)lo + j * kNT + t, cap - 1));
+  for (int j = 0; j < PF; ++j) cbuf[j] = load_code<R>(cunit, min((int64_t)lo + j * kNT + t, cap - 1));
   // This workgroup's exchange lines (its histogram window and its partial
   // record) have usually left L2 since the previous step; the unit's first
   // reads of them after the flag take about 1 us then, against about 0.4 us
@@ -275,7 +279,7 @@ __global__ __launch_bounds__(kNT) void decode_step_kernel(const StepArgs a) {
   // row n-1 of K (row 0 when this workgroup does not own it): dword `lane`
   const uint32_t krow = reinterpret_cast<const uint32_t*>(a.K + (row0 + (owns_new ? n - 1 : 0)) * kD)[lane];
   // ring refills: rows lo + li for li < cnt
-  const uint4* cbase = cunit + (cnt > 0 ? lo : 0);
+  const uint64_t* cbase = cunit + (int64_t)(cnt > 0 ? lo : 0) * W64;
 
   // ---- 2. encode the query rows.  Every staging slot is stored (slots past
   // the G query rows are zero), so no load is consumed under a branch.
@@ -290,13 +294,13 @@ __global__ __launch_bounds__(kNT) void decode_step_kernel(const StepArgs a) {
   for (int i = t; i < C::NBP; i += kNT) hist[i] = 0;
   if (t < 64) misc[t] = (t < 3) ? (uint32_t)NB : 0u;
   __syncthreads();
-  project_pack<G>(wr, qf, red, qcode, G);
+  project_pack<G, R>(wr, qf, red, qcode, G);
   if constexpr (SEP) {
     // Independent query and key encoders (HashAttention summary page,
     // "Approach"): the workgroup that owns the appended row reloads W's
     // registers, no longer needed for the queries, with the key encoder's
     // rows; the loads are in flight during its scan.
-    if (owns_new) load_w_regs(a.Wk + (int64_t)h * kD * kR, wr);
+    if (owns_new) load_w_regs<R>(a.Wk + (int64_t)h * kD * R, wr);
   }
   if (bad_len) {
     // invalid length: every workgroup of the unit leaves here, before any
@@ -310,21 +314,21 @@ __global__ __launch_bounds__(kNT) void decode_step_kernel(const StepArgs a) {
     }
     return;
   }
-  uint32_t qw[G][kWords32];
+  uint32_t qw[G][W32];
 #pragma unroll
-  for (int g = 0; g < G; ++g) {
-    const uint64_t x0 = qcode[g * 2], x1 = qcode[g * 2 + 1];
-    qw[g][0] = (uint32_t)x0; qw[g][1] = (uint32_t)(x0 >> 32);
-    qw[g][2] = (uint32_t)x1; qw[g][3] = (uint32_t)(x1 >> 32);
-  }
-  QMasks<G> qm;
-  build_qmasks<G>(qw, qm);
+  for (int g = 0; g < G; ++g)
+#pragma unroll
+    for (int wd = 0; wd < W32; ++wd) qw[g][wd] = (uint32_t)(qcode[g * W64 + (wd >> 1)] >> ((wd & 1) * 32));
+  QMasks<G, R> qm;
+  build_qmasks<G, R>(qw, qm);
 
   // ---- 3. score the owned tokens.  Each ring slot is scored, then refilled
   // with the load PF*256 tokens ahead.  Row n-1 is scored from the cache
   // like the others and corrected afterwards by the thread that scored it.
-  auto score_one = [&](const uint4 c, int li) {
-    const uint32_t s = gqa_hamming<G>(c, qm);
+  auto score_one = [&](const CodeRow<R>& c, int li) {
+    uint32_t cw[W32];
+    code_words<R>(c, cw);
+    const uint32_t s = gqa_hamming_w<G, R>(cw, qm);
     sc[li] = (uint16_t)s;
     atomicAdd(&hist[s], 1u);
   };
@@ -335,7 +339,7 @@ __global__ __launch_bounds__(kNT) void decode_step_kernel(const StepArgs a) {
     for (int j = 0; j < PF; ++j) {
       const int li = base + j * kNT + t;
       score_one(cbuf[j], li);
-      cbuf[j] = load_stream16(cbase + li + BATCH);
+      cbuf[j] = load_code<R>(cbase, li + BATCH);
     }
   }
   if (base + BATCH <= cnt) {  // a full batch, the next one partial or empty
@@ -343,7 +347,7 @@ __global__ __launch_bounds__(kNT) void decode_step_kernel(const StepArgs a) {
     for (int j = 0; j < PF; ++j) {
       const int li = base + j * kNT + t;
       score_one(cbuf[j], li);
-      if (li + BATCH < cnt) cbuf[j] = load_stream16(cbase + li + BATCH);
+      if (li + BATCH < cnt) cbuf[j] = load_code<R>(cbase, li + BATCH);
     }
     base += BATCH;
   }
@@ -364,13 +368,14 @@ __global__ __launch_bounds__(kNT) void decode_step_kernel(const StepArgs a) {
       qf[G * kD + 2 * lane + 1] = bf16_hi(krow);
     }
     __syncthreads();
-    project_pack<1>(wr, qf + G * kD, red, qcode + G * 2, 1);
-    const uint64_t k0 = qcode[G * 2], k1 = qcode[G * 2 + 1];
-    const uint4 newc = make_uint4((uint32_t)k0, (uint32_t)(k0 >> 32), (uint32_t)k1, (uint32_t)(k1 >> 32));
-    if (t == 0) reinterpret_cast<uint4*>(a.codes)[row0 + n - 1] = newc;
+    project_pack<1, R>(wr, qf + G * kD, red, qcode + G * W64, 1);
+    if (t < W64) a.codes[(row0 + n - 1) * W64 + t] = qcode[G * W64 + t];
     if (t == new_li % kNT) {
+      uint32_t cw[W32];
+#pragma unroll
+      for (int wd = 0; wd < W32; ++wd) cw[wd] = (uint32_t)(qcode[G * W64 + (wd >> 1)] >> ((wd & 1) * 32));
       const uint32_t s_old = sc[new_li];
-      const uint32_t s_new = gqa_hamming<G>(newc, qm);
+      const uint32_t s_new = gqa_hamming_w<G, R>(cw, qm);
       atomicSub(&hist[s_old], 1u);
       atomicAdd(&hist[s_new], 1u);
       sc[new_li] = (uint16_t)s_new;
@@ -806,8 +811,19 @@ bool xcd_round_robin(hipStream_t user) {
 
 }  // namespace
 
-StepPlan plan_decode_step(int B, int Hq, int Hkv, int64_t max_len, int k, int num_cus) {
+template <int G>
+static void cfg_sizes(int r, int k, int chunk, size_t* lds, size_t* recp) {
+  switch (r) {
+    case 32: *lds = Cfg<G, 32>::lds_bytes(k, chunk); *recp = Cfg<G, 32>::RECP; break;
+    case 64: *lds = Cfg<G, 64>::lds_bytes(k, chunk); *recp = Cfg<G, 64>::RECP; break;
+    case 256: *lds = Cfg<G, 256>::lds_bytes(k, chunk); *recp = Cfg<G, 256>::RECP; break;
+    default: *lds = Cfg<G, 128>::lds_bytes(k, chunk); *recp = Cfg<G, 128>::RECP; break;
+  }
+}
+
+StepPlan plan_decode_step(int B, int Hq, int Hkv, int64_t max_len, int k, int num_cus, int r) {
   StepPlan p;
+  p.R = r;
   p.G = Hq / Hkv;
   p.U = B * Hkv;
   const int U = p.U;
@@ -834,15 +850,15 @@ StepPlan plan_decode_step(int B, int Hq, int Hkv, int64_t max_len, int k, int nu
   p.xcd_map = (Wg > 1 && U % 8 == 0) ? 1 : 0;
   auto align = [](size_t x) { return (x + 255) / 256 * 256; };
   const int G = p.G;
-  const int NB = G * kR + 1;
+  const int NB = G * r + 1;
   p.full_words = (NB + 1) / 2;
   size_t recp = 0;
   if (p.fused) {
     switch (G) {
-      case 1: p.lds_bytes = Cfg<1>::lds_bytes(k, p.chunk); recp = Cfg<1>::RECP; break;
-      case 2: p.lds_bytes = Cfg<2>::lds_bytes(k, p.chunk); recp = Cfg<2>::RECP; break;
-      case 4: p.lds_bytes = Cfg<4>::lds_bytes(k, p.chunk); recp = Cfg<4>::RECP; break;
-      default: p.lds_bytes = Cfg<8>::lds_bytes(k, p.chunk); recp = Cfg<8>::RECP; break;
+      case 1: cfg_sizes<1>(r, k, p.chunk, &p.lds_bytes, &recp); break;
+      case 2: cfg_sizes<2>(r, k, p.chunk, &p.lds_bytes, &recp); break;
+      case 4: cfg_sizes<4>(r, k, p.chunk, &p.lds_bytes, &recp); break;
+      default: cfg_sizes<8>(r, k, p.chunk, &p.lds_bytes, &recp); break;
     }
     // 160 KiB of LDS per CU, less the kernel's static LDS and a margin
     if (p.lds_bytes > 159 * 1024) p.fused = false;
@@ -859,7 +875,7 @@ StepPlan plan_decode_step(int B, int Hq, int Hkv, int64_t max_len, int k, int nu
     }
   } else {
     // staged steps inside hata_decode_step
-    p.off_qc = off;     off = align(off + (size_t)B * Hq * 16);
+    p.off_qc = off;     off = align(off + (size_t)B * Hq * ((r + 63) / 64) * 8);
     p.off_scores = off; off = align(off + (size_t)U * max_len * 2);
     p.off_attn = off;   off = align(off + attn_part_floats(B, Hkv, G, k) * 4);
   }
@@ -867,19 +883,29 @@ StepPlan plan_decode_step(int B, int Hq, int Hkv, int64_t max_len, int k, int nu
   return p;
 }
 
-template <int G, bool SEP>
-static hipError_t launch_step_gs(const StepPlan& p, const StepArgs& a, hipStream_t s) {
+template <int G, bool SEP, int R>
+static hipError_t launch_step_gsr(const StepPlan& p, const StepArgs& a, hipStream_t s) {
   const size_t lds = p.lds_bytes;
   // raise the kernel's dynamic-LDS limit when a plan needs more than 64 KiB
   static std::atomic<size_t> configured{64 * 1024};
   if (lds > configured.load()) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&decode_step_kernel<G, SEP>),
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&decode_step_kernel<G, SEP, R>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
     configured.store(lds);
   }
-  hipLaunchKernelGGL((decode_step_kernel<G, SEP>), dim3(p.U * p.Wg), dim3(kNT), lds, s, a);
+  hipLaunchKernelGGL((decode_step_kernel<G, SEP, R>), dim3(p.U * p.Wg), dim3(kNT), lds, s, a);
   return hipGetLastError();
+}
+
+template <int G, bool SEP>
+static hipError_t launch_step_gs(const StepPlan& p, const StepArgs& a, hipStream_t s) {
+  switch (p.R) {
+    case 32: return launch_step_gsr<G, SEP, 32>(p, a, s);
+    case 64: return launch_step_gsr<G, SEP, 64>(p, a, s);
+    case 256: return launch_step_gsr<G, SEP, 256>(p, a, s);
+    default: return launch_step_gsr<G, SEP, 128>(p, a, s);
+  }
 }
 
 template <int G>

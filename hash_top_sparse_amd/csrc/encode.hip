@@ -7,9 +7,10 @@
 // word c/64, bit c%64.
 //
 // GEMV form for a few rows per (sequence, KV head): a 256-thread workgroup
-// holds the KV head's W_H in registers (16 float4 per thread) and packs each
-// 64-column half of a code with one wave64 ballot (project_pack); the fused
-// decode step uses the same routine, so both produce identical codes.
+// holds the KV head's W_H in registers (16 rows of r/32 columns per thread)
+// and packs each 64-column word of a code with one wave64 ballot
+// (project_pack); the fused decode step uses the same routine, so both
+// produce identical codes.  Code widths r = 32, 64, 128, 256.
 #include "hata_device.hpp"
 #include "hata_launch.hpp"
 
@@ -19,13 +20,15 @@ namespace {
 
 constexpr int kRowsPerBatch = 4;
 
+template <int R>
 __global__ __launch_bounds__(kNT) void encode_rows_kernel(
     const uint16_t* __restrict__ x, int64_t x_rows, int H, int Hkv, int n_new,
     const float* __restrict__ W, uint64_t* __restrict__ codes, int64_t cap,
     const int32_t* __restrict__ pos, int pos_off, int rows_per_block) {
+  constexpr int W64 = Width<R>::W64;
   __shared__ __align__(16) float xs[kRowsPerBatch * kD];
-  __shared__ __align__(16) float red[4 * kRowsPerBatch * kR];
-  __shared__ uint64_t cw[kRowsPerBatch * 2];
+  __shared__ __align__(16) float red[4 * kRowsPerBatch * R];
+  __shared__ uint64_t cw[kRowsPerBatch * W64];
   const int t = threadIdx.x;
   const int G = H / Hkv;
   const int bh = blockIdx.y;
@@ -36,8 +39,8 @@ __global__ __launch_bounds__(kNT) void encode_rows_kernel(
   const int r_end = min(total, r_begin + rows_per_block);
   if (r_begin >= r_end) return;
 
-  WRegs wr;
-  load_w_regs(W + (int64_t)hk * kD * kR, wr);
+  WRegs<R> wr;
+  load_w_regs<R>(W + (int64_t)hk * kD * R, wr);
 
   const int64_t p_b = (pos ? (int64_t)pos[b] : 0) + pos_off;
   const int64_t lim = x_rows < cap ? x_rows : cap;
@@ -63,14 +66,14 @@ __global__ __launch_bounds__(kNT) void encode_rows_kernel(
     }
     __syncthreads();
     const int nr = min(kRowsPerBatch, r_end - r0);
-    project_pack<kRowsPerBatch>(wr, xs, red, cw, nr);
-    if (t < nr * 2) {
-      const int r = r0 + (t >> 1);
+    project_pack<kRowsPerBatch, R>(wr, xs, red, cw, nr);
+    if (t < nr * W64) {
+      const int r = r0 + t / W64;
       const int g = r / n_new, j = r - g * n_new;
       const int64_t ridx = p_b + j;
       if (ridx >= 0 && ridx < lim) {
         const int64_t head = (int64_t)b * H + (int64_t)hk * G + g;
-        codes[(head * cap + ridx) * 2 + (t & 1)] = cw[t];
+        codes[(head * cap + ridx) * W64 + t % W64] = cw[t];
       }
     }
   }
@@ -80,7 +83,7 @@ __global__ __launch_bounds__(kNT) void encode_rows_kernel(
 
 hipError_t launch_encode_rows(const uint16_t* x, int64_t x_rows, int B, int H, int Hkv, int n_new,
                               const float* W, uint64_t* codes, int64_t cap, const int32_t* pos,
-                              int pos_off, hipStream_t s) {
+                              int pos_off, hipStream_t s, int r) {
   const int G = H / Hkv;
   const int64_t total = (int64_t)G * n_new;
   // enough blocks to cover the chip for long row runs, few rows per block otherwise
@@ -89,8 +92,16 @@ hipError_t launch_encode_rows(const uint16_t* x, int64_t x_rows, int B, int H, i
   rpb = (rpb + kRowsPerBatch - 1) / kRowsPerBatch * kRowsPerBatch;
   const int64_t nbx = (total + rpb - 1) / rpb;
   dim3 grid((unsigned)nbx, (unsigned)(B * Hkv));
-  hipLaunchKernelGGL(encode_rows_kernel, grid, dim3(kNT), 0, s, x, x_rows, H, Hkv, n_new, W, codes,
-                     cap, pos, pos_off, (int)rpb);
+  switch (r) {
+    case 32: hipLaunchKernelGGL(encode_rows_kernel<32>, grid, dim3(kNT), 0, s, x, x_rows, H, Hkv, n_new, W,
+                                codes, cap, pos, pos_off, (int)rpb); break;
+    case 64: hipLaunchKernelGGL(encode_rows_kernel<64>, grid, dim3(kNT), 0, s, x, x_rows, H, Hkv, n_new, W,
+                                codes, cap, pos, pos_off, (int)rpb); break;
+    case 256: hipLaunchKernelGGL(encode_rows_kernel<256>, grid, dim3(kNT), 0, s, x, x_rows, H, Hkv, n_new,
+                                 W, codes, cap, pos, pos_off, (int)rpb); break;
+    default: hipLaunchKernelGGL(encode_rows_kernel<128>, grid, dim3(kNT), 0, s, x, x_rows, H, Hkv, n_new,
+                                W, codes, cap, pos, pos_off, (int)rpb); break;
+  }
   return hipGetLastError();
 }
 

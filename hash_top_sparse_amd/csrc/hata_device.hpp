@@ -7,9 +7,19 @@
 namespace hata {
 
 constexpr int kD = 128;      // head dim
-constexpr int kR = 128;      // code bits
-constexpr int kWords32 = 4;  // 32-bit words per code
+constexpr int kR = 128;      // default code bits
+constexpr int kWords32 = 4;  // 32-bit words per default code
 constexpr int kNT = 256;     // threads per workgroup of the decode kernels
+
+// Code widths: R bits stored in ceil(R/64) 64-bit words per code row, the
+// bits past R zero (R = 32 keeps one 64-bit word).
+template <int R>
+struct Width {
+  static_assert(R == 32 || R == 64 || R == 128 || R == 256, "code width");
+  static constexpr int W64 = (R + 63) / 64;  // storage words per code row
+  static constexpr int W32 = (R + 31) / 32;  // 32-bit words that hold code bits
+  static constexpr int CPT = R / 32;         // projection columns per thread
+};
 
 // ---------------------------------------------------------------- bf16
 __device__ __forceinline__ float bf16_lo(uint32_t two) { return __uint_as_float(two << 16); }
@@ -26,9 +36,14 @@ __device__ __forceinline__ void unpack8(const uint4 v, float (&f)[8]) {
 // ------------------------------------------------------- memory access
 // Streaming 16-byte load that should not displace reusable lines.
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint4 load_stream16(const uint4* p) {
   const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
   return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ uint2 load_stream8(const uint2* p) {
+  const u32x2 v = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
+  return make_uint2(v.x, v.y);
 }
 
 // Agent-coherent accesses for data that workgroups of one launch exchange.
@@ -191,81 +206,109 @@ __device__ __forceinline__ uint32_t block_excl_scan_u32(uint32_t v, uint32_t* tm
 }
 
 // ------------------------------------------------------- HashEncode projection
-// Projection of R staged rows by one KV head's W_H ([128][128] fp32,
+// Projection of ROWS staged rows by one KV head's W_H ([128][R] fp32,
 // row-major) with a 256-thread workgroup, then sign + bit-pack:
-//   thread t owns columns 4*(t&31) .. +3 and input channels 16*(t>>5) .. +15
-//   (16 float4 loads of W per thread); partial sums over its 16 channels are
-//   added pairwise across the two channel groups of a wave (lanes l, l^32),
-//   then over the 4 waves in fixed order through LDS; each 64-column half of
-//   a code is one wave64 ballot of (p >= 0).
+//   thread t owns columns CPT*(t&31) .. +CPT-1 (CPT = R/32) and input
+//   channels 16*(t>>5) .. +15 (16*CPT floats of W per thread); partial sums
+//   over its 16 channels are added pairwise across the two channel groups of
+//   a wave (lanes l, l^32), then over the 4 waves in fixed order through
+//   LDS; each 64-column word of a code is one wave64 ballot of (p >= 0)
+//   (for R = 32 the lanes past column 31 vote 0).
 // The summation order is fixed, so every kernel that uses this function
 // produces identical codes.
+template <int R = kR>
 struct WRegs {
-  float4 w[16];
+  float w[16][Width<R>::CPT];
 };
-__device__ __forceinline__ void load_w_regs(const float* __restrict__ Wh, WRegs& wr) {
+template <int R = kR>
+__device__ __forceinline__ void load_w_regs(const float* __restrict__ Wh, WRegs<R>& wr) {
+  constexpr int CPT = Width<R>::CPT;
   const int t = threadIdx.x, cg = t & 31, rg = t >> 5;
-  const float4* src = reinterpret_cast<const float4*>(Wh + (rg * 16) * kR) + cg;
+  const float* src = Wh + (rg * 16) * R + cg * CPT;
 #pragma unroll
-  for (int i = 0; i < 16; ++i) wr.w[i] = src[i * (kR / 4)];
+  for (int i = 0; i < 16; ++i) {
+    if constexpr (CPT == 8) {
+      const float4 a = reinterpret_cast<const float4*>(src + i * R)[0];
+      const float4 b = reinterpret_cast<const float4*>(src + i * R)[1];
+      wr.w[i][0] = a.x; wr.w[i][1] = a.y; wr.w[i][2] = a.z; wr.w[i][3] = a.w;
+      wr.w[i][4] = b.x; wr.w[i][5] = b.y; wr.w[i][6] = b.z; wr.w[i][7] = b.w;
+    } else if constexpr (CPT == 4) {
+      const float4 a = *reinterpret_cast<const float4*>(src + i * R);
+      wr.w[i][0] = a.x; wr.w[i][1] = a.y; wr.w[i][2] = a.z; wr.w[i][3] = a.w;
+    } else if constexpr (CPT == 2) {
+      const float2 a = *reinterpret_cast<const float2*>(src + i * R);
+      wr.w[i][0] = a.x; wr.w[i][1] = a.y;
+    } else {
+      wr.w[i][0] = src[i * R];
+    }
+  }
 }
-// xs: LDS rows [R][128] fp32; red: LDS [4][R][128] fp32; out: LDS [R][2] uint64.
-// Rows >= nrows are not packed (their products are formed and dropped, so
-// they may hold anything).  The FMA loop runs over W's registers in load
-// order, all rows at once, so the products with the first W registers start
-// while the later ones are still arriving; each accumulator still takes its
-// 16 channels in ascending order.  Ends with __syncthreads.
-template <int R>
-__device__ __forceinline__ void project_pack(const WRegs& wr, const float* xs, float* red,
+// xs: LDS rows [ROWS][128] fp32; red: LDS [4][ROWS][R] fp32; out: LDS
+// [ROWS][W64] uint64.  Rows >= nrows are not packed (their products are
+// formed and dropped, so they may hold anything).  The FMA loop runs over
+// W's registers in load order, all rows at once, so the products with the
+// first W registers start while the later ones are still arriving; each
+// accumulator still takes its 16 channels in ascending order.  Ends with
+// __syncthreads.
+template <int ROWS, int R = kR>
+__device__ __forceinline__ void project_pack(const WRegs<R>& wr, const float* xs, float* red,
                                              uint64_t* out, int nrows) {
+  constexpr int CPT = Width<R>::CPT, W64 = Width<R>::W64;
   const int t = threadIdx.x, lane = t & 63, wv = t >> 6, cg = t & 31, rg = t >> 5;
-  float acc[R][4];
+  float acc[ROWS][CPT];
 #pragma unroll
-  for (int r = 0; r < R; ++r)
+  for (int r = 0; r < ROWS; ++r)
 #pragma unroll
-    for (int c = 0; c < 4; ++c) acc[r][c] = 0.f;
+    for (int c = 0; c < CPT; ++c) acc[r][c] = 0.f;
 #pragma unroll
   for (int i4 = 0; i4 < 4; ++i4) {
-    float4 xq[R];
+    float4 xq[ROWS];
 #pragma unroll
-    for (int r = 0; r < R; ++r) xq[r] = reinterpret_cast<const float4*>(xs + r * kD + rg * 16)[i4];
+    for (int r = 0; r < ROWS; ++r) xq[r] = reinterpret_cast<const float4*>(xs + r * kD + rg * 16)[i4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const float4 w = wr.w[i4 * 4 + j];
 #pragma unroll
-      for (int r = 0; r < R; ++r) {
+      for (int r = 0; r < ROWS; ++r) {
         const float xv = (j == 0) ? xq[r].x : (j == 1) ? xq[r].y : (j == 2) ? xq[r].z : xq[r].w;
-        acc[r][0] = fmaf(xv, w.x, acc[r][0]);
-        acc[r][1] = fmaf(xv, w.y, acc[r][1]);
-        acc[r][2] = fmaf(xv, w.z, acc[r][2]);
-        acc[r][3] = fmaf(xv, w.w, acc[r][3]);
+#pragma unroll
+        for (int c = 0; c < CPT; ++c) acc[r][c] = fmaf(xv, wr.w[i4 * 4 + j][c], acc[r][c]);
       }
     }
   }
 #pragma unroll
-  for (int r = 0; r < R; ++r) {
+  for (int r = 0; r < ROWS; ++r) {
     if (r >= nrows) break;
-    const float a0 = pair32_sum(acc[r][0]);
-    const float a1 = pair32_sum(acc[r][1]);
-    const float a2 = pair32_sum(acc[r][2]);
-    const float a3 = pair32_sum(acc[r][3]);
+    float sv[CPT];
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) sv[c] = pair32_sum(acc[r][c]);
     if (lane < 32) {
-      float* dst = red + (wv * R + r) * kR + cg * 4;
-      *reinterpret_cast<float4*>(dst) = make_float4(a0, a1, a2, a3);
+      float* dst = red + (wv * ROWS + r) * R + cg * CPT;
+      if constexpr (CPT == 8) {
+        reinterpret_cast<float4*>(dst)[0] = make_float4(sv[0], sv[1], sv[2], sv[3]);
+        reinterpret_cast<float4*>(dst)[1] = make_float4(sv[4], sv[5], sv[6], sv[7]);
+      } else if constexpr (CPT == 4) {
+        *reinterpret_cast<float4*>(dst) = make_float4(sv[0], sv[1], sv[2], sv[3]);
+      } else if constexpr (CPT == 2) {
+        *reinterpret_cast<float2*>(dst) = make_float2(sv[0], sv[1]);
+      } else {
+        dst[0] = sv[0];
+      }
     }
   }
   __syncthreads();
-  // wave wv: column half (wv & 1), rows r with r % 2 == wv >> 1
-  const int col = (wv & 1) * 64 + lane;
+  // (row, word) pair p = row * W64 + word goes to wave p % 4
 #pragma unroll
-  for (int r = (wv >> 1); r < R; r += 2) {
+  for (int p = wv; p < ROWS * W64; p += 4) {
+    const int r = p / W64, wd = p - r * W64;
     if (r >= nrows) break;
-    float s = red[(0 * R + r) * kR + col];
-    s += red[(1 * R + r) * kR + col];
-    s += red[(2 * R + r) * kR + col];
-    s += red[(3 * R + r) * kR + col];
-    const uint64_t m = __ballot(s >= 0.0f);
-    if (lane == 0) out[r * 2 + (wv & 1)] = m;
+    const int col = wd * 64 + lane;
+    const int cc = col < R ? col : R - 1;
+    float s = red[(0 * ROWS + r) * R + cc];
+    s += red[(1 * ROWS + r) * R + cc];
+    s += red[(2 * ROWS + r) * R + cc];
+    s += red[(3 * ROWS + r) * R + cc];
+    const uint64_t m = __ballot(col < R && s >= 0.0f);
+    if (lane == 0) out[p] = m;
   }
   __syncthreads();
 }
@@ -281,18 +324,18 @@ struct SliceCount {
   static constexpr int J = (G == 1) ? 1 : (G == 2) ? 2 : (G <= 7) ? 3 : 4;
 };
 
-template <int G>
+template <int G, int R = kR>
 struct QMasks {
-  uint32_t one[SliceCount<G>::J][kWords32];   // bit slices of #{g: q_g bit = 1}
-  uint32_t zero[SliceCount<G>::J][kWords32];  // bit slices of #{g: q_g bit = 0}
+  uint32_t one[SliceCount<G>::J][Width<R>::W32];   // bit slices of #{g: q_g bit = 1}
+  uint32_t zero[SliceCount<G>::J][Width<R>::W32];  // bit slices of #{g: q_g bit = 0}
 };
 
 // qw[g][w]: 32-bit word w of query code g.
-template <int G>
-__device__ __forceinline__ void build_qmasks(const uint32_t (&qw)[G][kWords32], QMasks<G>& m) {
+template <int G, int R = kR>
+__device__ __forceinline__ void build_qmasks(const uint32_t (&qw)[G][Width<R>::W32], QMasks<G, R>& m) {
   constexpr int J = SliceCount<G>::J;
 #pragma unroll
-  for (int w = 0; w < kWords32; ++w) {
+  for (int w = 0; w < Width<R>::W32; ++w) {
     uint32_t c1[J], c0[J];
 #pragma unroll
     for (int j = 0; j < J; ++j) { c1[j] = 0; c0[j] = 0; }
@@ -313,22 +356,60 @@ __device__ __forceinline__ void build_qmasks(const uint32_t (&qw)[G][kWords32], 
   }
 }
 
-template <int G>
-__device__ __forceinline__ uint32_t gqa_hamming(const uint4 c, const QMasks<G>& m) {
+// summed distance of one code (its W32 32-bit words) to the G query codes
+template <int G, int R>
+__device__ __forceinline__ uint32_t gqa_hamming_w(const uint32_t (&cw)[Width<R>::W32], const QMasks<G, R>& m) {
   constexpr int J = SliceCount<G>::J;
-  const uint32_t cw[4] = {c.x, c.y, c.z, c.w};
   uint32_t s = 0;
 #pragma unroll
   for (int j = 0; j < J; ++j) {
     uint32_t acc = 0;
 #pragma unroll
-    for (int w = 0; w < kWords32; ++w) {
+    for (int w = 0; w < Width<R>::W32; ++w) {
       uint32_t sel = (cw[w] & m.zero[j][w]) | (~cw[w] & m.one[j][w]);
       acc = __builtin_popcount(sel) + acc;
     }
     s += acc << j;
   }
   return s;
+}
+
+template <int G>
+__device__ __forceinline__ uint32_t gqa_hamming(const uint4 c, const QMasks<G>& m) {
+  const uint32_t cw[4] = {c.x, c.y, c.z, c.w};
+  return gqa_hamming_w<G, kR>(cw, m);
+}
+
+// One code row of R bits as loaded by the scans: 8 bytes (R <= 64), 16 or 32.
+template <int R>
+struct CodeRow {
+  uint4 v[(Width<R>::W64 + 1) / 2];
+};
+// streaming load of code row `row` (R/8 bytes rounded up to 8) from codes
+template <int R>
+__device__ __forceinline__ CodeRow<R> load_code(const uint64_t* codes, int64_t row) {
+  CodeRow<R> c;
+  if constexpr (Width<R>::W64 == 1) {
+    const uint2 v = load_stream8(reinterpret_cast<const uint2*>(codes + row));
+    c.v[0] = make_uint4(v.x, v.y, 0u, 0u);
+  } else {
+#pragma unroll
+    for (int i = 0; i < Width<R>::W64 / 2; ++i)
+      c.v[i] = load_stream16(reinterpret_cast<const uint4*>(codes + row * Width<R>::W64) + i);
+  }
+  return c;
+}
+template <int R>
+__device__ __forceinline__ void code_words(const CodeRow<R>& c, uint32_t (&cw)[Width<R>::W32]) {
+  if constexpr (Width<R>::W64 == 1) {
+    cw[0] = c.v[0].x;
+    if constexpr (Width<R>::W32 == 2) cw[1] = c.v[0].y;
+  } else {
+#pragma unroll
+    for (int i = 0; i < Width<R>::W64 / 2; ++i) {
+      cw[4 * i] = c.v[i].x; cw[4 * i + 1] = c.v[i].y; cw[4 * i + 2] = c.v[i].z; cw[4 * i + 3] = c.v[i].w;
+    }
+  }
 }
 
 // ------------------------------------------------------- online softmax

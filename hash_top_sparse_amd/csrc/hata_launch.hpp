@@ -12,7 +12,7 @@ namespace hata {
 // Row index of (b, j) is (pos ? pos[b] : 0) + pos_off + j.
 hipError_t launch_encode_rows(const uint16_t* x, int64_t x_rows, int B, int H, int Hkv, int n_new,
                               const float* W, uint64_t* codes, int64_t cap, const int32_t* pos,
-                              int pos_off, hipStream_t s);
+                              int pos_off, hipStream_t s, int r = 128);
 // Same contract, matrix-core path for long row runs (prefill).
 hipError_t launch_encode_bulk(const uint16_t* x, int64_t x_rows, int B, int H, int Hkv, int n_new,
                               const float* W, uint64_t* codes, int64_t cap, const int32_t* pos,
@@ -23,7 +23,7 @@ constexpr int kBulkMinRows = 512;
 // ---------------------------------------------------------------- score / select
 hipError_t launch_hamming(const uint64_t* qc, const uint64_t* kc, int B, int Hq, int Hkv,
                           int64_t cap, const int32_t* seq_lens, int64_t max_len, uint16_t* scores,
-                          int64_t sstride, hipStream_t s);
+                          int64_t sstride, hipStream_t s, int r = 128);
 hipError_t launch_topk(const uint16_t* scores, int64_t sstride, int B, int Hkv, int64_t cap,
                        const int32_t* seq_lens, int k, int max_score, int32_t* idx, hipStream_t s);
 
@@ -39,7 +39,7 @@ hipError_t launch_attention(const uint16_t* q, const uint16_t* K, const uint16_t
 // ---------------------------------------------------------------- fused step
 struct StepPlan {
   bool fused = false;
-  int G = 0, U = 0, Wg = 1, chunk = 0, xcd_map = 0;
+  int G = 0, U = 0, Wg = 1, chunk = 0, xcd_map = 0, R = 128;
   size_t lds_bytes = 0;
   // workspace layout (byte offsets)
   size_t off_err = 0, off_flags = 0, off_win = 0, off_full = 0, off_part = 0;
@@ -47,7 +47,7 @@ struct StepPlan {
   int full_words = 0;  // 32-bit words per workgroup in the full-histogram area
   size_t total = 0;
 };
-StepPlan plan_decode_step(int B, int Hq, int Hkv, int64_t max_len, int k, int num_cus);
+StepPlan plan_decode_step(int B, int Hq, int Hkv, int64_t max_len, int k, int num_cus, int r = 128);
 hipError_t launch_decode_step(const StepPlan& p, const uint16_t* q, const uint16_t* K,
                               const uint16_t* V, const float* W, const float* Wk, uint64_t* codes, int B, int Hq,
                               int Hkv, int64_t cap, const int32_t* seq_lens, int k, float scale,

@@ -15,7 +15,7 @@ namespace {
 
 constexpr int kHamTPT = 8;  // tokens per thread in the staged Hamming kernel
 
-template <int G>
+template <int G, int R>
 __global__ __launch_bounds__(kNT) void hamming_kernel(const uint64_t* __restrict__ qc,
                                                       const uint64_t* __restrict__ kc, int Hq,
                                                       int Hkv, int64_t cap,
@@ -32,29 +32,33 @@ __global__ __launch_bounds__(kNT) void hamming_kernel(const uint64_t* __restrict
   const int64_t i0 = (int64_t)blockIdx.x * (kNT * kHamTPT);
   if (i0 >= n) return;
 
-  uint32_t qw[G][kWords32];
+  constexpr int W64 = Width<R>::W64, W32 = Width<R>::W32;
+  uint32_t qw[G][W32];
 #pragma unroll
   for (int g = 0; g < G; ++g) {
-    const uint64_t* qp = qc + ((int64_t)b * Hq + (int64_t)h * G + g) * 2;
-    const uint64_t a = qp[0], c = qp[1];
-    qw[g][0] = (uint32_t)a; qw[g][1] = (uint32_t)(a >> 32);
-    qw[g][2] = (uint32_t)c; qw[g][3] = (uint32_t)(c >> 32);
+    const uint64_t* qp = qc + ((int64_t)b * Hq + (int64_t)h * G + g) * W64;
+#pragma unroll
+    for (int w = 0; w < W32; ++w) qw[g][w] = (uint32_t)(qp[w >> 1] >> ((w & 1) * 32));
   }
-  QMasks<G> m;
-  build_qmasks<G>(qw, m);
+  QMasks<G, R> m;
+  build_qmasks<G, R>(qw, m);
 
-  const uint4* src = reinterpret_cast<const uint4*>(kc) + ((int64_t)b * Hkv + h) * cap;
+  const uint64_t* src = kc + ((int64_t)b * Hkv + h) * cap * W64;
   uint16_t* dst = scores + ((int64_t)b * Hkv + h) * sstride;
-  uint4 c[kHamTPT];
+  CodeRow<R> c[kHamTPT];
 #pragma unroll
   for (int j = 0; j < kHamTPT; ++j) {
     const int64_t i = i0 + j * kNT + t;
-    if (i < n) c[j] = load_stream16(src + i);
+    if (i < n) c[j] = load_code<R>(src, i);
   }
 #pragma unroll
   for (int j = 0; j < kHamTPT; ++j) {
     const int64_t i = i0 + j * kNT + t;
-    if (i < n) dst[i] = (uint16_t)gqa_hamming<G>(c[j], m);
+    if (i < n) {
+      uint32_t cw[W32];
+      code_words<R>(c[j], cw);
+      dst[i] = (uint16_t)gqa_hamming_w<G, R>(cw, m);
+    }
   }
 }
 
@@ -62,7 +66,7 @@ __global__ __launch_bounds__(kNT) void hamming_kernel(const uint64_t* __restrict
 // smallest s with count(score <= s) >= k, then an ordered compaction that
 // keeps every score < T and the lowest-index (k - count(< T)) ties at T.
 constexpr int kTopkNT = 1024;
-constexpr int kMaxBins = 8 * kR + 1;
+constexpr int kMaxBins = 8 * 256 + 1;  // G * r + 1 at G = 8, r = 256
 
 __device__ __forceinline__ uint32_t block_excl_scan_1024(uint32_t v, uint32_t* tmp, uint32_t* total) {
   const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
@@ -162,20 +166,32 @@ __global__ __launch_bounds__(kTopkNT) void topk_kernel(const uint16_t* __restric
 
 }  // namespace
 
-hipError_t launch_hamming(const uint64_t* qc, const uint64_t* kc, int B, int Hq, int Hkv,
-                          int64_t cap, const int32_t* seq_lens, int64_t max_len, uint16_t* scores,
-                          int64_t sstride, hipStream_t s) {
-  const int G = Hq / Hkv;
-  const int64_t per_block = (int64_t)kNT * kHamTPT;
-  dim3 grid((unsigned)((max_len + per_block - 1) / per_block), (unsigned)(B * Hkv));
+template <int R>
+static hipError_t launch_hamming_r(const uint64_t* qc, const uint64_t* kc, int G, int Hq, int Hkv,
+                                   int64_t cap, const int32_t* seq_lens, uint16_t* scores, int64_t sstride,
+                                   dim3 grid, hipStream_t s) {
   switch (G) {
-    case 1: hipLaunchKernelGGL(hamming_kernel<1>, grid, dim3(kNT), 0, s, qc, kc, Hq, Hkv, cap, seq_lens, scores, sstride); break;
-    case 2: hipLaunchKernelGGL(hamming_kernel<2>, grid, dim3(kNT), 0, s, qc, kc, Hq, Hkv, cap, seq_lens, scores, sstride); break;
-    case 4: hipLaunchKernelGGL(hamming_kernel<4>, grid, dim3(kNT), 0, s, qc, kc, Hq, Hkv, cap, seq_lens, scores, sstride); break;
-    case 8: hipLaunchKernelGGL(hamming_kernel<8>, grid, dim3(kNT), 0, s, qc, kc, Hq, Hkv, cap, seq_lens, scores, sstride); break;
+    case 1: hipLaunchKernelGGL((hamming_kernel<1, R>), grid, dim3(kNT), 0, s, qc, kc, Hq, Hkv, cap, seq_lens, scores, sstride); break;
+    case 2: hipLaunchKernelGGL((hamming_kernel<2, R>), grid, dim3(kNT), 0, s, qc, kc, Hq, Hkv, cap, seq_lens, scores, sstride); break;
+    case 4: hipLaunchKernelGGL((hamming_kernel<4, R>), grid, dim3(kNT), 0, s, qc, kc, Hq, Hkv, cap, seq_lens, scores, sstride); break;
+    case 8: hipLaunchKernelGGL((hamming_kernel<8, R>), grid, dim3(kNT), 0, s, qc, kc, Hq, Hkv, cap, seq_lens, scores, sstride); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
+}
+
+hipError_t launch_hamming(const uint64_t* qc, const uint64_t* kc, int B, int Hq, int Hkv,
+                          int64_t cap, const int32_t* seq_lens, int64_t max_len, uint16_t* scores,
+                          int64_t sstride, hipStream_t s, int r) {
+  const int G = Hq / Hkv;
+  const int64_t per_block = (int64_t)kNT * kHamTPT;
+  dim3 grid((unsigned)((max_len + per_block - 1) / per_block), (unsigned)(B * Hkv));
+  switch (r) {
+    case 32: return launch_hamming_r<32>(qc, kc, G, Hq, Hkv, cap, seq_lens, scores, sstride, grid, s);
+    case 64: return launch_hamming_r<64>(qc, kc, G, Hq, Hkv, cap, seq_lens, scores, sstride, grid, s);
+    case 256: return launch_hamming_r<256>(qc, kc, G, Hq, Hkv, cap, seq_lens, scores, sstride, grid, s);
+    default: return launch_hamming_r<128>(qc, kc, G, Hq, Hkv, cap, seq_lens, scores, sstride, grid, s);
+  }
 }
 
 hipError_t launch_topk(const uint16_t* scores, int64_t sstride, int B, int Hkv, int64_t cap,

@@ -59,7 +59,8 @@ def test_encode_append_validation():
     assert _enc(x=None) == ENULL
     assert _enc(codes=None) == ENULL
     assert _enc(d=64) == EUNSUP
-    assert _enc(r=256) == EUNSUP
+    assert _enc(r=96) == EUNSUP
+    assert _enc(r=512) == EUNSUP
     assert _enc(H=6, Hkv=4) == ESHAPE
     assert _enc(n_new=-1) == ESHAPE
     assert _enc(n_new=17) == ESHAPE            # more rows than x_rows without pos
@@ -83,7 +84,8 @@ def test_hamming_validation():
     assert _ham(max_len=2048) == ESHAPE        # max_len > cap
     assert _ham(max_len=0) == ESHAPE
     assert _ham(kc=MIS) == EALIGN
-    assert _ham(r=64) == EUNSUP
+    assert _ham(r=96) == EUNSUP
+    assert _ham(r=16) == EUNSUP
 
 
 def _topk(**kw):
@@ -98,7 +100,7 @@ def test_topk_validation():
     assert _topk(idx=None) == ENULL
     assert _topk(k=0) == EUNSUP
     assert _topk(k=4097) == EUNSUP
-    assert _topk(max_score=1025) == EUNSUP
+    assert _topk(max_score=2049) == EUNSUP
     assert _topk(max_len=0) == ESHAPE
 
 

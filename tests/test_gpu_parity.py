@@ -395,7 +395,8 @@ def test_decode_step_qk_matches_oracle(hata_gpu, case):
     assert_close(out.cpu().numpy(), ref_out)
 
 
-def test_decode_step_qk_staged_shape(hata_gpu):
+@pytest.mark.parametrize("r", [128, 256])
+def test_decode_step_qk_staged_shape(hata_gpu, r):
     """A shape whose per-unit chunk cannot stay on chip (130 units of 32,800
     tokens: two workgroups per unit would need 260 CUs) runs the separate
     kernels inside the call; the key row is still encoded with W_Hk.  Inputs
@@ -406,22 +407,23 @@ def test_decode_step_qk_staged_shape(hata_gpu):
     q = torch.randn((B, Hq, 128), generator=g, device="cuda").to(torch.bfloat16)
     K = torch.randn((B, Hkv, N, 128), generator=g, device="cuda").to(torch.bfloat16)
     V = torch.randn((B, Hkv, N, 128), generator=g, device="cuda").to(torch.bfloat16)
-    Wq = torch.randn((Hkv, 128, 128), generator=g, device="cuda") / np.sqrt(128.0)
-    Wk = torch.randn((Hkv, 128, 128), generator=g, device="cuda") / np.sqrt(128.0)
+    Wq = torch.randn((Hkv, 128, r), generator=g, device="cuda") / np.sqrt(128.0)
+    Wk = torch.randn((Hkv, 128, r), generator=g, device="cuda") / np.sqrt(128.0)
     seq = torch.full((B,), N, dtype=torch.int32, device="cuda")
-    codes = torch.zeros((B, Hkv, N, 2), dtype=torch.int64, device="cuda")
+    wd = (r + 63) // 64
+    codes = torch.zeros((B, Hkv, N, wd), dtype=torch.int64, device="cuda")
     hata_gpu.encode_append(K, Wk, codes, n_new=N)
     codes[:, :, N - 1] = 0x1234
-    ws = hata_gpu.alloc_workspace(hata_gpu.OP_DECODE_STEP, B, Hq, Hkv, N, k)
+    ws = hata_gpu.alloc_workspace(hata_gpu.OP_DECODE_STEP, B, Hq, Hkv, N, k, r=r)
     out = torch.zeros((B, Hq, 128), dtype=torch.float32, device="cuda")
     idx = torch.zeros((B, Hkv, k), dtype=torch.int32, device="cuda")
-    _log("qk staged shape: 130 units x 32800")
+    _log(f"qk staged shape: 130 units x 32800, r={r}")
     hata_gpu.decode_step_qk(q, K, V, Wq, Wk, codes, seq, N, k, 1.0 / np.sqrt(128.0), out, ws, idx)
     torch.cuda.synchronize()
-    qc = torch.zeros((B, Hq, 1, 2), dtype=torch.int64, device="cuda")
+    qc = torch.zeros((B, Hq, 1, wd), dtype=torch.int64, device="cuda")
     hata_gpu.encode_append(q.view(B, Hq, 1, 128), Wq, qc, n_new=1)
     bits = lambda t: t.view(torch.int16).cpu().numpy().view(np.uint16)
-    qcn = codes_np(qc.view(B, Hq, 2))
+    qcn = codes_np(qc.view(B, Hq, wd))
     for h in (0, 1, 77, 129):
         kb, vb = bits(K[0, h]), bits(V[0, h])
         cn = codes_np(codes[0, h])
@@ -431,3 +433,87 @@ def test_decode_step_qk_staged_shape(hata_gpu):
         np.testing.assert_array_equal(idx[0, h].cpu().numpy(), ix)
         ref = oracle.attention(bits(q[0, h:h + 1]), kb, vb, ix, 1.0 / np.sqrt(128.0))
         assert_close(out[0, h:h + 1].cpu().numpy(), ref)
+
+
+# ------------------------------------------------- other code widths r
+# Codes of r in {32, 64, 256} bits (ceil(r/64) words per row, bits past r
+# zero): every stage against the oracle at that width.
+
+def _wshape(B, Hq, Hkv, N, k, r, dist="gauss", seed=8100):
+    return synth.Shape(f"w-{B}-{Hq}-{Hkv}-{N}-{k}-{r}-{dist}", B=B, Hq=Hq, Hkv=Hkv, N=N, k=k, dist=dist,
+                       seed_base=seed, r=r, needles=8 if dist == "gauss" else 0)
+
+
+def _wcache(hb, d: Dev, r: int) -> torch.Tensor:
+    codes = torch.zeros((d.B, d.Hkv, d.cap, (r + 63) // 64), dtype=torch.int64, device="cuda")
+    hb.encode_append(d.K, d.W, codes, n_new=d.cap)
+    return codes
+
+
+def _wqcodes(hb, d: Dev, r: int) -> torch.Tensor:
+    w = (r + 63) // 64
+    qc = torch.zeros((d.B, d.Hq, 1, w), dtype=torch.int64, device="cuda")
+    hb.encode_append(d.q.view(d.B, d.Hq, 1, 128), d.W, qc, n_new=1)
+    return qc.view(d.B, d.Hq, w)
+
+
+@pytest.mark.parametrize("r", [32, 64, 256])
+@pytest.mark.parametrize("dist", ["exact", "gauss"])
+def test_encode_and_hamming_each_width(hata_gpu, r, dist):
+    s = _wshape(2, 8, 2, 1500, 64, r, dist=dist, seed=8200 + r)
+    inp = synth.make_inputs(s)
+    d = Dev(inp)
+    _log(f"width r={r} {dist}: encode + hamming")
+    codes = _wcache(hata_gpu, d, r)
+    cn = codes_np(codes)
+    for b in range(2):
+        for h in range(2):
+            check_codes(cn[b, h], inp.K[b, h], inp.W[h], exact=dist == "exact")
+    if r == 32:
+        assert (cn >> np.uint64(32) == 0).all()  # bits past r stay zero
+    qc = _wqcodes(hata_gpu, d, r)
+    sc = torch.zeros((2, 2, d.cap), dtype=torch.int16, device="cuda")
+    hata_gpu.hamming_scores(qc, codes, d.seq, d.max_len, sc, r=r)
+    torch.cuda.synchronize()
+    qn, scn = codes_np(qc), sc.cpu().numpy().astype(np.int64)
+    for b in range(2):
+        n = int(inp.seq_lens[b])
+        for h in range(2):
+            np.testing.assert_array_equal(scn[b, h, :n], oracle.hamming_gqa(qn[b, h * 4:(h + 1) * 4], cn[b, h, :n]))
+
+
+WIDTH_STEP_CASES = [
+    # B, Hq, Hkv, N, k, dist
+    (1, 32, 8, 8192, 512, "gauss"),      # GQA-4, 32 workgroups per unit
+    (8, 32, 32, 2048, 128, "gauss"),     # one workgroup per unit
+    (1, 16, 2, 20000, 100, "gauss"),     # G = 8
+    (1, 4, 1, 4096, 256, "exact"),       # exact recipe, many ties
+]
+
+
+@pytest.mark.parametrize("r", [32, 64, 256])
+@pytest.mark.parametrize("case", WIDTH_STEP_CASES, ids=lambda c: f"B{c[0]}-Hq{c[1]}-Hkv{c[2]}-N{c[3]}-k{c[4]}-{c[5]}")
+def test_decode_step_each_width(hata_gpu, case, r):
+    B, Hq, Hkv, N, k, dist = case
+    s = _wshape(B, Hq, Hkv, N, k, r, dist=dist, seed=8300 + N % 83)
+    inp = synth.make_inputs(s)
+    d = Dev(inp)
+    _log(f"width r={r} step case {case}")
+    codes = _wcache(hata_gpu, d, r)
+    for b in range(B):
+        codes[b, :, int(inp.seq_lens[b]) - 1] = 0x1234
+    ws = hata_gpu.alloc_workspace(hata_gpu.OP_DECODE_STEP, B, Hq, Hkv, d.max_len, k, r=r)
+    out = torch.full((B, Hq, 128), np.nan, dtype=torch.float32, device="cuda")
+    idx = torch.full((B, Hkv, k), -9, dtype=torch.int32, device="cuda")
+    hata_gpu.decode_step(d.q, d.K, d.V, d.W, codes, d.seq, d.max_len, k, inp.scale, out, ws, idx)
+    torch.cuda.synchronize()
+    assert hata_gpu.workspace_check(ws) == 0
+    cn = codes_np(codes)
+    for b in range(B):
+        n = int(inp.seq_lens[b])
+        for h in range(Hkv):
+            check_codes(cn[b, h, n - 1:n], inp.K[b, h, n - 1:n], inp.W[h], exact=dist == "exact")
+    qc = codes_np(_wqcodes(hata_gpu, d, r))
+    _, ref_idx, ref_out = oracle_units(inp, qc, cn)
+    np.testing.assert_array_equal(idx.cpu().numpy(), ref_idx)
+    assert_close(out.cpu().numpy(), ref_out)
