@@ -163,17 +163,22 @@ def read_peak(gib: int = 4, reps: int = 5) -> float:
 
 
 def measure(cfg_id: int, steps: int, warmup: int, dense_steps: int, layers: int, use_graph: bool,
-            with_bulk: bool, with_qk: bool = True):
+            with_bulk: bool, with_qk: bool = True, r: int = 128):
     """Time the fused step (and the dense baseline) on one workload; returns
     (result dict, inputs)."""
     import torch
 
     from hash_top_sparse_amd import binding, synth
 
+    import dataclasses
+
     dev = torch.device("cuda:0")
     shape = synth.CONFIGS[cfg_id]
+    if r != shape.r:
+        shape = dataclasses.replace(shape, r=r, name=f"{shape.name}-r{r}")
     B, Hq, Hkv, N, k = shape.B, shape.Hq, shape.Hkv, shape.N, shape.k
-    per_step = step_bytes(B, Hq, Hkv, N, k)
+    words = (r + 63) // 64
+    per_step = step_bytes(B, Hq, Hkv, N, k, r=r)
     L = layers or max(2, min(64, int(np.ceil(1.5e9 / per_step))))
     log(f"workload {shape.name}: B={B} Hq={Hq} Hkv={Hkv} N={N} k={k}; {L} layer caches")
     t0 = time.perf_counter()
@@ -183,7 +188,7 @@ def measure(cfg_id: int, steps: int, warmup: int, dense_steps: int, layers: int,
     q0, K0, V0 = bf(inp.q), bf(inp.K), bf(inp.V)
     W = torch.from_numpy(inp.W).to(dev)
     seq = torch.from_numpy(inp.seq_lens).to(dev)
-    codes0 = torch.zeros((B, Hkv, N, 2), dtype=torch.int64, device=dev)
+    codes0 = torch.zeros((B, Hkv, N, words), dtype=torch.int64, device=dev)
     binding.encode_append(K0, W, codes0, n_new=N)
     torch.cuda.synchronize()
     layer_bufs = []
@@ -211,7 +216,7 @@ def measure(cfg_id: int, steps: int, warmup: int, dense_steps: int, layers: int,
         del scratch
         log(f"bulk encode: {bulk_ms * 1e3:.1f} us per layer")
 
-    ws = binding.alloc_workspace(binding.OP_DECODE_STEP, B, Hq, Hkv, N, k, device=dev)
+    ws = binding.alloc_workspace(binding.OP_DECODE_STEP, B, Hq, Hkv, N, k, device=dev, r=r)
     out = torch.zeros((B, Hq, 128), dtype=torch.float32, device=dev)
 
     def step(i):
@@ -308,7 +313,7 @@ def measure(cfg_id: int, steps: int, warmup: int, dense_steps: int, layers: int,
         dense = {"ms_per_step": d_ms, "GBs": dgb, "frac_of_peak": dgb / PEAK_HBM_GBS,
                  "speedup_of_hata": d_ms / ms_step}
         log(f"dense: {d_ms * 1e3:.1f} us/step, {dgb:.0f} GB/s, hata speedup {d_ms / ms_step:.2f}x")
-    res = {"workload": shape.name, "ms_per_step": ms_step, "steps_per_s": 1000.0 / ms_step,
+    res = {"workload": shape.name, "code_bits": r, "ms_per_step": ms_step, "steps_per_s": 1000.0 / ms_step,
            "tokens_per_s": B * 1000.0 / ms_step,
            "GBs": achieved, "frac_of_peak": achieved / PEAK_HBM_GBS, "bytes_per_step": per_step,
            "layers": L, "eager_step_spread": spread, "separate_key_encoder": qk, "dense": dense,
@@ -398,6 +403,8 @@ def main() -> int:
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="launch the timed steps eagerly")
     ap.add_argument("--sweep", action="store_true", help="also time the other workloads (2, 3, 5)")
+    ap.add_argument("--width-sweep", action="store_true",
+                    help="also time the workload with 32-, 64- and 256-bit codes")
     ap.add_argument("--model-sweep", action="store_true",
                     help="also time 32-layer decode (one graph per token) at 32K/64K/128K against dense")
     ap.add_argument("--pmc-run", action="store_true",
@@ -440,6 +447,18 @@ def main() -> int:
                            not args.no_graph, with_bulk=False, with_qk=False)
             sweep[str(c)] = r
 
+    wsweep = None
+    if args.width_sweep:
+        wsweep = {}
+        for r in (32, 64, 256):
+            rr, _ = measure(args.config, max(256, args.steps // 4), 16, 0, 0, not args.no_graph,
+                            with_bulk=False, with_qk=False, r=r)
+            B_, Hkv_, N_ = shape.B, shape.Hkv, shape.N
+            # the stored rows: ceil(r/64) words, so 32-bit codes move 8 bytes a row
+            layout = rr["bytes_per_step"] + B_ * Hkv_ * N_ * (((r + 63) // 64) * 8 - r // 8)
+            wsweep[str(r)] = {"ms_per_step": rr["ms_per_step"], "steps_per_s": rr["steps_per_s"],
+                              "GBs": rr["GBs"], "frac_of_peak": rr["frac_of_peak"],
+                              "bytes_per_step": rr["bytes_per_step"], "stored_bytes_per_step": layout}
     msweep = model_sweep() if args.model_sweep else None
     peak_meas = read_peak()
     log(f"streaming read of 4 GiB: {peak_meas:.0f} GB/s")
@@ -484,6 +503,8 @@ def main() -> int:
         res["sweep"] = sweep
     if msweep is not None:
         res["model_sweep"] = msweep
+    if wsweep is not None:
+        res["code_widths"] = wsweep
     print(json.dumps(res), flush=True)
     return 0
 

@@ -68,10 +68,11 @@ struct Cfg {
   static constexpr int W64 = Width<R>::W64;       // 64-bit words per code row
   static constexpr int NB = G * R + 1;            // histogram bins
   static constexpr int NBP = (NB + 63) / 64 * 64;
-  // code rows in flight per thread (a ring of 32 KiB per workgroup: 8 rows of
-  // 16 bytes, 16 of 8 or 4 of 32); deeper rings delay W_H, which shares the
-  // CU's vector-memory path
-  static constexpr int PF = (R <= 64) ? 16 : (R == 128) ? 8 : 4;
+  // code rows in flight per thread (8 rows of 8 or 16 bytes, 4 of 32: a
+  // ring of 16 or 32 KiB per workgroup); deeper rings delay W_H, which
+  // shares the CU's vector-memory path (16 rows of 8 bytes measured slower
+  // at 128K than 8)
+  static constexpr int PF = (R <= 128) ? 8 : 4;
   static constexpr int HDRP = (2 * G + 3) / 4 * 4; // partial record header floats (M[G], L[G])
   static constexpr int RECP = HDRP + G * kD;       // partial record floats
   static constexpr int PROJ = 4 * (G + 1) * R;     // projection reduction floats
