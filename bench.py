@@ -489,7 +489,7 @@ def main() -> int:
         "roofline": {"bound": "hbm", "achieved": head["GBs"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": head["GBs"] / PEAK_HBM_GBS,
                      "traffic": profiled_traffic() if args.config == 4 else None,
-                     "kernel": f"decode_step_kernel<{shape.G}>", "bytes_per_launch": head["bytes_per_step"],
+                     "kernel": f"decode_step_kernel<{shape.G}, false, 128>", "bytes_per_launch": head["bytes_per_step"],
                      "peak_measured": peak_meas, "frac_of_measured": head["GBs"] / peak_meas,
                      "peak_measured_by": "hata_stream_read over 4 GiB, best of 5"},
         "tokens_per_s": head["tokens_per_s"],
