@@ -61,7 +61,8 @@ def labels(q_bits, k_bits, q_pos, pos_permille: int = 100, s_max: float = 20.0,
 
 
 def hash_relaxed(X: np.ndarray, W: np.ndarray, sigma: float) -> np.ndarray:
-    return 2.0 / (1.0 + np.exp(-sigma * (X @ W))) - 1.0
+    # 2 * Sigmoid(z) - 1 == tanh(z / 2) exactly; the tanh form cannot overflow
+    return np.tanh(0.5 * sigma * (X @ W))
 
 
 def loss(q_bits, k_bits, q_pos, S, W, sigma, eps, eta, lam):
