@@ -58,6 +58,9 @@ def load() -> ctypes.CDLL:
         "hata_workspace_reset": ([P, SZ, P], I),
         "hata_workspace_check": ([P, SZ, ctypes.POINTER(I), P], I),
         "hata_stream_read": ([P, SZ, P, SZ, P], I),
+        "hata_hash_labels": ([P, P, P, I, I, I, I, F, F, P, P], I),
+        "hata_hash_train_step": ([P, P, P, P, I, I, I, I, F, F, F, F, F, P, P, P, P, SZ, P], I),
+        "hata_hash_train_workspace_bytes": ([I, I, I, I], SZ),
     }
     for name, (args, res) in sig.items():
         fn = getattr(L, name)
@@ -73,7 +76,8 @@ def exported_symbols() -> list[str]:
                         "hata_sparse_decode", "hata_decode_step", "hata_decode_step_qk",
                         "hata_dense_decode",
                         "hata_workspace_bytes", "hata_workspace_reset", "hata_workspace_check",
-                        "hata_stream_read")
+                        "hata_stream_read", "hata_hash_labels", "hata_hash_train_step",
+                        "hata_hash_train_workspace_bytes")
             if hasattr(load(), n)]
 
 
@@ -236,6 +240,45 @@ def decode_step_qk(q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, W_Hq: torc
     _check(load().hata_decode_step_qk(_ptr(q), _ptr(K), _ptr(V), _ptr(W_Hq), _ptr(W_Hk), _ptr(codes), B, Hq,
                                       Hkv, d, r, cap, _ptr(seq_lens), int(max_len), int(k), float(scale),
                                       _ptr(out), _ptr(idx_out), _ptr(ws), ws.numel(), _stream(stream)))
+
+
+def hash_labels(q: torch.Tensor, k: torch.Tensor, q_pos: torch.Tensor, labels: torch.Tensor,
+                pos_permille: int = 100, s_max: float = 20.0, s_min: float = 1.0, stream=None) -> None:
+    """q bf16 [J,d]; k bf16 [n,d]; q_pos int32 [J]; labels f32 [J,n] (see hata_hash_labels)."""
+    _need(q, torch.bfloat16, "q")
+    _need(k, torch.bfloat16, "k")
+    _need(q_pos, torch.int32, "q_pos")
+    _need(labels, torch.float32, "labels")
+    J, d = q.shape
+    n = k.shape[0]
+    _check(load().hata_hash_labels(_ptr(q), _ptr(k), _ptr(q_pos), J, n, d, int(pos_permille), float(s_max),
+                                   float(s_min), _ptr(labels), _stream(stream)))
+
+
+def hash_train_workspace(J: int, n: int, r: int, d: int = 128, device="cuda") -> torch.Tensor:
+    nb = int(load().hata_hash_train_workspace_bytes(J, n, d, r))
+    return torch.empty(max(nb, 256), dtype=torch.uint8, device=device)
+
+
+def hash_train_step(q: torch.Tensor, k: torch.Tensor, q_pos: torch.Tensor, labels: torch.Tensor,
+                    W: torch.Tensor, sigma: float, eps: float, eta: float, lam: float, lr: float,
+                    loss: torch.Tensor, ws: torch.Tensor, grad: torch.Tensor | None = None,
+                    stream=None) -> None:
+    """One gradient step on W f32 [d,r] in place (see hata_hash_train_step); loss f32 [4]."""
+    _need(q, torch.bfloat16, "q")
+    _need(k, torch.bfloat16, "k")
+    _need(q_pos, torch.int32, "q_pos")
+    _need(labels, torch.float32, "labels")
+    _need(W, torch.float32, "W")
+    _need(loss, torch.float32, "loss")
+    if grad is not None:
+        _need(grad, torch.float32, "grad")
+    J, d = q.shape
+    n = k.shape[0]
+    r = W.shape[1]
+    _check(load().hata_hash_train_step(_ptr(q), _ptr(k), _ptr(q_pos), _ptr(labels), J, n, d, r, float(sigma),
+                                       float(eps), float(eta), float(lam), float(lr), _ptr(W), _ptr(grad),
+                                       _ptr(loss), _ptr(ws), ws.numel(), _stream(stream)))
 
 
 def workspace_reset(ws: torch.Tensor, stream=None) -> None:

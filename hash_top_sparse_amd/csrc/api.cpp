@@ -306,6 +306,52 @@ int hata_decode_step_qk(const void* q, const void* K, const void* V, const float
                           out, idx_out, ws, ws_bytes, stream);
 }
 
+int hata_hash_labels(const void* q, const void* k, const int32_t* q_pos, int J, int n, int d,
+                     int pos_permille, float s_max, float s_min, float* labels, void* stream) {
+  if (!q || !k || !q_pos || !labels) return fail(HATA_ERR_NULL, "hash_labels: null pointer");
+  if (d != 128) return fail(HATA_ERR_UNSUPPORTED, "hash_labels: d=%d unsupported (only 128)", d);
+  if (J < 1 || n < 1) return fail(HATA_ERR_SHAPE, "hash_labels: J=%d n=%d must be >= 1", J, n);
+  if (n > hata::kMaxLabelKeys)
+    return fail(HATA_ERR_UNSUPPORTED, "hash_labels: n=%d above %d keys", n, hata::kMaxLabelKeys);
+  if (pos_permille < 1 || pos_permille > 1000)
+    return fail(HATA_ERR_SHAPE, "hash_labels: pos_permille=%d outside [1, 1000]", pos_permille);
+  if (!aligned(q, 4) || !aligned(k, 4) || !aligned(labels, 4))
+    return fail(HATA_ERR_ALIGN, "hash_labels: q, k and labels must be 4-byte aligned");
+  int st = pre_launch("hash_labels");
+  if (st) return st;
+  hipError_t e = hata::launch_hash_labels(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), q_pos,
+                                          J, n, pos_permille, s_max, s_min, labels,
+                                          reinterpret_cast<hipStream_t>(stream));
+  return check_launch(e, "hash_labels launch");
+}
+
+size_t hata_hash_train_workspace_bytes(int J, int n, int d, int r) {
+  if (J < 1 || n < 1 || d != 128 || r < 32 || r > 256 || r % 32 != 0) return 0;
+  return hata::plan_train(J, n, r).total;
+}
+
+int hata_hash_train_step(const void* q, const void* k, const int32_t* q_pos, const float* labels, int J, int n,
+                         int d, int r, float sigma, float eps, float eta, float lam, float lr, float* W,
+                         float* grad, float* loss, void* ws, size_t ws_bytes, void* stream) {
+  if (!q || !k || !q_pos || !labels || !W || !loss) return fail(HATA_ERR_NULL, "hash_train_step: null pointer");
+  if (d != 128) return fail(HATA_ERR_UNSUPPORTED, "hash_train_step: d=%d unsupported (only 128)", d);
+  if (r < 32 || r > 256 || r % 32 != 0)
+    return fail(HATA_ERR_UNSUPPORTED, "hash_train_step: r=%d unsupported (multiples of 32 up to 256)", r);
+  if (J < 1 || n < 1 || (int64_t)J * n > ((int64_t)1 << 31))
+    return fail(HATA_ERR_SHAPE, "hash_train_step: J=%d n=%d", J, n);
+  if (!aligned(q, 4) || !aligned(k, 4) || !aligned(labels, 4) || !aligned(W, 4))
+    return fail(HATA_ERR_ALIGN, "hash_train_step: misaligned buffer");
+  const hata::TrainPlan p = hata::plan_train(J, n, r);
+  if (!ws || ws_bytes < p.total)
+    return fail(HATA_ERR_WORKSPACE, "hash_train_step: workspace of %zu bytes needed, %zu given", p.total, ws_bytes);
+  int st = pre_launch("hash_train_step");
+  if (st) return st;
+  hipError_t e = hata::launch_hash_train_step(p, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                                              q_pos, labels, J, n, r, sigma, eps, eta, lam, lr, W, grad, loss,
+                                              static_cast<unsigned char*>(ws), reinterpret_cast<hipStream_t>(stream));
+  return check_launch(e, "hash_train_step launch");
+}
+
 size_t hata_workspace_bytes(int op, int B, int Hq, int Hkv, int d, int r, int64_t max_len, int k) {
   (void)d;
   if (B < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || max_len < 1 || k < 1) return 0;

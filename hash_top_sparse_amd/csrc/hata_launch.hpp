@@ -55,6 +55,21 @@ hipError_t launch_decode_step(const StepPlan& p, const uint16_t* q, const uint16
 
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s);
 
+// training step of the hash weights (train.hip)
+constexpr int kMaxLabelKeys = 8192;  // keys a label row may rank (LDS sort)
+struct TrainPlan {
+  size_t hq = 0, hk = 0, shk = 0, sthq = 0, cm = 0, mtc = 0, rs = 0, cs = 0, dzq = 0, dzk = 0, gram = 0,
+         dw = 0, wa = 0, partq = 0, partk = 0, fac = 0, total = 0;
+};
+TrainPlan plan_train(int J, int n, int r);
+size_t label_lds_bytes();
+hipError_t launch_hash_labels(const uint16_t* q, const uint16_t* k, const int32_t* q_pos, int J, int n,
+                              int pos_permille, float s_max, float s_min, float* S, hipStream_t s);
+hipError_t launch_hash_train_step(const TrainPlan& p, const uint16_t* q, const uint16_t* k, const int32_t* q_pos,
+                                  const float* S, int J, int n, int r, float sigma, float eps, float eta,
+                                  float lam, float lr, float* W, float* grad, float* loss, unsigned char* ws,
+                                  hipStream_t s);
+
 // read-only streaming reduction (measurement of the device's HBM read rate)
 int stream_read_blocks();
 hipError_t launch_stream_read(const void* src, size_t bytes, uint64_t* sink, int blocks, hipStream_t s);

@@ -213,6 +213,46 @@ int hata_dense_decode(const void* q, const void* K, const void* V, int B,
 int hata_stream_read(const void* src, size_t bytes, uint64_t* sink,
                      size_t sink_words, void* stream);
 
+/*
+ * Training pairs for the hash weights (HATA notes, "Key design",
+ * "Learning-to-Hash modelling", training-data construction): for sampled
+ * query j (row j of q [J][d] bf16, sitting at position q_pos[j] of the
+ * sequence, clamped into [0, n)), its keys 0..q_pos[j] of k [n][d] bf16 are
+ * scored by the fp32 dot product q.k and ranked (higher score first, ties to
+ * the lower key index); the first P = max(1, ceil((q_pos[j] + 1) *
+ * pos_permille / 1000)) are positives, labelled s_max for the first down to
+ * s_min for the P-th linearly in rank (s_max alone when P = 1), the others
+ * -1.  labels [J][n] fp32 (device): row j holds those labels for keys
+ * 0..q_pos[j] and 0 beyond.  The pages use the top 10% (pos_permille = 100)
+ * and labels in [1, 20].  d = 128; 1 <= n <= 8192 (HATA_ERR_UNSUPPORTED
+ * above); q_pos is a device int32[J].
+ */
+int hata_hash_labels(const void* q, const void* k, const int32_t* q_pos, int J,
+                     int n, int d, int pos_permille, float s_max, float s_min,
+                     float* labels, void* stream);
+
+/*
+ * One gradient step on one head's hash weights W [d][r] fp32 (device, updated
+ * in place), HATA notes, "Key design", "Learning-to-Hash modelling": with the
+ * relaxed hash h(x) = 2 Sigmoid(sigma x W) - 1 the loss is
+ *   eps * sum_j sum_{i <= q_pos[j]} labels[j][i] * ||h(q_j) - h(k_i)||^2
+ * + eta * sum_j ||sum_{i <= q_pos[j]} h(k_i)||^2 + lam * ||W^T W - I_r||_F
+ * (the Frobenius norm taken unsquared) and the step is W -= lr * dL/dW, all
+ * in fp32.  loss [4] fp32 (device) receives the total and the three terms
+ * before the step; grad [d][r] (device, nullable) the gradient.  labels as
+ * hata_hash_labels writes them; d = 128; r a multiple of 32 up to 256.
+ * ws: hata_hash_train_workspace_bytes(J, n, d, r) bytes (contents not
+ * kept between calls).
+ */
+int hata_hash_train_step(const void* q, const void* k, const int32_t* q_pos,
+                         const float* labels, int J, int n, int d, int r,
+                         float sigma, float eps, float eta, float lam, float lr,
+                         float* W, float* grad, float* loss, void* ws,
+                         size_t ws_bytes, void* stream);
+
+/* Workspace bytes of hata_hash_train_step (0 for unsupported sizes). */
+size_t hata_hash_train_workspace_bytes(int J, int n, int d, int r);
+
 /* Workspace bytes for operation `op` at these sizes (0 if none is needed). */
 size_t hata_workspace_bytes(int op, int B, int Hq, int Hkv, int d, int r,
                             int64_t max_len, int k);

@@ -17,6 +17,7 @@ P = ctypes.c_void_p
 F = ctypes.c_float
 A = P(0x10000)        # aligned, never dereferenced: validation fails or the hook fires first
 MIS = P(0x10008)      # 8-byte but not 16-byte aligned
+MIS2 = P(0x10002)     # 2-byte but not 4-byte aligned
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -157,6 +158,43 @@ def test_decode_step_qk_validation():
     assert step(k=0) == EUNSUP
     assert step(max_len=8192) == ESHAPE
     assert step(codes=MIS) == EALIGN
+
+
+def test_hash_labels_validation(lib):
+    f = lib.hata_hash_labels
+    ok = dict(q=A, k=A, pos=A, J=16, n=1024, d=128, pm=100, lab=A)
+
+    def call(**kw):
+        a = dict(ok)
+        a.update(kw)
+        return f(a["q"], a["k"], a["pos"], a["J"], a["n"], a["d"], a["pm"], F(20.0), F(1.0), a["lab"], None)
+    assert call(q=None) == ENULL
+    assert call(lab=None) == ENULL
+    assert call(d=64) == EUNSUP
+    assert call(n=8193) == EUNSUP
+    assert call(J=0) == ESHAPE
+    assert call(pm=0) == ESHAPE
+    assert call(pm=1001) == ESHAPE
+    assert call(k=MIS2) == EALIGN
+
+
+def test_hash_train_step_validation(lib):
+    f = lib.hata_hash_train_step
+    need = lib.hata_hash_train_workspace_bytes(64, 1024, 128, 128)
+    assert need > 0
+    assert lib.hata_hash_train_workspace_bytes(64, 1024, 128, 48) == 0
+    assert lib.hata_hash_train_workspace_bytes(64, 1024, 96, 128) == 0
+
+    def call(r=128, d=128, W=A, loss=A, ws_bytes=need, J=64, n=1024):
+        return f(A, A, A, A, J, n, d, r, F(1.0), F(1.0), F(1.0), F(1.0), F(0.01), W, None, loss, A,
+                 ctypes.c_size_t(ws_bytes), None)
+    assert call(W=None) == ENULL
+    assert call(loss=None) == ENULL
+    assert call(d=96) == EUNSUP
+    assert call(r=48) == EUNSUP
+    assert call(r=512) == EUNSUP
+    assert call(J=0) == ESHAPE
+    assert call(ws_bytes=need - 1) == EWS
 
 
 def lib_stream_read_valid():

@@ -1,0 +1,116 @@
+"""GPU parity of the hash-weight training step (hata_hash_labels,
+hata_hash_train_step) against the fp64 oracle (oracle/train.py), through the
+C ABI on seeded synthetic Q/K."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+from hash_top_sparse_amd import synth
+from helpers import bf16_tensor
+from oracle import train
+
+pytestmark = pytest.mark.gpu
+
+
+def _log(msg):
+    print(msg, flush=True)
+
+
+def _qk(J, n, seed, exact=False):
+    rng = np.random.default_rng(seed)
+    if exact:  # multiples of 1/8 with |a| <= 8: every fp32 dot product is exact
+        q = rng.integers(-8, 9, size=(J, 128)).astype(np.float32) / 8
+        k = rng.integers(-8, 9, size=(n, 128)).astype(np.float32) / 8
+    else:
+        q = rng.standard_normal((J, 128)).astype(np.float32)
+        k = rng.standard_normal((n, 128)).astype(np.float32)
+    pos = np.sort(rng.choice(n, size=J, replace=False)).astype(np.int32)
+    pos[0] = 0
+    pos[-1] = n - 1
+    return synth.bf16_bits(q), synth.bf16_bits(k), pos
+
+
+@pytest.mark.parametrize("n", [1, 700, 3000, 8192])
+def test_labels_exact_inputs_match_oracle(hata_gpu, n):
+    J = min(24, n)
+    q, k, pos = _qk(J, n, 9100 + n, exact=True)
+    if n == 1:
+        pos[:] = 0
+    _log(f"labels exact n={n}")
+    S = torch.full((J, n), np.nan, dtype=torch.float32, device="cuda")
+    hata_gpu.hash_labels(bf16_tensor(q), bf16_tensor(k), torch.from_numpy(pos).cuda(), S)
+    torch.cuda.synchronize()
+    ref = train.labels(q, k, pos)
+    got = S.cpu().numpy()
+    np.testing.assert_array_equal(got > 0, ref > 0)      # the same positives
+    np.testing.assert_array_equal(got == -1, ref == -1)  # the same negatives
+    np.testing.assert_allclose(got, ref, rtol=1e-6, atol=1e-6)
+
+
+def test_labels_gaussian_inputs_valid(hata_gpu):
+    """fp32 scores may order near-ties differently from fp64: every
+    disagreement must involve keys whose fp64 scores lie within 1e-4 of the
+    positive/negative boundary, and each row keeps exactly P positives."""
+    J, n = 32, 4096
+    q, k, pos = _qk(J, n, 9200)
+    S = torch.zeros((J, n), dtype=torch.float32, device="cuda")
+    hata_gpu.hash_labels(bf16_tensor(q), bf16_tensor(k), torch.from_numpy(pos).cuda(), S)
+    torch.cuda.synchronize()
+    got = S.cpu().numpy()
+    ref = train.labels(q, k, pos)
+    Q, K = train.bf16_to_f64(q), train.bf16_to_f64(k)
+    for j in range(J):
+        p = int(pos[j])
+        P = max(1, ((p + 1) * 100 + 999) // 1000)
+        assert int((got[j, :p + 1] > 0).sum()) == P
+        diff = np.nonzero((got[j, :p + 1] > 0) != (ref[j, :p + 1] > 0))[0]
+        if diff.size:
+            sc = K[:p + 1] @ Q[j]
+            edge = np.sort(sc)[::-1][P - 1]
+            assert np.all(np.abs(sc[diff] - edge) <= 1e-4 * max(1.0, abs(edge)))
+
+
+@pytest.mark.parametrize("r", [64, 128, 256])
+def test_train_step_matches_oracle(hata_gpu, r):
+    J, n = 64, 1536
+    q, k, pos = _qk(J, n, 9300 + r)
+    rng = np.random.default_rng(9400 + r)
+    W0 = (rng.standard_normal((128, r)) / np.sqrt(128.0)).astype(np.float32)
+    S = train.labels(q, k, pos)
+    sigma, eps, eta, lam, lr = 1.5, 1e-3, 2e-4, 0.3, 0.02
+    _log(f"train step r={r}")
+    W = torch.from_numpy(W0.copy()).cuda()
+    grad = torch.zeros_like(W)
+    loss = torch.zeros(4, dtype=torch.float32, device="cuda")
+    ws = hata_gpu.hash_train_workspace(J, n, r)
+    hata_gpu.hash_train_step(bf16_tensor(q), bf16_tensor(k), torch.from_numpy(pos).cuda(),
+                             torch.from_numpy(S.astype(np.float32)).cuda(), W, sigma, eps, eta, lam, lr,
+                             loss, ws, grad=grad)
+    torch.cuda.synchronize()
+    ref_g = train.grad(q, k, pos, S.astype(np.float32).astype(np.float64), W0, sigma, eps, eta, lam)
+    ref_l = train.loss(q, k, pos, S.astype(np.float32).astype(np.float64), W0, sigma, eps, eta, lam)
+    g = grad.cpu().numpy()
+    scale = np.abs(ref_g).max()
+    np.testing.assert_allclose(g, ref_g, rtol=2e-3, atol=2e-3 * scale)
+    np.testing.assert_allclose(loss.cpu().numpy(), np.array(ref_l), rtol=1e-3)
+    # the device forms W - lr * g with one fused multiply-add (one rounding)
+    np.testing.assert_allclose(W.cpu().numpy(), W0.astype(np.float64) - lr * g.astype(np.float64),
+                               rtol=0, atol=2e-7 * max(1.0, float(np.abs(W0).max())))
+
+
+def test_train_steps_descend_on_device(hata_gpu):
+    J, n, r = 128, 2048, 128
+    q, k, pos = _qk(J, n, 9500)
+    qd, kd, pd = bf16_tensor(q), bf16_tensor(k), torch.from_numpy(pos).cuda()
+    S = torch.zeros((J, n), dtype=torch.float32, device="cuda")
+    hata_gpu.hash_labels(qd, kd, pd, S)
+    W = (torch.randn((128, r), generator=torch.Generator().manual_seed(3)) / np.sqrt(128.0)).cuda()
+    loss = torch.zeros(4, dtype=torch.float32, device="cuda")
+    ws = hata_gpu.hash_train_workspace(J, n, r)
+    seen = []
+    for _ in range(8):
+        hata_gpu.hash_train_step(qd, kd, pd, S, W, 1.0, 1e-3, 1e-4, 0.1, 0.01, loss, ws)
+        seen.append(float(loss[0].item()))
+    assert seen[-1] < seen[0]
