@@ -390,6 +390,53 @@ def model_sweep(layers: int = 32, ctxs=(32768, 65536, 131072), reps: int = 10) -
     return res
 
 
+def train_bench(J: int = 512, n: int = 8192, r: int = 128, steps: int = 20) -> dict:
+    """Time the hash-weight training step for one head (synthetic bf16 N(0,1)
+    Q/K drawn on the device, J sampled queries at random positions of an
+    n-key sequence): the label kernel and one gradient step, HIP events over
+    `steps` calls each.  FLOP count of the step: the two projections, the
+    four J x n x r pair products, the two gradient products and the W^T W
+    terms."""
+    import torch
+
+    from hash_top_sparse_amd import binding
+
+    dev = torch.device("cuda:0")
+    g = torch.Generator(device=dev)
+    g.manual_seed(7100)
+    q = torch.randn((J, 128), generator=g, device=dev).to(torch.bfloat16)
+    k = torch.randn((n, 128), generator=g, device=dev).to(torch.bfloat16)
+    pos = torch.sort(torch.randperm(n, generator=torch.Generator().manual_seed(7101))[:J]).values
+    pos = pos.to(torch.int32).to(dev)
+    W = torch.randn((128, r), generator=g, device=dev) / np.sqrt(128.0)
+    S = torch.zeros((J, n), dtype=torch.float32, device=dev)
+    loss = torch.zeros(4, dtype=torch.float32, device=dev)
+    ws = binding.hash_train_workspace(J, n, r)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    binding.hash_labels(q, k, pos, S)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(steps):
+        binding.hash_labels(q, k, pos, S)
+    e1.record()
+    torch.cuda.synchronize()
+    lab_ms = e0.elapsed_time(e1) / steps
+    binding.hash_train_step(q, k, pos, S, W, 1.0, 1e-3, 1e-4, 0.1, 1e-3, loss, ws)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(steps):
+        binding.hash_train_step(q, k, pos, S, W, 1.0, 1e-3, 1e-4, 0.1, 1e-3, loss, ws)
+    e1.record()
+    torch.cuda.synchronize()
+    st_ms = e0.elapsed_time(e1) / steps
+    flops = 8.0 * J * n * r + 4.0 * (J + n) * 128 * r + 4.0 * 128 * r * r
+    tf = flops / (st_ms * 1e-3) / 1e12
+    log(f"hash training, J={J} n={n} r={r}: labels {lab_ms * 1e3:.1f} us, step {st_ms * 1e3:.1f} us "
+        f"({tf:.2f} TFLOP/s fp32)")
+    return {"J": J, "n": n, "r": r, "labels_ms": lab_ms, "step_ms": st_ms, "step_flops": flops,
+            "step_TFLOPs": tf, "frac_of_fp32_peak": tf / 157.3, "loss_after": loss.cpu().tolist()}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -403,6 +450,8 @@ def main() -> int:
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="launch the timed steps eagerly")
     ap.add_argument("--sweep", action="store_true", help="also time the other workloads (2, 3, 5)")
+    ap.add_argument("--train", action="store_true",
+                    help="also time the hash-weight training step (labels + one gradient step, one head)")
     ap.add_argument("--width-sweep", action="store_true",
                     help="also time the workload with 32-, 64- and 256-bit codes")
     ap.add_argument("--model-sweep", action="store_true",
@@ -460,6 +509,7 @@ def main() -> int:
                               "GBs": rr["GBs"], "frac_of_peak": rr["frac_of_peak"],
                               "bytes_per_step": rr["bytes_per_step"], "stored_bytes_per_step": layout}
     msweep = model_sweep() if args.model_sweep else None
+    tbench = train_bench() if args.train else None
     peak_meas = read_peak()
     log(f"streaming read of 4 GiB: {peak_meas:.0f} GB/s")
     cpu = None
@@ -505,6 +555,8 @@ def main() -> int:
         res["model_sweep"] = msweep
     if wsweep is not None:
         res["code_widths"] = wsweep
+    if tbench is not None:
+        res["hash_train"] = tbench
     print(json.dumps(res), flush=True)
     return 0
 

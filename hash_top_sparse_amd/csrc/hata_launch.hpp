@@ -59,9 +59,10 @@ hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s);
 constexpr int kMaxLabelKeys = 8192;  // keys a label row may rank (LDS sort)
 struct TrainPlan {
   size_t hq = 0, hk = 0, shk = 0, sthq = 0, cm = 0, mtc = 0, rs = 0, cs = 0, dzq = 0, dzk = 0, gram = 0,
-         dw = 0, wa = 0, partq = 0, partk = 0, fac = 0, total = 0;
+         dw = 0, wa = 0, partq = 0, partk = 0, fac = 0, part = 0, total = 0;
 };
 TrainPlan plan_train(int J, int n, int r);
+int train_gemm_splits(int M, int N, int K);
 size_t label_lds_bytes();
 hipError_t launch_hash_labels(const uint16_t* q, const uint16_t* k, const int32_t* q_pos, int J, int n,
                               int pos_permille, float s_max, float s_min, float* S, hipStream_t s);

@@ -18,6 +18,8 @@
 //   dL/dHk = 2 eps (colsum(S) Hk - S^T Hq) + 2 eta M^T (M Hk),  M_ji = [i <= p_j]
 //   dL/dW  = sigma (Q^T dZq + K^T dZk) + 2 lam W A / ||A||_F,   A = W^T W - I
 // then W <- W - lr dL/dW.  The loss terms come from the same products.
+#include <algorithm>
+
 #include "hata_device.hpp"
 #include "hata_launch.hpp"
 
@@ -90,66 +92,108 @@ __global__ __launch_bounds__(kLabNT) void labels_kernel(const uint16_t* __restri
 
 // ------------------------------------------------------------ tiled GEMM
 // C[M][N] = alpha * sum_k A(m, k) B(k, n) (+ C if accumulate), fp32.  A and
-// B are read through accessor structs; 64 x 64 tiles, 16-deep k steps staged
-// in LDS, 256 threads with 4 x 4 outputs each.
+// B are read through accessor structs; kColFast says whether consecutive
+// column indices are adjacent in memory, and the tile fill lets consecutive
+// lanes walk that index so the global reads coalesce.  64 x 64 output tiles,
+// 32-deep k steps staged in LDS (rows padded by 4 floats: 16-byte aligned
+// vector reads, conflict-free column writes), the next step's operands held
+// in registers while the current one is multiplied, 256 threads with 4 x 4
+// outputs each.  Products with few output tiles and a long k split k over
+// blockIdx.z; each split writes its own partial tile and a second kernel
+// adds the partials in split order (deterministic).
 struct AccF32 {  // row-major [rows][ld]
+  static constexpr bool kColFast = true;
   const float* p; int ld;
   __device__ float operator()(int r, int c) const { return p[(int64_t)r * ld + c]; }
 };
 struct AccF32T {  // element (r, c) of the transpose of a row-major [.][ld]
+  static constexpr bool kColFast = false;
   const float* p; int ld;
   __device__ float operator()(int r, int c) const { return p[(int64_t)c * ld + r]; }
 };
 struct AccBf16 {
+  static constexpr bool kColFast = true;
   const uint16_t* p; int ld;
   __device__ float operator()(int r, int c) const { return __uint_as_float((uint32_t)p[(int64_t)r * ld + c] << 16); }
 };
 struct AccBf16T {
+  static constexpr bool kColFast = false;
   const uint16_t* p; int ld;
   __device__ float operator()(int r, int c) const { return __uint_as_float((uint32_t)p[(int64_t)c * ld + r] << 16); }
 };
 struct AccMask {  // M_ji = [i <= p_j] (rows j, columns i)
+  static constexpr bool kColFast = true;
   const int32_t* pos; int n;
   __device__ float operator()(int r, int c) const { return c <= min(max(pos[r], 0), n - 1) ? 1.f : 0.f; }
 };
 struct AccMaskT {  // M^T
+  static constexpr bool kColFast = false;
   const int32_t* pos; int n;
   __device__ float operator()(int r, int c) const { return r <= min(max(pos[c], 0), n - 1) ? 1.f : 0.f; }
 };
 struct AccGramMinusI {  // (W^T W - I)[r][c] from a precomputed W^T W
+  static constexpr bool kColFast = true;
   const float* p; int ld;
   __device__ float operator()(int r, int c) const { return p[(int64_t)r * ld + c] - (r == c ? 1.f : 0.f); }
 };
 
-constexpr int kT = 64, kKS = 16;
+constexpr int kT = 64, kKS = 32, kLdsRow = kT + 4, kFill = kT * kKS / 256;
+
+// element u of this thread's share of the A tile (rows m0.., k k0..)
+template <bool ColFast>
+__device__ inline void a_slot(int t, int u, int& mm, int& kk) {
+  const int e = t + 256 * u;
+  if constexpr (ColFast) { mm = e / kKS; kk = e % kKS; } else { mm = e % kT; kk = e / kT; }
+}
+// element u of this thread's share of the B tile (k k0.., columns n0..)
+template <bool ColFast>
+__device__ inline void b_slot(int t, int u, int& kk, int& nn) {
+  const int e = t + 256 * u;
+  if constexpr (ColFast) { nn = e % kT; kk = e / kT; } else { nn = e / kKS; kk = e % kKS; }
+}
 
 template <class A, class B>
-__global__ __launch_bounds__(256) void gemm_kernel(int M, int N, int K, A a, B b, float* __restrict__ C,
-                                                   int ldc, float alpha, int accumulate) {
-  __shared__ float as[kKS][kT + 1];
-  __shared__ float bs[kKS][kT + 1];
+__global__ __launch_bounds__(256) void gemm_kernel(int M, int N, int K, int kchunk, A a, B b,
+                                                   float* __restrict__ C, int ldc, float alpha, int accumulate,
+                                                   float* __restrict__ part, int tanh_out) {
+  __shared__ __align__(16) float as[kKS][kLdsRow];
+  __shared__ __align__(16) float bs[kKS][kLdsRow];
   const int t = threadIdx.x, tx = t & 15, ty = t >> 4;
   const int m0 = blockIdx.y * kT, n0 = blockIdx.x * kT;
+  const int kbeg = blockIdx.z * kchunk, kend = min(K, kbeg + kchunk);
+  float ra[kFill], rb[kFill];
+  auto fetch = [&](int k0) {
+#pragma unroll
+    for (int u = 0; u < kFill; ++u) {
+      int mm, kk, nn, kb;
+      a_slot<A::kColFast>(t, u, mm, kk);
+      ra[u] = (m0 + mm < M && k0 + kk < kend) ? a(m0 + mm, k0 + kk) : 0.f;
+      b_slot<B::kColFast>(t, u, kb, nn);
+      rb[u] = (k0 + kb < kend && n0 + nn < N) ? b(k0 + kb, n0 + nn) : 0.f;
+    }
+  };
   float acc[4][4] = {};
-  for (int k0 = 0; k0 < K; k0 += kKS) {
-    for (int e = t; e < kT * kKS; e += 256) {
-      const int mm = e / kKS, kk = e % kKS;
-      as[kk][mm] = (m0 + mm < M && k0 + kk < K) ? a(m0 + mm, k0 + kk) : 0.f;
-      const int kb = e / kT, nn = e % kT;
-      bs[kb][nn] = (k0 + kb < K && n0 + nn < N) ? b(k0 + kb, n0 + nn) : 0.f;
+  if (kbeg < kend) fetch(kbeg);
+  for (int k0 = kbeg; k0 < kend; k0 += kKS) {
+#pragma unroll
+    for (int u = 0; u < kFill; ++u) {
+      int mm, kk, nn, kb;
+      a_slot<A::kColFast>(t, u, mm, kk);
+      as[kk][mm] = ra[u];
+      b_slot<B::kColFast>(t, u, kb, nn);
+      bs[kb][nn] = rb[u];
     }
     __syncthreads();
-#pragma unroll
+    if (k0 + kKS < kend) fetch(k0 + kKS);
+#pragma unroll 8
     for (int kk = 0; kk < kKS; ++kk) {
-      float av[4], bv[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) av[i] = as[kk][ty * 4 + i];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) bv[i] = bs[kk][tx * 4 + i];
+      const float4 av = *reinterpret_cast<const float4*>(&as[kk][ty * 4]);
+      const float4 bv = *reinterpret_cast<const float4*>(&bs[kk][tx * 4]);
+      const float ax[4] = {av.x, av.y, av.z, av.w}, bx[4] = {bv.x, bv.y, bv.z, bv.w};
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) acc[i][jj] = fmaf(av[i], bv[jj], acc[i][jj]);
+        for (int jj = 0; jj < 4; ++jj) acc[i][jj] = fmaf(ax[i], bx[jj], acc[i][jj]);
     }
     __syncthreads();
   }
@@ -159,25 +203,79 @@ __global__ __launch_bounds__(256) void gemm_kernel(int M, int N, int K, A a, B b
     for (int jj = 0; jj < 4; ++jj) {
       const int mm = m0 + ty * 4 + i, nn = n0 + tx * 4 + jj;
       if (mm < M && nn < N) {
-        float* c = C + (int64_t)mm * ldc + nn;
-        *c = alpha * acc[i][jj] + (accumulate ? *c : 0.f);
+        if (part) {
+          part[((int64_t)blockIdx.z * M + mm) * N + nn] = acc[i][jj];
+        } else {
+          float* c = C + (int64_t)mm * ldc + nn;
+          const float v = alpha * acc[i][jj] + (accumulate ? *c : 0.f);
+          *c = tanh_out ? tanhf(v) : v;
+        }
       }
     }
 }
 
+// C = alpha * sum_z part[z] (+ C), splits added in order; four adjacent
+// outputs per thread (N and ldc are multiples of 4), eight splits' loads
+// issued before their adds
+__global__ void splitk_reduce_kernel(const float* __restrict__ part, int splits, int M, int N,
+                                     float* __restrict__ C, int ldc, float alpha, int accumulate) {
+  const int64_t e4 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t mn = (int64_t)M * N;
+  if (e4 * 4 >= mn) return;
+  const float4* p4 = reinterpret_cast<const float4*>(part) + e4;
+  const int64_t zs = mn / 4;
+  float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+  int z = 0;
+  for (; z + 8 <= splits; z += 8) {
+    float4 t[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) t[u] = p4[(z + u) * zs];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) { v.x += t[u].x; v.y += t[u].y; v.z += t[u].z; v.w += t[u].w; }
+  }
+  for (; z < splits; ++z) {
+    const float4 t = p4[z * zs];
+    v.x += t.x; v.y += t.y; v.z += t.z; v.w += t.w;
+  }
+  const int64_t e = e4 * 4;
+  float* c = C + (e / N) * ldc + e % N;
+  const float o[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int u = 0; u < 4; ++u) c[u] = alpha * o[u] + (accumulate ? c[u] : 0.f);
+}
+
+}  // namespace
+
+// number of k splits for an M x N x K product: aim at about four
+// workgroups per compute unit, each split at least 128 deep
+int train_gemm_splits(int M, int N, int K) {
+  const int tiles = ((M + kT - 1) / kT) * ((N + kT - 1) / kT);
+  const int want = (1024 + tiles - 1) / tiles;
+  const int s = std::min(want, K / 128);
+  return std::max(s, 1);
+}
+
+namespace {
+
 template <class A, class B>
-hipError_t gemm(int M, int N, int K, A a, B b, float* C, int ldc, float alpha, bool accumulate, hipStream_t s) {
-  dim3 grid((unsigned)((N + kT - 1) / kT), (unsigned)((M + kT - 1) / kT));
-  hipLaunchKernelGGL((gemm_kernel<A, B>), grid, dim3(256), 0, s, M, N, K, a, b, C, ldc, alpha, accumulate ? 1 : 0);
+hipError_t gemm(int M, int N, int K, A a, B b, float* C, int ldc, float alpha, bool accumulate, float* part,
+                hipStream_t s, bool tanh_out = false) {
+  const int splits = tanh_out ? 1 : train_gemm_splits(M, N, K);
+  const int kchunk = splits == 1 ? K : ((K + splits - 1) / splits + kKS - 1) / kKS * kKS;
+  const int z = splits == 1 ? 1 : (K + kchunk - 1) / kchunk;
+  dim3 grid((unsigned)((N + kT - 1) / kT), (unsigned)((M + kT - 1) / kT), (unsigned)z);
+  hipLaunchKernelGGL((gemm_kernel<A, B>), grid, dim3(256), 0, s, M, N, K, kchunk, a, b, C, ldc, alpha,
+                     accumulate ? 1 : 0, z == 1 ? (float*)nullptr : part, tanh_out ? 1 : 0);
+  if (z > 1) {
+    if (N % 4 != 0 || ldc % 4 != 0) return hipErrorInvalidValue;
+    const int64_t cnt = (int64_t)M * N / 4;
+    hipLaunchKernelGGL(splitk_reduce_kernel, dim3((unsigned)((cnt + 255) / 256)), dim3(256), 0, s, part, z, M, N,
+                       C, ldc, alpha, accumulate ? 1 : 0);
+  }
   return hipGetLastError();
 }
 
 // ------------------------------------------------------------ elementwise
-__global__ void tanh_half_kernel(float* z, int64_t count, float half_sigma) {
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < count) z[i] = tanhf(half_sigma * z[i]);
-}
-
 // rows of X [rows][cols]: out[r] = sum_c X[r][c] (sums S_j) or columns
 __global__ void row_sums_kernel(const float* __restrict__ X, int rows, int cols, float* __restrict__ out) {
   const int r = blockIdx.x;
@@ -192,24 +290,46 @@ __global__ void row_sums_kernel(const float* __restrict__ X, int rows, int cols,
   }
   if (threadIdx.x == 0) out[r] = red[0];
 }
-__global__ void col_sums_kernel(const float* __restrict__ X, int rows, int cols, float* __restrict__ out) {
+// column sums in two passes: pass 1 gives kColChunks partial sums per
+// column (workgroup = 64 columns x 4 row slices of one row chunk), pass 2
+// adds the partials in chunk order
+constexpr int kColChunks = 16;
+__global__ void col_sums_part_kernel(const float* __restrict__ X, int rows, int cols, float* __restrict__ part) {
+  __shared__ float red[4][64];
+  const int c = blockIdx.x * 64 + (threadIdx.x & 63), sl = threadIdx.x >> 6;
+  const int per = (rows + kColChunks - 1) / kColChunks;
+  const int r0 = blockIdx.y * per, r1 = min(rows, r0 + per);
+  float a = 0.f;
+  if (c < cols)
+    for (int r = r0 + sl; r < r1; r += 4) a += X[(int64_t)r * cols + c];
+  red[sl][threadIdx.x & 63] = a;
+  __syncthreads();
+  if (sl == 0 && c < cols) {
+    const int l = threadIdx.x;
+    part[(int64_t)blockIdx.y * cols + c] = ((red[0][l] + red[1][l]) + red[2][l]) + red[3][l];
+  }
+}
+__global__ void col_sums_finish_kernel(const float* __restrict__ part, int cols, float* __restrict__ out) {
   const int c = blockIdx.x * blockDim.x + threadIdx.x;
   if (c >= cols) return;
   float a = 0.f;
-  for (int r = 0; r < rows; ++r) a += X[(int64_t)r * cols + c];
+#pragma unroll
+  for (int z = 0; z < kColChunks; ++z) a += part[(int64_t)z * cols + c];
   out[c] = a;
 }
 
 // dZ = (2 eps (rs * H - P) + 2 eta Qb) * (1 - H^2) / 2 per element, where P
 // is the pair product (S Hk or S^T Hq) and Qb the balance product (M^T C,
 // or null for the queries).  Also the per-row partial loss sums:
-// part[row] = rs * ||H_row||^2 (for the similarity term) and
-// part2[row] = H_row . P_row.
+// part[3 row] = rs * ||H_row||^2 (for the similarity term),
+// part[3 row + 1] = H_row . P_row and part[3 row + 2] = ||Cb_row||^2 (the
+// balance term; Cb = M Hk for the queries, null for the keys).
 __global__ void dz_kernel(const float* __restrict__ H, const float* __restrict__ P,
-                          const float* __restrict__ Qb, const float* __restrict__ rs, int rows, int r,
+                          const float* __restrict__ Qb, const float* __restrict__ Cb,
+                          const float* __restrict__ rs, int rows, int r,
                           float eps, float eta, float* __restrict__ dZ, float* __restrict__ part) {
   const int row = blockIdx.x;
-  float a1 = 0.f, a2 = 0.f;
+  float a1 = 0.f, a2 = 0.f, a3 = 0.f;
   const float w = rs[row];
   for (int c = threadIdx.x; c < r; c += blockDim.x) {
     const int64_t e = (int64_t)row * r + c;
@@ -219,43 +339,48 @@ __global__ void dz_kernel(const float* __restrict__ H, const float* __restrict__
     dZ[e] = g * (1.f - h * h) * 0.5f;
     a1 += w * h * h;
     a2 += h * pp;
+    if (Cb) a3 += Cb[e] * Cb[e];
   }
-  __shared__ float red[2][256];
+  __shared__ float red[3][256];
   red[0][threadIdx.x] = a1;
   red[1][threadIdx.x] = a2;
+  red[2][threadIdx.x] = a3;
   __syncthreads();
   for (int o = blockDim.x / 2; o > 0; o >>= 1) {
-    if ((int)threadIdx.x < o) {
-      red[0][threadIdx.x] += red[0][threadIdx.x + o];
-      red[1][threadIdx.x] += red[1][threadIdx.x + o];
-    }
+    if ((int)threadIdx.x < o)
+      for (int u = 0; u < 3; ++u) red[u][threadIdx.x] += red[u][threadIdx.x + o];
     __syncthreads();
   }
-  if (threadIdx.x == 0) {
-    part[2 * row] = red[0][0];
-    part[2 * row + 1] = red[1][0];
-  }
+  if (threadIdx.x == 0)
+    for (int u = 0; u < 3; ++u) part[3 * row + u] = red[u][0];
 }
 
-// Final loss terms and the decorrelation factor, one workgroup (fixed
-// order): loss[0..3] = total, similarity, balance, decorrelation;
-// fac[0] = 2 lam / ||A||_F (0 when A == 0), A = W^T W - I.
-__global__ void loss_kernel(const float* __restrict__ part_q, int J, const float* __restrict__ part_k, int n,
-                            const float* __restrict__ Cm, int r, const float* __restrict__ gram,
-                            float eps, float eta, float lam, float* __restrict__ loss, float* __restrict__ fac) {
-  __shared__ float red[4][256];
+// Final loss terms and the decorrelation factor, one workgroup of 1024
+// threads (fixed order): loss[0..3] = total, similarity, balance,
+// decorrelation; fac[0] = 2 lam / ||A||_F (0 when A == 0), A = W^T W - I.
+constexpr int kLossNT = 1024;
+__global__ __launch_bounds__(kLossNT) void loss_kernel(const float* __restrict__ part_q, int J,
+                                                       const float* __restrict__ part_k, int n, int r,
+                                                       const float* __restrict__ gram, float eps, float eta,
+                                                       float lam, float* __restrict__ loss,
+                                                       float* __restrict__ fac) {
+  __shared__ float red[4][kLossNT];
   const int t = threadIdx.x;
   float sq = 0.f, sk = 0.f, bal = 0.f, dec = 0.f;
-  for (int j = t; j < J; j += 256) sq += part_q[2 * j] - 2.f * part_q[2 * j + 1];
-  for (int i = t; i < n; i += 256) sk += part_k[2 * i];
-  for (int64_t e = t; e < (int64_t)J * r; e += 256) bal += Cm[e] * Cm[e];
-  for (int e = t; e < r * r; e += 256) {
+  for (int j = t; j < J; j += kLossNT) {
+    sq += part_q[3 * j] - 2.f * part_q[3 * j + 1];
+    bal += part_q[3 * j + 2];
+  }
+#pragma unroll 4
+  for (int i = t; i < n; i += kLossNT) sk += part_k[3 * i];
+#pragma unroll 4
+  for (int e = t; e < r * r; e += kLossNT) {
     const float v = gram[e] - ((e / r) == (e % r) ? 1.f : 0.f);
     dec += v * v;
   }
   red[0][t] = sq; red[1][t] = sk; red[2][t] = bal; red[3][t] = dec;
   __syncthreads();
-  for (int o = 128; o > 0; o >>= 1) {
+  for (int o = kLossNT / 2; o > 0; o >>= 1) {
     if (t < o)
       for (int q = 0; q < 4; ++q) red[q][t] += red[q][t + o];
     __syncthreads();
@@ -270,20 +395,14 @@ __global__ void loss_kernel(const float* __restrict__ part_q, int J, const float
   }
 }
 
-// W -= lr * dW, with dW += fac * W A already accumulated; optional gradient copy
-__global__ void update_kernel(float* __restrict__ W, const float* __restrict__ dW, float* __restrict__ grad,
-                              int count, float lr) {
+// g = dW + fac * W A (the full gradient), W -= lr * g; optional gradient copy
+__global__ void update_kernel(float* __restrict__ W, const float* __restrict__ dW, const float* __restrict__ WA,
+                              const float* __restrict__ fac, float* __restrict__ grad, int count, float lr) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= count) return;
-  const float g = dW[i];
+  const float g = dW[i] + fac[0] * WA[i];
   if (grad) grad[i] = g;
   W[i] -= lr * g;
-}
-
-__global__ void scale_add_wa_kernel(float* __restrict__ dW, const float* __restrict__ WA,
-                                    const float* __restrict__ fac, int count) {
-  const int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < count) dW[i] += fac[0] * WA[i];
 }
 
 }  // namespace
@@ -322,9 +441,19 @@ TrainPlan plan_train(int J, int n, int r) {
   p.gram = take((size_t)r * r);
   p.dw = take((size_t)kD * r);
   p.wa = take((size_t)kD * r);
-  p.partq = take((size_t)2 * J);
-  p.partk = take((size_t)2 * n);
+  p.partq = take((size_t)3 * J);
+  p.partk = take((size_t)3 * n);
   p.fac = take(4);
+  // the largest split-k partial buffer over the step's products
+  const int shapes[10][3] = {{J, r, kD}, {n, r, kD}, {J, r, n}, {n, r, J}, {J, r, n},
+                             {n, r, J}, {kD, r, J}, {kD, r, n}, {r, r, kD}, {kD, r, r}};
+  size_t part = 0;
+  for (const auto& g : shapes) {
+    const int sp = train_gemm_splits(g[0], g[1], g[2]);
+    if (sp > 1) part = std::max(part, (size_t)sp * g[0] * g[1]);
+  }
+  part = std::max(part, (size_t)kColChunks * n);  // column-sum partials
+  p.part = take(part);
   p.total = off;
   return p;
 }
@@ -336,39 +465,38 @@ hipError_t launch_hash_train_step(const TrainPlan& p, const uint16_t* q, const u
   auto F = [&](size_t off) { return reinterpret_cast<float*>(ws + off); };
   float *Hq = F(p.hq), *Hk = F(p.hk), *SHk = F(p.shk), *StHq = F(p.sthq), *Cm = F(p.cm), *MtC = F(p.mtc);
   float *rs = F(p.rs), *cs = F(p.cs), *dZq = F(p.dzq), *dZk = F(p.dzk), *gram = F(p.gram), *dW = F(p.dw);
-  float *WA = F(p.wa), *partq = F(p.partq), *partk = F(p.partk), *fac = F(p.fac);
+  float *WA = F(p.wa), *partq = F(p.partq), *partk = F(p.partk), *fac = F(p.fac), *part = F(p.part);
   hipError_t e;
 #define HATA_TRY(x) do { e = (x); if (e != hipSuccess) return e; } while (0)
   // H = tanh(sigma/2 * X W)
-  HATA_TRY(gemm(J, r, kD, AccBf16{q, kD}, AccF32{W, r}, Hq, r, 1.f, false, s));
-  HATA_TRY(gemm(n, r, kD, AccBf16{k, kD}, AccF32{W, r}, Hk, r, 1.f, false, s));
-  {
-    const int64_t a = (int64_t)J * r, b = (int64_t)n * r;
-    hipLaunchKernelGGL(tanh_half_kernel, dim3((unsigned)((a + 255) / 256)), dim3(256), 0, s, Hq, a, 0.5f * sigma);
-    hipLaunchKernelGGL(tanh_half_kernel, dim3((unsigned)((b + 255) / 256)), dim3(256), 0, s, Hk, b, 0.5f * sigma);
-    HATA_TRY(hipGetLastError());
-  }
+  HATA_TRY(gemm(J, r, kD, AccBf16{q, kD}, AccF32{W, r}, Hq, r, 0.5f * sigma, false, part, s, true));
+  HATA_TRY(gemm(n, r, kD, AccBf16{k, kD}, AccF32{W, r}, Hk, r, 0.5f * sigma, false, part, s, true));
   // pair products, label sums, balance products
-  HATA_TRY(gemm(J, r, n, AccF32{S, n}, AccF32{Hk, r}, SHk, r, 1.f, false, s));
-  HATA_TRY(gemm(n, r, J, AccF32T{S, n}, AccF32{Hq, r}, StHq, r, 1.f, false, s));
-  HATA_TRY(gemm(J, r, n, AccMask{q_pos, n}, AccF32{Hk, r}, Cm, r, 1.f, false, s));
-  HATA_TRY(gemm(n, r, J, AccMaskT{q_pos, n}, AccF32{Cm, r}, MtC, r, 1.f, false, s));
+  HATA_TRY(gemm(J, r, n, AccF32{S, n}, AccF32{Hk, r}, SHk, r, 1.f, false, part, s));
+  HATA_TRY(gemm(n, r, J, AccF32T{S, n}, AccF32{Hq, r}, StHq, r, 1.f, false, part, s));
+  HATA_TRY(gemm(J, r, n, AccMask{q_pos, n}, AccF32{Hk, r}, Cm, r, 1.f, false, part, s));
+  HATA_TRY(gemm(n, r, J, AccMaskT{q_pos, n}, AccF32{Cm, r}, MtC, r, 1.f, false, part, s));
   hipLaunchKernelGGL(row_sums_kernel, dim3(J), dim3(256), 0, s, S, J, n, rs);
-  hipLaunchKernelGGL(col_sums_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, S, J, n, cs);
+  hipLaunchKernelGGL(col_sums_part_kernel, dim3((unsigned)((n + 63) / 64), kColChunks), dim3(256), 0, s, S, J, n,
+                     part);
+  hipLaunchKernelGGL(col_sums_finish_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, part, n, cs);
   HATA_TRY(hipGetLastError());
   // dZ and the per-row loss parts
-  hipLaunchKernelGGL(dz_kernel, dim3(J), dim3(128), 0, s, Hq, SHk, (const float*)nullptr, rs, J, r, eps, eta, dZq, partq);
-  hipLaunchKernelGGL(dz_kernel, dim3(n), dim3(128), 0, s, Hk, StHq, MtC, cs, n, r, eps, eta, dZk, partk);
+  hipLaunchKernelGGL(dz_kernel, dim3(J), dim3(128), 0, s, Hq, SHk, (const float*)nullptr, (const float*)Cm, rs, J, r,
+                     eps, eta, dZq, partq);
+  hipLaunchKernelGGL(dz_kernel, dim3(n), dim3(128), 0, s, Hk, StHq, (const float*)MtC, (const float*)nullptr, cs, n,
+                     r, eps, eta, dZk, partk);
   HATA_TRY(hipGetLastError());
   // dW = sigma (Q^T dZq + K^T dZk)
-  HATA_TRY(gemm(kD, r, J, AccBf16T{q, kD}, AccF32{dZq, r}, dW, r, sigma, false, s));
-  HATA_TRY(gemm(kD, r, n, AccBf16T{k, kD}, AccF32{dZk, r}, dW, r, sigma, true, s));
+  HATA_TRY(gemm(kD, r, J, AccBf16T{q, kD}, AccF32{dZq, r}, dW, r, sigma, false, part, s));
+  HATA_TRY(gemm(kD, r, n, AccBf16T{k, kD}, AccF32{dZk, r}, dW, r, sigma, true, part, s));
   // decorrelation: gram = W^T W, WA = W (gram - I), dW += 2 lam / ||A|| * WA
-  HATA_TRY(gemm(r, r, kD, AccF32T{W, r}, AccF32{W, r}, gram, r, 1.f, false, s));
-  HATA_TRY(gemm(kD, r, r, AccF32{W, r}, AccGramMinusI{gram, r}, WA, r, 1.f, false, s));
-  hipLaunchKernelGGL(loss_kernel, dim3(1), dim3(256), 0, s, partq, J, partk, n, Cm, r, gram, eps, eta, lam, loss, fac);
-  hipLaunchKernelGGL(scale_add_wa_kernel, dim3((kD * r + 255) / 256), dim3(256), 0, s, dW, WA, fac, kD * r);
-  hipLaunchKernelGGL(update_kernel, dim3((kD * r + 255) / 256), dim3(256), 0, s, W, dW, grad, kD * r, lr);
+  HATA_TRY(gemm(r, r, kD, AccF32T{W, r}, AccF32{W, r}, gram, r, 1.f, false, part, s));
+  HATA_TRY(gemm(kD, r, r, AccF32{W, r}, AccGramMinusI{gram, r}, WA, r, 1.f, false, part, s));
+  hipLaunchKernelGGL(loss_kernel, dim3(1), dim3(kLossNT), 0, s, partq, J, partk, n, r, gram, eps, eta, lam, loss,
+                     fac);
+  hipLaunchKernelGGL(update_kernel, dim3((kD * r + 255) / 256), dim3(256), 0, s, W, (const float*)dW,
+                     (const float*)WA, (const float*)fac, grad, kD * r, lr);
   return hipGetLastError();
 #undef HATA_TRY
 }

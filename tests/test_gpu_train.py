@@ -72,15 +72,17 @@ def test_labels_gaussian_inputs_valid(hata_gpu):
             assert np.all(np.abs(sc[diff] - edge) <= 1e-4 * max(1.0, abs(edge)))
 
 
-@pytest.mark.parametrize("r", [64, 128, 256])
-def test_train_step_matches_oracle(hata_gpu, r):
-    J, n = 64, 1536
-    q, k, pos = _qk(J, n, 9300 + r)
-    rng = np.random.default_rng(9400 + r)
+@pytest.mark.parametrize("J,n,r", [(64, 1536, 64), (64, 1536, 128), (64, 1536, 256), (50, 1500, 128),
+                                   (200, 3001, 96)])
+def test_train_step_matches_oracle(hata_gpu, J, n, r):
+    """Ragged shapes cover partial output tiles, a short last k split and
+    the split-k partial sums (products over n with few output tiles)."""
+    q, k, pos = _qk(J, n, 9300 + r + J + n)
+    rng = np.random.default_rng(9400 + r + J + n)
     W0 = (rng.standard_normal((128, r)) / np.sqrt(128.0)).astype(np.float32)
     S = train.labels(q, k, pos)
     sigma, eps, eta, lam, lr = 1.5, 1e-3, 2e-4, 0.3, 0.02
-    _log(f"train step r={r}")
+    _log(f"train step J={J} n={n} r={r}")
     W = torch.from_numpy(W0.copy()).cuda()
     grad = torch.zeros_like(W)
     loss = torch.zeros(4, dtype=torch.float32, device="cuda")
