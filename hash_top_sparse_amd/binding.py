@@ -61,6 +61,7 @@ def load() -> ctypes.CDLL:
         "hata_hash_labels": ([P, P, P, I, I, I, I, F, F, P, P], I),
         "hata_hash_train_step": ([P, P, P, P, I, I, I, I, F, F, F, F, F, P, P, P, P, SZ, P], I),
         "hata_hash_train_workspace_bytes": ([I, I, I, I], SZ),
+        "hata_prefill": ([P, P, P, P, P, I, I, I, I, I, I64, I64, P, I64, F, P, P], I),
     }
     for name, (args, res) in sig.items():
         fn = getattr(L, name)
@@ -77,7 +78,7 @@ def exported_symbols() -> list[str]:
                         "hata_dense_decode",
                         "hata_workspace_bytes", "hata_workspace_reset", "hata_workspace_check",
                         "hata_stream_read", "hata_hash_labels", "hata_hash_train_step",
-                        "hata_hash_train_workspace_bytes")
+                        "hata_hash_train_workspace_bytes", "hata_prefill")
             if hasattr(load(), n)]
 
 
@@ -189,6 +190,24 @@ def dense_decode(q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, seq_lens: to
     _check(load().hata_dense_decode(_ptr(q), _ptr(K), _ptr(V), B, Hq, Hkv, d, cap, _ptr(seq_lens),
                                     int(max_len), float(scale), _ptr(out), _ptr(ws), ws.numel(),
                                     _stream(stream)))
+
+
+def prefill(q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, W_H: torch.Tensor, codes: torch.Tensor,
+            seq_lens: torch.Tensor, max_len: int, scale: float, out: torch.Tensor, stream=None) -> None:
+    """Causal prompt attention with the prompt keys' codes written to the cache.
+    q bf16 [B,Hq,q_rows,d]; K,V bf16 [B,Hkv,cap,d]; W_H f32 [Hkv,d,r]; codes int64
+    [B,Hkv,cap,ceil(r/64)]; seq_lens int32 [B]; out f32 [B,Hq,q_rows,d]."""
+    for t, n in ((q, "q"), (K, "K"), (V, "V")):
+        _need(t, torch.bfloat16, n)
+    _need(W_H, torch.float32, "W_H")
+    _need(codes, torch.int64, "codes")
+    _need(seq_lens, torch.int32, "seq_lens")
+    _need(out, torch.float32, "out")
+    B, Hq, q_rows, d = q.shape
+    _, Hkv, cap, _ = K.shape
+    r = W_H.shape[2]
+    _check(load().hata_prefill(_ptr(q), _ptr(K), _ptr(V), _ptr(W_H), _ptr(codes), B, Hq, Hkv, d, r, q_rows, cap,
+                               _ptr(seq_lens), int(max_len), float(scale), _ptr(out), _stream(stream)))
 
 
 def stream_read(src: torch.Tensor, sink: torch.Tensor, stream=None) -> None:

@@ -19,7 +19,7 @@ LIB = os.path.join(HERE, "libhata.so")
 ARCH = "gfx950"
 
 HIP_SOURCES = ["encode.hip", "encode_bulk.hip", "score_select.hip", "attention.hip",
-               "decode_step.hip", "stream_read.hip", "train.hip"]
+               "decode_step.hip", "stream_read.hip", "train.hip", "prefill.hip"]
 CPP_SOURCES = ["api.cpp"]
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", os.path.join(ROOT, "include"),

@@ -325,6 +325,35 @@ int hata_hash_labels(const void* q, const void* k, const int32_t* q_pos, int J, 
   return check_launch(e, "hash_labels launch");
 }
 
+int hata_prefill(const void* q, const void* K, const void* V, const float* W_H, uint64_t* codes, int B, int Hq,
+                 int Hkv, int d, int r, int64_t q_rows, int64_t cap, const int32_t* seq_lens, int64_t max_len,
+                 float scale, float* out, void* stream) {
+  if (!q || !K || !V || !W_H || !codes || !seq_lens || !out)
+    return fail(HATA_ERR_NULL, "prefill: q, K, V, W_H, codes, seq_lens and out are required");
+  int st = check_dims(d, r);
+  if (st) return st;
+  st = check_heads(B, Hq, Hkv);
+  if (st) return st;
+  st = check_len(cap, max_len);
+  if (st) return st;
+  if (q_rows < max_len)
+    return fail(HATA_ERR_SHAPE, "prefill: q_rows=%lld below max_len=%lld", (long long)q_rows, (long long)max_len);
+  if (!aligned(q, 16) || !aligned(K, 16) || !aligned(V, 16) || !aligned(out, 16))
+    return fail(HATA_ERR_ALIGN, "prefill: q, K, V and out must be 16-byte aligned");
+  if (!aligned(codes, 8) || !aligned(W_H, 4) || !aligned(seq_lens, 4))
+    return fail(HATA_ERR_ALIGN, "prefill: codes must be 8-byte, W_H and seq_lens 4-byte aligned");
+  const int G = Hq / Hkv;
+  const int64_t blocks = (max_len + hata::prefill_positions_per_block(G) - 1) / hata::prefill_positions_per_block(G);
+  if (blocks * B * Hkv > ((int64_t)1 << 31) - 1)
+    return fail(HATA_ERR_SHAPE, "prefill: grid of %lld workgroups too large", (long long)(blocks * B * Hkv));
+  st = pre_launch("prefill");
+  if (st) return st;
+  hipError_t e = hata::launch_prefill(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(K),
+                                      static_cast<const uint16_t*>(V), W_H, codes, B, Hq, Hkv, q_rows, cap, seq_lens,
+                                      (int)max_len, scale, out, r, reinterpret_cast<hipStream_t>(stream));
+  return check_launch(e, "prefill launch");
+}
+
 size_t hata_hash_train_workspace_bytes(int J, int n, int d, int r) {
   if (J < 1 || n < 1 || d != 128 || r < 32 || r > 256 || r % 32 != 0) return 0;
   return hata::plan_train(J, n, r).total;

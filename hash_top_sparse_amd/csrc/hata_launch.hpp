@@ -55,6 +55,18 @@ hipError_t launch_decode_step(const StepPlan& p, const uint16_t* q, const uint16
 
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s);
 
+// ---------------------------------------------------------------- prefill
+// Causal attention over each sequence's prompt (queries [B][Hq][q_rows][128]
+// at positions 0..n_b-1, keys/values [B][Hkv][cap][128]) into out fp32
+// [B][Hq][q_rows][128], with code rows 0..n_b-1 written to codes
+// [B][Hkv][cap][r/64 rounded up]; n_b = min(seq_lens[b], max_len).
+// G = Hq / Hkv in {1, 2, 4, 8}, r in {32, 64, 128, 256}.
+int prefill_positions_per_block(int G);
+hipError_t launch_prefill(const uint16_t* q, const uint16_t* K, const uint16_t* V, const float* W,
+                          uint64_t* codes, int B, int Hq, int Hkv, int64_t q_rows, int64_t cap,
+                          const int32_t* seq_lens, int max_len, float scale, float* out, int r,
+                          hipStream_t s);
+
 // training step of the hash weights (train.hip)
 constexpr int kMaxLabelKeys = 8192;  // keys a label row may rank (LDS sort)
 struct TrainPlan {

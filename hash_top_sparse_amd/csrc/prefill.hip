@@ -1,0 +1,348 @@
+// prefill.hip -- causal prefill attention on the matrix cores, with the key
+// codes formed while each key tile sits in LDS.
+//
+// HATA notes, section "Method", "Overall framework", second stage: during
+// prefill, attention is computed as usual while the keys are encoded into
+// binary hash codes and cached; section "Key findings": the encode adds
+// under one percent to prefill compute because r is far below the sequence
+// length.  Here the encode reuses the key tile that the attention has
+// already staged in LDS, so the keys are read from HBM once for both.
+//
+// Work split: one workgroup per (sequence, KV head, block of 128 query rows)
+// where the 128 rows are the G query heads of the KV head times 128/G
+// positions, so the G heads share every staged K/V tile.  Wave w owns 32
+// (head, position) pairs.  Per 64-key tile:
+//   S^T = K Q^T   v_mfma_f32_32x32x16_bf16, A = K rows from LDS, B = this
+//                 wave's queries (registers); a lane's accumulators all
+//                 belong to one query (lane % 32), half its keys each in
+//                 lanes l and l ^ 32
+//   online softmax in the log2 domain (scale * log2 e folded into the
+//                 logits), row max / sum over the lane pair
+//   O^T += V^T P^T  A = V^T from a transposed LDS copy, B = P rounded to
+//                 bf16 straight from the S^T accumulators; the MFMA's k
+//                 index runs over the keys in the order the accumulators
+//                 hold them (any order gives the same contraction as long as
+//                 A and B agree)
+// The workgroup also encodes its own rows [p0, p0 + 128/G): when a tile
+// holding some of them is staged, each wave multiplies the 32-row halves of
+// the tile by 32-column slices of W_H split exactly into three bf16 terms
+// (every product exact, fp32 accumulation), takes the sign with ballots and
+// collects the 32-bit code words in LDS; the rows go to the cache at the end.
+//
+// Blocks are issued heaviest first (the causal work grows with the position)
+// and (sequence, KV head) varies fastest, so with B * Hkv a multiple of 8
+// each XCD serves whole heads and their K/V stay in its L2.
+#include "hata_device.hpp"
+#include "hata_launch.hpp"
+
+namespace hata {
+
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int kBK = 64;              // keys per staged tile
+constexpr int kKsStride = kD + 8;    // bf16 per staged key row (272 bytes)
+constexpr int kVtStride = kBK + 4;   // bf16 per transposed value row (136 bytes)
+
+struct PrefillArgs {
+  const uint16_t* q;
+  const uint16_t* K;
+  const uint16_t* V;
+  const float* W;
+  uint64_t* codes;
+  const int32_t* seq_lens;
+  float* out;
+  int B, Hq, Hkv;
+  int64_t q_rows, cap;
+  int max_len, nqb;
+  float scale_log2;
+};
+
+__device__ __forceinline__ uint32_t half16(const uint4& v, int e) {
+  const uint32_t w = e < 2 ? v.x : e < 4 ? v.y : e < 6 ? v.z : v.w;
+  return (e & 1) ? (w >> 16) : (w & 0xFFFFu);
+}
+
+template <int G, int R>
+__global__ __launch_bounds__(kNT, 2) void prefill_kernel(PrefillArgs a) {
+  constexpr int QP = 128 / G;         // positions per workgroup
+  constexpr int W64 = Width<R>::W64;  // 64-bit words per code row
+  constexpr int CT = R / 32;          // 32-column slices of the code
+  __shared__ __align__(16) uint16_t ks[kBK * kKsStride];
+  __shared__ __align__(16) uint16_t vt[kD * kVtStride];
+  __shared__ uint32_t cw[QP * CT];
+
+  const int t = threadIdx.x, lane = t & 63, half = lane >> 5;
+  const int wv = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int heads = a.B * a.Hkv;
+  const int bh = blockIdx.x % heads;
+  const int qb = a.nqb - 1 - (int)(blockIdx.x / heads);
+  const int b = bh / a.Hkv, hk = bh - b * a.Hkv;
+  const int p0 = qb * QP;
+  const int L = min(max(a.seq_lens[b], 0), a.max_len);
+  if (p0 >= L) return;
+  const int pend = min(p0 + QP, L);
+  const int ntiles = (pend + kBK - 1) / kBK;
+
+  // this lane's query: pair 32 wv + lane % 32 -> (head, position)
+  const int pair = 32 * wv + (lane & 31);
+  const int hq = hk * G + pair / QP;
+  const int pos = p0 + pair % QP;
+  const bool qvalid = pos < L;
+  const int wpos_min = p0 + (32 * wv) % QP;
+  const int wpos_max = min(wpos_min + (QP < 32 ? QP : 32) - 1, L - 1);
+  const bool wactive = wpos_min < L;
+
+  bf16x8 qf[8];
+  {
+    const uint16_t* qrow = a.q + (((int64_t)b * a.Hq + hq) * a.q_rows + (qvalid ? pos : 0)) * kD;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      uint4 v = make_uint4(0, 0, 0, 0);
+      if (qvalid) v = *reinterpret_cast<const uint4*>(qrow + 16 * s + 8 * half);
+      qf[s] = __builtin_bit_cast(bf16x8, v);
+    }
+  }
+
+  const int64_t kvoff = ((int64_t)b * a.Hkv + hk) * a.cap * kD;
+  const uint16_t* Kh = a.K + kvoff;
+  const uint16_t* Vh = a.V + kvoff;
+  uint4 kreg[4], vreg[4];
+  const int vkg = t >> 4, vc = t & 15;  // value rows 4 vkg .. 4 vkg + 3, columns 8 vc ..
+  auto fetch = [&](int tile) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int id = t + kNT * i, key = id >> 4, c = id & 15;
+      const int row = tile * kBK + key;
+      kreg[i] = row < L ? *reinterpret_cast<const uint4*>(Kh + (int64_t)row * kD + c * 8) : make_uint4(0, 0, 0, 0);
+      const int vrow = tile * kBK + 4 * vkg + i;
+      vreg[i] = vrow < L ? *reinterpret_cast<const uint4*>(Vh + (int64_t)vrow * kD + vc * 8) : make_uint4(0, 0, 0, 0);
+    }
+  };
+
+  float m_run = -INFINITY, l_run = 0.f;
+  f32x16 o[4];
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) o[dt][i] = 0.f;
+
+  const float* Wh = a.W + (int64_t)hk * kD * R;
+
+  fetch(0);
+  for (int tile = 0; tile < ntiles; ++tile) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int id = t + kNT * i, key = id >> 4, c = id & 15;
+      *reinterpret_cast<uint4*>(ks + key * kKsStride + c * 8) = kreg[i];
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const uint32_t lo = half16(vreg[0], e) | (half16(vreg[1], e) << 16);
+      const uint32_t hi = half16(vreg[2], e) | (half16(vreg[3], e) << 16);
+      *reinterpret_cast<uint2*>(vt + (vc * 8 + e) * kVtStride + 4 * vkg) = make_uint2(lo, hi);
+    }
+    __syncthreads();
+    if (tile + 1 < ntiles) fetch(tile + 1);
+    const int k0 = tile * kBK;
+
+    if (wactive && k0 <= wpos_max) {
+      const bool act1 = k0 + 32 <= wpos_max;
+      f32x16 s[2];
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) s[st][i] = 0.f;
+        if (st == 1 && !act1) continue;
+        const uint16_t* krow = ks + (32 * st + (lane & 31)) * kKsStride + 8 * half;
+#pragma unroll
+        for (int kk = 0; kk < 8; ++kk) {
+          const bf16x8 af = *reinterpret_cast<const bf16x8*>(krow + 16 * kk);
+          s[st] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, qf[kk], s[st], 0, 0, 0);
+        }
+      }
+      // scale, causal mask, running max
+      const bool need_mask = k0 + kBK - 1 > wpos_min;
+      float mx = -INFINITY;
+#pragma unroll
+      for (int st = 0; st < 2; ++st)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int key = k0 + 32 * st + 8 * (i >> 2) + (i & 3) + 4 * half;
+          float v = s[st][i] * a.scale_log2;
+          if ((st == 1 && !act1) || (need_mask && key > pos)) v = -INFINITY;
+          s[st][i] = v;
+          mx = fmaxf(mx, v);
+        }
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float m_new = fmaxf(m_run, mx);
+      const float mref = m_new == -INFINITY ? 0.f : m_new;
+      const float alpha = __builtin_amdgcn_exp2f(m_run - mref);
+      float psum = 0.f;
+#pragma unroll
+      for (int st = 0; st < 2; ++st)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const float p = __builtin_amdgcn_exp2f(s[st][i] - mref);
+          s[st][i] = p;
+          psum += p;
+        }
+      l_run = l_run * alpha + psum;
+      m_run = m_new;
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) o[dt][i] *= alpha;
+      // O^T += V^T P^T over the active 32-key halves, 16 keys per MFMA
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
+        if (st == 1 && !act1) continue;
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+          bf16x8 pf;
+#pragma unroll
+          for (int j = 0; j < 8; ++j) pf[j] = (__bf16)s[st][8 * kk + j];
+          const int key0 = 32 * st + 16 * kk + 4 * half;
+#pragma unroll
+          for (int dt = 0; dt < 4; ++dt) {
+            const uint16_t* vrow = vt + (32 * dt + (lane & 31)) * kVtStride + key0;
+            const uint2 x0 = *reinterpret_cast<const uint2*>(vrow);
+            const uint2 x1 = *reinterpret_cast<const uint2*>(vrow + 8);
+            const bf16x8 vf = __builtin_bit_cast(bf16x8, make_uint4(x0.x, x0.y, x1.x, x1.y));
+            o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf, o[dt], 0, 0, 0);
+          }
+        }
+      }
+    }
+
+    __syncthreads();
+  }
+
+  // normalise and store this lane's query row: accumulator i of slice dt
+  // holds column 32 dt + 8 (i/4) + i%4 + 4 half
+  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  if (qvalid) {
+    const float inv = 1.f / l_tot;
+    float* orow = a.out + (((int64_t)b * a.Hq + hq) * a.q_rows + pos) * kD;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const float4 v = make_float4(o[dt][4 * g] * inv, o[dt][4 * g + 1] * inv, o[dt][4 * g + 2] * inv,
+                                     o[dt][4 * g + 3] * inv);
+        *reinterpret_cast<float4*>(orow + 32 * dt + 8 * g + 4 * half) = v;
+      }
+  }
+  // encode this workgroup's own rows [p0, pend).  They lie in the last
+  // staged tile, still in LDS, except for G = 1 (128 positions, two tiles),
+  // where both tiles are staged again (from L2: they were read a moment
+  // ago).  Done after the output store so the attention registers are free.
+  const bool restage = ntiles - 1 != p0 / kBK;
+  for (int tile = p0 / kBK; tile < ntiles; ++tile) {
+    const int k0 = tile * kBK;
+    if (restage) {
+      __syncthreads();
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int id = t + kNT * i, key = id >> 4, c = id & 15;
+        const int row = k0 + key;
+        const uint4 v = row < L ? *reinterpret_cast<const uint4*>(Kh + (int64_t)row * kD + c * 8)
+                                : make_uint4(0, 0, 0, 0);
+        *reinterpret_cast<uint4*>(ks + key * kKsStride + c * 8) = v;
+      }
+      __syncthreads();
+    }
+    {
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
+        const int r0 = k0 + 32 * st;
+        if (r0 >= pend || r0 + 31 < p0) continue;
+        const uint16_t* krow = ks + (32 * st + (lane & 31)) * kKsStride + 8 * half;
+        for (int ct = wv; ct < CT; ct += 4) {
+          f32x16 e;
+#pragma unroll
+          for (int i = 0; i < 16; ++i) e[i] = 0.f;
+#pragma unroll 1
+          for (int kk = 0; kk < 8; ++kk) {
+            bf16x8 w1, w2, w3;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+              const float v = Wh[(16 * kk + 8 * half + j) * R + 32 * ct + (lane & 31)];
+              const __bf16 a1 = (__bf16)v;
+              const float r1 = v - (float)a1;
+              const __bf16 a2 = (__bf16)r1;
+              w1[j] = a1;
+              w2[j] = a2;
+              w3[j] = (__bf16)(r1 - (float)a2);
+            }
+            const bf16x8 af = *reinterpret_cast<const bf16x8*>(krow + 16 * kk);
+            e = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, w1, e, 0, 0, 0);
+            e = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, w2, e, 0, 0, 0);
+            e = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, w3, e, 0, 0, 0);
+          }
+          // element i: lanes 0-31 hold row 8 (i/4) + i%4, lanes 32-63 the
+          // row 4 below, at columns 32 ct + lane % 32
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const uint64_t m = __ballot(e[i] >= 0.0f);
+            if (lane == 0) {
+              const int key = r0 + 8 * (i >> 2) + (i & 3);
+              if (key >= p0 && key < pend) cw[(key - p0) * CT + ct] = (uint32_t)m;
+              if (key + 4 >= p0 && key + 4 < pend) cw[(key + 4 - p0) * CT + ct] = (uint32_t)(m >> 32);
+            }
+          }
+        }
+      }
+    }
+  }
+  __syncthreads();
+
+  // code rows [p0, pend)
+  uint64_t* crow = a.codes + (((int64_t)b * a.Hkv + hk) * a.cap + p0) * W64;
+  for (int e = t; e < (pend - p0) * W64; e += kNT) {
+    const int row = e / W64, w = e - row * W64;
+    const uint64_t lo = cw[row * CT + 2 * w];
+    const uint64_t hi = (2 * w + 1 < CT) ? cw[row * CT + 2 * w + 1] : 0u;
+    crow[e] = lo | (hi << 32);
+  }
+}
+
+template <int G>
+hipError_t launch_g(const PrefillArgs& a, int r, hipStream_t s) {
+  const dim3 grid((unsigned)((int64_t)a.nqb * a.B * a.Hkv));
+  switch (r) {
+    case 32: hipLaunchKernelGGL((prefill_kernel<G, 32>), grid, dim3(kNT), 0, s, a); break;
+    case 64: hipLaunchKernelGGL((prefill_kernel<G, 64>), grid, dim3(kNT), 0, s, a); break;
+    case 128: hipLaunchKernelGGL((prefill_kernel<G, 128>), grid, dim3(kNT), 0, s, a); break;
+    case 256: hipLaunchKernelGGL((prefill_kernel<G, 256>), grid, dim3(kNT), 0, s, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+int prefill_positions_per_block(int G) { return 128 / G; }
+
+hipError_t launch_prefill(const uint16_t* q, const uint16_t* K, const uint16_t* V, const float* W,
+                          uint64_t* codes, int B, int Hq, int Hkv, int64_t q_rows, int64_t cap,
+                          const int32_t* seq_lens, int max_len, float scale, float* out, int r,
+                          hipStream_t s) {
+  const int G = Hq / Hkv;
+  PrefillArgs a;
+  a.q = q; a.K = K; a.V = V; a.W = W; a.codes = codes; a.seq_lens = seq_lens; a.out = out;
+  a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.q_rows = q_rows; a.cap = cap; a.max_len = max_len;
+  a.nqb = (max_len + 128 / G - 1) / (128 / G);
+  a.scale_log2 = scale * 1.4426950408889634f;
+  switch (G) {
+    case 1: return launch_g<1>(a, r, s);
+    case 2: return launch_g<2>(a, r, s);
+    case 4: return launch_g<4>(a, r, s);
+    case 8: return launch_g<8>(a, r, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace hata

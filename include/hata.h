@@ -190,6 +190,34 @@ int hata_decode_step_qk(const void* q, const void* K, const void* V,
                         size_t ws_bytes, void* stream);
 
 /*
+ * Prefill of a prompt (HATA notes, "Method", "Overall framework", second
+ * stage: attention computed as usual while the keys are encoded and the
+ * codes cached).  For every sequence b with n_b = min(seq_lens[b], max_len)
+ * prompt tokens at positions 0..n_b-1:
+ *   out[b][h][i] = sum_{j <= i} softmax_j(scale * q[b][h][i] . K[b][h/G][j])
+ *                  * V[b][h/G][j]          (causal, fp32 result)
+ *   codes[b][g][j] = HashEncode(K[b][g][j], W_H[g]) for j < n_b
+ * (the same codes as hata_encode_append), formed from the key tiles the
+ * attention has staged, so the prompt keys are read from HBM once.
+ * Layouts (device memory): q bf16 [B][Hq][q_rows][d]; K, V bf16
+ * [B][Hkv][cap][d] (rows 0..n_b-1 hold the prompt); W_H fp32 [Hkv][d][r];
+ * codes uint64 [B][Hkv][cap][ceil(r/64)]; seq_lens int32 [B]; out fp32
+ * [B][Hq][q_rows][d].  Rows at positions >= n_b of out and codes are left
+ * as they are.  The weights of the value product are rounded to bf16 (as
+ * flash attention does); the scores, the softmax statistics and all
+ * accumulation are fp32.  d = 128; r in {32, 64, 128, 256}; G = Hq / Hkv in
+ * {1, 2, 4, 8}; 1 <= max_len <= min(q_rows, cap); q, K, V, out 16-byte
+ * aligned, codes 8-byte aligned.  No workspace.  Errors: HATA_ERR_NULL,
+ * _SHAPE, _UNSUPPORTED, _ALIGN as for the decode step, HATA_ERR_HIP on a
+ * launch failure.
+ */
+int hata_prefill(const void* q, const void* K, const void* V,
+                 const float* W_H, uint64_t* codes, int B, int Hq, int Hkv,
+                 int d, int r, int64_t q_rows, int64_t cap,
+                 const int32_t* seq_lens, int64_t max_len, float scale,
+                 float* out, void* stream);
+
+/*
  * Dense flash-decode baseline over all n_b rows of every unit (the same
  * attention with the kept set = every token), same layouts.
  * ws: hata_workspace_bytes(HATA_OP_DENSE_DECODE, ...).

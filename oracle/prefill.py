@@ -85,6 +85,29 @@ def abs_weighted_values(q_bits, K_bits, V_bits, seq_lens, scale=None) -> np.ndar
     return out
 
 
+def attention_rows(q_rows_bits, positions, K_bits, V_bits, scale=None, with_abs=False):
+    """Single rows of the same attention: query row m (bf16 bits [d]) at
+    position positions[m] attends keys 0..positions[m] of K, V [n, d] (one
+    KV head).  For sampled checks of long prompts.  with_abs also returns the
+    weights applied to |V| (as abs_weighted_values)."""
+    d = K_bits.shape[1]
+    scale = 1.0 / np.sqrt(d) if scale is None else float(scale)
+    out = np.zeros((len(positions), d))
+    absw = np.zeros((len(positions), d))
+    for m, i in enumerate(positions):
+        i = int(i)
+        Q = _f64(q_rows_bits[m])
+        Kh = _f64(K_bits[:i + 1])
+        logits = (Kh @ Q) * scale
+        logits -= logits.max()
+        p = np.exp(logits)
+        p /= p.sum()
+        Vh = _f64(V_bits[:i + 1])
+        out[m] = p @ Vh
+        absw[m] = p @ np.abs(Vh)
+    return (out, absw) if with_abs else out
+
+
 def prefill(q_bits, K_bits, V_bits, W, seq_lens, scale=None):
     """Attention output (fp64) and the code cache rows 0..L-1 of every
     (sequence, KV head), as oracle.build_cache lays them out."""

@@ -197,6 +197,32 @@ def test_hash_train_step_validation(lib):
     assert call(ws_bytes=need - 1) == EWS
 
 
+def _prefill(**kw):
+    a = dict(q=A, K=A, V=A, W=A, codes=A, B=1, Hq=32, Hkv=8, d=128, r=128, q_rows=4096, cap=4096, seq=A,
+             max_len=4096, out=A)
+    a.update(kw)
+    return binding.raw_call("hata_prefill", a["q"], a["K"], a["V"], a["W"], a["codes"], a["B"], a["Hq"],
+                            a["Hkv"], a["d"], a["r"], ctypes.c_int64(a["q_rows"]), ctypes.c_int64(a["cap"]),
+                            a["seq"], ctypes.c_int64(a["max_len"]), F(0.088), a["out"], None)
+
+
+def test_prefill_validation():
+    assert _prefill(q=None) == ENULL
+    assert _prefill(codes=None) == ENULL
+    assert _prefill(seq=None) == ENULL
+    assert _prefill(out=None) == ENULL
+    assert _prefill(d=64) == EUNSUP
+    assert _prefill(r=96) == EUNSUP
+    assert _prefill(Hq=48, Hkv=4) == EUNSUP      # G = 12
+    assert _prefill(Hq=30, Hkv=8) == ESHAPE      # not a multiple
+    assert _prefill(max_len=4097) == ESHAPE      # beyond cap
+    assert _prefill(q_rows=4095) == ESHAPE       # queries shorter than max_len
+    assert _prefill(max_len=0) == ESHAPE
+    assert _prefill(q=MIS) == EALIGN
+    assert _prefill(out=MIS) == EALIGN
+    assert _prefill(codes=MIS2) == EALIGN
+
+
 def lib_stream_read_valid():
     return binding.load().hata_stream_read(A, ctypes.c_size_t(4096), A, ctypes.c_size_t(1024), P(None))
 
@@ -221,6 +247,7 @@ def test_forced_launch_failure_propagates():
         assert _topk() == EHIP
         assert _enc() == EHIP
         assert lib_stream_read_valid() == EHIP
+        assert _prefill() == EHIP
         with pytest.raises(binding.HataError) as ei:
             binding._check(_ham())
         assert ei.value.status == EHIP

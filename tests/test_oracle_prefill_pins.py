@@ -97,3 +97,12 @@ def test_prefill_codes_are_the_encoded_keys():
     for h in range(Hkv):
         np.testing.assert_array_equal(codes[0, h, :13], oracle.encode(K[0, h, :13], W[h]))
     assert not codes[0, :, 13:].any()
+
+
+def test_attention_rows_match_full_prefill_rows():
+    B, Hq, Hkv, S, d = 1, 2, 1, 50, 16
+    q, K, V = _gauss((B, Hq, S, d)), _gauss((B, Hkv, S, d)), _gauss((B, Hkv, S, d))
+    full = prefill.causal_attention(q, K, V, [S])
+    pos = [0, 1, 17, 49]
+    rows = prefill.attention_rows(q[0, 1, pos], pos, K[0, 0], V[0, 0])
+    np.testing.assert_allclose(rows, full[0, 1, pos], rtol=1e-12, atol=1e-14)
