@@ -390,6 +390,60 @@ def model_sweep(layers: int = 32, ctxs=(32768, 65536, 131072), reps: int = 10) -
     return res
 
 
+def prefill_bench(N: int = 32768, B: int = 1, Hq: int = 32, Hkv: int = 8, r: int = 128, reps: int = 5) -> dict:
+    """Time hata_prefill on one Llama-3.1-8B-shaped layer (bf16 N(0,1) q/K/V
+    and fp32 N(0, 1/128) W_H drawn on the device; parity is in the tests):
+    causal attention over an N-token prompt with the prompt keys' codes
+    written to the cache.  Algorithmic work: 4 d per visible (query, key)
+    pair and query head (the two products), i.e. 2 d Hq N (N + 1) flops, plus
+    the encode.  Beside it, the separate bulk encode of the same keys
+    (hata_encode_append), the pass that the fused encode replaces."""
+    import torch
+
+    from hash_top_sparse_amd import binding
+
+    dev = torch.device("cuda:0")
+    g = torch.Generator(device=dev)
+    g.manual_seed(7300)
+    q = torch.randn((B, Hq, N, 128), generator=g, device=dev).to(torch.bfloat16)
+    K = torch.randn((B, Hkv, N, 128), generator=g, device=dev).to(torch.bfloat16)
+    V = torch.randn((B, Hkv, N, 128), generator=g, device=dev).to(torch.bfloat16)
+    W = torch.randn((Hkv, 128, r), generator=g, device=dev) / np.sqrt(128.0)
+    out = torch.empty((B, Hq, N, 128), dtype=torch.float32, device=dev)
+    codes = torch.zeros((B, Hkv, N, (r + 63) // 64), dtype=torch.int64, device=dev)
+    seq = torch.full((B,), N, dtype=torch.int32, device=dev)
+    scale = 1.0 / np.sqrt(128.0)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    binding.prefill(q, K, V, W, codes, seq, N, scale, out)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        binding.prefill(q, K, V, W, codes, seq, N, scale, out)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    binding.encode_append(K, W, codes, n_new=N)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        binding.encode_append(K, W, codes, n_new=N)
+    e1.record()
+    torch.cuda.synchronize()
+    enc_ms = e0.elapsed_time(e1) / reps
+    flops = 2.0 * 128 * Hq * B * N * (N + 1)
+    enc_flops = 2.0 * 128 * r * B * Hkv * N
+    tf = (flops + enc_flops) / (ms * 1e-3) / 1e12
+    log(f"prefill {N} tokens x {Hq}/{Hkv} heads: {ms:.2f} ms ({tf:.0f} TFLOP/s, {tf / 2500:.1%} of bf16 peak); "
+        f"separate bulk encode of the keys {enc_ms * 1e3:.0f} us")
+    del q, K, V, out
+    torch.cuda.empty_cache()
+    return {"workload": f"Llama-3.1-8B-shaped layer prefill, B={B}, {Hq}/{Hkv} heads, d=128, r={r}",
+            "tokens": B * N, "ms": ms, "tokens_per_s": B * N / (ms * 1e-3),
+            "flops": flops + enc_flops, "TFLOPs": tf, "peak_TFLOPs": 2500.0, "frac_of_peak": tf / 2500.0,
+            "encode_flops_share": enc_flops / (flops + enc_flops),
+            "separate_bulk_encode_ms": enc_ms}
+
+
 def train_bench(J: int = 512, n: int = 8192, r: int = 128, steps: int = 20) -> dict:
     """Time the hash-weight training step for one head (synthetic bf16 N(0,1)
     Q/K drawn on the device, J sampled queries at random positions of an
@@ -450,6 +504,7 @@ def main() -> int:
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="launch the timed steps eagerly")
     ap.add_argument("--sweep", action="store_true", help="also time the other workloads (2, 3, 5)")
+    ap.add_argument("--no-prefill", action="store_true", help="skip the 32K-token prefill measurement")
     ap.add_argument("--train", action="store_true",
                     help="also time the hash-weight training step (labels + one gradient step, one head)")
     ap.add_argument("--width-sweep", action="store_true",
@@ -508,6 +563,7 @@ def main() -> int:
             wsweep[str(r)] = {"ms_per_step": rr["ms_per_step"], "steps_per_s": rr["steps_per_s"],
                               "GBs": rr["GBs"], "frac_of_peak": rr["frac_of_peak"],
                               "bytes_per_step": rr["bytes_per_step"], "stored_bytes_per_step": layout}
+    pbench = None if args.no_prefill else prefill_bench()
     msweep = model_sweep() if args.model_sweep else None
     tbench = train_bench() if args.train else None
     peak_meas = read_peak()
@@ -557,6 +613,8 @@ def main() -> int:
         res["code_widths"] = wsweep
     if tbench is not None:
         res["hash_train"] = tbench
+    if pbench is not None:
+        res["prefill"] = pbench
     print(json.dumps(res), flush=True)
     return 0
 

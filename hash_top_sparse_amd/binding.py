@@ -24,6 +24,7 @@ OP_TOPK = 1
 OP_SPARSE_DECODE = 2
 OP_DECODE_STEP = 3
 OP_DENSE_DECODE = 4
+OP_DECODE_STEP_PAGED = 5
 
 _lib = None
 
@@ -62,6 +63,7 @@ def load() -> ctypes.CDLL:
         "hata_hash_train_step": ([P, P, P, P, I, I, I, I, F, F, F, F, F, P, P, P, P, SZ, P], I),
         "hata_hash_train_workspace_bytes": ([I, I, I, I], SZ),
         "hata_prefill": ([P, P, P, P, P, I, I, I, I, I, I64, I64, P, I64, F, P, P], I),
+        "hata_decode_step_paged": ([P, P, P, P, P, P, I, I, I, I, I, I, I, I, P, I64, I, F, P, P, P, SZ, P], I),
     }
     for name, (args, res) in sig.items():
         fn = getattr(L, name)
@@ -78,7 +80,7 @@ def exported_symbols() -> list[str]:
                         "hata_dense_decode",
                         "hata_workspace_bytes", "hata_workspace_reset", "hata_workspace_check",
                         "hata_stream_read", "hata_hash_labels", "hata_hash_train_step",
-                        "hata_hash_train_workspace_bytes", "hata_prefill")
+                        "hata_hash_train_workspace_bytes", "hata_prefill", "hata_decode_step_paged")
             if hasattr(load(), n)]
 
 
@@ -208,6 +210,30 @@ def prefill(q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, W_H: torch.Tensor
     r = W_H.shape[2]
     _check(load().hata_prefill(_ptr(q), _ptr(K), _ptr(V), _ptr(W_H), _ptr(codes), B, Hq, Hkv, d, r, q_rows, cap,
                                _ptr(seq_lens), int(max_len), float(scale), _ptr(out), _stream(stream)))
+
+
+def decode_step_paged(q: torch.Tensor, K_pool: torch.Tensor, V_pool: torch.Tensor, W_H: torch.Tensor,
+                      code_pool: torch.Tensor, block_table: torch.Tensor, seq_lens: torch.Tensor, max_len: int,
+                      k: int, scale: float, out: torch.Tensor, ws: torch.Tensor, idx_out: torch.Tensor | None = None,
+                      stream=None) -> None:
+    """q bf16 [B,Hq,d]; K_pool, V_pool bf16 [pages,Hkv,P,d]; code_pool int64 [pages,Hkv,P,ceil(r/64)];
+    block_table int32 [B,max_pages]; out f32 [B,Hq,d]; idx_out int32 [B,Hkv,k] or None."""
+    for t, n in ((q, "q"), (K_pool, "K_pool"), (V_pool, "V_pool")):
+        _need(t, torch.bfloat16, n)
+    _need(W_H, torch.float32, "W_H")
+    _need(code_pool, torch.int64, "code_pool")
+    _need(block_table, torch.int32, "block_table")
+    _need(seq_lens, torch.int32, "seq_lens")
+    _need(out, torch.float32, "out")
+    if idx_out is not None:
+        _need(idx_out, torch.int32, "idx_out")
+    B, Hq, d = q.shape
+    num_pages, Hkv, P, _ = K_pool.shape
+    r = W_H.shape[2]
+    _check(load().hata_decode_step_paged(_ptr(q), _ptr(K_pool), _ptr(V_pool), _ptr(W_H), _ptr(code_pool),
+                                         _ptr(block_table), block_table.shape[1], num_pages, P, B, Hq, Hkv, d, r,
+                                         _ptr(seq_lens), int(max_len), int(k), float(scale), _ptr(out),
+                                         _ptr(idx_out), _ptr(ws), ws.numel(), _stream(stream)))
 
 
 def stream_read(src: torch.Tensor, sink: torch.Tensor, stream=None) -> None:

@@ -290,6 +290,79 @@ static int decode_step_impl(const void* q, const void* K, const void* V, const f
   return check_launch(e, "decode_step (staged) launch");
 }
 
+namespace {
+// workspace of the paged step: query codes, scores, kept indices, attention records
+struct PagedPlan {
+  size_t qc = 0, sc = 0, idx = 0, attn = 0, total = 0;
+};
+PagedPlan plan_paged(int B, int Hq, int Hkv, int64_t max_len, int k, int r) {
+  auto al = [](size_t x) { return (x + 255) / 256 * 256; };
+  PagedPlan p;
+  const size_t U = (size_t)B * Hkv;
+  size_t off = 0;
+  p.qc = off;   off = al(off + (size_t)B * Hq * ((r + 63) / 64) * 8);
+  p.sc = off;   off = al(off + U * (size_t)max_len * 2);
+  p.idx = off;  off = al(off + U * (size_t)k * 4);
+  p.attn = off; off = al(off + hata::attn_part_floats(B, Hkv, Hq / Hkv, k) * 4);
+  p.total = off;
+  return p;
+}
+}  // namespace
+
+int hata_decode_step_paged(const void* q, const void* K_pool, const void* V_pool, const float* W_H,
+                           uint64_t* code_pool, const int32_t* block_table, int max_pages, int num_pages,
+                           int page_rows, int B, int Hq, int Hkv, int d, int r, const int32_t* seq_lens,
+                           int64_t max_len, int k, float scale, float* out, int32_t* idx_out, void* ws,
+                           size_t ws_bytes, void* stream) {
+  if (!q || !K_pool || !V_pool || !W_H || !code_pool || !block_table || !seq_lens || !out)
+    return fail(HATA_ERR_NULL, "decode_step_paged: null pointer");
+  int st = check_dims(d, r);
+  if (st) return st;
+  if ((st = check_heads(B, Hq, Hkv))) return st;
+  if ((st = check_k(k))) return st;
+  if (page_rows < 16 || page_rows > 65536 || (page_rows & (page_rows - 1)) != 0)
+    return fail(HATA_ERR_UNSUPPORTED, "decode_step_paged: page_rows=%d not a power of two in [16, 65536]",
+                page_rows);
+  if (max_pages < 1 || num_pages < 1)
+    return fail(HATA_ERR_SHAPE, "decode_step_paged: max_pages=%d, num_pages=%d must be >= 1", max_pages, num_pages);
+  const int64_t cap = (int64_t)max_pages * page_rows;
+  if ((st = check_len(cap, max_len))) return st;
+  if (!aligned(code_pool, 16) || !aligned(q, 16) || !aligned(K_pool, 16) || !aligned(V_pool, 16))
+    return fail(HATA_ERR_ALIGN, "decode_step_paged: q, K_pool, V_pool and code_pool must be 16-byte aligned");
+  if (!aligned(block_table, 4)) return fail(HATA_ERR_ALIGN, "decode_step_paged: block_table must be 4-byte aligned");
+  const PagedPlan p = plan_paged(B, Hq, Hkv, max_len, k, r);
+  if (!ws || ws_bytes < p.total)
+    return fail(HATA_ERR_WORKSPACE, "decode_step_paged: workspace of %zu bytes needed, %zu given", p.total,
+                ws_bytes);
+  if ((st = pre_launch("decode_step_paged"))) return st;
+  hata::PageMap pm;
+  pm.bt = block_table;
+  pm.max_pages = max_pages;
+  pm.num_pages = num_pages;
+  int lg = 0;
+  while ((1 << lg) < page_rows) ++lg;
+  pm.log2P = lg;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  auto* wsb = static_cast<unsigned char*>(ws);
+  const auto* qb = static_cast<const uint16_t*>(q);
+  const auto* Kb = static_cast<const uint16_t*>(K_pool);
+  const auto* Vb = static_cast<const uint16_t*>(V_pool);
+  const int G = Hq / Hkv;
+  auto* qc = reinterpret_cast<uint64_t*>(wsb + p.qc);
+  auto* sc = reinterpret_cast<uint16_t*>(wsb + p.sc);
+  int32_t* idx = idx_out ? idx_out : reinterpret_cast<int32_t*>(wsb + p.idx);
+  auto* part = reinterpret_cast<float*>(wsb + p.attn);
+  hipError_t e = hata::launch_encode_rows(qb, 1, B, Hq, Hkv, 1, W_H, qc, 1, nullptr, 0, s, r);
+  if (e == hipSuccess)  // key append at logical row seq_lens[b] - 1, through the page table
+    e = hata::launch_encode_rows(Kb, cap, B, Hkv, Hkv, 1, W_H, code_pool, cap, seq_lens, -1, s, r, &pm);
+  if (e == hipSuccess)
+    e = hata::launch_hamming(qc, code_pool, B, Hq, Hkv, cap, seq_lens, max_len, sc, max_len, s, r, &pm);
+  if (e == hipSuccess) e = hata::launch_topk(sc, max_len, B, Hkv, cap, seq_lens, k, G * r, idx, s);
+  if (e == hipSuccess)
+    e = hata::launch_attention(qb, Kb, Vb, B, Hq, Hkv, cap, idx, k, nullptr, k, scale, out, part, s, &pm);
+  return check_launch(e, "decode_step_paged launch");
+}
+
 int hata_decode_step(const void* q, const void* K, const void* V, const float* W_H, uint64_t* codes,
                      int B, int Hq, int Hkv, int d, int r, int64_t cap, const int32_t* seq_lens,
                      int64_t max_len, int k, float scale, float* out, int32_t* idx_out, void* ws,
@@ -398,6 +471,8 @@ size_t hata_workspace_bytes(int op, int B, int Hq, int Hkv, int d, int r, int64_
       if (current_cus(&cus) != HATA_OK) return 0;
       return hata::plan_decode_step(B, Hq, Hkv, max_len, k, cus, r).total;
     }
+    case HATA_OP_DECODE_STEP_PAGED:
+      return plan_paged(B, Hq, Hkv, max_len, k, r).total;
     default:
       return 0;
   }

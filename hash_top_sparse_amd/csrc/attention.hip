@@ -38,12 +38,13 @@ int splits_for(int units, int64_t rows, bool dense, int* rows_per_split) {
   return (int)sp;
 }
 
-template <int G>
+// PAGED: K and V are page pools addressed through pm.
+template <int G, bool PAGED>
 __global__ __launch_bounds__(kNT) void attn_partial_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     int Hq, int Hkv, int64_t cap, const int32_t* __restrict__ idx, int k,
     const int32_t* __restrict__ seq_lens, int rows_per_split, int splits, float scale,
-    float* __restrict__ part) {
+    float* __restrict__ part, PageMap pm) {
   __shared__ float red[kMergeFloats<G>];
   const int t = threadIdx.x, slot = t >> 4, sub = t & 15;
   const int unit = blockIdx.y, split = blockIdx.x;
@@ -64,7 +65,7 @@ __global__ __launch_bounds__(kNT) void attn_partial_kernel(
     const uint4 v = *reinterpret_cast<const uint4*>(q + ((int64_t)b * Hq + (int64_t)h * G + g) * kD + sub * 8);
     unpack8(v, qreg[g]);
   }
-  const int64_t row0 = ((int64_t)b * Hkv + h) * cap;
+  const int64_t row0 = PAGED ? 0 : ((int64_t)b * Hkv + h) * cap;
   const uint16_t* Kb = K + row0 * kD + sub * 8;
   const uint16_t* Vb = V + row0 * kD + sub * 8;
   const int32_t* ib = idx ? idx + (int64_t)unit * k : nullptr;
@@ -84,8 +85,9 @@ __global__ __launch_bounds__(kNT) void attn_partial_kernel(
         const int64_t tok = ib ? (int64_t)ib[r] : r;
         if (tok >= 0 && tok < n) {
           valid[u] = true;
-          kv[u] = *reinterpret_cast<const uint4*>(Kb + tok * kD);
-          vv[u] = *reinterpret_cast<const uint4*>(Vb + tok * kD);
+          const int64_t pr = PAGED ? pm.row(b, h, Hkv, tok) : tok;
+          kv[u] = *reinterpret_cast<const uint4*>(Kb + pr * kD);
+          vv[u] = *reinterpret_cast<const uint4*>(Vb + pr * kD);
         }
       }
     }
@@ -145,12 +147,16 @@ template <int G>
 hipError_t launch_attention_g(const uint16_t* q, const uint16_t* K, const uint16_t* V, int B,
                               int Hq, int Hkv, int64_t cap, const int32_t* idx, int k,
                               const int32_t* seq_lens, int64_t max_len, float scale, float* out,
-                              float* part, hipStream_t s) {
+                              float* part, hipStream_t s, const PageMap* pm) {
   const int U = B * Hkv;
   int rps;
   const int splits = splits_for(U, idx ? (int64_t)k : max_len, idx == nullptr, &rps);
-  hipLaunchKernelGGL(attn_partial_kernel<G>, dim3(splits, U), dim3(kNT), 0, s, q, K, V, Hq, Hkv,
-                     cap, idx, k, seq_lens, rps, splits, scale, part);
+  if (pm && pm->bt)
+    hipLaunchKernelGGL((attn_partial_kernel<G, true>), dim3(splits, U), dim3(kNT), 0, s, q, K, V, Hq, Hkv,
+                       cap, idx, k, seq_lens, rps, splits, scale, part, *pm);
+  else
+    hipLaunchKernelGGL((attn_partial_kernel<G, false>), dim3(splits, U), dim3(kNT), 0, s, q, K, V, Hq, Hkv,
+                       cap, idx, k, seq_lens, rps, splits, scale, part, PageMap());
   hipLaunchKernelGGL(attn_combine_kernel<G>, dim3(U, G, kD / 16), dim3(kNT), 0, s, part, splits, Hq,
                      Hkv, out);
   return hipGetLastError();
@@ -171,12 +177,12 @@ size_t attn_part_floats(int B, int Hkv, int G, int64_t max_rows_sparse_or_dense)
 hipError_t launch_attention(const uint16_t* q, const uint16_t* K, const uint16_t* V, int B, int Hq,
                             int Hkv, int64_t cap, const int32_t* idx, int k,
                             const int32_t* seq_lens, int64_t max_len, float scale, float* out,
-                            float* part, hipStream_t s) {
+                            float* part, hipStream_t s, const PageMap* pm) {
   switch (Hq / Hkv) {
-    case 1: return launch_attention_g<1>(q, K, V, B, Hq, Hkv, cap, idx, k, seq_lens, max_len, scale, out, part, s);
-    case 2: return launch_attention_g<2>(q, K, V, B, Hq, Hkv, cap, idx, k, seq_lens, max_len, scale, out, part, s);
-    case 4: return launch_attention_g<4>(q, K, V, B, Hq, Hkv, cap, idx, k, seq_lens, max_len, scale, out, part, s);
-    case 8: return launch_attention_g<8>(q, K, V, B, Hq, Hkv, cap, idx, k, seq_lens, max_len, scale, out, part, s);
+    case 1: return launch_attention_g<1>(q, K, V, B, Hq, Hkv, cap, idx, k, seq_lens, max_len, scale, out, part, s, pm);
+    case 2: return launch_attention_g<2>(q, K, V, B, Hq, Hkv, cap, idx, k, seq_lens, max_len, scale, out, part, s, pm);
+    case 4: return launch_attention_g<4>(q, K, V, B, Hq, Hkv, cap, idx, k, seq_lens, max_len, scale, out, part, s, pm);
+    case 8: return launch_attention_g<8>(q, K, V, B, Hq, Hkv, cap, idx, k, seq_lens, max_len, scale, out, part, s, pm);
     default: return hipErrorInvalidValue;
   }
 }

@@ -20,11 +20,12 @@ namespace {
 
 constexpr int kRowsPerBatch = 4;
 
-template <int R>
+// PAGED: x and codes are page pools addressed through pm (H == Hkv).
+template <int R, bool PAGED>
 __global__ __launch_bounds__(kNT) void encode_rows_kernel(
     const uint16_t* __restrict__ x, int64_t x_rows, int H, int Hkv, int n_new,
     const float* __restrict__ W, uint64_t* __restrict__ codes, int64_t cap,
-    const int32_t* __restrict__ pos, int pos_off, int rows_per_block) {
+    const int32_t* __restrict__ pos, int pos_off, int rows_per_block, PageMap pm) {
   constexpr int W64 = Width<R>::W64;
   __shared__ __align__(16) float xs[kRowsPerBatch * kD];
   __shared__ __align__(16) float red[4 * kRowsPerBatch * R];
@@ -56,7 +57,8 @@ __global__ __launch_bounds__(kNT) void encode_rows_kernel(
         const int64_t ridx = p_b + j;
         if (ridx >= 0 && ridx < lim) {
           const int64_t head = (int64_t)b * H + (int64_t)hk * G + g;
-          const uint32_t two = reinterpret_cast<const uint32_t*>(x + (head * x_rows + ridx) * kD)[c2];
+          const int64_t xr = PAGED ? pm.row(b, hk, Hkv, ridx) : head * x_rows + ridx;
+          const uint32_t two = reinterpret_cast<const uint32_t*>(x + xr * kD)[c2];
           lo = bf16_lo(two);
           hi = bf16_hi(two);
         }
@@ -73,17 +75,31 @@ __global__ __launch_bounds__(kNT) void encode_rows_kernel(
       const int64_t ridx = p_b + j;
       if (ridx >= 0 && ridx < lim) {
         const int64_t head = (int64_t)b * H + (int64_t)hk * G + g;
-        codes[(head * cap + ridx) * W64 + t % W64] = cw[t];
+        const int64_t cr = PAGED ? pm.row(b, hk, Hkv, ridx) : head * cap + ridx;
+        codes[cr * W64 + t % W64] = cw[t];
       }
     }
   }
+}
+
+template <int R>
+void launch_encode_r(dim3 grid, const uint16_t* x, int64_t x_rows, int H, int Hkv, int n_new, const float* W,
+                     uint64_t* codes, int64_t cap, const int32_t* pos, int pos_off, int rpb, const PageMap* pm,
+                     hipStream_t s) {
+  if (pm && pm->bt)
+    hipLaunchKernelGGL((encode_rows_kernel<R, true>), grid, dim3(kNT), 0, s, x, x_rows, H, Hkv, n_new, W, codes,
+                       cap, pos, pos_off, rpb, *pm);
+  else
+    hipLaunchKernelGGL((encode_rows_kernel<R, false>), grid, dim3(kNT), 0, s, x, x_rows, H, Hkv, n_new, W, codes,
+                       cap, pos, pos_off, rpb, PageMap());
 }
 
 }  // namespace
 
 hipError_t launch_encode_rows(const uint16_t* x, int64_t x_rows, int B, int H, int Hkv, int n_new,
                               const float* W, uint64_t* codes, int64_t cap, const int32_t* pos,
-                              int pos_off, hipStream_t s, int r) {
+                              int pos_off, hipStream_t s, int r, const PageMap* pm) {
+  if (pm && pm->bt && H != Hkv) return hipErrorInvalidValue;
   const int G = H / Hkv;
   const int64_t total = (int64_t)G * n_new;
   // enough blocks to cover the chip for long row runs, few rows per block otherwise
@@ -93,14 +109,10 @@ hipError_t launch_encode_rows(const uint16_t* x, int64_t x_rows, int B, int H, i
   const int64_t nbx = (total + rpb - 1) / rpb;
   dim3 grid((unsigned)nbx, (unsigned)(B * Hkv));
   switch (r) {
-    case 32: hipLaunchKernelGGL(encode_rows_kernel<32>, grid, dim3(kNT), 0, s, x, x_rows, H, Hkv, n_new, W,
-                                codes, cap, pos, pos_off, (int)rpb); break;
-    case 64: hipLaunchKernelGGL(encode_rows_kernel<64>, grid, dim3(kNT), 0, s, x, x_rows, H, Hkv, n_new, W,
-                                codes, cap, pos, pos_off, (int)rpb); break;
-    case 256: hipLaunchKernelGGL(encode_rows_kernel<256>, grid, dim3(kNT), 0, s, x, x_rows, H, Hkv, n_new,
-                                 W, codes, cap, pos, pos_off, (int)rpb); break;
-    default: hipLaunchKernelGGL(encode_rows_kernel<128>, grid, dim3(kNT), 0, s, x, x_rows, H, Hkv, n_new,
-                                W, codes, cap, pos, pos_off, (int)rpb); break;
+    case 32: launch_encode_r<32>(grid, x, x_rows, H, Hkv, n_new, W, codes, cap, pos, pos_off, (int)rpb, pm, s); break;
+    case 64: launch_encode_r<64>(grid, x, x_rows, H, Hkv, n_new, W, codes, cap, pos, pos_off, (int)rpb, pm, s); break;
+    case 256: launch_encode_r<256>(grid, x, x_rows, H, Hkv, n_new, W, codes, cap, pos, pos_off, (int)rpb, pm, s); break;
+    default: launch_encode_r<128>(grid, x, x_rows, H, Hkv, n_new, W, codes, cap, pos, pos_off, (int)rpb, pm, s); break;
   }
   return hipGetLastError();
 }

@@ -7,12 +7,26 @@
 
 namespace hata {
 
+// A paged cache (PagedAttention-style block table): row j of (sequence b,
+// KV head h) lives in page bt[b * max_pages + j / P] of a pool laid out
+// [pages][Hkv][P][row], P = 2^log2P.  Page ids outside [0, num_pages) are
+// clamped into it, so the accesses stay inside the pool.
+struct PageMap {
+  const int32_t* bt = nullptr;
+  int max_pages = 0, num_pages = 0, log2P = 0;
+  __device__ __forceinline__ int64_t row(int b, int h, int Hkv, int64_t j) const {
+    int pg = bt[(int64_t)b * max_pages + (int)(j >> log2P)];
+    pg = min(max(pg, 0), num_pages - 1);
+    return (((int64_t)pg * Hkv + h) << log2P) + (j & ((int64_t(1) << log2P) - 1));
+  }
+};
+
 // ---------------------------------------------------------------- encode
 // x bf16 [B][H][x_rows][128]; rows p_b + j (j < n_new) -> codes [B][H][cap][2].
 // Row index of (b, j) is (pos ? pos[b] : 0) + pos_off + j.
 hipError_t launch_encode_rows(const uint16_t* x, int64_t x_rows, int B, int H, int Hkv, int n_new,
                               const float* W, uint64_t* codes, int64_t cap, const int32_t* pos,
-                              int pos_off, hipStream_t s, int r = 128);
+                              int pos_off, hipStream_t s, int r = 128, const PageMap* pm = nullptr);
 // Same contract, matrix-core path for long row runs (prefill).
 hipError_t launch_encode_bulk(const uint16_t* x, int64_t x_rows, int B, int H, int Hkv, int n_new,
                               const float* W, uint64_t* codes, int64_t cap, const int32_t* pos,
@@ -23,7 +37,7 @@ constexpr int kBulkMinRows = 512;
 // ---------------------------------------------------------------- score / select
 hipError_t launch_hamming(const uint64_t* qc, const uint64_t* kc, int B, int Hq, int Hkv,
                           int64_t cap, const int32_t* seq_lens, int64_t max_len, uint16_t* scores,
-                          int64_t sstride, hipStream_t s, int r = 128);
+                          int64_t sstride, hipStream_t s, int r = 128, const PageMap* pm = nullptr);
 hipError_t launch_topk(const uint16_t* scores, int64_t sstride, int B, int Hkv, int64_t cap,
                        const int32_t* seq_lens, int k, int max_score, int32_t* idx, hipStream_t s);
 
@@ -34,7 +48,7 @@ size_t attn_part_floats(int B, int Hkv, int G, int64_t max_rows);
 hipError_t launch_attention(const uint16_t* q, const uint16_t* K, const uint16_t* V, int B, int Hq,
                             int Hkv, int64_t cap, const int32_t* idx, int k,
                             const int32_t* seq_lens, int64_t max_len, float scale, float* out,
-                            float* part, hipStream_t s);
+                            float* part, hipStream_t s, const PageMap* pm = nullptr);
 
 // ---------------------------------------------------------------- fused step
 struct StepPlan {

@@ -163,7 +163,9 @@ __global__ __launch_bounds__(kNT, 2) void prefill_kernel(PrefillArgs a) {
           s[st] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, qf[kk], s[st], 0, 0, 0);
         }
       }
-      // scale, causal mask, running max
+      // causal mask and running max on the raw scores (the scale is
+      // positive, so it commutes with the max and is applied inside the
+      // exponent: p = 2^(s c - m c))
       const bool need_mask = k0 + kBK - 1 > wpos_min;
       float mx = -INFINITY;
 #pragma unroll
@@ -171,30 +173,35 @@ __global__ __launch_bounds__(kNT, 2) void prefill_kernel(PrefillArgs a) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int key = k0 + 32 * st + 8 * (i >> 2) + (i & 3) + 4 * half;
-          float v = s[st][i] * a.scale_log2;
-          if ((st == 1 && !act1) || (need_mask && key > pos)) v = -INFINITY;
-          s[st][i] = v;
-          mx = fmaxf(mx, v);
+          if ((st == 1 && !act1) || (need_mask && key > pos)) s[st][i] = -INFINITY;
+          mx = fmaxf(mx, s[st][i]);
         }
       mx = fmaxf(mx, __shfl_xor(mx, 32));
       const float m_new = fmaxf(m_run, mx);
-      const float mref = m_new == -INFINITY ? 0.f : m_new;
-      const float alpha = __builtin_amdgcn_exp2f(m_run - mref);
+      const float mref = m_new == -INFINITY ? 0.f : __fmul_rn(m_new, a.scale_log2);
       float psum = 0.f;
 #pragma unroll
       for (int st = 0; st < 2; ++st)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          const float p = __builtin_amdgcn_exp2f(s[st][i] - mref);
+          const float p = __builtin_amdgcn_exp2f(fmaf(s[st][i], a.scale_log2, -mref));
           s[st][i] = p;
           psum += p;
         }
-      l_run = l_run * alpha + psum;
+      // rescale only when some row's max moved (after the first tiles it
+      // rarely does)
+      if (__ballot(m_new != m_run) != 0) {
+        // the previous tiles' weights are relative to m_run * c, rounded the
+        // same way, so an unchanged max gives alpha = 1 exactly
+        const float alpha = __builtin_amdgcn_exp2f(__fmul_rn(m_run, a.scale_log2) - mref);
+        l_run *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) o[dt][i] *= alpha;
+      }
+      l_run += psum;
       m_run = m_new;
-#pragma unroll
-      for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) o[dt][i] *= alpha;
       // O^T += V^T P^T over the active 32-key halves, 16 keys per MFMA
 #pragma unroll
       for (int st = 0; st < 2; ++st) {

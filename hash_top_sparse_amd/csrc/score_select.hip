@@ -15,13 +15,14 @@ namespace {
 
 constexpr int kHamTPT = 8;  // tokens per thread in the staged Hamming kernel
 
-template <int G, int R>
+// PAGED: kc is a page pool addressed through pm.
+template <int G, int R, bool PAGED>
 __global__ __launch_bounds__(kNT) void hamming_kernel(const uint64_t* __restrict__ qc,
                                                       const uint64_t* __restrict__ kc, int Hq,
                                                       int Hkv, int64_t cap,
                                                       const int32_t* __restrict__ seq_lens,
                                                       uint16_t* __restrict__ scores,
-                                                      int64_t sstride) {
+                                                      int64_t sstride, PageMap pm) {
   const int t = threadIdx.x;
   const int unit = blockIdx.y;
   const int b = unit / Hkv, h = unit - b * Hkv;
@@ -49,7 +50,7 @@ __global__ __launch_bounds__(kNT) void hamming_kernel(const uint64_t* __restrict
 #pragma unroll
   for (int j = 0; j < kHamTPT; ++j) {
     const int64_t i = i0 + j * kNT + t;
-    if (i < n) c[j] = load_code<R>(src, i);
+    if (i < n) c[j] = PAGED ? load_code<R>(kc, pm.row(b, h, Hkv, i)) : load_code<R>(src, i);
   }
 #pragma unroll
   for (int j = 0; j < kHamTPT; ++j) {
@@ -166,15 +167,27 @@ __global__ __launch_bounds__(kTopkNT) void topk_kernel(const uint16_t* __restric
 
 }  // namespace
 
+template <int G, int R>
+static void launch_hamming_gr(const uint64_t* qc, const uint64_t* kc, int Hq, int Hkv, int64_t cap,
+                              const int32_t* seq_lens, uint16_t* scores, int64_t sstride, dim3 grid,
+                              const PageMap* pm, hipStream_t s) {
+  if (pm && pm->bt)
+    hipLaunchKernelGGL((hamming_kernel<G, R, true>), grid, dim3(kNT), 0, s, qc, kc, Hq, Hkv, cap, seq_lens,
+                       scores, sstride, *pm);
+  else
+    hipLaunchKernelGGL((hamming_kernel<G, R, false>), grid, dim3(kNT), 0, s, qc, kc, Hq, Hkv, cap, seq_lens,
+                       scores, sstride, PageMap());
+}
+
 template <int R>
 static hipError_t launch_hamming_r(const uint64_t* qc, const uint64_t* kc, int G, int Hq, int Hkv,
                                    int64_t cap, const int32_t* seq_lens, uint16_t* scores, int64_t sstride,
-                                   dim3 grid, hipStream_t s) {
+                                   dim3 grid, const PageMap* pm, hipStream_t s) {
   switch (G) {
-    case 1: hipLaunchKernelGGL((hamming_kernel<1, R>), grid, dim3(kNT), 0, s, qc, kc, Hq, Hkv, cap, seq_lens, scores, sstride); break;
-    case 2: hipLaunchKernelGGL((hamming_kernel<2, R>), grid, dim3(kNT), 0, s, qc, kc, Hq, Hkv, cap, seq_lens, scores, sstride); break;
-    case 4: hipLaunchKernelGGL((hamming_kernel<4, R>), grid, dim3(kNT), 0, s, qc, kc, Hq, Hkv, cap, seq_lens, scores, sstride); break;
-    case 8: hipLaunchKernelGGL((hamming_kernel<8, R>), grid, dim3(kNT), 0, s, qc, kc, Hq, Hkv, cap, seq_lens, scores, sstride); break;
+    case 1: launch_hamming_gr<1, R>(qc, kc, Hq, Hkv, cap, seq_lens, scores, sstride, grid, pm, s); break;
+    case 2: launch_hamming_gr<2, R>(qc, kc, Hq, Hkv, cap, seq_lens, scores, sstride, grid, pm, s); break;
+    case 4: launch_hamming_gr<4, R>(qc, kc, Hq, Hkv, cap, seq_lens, scores, sstride, grid, pm, s); break;
+    case 8: launch_hamming_gr<8, R>(qc, kc, Hq, Hkv, cap, seq_lens, scores, sstride, grid, pm, s); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -182,15 +195,15 @@ static hipError_t launch_hamming_r(const uint64_t* qc, const uint64_t* kc, int G
 
 hipError_t launch_hamming(const uint64_t* qc, const uint64_t* kc, int B, int Hq, int Hkv,
                           int64_t cap, const int32_t* seq_lens, int64_t max_len, uint16_t* scores,
-                          int64_t sstride, hipStream_t s, int r) {
+                          int64_t sstride, hipStream_t s, int r, const PageMap* pm) {
   const int G = Hq / Hkv;
   const int64_t per_block = (int64_t)kNT * kHamTPT;
   dim3 grid((unsigned)((max_len + per_block - 1) / per_block), (unsigned)(B * Hkv));
   switch (r) {
-    case 32: return launch_hamming_r<32>(qc, kc, G, Hq, Hkv, cap, seq_lens, scores, sstride, grid, s);
-    case 64: return launch_hamming_r<64>(qc, kc, G, Hq, Hkv, cap, seq_lens, scores, sstride, grid, s);
-    case 256: return launch_hamming_r<256>(qc, kc, G, Hq, Hkv, cap, seq_lens, scores, sstride, grid, s);
-    default: return launch_hamming_r<128>(qc, kc, G, Hq, Hkv, cap, seq_lens, scores, sstride, grid, s);
+    case 32: return launch_hamming_r<32>(qc, kc, G, Hq, Hkv, cap, seq_lens, scores, sstride, grid, pm, s);
+    case 64: return launch_hamming_r<64>(qc, kc, G, Hq, Hkv, cap, seq_lens, scores, sstride, grid, pm, s);
+    case 256: return launch_hamming_r<256>(qc, kc, G, Hq, Hkv, cap, seq_lens, scores, sstride, grid, pm, s);
+    default: return launch_hamming_r<128>(qc, kc, G, Hq, Hkv, cap, seq_lens, scores, sstride, grid, pm, s);
   }
 }
 

@@ -84,7 +84,8 @@ enum {
   HATA_OP_TOPK = 1,
   HATA_OP_SPARSE_DECODE = 2,
   HATA_OP_DECODE_STEP = 3,
-  HATA_OP_DENSE_DECODE = 4
+  HATA_OP_DENSE_DECODE = 4,
+  HATA_OP_DECODE_STEP_PAGED = 5
 };
 
 /* Static description of a status code. */
@@ -216,6 +217,35 @@ int hata_prefill(const void* q, const void* K, const void* V,
                  int d, int r, int64_t q_rows, int64_t cap,
                  const int32_t* seq_lens, int64_t max_len, float scale,
                  float* out, void* stream);
+
+/*
+ * hata_decode_step over a paged cache (the block-table layout of
+ * PagedAttention, which the HATA notes build on; their decode step is
+ * unchanged): row j of sequence b lives in page block_table[b * max_pages +
+ * j / page_rows] of three pools that share the table,
+ *   K_pool, V_pool bf16 [num_pages][Hkv][page_rows][d]
+ *   code_pool uint64    [num_pages][Hkv][page_rows][ceil(r/64)]
+ * block_table int32 [B][max_pages] (device); page ids outside
+ * [0, num_pages) are clamped into it (reads and writes stay in the pools;
+ * the results for such rows are then unspecified).  The logical capacity is
+ * cap = max_pages * page_rows; seq_lens[b] in [1, max_len], max_len <= cap.
+ * Same steps and results as hata_decode_step on the gathered contiguous
+ * cache: the key row n_b-1 is encoded and its code written through the
+ * table, every code row 0..n_b-1 is scored, top-k by (score, index), and
+ * the attention gathers the kept K/V rows through the table.  Runs as
+ * separate kernels (row encode, Hamming scan, top-k, gather attention).
+ * page_rows a power of two in [16, 65536]; q, the pools 16-byte aligned;
+ * idx_out [B][Hkv][k] optional.  ws: hata_workspace_bytes(
+ * HATA_OP_DECODE_STEP_PAGED, ...) (contents need no initialisation).
+ */
+int hata_decode_step_paged(const void* q, const void* K_pool,
+                           const void* V_pool, const float* W_H,
+                           uint64_t* code_pool, const int32_t* block_table,
+                           int max_pages, int num_pages, int page_rows, int B,
+                           int Hq, int Hkv, int d, int r,
+                           const int32_t* seq_lens, int64_t max_len, int k,
+                           float scale, float* out, int32_t* idx_out,
+                           void* ws, size_t ws_bytes, void* stream);
 
 /*
  * Dense flash-decode baseline over all n_b rows of every unit (the same

@@ -223,6 +223,33 @@ def test_prefill_validation():
     assert _prefill(codes=MIS2) == EALIGN
 
 
+def _paged(**kw):
+    a = dict(q=A, K=A, V=A, W=A, codes=A, bt=A, max_pages=256, num_pages=300, P=16, B=1, Hq=32, Hkv=8, d=128,
+             r=128, seq=A, max_len=4096, k=512, out=A, ws_bytes=1 << 30)
+    a.update(kw)
+    return binding.raw_call("hata_decode_step_paged", a["q"], a["K"], a["V"], a["W"], a["codes"], a["bt"],
+                            a["max_pages"], a["num_pages"], a["P"], a["B"], a["Hq"], a["Hkv"], a["d"], a["r"],
+                            a["seq"], ctypes.c_int64(a["max_len"]), a["k"], F(0.088), a["out"], None, A,
+                            ctypes.c_size_t(a["ws_bytes"]), None)
+
+
+def test_decode_step_paged_validation(lib):
+    need = lib.hata_workspace_bytes(5, 1, 32, 8, 128, 128, ctypes.c_int64(4096), 512)
+    assert need > 0
+    assert _paged(bt=None) == ENULL
+    assert _paged(codes=None) == ENULL
+    assert _paged(d=64) == EUNSUP
+    assert _paged(P=24) == EUNSUP               # not a power of two
+    assert _paged(P=8) == EUNSUP
+    assert _paged(k=0) == EUNSUP
+    assert _paged(max_pages=0) == ESHAPE
+    assert _paged(num_pages=0) == ESHAPE
+    assert _paged(max_len=4097) == ESHAPE       # beyond max_pages * page_rows
+    assert _paged(codes=MIS) == EALIGN
+    assert _paged(bt=MIS2) == EALIGN
+    assert _paged(ws_bytes=need - 1) == EWS
+
+
 def lib_stream_read_valid():
     return binding.load().hata_stream_read(A, ctypes.c_size_t(4096), A, ctypes.c_size_t(1024), P(None))
 
@@ -248,6 +275,7 @@ def test_forced_launch_failure_propagates():
         assert _enc() == EHIP
         assert lib_stream_read_valid() == EHIP
         assert _prefill() == EHIP
+        assert _paged() == EHIP
         with pytest.raises(binding.HataError) as ei:
             binding._check(_ham())
         assert ei.value.status == EHIP

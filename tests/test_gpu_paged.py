@@ -1,0 +1,112 @@
+"""GPU parity of hata_decode_step_paged: the cache rows of each sequence are
+scattered over shuffled pages of K/V/code pools; the step must give the
+oracle's results on the gathered contiguous cache (codes, kept set, output)
+and agree with hata_decode_step on the contiguous cache."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+from hash_top_sparse_amd import synth
+from helpers import Dev, assert_close, check_codes, codes_np, gpu_build_cache, gpu_query_codes, oracle_units
+
+pytestmark = pytest.mark.gpu
+
+
+def _log(msg):
+    print(msg, flush=True)
+
+
+def _paginate(x: torch.Tensor, P: int, bt: torch.Tensor, num_pages: int, fill=0) -> torch.Tensor:
+    """x [B, Hkv, cap, C] -> pool [num_pages, Hkv, P, C] with page bt[b, i]
+    holding rows [i P, (i + 1) P) of sequence b (unused pages keep `fill`)."""
+    B, Hkv, cap, C = x.shape
+    mp = bt.shape[1]
+    xp = torch.full((B, Hkv, mp * P, C), fill, dtype=x.dtype, device=x.device)
+    xp[:, :, :cap] = x
+    pool = torch.full((num_pages, Hkv, P, C), fill, dtype=x.dtype, device=x.device)
+    pool[bt.reshape(-1).long()] = xp.view(B, Hkv, mp, P, C).permute(0, 2, 1, 3, 4).reshape(B * mp, Hkv, P, C)
+    return pool
+
+
+def _gather(pool: torch.Tensor, bt: torch.Tensor, cap: int) -> torch.Tensor:
+    num_pages, Hkv, P, C = pool.shape
+    B, mp = bt.shape
+    g = pool[bt.reshape(-1).long()].view(B, mp, Hkv, P, C).permute(0, 2, 1, 3, 4).reshape(B, Hkv, mp * P, C)
+    return g[:, :, :cap]
+
+
+CASES = [
+    # B, Hq, Hkv, N, lens, k, P, r, dist, spare pages
+    (2, 32, 8, 6000, [6000, 4321], 512, 16, 128, "gauss", 7),
+    (3, 8, 8, 2100, [1, 700, 2049], 64, 256, 128, "exact", 0),
+    (2, 8, 4, 3000, [3000, 1500], 100, 64, 64, "gauss", 3),
+    (1, 16, 2, 1000, [999], 32, 128, 256, "gauss", 1),
+    (2, 8, 1, 1500, [1500, 37], 16, 32, 32, "gauss", 2),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=[f"P{c[6]}-r{c[7]}-G{c[1] // c[2]}-{c[8]}" for c in CASES])
+def test_paged_step_matches_oracle_and_contiguous_step(hata_gpu, case):
+    B, Hq, Hkv, N, lens, k, P, r, dist, spare = case
+    _log(f"paged step B={B} Hq={Hq} Hkv={Hkv} lens={lens} k={k} P={P} r={r} {dist}")
+    s = synth.Shape(f"paged-{B}-{Hq}-{Hkv}-{N}", B=B, Hq=Hq, Hkv=Hkv, N=N, k=k, r=r, dist=dist,
+                    seed_base=7700 + P + r, outliers=4 if dist == "gauss" else 0,
+                    needles=8 if dist == "gauss" else 0)
+    inp = synth.make_inputs(s, seq_lens=np.array(lens, np.int32))
+    d = Dev(inp)
+    codes = gpu_build_cache(hata_gpu, d) if r == 128 else None
+    if codes is None:
+        words = (r + 63) // 64
+        codes = torch.zeros((B, Hkv, d.cap, words), dtype=torch.int64, device="cuda")
+        hata_gpu.encode_append(d.K, d.W, codes, n_new=d.cap)
+    mp = (d.cap + P - 1) // P
+    num_pages = B * mp + spare
+    perm = np.random.default_rng(7701 + P).permutation(num_pages)[:B * mp].astype(np.int32)
+    bt = torch.from_numpy(perm.reshape(B, mp)).cuda()
+    Kp = _paginate(d.K, P, bt, num_pages)
+    Vp = _paginate(d.V, P, bt, num_pages)
+    Cp = _paginate(codes, P, bt, num_pages, fill=0x1234)
+    Cp_before = Cp.clone()
+
+    ws = hata_gpu.alloc_workspace(hata_gpu.OP_DECODE_STEP_PAGED, B, Hq, Hkv, d.max_len, k, r=r)
+    out = torch.zeros((B, Hq, 128), dtype=torch.float32, device="cuda")
+    idx = torch.zeros((B, Hkv, k), dtype=torch.int32, device="cuda")
+    hata_gpu.decode_step_paged(d.q, Kp, Vp, d.W, Cp, bt, d.seq, d.max_len, k, inp.scale, out, ws, idx_out=idx)
+    torch.cuda.synchronize()
+
+    # only the appended rows changed in the pool
+    got_codes = _gather(Cp, bt, d.cap)
+    changed = (Cp != Cp_before).any(dim=-1)
+    expect_changed = torch.zeros_like(changed)
+    for b, n in enumerate(lens):
+        pg = int(perm[b * mp + (n - 1) // P])
+        expect_changed[pg, :, (n - 1) % P] = True
+    assert not (changed & ~expect_changed).any()
+
+    # oracle stages on the GPU's own codes (an allowed flip cannot cascade)
+    cn = codes_np(got_codes)
+    for b, n in enumerate(lens):
+        for h in range(Hkv):
+            check_codes(cn[b, h, n - 1:n], inp.K[b, h, n - 1:n], inp.W[h], dist == "exact")
+    qc = gpu_query_codes(hata_gpu, d) if r == 128 else None
+    if qc is None:
+        words = (r + 63) // 64
+        qc4 = torch.zeros((B, Hq, 1, words), dtype=torch.int64, device="cuda")
+        hata_gpu.encode_append(d.q.view(B, Hq, 1, 128), d.W, qc4, n_new=1)
+        qc = qc4.view(B, Hq, words)
+    _, ridx, rout = oracle_units(inp, codes_np(qc), cn)
+    np.testing.assert_array_equal(idx.cpu().numpy(), ridx)
+    assert_close(out.cpu().numpy(), rout, "paged vs oracle")
+
+    # the contiguous fused step on the same cache gives the same codes and kept set
+    cws = hata_gpu.alloc_workspace(hata_gpu.OP_DECODE_STEP, B, Hq, Hkv, d.max_len, k, r=r)
+    cout = torch.zeros_like(out)
+    cidx = torch.zeros_like(idx)
+    hata_gpu.decode_step(d.q, d.K, d.V, d.W, codes, d.seq, d.max_len, k, inp.scale, cout, cws, cidx)
+    torch.cuda.synchronize()
+    for b, n in enumerate(lens):
+        assert torch.equal(codes[b, :, :n], got_codes[b, :, :n])
+    assert torch.equal(idx, cidx)
+    assert_close(out.cpu().numpy(), cout.cpu().numpy(), "paged vs contiguous")
