@@ -444,6 +444,54 @@ def prefill_bench(N: int = 32768, B: int = 1, Hq: int = 32, Hkv: int = 8, r: int
             "separate_bulk_encode_ms": enc_ms}
 
 
+def paged_bench(config: int = 4, pages=(16, 256), steps: int = 200) -> dict:
+    """Time hata_decode_step_paged on the workload's shape with K/V/code
+    pools of fixed-size pages in shuffled order (bf16 N(0,1) K/V, random
+    codes, fp32 N(0, 1/128) W_H drawn on the device; parity is in the tests),
+    eager launches timed with HIP events, beside the contiguous fused step."""
+    import torch
+
+    from hash_top_sparse_amd import binding, synth
+
+    shape = synth.CONFIGS[config]
+    B, Hq, Hkv, N, k = shape.B, shape.Hq, shape.Hkv, shape.N, shape.k
+    dev = torch.device("cuda:0")
+    g = torch.Generator(device=dev)
+    g.manual_seed(7400)
+    q = torch.randn((B, Hq, 128), generator=g, device=dev).to(torch.bfloat16)
+    W = torch.randn((Hkv, 128, 128), generator=g, device=dev) / np.sqrt(128.0)
+    seq = torch.full((B,), N, dtype=torch.int32, device=dev)
+    out = torch.zeros((B, Hq, 128), dtype=torch.float32, device=dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    res = {"workload": shape.name}
+    for P in pages:
+        mp = (N + P - 1) // P
+        num_pages = B * mp
+        Kp = torch.randn((num_pages, Hkv, P, 128), generator=g, device=dev).to(torch.bfloat16)
+        Vp = torch.randn((num_pages, Hkv, P, 128), generator=g, device=dev).to(torch.bfloat16)
+        Cp = torch.randint(-(1 << 62), 1 << 62, (num_pages, Hkv, P, 2), generator=g, device=dev)
+        bt = torch.randperm(num_pages, generator=g, device=dev).to(torch.int32).view(B, mp)
+        ws = binding.alloc_workspace(binding.OP_DECODE_STEP_PAGED, B, Hq, Hkv, N, k)
+
+        def step():
+            binding.decode_step_paged(q, Kp, Vp, W, Cp, bt, seq, N, k, 1.0 / np.sqrt(128.0), out, ws)
+
+        for _ in range(10):
+            step()
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(steps):
+            step()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / steps
+        res[f"page_rows_{P}"] = {"ms_per_step": ms, "steps_per_s": 1000.0 / ms}
+        log(f"paged step ({shape.name}, {P}-row pages): {ms * 1e3:.1f} us/step")
+        del Kp, Vp, Cp
+        torch.cuda.empty_cache()
+    return res
+
+
 def train_bench(J: int = 512, n: int = 8192, r: int = 128, steps: int = 20) -> dict:
     """Time the hash-weight training step for one head (synthetic bf16 N(0,1)
     Q/K drawn on the device, J sampled queries at random positions of an
@@ -505,6 +553,7 @@ def main() -> int:
     ap.add_argument("--no-graph", action="store_true", help="launch the timed steps eagerly")
     ap.add_argument("--sweep", action="store_true", help="also time the other workloads (2, 3, 5)")
     ap.add_argument("--no-prefill", action="store_true", help="skip the 32K-token prefill measurement")
+    ap.add_argument("--no-paged", action="store_true", help="skip the paged-cache step measurement")
     ap.add_argument("--train", action="store_true",
                     help="also time the hash-weight training step (labels + one gradient step, one head)")
     ap.add_argument("--width-sweep", action="store_true",
@@ -564,6 +613,7 @@ def main() -> int:
                               "GBs": rr["GBs"], "frac_of_peak": rr["frac_of_peak"],
                               "bytes_per_step": rr["bytes_per_step"], "stored_bytes_per_step": layout}
     pbench = None if args.no_prefill else prefill_bench()
+    gbench = None if args.no_paged else paged_bench(args.config)
     msweep = model_sweep() if args.model_sweep else None
     tbench = train_bench() if args.train else None
     peak_meas = read_peak()
@@ -615,6 +665,8 @@ def main() -> int:
         res["hash_train"] = tbench
     if pbench is not None:
         res["prefill"] = pbench
+    if gbench is not None:
+        res["paged_step"] = gbench
     print(json.dumps(res), flush=True)
     return 0
 

@@ -143,14 +143,16 @@ def hamming_scores(q_codes: torch.Tensor, k_codes: torch.Tensor, seq_lens: torch
 
 
 def topk(scores: torch.Tensor, seq_lens: torch.Tensor, max_len: int, k: int, max_score: int,
-         idx: torch.Tensor, stream=None) -> None:
-    """scores int16 [B,Hkv,cap]; idx int32 [B,Hkv,k]."""
+         idx: torch.Tensor, stream=None, ws: torch.Tensor | None = None) -> None:
+    """scores int16 [B,Hkv,cap]; idx int32 [B,Hkv,k].  ws (uint8, at least
+    workspace_bytes(OP_TOPK, ...)) lets long sequences use many workgroups."""
     _need(scores, torch.int16, "scores")
     _need(idx, torch.int32, "idx")
     _need(seq_lens, torch.int32, "seq_lens")
     B, Hkv, cap = scores.shape
     _check(load().hata_topk(_ptr(scores), B, Hkv, cap, _ptr(seq_lens), int(max_len), int(k),
-                            int(max_score), _ptr(idx), None, 0, _stream(stream)))
+                            int(max_score), _ptr(idx), _ptr(ws), 0 if ws is None else ws.numel(),
+                            _stream(stream)))
 
 
 def workspace_bytes(op: int, B: int, Hq: int, Hkv: int, max_len: int, k: int, d: int = 128,

@@ -167,8 +167,6 @@ int hata_hamming_scores(const uint64_t* q_codes, const uint64_t* k_codes, int B,
 int hata_topk(const uint16_t* scores, int B, int Hkv, int64_t cap, const int32_t* seq_lens,
               int64_t max_len, int k, int max_score, int32_t* idx, void* ws, size_t ws_bytes,
               void* stream) {
-  (void)ws;
-  (void)ws_bytes;
   if (!scores || !seq_lens || !idx) return fail(HATA_ERR_NULL, "topk: null pointer");
   if (B < 1 || Hkv < 1) return fail(HATA_ERR_SHAPE, "topk: B=%d Hkv=%d", B, Hkv);
   int st = check_len(cap, max_len);
@@ -178,8 +176,10 @@ int hata_topk(const uint16_t* scores, int B, int Hkv, int64_t cap, const int32_t
     return fail(HATA_ERR_UNSUPPORTED, "topk: max_score=%d outside [0, 2048]", max_score);
   if (!aligned(scores, 2) || !aligned(idx, 4)) return fail(HATA_ERR_ALIGN, "topk: misaligned buffer");
   if ((st = pre_launch("topk"))) return st;
+  // with a large enough workspace, long sequences are split over many workgroups
+  void* scratch = (ws && ws_bytes >= hata::topk_scratch_bytes(B, Hkv, max_len, max_score)) ? ws : nullptr;
   hipError_t e = hata::launch_topk(scores, cap, B, Hkv, cap, seq_lens, k, max_score, idx,
-                                   reinterpret_cast<hipStream_t>(stream));
+                                   reinterpret_cast<hipStream_t>(stream), scratch, max_len);
   return check_launch(e, "topk launch");
 }
 
@@ -284,7 +284,8 @@ static int decode_step_impl(const void* q, const void* K, const void* V, const f
   if (e == hipSuccess) e = hata::launch_hamming(qc, codes, B, Hq, Hkv, cap, seq_lens, max_len, sc, max_len, s, r);
   int32_t* idx = idx_out;
   if (e == hipSuccess && !idx) return fail(HATA_ERR_UNSUPPORTED, "decode_step: this shape needs idx_out");
-  if (e == hipSuccess) e = hata::launch_topk(sc, max_len, B, Hkv, cap, seq_lens, k, G * r, idx, s);
+  if (e == hipSuccess)
+    e = hata::launch_topk(sc, max_len, B, Hkv, cap, seq_lens, k, G * r, idx, s, wsb + p.off_topk, max_len);
   if (e == hipSuccess)
     e = hata::launch_attention(qb, Kb, Vb, B, Hq, Hkv, cap, idx, k, nullptr, k, scale, out, part, s);
   return check_launch(e, "decode_step (staged) launch");
@@ -293,7 +294,7 @@ static int decode_step_impl(const void* q, const void* K, const void* V, const f
 namespace {
 // workspace of the paged step: query codes, scores, kept indices, attention records
 struct PagedPlan {
-  size_t qc = 0, sc = 0, idx = 0, attn = 0, total = 0;
+  size_t qc = 0, sc = 0, idx = 0, attn = 0, topk = 0, total = 0;
 };
 PagedPlan plan_paged(int B, int Hq, int Hkv, int64_t max_len, int k, int r) {
   auto al = [](size_t x) { return (x + 255) / 256 * 256; };
@@ -304,6 +305,7 @@ PagedPlan plan_paged(int B, int Hq, int Hkv, int64_t max_len, int k, int r) {
   p.sc = off;   off = al(off + U * (size_t)max_len * 2);
   p.idx = off;  off = al(off + U * (size_t)k * 4);
   p.attn = off; off = al(off + hata::attn_part_floats(B, Hkv, Hq / Hkv, k) * 4);
+  p.topk = off; off = al(off + hata::topk_scratch_bytes(B, Hkv, max_len, (Hq / Hkv) * r));
   p.total = off;
   return p;
 }
@@ -357,7 +359,8 @@ int hata_decode_step_paged(const void* q, const void* K_pool, const void* V_pool
     e = hata::launch_encode_rows(Kb, cap, B, Hkv, Hkv, 1, W_H, code_pool, cap, seq_lens, -1, s, r, &pm);
   if (e == hipSuccess)
     e = hata::launch_hamming(qc, code_pool, B, Hq, Hkv, cap, seq_lens, max_len, sc, max_len, s, r, &pm);
-  if (e == hipSuccess) e = hata::launch_topk(sc, max_len, B, Hkv, cap, seq_lens, k, G * r, idx, s);
+  if (e == hipSuccess)
+    e = hata::launch_topk(sc, max_len, B, Hkv, cap, seq_lens, k, G * r, idx, s, wsb + p.topk, max_len);
   if (e == hipSuccess)
     e = hata::launch_attention(qb, Kb, Vb, B, Hq, Hkv, cap, idx, k, nullptr, k, scale, out, part, s, &pm);
   return check_launch(e, "decode_step_paged launch");
@@ -461,7 +464,7 @@ size_t hata_workspace_bytes(int op, int B, int Hq, int Hkv, int d, int r, int64_
   const int G = Hq / Hkv;
   switch (op) {
     case HATA_OP_TOPK:
-      return 0;
+      return hata::topk_scratch_bytes(B, Hkv, max_len, G * r);
     case HATA_OP_SPARSE_DECODE:
       return hata::attn_part_floats(B, Hkv, G, k) * sizeof(float);
     case HATA_OP_DENSE_DECODE:

@@ -879,6 +879,7 @@ StepPlan plan_decode_step(int B, int Hq, int Hkv, int64_t max_len, int k, int nu
     p.off_qc = off;     off = align(off + (size_t)B * Hq * ((r + 63) / 64) * 8);
     p.off_scores = off; off = align(off + (size_t)U * max_len * 2);
     p.off_attn = off;   off = align(off + attn_part_floats(B, Hkv, G, k) * 4);
+    p.off_topk = off;   off = align(off + topk_scratch_bytes(B, Hkv, max_len, G * r));
   }
   p.total = off;
   return p;

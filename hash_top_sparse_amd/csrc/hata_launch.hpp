@@ -38,8 +38,13 @@ constexpr int kBulkMinRows = 512;
 hipError_t launch_hamming(const uint64_t* qc, const uint64_t* kc, int B, int Hq, int Hkv,
                           int64_t cap, const int32_t* seq_lens, int64_t max_len, uint16_t* scores,
                           int64_t sstride, hipStream_t s, int r = 128, const PageMap* pm = nullptr);
+// scratch (optional, topk_scratch_bytes bytes, no initialisation needed):
+// with it, sequences longer than 4096 rows are selected by many workgroups
+// per unit; the result is the same.  max_len bounds the sequence lengths.
+size_t topk_scratch_bytes(int B, int Hkv, int64_t max_len, int max_score);
 hipError_t launch_topk(const uint16_t* scores, int64_t sstride, int B, int Hkv, int64_t cap,
-                       const int32_t* seq_lens, int k, int max_score, int32_t* idx, hipStream_t s);
+                       const int32_t* seq_lens, int k, int max_score, int32_t* idx, hipStream_t s,
+                       void* scratch = nullptr, int64_t max_len = 0);
 
 // ---------------------------------------------------------------- attention
 // Split-K partial attention + combine.  idx == nullptr means dense (rows
@@ -57,7 +62,7 @@ struct StepPlan {
   size_t lds_bytes = 0;
   // workspace layout (byte offsets)
   size_t off_err = 0, off_flags = 0, off_win = 0, off_full = 0, off_part = 0;
-  size_t off_qc = 0, off_scores = 0, off_attn = 0;
+  size_t off_qc = 0, off_scores = 0, off_attn = 0, off_topk = 0;
   int full_words = 0;  // 32-bit words per workgroup in the full-histogram area
   size_t total = 0;
 };

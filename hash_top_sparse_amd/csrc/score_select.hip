@@ -165,7 +165,169 @@ __global__ __launch_bounds__(kTopkNT) void topk_kernel(const uint16_t* __restric
   for (int j = m + t; j < k; j += kTopkNT) out[j] = -1;
 }
 
+// ---- multi-workgroup top-k for long sequences: the same selection as
+// topk_kernel in four passes over chunks of kTkChunk scores.
+//   1. unit histogram (per-chunk LDS histograms added into the unit's)
+//   2. threshold T and tie quota per unit; -1 padding past min(k, n)
+//   3. per chunk: counts of scores < T and == T
+//   4. per chunk: ordered compaction at offset (kept rows in earlier chunks),
+//      a row's slot being (#rows < T before it) + min(#ties before it, quota)
+constexpr int kTkChunk = 4096;
+
+__device__ __forceinline__ int unit_len(const int32_t* seq_lens, int b, int64_t cap, int64_t sstride) {
+  int64_t n = seq_lens[b];
+  if (n < 0) n = 0;
+  if (n > cap) n = cap;
+  if (n > sstride) n = sstride;
+  return (int)n;
+}
+
+__global__ __launch_bounds__(kNT) void topk_hist_kernel(const uint16_t* __restrict__ scores, int64_t sstride,
+                                                        int Hkv, int64_t cap, const int32_t* __restrict__ seq_lens,
+                                                        int max_score, uint32_t* __restrict__ hist) {
+  __shared__ uint32_t h[kMaxBins];
+  const int t = threadIdx.x, unit = blockIdx.y;
+  const int n = unit_len(seq_lens, unit / Hkv, cap, sstride);
+  const int i0 = blockIdx.x * kTkChunk;
+  if (i0 >= n) return;
+  const int nb = max_score + 1;
+  for (int i = t; i < nb; i += kNT) h[i] = 0;
+  __syncthreads();
+  const uint16_t* sc = scores + (int64_t)unit * sstride;
+  const int i1 = min(n, i0 + kTkChunk);
+  for (int i = i0 + t; i < i1; i += kNT) atomicAdd(&h[min((int)sc[i], max_score)], 1u);
+  __syncthreads();
+  for (int i = t; i < nb; i += kNT)
+    if (h[i]) atomicAdd(&hist[(int64_t)unit * nb + i], h[i]);
+}
+
+__global__ __launch_bounds__(kNT) void topk_thresh_kernel(const uint32_t* __restrict__ hist, int nb, int Hkv,
+                                                          int64_t cap, int64_t sstride,
+                                                          const int32_t* __restrict__ seq_lens, int k,
+                                                          uint32_t* __restrict__ params, int32_t* __restrict__ idx) {
+  __shared__ uint32_t tmp[16];
+  __shared__ uint32_t stat;
+  const int t = threadIdx.x, unit = blockIdx.x;
+  const int n = unit_len(seq_lens, unit / Hkv, cap, sstride);
+  const uint32_t* hu = hist + (int64_t)unit * nb;
+  const int bpt = (nb + kNT - 1) / kNT;
+  uint32_t loc = 0;
+  for (int j = 0; j < bpt; ++j) {
+    const int s = t * bpt + j;
+    if (s < nb) loc += hu[s];
+  }
+  if (t == 0) stat = 0;
+  uint32_t tot;
+  uint32_t run = block_excl_scan_u32(loc, tmp, &tot);
+  uint32_t below_k = 0;  // bins with cum < k
+  for (int j = 0; j < bpt; ++j) {
+    const int s = t * bpt + j;
+    if (s < nb) {
+      run += hu[s];
+      below_k += (run < (uint32_t)k) ? 1u : 0u;
+    }
+  }
+  atomicAdd(&stat, below_k);
+  __syncthreads();
+  int T = (int)stat;
+  if (T >= nb) T = nb - 1;  // fewer than k tokens: keep everything
+  // count of scores < T
+  uint32_t lt = 0;
+  for (int j = 0; j < bpt; ++j) {
+    const int s = t * bpt + j;
+    if (s < T) lt += hu[s];
+  }
+  uint32_t lt_total;
+  (void)block_excl_scan_u32(lt, tmp, &lt_total);
+  if (t == 0) {
+    params[2 * unit] = (uint32_t)T;
+    params[2 * unit + 1] = (uint32_t)k - lt_total;  // ties to keep
+  }
+  int32_t* out = idx + (int64_t)unit * k;
+  for (int j = min(k, n) + t; j < k; j += kNT) out[j] = -1;
+}
+
+__global__ __launch_bounds__(kNT) void topk_count_kernel(const uint16_t* __restrict__ scores, int64_t sstride,
+                                                         int Hkv, int64_t cap, const int32_t* __restrict__ seq_lens,
+                                                         int max_score, const uint32_t* __restrict__ params,
+                                                         int chunks, uint32_t* __restrict__ cnt) {
+  __shared__ uint32_t tmp[16];
+  const int t = threadIdx.x, unit = blockIdx.y, c = blockIdx.x;
+  const int n = unit_len(seq_lens, unit / Hkv, cap, sstride);
+  const int i0 = c * kTkChunk, i1 = min(n, i0 + kTkChunk);
+  const int T = (int)params[2 * unit];
+  const uint16_t* sc = scores + (int64_t)unit * sstride;
+  uint32_t lt = 0, eq = 0;
+  for (int i = i0 + t; i < i1; i += kNT) {
+    const int sv = min((int)sc[i], max_score);
+    lt += sv < T;
+    eq += sv == T;
+  }
+  uint32_t lt_tot, eq_tot;
+  (void)block_excl_scan_u32(lt, tmp, &lt_tot);
+  (void)block_excl_scan_u32(eq, tmp, &eq_tot);
+  if (t == 0) {
+    cnt[((int64_t)unit * chunks + c) * 2] = lt_tot;
+    cnt[((int64_t)unit * chunks + c) * 2 + 1] = eq_tot;
+  }
+}
+
+__global__ __launch_bounds__(kNT) void topk_compact_kernel(const uint16_t* __restrict__ scores, int64_t sstride,
+                                                           int Hkv, int64_t cap,
+                                                           const int32_t* __restrict__ seq_lens, int max_score,
+                                                           const uint32_t* __restrict__ params, int chunks,
+                                                           const uint32_t* __restrict__ cnt, int k,
+                                                           int32_t* __restrict__ idx) {
+  __shared__ uint32_t tmp[16];
+  const int t = threadIdx.x, unit = blockIdx.y, c = blockIdx.x;
+  const int n = unit_len(seq_lens, unit / Hkv, cap, sstride);
+  const int i0 = c * kTkChunk;
+  if (i0 >= n) return;
+  const int T = (int)params[2 * unit];
+  const uint32_t quota = params[2 * unit + 1];
+  // rows < T and ties in the chunks before this one
+  uint32_t lt_p = 0, eq_p = 0;
+  for (int cc = t; cc < c; cc += kNT) {
+    lt_p += cnt[((int64_t)unit * chunks + cc) * 2];
+    eq_p += cnt[((int64_t)unit * chunks + cc) * 2 + 1];
+  }
+  uint32_t lt_before, eq_before;
+  (void)block_excl_scan_u32(lt_p, tmp, &lt_before);
+  (void)block_excl_scan_u32(eq_p, tmp, &eq_before);
+  // this chunk: thread t owns rows [i0 + t * per, ...) in order
+  constexpr int per = kTkChunk / kNT;
+  const int b0 = i0 + t * per, b1 = min(n, b0 + per);
+  const uint16_t* sc = scores + (int64_t)unit * sstride;
+  uint32_t lt = 0, eq = 0;
+  for (int i = b0; i < b1; ++i) {
+    const int sv = min((int)sc[i], max_score);
+    lt += sv < T;
+    eq += sv == T;
+  }
+  uint32_t dummy;
+  uint32_t ltb = lt_before + block_excl_scan_u32(lt, tmp, &dummy);
+  uint32_t eqb = eq_before + block_excl_scan_u32(eq, tmp, &dummy);
+  int32_t* out = idx + (int64_t)unit * k;
+  for (int i = b0; i < b1; ++i) {
+    const int sv = min((int)sc[i], max_score);
+    if (sv < T) {
+      out[ltb + min(eqb, quota)] = i;
+      ++ltb;
+    } else if (sv == T) {
+      if (eqb < quota) out[ltb + eqb] = i;
+      ++eqb;
+    }
+  }
+}
+
 }  // namespace
+
+size_t topk_scratch_bytes(int B, int Hkv, int64_t max_len, int max_score) {
+  const size_t U = (size_t)B * Hkv;
+  const size_t chunks = (size_t)((max_len + kTkChunk - 1) / kTkChunk);
+  const size_t nb = (size_t)max_score + 1;
+  return (U * nb + U * 2 + U * chunks * 2) * 4;
+}
 
 template <int G, int R>
 static void launch_hamming_gr(const uint64_t* qc, const uint64_t* kc, int Hq, int Hkv, int64_t cap,
@@ -208,10 +370,30 @@ hipError_t launch_hamming(const uint64_t* qc, const uint64_t* kc, int B, int Hq,
 }
 
 hipError_t launch_topk(const uint16_t* scores, int64_t sstride, int B, int Hkv, int64_t cap,
-                       const int32_t* seq_lens, int k, int max_score, int32_t* idx, hipStream_t s) {
+                       const int32_t* seq_lens, int k, int max_score, int32_t* idx, hipStream_t s,
+                       void* scratch, int64_t max_len) {
   if (max_score + 1 > kMaxBins) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(topk_kernel, dim3(B * Hkv), dim3(kTopkNT), 0, s, scores, sstride, Hkv, cap,
-                     seq_lens, k, max_score, idx);
+  if (max_len > sstride) max_len = sstride;
+  if (!scratch || max_len <= kTkChunk) {
+    hipLaunchKernelGGL(topk_kernel, dim3(B * Hkv), dim3(kTopkNT), 0, s, scores, sstride, Hkv, cap,
+                       seq_lens, k, max_score, idx);
+    return hipGetLastError();
+  }
+  const int U = B * Hkv, nb = max_score + 1;
+  const int chunks = (int)((max_len + kTkChunk - 1) / kTkChunk);
+  uint32_t* hist = static_cast<uint32_t*>(scratch);
+  uint32_t* params = hist + (size_t)U * nb;
+  uint32_t* cnt = params + (size_t)U * 2;
+  hipError_t e = launch_fill_zero(hist, (size_t)U * nb * 4, s);
+  if (e != hipSuccess) return e;
+  const dim3 grid((unsigned)chunks, (unsigned)U);
+  hipLaunchKernelGGL(topk_hist_kernel, grid, dim3(kNT), 0, s, scores, sstride, Hkv, cap, seq_lens, max_score, hist);
+  hipLaunchKernelGGL(topk_thresh_kernel, dim3(U), dim3(kNT), 0, s, hist, nb, Hkv, cap, sstride, seq_lens, k, params,
+                     idx);
+  hipLaunchKernelGGL(topk_count_kernel, grid, dim3(kNT), 0, s, scores, sstride, Hkv, cap, seq_lens, max_score,
+                     params, chunks, cnt);
+  hipLaunchKernelGGL(topk_compact_kernel, grid, dim3(kNT), 0, s, scores, sstride, Hkv, cap, seq_lens, max_score,
+                     params, chunks, cnt, k, idx);
   return hipGetLastError();
 }
 

@@ -132,7 +132,12 @@ int hata_hamming_scores(const uint64_t* q_codes, const uint64_t* k_codes, int B,
  * ascending token ids of the first min(k, n_b) tokens in (score, id) order;
  * idx[b][h][min(k,n_b):k] = -1.  scores as produced by hata_hamming_scores,
  * every valid entry <= max_score (max_score = G*r; larger values are clamped
- * to max_score).  ws: hata_workspace_bytes(HATA_OP_TOPK, ...).
+ * to max_score).  ws (optional): with at least hata_workspace_bytes(
+ * HATA_OP_TOPK, B, Hq, Hkv, d, r, max_len, k) bytes (any contents, G*r >=
+ * max_score), sequences longer than 4096 tokens are selected by many
+ * workgroups each (chunk histograms, threshold, chunk counts, ordered
+ * compaction); without it (NULL or smaller) one workgroup per unit does it.
+ * The result is the same either way.
  */
 int hata_topk(const uint16_t* scores, int B, int Hkv, int64_t cap,
               const int32_t* seq_lens, int64_t max_len, int k, int max_score,

@@ -122,7 +122,10 @@ def test_sparse_and_dense_workspace_checks(lib):
     rc = binding.raw_call("hata_dense_decode", A, A, A, 1, 32, 8, 128, ctypes.c_int64(4096), A,
                           ctypes.c_int64(4096), F(0.088), A, A, ctypes.c_size_t(dneed - 4), None)
     assert rc == EWS
-    assert binding.workspace_bytes(binding.OP_TOPK, 1, 32, 8, 4096, 512) == 0
+    # top-k: the optional scratch of the many-workgroup selection (unit
+    # histograms of G r + 1 bins, threshold and tie quota, per-chunk counts)
+    U, nb, chunks = 8, 4 * 128 + 1, 1
+    assert binding.workspace_bytes(binding.OP_TOPK, 1, 32, 8, 4096, 512) == 4 * (U * nb + 2 * U + 2 * U * chunks)
 
 
 def test_decode_step_validation():

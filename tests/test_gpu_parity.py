@@ -97,9 +97,12 @@ def test_hamming_scores_exact(hata_gpu, G):
             assert (got[b, h, n:] == 0xFFFF).all()   # rows past n untouched
 
 
-@pytest.mark.parametrize("case", ["random", "ties", "all_equal", "k_ge_n", "n1", "max_score"])
+TOPK_CASES = ["random", "ties", "all_equal", "k_ge_n", "n1", "max_score"]
+
+
+@pytest.mark.parametrize("case", TOPK_CASES)
 def test_topk_exact(hata_gpu, case):
-    rng = np.random.default_rng(hash(case) % 1000)
+    rng = np.random.default_rng(600 + TOPK_CASES.index(case))
     B, Hkv, cap = 2, 3, 5000
     k = 512
     lens = np.array([5000, 3333], np.int32)
@@ -129,6 +132,46 @@ def test_topk_exact(hata_gpu, case):
         for h in range(Hkv):
             ref = oracle.topk(S[b, h, :lens[b]].astype(np.int32), k)
             np.testing.assert_array_equal(got[b, h], ref)
+
+
+MULTI_TOPK_CASES = [
+    # lens, k, score range (low, high), max_score
+    ([20000, 4097], 512, (200, 330), 512),      # random; one length just past one chunk
+    ([20000, 13000], 512, (0, 4), 512),          # heavy ties crossing chunk boundaries
+    ([20000, 8192], 4096, (77, 78), 512),        # all equal: the first k rows
+    ([20000, 100], 512, (0, 513), 512),          # a sequence shorter than k
+    ([131072, 65536], 1, (0, 1025), 1024),       # k = 1, long rows
+    ([40000, 40000], 2048, (0, 2049), 2048),     # widest bins (G r = 2048)
+]
+
+
+@pytest.mark.parametrize("case", range(len(MULTI_TOPK_CASES)))
+def test_topk_many_workgroups_exact(hata_gpu, case):
+    """With its workspace, hata_topk splits long sequences over workgroups
+    (chunk histograms, threshold, chunk counts, ordered compaction); the kept
+    set must be the oracle's, including the lowest-index tie rule across
+    chunks, and equal to the one-workgroup selection."""
+    lens, k, (lo, hi), max_score = MULTI_TOPK_CASES[case]
+    rng = np.random.default_rng(650 + case)
+    B, Hkv, cap = 2, 2, max(lens)
+    lens = np.array(lens, np.int32)
+    S = rng.integers(lo, hi, size=(B, Hkv, cap))
+    sc = torch.from_numpy(S.astype(np.uint16).view(np.int16)).cuda()
+    seq = torch.from_numpy(lens).cuda()
+    nbytes = hata_gpu.workspace_bytes(hata_gpu.OP_TOPK, B, Hkv * (max_score // 128), Hkv, cap, k)
+    assert nbytes >= 4 * (B * Hkv * (max_score + 1) + 2 * B * Hkv * (1 + cap // 4096))
+    ws = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
+    idx = torch.full((B, Hkv, k), -7, dtype=torch.int32, device="cuda")
+    hata_gpu.topk(sc, seq, cap, k, max_score, idx, ws=ws)
+    one = torch.full_like(idx, -9)
+    hata_gpu.topk(sc, seq, cap, k, max_score, one)
+    torch.cuda.synchronize()
+    got = idx.cpu().numpy()
+    for b in range(B):
+        for h in range(Hkv):
+            ref = oracle.topk(S[b, h, :lens[b]].astype(np.int32), k)
+            np.testing.assert_array_equal(got[b, h], ref)
+    assert torch.equal(idx, one)
 
 
 # ------------------------------------------------------------------ attention
