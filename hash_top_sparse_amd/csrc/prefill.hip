@@ -110,15 +110,35 @@ __global__ __launch_bounds__(kNT, 2) void prefill_kernel(PrefillArgs a) {
   const uint16_t* Kh = a.K + kvoff;
   const uint16_t* Vh = a.V + kvoff;
   uint4 kreg[4], vreg[4];
-  const int vkg = t >> 4, vc = t & 15;  // value rows 4 vkg .. 4 vkg + 3, columns 8 vc ..
+  // value staging: thread t loads rows 4 vkg .. 4 vkg + 3 at columns 8 vc ..
+  // 8 vc + 7 and writes them transposed, 4 keys per 8-byte store.  A store
+  // of element e lands at dword 34 (8 vc + e) + 2 vkg, i.e. bank
+  // 16 vc + 34 e + 2 vkg (mod 64): with vkg = t % 16 and the two column
+  // blocks of each half-wave 2 apart, the 32 lanes of a half-wave hit 32
+  // distinct bank pairs.
+  const int vkg = t & 15, vu = t >> 4;
+  const int vc = 4 * (vu >> 2) + ((vu & 1) << 1) + ((vu >> 1) & 1);
+  // element offsets inside a tile: key chunk i of this thread is row
+  // t/16 + 16 i, columns 8 (t % 16) ..; value chunk i is row 4 vkg + i
+  const int koff = (t >> 4) * kD + (t & 15) * 8;
+  const int voff = 4 * vkg * kD + vc * 8;
   auto fetch = [&](int tile) {
+    const uint16_t* kt = Kh + (int64_t)tile * kBK * kD;
+    const uint16_t* vtl = Vh + (int64_t)tile * kBK * kD;
+    if (tile * kBK + kBK <= L) {  // a full tile (all but possibly the last)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int id = t + kNT * i, key = id >> 4, c = id & 15;
-      const int row = tile * kBK + key;
-      kreg[i] = row < L ? *reinterpret_cast<const uint4*>(Kh + (int64_t)row * kD + c * 8) : make_uint4(0, 0, 0, 0);
-      const int vrow = tile * kBK + 4 * vkg + i;
-      vreg[i] = vrow < L ? *reinterpret_cast<const uint4*>(Vh + (int64_t)vrow * kD + vc * 8) : make_uint4(0, 0, 0, 0);
+      for (int i = 0; i < 4; ++i) {
+        kreg[i] = *reinterpret_cast<const uint4*>(kt + koff + i * 16 * kD);
+        vreg[i] = *reinterpret_cast<const uint4*>(vtl + voff + i * kD);
+      }
+    } else {
+      const int rows = L - tile * kBK;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        kreg[i] = (t >> 4) + 16 * i < rows ? *reinterpret_cast<const uint4*>(kt + koff + i * 16 * kD)
+                                           : make_uint4(0, 0, 0, 0);
+        vreg[i] = 4 * vkg + i < rows ? *reinterpret_cast<const uint4*>(vtl + voff + i * kD) : make_uint4(0, 0, 0, 0);
+      }
     }
   };
 
@@ -166,16 +186,23 @@ __global__ __launch_bounds__(kNT, 2) void prefill_kernel(PrefillArgs a) {
       // causal mask and running max on the raw scores (the scale is
       // positive, so it commutes with the max and is applied inside the
       // exponent: p = 2^(s c - m c))
-      const bool need_mask = k0 + kBK - 1 > wpos_min;
+      const bool need_mask = k0 + kBK - 1 > wpos_min;  // some key may follow some query of the wave
       float mx = -INFINITY;
+      if (need_mask) {
 #pragma unroll
-      for (int st = 0; st < 2; ++st)
+        for (int st = 0; st < 2; ++st)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int key = k0 + 32 * st + 8 * (i >> 2) + (i & 3) + 4 * half;
-          if ((st == 1 && !act1) || (need_mask && key > pos)) s[st][i] = -INFINITY;
-          mx = fmaxf(mx, s[st][i]);
-        }
+          for (int i = 0; i < 16; ++i) {
+            const int key = k0 + 32 * st + 8 * (i >> 2) + (i & 3) + 4 * half;
+            if ((st == 1 && !act1) || key > pos) s[st][i] = -INFINITY;
+            mx = fmaxf(mx, s[st][i]);
+          }
+      } else {
+#pragma unroll
+        for (int st = 0; st < 2; ++st)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[st][i]);
+      }
       mx = fmaxf(mx, __shfl_xor(mx, 32));
       const float m_new = fmaxf(m_run, mx);
       const float mref = m_new == -INFINITY ? 0.f : __fmul_rn(m_new, a.scale_log2);
