@@ -45,6 +45,12 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 constexpr int kBK = 64;              // keys per staged tile
 constexpr int kKsStride = kD + 8;    // bf16 per staged key row (272 bytes)
 constexpr int kVtStride = kBK + 4;   // bf16 per transposed value row (136 bytes)
+constexpr int kBufElems = kBK * kKsStride + kD * kVtStride;  // bf16 per K/V tile buffer
+
+template <int G, int R>
+constexpr size_t prefill_lds_bytes() {
+  return 2 * kBufElems * sizeof(uint16_t) + (128 / G) * (R / 32) * sizeof(uint32_t);
+}
 
 struct PrefillArgs {
   const uint16_t* q;
@@ -70,9 +76,11 @@ __global__ __launch_bounds__(kNT, 2) void prefill_kernel(PrefillArgs a) {
   constexpr int QP = 128 / G;         // positions per workgroup
   constexpr int W64 = Width<R>::W64;  // 64-bit words per code row
   constexpr int CT = R / 32;          // 32-column slices of the code
-  __shared__ __align__(16) uint16_t ks[kBK * kKsStride];
-  __shared__ __align__(16) uint16_t vt[kD * kVtStride];
-  __shared__ uint32_t cw[QP * CT];
+  // two K/V tile buffers (the next tile is stored while the current one is
+  // multiplied: one barrier per tile), then the code words
+  extern __shared__ __align__(16) unsigned char smem[];
+  uint16_t* lds = reinterpret_cast<uint16_t*>(smem);
+  uint32_t* cw = reinterpret_cast<uint32_t*>(smem + 2 * kBufElems * sizeof(uint16_t));
 
   const int t = threadIdx.x, lane = t & 63, half = lane >> 5;
   const int wv = __builtin_amdgcn_readfirstlane(t >> 6);
@@ -151,88 +159,108 @@ __global__ __launch_bounds__(kNT, 2) void prefill_kernel(PrefillArgs a) {
 
   const float* Wh = a.W + (int64_t)hk * kD * R;
 
-  fetch(0);
-  for (int tile = 0; tile < ntiles; ++tile) {
+  auto stage = [&](int buf) {
+    uint16_t* ksb = lds + buf * kBufElems;
+    uint16_t* vtb = ksb + kBK * kKsStride;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int id = t + kNT * i, key = id >> 4, c = id & 15;
-      *reinterpret_cast<uint4*>(ks + key * kKsStride + c * 8) = kreg[i];
+      *reinterpret_cast<uint4*>(ksb + key * kKsStride + c * 8) = kreg[i];
     }
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const uint32_t lo = half16(vreg[0], e) | (half16(vreg[1], e) << 16);
       const uint32_t hi = half16(vreg[2], e) | (half16(vreg[3], e) << 16);
-      *reinterpret_cast<uint2*>(vt + (vc * 8 + e) * kVtStride + 4 * vkg) = make_uint2(lo, hi);
+      *reinterpret_cast<uint2*>(vtb + (vc * 8 + e) * kVtStride + 4 * vkg) = make_uint2(lo, hi);
     }
+  };
+  fetch(0);
+  stage(0);
+  if (ntiles > 1) fetch(1);
+  for (int tile = 0; tile < ntiles; ++tile) {
+    // tile's buffer is complete and every wave is done with the other
+    // buffer (tile - 1): store tile + 1 there and fetch tile + 2
     __syncthreads();
-    if (tile + 1 < ntiles) fetch(tile + 1);
+    if (tile + 1 < ntiles) {
+      stage((tile + 1) & 1);
+      if (tile + 2 < ntiles) fetch(tile + 2);
+    }
+    const uint16_t* ks = lds + (tile & 1) * kBufElems;
+    const uint16_t* vt = ks + kBK * kKsStride;
     const int k0 = tile * kBK;
 
     if (wactive && k0 <= wpos_max) {
       const bool act1 = k0 + 32 <= wpos_max;
       f32x16 s[2];
 #pragma unroll
-      for (int st = 0; st < 2; ++st) {
+      for (int st = 0; st < 2; ++st)
 #pragma unroll
         for (int i = 0; i < 16; ++i) s[st][i] = 0.f;
-        if (st == 1 && !act1) continue;
-        const uint16_t* krow = ks + (32 * st + (lane & 31)) * kKsStride + 8 * half;
+      {
+        // the two 32-key halves as two independent accumulation chains in
+        // one block, so their MFMAs and fragment reads interleave
+        const uint16_t* krow = ks + (lane & 31) * kKsStride + 8 * half;
+        if (act1) {
 #pragma unroll
-        for (int kk = 0; kk < 8; ++kk) {
-          const bf16x8 af = *reinterpret_cast<const bf16x8*>(krow + 16 * kk);
-          s[st] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, qf[kk], s[st], 0, 0, 0);
+          for (int kk = 0; kk < 8; ++kk) {
+            const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(krow + 16 * kk);
+            const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(krow + 32 * kKsStride + 16 * kk);
+            s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qf[kk], s[0], 0, 0, 0);
+            s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qf[kk], s[1], 0, 0, 0);
+          }
+        } else {
+#pragma unroll
+          for (int kk = 0; kk < 8; ++kk) {
+            const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(krow + 16 * kk);
+            s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qf[kk], s[0], 0, 0, 0);
+          }
         }
       }
-      // causal mask and running max on the raw scores (the scale is
+      // Online softmax and O^T += V^T P^T, one 32-key half at a time, so the
+      // softmax of the first half overlaps the second half's score MFMAs
+      // and the second half's softmax overlaps the first half's value
+      // MFMAs.  Causal mask and running max on the raw scores (the scale is
       // positive, so it commutes with the max and is applied inside the
-      // exponent: p = 2^(s c - m c))
+      // exponent: p = 2^(s c - m c)).
       const bool need_mask = k0 + kBK - 1 > wpos_min;  // some key may follow some query of the wave
-      float mx = -INFINITY;
-      if (need_mask) {
 #pragma unroll
-        for (int st = 0; st < 2; ++st)
+      for (int st = 0; st < 2; ++st) {
+        if (st == 1 && !act1) continue;
+        float mx = -INFINITY;
+        if (need_mask) {
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
             const int key = k0 + 32 * st + 8 * (i >> 2) + (i & 3) + 4 * half;
-            if ((st == 1 && !act1) || key > pos) s[st][i] = -INFINITY;
+            if (key > pos) s[st][i] = -INFINITY;
             mx = fmaxf(mx, s[st][i]);
           }
-      } else {
-#pragma unroll
-        for (int st = 0; st < 2; ++st)
+        } else {
 #pragma unroll
           for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[st][i]);
-      }
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float m_new = fmaxf(m_run, mx);
-      const float mref = m_new == -INFINITY ? 0.f : __fmul_rn(m_new, a.scale_log2);
-      float psum = 0.f;
-#pragma unroll
-      for (int st = 0; st < 2; ++st)
+        }
+        mx = pair32_max(mx);
+        const float m_new = fmaxf(m_run, mx);
+        const float mref = m_new == -INFINITY ? 0.f : __fmul_rn(m_new, a.scale_log2);
+        float psum = 0.f;
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const float p = __builtin_amdgcn_exp2f(fmaf(s[st][i], a.scale_log2, -mref));
           s[st][i] = p;
           psum += p;
         }
-      // rescale only when some row's max moved (after the first tiles it
-      // rarely does)
-      if (__ballot(m_new != m_run) != 0) {
-        // the previous tiles' weights are relative to m_run * c, rounded the
-        // same way, so an unchanged max gives alpha = 1 exactly
-        const float alpha = __builtin_amdgcn_exp2f(__fmul_rn(m_run, a.scale_log2) - mref);
-        l_run *= alpha;
+        // rescale only when some row's max moved (after the first tiles it
+        // rarely does); the earlier weights are relative to m_run * c,
+        // rounded the same way, so an unchanged max gives alpha = 1 exactly
+        if (__ballot(m_new != m_run) != 0) {
+          const float alpha = __builtin_amdgcn_exp2f(__fmul_rn(m_run, a.scale_log2) - mref);
+          l_run *= alpha;
 #pragma unroll
-        for (int dt = 0; dt < 4; ++dt)
+          for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-          for (int i = 0; i < 16; ++i) o[dt][i] *= alpha;
-      }
-      l_run += psum;
-      m_run = m_new;
-      // O^T += V^T P^T over the active 32-key halves, 16 keys per MFMA
-#pragma unroll
-      for (int st = 0; st < 2; ++st) {
-        if (st == 1 && !act1) continue;
+            for (int i = 0; i < 16; ++i) o[dt][i] *= alpha;
+        }
+        l_run += psum;
+        m_run = m_new;
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
           bf16x8 pf;
@@ -250,13 +278,11 @@ __global__ __launch_bounds__(kNT, 2) void prefill_kernel(PrefillArgs a) {
         }
       }
     }
-
-    __syncthreads();
   }
 
   // normalise and store this lane's query row: accumulator i of slice dt
   // holds column 32 dt + 8 (i/4) + i%4 + 4 half
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  const float l_tot = pair32_sum(l_run);
   if (qvalid) {
     const float inv = 1.f / l_tot;
     float* orow = a.out + (((int64_t)b * a.Hq + hq) * a.q_rows + pos) * kD;
@@ -274,6 +300,8 @@ __global__ __launch_bounds__(kNT, 2) void prefill_kernel(PrefillArgs a) {
   // where both tiles are staged again (from L2: they were read a moment
   // ago).  Done after the output store so the attention registers are free.
   const bool restage = ntiles - 1 != p0 / kBK;
+  // the last tile's buffer, or buffer 0 for the restaged tiles
+  uint16_t* ks = lds + (restage ? 0 : ((ntiles - 1) & 1) * kBufElems);
   for (int tile = p0 / kBK; tile < ntiles; ++tile) {
     const int k0 = tile * kBK;
     if (restage) {
@@ -343,17 +371,30 @@ __global__ __launch_bounds__(kNT, 2) void prefill_kernel(PrefillArgs a) {
   }
 }
 
+template <int G, int R>
+hipError_t launch_gr(const PrefillArgs& a, hipStream_t s) {
+  constexpr size_t lds = prefill_lds_bytes<G, R>();
+  static bool configured = false;  // dynamic LDS above 64 KiB needs an opt-in per kernel
+  if (!configured) {
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&prefill_kernel<G, R>),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    configured = true;
+  }
+  const dim3 grid((unsigned)((int64_t)a.nqb * a.B * a.Hkv));
+  hipLaunchKernelGGL((prefill_kernel<G, R>), grid, dim3(kNT), lds, s, a);
+  return hipGetLastError();
+}
+
 template <int G>
 hipError_t launch_g(const PrefillArgs& a, int r, hipStream_t s) {
-  const dim3 grid((unsigned)((int64_t)a.nqb * a.B * a.Hkv));
   switch (r) {
-    case 32: hipLaunchKernelGGL((prefill_kernel<G, 32>), grid, dim3(kNT), 0, s, a); break;
-    case 64: hipLaunchKernelGGL((prefill_kernel<G, 64>), grid, dim3(kNT), 0, s, a); break;
-    case 128: hipLaunchKernelGGL((prefill_kernel<G, 128>), grid, dim3(kNT), 0, s, a); break;
-    case 256: hipLaunchKernelGGL((prefill_kernel<G, 256>), grid, dim3(kNT), 0, s, a); break;
+    case 32: return launch_gr<G, 32>(a, s);
+    case 64: return launch_gr<G, 64>(a, s);
+    case 128: return launch_gr<G, 128>(a, s);
+    case 256: return launch_gr<G, 256>(a, s);
     default: return hipErrorInvalidValue;
   }
-  return hipGetLastError();
 }
 
 }  // namespace
