@@ -277,15 +277,18 @@ static int decode_step_impl(const void* q, const void* K, const void* V, const f
   auto* qc = reinterpret_cast<uint64_t*>(wsb + p.off_qc);
   auto* sc = reinterpret_cast<uint16_t*>(wsb + p.off_scores);
   auto* part = reinterpret_cast<float*>(wsb + p.off_attn);
-  hipError_t e = hata::launch_encode_rows(qb, 1, B, Hq, Hkv, 1, W_H, qc, 1, nullptr, 0, s, r);
+  int32_t* idx = idx_out;
+  if (!idx) return fail(HATA_ERR_UNSUPPORTED, "decode_step: this shape needs idx_out");
+  auto* hist = reinterpret_cast<uint32_t*>(wsb + p.off_topk);  // unit histograms, filled by the scan
+  hipError_t e = hata::launch_fill_zero(hist, (size_t)B * Hkv * (G * r + 1) * 4, s);
+  if (e == hipSuccess) e = hata::launch_encode_rows(qb, 1, B, Hq, Hkv, 1, W_H, qc, 1, nullptr, 0, s, r);
   if (e == hipSuccess)  // key append at row seq_lens[b] - 1
     e = hata::launch_encode_rows(Kb, cap, B, Hkv, Hkv, 1, W_Hk, codes, cap, seq_lens, -1, s, r);
-  (void)G;
-  if (e == hipSuccess) e = hata::launch_hamming(qc, codes, B, Hq, Hkv, cap, seq_lens, max_len, sc, max_len, s, r);
-  int32_t* idx = idx_out;
-  if (e == hipSuccess && !idx) return fail(HATA_ERR_UNSUPPORTED, "decode_step: this shape needs idx_out");
   if (e == hipSuccess)
-    e = hata::launch_topk(sc, max_len, B, Hkv, cap, seq_lens, k, G * r, idx, s, wsb + p.off_topk, max_len);
+    e = hata::launch_hamming(qc, codes, B, Hq, Hkv, cap, seq_lens, max_len, sc, max_len, s, r, nullptr, hist);
+  if (e == hipSuccess)
+    e = hata::launch_topk_after_hamming(sc, max_len, B, Hkv, cap, seq_lens, k, G * r, idx, s, wsb + p.off_topk,
+                                        max_len);
   if (e == hipSuccess)
     e = hata::launch_attention(qb, Kb, Vb, B, Hq, Hkv, cap, idx, k, nullptr, k, scale, out, part, s);
   return check_launch(e, "decode_step (staged) launch");
@@ -354,13 +357,18 @@ int hata_decode_step_paged(const void* q, const void* K_pool, const void* V_pool
   auto* sc = reinterpret_cast<uint16_t*>(wsb + p.sc);
   int32_t* idx = idx_out ? idx_out : reinterpret_cast<int32_t*>(wsb + p.idx);
   auto* part = reinterpret_cast<float*>(wsb + p.attn);
-  hipError_t e = hata::launch_encode_rows(qb, 1, B, Hq, Hkv, 1, W_H, qc, 1, nullptr, 0, s, r);
+  // the top-k scratch starts with the unit histograms, which the Hamming
+  // scan fills
+  auto* hist = reinterpret_cast<uint32_t*>(wsb + p.topk);
+  hipError_t e = hata::launch_fill_zero(hist, (size_t)B * Hkv * (G * r + 1) * 4, s);
+  if (e == hipSuccess) e = hata::launch_encode_rows(qb, 1, B, Hq, Hkv, 1, W_H, qc, 1, nullptr, 0, s, r);
   if (e == hipSuccess)  // key append at logical row seq_lens[b] - 1, through the page table
     e = hata::launch_encode_rows(Kb, cap, B, Hkv, Hkv, 1, W_H, code_pool, cap, seq_lens, -1, s, r, &pm);
   if (e == hipSuccess)
-    e = hata::launch_hamming(qc, code_pool, B, Hq, Hkv, cap, seq_lens, max_len, sc, max_len, s, r, &pm);
+    e = hata::launch_hamming(qc, code_pool, B, Hq, Hkv, cap, seq_lens, max_len, sc, max_len, s, r, &pm, hist);
   if (e == hipSuccess)
-    e = hata::launch_topk(sc, max_len, B, Hkv, cap, seq_lens, k, G * r, idx, s, wsb + p.topk, max_len);
+    e = hata::launch_topk_after_hamming(sc, max_len, B, Hkv, cap, seq_lens, k, G * r, idx, s, wsb + p.topk,
+                                        max_len);
   if (e == hipSuccess)
     e = hata::launch_attention(qb, Kb, Vb, B, Hq, Hkv, cap, idx, k, nullptr, k, scale, out, part, s, &pm);
   return check_launch(e, "decode_step_paged launch");

@@ -37,7 +37,8 @@ constexpr int kBulkMinRows = 512;
 // ---------------------------------------------------------------- score / select
 hipError_t launch_hamming(const uint64_t* qc, const uint64_t* kc, int B, int Hq, int Hkv,
                           int64_t cap, const int32_t* seq_lens, int64_t max_len, uint16_t* scores,
-                          int64_t sstride, hipStream_t s, int r = 128, const PageMap* pm = nullptr);
+                          int64_t sstride, hipStream_t s, int r = 128, const PageMap* pm = nullptr,
+                          uint32_t* hist = nullptr);
 // scratch (optional, topk_scratch_bytes bytes, no initialisation needed):
 // with it, sequences longer than 4096 rows are selected by many workgroups
 // per unit; the result is the same.  max_len bounds the sequence lengths.
@@ -45,6 +46,11 @@ size_t topk_scratch_bytes(int B, int Hkv, int64_t max_len, int max_score);
 hipError_t launch_topk(const uint16_t* scores, int64_t sstride, int B, int Hkv, int64_t cap,
                        const int32_t* seq_lens, int k, int max_score, int32_t* idx, hipStream_t s,
                        void* scratch = nullptr, int64_t max_len = 0);
+// The same selection when launch_hamming already filled the unit histograms
+// (hist = the start of scratch, zeroed before the Hamming launch).
+hipError_t launch_topk_after_hamming(const uint16_t* scores, int64_t sstride, int B, int Hkv, int64_t cap,
+                                     const int32_t* seq_lens, int k, int max_score, int32_t* idx, hipStream_t s,
+                                     void* scratch, int64_t max_len);
 
 // ---------------------------------------------------------------- attention
 // Split-K partial attention + combine.  idx == nullptr means dense (rows

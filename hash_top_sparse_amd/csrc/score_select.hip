@@ -15,14 +15,17 @@ namespace {
 
 constexpr int kHamTPT = 8;  // tokens per thread in the staged Hamming kernel
 
-// PAGED: kc is a page pool addressed through pm.
-template <int G, int R, bool PAGED>
+// PAGED: kc is a page pool addressed through pm.  HIST: also add this
+// workgroup's score histogram (bins 0..G r) into hist[unit][G r + 1] (for the
+// many-workgroup top-k; hist zeroed beforehand).
+template <int G, int R, bool PAGED, bool HIST>
 __global__ __launch_bounds__(kNT) void hamming_kernel(const uint64_t* __restrict__ qc,
                                                       const uint64_t* __restrict__ kc, int Hq,
                                                       int Hkv, int64_t cap,
                                                       const int32_t* __restrict__ seq_lens,
                                                       uint16_t* __restrict__ scores,
-                                                      int64_t sstride, PageMap pm) {
+                                                      int64_t sstride, PageMap pm,
+                                                      uint32_t* __restrict__ hist) {
   const int t = threadIdx.x;
   const int unit = blockIdx.y;
   const int b = unit / Hkv, h = unit - b * Hkv;
@@ -52,14 +55,27 @@ __global__ __launch_bounds__(kNT) void hamming_kernel(const uint64_t* __restrict
     const int64_t i = i0 + j * kNT + t;
     if (i < n) c[j] = PAGED ? load_code<R>(kc, pm.row(b, h, Hkv, i)) : load_code<R>(src, i);
   }
+  constexpr int NB = G * R + 1;
+  __shared__ uint32_t bins[HIST ? NB : 1];
+  if constexpr (HIST) {
+    for (int e = t; e < NB; e += kNT) bins[e] = 0;
+    __syncthreads();
+  }
 #pragma unroll
   for (int j = 0; j < kHamTPT; ++j) {
     const int64_t i = i0 + j * kNT + t;
     if (i < n) {
       uint32_t cw[W32];
       code_words<R>(c[j], cw);
-      dst[i] = (uint16_t)gqa_hamming_w<G, R>(cw, m);
+      const uint32_t sv = gqa_hamming_w<G, R>(cw, m);
+      dst[i] = (uint16_t)sv;
+      if constexpr (HIST) atomicAdd(&bins[sv], 1u);
     }
+  }
+  if constexpr (HIST) {
+    __syncthreads();
+    for (int e = t; e < NB; e += kNT)
+      if (bins[e]) atomicAdd(&hist[(int64_t)unit * NB + e], bins[e]);
   }
 }
 
@@ -201,22 +217,19 @@ __global__ __launch_bounds__(kNT) void topk_hist_kernel(const uint16_t* __restri
     if (h[i]) atomicAdd(&hist[(int64_t)unit * nb + i], h[i]);
 }
 
-__global__ __launch_bounds__(kNT) void topk_thresh_kernel(const uint32_t* __restrict__ hist, int nb, int Hkv,
-                                                          int64_t cap, int64_t sstride,
-                                                          const int32_t* __restrict__ seq_lens, int k,
-                                                          uint32_t* __restrict__ params, int32_t* __restrict__ idx) {
-  __shared__ uint32_t tmp[16];
-  __shared__ uint32_t stat;
-  const int t = threadIdx.x, unit = blockIdx.x;
-  const int n = unit_len(seq_lens, unit / Hkv, cap, sstride);
-  const uint32_t* hu = hist + (int64_t)unit * nb;
+// T = smallest score s with count(<= s) >= k (the top bin when the unit has
+// fewer than k scores) and the tie quota k - count(< T), from the unit's
+// histogram; every thread of the workgroup gets them.
+__device__ __forceinline__ void unit_threshold(const uint32_t* __restrict__ hu, int nb, int k, uint32_t* tmp,
+                                               uint32_t* stat, int* T_out, uint32_t* quota_out) {
+  const int t = threadIdx.x;
   const int bpt = (nb + kNT - 1) / kNT;
   uint32_t loc = 0;
   for (int j = 0; j < bpt; ++j) {
     const int s = t * bpt + j;
     if (s < nb) loc += hu[s];
   }
-  if (t == 0) stat = 0;
+  if (t == 0) *stat = 0;
   uint32_t tot;
   uint32_t run = block_excl_scan_u32(loc, tmp, &tot);
   uint32_t below_k = 0;  // bins with cum < k
@@ -227,11 +240,10 @@ __global__ __launch_bounds__(kNT) void topk_thresh_kernel(const uint32_t* __rest
       below_k += (run < (uint32_t)k) ? 1u : 0u;
     }
   }
-  atomicAdd(&stat, below_k);
+  atomicAdd(stat, below_k);
   __syncthreads();
-  int T = (int)stat;
+  int T = (int)*stat;
   if (T >= nb) T = nb - 1;  // fewer than k tokens: keep everything
-  // count of scores < T
   uint32_t lt = 0;
   for (int j = 0; j < bpt; ++j) {
     const int s = t * bpt + j;
@@ -239,36 +251,93 @@ __global__ __launch_bounds__(kNT) void topk_thresh_kernel(const uint32_t* __rest
   }
   uint32_t lt_total;
   (void)block_excl_scan_u32(lt, tmp, &lt_total);
+  *T_out = T;
+  *quota_out = (uint32_t)k - lt_total;
+}
+
+// One workgroup per unit: T and the tie quota into params, -1 padding past
+// min(k, n).
+__global__ __launch_bounds__(kNT) void topk_thresh_kernel(const uint32_t* __restrict__ hist, int nb, int Hkv,
+                                                          int64_t cap, int64_t sstride,
+                                                          const int32_t* __restrict__ seq_lens, int k,
+                                                          uint32_t* __restrict__ params, int32_t* __restrict__ idx) {
+  __shared__ uint32_t tmp[16];
+  __shared__ uint32_t stat;
+  const int t = threadIdx.x, unit = blockIdx.x;
+  const int n = unit_len(seq_lens, unit / Hkv, cap, sstride);
+  int T;
+  uint32_t quota;
+  unit_threshold(hist + (int64_t)unit * nb, nb, k, tmp, &stat, &T, &quota);
   if (t == 0) {
     params[2 * unit] = (uint32_t)T;
-    params[2 * unit + 1] = (uint32_t)k - lt_total;  // ties to keep
+    params[2 * unit + 1] = quota;
   }
   int32_t* out = idx + (int64_t)unit * k;
   for (int j = min(k, n) + t; j < k; j += kNT) out[j] = -1;
 }
 
+// This thread's 16 consecutive scores from row b0 (rows past n read as
+// max_score + 1, which no threshold selects).
+__device__ __forceinline__ void load16(const uint16_t* sc, int b0, int n, int max_score, int (&v)[16]) {
+  if (b0 + 16 <= n && (reinterpret_cast<uintptr_t>(sc + b0) & 15) == 0) {
+    const uint4 x = *reinterpret_cast<const uint4*>(sc + b0);
+    const uint4 y = *reinterpret_cast<const uint4*>(sc + b0 + 8);
+    const uint32_t w[8] = {x.x, x.y, x.z, x.w, y.x, y.y, y.z, y.w};
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      v[2 * j] = min((int)(w[j] & 0xFFFFu), max_score);
+      v[2 * j + 1] = min((int)(w[j] >> 16), max_score);
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < 16; ++j) v[j] = b0 + j < n ? min((int)sc[b0 + j], max_score) : max_score + 1;
+  }
+}
+
+// Per chunk: counts of scores < T and == T.  own_threshold: T and the tie
+// quota come from the unit histogram (unit_threshold, computed while this
+// thread's scores load), and chunk 0 stores them in params and writes the -1
+// padding past min(k, n); otherwise they are read from params.
 __global__ __launch_bounds__(kNT) void topk_count_kernel(const uint16_t* __restrict__ scores, int64_t sstride,
                                                          int Hkv, int64_t cap, const int32_t* __restrict__ seq_lens,
-                                                         int max_score, const uint32_t* __restrict__ params,
-                                                         int chunks, uint32_t* __restrict__ cnt) {
+                                                         int max_score, uint32_t* __restrict__ params,
+                                                         int chunks, uint32_t* __restrict__ cnt,
+                                                         const uint32_t* __restrict__ hist, int k,
+                                                         int own_threshold, int32_t* __restrict__ idx) {
   __shared__ uint32_t tmp[16];
+  __shared__ uint32_t stat;
   const int t = threadIdx.x, unit = blockIdx.y, c = blockIdx.x;
   const int n = unit_len(seq_lens, unit / Hkv, cap, sstride);
-  const int i0 = c * kTkChunk, i1 = min(n, i0 + kTkChunk);
-  const int T = (int)params[2 * unit];
-  const uint16_t* sc = scores + (int64_t)unit * sstride;
-  uint32_t lt = 0, eq = 0;
-  for (int i = i0 + t; i < i1; i += kNT) {
-    const int sv = min((int)sc[i], max_score);
-    lt += sv < T;
-    eq += sv == T;
+  const int i0 = c * kTkChunk;
+  if (own_threshold && c == 0) {
+    int32_t* out = idx + (int64_t)unit * k;
+    for (int j = min(k, n) + t; j < k; j += kNT) out[j] = -1;
   }
-  uint32_t lt_tot, eq_tot;
-  (void)block_excl_scan_u32(lt, tmp, &lt_tot);
-  (void)block_excl_scan_u32(eq, tmp, &eq_tot);
+  if (i0 >= n) return;  // chunks past the end are never summed
+  int v[16];
+  load16(scores + (int64_t)unit * sstride, i0 + 16 * t, n, max_score, v);
+  int T;
+  if (own_threshold) {
+    uint32_t quota;
+    unit_threshold(hist + (int64_t)unit * (max_score + 1), max_score + 1, k, tmp, &stat, &T, &quota);
+    if (c == 0 && t == 0) {
+      params[2 * unit] = (uint32_t)T;
+      params[2 * unit + 1] = quota;
+    }
+  } else {
+    T = (int)params[2 * unit];
+  }
+  uint32_t lt = 0, eq = 0;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    lt += v[j] < T;
+    eq += v[j] == T;
+  }
+  uint32_t both;  // a chunk holds at most 4096 scores: both counts fit in 16 bits
+  (void)block_excl_scan_u32(lt | (eq << 16), tmp, &both);
   if (t == 0) {
-    cnt[((int64_t)unit * chunks + c) * 2] = lt_tot;
-    cnt[((int64_t)unit * chunks + c) * 2 + 1] = eq_tot;
+    cnt[((int64_t)unit * chunks + c) * 2] = both & 0xFFFFu;
+    cnt[((int64_t)unit * chunks + c) * 2 + 1] = both >> 16;
   }
 }
 
@@ -283,6 +352,9 @@ __global__ __launch_bounds__(kNT) void topk_compact_kernel(const uint16_t* __res
   const int n = unit_len(seq_lens, unit / Hkv, cap, sstride);
   const int i0 = c * kTkChunk;
   if (i0 >= n) return;
+  const int b0 = i0 + 16 * t;
+  int v[16];
+  load16(scores + (int64_t)unit * sstride, b0, n, max_score, v);
   const int T = (int)params[2 * unit];
   const uint32_t quota = params[2 * unit + 1];
   // rows < T and ties in the chunks before this one
@@ -294,27 +366,26 @@ __global__ __launch_bounds__(kNT) void topk_compact_kernel(const uint16_t* __res
   uint32_t lt_before, eq_before;
   (void)block_excl_scan_u32(lt_p, tmp, &lt_before);
   (void)block_excl_scan_u32(eq_p, tmp, &eq_before);
-  // this chunk: thread t owns rows [i0 + t * per, ...) in order
-  constexpr int per = kTkChunk / kNT;
-  const int b0 = i0 + t * per, b1 = min(n, b0 + per);
-  const uint16_t* sc = scores + (int64_t)unit * sstride;
+  // this chunk: thread t owns rows b0 .. b0 + 15 in order; a row's slot is
+  // #(< T) before it + min(#(= T) before it, quota)
   uint32_t lt = 0, eq = 0;
-  for (int i = b0; i < b1; ++i) {
-    const int sv = min((int)sc[i], max_score);
-    lt += sv < T;
-    eq += sv == T;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    lt += v[j] < T;
+    eq += v[j] == T;
   }
   uint32_t dummy;
-  uint32_t ltb = lt_before + block_excl_scan_u32(lt, tmp, &dummy);
-  uint32_t eqb = eq_before + block_excl_scan_u32(eq, tmp, &dummy);
+  const uint32_t pre = block_excl_scan_u32(lt | (eq << 16), tmp, &dummy);
+  uint32_t ltb = lt_before + (pre & 0xFFFFu);
+  uint32_t eqb = eq_before + (pre >> 16);
   int32_t* out = idx + (int64_t)unit * k;
-  for (int i = b0; i < b1; ++i) {
-    const int sv = min((int)sc[i], max_score);
-    if (sv < T) {
-      out[ltb + min(eqb, quota)] = i;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    if (v[j] < T) {
+      out[ltb + min(eqb, quota)] = b0 + j;
       ++ltb;
-    } else if (sv == T) {
-      if (eqb < quota) out[ltb + eqb] = i;
+    } else if (v[j] == T) {
+      if (eqb < quota) out[ltb + eqb] = b0 + j;
       ++eqb;
     }
   }
@@ -332,24 +403,32 @@ size_t topk_scratch_bytes(int B, int Hkv, int64_t max_len, int max_score) {
 template <int G, int R>
 static void launch_hamming_gr(const uint64_t* qc, const uint64_t* kc, int Hq, int Hkv, int64_t cap,
                               const int32_t* seq_lens, uint16_t* scores, int64_t sstride, dim3 grid,
-                              const PageMap* pm, hipStream_t s) {
-  if (pm && pm->bt)
-    hipLaunchKernelGGL((hamming_kernel<G, R, true>), grid, dim3(kNT), 0, s, qc, kc, Hq, Hkv, cap, seq_lens,
-                       scores, sstride, *pm);
+                              const PageMap* pm, uint32_t* hist, hipStream_t s) {
+  const bool paged = pm && pm->bt;
+  const PageMap m = paged ? *pm : PageMap();
+  if (paged && hist)
+    hipLaunchKernelGGL((hamming_kernel<G, R, true, true>), grid, dim3(kNT), 0, s, qc, kc, Hq, Hkv, cap, seq_lens,
+                       scores, sstride, m, hist);
+  else if (paged)
+    hipLaunchKernelGGL((hamming_kernel<G, R, true, false>), grid, dim3(kNT), 0, s, qc, kc, Hq, Hkv, cap, seq_lens,
+                       scores, sstride, m, hist);
+  else if (hist)
+    hipLaunchKernelGGL((hamming_kernel<G, R, false, true>), grid, dim3(kNT), 0, s, qc, kc, Hq, Hkv, cap, seq_lens,
+                       scores, sstride, m, hist);
   else
-    hipLaunchKernelGGL((hamming_kernel<G, R, false>), grid, dim3(kNT), 0, s, qc, kc, Hq, Hkv, cap, seq_lens,
-                       scores, sstride, PageMap());
+    hipLaunchKernelGGL((hamming_kernel<G, R, false, false>), grid, dim3(kNT), 0, s, qc, kc, Hq, Hkv, cap, seq_lens,
+                       scores, sstride, m, hist);
 }
 
 template <int R>
 static hipError_t launch_hamming_r(const uint64_t* qc, const uint64_t* kc, int G, int Hq, int Hkv,
                                    int64_t cap, const int32_t* seq_lens, uint16_t* scores, int64_t sstride,
-                                   dim3 grid, const PageMap* pm, hipStream_t s) {
+                                   dim3 grid, const PageMap* pm, uint32_t* hist, hipStream_t s) {
   switch (G) {
-    case 1: launch_hamming_gr<1, R>(qc, kc, Hq, Hkv, cap, seq_lens, scores, sstride, grid, pm, s); break;
-    case 2: launch_hamming_gr<2, R>(qc, kc, Hq, Hkv, cap, seq_lens, scores, sstride, grid, pm, s); break;
-    case 4: launch_hamming_gr<4, R>(qc, kc, Hq, Hkv, cap, seq_lens, scores, sstride, grid, pm, s); break;
-    case 8: launch_hamming_gr<8, R>(qc, kc, Hq, Hkv, cap, seq_lens, scores, sstride, grid, pm, s); break;
+    case 1: launch_hamming_gr<1, R>(qc, kc, Hq, Hkv, cap, seq_lens, scores, sstride, grid, pm, hist, s); break;
+    case 2: launch_hamming_gr<2, R>(qc, kc, Hq, Hkv, cap, seq_lens, scores, sstride, grid, pm, hist, s); break;
+    case 4: launch_hamming_gr<4, R>(qc, kc, Hq, Hkv, cap, seq_lens, scores, sstride, grid, pm, hist, s); break;
+    case 8: launch_hamming_gr<8, R>(qc, kc, Hq, Hkv, cap, seq_lens, scores, sstride, grid, pm, hist, s); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -357,15 +436,15 @@ static hipError_t launch_hamming_r(const uint64_t* qc, const uint64_t* kc, int G
 
 hipError_t launch_hamming(const uint64_t* qc, const uint64_t* kc, int B, int Hq, int Hkv,
                           int64_t cap, const int32_t* seq_lens, int64_t max_len, uint16_t* scores,
-                          int64_t sstride, hipStream_t s, int r, const PageMap* pm) {
+                          int64_t sstride, hipStream_t s, int r, const PageMap* pm, uint32_t* hist) {
   const int G = Hq / Hkv;
   const int64_t per_block = (int64_t)kNT * kHamTPT;
   dim3 grid((unsigned)((max_len + per_block - 1) / per_block), (unsigned)(B * Hkv));
   switch (r) {
-    case 32: return launch_hamming_r<32>(qc, kc, G, Hq, Hkv, cap, seq_lens, scores, sstride, grid, pm, s);
-    case 64: return launch_hamming_r<64>(qc, kc, G, Hq, Hkv, cap, seq_lens, scores, sstride, grid, pm, s);
-    case 256: return launch_hamming_r<256>(qc, kc, G, Hq, Hkv, cap, seq_lens, scores, sstride, grid, pm, s);
-    default: return launch_hamming_r<128>(qc, kc, G, Hq, Hkv, cap, seq_lens, scores, sstride, grid, pm, s);
+    case 32: return launch_hamming_r<32>(qc, kc, G, Hq, Hkv, cap, seq_lens, scores, sstride, grid, pm, hist, s);
+    case 64: return launch_hamming_r<64>(qc, kc, G, Hq, Hkv, cap, seq_lens, scores, sstride, grid, pm, hist, s);
+    case 256: return launch_hamming_r<256>(qc, kc, G, Hq, Hkv, cap, seq_lens, scores, sstride, grid, pm, hist, s);
+    default: return launch_hamming_r<128>(qc, kc, G, Hq, Hkv, cap, seq_lens, scores, sstride, grid, pm, hist, s);
   }
 }
 
@@ -391,9 +470,27 @@ hipError_t launch_topk(const uint16_t* scores, int64_t sstride, int B, int Hkv, 
   hipLaunchKernelGGL(topk_thresh_kernel, dim3(U), dim3(kNT), 0, s, hist, nb, Hkv, cap, sstride, seq_lens, k, params,
                      idx);
   hipLaunchKernelGGL(topk_count_kernel, grid, dim3(kNT), 0, s, scores, sstride, Hkv, cap, seq_lens, max_score,
-                     params, chunks, cnt);
+                     params, chunks, cnt, (const uint32_t*)hist, k, 0, idx);
   hipLaunchKernelGGL(topk_compact_kernel, grid, dim3(kNT), 0, s, scores, sstride, Hkv, cap, seq_lens, max_score,
-                     params, chunks, cnt, k, idx);
+                     (const uint32_t*)params, chunks, (const uint32_t*)cnt, k, idx);
+  return hipGetLastError();
+}
+
+hipError_t launch_topk_after_hamming(const uint16_t* scores, int64_t sstride, int B, int Hkv, int64_t cap,
+                                     const int32_t* seq_lens, int k, int max_score, int32_t* idx, hipStream_t s,
+                                     void* scratch, int64_t max_len) {
+  if (max_score + 1 > kMaxBins) return hipErrorInvalidValue;
+  if (max_len > sstride) max_len = sstride;
+  const int U = B * Hkv, nb = max_score + 1;
+  const int chunks = (int)((max_len + kTkChunk - 1) / kTkChunk);
+  const uint32_t* hist = static_cast<const uint32_t*>(scratch);
+  uint32_t* params = static_cast<uint32_t*>(scratch) + (size_t)U * nb;
+  uint32_t* cnt = params + (size_t)U * 2;
+  const dim3 grid((unsigned)chunks, (unsigned)U);
+  hipLaunchKernelGGL(topk_count_kernel, grid, dim3(kNT), 0, s, scores, sstride, Hkv, cap, seq_lens, max_score,
+                     params, chunks, cnt, hist, k, 1, idx);
+  hipLaunchKernelGGL(topk_compact_kernel, grid, dim3(kNT), 0, s, scores, sstride, Hkv, cap, seq_lens, max_score,
+                     (const uint32_t*)params, chunks, (const uint32_t*)cnt, k, idx);
   return hipGetLastError();
 }
 
