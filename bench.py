@@ -446,9 +446,10 @@ def prefill_bench(N: int = 32768, B: int = 1, Hq: int = 32, Hkv: int = 8, r: int
 
 def paged_bench(config: int = 4, pages=(16, 256), steps: int = 200) -> dict:
     """Time hata_decode_step_paged on the workload's shape with K/V/code
-    pools of fixed-size pages in shuffled order (bf16 N(0,1) K/V, random
-    codes, fp32 N(0, 1/128) W_H drawn on the device; parity is in the tests),
-    eager launches timed with HIP events, beside the contiguous fused step."""
+    pools of fixed-size pages in shuffled order, against hata_decode_step on
+    the same data laid out contiguously (bf16 N(0,1) K/V, random codes,
+    fp32 N(0, 1/128) W_H drawn on the device; one layer, no cache rotation;
+    parity is in the tests).  Eager launches timed with HIP events."""
     import torch
 
     from hash_top_sparse_amd import binding, synth
@@ -462,20 +463,12 @@ def paged_bench(config: int = 4, pages=(16, 256), steps: int = 200) -> dict:
     W = torch.randn((Hkv, 128, 128), generator=g, device=dev) / np.sqrt(128.0)
     seq = torch.full((B,), N, dtype=torch.int32, device=dev)
     out = torch.zeros((B, Hq, 128), dtype=torch.float32, device=dev)
+    K = torch.randn((B, Hkv, N, 128), generator=g, device=dev).to(torch.bfloat16)
+    V = torch.randn((B, Hkv, N, 128), generator=g, device=dev).to(torch.bfloat16)
+    C = torch.randint(-(1 << 62), 1 << 62, (B, Hkv, N, 2), generator=g, device=dev)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    res = {"workload": shape.name}
-    for P in pages:
-        mp = (N + P - 1) // P
-        num_pages = B * mp
-        Kp = torch.randn((num_pages, Hkv, P, 128), generator=g, device=dev).to(torch.bfloat16)
-        Vp = torch.randn((num_pages, Hkv, P, 128), generator=g, device=dev).to(torch.bfloat16)
-        Cp = torch.randint(-(1 << 62), 1 << 62, (num_pages, Hkv, P, 2), generator=g, device=dev)
-        bt = torch.randperm(num_pages, generator=g, device=dev).to(torch.int32).view(B, mp)
-        ws = binding.alloc_workspace(binding.OP_DECODE_STEP_PAGED, B, Hq, Hkv, N, k)
 
-        def step():
-            binding.decode_step_paged(q, Kp, Vp, W, Cp, bt, seq, N, k, 1.0 / np.sqrt(128.0), out, ws)
-
+    def timed(step):
         for _ in range(10):
             step()
         torch.cuda.synchronize()
@@ -484,7 +477,30 @@ def paged_bench(config: int = 4, pages=(16, 256), steps: int = 200) -> dict:
             step()
         e1.record()
         torch.cuda.synchronize()
-        ms = e0.elapsed_time(e1) / steps
+        return e0.elapsed_time(e1) / steps
+
+    cws = binding.alloc_workspace(binding.OP_DECODE_STEP, B, Hq, Hkv, N, k)
+    cms = timed(lambda: binding.decode_step(q, K, V, W, C, seq, N, k, 1.0 / np.sqrt(128.0), out, cws))
+    res = {"workload": shape.name, "contiguous_ms_per_step": cms}
+    log(f"contiguous step on the same data ({shape.name}): {cms * 1e3:.1f} us/step")
+    for P in pages:
+        mp = (N + P - 1) // P
+        num_pages = B * mp
+        bt = torch.randperm(num_pages, generator=g, device=dev).to(torch.int32).view(B, mp)
+        idx = bt.reshape(-1).long()
+
+        def pool(x):
+            c = x.shape[-1]
+            xp = torch.zeros((B, Hkv, mp * P, c), dtype=x.dtype, device=dev)
+            xp[:, :, :N] = x
+            p = torch.empty((num_pages, Hkv, P, c), dtype=x.dtype, device=dev)
+            p[idx] = xp.view(B, Hkv, mp, P, c).permute(0, 2, 1, 3, 4).reshape(B * mp, Hkv, P, c)
+            return p
+
+        Kp, Vp, Cp = pool(K), pool(V), pool(C)
+        ws = binding.alloc_workspace(binding.OP_DECODE_STEP_PAGED, B, Hq, Hkv, N, k)
+        ms = timed(lambda: binding.decode_step_paged(q, Kp, Vp, W, Cp, bt, seq, N, k, 1.0 / np.sqrt(128.0),
+                                                     out, ws))
         res[f"page_rows_{P}"] = {"ms_per_step": ms, "steps_per_s": 1000.0 / ms}
         log(f"paged step ({shape.name}, {P}-row pages): {ms * 1e3:.1f} us/step")
         del Kp, Vp, Cp

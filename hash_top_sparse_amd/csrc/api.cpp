@@ -335,10 +335,14 @@ int hata_decode_step_paged(const void* q, const void* K_pool, const void* V_pool
   if (!aligned(code_pool, 16) || !aligned(q, 16) || !aligned(K_pool, 16) || !aligned(V_pool, 16))
     return fail(HATA_ERR_ALIGN, "decode_step_paged: q, K_pool, V_pool and code_pool must be 16-byte aligned");
   if (!aligned(block_table, 4)) return fail(HATA_ERR_ALIGN, "decode_step_paged: block_table must be 4-byte aligned");
+  // workspace: the fused step's area, then the staged steps' area
+  int cus = 0;
+  if ((st = current_cus(&cus))) return st;
+  const hata::StepPlan sp = hata::plan_decode_step(B, Hq, Hkv, max_len, k, cus, r);
   const PagedPlan p = plan_paged(B, Hq, Hkv, max_len, k, r);
-  if (!ws || ws_bytes < p.total)
-    return fail(HATA_ERR_WORKSPACE, "decode_step_paged: workspace of %zu bytes needed, %zu given", p.total,
-                ws_bytes);
+  const size_t need = sp.total + p.total;
+  if (!ws || ws_bytes < need)
+    return fail(HATA_ERR_WORKSPACE, "decode_step_paged: workspace of %zu bytes needed, %zu given", need, ws_bytes);
   if ((st = pre_launch("decode_step_paged"))) return st;
   hata::PageMap pm;
   pm.bt = block_table;
@@ -348,7 +352,14 @@ int hata_decode_step_paged(const void* q, const void* K_pool, const void* V_pool
   while ((1 << lg) < page_rows) ++lg;
   pm.log2P = lg;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  auto* wsb = static_cast<unsigned char*>(ws);
+  if (hata::decode_step_paged_fusable(sp, page_rows)) {
+    hipError_t e = hata::launch_decode_step_paged(sp, static_cast<const uint16_t*>(q),
+                                                  static_cast<const uint16_t*>(K_pool),
+                                                  static_cast<const uint16_t*>(V_pool), W_H, code_pool, pm, Hq, Hkv,
+                                                  seq_lens, k, scale, out, idx_out, static_cast<unsigned char*>(ws), s);
+    return check_launch(e, "decode_step_paged launch");
+  }
+  auto* wsb = static_cast<unsigned char*>(ws) + sp.total;
   const auto* qb = static_cast<const uint16_t*>(q);
   const auto* Kb = static_cast<const uint16_t*>(K_pool);
   const auto* Vb = static_cast<const uint16_t*>(V_pool);
@@ -482,8 +493,11 @@ size_t hata_workspace_bytes(int op, int B, int Hq, int Hkv, int d, int r, int64_
       if (current_cus(&cus) != HATA_OK) return 0;
       return hata::plan_decode_step(B, Hq, Hkv, max_len, k, cus, r).total;
     }
-    case HATA_OP_DECODE_STEP_PAGED:
-      return plan_paged(B, Hq, Hkv, max_len, k, r).total;
+    case HATA_OP_DECODE_STEP_PAGED: {
+      int cus = 0;
+      if (current_cus(&cus) != HATA_OK) return 0;
+      return hata::plan_decode_step(B, Hq, Hkv, max_len, k, cus, r).total + plan_paged(B, Hq, Hkv, max_len, k, r).total;
+    }
     default:
       return 0;
   }

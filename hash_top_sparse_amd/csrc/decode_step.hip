@@ -62,8 +62,9 @@ constexpr uint32_t kSpinLimit = 1u << 22;
 // wave runs on
 constexpr int kXccIdReg = 20 | (31 << 11);
 constexpr int kShortList = 64;     // kept rows staged in LDS per attention batch
+constexpr int kMaxPgl = kMaxChunk / kNT + 8;  // page ids of one chunk (pages of >= 256 rows)
 
-template <int G, int R = kR>
+template <int G, int R = kR, bool PAGED = false>
 struct Cfg {
   static constexpr int W64 = Width<R>::W64;       // 64-bit words per code row
   static constexpr int NB = G * R + 1;            // histogram bins
@@ -88,7 +89,8 @@ struct Cfg {
   static constexpr int o_whdr = o_misc + 64 * 4;                 // kMaxWg int4 + 2*4*64 uint32
   static constexpr int o_win = o_whdr + 4 * kMaxWg * 4 + 2048;   // kMaxWg*kWinBytes (also combine staging)
   static constexpr int o_kvs = o_win + kMaxWg * kWinBytes;       // kShortList K/V rows
-  static constexpr int o_sel = o_kvs + kShortList * 512;         // k + 1 int32
+  static constexpr int o_pgl = o_kvs + kShortList * 512;         // paged: kMaxPgl int32 page ids
+  static constexpr int o_sel = o_pgl + (PAGED ? kMaxPgl * 4 : 0); // k + 1 int32
   static size_t lds_bytes(int k, int chunk) {
     size_t s = (size_t)o_sel + (size_t)(k + 1) * 4;
     s = (s + 15) / 16 * 16;
@@ -118,6 +120,10 @@ struct StepArgs {
   uint32_t* full;   // [U][kMaxWg][full_words]  (only for overflowing windows)
   float* part;      // [U][kMaxWg][RECP]
   int full_words;
+  // paged cache (the PAGED instance): row j of (b, h) is row j % P of page
+  // bt[b * max_pages + j / P] of pools [num_pages][Hkv][P][.], P = 2^log2P >= 256
+  const int32_t* bt;
+  int max_pages, num_pages, log2P;
 };
 
 __device__ __forceinline__ void map_block(const StepArgs& a, int* unit, int* w) {
@@ -190,9 +196,11 @@ __device__ __forceinline__ void cum_hist(uint32_t* hist, uint32_t* misc, uint32_
 // SEP: the appended key row is encoded with a separate key encoder a.Wk
 // (a separate instance, so the shared-encoder code is unchanged).  R: code
 // width in bits (32, 64, 128, 256).
-template <int G, bool SEP, int R>
+// PAGED: K, V and codes are page pools addressed through a.bt (separate
+// instance; the contiguous code is unchanged).
+template <int G, bool SEP, int R, bool PAGED>
 __global__ __launch_bounds__(kNT) void decode_step_kernel(const StepArgs a) {
-  using C = Cfg<G, R>;
+  using C = Cfg<G, R, PAGED>;
   constexpr int W64 = C::W64, W32 = Width<R>::W32;
   constexpr int NB = C::NB;
   constexpr int PF = C::PF;
@@ -214,7 +222,40 @@ __global__ __launch_bounds__(kNT) void decode_step_kernel(const StepArgs a) {
   const int b = unit / a.Hkv, h = unit - b * a.Hkv;
   const int64_t cap = a.cap;
   const int k = a.k;
-  const int64_t row0 = ((int64_t)b * a.Hkv + h) * cap;
+  const int64_t row0 = PAGED ? 0 : ((int64_t)b * a.Hkv + h) * cap;
+  // PAGED: physical row of logical row r of this unit, for a uniform r (one
+  // scalar load of the page id; the page index is clamped into the table and
+  // the id into the pool)
+  auto prow = [&](int r) -> int64_t {
+    const int pg = min(r >> a.log2P, a.max_pages - 1);
+    const int pid = min(max(a.bt[(int64_t)b * a.max_pages + pg], 0), a.num_pages - 1);
+    return (((int64_t)pid * a.Hkv + h) << a.log2P) + (r & ((1 << a.log2P) - 1));
+  };
+  int32_t* pgl = reinterpret_cast<int32_t*>(smem + C::o_pgl);  // PAGED: the chunk's page ids
+  int pgv = 0;  // PAGED: this thread's page id of the chunk (t < pages), stored with the staging
+  // PAGED: page ids of the chunk's 256-row batches l and l + 64 in lane l of
+  // every wave (a chunk has at most 128 batches), so a ring refill takes its
+  // id with a readlane instead of a scalar load, whose wait would also drain
+  // the scan's LDS atomics
+  int bpid0 = 0, bpid1 = 0;
+  if constexpr (PAGED) {
+    auto pid_of = [&](int r) {
+      const int pg = min(r >> a.log2P, a.max_pages - 1);
+      return min(max(a.bt[(int64_t)b * a.max_pages + pg], 0), a.num_pages - 1);
+    };
+    const int fp = (w * a.chunk) >> a.log2P;
+    const int npg = ((w * a.chunk + a.chunk - 1) >> a.log2P) - fp + 1;
+    if (t < npg) pgv = pid_of((fp + t) << a.log2P);
+    bpid0 = pid_of(w * a.chunk + lane * kNT);
+    bpid1 = pid_of(w * a.chunk + (lane + 64) * kNT);
+  }
+  // PAGED: physical row of the chunk's row lo + i for a uniform, 256-aligned
+  // i < 32768 + BATCH (batch i / 256 of the chunk)
+  auto prow_batch = [&](int lo_, int i) -> int64_t {
+    const int bi = i >> 8;
+    const int pid = __builtin_amdgcn_readlane(bi < 64 ? bpid0 : bpid1, bi & 63);
+    return (((int64_t)pid * a.Hkv + h) << a.log2P) + ((lo_ + i) & ((1 << a.log2P) - 1));
+  };
 
   // ---- 1. loads.  The query rows, W_H, this workgroup's flag, the first
   // PF*256 rows of its code chunk and its exchange lines do not depend on
@@ -245,8 +286,18 @@ __global__ __launch_bounds__(kNT) void decode_step_kernel(const StepArgs a) {
   // (rows past the sequence end are loaded and never scored)
   const uint64_t* cunit = a.codes + row0 * W64;
   CodeRow<R> cbuf[PF];
+  if constexpr (PAGED) {
+    // a 256-row batch lies in one page (pages of >= 256 rows, lo a multiple
+    // of 256); batches past the table load its last full batch (never scored)
 #pragma unroll
-  for (int j = 0; j < PF; ++j) cbuf[j] = load_code<R>(cunit, min((int64_t)lo + j * kNT + t, cap - 1));
+    for (int j = 0; j < PF; ++j) {
+      const int rb = (int)min((int64_t)lo + j * kNT, cap - kNT);
+      cbuf[j] = load_code<R>(a.codes, prow(rb) + t);
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < PF; ++j) cbuf[j] = load_code<R>(cunit, min((int64_t)lo + j * kNT + t, cap - 1));
+  }
   // This workgroup's exchange lines (its histogram window and its partial
   // record) have usually left L2 since the previous step; the unit's first
   // reads of them after the flag take about 1 us then, against about 0.4 us
@@ -278,7 +329,8 @@ __global__ __launch_bounds__(kNT) void decode_step_kernel(const StepArgs a) {
   const bool owns_new = (n - 1 >= lo) && (n - 1 < lo + cnt);
   const int new_li = n - 1 - lo;
   // row n-1 of K (row 0 when this workgroup does not own it): dword `lane`
-  const uint32_t krow = reinterpret_cast<const uint32_t*>(a.K + (row0 + (owns_new ? n - 1 : 0)) * kD)[lane];
+  const int64_t krow_at = PAGED ? prow(owns_new ? n - 1 : 0) : row0 + (owns_new ? n - 1 : 0);
+  const uint32_t krow = reinterpret_cast<const uint32_t*>(a.K + krow_at * kD)[lane];
   // ring refills: rows lo + li for li < cnt
   const uint64_t* cbase = cunit + (int64_t)(cnt > 0 ? lo : 0) * W64;
 
@@ -294,6 +346,8 @@ __global__ __launch_bounds__(kNT) void decode_step_kernel(const StepArgs a) {
   }
   for (int i = t; i < C::NBP; i += kNT) hist[i] = 0;
   if (t < 64) misc[t] = (t < 3) ? (uint32_t)NB : 0u;
+  if constexpr (PAGED)
+    if (t < kMaxPgl) pgl[t] = pgv;
   __syncthreads();
   project_pack<G, R>(wr, qf, red, qcode, G);
   if constexpr (SEP) {
@@ -340,7 +394,10 @@ __global__ __launch_bounds__(kNT) void decode_step_kernel(const StepArgs a) {
     for (int j = 0; j < PF; ++j) {
       const int li = base + j * kNT + t;
       score_one(cbuf[j], li);
-      cbuf[j] = load_code<R>(cbase, li + BATCH);
+      if constexpr (PAGED)
+        cbuf[j] = load_code<R>(a.codes, prow_batch(lo, base + j * kNT + BATCH) + t);
+      else
+        cbuf[j] = load_code<R>(cbase, li + BATCH);
     }
   }
   if (base + BATCH <= cnt) {  // a full batch, the next one partial or empty
@@ -348,7 +405,12 @@ __global__ __launch_bounds__(kNT) void decode_step_kernel(const StepArgs a) {
     for (int j = 0; j < PF; ++j) {
       const int li = base + j * kNT + t;
       score_one(cbuf[j], li);
-      if (li + BATCH < cnt) cbuf[j] = load_code<R>(cbase, li + BATCH);
+      if constexpr (PAGED) {
+        const int64_t rb = prow_batch(lo, base + j * kNT + BATCH);
+        if (li + BATCH < cnt) cbuf[j] = load_code<R>(a.codes, rb + t);
+      } else {
+        if (li + BATCH < cnt) cbuf[j] = load_code<R>(cbase, li + BATCH);
+      }
     }
     base += BATCH;
   }
@@ -370,7 +432,7 @@ __global__ __launch_bounds__(kNT) void decode_step_kernel(const StepArgs a) {
     }
     __syncthreads();
     project_pack<1, R>(wr, qf + G * kD, red, qcode + G * W64, 1);
-    if (t < W64) a.codes[(row0 + n - 1) * W64 + t] = qcode[G * W64 + t];
+    if (t < W64) a.codes[(PAGED ? prow(n - 1) : row0 + n - 1) * W64 + t] = qcode[G * W64 + t];
     if (t == new_li % kNT) {
       uint32_t cw[W32];
 #pragma unroll
@@ -643,11 +705,19 @@ __global__ __launch_bounds__(kNT) void decode_step_kernel(const StepArgs a) {
   // kShortList rows staged in LDS, the next batch's loads in flight while a
   // batch is used, waves assigned to heads; G = 1: rows gathered straight
   // into registers, three steps of 64 rows in flight)
-  if constexpr (G == 1)
-    attend_rows_g1<4, 3>(qf, sel, m_self, n, a.K + row0 * kD, a.V + row0 * kD, a.scale, red);
-  else
-    attend_heads<G, kShortList>(qf, sel, m_self, n, a.K + row0 * kD, a.V + row0 * kD, a.scale, red,
-                                reinterpret_cast<uint4*>(kvs));
+  if constexpr (PAGED) {
+    const PagedRows map{pgl, (w * a.chunk) >> a.log2P, a.log2P, a.Hkv, h, kMaxPgl - 1};
+    if constexpr (G == 1)
+      attend_rows_g1<4, 3>(qf, sel, m_self, n, a.K, a.V, a.scale, red, map);
+    else
+      attend_heads<G, kShortList>(qf, sel, m_self, n, a.K, a.V, a.scale, red, reinterpret_cast<uint4*>(kvs), map);
+  } else {
+    if constexpr (G == 1)
+      attend_rows_g1<4, 3>(qf, sel, m_self, n, a.K + row0 * kD, a.V + row0 * kD, a.scale, red);
+    else
+      attend_heads<G, kShortList>(qf, sel, m_self, n, a.K + row0 * kD, a.V + row0 * kD, a.scale, red,
+                                  reinterpret_cast<uint4*>(kvs));
+  }
 
   // kept indices, written once the attention no longer needs the LDS list
   // (coalesced, and no barrier waits on these stores)
@@ -885,18 +955,18 @@ StepPlan plan_decode_step(int B, int Hq, int Hkv, int64_t max_len, int k, int nu
   return p;
 }
 
-template <int G, bool SEP, int R>
+template <int G, bool SEP, int R, bool PAGED = false>
 static hipError_t launch_step_gsr(const StepPlan& p, const StepArgs& a, hipStream_t s) {
-  const size_t lds = p.lds_bytes;
+  const size_t lds = p.lds_bytes + (PAGED ? kMaxPgl * 4 : 0);
   // raise the kernel's dynamic-LDS limit when a plan needs more than 64 KiB
   static std::atomic<size_t> configured{64 * 1024};
   if (lds > configured.load()) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&decode_step_kernel<G, SEP, R>),
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&decode_step_kernel<G, SEP, R, PAGED>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
     configured.store(lds);
   }
-  hipLaunchKernelGGL((decode_step_kernel<G, SEP, R>), dim3(p.U * p.Wg), dim3(kNT), lds, s, a);
+  hipLaunchKernelGGL((decode_step_kernel<G, SEP, R, PAGED>), dim3(p.U * p.Wg), dim3(kNT), lds, s, a);
   return hipGetLastError();
 }
 
@@ -930,12 +1000,43 @@ hipError_t launch_decode_step(const StepPlan& p, const uint16_t* q, const uint16
   a.full = p.Wg > 1 ? reinterpret_cast<uint32_t*>(ws + p.off_full) : nullptr;
   a.part = p.Wg > 1 ? reinterpret_cast<float*>(ws + p.off_part) : nullptr;
   a.full_words = p.full_words;
+  a.bt = nullptr; a.max_pages = 0; a.num_pages = 0; a.log2P = 0;
   (void)B;
   switch (p.G) {
     case 1: return launch_step_g<1>(p, a, s);
     case 2: return launch_step_g<2>(p, a, s);
     case 4: return launch_step_g<4>(p, a, s);
     case 8: return launch_step_g<8>(p, a, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+bool decode_step_paged_fusable(const StepPlan& p, int page_rows) {
+  return p.fused && p.R == 128 && page_rows >= kNT && p.lds_bytes + kMaxPgl * 4 <= 159 * 1024;
+}
+
+hipError_t launch_decode_step_paged(const StepPlan& p, const uint16_t* q, const uint16_t* K, const uint16_t* V,
+                                    const float* W, uint64_t* codes, const PageMap& pm, int Hq, int Hkv,
+                                    const int32_t* seq_lens, int k, float scale, float* out, int32_t* idx_out,
+                                    unsigned char* ws, hipStream_t s) {
+  if (!decode_step_paged_fusable(p, 1 << pm.log2P)) return hipErrorInvalidValue;
+  StepArgs a;
+  a.q = q; a.K = K; a.V = V; a.W = W; a.Wk = W; a.codes = codes; a.seq_lens = seq_lens;
+  a.out = out; a.idx_out = idx_out; a.cap = (int64_t)pm.max_pages << pm.log2P; a.Hq = Hq; a.Hkv = Hkv; a.k = k;
+  a.scale = scale; a.Wg = p.Wg; a.chunk = p.chunk; a.xcd_map = p.xcd_map; a.U = p.U;
+  a.xcd_local = (p.xcd_map && p.Wg > 1 && xcd_round_robin(s)) ? 1 : 0;
+  a.err = reinterpret_cast<uint32_t*>(ws + p.off_err);
+  a.flags = reinterpret_cast<uint32_t*>(ws + p.off_flags);
+  a.win = p.Wg > 1 ? reinterpret_cast<uint32_t*>(ws + p.off_win) : nullptr;
+  a.full = p.Wg > 1 ? reinterpret_cast<uint32_t*>(ws + p.off_full) : nullptr;
+  a.part = p.Wg > 1 ? reinterpret_cast<float*>(ws + p.off_part) : nullptr;
+  a.full_words = p.full_words;
+  a.bt = pm.bt; a.max_pages = pm.max_pages; a.num_pages = pm.num_pages; a.log2P = pm.log2P;
+  switch (p.G) {
+    case 1: return launch_step_gsr<1, false, 128, true>(p, a, s);
+    case 2: return launch_step_gsr<2, false, 128, true>(p, a, s);
+    case 4: return launch_step_gsr<4, false, 128, true>(p, a, s);
+    case 8: return launch_step_gsr<8, false, 128, true>(p, a, s);
     default: return hipErrorInvalidValue;
   }
 }

@@ -600,10 +600,28 @@ __device__ __forceinline__ void finish_heads(const SoftmaxState<(G >= 4) ? G / 4
 // Row ids past the list are clamped to its last row, so every load is issued
 // unconditionally (the compiler can count them exactly) and the extra rows
 // are masked out of the softmax.  Same output as attend_heads<1, ...>.
-template <int UN, int NPF>
+// Row map of the gather: cache row of a kept token (the identity for a
+// contiguous cache).
+struct SameRows {
+  __device__ __forceinline__ int64_t operator()(int64_t tok) const { return tok; }
+};
+// Paged cache: token tok of KV head h lives in page pgl[tok / P - fp] (the
+// page ids of a workgroup's chunk, held in LDS, all valid pool pages) of a
+// pool laid out [pages][Hkv][P][128]; the LDS index is clamped into the
+// list, so even a stray token id maps into the pool.
+struct PagedRows {
+  const int32_t* pgl;
+  int fp, log2P, Hkv, h, last;
+  __device__ __forceinline__ int64_t operator()(int64_t tok) const {
+    const int i = min(max((int)(tok >> log2P) - fp, 0), last);
+    return (((int64_t)pgl[i] * Hkv + h) << log2P) + (tok & ((int64_t(1) << log2P) - 1));
+  }
+};
+
+template <int UN, int NPF, class Map = SameRows>
 __device__ __forceinline__ void attend_rows_g1(const float* qf, const int32_t* sel, int m, int n,
                                                const uint16_t* K, const uint16_t* V, float scale,
-                                               float* red) {
+                                               float* red, const Map& map = Map()) {
   const int t = threadIdx.x, lane = t & 63, wv = t >> 6, rg = lane >> 4, sub = lane & 15;
   const int grp = wv * 4 + rg;
   float qreg[1][8];
@@ -618,7 +636,7 @@ __device__ __forceinline__ void attend_rows_g1(const float* qf, const int32_t* s
     for (int u = 0; u < UN; ++u) tok[u] = sel[max(min((step * UN + u) * 16 + grp, m - 1), 0)];
 #pragma unroll
     for (int u = 0; u < UN; ++u) {
-      const int64_t off = (int64_t)min(max(tok[u], 0), n - 1) * kD + sub * 8;
+      const int64_t off = map((int64_t)min(max(tok[u], 0), n - 1)) * kD + sub * 8;
       kk[u] = *reinterpret_cast<const uint4*>(K + off);
       vv[u] = *reinterpret_cast<const uint4*>(V + off);
     }
@@ -653,10 +671,10 @@ __device__ __forceinline__ void attend_rows_g1(const float* qf, const int32_t* s
 // merge is needed for G >= 4.  kvs: LDS of MAXR * 512 bytes.  Writes
 // red[g*kRec + {M, L, A[128]}] (red holds at least (G + 4) * kRec floats);
 // ends with __syncthreads.
-template <int G, int MAXR>
+template <int G, int MAXR, class Map = SameRows>
 __device__ __forceinline__ void attend_heads(const float* qf, const int32_t* sel, int m, int n,
                                              const uint16_t* K, const uint16_t* V, float scale,
-                                             float* red, uint4* kvs) {
+                                             float* red, uint4* kvs, const Map& map = Map()) {
   constexpr int HPW = (G >= 4) ? G / 4 : 1;  // heads per wave
   constexpr int WPH = (G >= 4) ? 1 : 4 / G;  // waves per head
   constexpr int LPT = MAXR * 32 / kNT;       // staging loads per thread and batch
@@ -673,7 +691,7 @@ __device__ __forceinline__ void attend_heads(const float* qf, const int32_t* sel
       v[i] = make_uint4(0, 0, 0, 0);
       if (r < mb) {
         const int64_t tok = min(max(tokv[i], 0), n - 1);
-        const uint16_t* src = (part16 < 16 ? K : V) + tok * kD + (part16 & 15) * 8;
+        const uint16_t* src = (part16 < 16 ? K : V) + map(tok) * kD + (part16 & 15) * 8;
         v[i] = *reinterpret_cast<const uint4*>(src);
       }
     }

@@ -78,6 +78,14 @@ hipError_t launch_decode_step(const StepPlan& p, const uint16_t* q, const uint16
                               int Hkv, int64_t cap, const int32_t* seq_lens, int k, float scale,
                               float* out, int32_t* idx_out, unsigned char* ws, hipStream_t s);
 
+// The fused step over a paged cache (K, V, codes in page pools, pm): plans
+// whose step is fused, r = 128 and pages of at least 256 rows.
+bool decode_step_paged_fusable(const StepPlan& p, int page_rows);
+hipError_t launch_decode_step_paged(const StepPlan& p, const uint16_t* q, const uint16_t* K, const uint16_t* V,
+                                    const float* W, uint64_t* codes, const PageMap& pm, int Hq, int Hkv,
+                                    const int32_t* seq_lens, int k, float scale, float* out, int32_t* idx_out,
+                                    unsigned char* ws, hipStream_t s);
+
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s);
 
 // ---------------------------------------------------------------- prefill

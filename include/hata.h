@@ -237,11 +237,15 @@ int hata_prefill(const void* q, const void* K, const void* V,
  * Same steps and results as hata_decode_step on the gathered contiguous
  * cache: the key row n_b-1 is encoded and its code written through the
  * table, every code row 0..n_b-1 is scored, top-k by (score, index), and
- * the attention gathers the kept K/V rows through the table.  Runs as
- * separate kernels (row encode, Hamming scan, top-k, gather attention).
- * page_rows a power of two in [16, 65536]; q, the pools 16-byte aligned;
- * idx_out [B][Hkv][k] optional.  ws: hata_workspace_bytes(
- * HATA_OP_DECODE_STEP_PAGED, ...) (contents need no initialisation).
+ * the attention gathers the kept K/V rows through the table.  With pages
+ * of at least 256 rows, r = 128 and a shape whose step fits on chip, the
+ * step runs as hata_decode_step's single kernel (each 256-row batch of
+ * codes lies in one page; page ids come from the table with the first
+ * loads); otherwise as separate kernels (row encode, Hamming scan, top-k,
+ * gather attention).  page_rows a power of two in [16, 65536]; q, the pools
+ * 16-byte aligned; idx_out [B][Hkv][k] optional.  ws: hata_workspace_bytes(
+ * HATA_OP_DECODE_STEP_PAGED, ...), zeroed once before first use (as for
+ * hata_decode_step).
  */
 int hata_decode_step_paged(const void* q, const void* K_pool,
                            const void* V_pool, const float* W_H,

@@ -110,3 +110,49 @@ def test_paged_step_matches_oracle_and_contiguous_step(hata_gpu, case):
         assert torch.equal(codes[b, :, :n], got_codes[b, :, :n])
     assert torch.equal(idx, cidx)
     assert_close(out.cpu().numpy(), cout.cpu().numpy(), "paged vs contiguous")
+
+
+FUSED_CASES = [
+    # B, Hq, Hkv, N, lens, k, P, spare pages
+    (1, 32, 8, 20000, [20000], 512, 256, 5),      # several workgroups per unit (exchange path)
+    (1, 32, 8, 20000, [20000], 512, 1024, 0),
+    (2, 8, 8, 5000, [5000, 777], 64, 512, 2),      # G = 1
+    (2, 64, 8, 3000, [3000, 1], 128, 256, 1),      # G = 8, a one-token sequence
+]
+
+
+@pytest.mark.parametrize("case", FUSED_CASES, ids=[f"P{c[6]}-G{c[1] // c[2]}-N{c[3]}" for c in FUSED_CASES])
+def test_fused_paged_step_equals_contiguous_step_bitwise(hata_gpu, case):
+    """With pages of >= 256 rows and 128-bit codes the paged step runs the
+    fused kernel; it differs from the contiguous one only in its addresses,
+    so codes, kept set and output must be bit-identical."""
+    B, Hq, Hkv, N, lens, k, P, spare = case
+    _log(f"fused paged B={B} Hq={Hq} Hkv={Hkv} lens={lens} k={k} P={P}")
+    s = synth.Shape(f"fpaged-{B}-{Hq}-{Hkv}-{N}", B=B, Hq=Hq, Hkv=Hkv, N=N, k=k, dist="gauss",
+                    seed_base=7900 + P, outliers=4, needles=8)
+    inp = synth.make_inputs(s, seq_lens=np.array(lens, np.int32))
+    d = Dev(inp)
+    codes = gpu_build_cache(hata_gpu, d)
+    mp = (d.cap + P - 1) // P
+    num_pages = B * mp + spare
+    perm = np.random.default_rng(7901 + P).permutation(num_pages)[:B * mp].astype(np.int32)
+    bt = torch.from_numpy(perm.reshape(B, mp)).cuda()
+    Kp = _paginate(d.K, P, bt, num_pages)
+    Vp = _paginate(d.V, P, bt, num_pages)
+    Cp = _paginate(codes, P, bt, num_pages, fill=0x1234)
+    ws = hata_gpu.alloc_workspace(hata_gpu.OP_DECODE_STEP_PAGED, B, Hq, Hkv, d.max_len, k)
+    out = torch.zeros((B, Hq, 128), dtype=torch.float32, device="cuda")
+    idx = torch.zeros((B, Hkv, k), dtype=torch.int32, device="cuda")
+    for rep in range(2):  # the workspace's flags carry over between calls
+        hata_gpu.decode_step_paged(d.q, Kp, Vp, d.W, Cp, bt, d.seq, d.max_len, k, inp.scale, out, ws, idx_out=idx)
+    cws = hata_gpu.alloc_workspace(hata_gpu.OP_DECODE_STEP, B, Hq, Hkv, d.max_len, k)
+    cout = torch.zeros_like(out)
+    cidx = torch.zeros_like(idx)
+    hata_gpu.decode_step(d.q, d.K, d.V, d.W, codes, d.seq, d.max_len, k, inp.scale, cout, cws, cidx)
+    torch.cuda.synchronize()
+    assert hata_gpu.workspace_check(ws) == 0
+    got_codes = _gather(Cp, bt, d.cap)
+    for b, n in enumerate(lens):
+        assert torch.equal(codes[b, :, :n], got_codes[b, :, :n])
+    assert torch.equal(idx, cidx)
+    assert torch.equal(out, cout)
