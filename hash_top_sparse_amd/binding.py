@@ -64,6 +64,7 @@ def load() -> ctypes.CDLL:
         "hata_hash_train_workspace_bytes": ([I, I, I, I], SZ),
         "hata_prefill": ([P, P, P, P, P, I, I, I, I, I, I64, I64, P, I64, F, P, P], I),
         "hata_decode_step_paged": ([P, P, P, P, P, P, I, I, I, I, I, I, I, I, P, I64, I, F, P, P, P, SZ, P], I),
+        "hata_prefill_paged": ([P, P, P, P, P, P, I, I, I, I, I, I, I, I, I64, P, I64, F, P, P], I),
     }
     for name, (args, res) in sig.items():
         fn = getattr(L, name)
@@ -80,7 +81,8 @@ def exported_symbols() -> list[str]:
                         "hata_dense_decode",
                         "hata_workspace_bytes", "hata_workspace_reset", "hata_workspace_check",
                         "hata_stream_read", "hata_hash_labels", "hata_hash_train_step",
-                        "hata_hash_train_workspace_bytes", "hata_prefill", "hata_decode_step_paged")
+                        "hata_hash_train_workspace_bytes", "hata_prefill", "hata_decode_step_paged",
+                        "hata_prefill_paged")
             if hasattr(load(), n)]
 
 
@@ -236,6 +238,26 @@ def decode_step_paged(q: torch.Tensor, K_pool: torch.Tensor, V_pool: torch.Tenso
                                          _ptr(block_table), block_table.shape[1], num_pages, P, B, Hq, Hkv, d, r,
                                          _ptr(seq_lens), int(max_len), int(k), float(scale), _ptr(out),
                                          _ptr(idx_out), _ptr(ws), ws.numel(), _stream(stream)))
+
+
+def prefill_paged(q: torch.Tensor, K_pool: torch.Tensor, V_pool: torch.Tensor, W_H: torch.Tensor,
+                  code_pool: torch.Tensor, block_table: torch.Tensor, seq_lens: torch.Tensor, max_len: int,
+                  scale: float, out: torch.Tensor, stream=None) -> None:
+    """hata_prefill into page pools: q bf16 [B,Hq,q_rows,d]; K_pool, V_pool bf16 [pages,Hkv,P,d];
+    code_pool int64 [pages,Hkv,P,ceil(r/64)]; block_table int32 [B,max_pages]; out f32 [B,Hq,q_rows,d]."""
+    for t, n in ((q, "q"), (K_pool, "K_pool"), (V_pool, "V_pool")):
+        _need(t, torch.bfloat16, n)
+    _need(W_H, torch.float32, "W_H")
+    _need(code_pool, torch.int64, "code_pool")
+    _need(block_table, torch.int32, "block_table")
+    _need(seq_lens, torch.int32, "seq_lens")
+    _need(out, torch.float32, "out")
+    B, Hq, q_rows, d = q.shape
+    num_pages, Hkv, P, _ = K_pool.shape
+    r = W_H.shape[2]
+    _check(load().hata_prefill_paged(_ptr(q), _ptr(K_pool), _ptr(V_pool), _ptr(W_H), _ptr(code_pool),
+                                     _ptr(block_table), block_table.shape[1], num_pages, P, B, Hq, Hkv, d, r, q_rows,
+                                     _ptr(seq_lens), int(max_len), float(scale), _ptr(out), _stream(stream)))
 
 
 def stream_read(src: torch.Tensor, sink: torch.Tensor, stream=None) -> None:

@@ -449,6 +449,47 @@ int hata_prefill(const void* q, const void* K, const void* V, const float* W_H, 
   return check_launch(e, "prefill launch");
 }
 
+int hata_prefill_paged(const void* q, const void* K_pool, const void* V_pool, const float* W_H,
+                       uint64_t* code_pool, const int32_t* block_table, int max_pages, int num_pages, int page_rows,
+                       int B, int Hq, int Hkv, int d, int r, int64_t q_rows, const int32_t* seq_lens,
+                       int64_t max_len, float scale, float* out, void* stream) {
+  if (!q || !K_pool || !V_pool || !W_H || !code_pool || !block_table || !seq_lens || !out)
+    return fail(HATA_ERR_NULL, "prefill_paged: null pointer");
+  int st = check_dims(d, r);
+  if (st) return st;
+  if ((st = check_heads(B, Hq, Hkv))) return st;
+  if (page_rows < 16 || page_rows > 65536 || (page_rows & (page_rows - 1)) != 0)
+    return fail(HATA_ERR_UNSUPPORTED, "prefill_paged: page_rows=%d not a power of two in [16, 65536]", page_rows);
+  if (max_pages < 1 || num_pages < 1)
+    return fail(HATA_ERR_SHAPE, "prefill_paged: max_pages=%d, num_pages=%d must be >= 1", max_pages, num_pages);
+  const int64_t cap = (int64_t)max_pages * page_rows;
+  if ((st = check_len(cap, max_len))) return st;
+  if (q_rows < max_len)
+    return fail(HATA_ERR_SHAPE, "prefill_paged: q_rows=%lld below max_len=%lld", (long long)q_rows,
+                (long long)max_len);
+  if (!aligned(q, 16) || !aligned(K_pool, 16) || !aligned(V_pool, 16) || !aligned(out, 16))
+    return fail(HATA_ERR_ALIGN, "prefill_paged: q, K_pool, V_pool and out must be 16-byte aligned");
+  if (!aligned(code_pool, 8) || !aligned(W_H, 4) || !aligned(seq_lens, 4) || !aligned(block_table, 4))
+    return fail(HATA_ERR_ALIGN, "prefill_paged: code_pool must be 8-byte, W_H, seq_lens and block_table 4-byte aligned");
+  const int G = Hq / Hkv;
+  const int64_t blocks = (max_len + hata::prefill_positions_per_block(G) - 1) / hata::prefill_positions_per_block(G);
+  if (blocks * B * Hkv > ((int64_t)1 << 31) - 1)
+    return fail(HATA_ERR_SHAPE, "prefill_paged: grid of %lld workgroups too large", (long long)(blocks * B * Hkv));
+  if ((st = pre_launch("prefill_paged"))) return st;
+  hata::PageMap pm;
+  pm.bt = block_table;
+  pm.max_pages = max_pages;
+  pm.num_pages = num_pages;
+  int lg = 0;
+  while ((1 << lg) < page_rows) ++lg;
+  pm.log2P = lg;
+  hipError_t e = hata::launch_prefill(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(K_pool),
+                                      static_cast<const uint16_t*>(V_pool), W_H, code_pool, B, Hq, Hkv, q_rows, cap,
+                                      seq_lens, (int)max_len, scale, out, r, reinterpret_cast<hipStream_t>(stream),
+                                      &pm);
+  return check_launch(e, "prefill_paged launch");
+}
+
 size_t hata_hash_train_workspace_bytes(int J, int n, int d, int r) {
   if (J < 1 || n < 1 || d != 128 || r < 32 || r > 256 || r % 32 != 0) return 0;
   return hata::plan_train(J, n, r).total;

@@ -93,12 +93,13 @@ hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s);
 // at positions 0..n_b-1, keys/values [B][Hkv][cap][128]) into out fp32
 // [B][Hq][q_rows][128], with code rows 0..n_b-1 written to codes
 // [B][Hkv][cap][r/64 rounded up]; n_b = min(seq_lens[b], max_len).
-// G = Hq / Hkv in {1, 2, 4, 8}, r in {32, 64, 128, 256}.
+// G = Hq / Hkv in {1, 2, 4, 8}, r in {32, 64, 128, 256}.  pm (optional): K, V
+// and codes are page pools addressed through it (cap = max_pages * P).
 int prefill_positions_per_block(int G);
 hipError_t launch_prefill(const uint16_t* q, const uint16_t* K, const uint16_t* V, const float* W,
                           uint64_t* codes, int B, int Hq, int Hkv, int64_t q_rows, int64_t cap,
                           const int32_t* seq_lens, int max_len, float scale, float* out, int r,
-                          hipStream_t s);
+                          hipStream_t s, const PageMap* pm = nullptr);
 
 // training step of the hash weights (train.hip)
 constexpr int kMaxLabelKeys = 8192;  // keys a label row may rank (LDS sort)

@@ -64,6 +64,7 @@ struct PrefillArgs {
   int64_t q_rows, cap;
   int max_len, nqb;
   float scale_log2;
+  PageMap pm;  // PAGED: K, V and codes are page pools addressed through it
 };
 
 __device__ __forceinline__ uint32_t half16(const uint4& v, int e) {
@@ -71,7 +72,9 @@ __device__ __forceinline__ uint32_t half16(const uint4& v, int e) {
   return (e & 1) ? (w >> 16) : (w & 0xFFFFu);
 }
 
-template <int G, int R>
+// PAGED: K, V and codes are page pools (a.pm); a separate instance, the
+// contiguous code is unchanged.
+template <int G, int R, bool PAGED>
 __global__ __launch_bounds__(kNT, 2) void prefill_kernel(PrefillArgs a) {
   constexpr int QP = 128 / G;         // positions per workgroup
   constexpr int W64 = Width<R>::W64;  // 64-bit words per code row
@@ -131,6 +134,17 @@ __global__ __launch_bounds__(kNT, 2) void prefill_kernel(PrefillArgs a) {
   const int koff = (t >> 4) * kD + (t & 15) * 8;
   const int voff = 4 * vkg * kD + vc * 8;
   auto fetch = [&](int tile) {
+    if constexpr (PAGED) {  // every row through the block table (any page size)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int kr = tile * kBK + (t >> 4) + 16 * i, vr = tile * kBK + 4 * vkg + i;
+        kreg[i] = kr < L ? *reinterpret_cast<const uint4*>(a.K + a.pm.row(b, hk, a.Hkv, kr) * kD + (t & 15) * 8)
+                         : make_uint4(0, 0, 0, 0);
+        vreg[i] = vr < L ? *reinterpret_cast<const uint4*>(a.V + a.pm.row(b, hk, a.Hkv, vr) * kD + vc * 8)
+                         : make_uint4(0, 0, 0, 0);
+      }
+      return;
+    }
     const uint16_t* kt = Kh + (int64_t)tile * kBK * kD;
     const uint16_t* vtl = Vh + (int64_t)tile * kBK * kD;
     if (tile * kBK + kBK <= L) {  // a full tile (all but possibly the last)
@@ -310,8 +324,8 @@ __global__ __launch_bounds__(kNT, 2) void prefill_kernel(PrefillArgs a) {
       for (int i = 0; i < 4; ++i) {
         const int id = t + kNT * i, key = id >> 4, c = id & 15;
         const int row = k0 + key;
-        const uint4 v = row < L ? *reinterpret_cast<const uint4*>(Kh + (int64_t)row * kD + c * 8)
-                                : make_uint4(0, 0, 0, 0);
+        const int64_t at = PAGED ? a.pm.row(b, hk, a.Hkv, row) : (int64_t)row + kvoff / kD;
+        const uint4 v = row < L ? *reinterpret_cast<const uint4*>(a.K + at * kD + c * 8) : make_uint4(0, 0, 0, 0);
         *reinterpret_cast<uint4*>(ks + key * kKsStride + c * 8) = v;
       }
       __syncthreads();
@@ -367,32 +381,46 @@ __global__ __launch_bounds__(kNT, 2) void prefill_kernel(PrefillArgs a) {
     const int row = e / W64, w = e - row * W64;
     const uint64_t lo = cw[row * CT + 2 * w];
     const uint64_t hi = (2 * w + 1 < CT) ? cw[row * CT + 2 * w + 1] : 0u;
-    crow[e] = lo | (hi << 32);
+    if constexpr (PAGED)
+      a.codes[a.pm.row(b, hk, a.Hkv, p0 + row) * W64 + w] = lo | (hi << 32);
+    else
+      crow[e] = lo | (hi << 32);
   }
 }
 
-template <int G, int R>
+template <int G, int R, bool PAGED>
 hipError_t launch_gr(const PrefillArgs& a, hipStream_t s) {
   constexpr size_t lds = prefill_lds_bytes<G, R>();
   static bool configured = false;  // dynamic LDS above 64 KiB needs an opt-in per kernel
   if (!configured) {
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&prefill_kernel<G, R>),
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&prefill_kernel<G, R, PAGED>),
                                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
     configured = true;
   }
   const dim3 grid((unsigned)((int64_t)a.nqb * a.B * a.Hkv));
-  hipLaunchKernelGGL((prefill_kernel<G, R>), grid, dim3(kNT), lds, s, a);
+  hipLaunchKernelGGL((prefill_kernel<G, R, PAGED>), grid, dim3(kNT), lds, s, a);
   return hipGetLastError();
 }
 
-template <int G>
+template <int G, bool PAGED>
 hipError_t launch_g(const PrefillArgs& a, int r, hipStream_t s) {
   switch (r) {
-    case 32: return launch_gr<G, 32>(a, s);
-    case 64: return launch_gr<G, 64>(a, s);
-    case 128: return launch_gr<G, 128>(a, s);
-    case 256: return launch_gr<G, 256>(a, s);
+    case 32: return launch_gr<G, 32, PAGED>(a, s);
+    case 64: return launch_gr<G, 64, PAGED>(a, s);
+    case 128: return launch_gr<G, 128, PAGED>(a, s);
+    case 256: return launch_gr<G, 256, PAGED>(a, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <bool PAGED>
+hipError_t launch_p(const PrefillArgs& a, int G, int r, hipStream_t s) {
+  switch (G) {
+    case 1: return launch_g<1, PAGED>(a, r, s);
+    case 2: return launch_g<2, PAGED>(a, r, s);
+    case 4: return launch_g<4, PAGED>(a, r, s);
+    case 8: return launch_g<8, PAGED>(a, r, s);
     default: return hipErrorInvalidValue;
   }
 }
@@ -404,20 +432,19 @@ int prefill_positions_per_block(int G) { return 128 / G; }
 hipError_t launch_prefill(const uint16_t* q, const uint16_t* K, const uint16_t* V, const float* W,
                           uint64_t* codes, int B, int Hq, int Hkv, int64_t q_rows, int64_t cap,
                           const int32_t* seq_lens, int max_len, float scale, float* out, int r,
-                          hipStream_t s) {
+                          hipStream_t s, const PageMap* pm) {
   const int G = Hq / Hkv;
   PrefillArgs a;
   a.q = q; a.K = K; a.V = V; a.W = W; a.codes = codes; a.seq_lens = seq_lens; a.out = out;
   a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.q_rows = q_rows; a.cap = cap; a.max_len = max_len;
   a.nqb = (max_len + 128 / G - 1) / (128 / G);
   a.scale_log2 = scale * 1.4426950408889634f;
-  switch (G) {
-    case 1: return launch_g<1>(a, r, s);
-    case 2: return launch_g<2>(a, r, s);
-    case 4: return launch_g<4>(a, r, s);
-    case 8: return launch_g<8>(a, r, s);
-    default: return hipErrorInvalidValue;
+  if (pm && pm->bt) {
+    a.pm = *pm;
+    return launch_p<true>(a, G, r, s);
   }
+  a.pm = PageMap();
+  return launch_p<false>(a, G, r, s);
 }
 
 }  // namespace hata

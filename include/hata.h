@@ -224,6 +224,27 @@ int hata_prefill(const void* q, const void* K, const void* V,
                  float* out, void* stream);
 
 /*
+ * hata_prefill into a paged cache: the prompt's K/V rows are read from, and
+ * its code rows written to, pools addressed through a block table, as in
+ * hata_decode_step_paged (row j of sequence b lives in page
+ * block_table[b * max_pages + j / page_rows]; K_pool, V_pool bf16
+ * [num_pages][Hkv][page_rows][d], code_pool uint64
+ * [num_pages][Hkv][page_rows][ceil(r/64)]; page ids clamped into
+ * [0, num_pages)).  q and out keep hata_prefill's layouts.  The results are
+ * those of hata_prefill on the gathered contiguous cache (bit for bit; the
+ * same kernel reads its rows through the table).  page_rows a power of two
+ * in [16, 65536]; max_len <= max_pages * page_rows; alignments and errors
+ * as for hata_prefill.  No workspace.
+ */
+int hata_prefill_paged(const void* q, const void* K_pool, const void* V_pool,
+                       const float* W_H, uint64_t* code_pool,
+                       const int32_t* block_table, int max_pages,
+                       int num_pages, int page_rows, int B, int Hq, int Hkv,
+                       int d, int r, int64_t q_rows, const int32_t* seq_lens,
+                       int64_t max_len, float scale, float* out,
+                       void* stream);
+
+/*
  * hata_decode_step over a paged cache (the block-table layout of
  * PagedAttention, which the HATA notes build on; their decode step is
  * unchanged): row j of sequence b lives in page block_table[b * max_pages +

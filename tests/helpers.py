@@ -123,3 +123,22 @@ def assert_close(gpu: np.ndarray, ref: np.ndarray, what: str = "out"):
                              f"gpu={gpu[tuple(i)]} ref={ref[tuple(i)]}")
     big = np.abs(ref) > 1e-2
     return float(err.max()), float((err[big] / np.abs(ref[big])).max()) if big.any() else 0.0
+
+
+def paginate(x: torch.Tensor, P: int, bt: torch.Tensor, num_pages: int, fill=0) -> torch.Tensor:
+    """x [B, Hkv, cap, C] -> pool [num_pages, Hkv, P, C] with page bt[b, i]
+    holding rows [i P, (i + 1) P) of sequence b (unused pages keep `fill`)."""
+    B, Hkv, cap, C = x.shape
+    mp = bt.shape[1]
+    xp = torch.full((B, Hkv, mp * P, C), fill, dtype=x.dtype, device=x.device)
+    xp[:, :, :cap] = x
+    pool = torch.full((num_pages, Hkv, P, C), fill, dtype=x.dtype, device=x.device)
+    pool[bt.reshape(-1).long()] = xp.view(B, Hkv, mp, P, C).permute(0, 2, 1, 3, 4).reshape(B * mp, Hkv, P, C)
+    return pool
+
+
+def gather_pages(pool: torch.Tensor, bt: torch.Tensor, cap: int) -> torch.Tensor:
+    num_pages, Hkv, P, C = pool.shape
+    B, mp = bt.shape
+    g = pool[bt.reshape(-1).long()].view(B, mp, Hkv, P, C).permute(0, 2, 1, 3, 4).reshape(B, Hkv, mp * P, C)
+    return g[:, :, :cap]

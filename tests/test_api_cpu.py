@@ -252,6 +252,29 @@ def test_decode_step_paged_validation(lib):
     assert _paged(bt=MIS2) == EALIGN
 
 
+def _prefill_paged(**kw):
+    a = dict(q=A, K=A, V=A, W=A, codes=A, bt=A, max_pages=256, num_pages=300, P=16, B=1, Hq=32, Hkv=8, d=128,
+             r=128, q_rows=4096, seq=A, max_len=4096, out=A)
+    a.update(kw)
+    return binding.raw_call("hata_prefill_paged", a["q"], a["K"], a["V"], a["W"], a["codes"], a["bt"],
+                            a["max_pages"], a["num_pages"], a["P"], a["B"], a["Hq"], a["Hkv"], a["d"], a["r"],
+                            ctypes.c_int64(a["q_rows"]), a["seq"], ctypes.c_int64(a["max_len"]), F(0.088), a["out"],
+                            None)
+
+
+def test_prefill_paged_validation():
+    assert _prefill_paged(bt=None) == ENULL
+    assert _prefill_paged(codes=None) == ENULL
+    assert _prefill_paged(d=64) == EUNSUP
+    assert _prefill_paged(P=48) == EUNSUP
+    assert _prefill_paged(Hq=48, Hkv=4) == EUNSUP
+    assert _prefill_paged(max_pages=0) == ESHAPE
+    assert _prefill_paged(max_len=4097) == ESHAPE       # beyond max_pages * page_rows
+    assert _prefill_paged(q_rows=100) == ESHAPE
+    assert _prefill_paged(K=MIS) == EALIGN
+    assert _prefill_paged(bt=MIS2) == EALIGN
+
+
 def lib_stream_read_valid():
     return binding.load().hata_stream_read(A, ctypes.c_size_t(4096), A, ctypes.c_size_t(1024), P(None))
 
@@ -278,6 +301,7 @@ def test_forced_launch_failure_propagates():
         assert lib_stream_read_valid() == EHIP
         assert _prefill() == EHIP
         assert _paged() == EHIP
+        assert _prefill_paged() == EHIP
         with pytest.raises(binding.HataError) as ei:
             binding._check(_ham())
         assert ei.value.status == EHIP

@@ -9,32 +9,14 @@ import pytest
 import torch
 
 from hash_top_sparse_amd import synth
-from helpers import Dev, assert_close, check_codes, codes_np, gpu_build_cache, gpu_query_codes, oracle_units
+from helpers import (Dev, assert_close, check_codes, codes_np, gather_pages as _gather, gpu_build_cache,
+                     gpu_query_codes, oracle_units, paginate as _paginate)
 
 pytestmark = pytest.mark.gpu
 
 
 def _log(msg):
     print(msg, flush=True)
-
-
-def _paginate(x: torch.Tensor, P: int, bt: torch.Tensor, num_pages: int, fill=0) -> torch.Tensor:
-    """x [B, Hkv, cap, C] -> pool [num_pages, Hkv, P, C] with page bt[b, i]
-    holding rows [i P, (i + 1) P) of sequence b (unused pages keep `fill`)."""
-    B, Hkv, cap, C = x.shape
-    mp = bt.shape[1]
-    xp = torch.full((B, Hkv, mp * P, C), fill, dtype=x.dtype, device=x.device)
-    xp[:, :, :cap] = x
-    pool = torch.full((num_pages, Hkv, P, C), fill, dtype=x.dtype, device=x.device)
-    pool[bt.reshape(-1).long()] = xp.view(B, Hkv, mp, P, C).permute(0, 2, 1, 3, 4).reshape(B * mp, Hkv, P, C)
-    return pool
-
-
-def _gather(pool: torch.Tensor, bt: torch.Tensor, cap: int) -> torch.Tensor:
-    num_pages, Hkv, P, C = pool.shape
-    B, mp = bt.shape
-    g = pool[bt.reshape(-1).long()].view(B, mp, Hkv, P, C).permute(0, 2, 1, 3, 4).reshape(B, Hkv, mp * P, C)
-    return g[:, :, :cap]
 
 
 CASES = [

@@ -15,7 +15,7 @@ import pytest
 import torch
 
 from hash_top_sparse_amd import synth
-from helpers import bf16_tensor, check_codes, codes_np
+from helpers import bf16_tensor, check_codes, codes_np, gather_pages, paginate
 from oracle import prefill as oprefill
 
 pytestmark = pytest.mark.gpu
@@ -160,3 +160,47 @@ def test_prefill_full_size_sampled(hata_gpu):
     for h in range(Hkv):
         flips += check_codes(cn[0, h, rows], Kb[0, h, rows], Wn[h], False)
     _log(f"  sampled {len(pos)} rows x {Hq} heads, {len(rows)} code rows x {Hkv} heads, flips {flips}")
+
+
+PAGED_CASES = [
+    # page rows, G, r, lens, spare pages
+    (16, 4, 128, [300, 77], 3),
+    (64, 1, 64, [700], 1),
+    (256, 8, 256, [333], 0),
+    (32, 2, 128, [1, 130], 2),
+]
+
+
+@pytest.mark.parametrize("case", PAGED_CASES, ids=[f"P{c[0]}-G{c[1]}-r{c[2]}-{c[3]}" for c in PAGED_CASES])
+def test_paged_prefill_equals_contiguous_bitwise(hata_gpu, case):
+    """The prompt's K/V read from, and its codes written to, shuffled pages:
+    the same kernel through the block table, so outputs and codes are
+    bit-identical to the contiguous prefill; other pool rows untouched."""
+    P, G, r, lens, spare = case
+    B, Hkv = len(lens), (1 if G == 8 else 2)
+    Hq, q_rows, cap = G * Hkv, max(lens) + 3, max(lens) + 5
+    _log(f"paged prefill P={P} G={G} r={r} lens={lens}")
+    q, K, V, W = _inputs(B, Hq, Hkv, q_rows, cap, r, seed=8700 + P + r)
+    scale = 1.0 / np.sqrt(128.0)
+    out_c, codes_c = _run(hata_gpu, q, K, V, W, lens, max(lens), scale)
+    mp = (cap + P - 1) // P
+    num_pages = B * mp + spare
+    perm = np.random.default_rng(8701 + P).permutation(num_pages)[:B * mp].astype(np.int32)
+    bt = torch.from_numpy(perm.reshape(B, mp)).cuda()
+    words = (r + 63) // 64
+    Kp = paginate(bf16_tensor(K), P, bt, num_pages)
+    Vp = paginate(bf16_tensor(V), P, bt, num_pages)
+    Cp = paginate(torch.full((B, Hkv, cap, words), SENT_CODE, dtype=torch.int64, device="cuda"), P, bt, num_pages,
+                  fill=SENT_CODE)
+    out = torch.full((B, Hq, q_rows, 128), SENT_OUT, dtype=torch.float32, device="cuda")
+    hata_gpu.prefill_paged(bf16_tensor(q), Kp, Vp, torch.from_numpy(W).cuda(), Cp, bt,
+                           torch.from_numpy(np.asarray(lens, np.int32)).cuda(), max(lens), scale, out)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(out.cpu().numpy(), out_c)     # sentinels past each length included
+    got = codes_np(gather_pages(Cp, bt, cap))
+    np.testing.assert_array_equal(got, codes_c)
+    # pages no sequence owns keep their contents
+    used = set(perm.tolist())
+    for pg in range(num_pages):
+        if pg not in used:
+            assert (codes_np(Cp[pg]) == np.uint64(SENT_CODE)).all()
