@@ -97,10 +97,12 @@ __global__ __launch_bounds__(kLabNT) void labels_kernel(const uint16_t* __restri
 // lanes walk that index so the global reads coalesce.  64 x 64 output tiles,
 // 32-deep k steps staged in LDS (rows padded by 4 floats: 16-byte aligned
 // vector reads, conflict-free column writes), the next step's operands held
-// in registers while the current one is multiplied, 256 threads with 4 x 4
-// outputs each.  Products with few output tiles and a long k split k over
-// blockIdx.z; each split writes its own partial tile and a second kernel
-// adds the partials in split order (deterministic).
+// in registers while the current one is multiplied.  The 4 waves take the
+// tile's 32 x 32 quarters on v_mfma_f32_32x32x2_f32 (fp32 operands and
+// accumulation): per MFMA, lane l brings A(row l % 32, k 2 kk + l / 32) and
+// B(k 2 kk + l / 32, col l % 32).  Products with few output tiles and a
+// long k split k over blockIdx.z; each split writes its own partial tile and
+// a second kernel adds the partials in split order (deterministic).
 struct AccF32 {  // row-major [rows][ld]
   static constexpr bool kColFast = true;
   const float* p; int ld;
@@ -158,7 +160,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(int M, int N, int K, int kchu
                                                    float* __restrict__ part, int tanh_out) {
   __shared__ __align__(16) float as[kKS][kLdsRow];
   __shared__ __align__(16) float bs[kKS][kLdsRow];
-  const int t = threadIdx.x, tx = t & 15, ty = t >> 4;
+  const int t = threadIdx.x;
   const int m0 = blockIdx.y * kT, n0 = blockIdx.x * kT;
   const int kbeg = blockIdx.z * kchunk, kend = min(K, kbeg + kchunk);
   float ra[kFill], rb[kFill];
@@ -172,7 +174,11 @@ __global__ __launch_bounds__(256) void gemm_kernel(int M, int N, int K, int kchu
       rb[u] = (k0 + kb < kend && n0 + nn < N) ? b(k0 + kb, n0 + nn) : 0.f;
     }
   };
-  float acc[4][4] = {};
+  typedef float f32x16 __attribute__((ext_vector_type(16)));
+  const int lane = t & 63, wv = t >> 6, wm = wv >> 1, wn = wv & 1;
+  f32x16 acc;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) acc[i] = 0.f;
   if (kbeg < kend) fetch(kbeg);
   for (int k0 = kbeg; k0 < kend; k0 += kKS) {
 #pragma unroll
@@ -185,33 +191,31 @@ __global__ __launch_bounds__(256) void gemm_kernel(int M, int N, int K, int kchu
     }
     __syncthreads();
     if (k0 + kKS < kend) fetch(k0 + kKS);
-#pragma unroll 8
-    for (int kk = 0; kk < kKS; ++kk) {
-      const float4 av = *reinterpret_cast<const float4*>(&as[kk][ty * 4]);
-      const float4 bv = *reinterpret_cast<const float4*>(&bs[kk][tx * 4]);
-      const float ax[4] = {av.x, av.y, av.z, av.w}, bx[4] = {bv.x, bv.y, bv.z, bv.w};
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj) acc[i][jj] = fmaf(ax[i], bx[jj], acc[i][jj]);
+    for (int kk = 0; kk < kKS / 2; ++kk) {
+      const float av = as[2 * kk + (lane >> 5)][32 * wm + (lane & 31)];
+      const float bv = bs[2 * kk + (lane >> 5)][32 * wn + (lane & 31)];
+      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(av, bv, acc, 0, 0, 0);
     }
     __syncthreads();
   }
+  // accumulator i: row 8 (i / 4) + i % 4 + 4 (lane / 32), column lane % 32
+  // of this wave's quarter
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int jj = 0; jj < 4; ++jj) {
-      const int mm = m0 + ty * 4 + i, nn = n0 + tx * 4 + jj;
-      if (mm < M && nn < N) {
-        if (part) {
-          part[((int64_t)blockIdx.z * M + mm) * N + nn] = acc[i][jj];
-        } else {
-          float* c = C + (int64_t)mm * ldc + nn;
-          const float v = alpha * acc[i][jj] + (accumulate ? *c : 0.f);
-          *c = tanh_out ? tanhf(v) : v;
-        }
+  for (int i = 0; i < 16; ++i) {
+    const int mm = m0 + 32 * wm + 8 * (i >> 2) + (i & 3) + 4 * (lane >> 5);
+    const int nn = n0 + 32 * wn + (lane & 31);
+    const float accv = acc[i];
+    if (mm < M && nn < N) {
+      if (part) {
+        part[((int64_t)blockIdx.z * M + mm) * N + nn] = accv;
+      } else {
+        float* c = C + (int64_t)mm * ldc + nn;
+        const float v = alpha * accv + (accumulate ? *c : 0.f);
+        *c = tanh_out ? tanhf(v) : v;
       }
     }
+  }
 }
 
 // C = alpha * sum_z part[z] (+ C), splits added in order; four adjacent
