@@ -62,7 +62,8 @@ constexpr uint32_t kSpinLimit = 1u << 22;
 // wave runs on
 constexpr int kXccIdReg = 20 | (31 << 11);
 constexpr int kShortList = 64;     // kept rows staged in LDS per attention batch
-constexpr int kMaxPgl = kMaxChunk / kNT + 8;  // page ids of one chunk (pages of >= 256 rows)
+constexpr int kMaxPgl = kMaxChunk / 16 + 8;   // page ids of one chunk (pages of >= 16 rows)
+constexpr int kPglPerThread = (kMaxPgl + kNT - 1) / kNT;
 
 template <int G, int R = kR, bool PAGED = false>
 struct Cfg {
@@ -232,7 +233,9 @@ __global__ __launch_bounds__(kNT) void decode_step_kernel(const StepArgs a) {
     return (((int64_t)pid * a.Hkv + h) << a.log2P) + (r & ((1 << a.log2P) - 1));
   };
   int32_t* pgl = reinterpret_cast<int32_t*>(smem + C::o_pgl);  // PAGED: the chunk's page ids
-  int pgv = 0;  // PAGED: this thread's page id of the chunk (t < pages), stored with the staging
+  // PAGED: page ids t, t + 256, ... of the chunk (0 past its pages), stored
+  // into the LDS list with the staging
+  int pgv[kPglPerThread] = {};
   // PAGED: page ids of the chunk's 256-row batches l and l + 64 in lane l of
   // every wave (a chunk has at most 128 batches), so a ring refill takes its
   // id with a readlane instead of a scalar load, whose wait would also drain
@@ -245,9 +248,13 @@ __global__ __launch_bounds__(kNT) void decode_step_kernel(const StepArgs a) {
     };
     const int fp = (w * a.chunk) >> a.log2P;
     const int npg = ((w * a.chunk + a.chunk - 1) >> a.log2P) - fp + 1;
-    if (t < npg) pgv = pid_of((fp + t) << a.log2P);
-    bpid0 = pid_of(w * a.chunk + lane * kNT);
-    bpid1 = pid_of(w * a.chunk + (lane + 64) * kNT);
+#pragma unroll
+    for (int u = 0; u < kPglPerThread; ++u)
+      if (t + kNT * u < npg) pgv[u] = pid_of((fp + t + kNT * u) << a.log2P);
+    if (a.log2P >= 8) {
+      bpid0 = pid_of(w * a.chunk + lane * kNT);
+      bpid1 = pid_of(w * a.chunk + (lane + 64) * kNT);
+    }
   }
   // PAGED: physical row of the chunk's row lo + i for a uniform, 256-aligned
   // i < 32768 + BATCH (batch i / 256 of the chunk)
@@ -255,6 +262,13 @@ __global__ __launch_bounds__(kNT) void decode_step_kernel(const StepArgs a) {
     const int bi = i >> 8;
     const int pid = __builtin_amdgcn_readlane(bi < 64 ? bpid0 : bpid1, bi & 63);
     return (((int64_t)pid * a.Hkv + h) << a.log2P) + ((lo_ + i) & ((1 << a.log2P) - 1));
+  };
+  // PAGED, pages of < 256 rows: physical row of this lane's row lo + i + t
+  // from the chunk's page list in LDS (the index clamped into the list)
+  auto prow_lane = [&](int lo_, int i) -> int64_t {
+    const int r = lo_ + i + t;
+    const int pi = min(max((r >> a.log2P) - (lo_ >> a.log2P), 0), kMaxPgl - 1);
+    return (((int64_t)pgl[pi] * a.Hkv + h) << a.log2P) + (r & ((1 << a.log2P) - 1));
   };
 
   // ---- 1. loads.  The query rows, W_H, this workgroup's flag, the first
@@ -287,12 +301,25 @@ __global__ __launch_bounds__(kNT) void decode_step_kernel(const StepArgs a) {
   const uint64_t* cunit = a.codes + row0 * W64;
   CodeRow<R> cbuf[PF];
   if constexpr (PAGED) {
-    // a 256-row batch lies in one page (pages of >= 256 rows, lo a multiple
-    // of 256); batches past the table load its last full batch (never scored)
+    // pages of >= 256 rows: a 256-row batch lies in one page (lo is a
+    // multiple of 256), one uniform page id per batch; smaller pages: each
+    // lane's own page id.  Batches past the table load its last full batch
+    // (never scored).
+    if (a.log2P >= 8) {
 #pragma unroll
-    for (int j = 0; j < PF; ++j) {
-      const int rb = (int)min((int64_t)lo + j * kNT, cap - kNT);
-      cbuf[j] = load_code<R>(a.codes, prow(rb) + t);
+      for (int j = 0; j < PF; ++j) {
+        const int rb = (int)min((int64_t)lo + j * kNT, cap - kNT);
+        cbuf[j] = load_code<R>(a.codes, prow(rb) + t);
+      }
+    } else {
+      // (cap need not be a multiple of 256 here: clamp each row, not the batch)
+#pragma unroll
+      for (int j = 0; j < PF; ++j) {
+        const int r = (int)min((int64_t)lo + j * kNT + t, cap - 1);
+        const int pg = min(r >> a.log2P, a.max_pages - 1);
+        const int pid = min(max(a.bt[(int64_t)b * a.max_pages + pg], 0), a.num_pages - 1);
+        cbuf[j] = load_code<R>(a.codes, (((int64_t)pid * a.Hkv + h) << a.log2P) + (r & ((1 << a.log2P) - 1)));
+      }
     }
   } else {
 #pragma unroll
@@ -346,8 +373,11 @@ __global__ __launch_bounds__(kNT) void decode_step_kernel(const StepArgs a) {
   }
   for (int i = t; i < C::NBP; i += kNT) hist[i] = 0;
   if (t < 64) misc[t] = (t < 3) ? (uint32_t)NB : 0u;
-  if constexpr (PAGED)
-    if (t < kMaxPgl) pgl[t] = pgv;
+  if constexpr (PAGED) {
+#pragma unroll
+    for (int u = 0; u < kPglPerThread; ++u)
+      if (t + kNT * u < kMaxPgl) pgl[t + kNT * u] = pgv[u];
+  }
   __syncthreads();
   project_pack<G, R>(wr, qf, red, qcode, G);
   if constexpr (SEP) {
@@ -395,7 +425,8 @@ __global__ __launch_bounds__(kNT) void decode_step_kernel(const StepArgs a) {
       const int li = base + j * kNT + t;
       score_one(cbuf[j], li);
       if constexpr (PAGED)
-        cbuf[j] = load_code<R>(a.codes, prow_batch(lo, base + j * kNT + BATCH) + t);
+        cbuf[j] = load_code<R>(a.codes, a.log2P >= 8 ? prow_batch(lo, base + j * kNT + BATCH) + t
+                                                     : prow_lane(lo, base + j * kNT + BATCH));
       else
         cbuf[j] = load_code<R>(cbase, li + BATCH);
     }
@@ -406,8 +437,9 @@ __global__ __launch_bounds__(kNT) void decode_step_kernel(const StepArgs a) {
       const int li = base + j * kNT + t;
       score_one(cbuf[j], li);
       if constexpr (PAGED) {
-        const int64_t rb = prow_batch(lo, base + j * kNT + BATCH);
-        if (li + BATCH < cnt) cbuf[j] = load_code<R>(a.codes, rb + t);
+        const int64_t rr = a.log2P >= 8 ? prow_batch(lo, base + j * kNT + BATCH) + t
+                                        : prow_lane(lo, base + j * kNT + BATCH);
+        if (li + BATCH < cnt) cbuf[j] = load_code<R>(a.codes, rr);
       } else {
         if (li + BATCH < cnt) cbuf[j] = load_code<R>(cbase, li + BATCH);
       }
@@ -1012,7 +1044,7 @@ hipError_t launch_decode_step(const StepPlan& p, const uint16_t* q, const uint16
 }
 
 bool decode_step_paged_fusable(const StepPlan& p, int page_rows) {
-  return p.fused && p.R == 128 && page_rows >= kNT && p.lds_bytes + kMaxPgl * 4 <= 159 * 1024;
+  return p.fused && p.R == 128 && page_rows >= 16 && p.lds_bytes + kMaxPgl * 4 <= 159 * 1024;
 }
 
 hipError_t launch_decode_step_paged(const StepPlan& p, const uint16_t* q, const uint16_t* K, const uint16_t* V,

@@ -100,14 +100,18 @@ FUSED_CASES = [
     (1, 32, 8, 20000, [20000], 512, 1024, 0),
     (2, 8, 8, 5000, [5000, 777], 64, 512, 2),      # G = 1
     (2, 64, 8, 3000, [3000, 1], 128, 256, 1),      # G = 8, a one-token sequence
+    (1, 32, 8, 20000, [20000], 512, 16, 3),        # 16-row pages: page ids per lane
+    (2, 8, 8, 5000, [5000, 777], 64, 32, 2),
+    (2, 64, 8, 3000, [3000, 1], 128, 64, 1),
 ]
 
 
 @pytest.mark.parametrize("case", FUSED_CASES, ids=[f"P{c[6]}-G{c[1] // c[2]}-N{c[3]}" for c in FUSED_CASES])
 def test_fused_paged_step_equals_contiguous_step_bitwise(hata_gpu, case):
-    """With pages of >= 256 rows and 128-bit codes the paged step runs the
-    fused kernel; it differs from the contiguous one only in its addresses,
-    so codes, kept set and output must be bit-identical."""
+    """With 128-bit codes the paged step runs the fused kernel (one page id
+    per 256-row batch for pages of >= 256 rows, per lane for smaller ones);
+    it differs from the contiguous one only in its addresses, so codes, kept
+    set and output must be bit-identical."""
     B, Hq, Hkv, N, lens, k, P, spare = case
     _log(f"fused paged B={B} Hq={Hq} Hkv={Hkv} lens={lens} k={k} P={P}")
     s = synth.Shape(f"fpaged-{B}-{Hq}-{Hkv}-{N}", B=B, Hq=Hq, Hkv=Hkv, N=N, k=k, dist="gauss",
