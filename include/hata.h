@@ -258,10 +258,9 @@ int hata_prefill_paged(const void* q, const void* K_pool, const void* V_pool,
  * Same steps and results as hata_decode_step on the gathered contiguous
  * cache: the key row n_b-1 is encoded and its code written through the
  * table, every code row 0..n_b-1 is scored, top-k by (score, index), and
- * the attention gathers the kept K/V rows through the table.  With pages
- * of at least 256 rows, r = 128 and a shape whose step fits on chip, the
- * step runs as hata_decode_step's single kernel (each 256-row batch of
- * codes lies in one page; page ids come from the table with the first
+ * the attention gathers the kept K/V rows through the table.  With r = 128
+ * and a shape whose step fits on chip, the step runs as hata_decode_step's
+ * single kernel (page ids of each workgroup's rows loaded with its first
  * loads); otherwise as separate kernels (row encode, Hamming scan, top-k,
  * gather attention).  page_rows a power of two in [16, 65536]; q, the pools
  * 16-byte aligned; idx_out [B][Hkv][k] optional.  ws: hata_workspace_bytes(
