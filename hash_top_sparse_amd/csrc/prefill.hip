@@ -67,11 +67,6 @@ struct PrefillArgs {
   PageMap pm;  // PAGED: K, V and codes are page pools addressed through it
 };
 
-__device__ __forceinline__ uint32_t half16(const uint4& v, int e) {
-  const uint32_t w = e < 2 ? v.x : e < 4 ? v.y : e < 6 ? v.z : v.w;
-  return (e & 1) ? (w >> 16) : (w & 0xFFFFu);
-}
-
 // PAGED: K, V and codes are page pools (a.pm); a separate instance, the
 // contiguous code is unchanged.
 template <int G, int R, bool PAGED>
@@ -181,10 +176,18 @@ __global__ __launch_bounds__(kNT, 2) void prefill_kernel(PrefillArgs a) {
       const int id = t + kNT * i, key = id >> 4, c = id & 15;
       *reinterpret_cast<uint4*>(ksb + key * kKsStride + c * 8) = kreg[i];
     }
+    // element e of four rows -> 4 keys of one column: one byte permute per
+    // pair of rows (bytes 0-3 of the selector's source are the second
+    // operand, 4-7 the first)
+    const uint32_t w0[4] = {vreg[0].x, vreg[0].y, vreg[0].z, vreg[0].w};
+    const uint32_t w1[4] = {vreg[1].x, vreg[1].y, vreg[1].z, vreg[1].w};
+    const uint32_t w2[4] = {vreg[2].x, vreg[2].y, vreg[2].z, vreg[2].w};
+    const uint32_t w3[4] = {vreg[3].x, vreg[3].y, vreg[3].z, vreg[3].w};
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const uint32_t lo = half16(vreg[0], e) | (half16(vreg[1], e) << 16);
-      const uint32_t hi = half16(vreg[2], e) | (half16(vreg[3], e) << 16);
+      const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
+      const uint32_t lo = __builtin_amdgcn_perm(w1[e >> 1], w0[e >> 1], sel);
+      const uint32_t hi = __builtin_amdgcn_perm(w3[e >> 1], w2[e >> 1], sel);
       *reinterpret_cast<uint2*>(vtb + (vc * 8 + e) * kVtStride + 4 * vkg) = make_uint2(lo, hi);
     }
   };
