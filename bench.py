@@ -576,6 +576,8 @@ def main() -> int:
                     help="also time the workload with 32-, 64- and 256-bit codes")
     ap.add_argument("--model-sweep", action="store_true",
                     help="also time 32-layer decode (one graph per token) at 32K/64K/128K against dense")
+    ap.add_argument("--prefill-run", action="store_true",
+                    help="short run for hardware-counter passes on the prefill: one 32K-token prefill")
     ap.add_argument("--pmc-run", action="store_true",
                     help="short run for hardware-counter passes: 32 eager fused steps over the layer "
                          "caches, then one plain device copy of 1 GiB as the byte-counter reference")
@@ -593,6 +595,10 @@ def main() -> int:
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     binding.load()
     torch.cuda.set_device(0)
+    if args.prefill_run:
+        prefill_bench(reps=1)
+        log("prefill run done")
+        return 0
     if args.pmc_run:
         measure(args.config, 32, 8, 0, args.layers, False, with_bulk=False, with_qk=False)
         src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
@@ -661,7 +667,7 @@ def main() -> int:
         "roofline": {"bound": "hbm", "achieved": head["GBs"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": head["GBs"] / PEAK_HBM_GBS,
                      "traffic": profiled_traffic() if args.config == 4 else None,
-                     "kernel": f"decode_step_kernel<{shape.G}, false, 128>", "bytes_per_launch": head["bytes_per_step"],
+                     "kernel": f"decode_step_kernel<{shape.G}, false, 128, false>", "bytes_per_launch": head["bytes_per_step"],
                      "peak_measured": peak_meas, "frac_of_measured": head["GBs"] / peak_meas,
                      "peak_measured_by": "hata_stream_read over 4 GiB, best of 5"},
         "tokens_per_s": head["tokens_per_s"],
