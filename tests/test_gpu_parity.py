@@ -142,6 +142,7 @@ MULTI_TOPK_CASES = [
     ([20000, 100], 512, (0, 513), 512),          # a sequence shorter than k
     ([131072, 65536], 1, (0, 1025), 1024),       # k = 1, long rows
     ([40000, 40000], 2048, (0, 2049), 2048),     # widest bins (G r = 2048)
+    ([20001, 9999], 512, (0, 8), 512),           # odd row stride: unaligned score rows read per score
 ]
 
 
