@@ -142,3 +142,37 @@ def test_fused_paged_step_equals_contiguous_step_bitwise(hata_gpu, case):
         assert torch.equal(codes[b, :, :n], got_codes[b, :, :n])
     assert torch.equal(idx, cidx)
     assert torch.equal(out, cout)
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("P", [16, 256])
+def test_fused_paged_step_full_size_bitwise(hata_gpu, P):
+    """The 128K workload's shape (32 query / 8 KV heads, k = 512) over
+    shuffled pages: bit-identical to the contiguous step."""
+    B, Hq, Hkv, N, k = 1, 32, 8, 131072, 512
+    _log(f"fused paged full size P={P}")
+    g = torch.Generator(device="cuda")
+    g.manual_seed(9700 + P)
+    q = torch.randn((B, Hq, 128), generator=g, device="cuda").to(torch.bfloat16)
+    K = torch.randn((B, Hkv, N, 128), generator=g, device="cuda").to(torch.bfloat16)
+    V = torch.randn((B, Hkv, N, 128), generator=g, device="cuda").to(torch.bfloat16)
+    W = torch.randn((Hkv, 128, 128), generator=g, device="cuda") / np.sqrt(128.0)
+    codes = torch.zeros((B, Hkv, N, 2), dtype=torch.int64, device="cuda")
+    hata_gpu.encode_append(K, W, codes, n_new=N)
+    seq = torch.full((B,), N, dtype=torch.int32, device="cuda")
+    mp = N // P
+    bt = torch.randperm(B * mp + 3, generator=g, device="cuda")[:B * mp].to(torch.int32).view(B, mp)
+    Kp, Vp = _paginate(K, P, bt, B * mp + 3), _paginate(V, P, bt, B * mp + 3)
+    Cp = _paginate(codes, P, bt, B * mp + 3)
+    ws = hata_gpu.alloc_workspace(hata_gpu.OP_DECODE_STEP_PAGED, B, Hq, Hkv, N, k)
+    out = torch.zeros((B, Hq, 128), dtype=torch.float32, device="cuda")
+    idx = torch.zeros((B, Hkv, k), dtype=torch.int32, device="cuda")
+    hata_gpu.decode_step_paged(q, Kp, Vp, W, Cp, bt, seq, N, k, 0.0883883, out, ws, idx_out=idx)
+    cws = hata_gpu.alloc_workspace(hata_gpu.OP_DECODE_STEP, B, Hq, Hkv, N, k)
+    cout, cidx = torch.zeros_like(out), torch.zeros_like(idx)
+    hata_gpu.decode_step(q, K, V, W, codes, seq, N, k, 0.0883883, cout, cws, cidx)
+    torch.cuda.synchronize()
+    assert hata_gpu.workspace_check(ws) == 0 and hata_gpu.workspace_check(cws) == 0
+    assert torch.equal(idx, cidx)
+    assert torch.equal(out, cout)
+    assert torch.equal(_gather(Cp, bt, N), codes)

@@ -123,12 +123,15 @@ def test_prefill_equals_separate_encode(hata_gpu):
 
 
 @pytest.mark.slow
-def test_prefill_full_size_sampled(hata_gpu):
-    """32K-token prompt of a Llama-3.1-8B-shaped layer (32 query / 8 KV
-    heads, d = 128, r = 128), inputs drawn on the device; sampled rows of
-    every head against the oracle, sampled code rows against the encode
-    oracle."""
-    B, Hq, Hkv, N, r = 1, 32, 8, 32768, 128
+@pytest.mark.parametrize("Hq,Hkv,N", [(32, 8, 32768), (32, 32, 8192)], ids=["gqa4-32k", "mha-8k"])
+def test_prefill_full_size_sampled(hata_gpu, Hq, Hkv, N):
+    """Long prompts of a Llama-3.1-8B-shaped layer (32 query / 8 KV heads,
+    32K tokens) and of an MHA layer (32 heads, 8K tokens; one query head per
+    KV head, own rows spanning two key tiles), d = 128, r = 128, inputs drawn
+    on the device; sampled rows of every head against the oracle, sampled
+    code rows against the encode oracle."""
+    B, r = 1, 128
+    G = Hq // Hkv
     _log(f"prefill full size N={N}")
     g = torch.Generator(device="cuda")
     g.manual_seed(9900)
@@ -150,7 +153,7 @@ def test_prefill_full_size_sampled(hata_gpu):
     Wn = W.cpu().numpy()
     for h in range(Hq):
         qrows = q[0, h, torch.from_numpy(pos).cuda()].view(torch.int16).cpu().numpy().view(np.uint16)
-        ref, absw = oprefill.attention_rows(qrows, pos, Kb[0, h // 4], Vb[0, h // 4], scale, with_abs=True)
+        ref, absw = oprefill.attention_rows(qrows, pos, Kb[0, h // G], Vb[0, h // G], scale, with_abs=True)
         got = out[0, h, torch.from_numpy(pos).cuda()].cpu().numpy()
         err = np.abs(got - ref)
         assert (err <= _bar(ref, absw)).all(), f"head {h}: max err {err.max():.3e}"
