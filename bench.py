@@ -513,8 +513,9 @@ def train_bench(J: int = 512, n: int = 8192, r: int = 128, steps: int = 20) -> d
     Q/K drawn on the device, J sampled queries at random positions of an
     n-key sequence): the label kernel and one gradient step, HIP events over
     `steps` calls each.  FLOP count of the step: the two projections, the
-    four J x n x r pair products, the two gradient products and the W^T W
-    terms."""
+    two J x n x r label-weighted pair products, the two gradient products
+    and the W^T W terms (the causal-mask sums, O((n + J) r) adds, are not
+    counted)."""
     import torch
 
     from hash_top_sparse_amd import binding
@@ -547,7 +548,7 @@ def train_bench(J: int = 512, n: int = 8192, r: int = 128, steps: int = 20) -> d
     e1.record()
     torch.cuda.synchronize()
     st_ms = e0.elapsed_time(e1) / steps
-    flops = 8.0 * J * n * r + 4.0 * (J + n) * 128 * r + 4.0 * 128 * r * r
+    flops = 4.0 * J * n * r + 4.0 * (J + n) * 128 * r + 4.0 * 128 * r * r
     tf = flops / (st_ms * 1e-3) / 1e12
     log(f"hash training, J={J} n={n} r={r}: labels {lab_ms * 1e3:.1f} us, step {st_ms * 1e3:.1f} us "
         f"({tf:.2f} TFLOP/s fp32)")

@@ -17,7 +17,10 @@
 //   dL/dHq = 2 eps (rowsum(S) Hq - S Hk)
 //   dL/dHk = 2 eps (colsum(S) Hk - S^T Hq) + 2 eta M^T (M Hk),  M_ji = [i <= p_j]
 //   dL/dW  = sigma (Q^T dZq + K^T dZk) + 2 lam W A / ||A||_F,   A = W^T W - I
-// then W <- W - lr dL/dW.  The loss terms come from the same products.
+// then W <- W - lr dL/dW.  The loss terms come from the same products.  The
+// causal-mask products are sums, not GEMMs: row j of M Hk is the sum of the
+// key rows 0..p_j, and row i of M^T (M Hk) the sum of the rows j of M Hk with
+// p_j >= i; both are formed from 64-row chunk sums in O((n + J) r) adds.
 #include <algorithm>
 
 #include "hata_device.hpp"
@@ -122,16 +125,6 @@ struct AccBf16T {
   static constexpr bool kColFast = false;
   const uint16_t* p; int ld;
   __device__ float operator()(int r, int c) const { return __uint_as_float((uint32_t)p[(int64_t)c * ld + r] << 16); }
-};
-struct AccMask {  // M_ji = [i <= p_j] (rows j, columns i)
-  static constexpr bool kColFast = true;
-  const int32_t* pos; int n;
-  __device__ float operator()(int r, int c) const { return c <= min(max(pos[r], 0), n - 1) ? 1.f : 0.f; }
-};
-struct AccMaskT {  // M^T
-  static constexpr bool kColFast = false;
-  const int32_t* pos; int n;
-  __device__ float operator()(int r, int c) const { return r <= min(max(pos[c], 0), n - 1) ? 1.f : 0.f; }
 };
 struct AccGramMinusI {  // (W^T W - I)[r][c] from a precomputed W^T W
   static constexpr bool kColFast = true;
@@ -277,6 +270,144 @@ hipError_t gemm(int M, int N, int K, A a, B b, float* C, int ldc, float alpha, b
                        C, ldc, alpha, accumulate ? 1 : 0);
   }
   return hipGetLastError();
+}
+
+// ------------------------------------------------------------ causal-mask sums
+// M_ji = [i <= p_j] with p_j clamped into [0, n - 1].  Fixed summation
+// orders throughout (no atomics), so the results do not vary between runs.
+constexpr int kMaskRows = 64;  // key rows per chunk
+
+// The kernels below are bound by the latency of their loads, so every loop
+// over rows or queries loads all its operands first (indices clamped into
+// range, a select dropping the extra ones) and adds them afterwards.
+
+// T[c][col] = sum of Hk rows 64c .. 64c + 63.  Workgroup = (chunk, 64
+// columns), thread = (column, quarter u): rows 16u .. 16u + 15 ascending,
+// then the four sums in quarter order.
+__global__ __launch_bounds__(256) void mask_chunk_sums_kernel(const float* __restrict__ Hk, int n, int r,
+                                                              float* __restrict__ T) {
+  __shared__ float qs[4][64];
+  const int t = threadIdx.x, lane = t & 63, u = t >> 6;
+  const int c = blockIdx.x;
+  const int col = blockIdx.y * 64 + lane;
+  const int cc = min(col, r - 1);
+  const int i0 = c * kMaskRows + 16 * u, i1 = min(n, c * kMaskRows + kMaskRows);
+  float v[16];
+#pragma unroll
+  for (int q = 0; q < 16; ++q) v[q] = Hk[(int64_t)min(i0 + q, n - 1) * r + cc];
+  float s = 0.f;
+#pragma unroll
+  for (int q = 0; q < 16; ++q) s += (i0 + q < i1) ? v[q] : 0.f;
+  qs[u][lane] = s;
+  __syncthreads();
+  if (u == 0 && col < r) T[(int64_t)c * r + col] = ((qs[0][lane] + qs[1][lane]) + qs[2][lane]) + qs[3][lane];
+}
+
+// Cm[j] = (M Hk)_j = sum_{i <= p_j} Hk[i].  Workgroup = (query j, 64
+// columns), thread = (column, quarter u): quarter u sums the chunk sums
+// u, u + 4, ... before p_j's chunk (32 loads in flight at a time), then rows
+// 16u .. 16u + 15 of that chunk up to p_j (ascending); the four sums are
+// added in quarter order.
+__global__ __launch_bounds__(256) void mask_rows_kernel(const float* __restrict__ Hk, const float* __restrict__ T,
+                                                        const int32_t* __restrict__ pos, int J, int n, int r,
+                                                        float* __restrict__ Cm) {
+  __shared__ float qs[4][64];
+  const int t = threadIdx.x, lane = t & 63, u = t >> 6;
+  const int j = blockIdx.x;
+  const int col = blockIdx.y * 64 + lane;
+  const int cc = min(col, r - 1);
+  const int p = min(max(pos[j], 0), n - 1);
+  const int cj = p / kMaskRows;
+  float s = 0.f;
+  for (int c0 = u; c0 < cj; c0 += 4 * 32) {
+    float v[32];
+#pragma unroll
+    for (int q = 0; q < 32; ++q) v[q] = T[(int64_t)min(c0 + 4 * q, cj - 1) * r + cc];
+#pragma unroll
+    for (int q = 0; q < 32; ++q) s += (c0 + 4 * q < cj) ? v[q] : 0.f;
+  }
+  const int ib = cj * kMaskRows + 16 * u;
+  float v[16];
+#pragma unroll
+  for (int q = 0; q < 16; ++q) v[q] = Hk[(int64_t)min(ib + q, n - 1) * r + cc];
+#pragma unroll
+  for (int q = 0; q < 16; ++q) s += (ib + q <= p) ? v[q] : 0.f;
+  qs[u][lane] = s;
+  __syncthreads();
+  if (u == 0 && col < r) Cm[(int64_t)j * r + col] = ((qs[0][lane] + qs[1][lane]) + qs[2][lane]) + qs[3][lane];
+}
+
+// MtC[i] = (M^T Cm)_i = sum_{j : p_j >= i} Cm[j].  Workgroup = (64-row chunk,
+// 64 columns), thread = (column, quarter u).  Queries are taken in batches of
+// 256: those positioned past the chunk add to every row of it (quarter u
+// sums batch entries 64u .. 64u + 63 in order; the four sums are added in
+// quarter order at the end); those inside the chunk are listed in LDS in
+// query order and added, 8 list entries per round of loads, to the rows at
+// or before their position (quarter u owns rows 16u .. 16u + 15).
+__global__ __launch_bounds__(256) void mask_cols_kernel(const float* __restrict__ Cm, const int32_t* __restrict__ pos,
+                                                        int J, int n, int r, float* __restrict__ MtC) {
+  __shared__ int bp[256];           // positions of the batch (-1 past J)
+  __shared__ int lj[256], lp[256];  // in-chunk queries of the batch, in query order
+  __shared__ int wcnt[4];
+  __shared__ float qs[4][64];
+  const int t = threadIdx.x, lane = t & 63, u = t >> 6;
+  const int col = blockIdx.y * 64 + lane;
+  const int cc = min(col, r - 1);
+  const int i0 = blockIdx.x * kMaskRows, i1 = min(n, i0 + kMaskRows);
+  const int r0 = i0 + 16 * u;  // this thread's first row
+  float past = 0.f;
+  float acc[16];
+#pragma unroll
+  for (int q = 0; q < 16; ++q) acc[q] = 0.f;
+  for (int jb = 0; jb < J; jb += 256) {
+    const int j = jb + t;
+    const int p = (j < J) ? min(max(pos[j], 0), n - 1) : -1;
+    bp[t] = p;
+    const bool in = p >= i0 && p < i1;
+    const uint64_t m = __ballot(in);
+    if (lane == 0) wcnt[u] = __popcll(m);
+    __syncthreads();
+    int off = 0;
+    for (int w = 0; w < u; ++w) off += wcnt[w];
+    const int nin = wcnt[0] + wcnt[1] + wcnt[2] + wcnt[3];
+    if (in) {
+      const int e = off + __popcll(m & ((1ull << lane) - 1));
+      lj[e] = j;
+      lp[e] = p;
+    }
+    __syncthreads();
+    {
+      float v[64];
+#pragma unroll
+      for (int e = 0; e < 64; ++e) v[e] = Cm[(int64_t)min(jb + 64 * u + e, J - 1) * r + cc];
+#pragma unroll
+      for (int e = 0; e < 64; ++e) past += (bp[64 * u + e] >= i1) ? v[e] : 0.f;
+    }
+    for (int e0 = 0; e0 < nin; e0 += 8) {
+      float v[8];
+      int pe[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const int e = min(e0 + q, nin - 1);
+        v[q] = Cm[(int64_t)lj[e] * r + cc];
+        pe[q] = (e0 + q < nin) ? lp[e] : -1;
+      }
+#pragma unroll
+      for (int q = 0; q < 8; ++q)
+#pragma unroll
+        for (int x = 0; x < 16; ++x)
+          if (pe[q] >= r0 + x) acc[x] += v[q];
+    }
+    __syncthreads();
+  }
+  qs[u][lane] = past;
+  __syncthreads();
+  const float tot = ((qs[0][lane] + qs[1][lane]) + qs[2][lane]) + qs[3][lane];
+  if (col < r) {
+#pragma unroll
+    for (int q = 0; q < 16; ++q)
+      if (r0 + q < i1) MtC[(int64_t)(r0 + q) * r + col] = tot + acc[q];
+  }
 }
 
 // ------------------------------------------------------------ elementwise
@@ -449,14 +580,15 @@ TrainPlan plan_train(int J, int n, int r) {
   p.partk = take((size_t)3 * n);
   p.fac = take(4);
   // the largest split-k partial buffer over the step's products
-  const int shapes[10][3] = {{J, r, kD}, {n, r, kD}, {J, r, n}, {n, r, J}, {J, r, n},
-                             {n, r, J}, {kD, r, J}, {kD, r, n}, {r, r, kD}, {kD, r, r}};
+  const int shapes[8][3] = {{J, r, kD}, {n, r, kD}, {J, r, n}, {n, r, J},
+                            {kD, r, J}, {kD, r, n}, {r, r, kD}, {kD, r, r}};
   size_t part = 0;
   for (const auto& g : shapes) {
     const int sp = train_gemm_splits(g[0], g[1], g[2]);
     if (sp > 1) part = std::max(part, (size_t)sp * g[0] * g[1]);
   }
   part = std::max(part, (size_t)kColChunks * n);  // column-sum partials
+  part = std::max(part, (size_t)((n + kMaskRows - 1) / kMaskRows) * r);  // chunk sums of Hk
   p.part = take(part);
   p.total = off;
   return p;
@@ -478,8 +610,15 @@ hipError_t launch_hash_train_step(const TrainPlan& p, const uint16_t* q, const u
   // pair products, label sums, balance products
   HATA_TRY(gemm(J, r, n, AccF32{S, n}, AccF32{Hk, r}, SHk, r, 1.f, false, part, s));
   HATA_TRY(gemm(n, r, J, AccF32T{S, n}, AccF32{Hq, r}, StHq, r, 1.f, false, part, s));
-  HATA_TRY(gemm(J, r, n, AccMask{q_pos, n}, AccF32{Hk, r}, Cm, r, 1.f, false, part, s));
-  HATA_TRY(gemm(n, r, J, AccMaskT{q_pos, n}, AccF32{Cm, r}, MtC, r, 1.f, false, part, s));
+  {
+    const unsigned nc = (unsigned)((n + kMaskRows - 1) / kMaskRows), cb = (unsigned)((r + 63) / 64);
+    hipLaunchKernelGGL(mask_chunk_sums_kernel, dim3(nc, cb), dim3(256), 0, s, (const float*)Hk, n, r,
+                       part);
+    hipLaunchKernelGGL(mask_rows_kernel, dim3((unsigned)J, cb), dim3(256), 0, s, (const float*)Hk,
+                       (const float*)part, q_pos, J, n, r, Cm);
+    hipLaunchKernelGGL(mask_cols_kernel, dim3(nc, cb), dim3(256), 0, s, (const float*)Cm, q_pos, J, n, r, MtC);
+    HATA_TRY(hipGetLastError());
+  }
   hipLaunchKernelGGL(row_sums_kernel, dim3(J), dim3(256), 0, s, S, J, n, rs);
   hipLaunchKernelGGL(col_sums_part_kernel, dim3((unsigned)((n + 63) / 64), kColChunks), dim3(256), 0, s, S, J, n,
                      part);

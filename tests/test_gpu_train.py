@@ -78,7 +78,26 @@ def test_train_step_matches_oracle(hata_gpu, J, n, r):
     """Ragged shapes cover partial output tiles, a short last k split and
     the split-k partial sums (products over n with few output tiles)."""
     q, k, pos = _qk(J, n, 9300 + r + J + n)
-    rng = np.random.default_rng(9400 + r + J + n)
+    _check_step(hata_gpu, q, k, pos, r, 9400 + r + J + n)
+
+
+def test_train_step_unsorted_clustered_positions(hata_gpu):
+    """Query positions need not be sorted or distinct: 300 queries (two
+    batches of the mask-sum kernels) with runs of equal positions at both
+    sides of 64-row chunk boundaries, the first and last key, and a cluster
+    inside one chunk, in shuffled order."""
+    J, n, r = 300, 1000, 128
+    q, k, _ = _qk(J, n, 9600)
+    rng = np.random.default_rng(9601)
+    pos = np.concatenate([np.full(40, 63), np.full(30, 64), np.full(10, 0), np.full(10, n - 1),
+                          rng.integers(128, 192, size=60), rng.integers(0, n, size=J - 150)]).astype(np.int32)
+    pos = pos[rng.permutation(J)]
+    _check_step(hata_gpu, q, k, pos, r, 9602)
+
+
+def _check_step(hata_gpu, q, k, pos, r, seed):
+    J, n = q.shape[0], k.shape[0]
+    rng = np.random.default_rng(seed)
     W0 = (rng.standard_normal((128, r)) / np.sqrt(128.0)).astype(np.float32)
     S = train.labels(q, k, pos)
     sigma, eps, eta, lam, lr = 1.5, 1e-3, 2e-4, 0.3, 0.02
