@@ -579,6 +579,8 @@ def main() -> int:
                     help="also time 32-layer decode (one graph per token) at 32K/64K/128K against dense")
     ap.add_argument("--prefill-run", action="store_true",
                     help="short run for hardware-counter passes on the prefill: one 32K-token prefill")
+    ap.add_argument("--train-run", action="store_true",
+                    help="only the training step, 20 calls (for kernel traces)")
     ap.add_argument("--pmc-run", action="store_true",
                     help="short run for hardware-counter passes: 32 eager fused steps over the layer "
                          "caches, then one plain device copy of 1 GiB as the byte-counter reference")
@@ -599,6 +601,10 @@ def main() -> int:
     if args.prefill_run:
         prefill_bench(reps=1)
         log("prefill run done")
+        return 0
+    if args.train_run:
+        train_bench(steps=20)
+        log("train run done")
         return 0
     if args.pmc_run:
         measure(args.config, 32, 8, 0, args.layers, False, with_bulk=False, with_qk=False)
