@@ -530,14 +530,14 @@ __global__ __launch_bounds__(kLossNT) void loss_kernel(const float* __restrict__
   }
 }
 
-// g = dW + fac * W A (the full gradient), W -= lr * g; optional gradient copy
+// g = dW + fac * W A (the full gradient), W <- W - lr g; optional gradient copy
 __global__ void update_kernel(float* __restrict__ W, const float* __restrict__ dW, const float* __restrict__ WA,
                               const float* __restrict__ fac, float* __restrict__ grad, int count, float lr) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= count) return;
   const float g = dW[i] + fac[0] * WA[i];
   if (grad) grad[i] = g;
-  W[i] -= lr * g;
+  W[i] = fmaf(-lr, g, W[i]);  // one rounding of the updated weight
 }
 
 }  // namespace

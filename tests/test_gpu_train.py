@@ -116,9 +116,12 @@ def _check_step(hata_gpu, q, k, pos, r, seed):
     scale = np.abs(ref_g).max()
     np.testing.assert_allclose(g, ref_g, rtol=2e-3, atol=2e-3 * scale)
     np.testing.assert_allclose(loss.cpu().numpy(), np.array(ref_l), rtol=1e-3)
-    # the device forms W - lr * g with one fused multiply-add (one rounding)
-    np.testing.assert_allclose(W.cpu().numpy(), W0.astype(np.float64) - lr * g.astype(np.float64),
-                               rtol=0, atol=2e-7 * max(1.0, float(np.abs(W0).max())))
+    # the device forms W - lr * g, lr as fp32, with one fused multiply-add:
+    # one fp32 rounding of the updated value, at most half an ulp of it
+    # (2^-24 relative); the bound is set at twice that
+    lr32 = float(np.float32(lr))
+    np.testing.assert_allclose(W.cpu().numpy(), W0.astype(np.float64) - lr32 * g.astype(np.float64),
+                               rtol=2.0 ** -23, atol=1e-30)
 
 
 def test_train_steps_descend_on_device(hata_gpu):
