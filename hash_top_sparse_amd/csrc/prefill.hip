@@ -17,7 +17,9 @@
 //                 belong to one query (lane % 32), half its keys each in
 //                 lanes l and l ^ 32
 //   online softmax in the log2 domain (scale * log2 e folded into the
-//                 logits), row max / sum over the lane pair
+//                 logits), row max / sum over the lane pair; the running
+//                 sums are rescaled only when a row's max passes the
+//                 reference by more than 2^8 in weight
 //   O^T += V^T P^T  A = V^T from a transposed LDS copy, B = P rounded to
 //                 bf16 straight from the S^T accumulators; the MFMA's k
 //                 index runs over the keys in the order the accumulators
@@ -43,6 +45,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kBK = 64;              // keys per staged tile
+constexpr float kLazyLog2 = 8.f;     // reference-max slack (log2 units)
 constexpr int kKsStride = kD + 8;    // bf16 per staged key row (272 bytes)
 constexpr int kVtStride = kBK + 4;   // bf16 per transposed value row (136 bytes)
 constexpr int kBufElems = kBK * kKsStride + kD * kVtStride;  // bf16 per K/V tile buffer
@@ -256,8 +259,18 @@ __global__ __launch_bounds__(kNT, 2) void prefill_kernel(PrefillArgs a) {
           for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[st][i]);
         }
         mx = pair32_max(mx);
-        const float m_new = fmaxf(m_run, mx);
-        const float mref = m_new == -INFINITY ? 0.f : __fmul_rn(m_new, a.scale_log2);
+        // The weights are taken relative to a reference max m_run, which
+        // moves only when some row's max has risen past it by more than
+        // kLazyLog2 in the exponent (or on a row's first unmasked keys):
+        // weights stay below 2^kLazyLog2, keep bf16's relative precision
+        // when rounded, and the final division by the row sum removes the
+        // reference.  When the wave moves it, every row takes its own
+        // max(m_run, mx), rounded as before, so a row whose max did not rise
+        // gets alpha = 1 exactly.
+        const bool rise = __fmul_rn(mx, a.scale_log2) > __fmul_rn(m_run, a.scale_log2) + kLazyLog2;
+        const bool move = __ballot(rise) != 0;
+        const float m_ref = move ? fmaxf(m_run, mx) : m_run;
+        const float mref = m_ref == -INFINITY ? 0.f : __fmul_rn(m_ref, a.scale_log2);
         float psum = 0.f;
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
@@ -265,10 +278,7 @@ __global__ __launch_bounds__(kNT, 2) void prefill_kernel(PrefillArgs a) {
           s[st][i] = p;
           psum += p;
         }
-        // rescale only when some row's max moved (after the first tiles it
-        // rarely does); the earlier weights are relative to m_run * c,
-        // rounded the same way, so an unchanged max gives alpha = 1 exactly
-        if (__ballot(m_new != m_run) != 0) {
+        if (move) {
           const float alpha = __builtin_amdgcn_exp2f(__fmul_rn(m_run, a.scale_log2) - mref);
           l_run *= alpha;
 #pragma unroll
@@ -277,7 +287,7 @@ __global__ __launch_bounds__(kNT, 2) void prefill_kernel(PrefillArgs a) {
             for (int i = 0; i < 16; ++i) o[dt][i] *= alpha;
         }
         l_run += psum;
-        m_run = m_new;
+        m_run = m_ref;
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
           bf16x8 pf;
