@@ -410,8 +410,8 @@ int hata_hash_labels(const void* q, const void* k, const int32_t* q_pos, int J, 
     return fail(HATA_ERR_UNSUPPORTED, "hash_labels: n=%d above %d keys", n, hata::kMaxLabelKeys);
   if (pos_permille < 1 || pos_permille > 1000)
     return fail(HATA_ERR_SHAPE, "hash_labels: pos_permille=%d outside [1, 1000]", pos_permille);
-  if (!aligned(q, 4) || !aligned(k, 4) || !aligned(labels, 4))
-    return fail(HATA_ERR_ALIGN, "hash_labels: q, k and labels must be 4-byte aligned");
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(labels, 4))
+    return fail(HATA_ERR_ALIGN, "hash_labels: q and k must be 16-byte aligned, labels 4-byte aligned");
   int st = pre_launch("hash_labels");
   if (st) return st;
   hipError_t e = hata::launch_hash_labels(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), q_pos,

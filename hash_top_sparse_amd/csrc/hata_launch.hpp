@@ -109,7 +109,7 @@ struct TrainPlan {
 };
 TrainPlan plan_train(int J, int n, int r);
 int train_gemm_splits(int M, int N, int K);
-size_t label_lds_bytes();
+size_t label_lds_bytes(int n, int pos_permille);
 hipError_t launch_hash_labels(const uint16_t* q, const uint16_t* k, const int32_t* q_pos, int J, int n,
                               int pos_permille, float s_max, float s_min, float* S, hipStream_t s);
 hipError_t launch_hash_train_step(const TrainPlan& p, const uint16_t* q, const uint16_t* k, const int32_t* q_pos,

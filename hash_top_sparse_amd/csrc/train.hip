@@ -10,8 +10,10 @@
 // keys 0..p_j; the top tenth by q.k are positives with labels falling
 // linearly from 20 to 1, the rest negatives with label -1.
 //
-// Labels: one workgroup per query computes its scores (fp32) and sorts
-// (score descending, index ascending) with a bitonic sort in LDS.  Step: the
+// Labels: one workgroup per query computes its scores (fp32; 16 lanes per
+// key, so each load instruction reads whole 256-byte key rows), selects the
+// positives by a radix select on order-preserving score keys and ranks only
+// them (score descending, index ascending) with a bitonic sort in LDS.  Step: the
 // gradient by the chain rule through h (dh/dz = (1 - h^2)/2), with the pair
 // sums as tiled fp32 GEMMs:
 //   dL/dHq = 2 eps (rowsum(S) Hq - S Hk)
@@ -33,64 +35,182 @@ namespace {
 // ------------------------------------------------------------ labels
 constexpr int kLabNT = 256;
 
+// Order-preserving key of a finite fp32 score: a larger score gives a larger
+// key, and -0 and +0 (equal scores) give the same key.
+__device__ __forceinline__ uint32_t score_key(float s) {
+  uint32_t u = __float_as_uint(s);
+  if (u == 0x80000000u) u = 0u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// Candidate slots for the ranked positives: a power of two >= the largest
+// positive count at this n.
+__host__ __device__ inline int label_cand_slots(int n, int pos_permille) {
+  const int pp = (n * pos_permille + 999) / 1000;
+  const int pmax = pp > 1 ? pp : 1;
+  int c = 1;
+  while (c < pmax) c <<= 1;
+  return c;
+}
+
+// One workgroup per query j.  LDS: key[n] (score keys, then the row's
+// labels), ck[CL] / ci[CL] (candidate keys and key indices), hist[256],
+// misc[16].
+//  1. scores of keys 0..p (fp32; 16 lanes per key, lane c multiplying
+//     channels 8c .. 8c + 7 from one 16-byte load, the group's 16 partials
+//     summed in a fixed order), stored as order-preserving keys;
+//  2. radix select, 8 bits per pass from the top: the P-th largest key T and
+//     the number `need` of keys equal to T that are positives (ties go to
+//     the lower key index, so the first `need` of them in index order);
+//  3. the P positives collected by an ordered block scan over runs of
+//     consecutive indices, then ranked by a bitonic sort (key descending,
+//     index ascending) over the next power of two;
+//  4. labels built in LDS and written once per key.
 __global__ __launch_bounds__(kLabNT) void labels_kernel(const uint16_t* __restrict__ q,
                                                         const uint16_t* __restrict__ k,
                                                         const int32_t* __restrict__ q_pos, int n,
                                                         int pos_permille, float s_max, float s_min,
                                                         float* __restrict__ S) {
   extern __shared__ __align__(16) unsigned char smem[];
-  float* qs = reinterpret_cast<float*>(smem);          // [128]
-  float* key = qs + kD;                                 // [L] scores
-  int* ids = reinterpret_cast<int*>(key + kMaxLabelKeys);  // [L]
+  const int CL = label_cand_slots(n, pos_permille);
+  uint32_t* key = reinterpret_cast<uint32_t*>(smem);        // [n]
+  uint32_t* ck = key + (n + 3) / 4 * 4;                     // [CL]
+  int* ci = reinterpret_cast<int*>(ck + CL);                // [CL]
+  uint32_t* hist = reinterpret_cast<uint32_t*>(ci + CL);    // [256]
+  uint32_t* misc = hist + 256;                              // [16]
   const int t = threadIdx.x, j = blockIdx.x;
   const int p = min(max(q_pos[j], 0), n - 1);
   const int m = p + 1;
-  int L = 1;
-  while (L < m) L <<= 1;
-  for (int c = t; c < kD; c += kLabNT) qs[c] = __uint_as_float((uint32_t)q[(int64_t)j * kD + c] << 16);
-  __syncthreads();
-  for (int i = t; i < L; i += kLabNT) {
-    float s = -INFINITY;
-    if (i < m) {
-      const uint32_t* kr = reinterpret_cast<const uint32_t*>(k + (int64_t)i * kD);
-      float a = 0.f;
-#pragma unroll 8
-      for (int c2 = 0; c2 < kD / 2; ++c2) {
-        const uint32_t two = kr[c2];
-        a = fmaf(qs[2 * c2], bf16_lo(two), a);
-        a = fmaf(qs[2 * c2 + 1], bf16_hi(two), a);
+  const int P = max(1, (m * pos_permille + 999) / 1000);
+
+  // 1. scores, four rounds of 16 keys' loads in flight
+  {
+    const int sub = t & 15, grp = t >> 4;
+    float qv[8];
+    {
+      const uint4 v = *reinterpret_cast<const uint4*>(q + (int64_t)j * kD + 8 * sub);
+      const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        qv[2 * e] = bf16_lo(w4[e]);
+        qv[2 * e + 1] = bf16_hi(w4[e]);
       }
-      s = a;
     }
-    key[i] = s;
-    ids[i] = i;
+    constexpr int kPerRound = kLabNT / 16, kDepth = 4;
+    for (int i0 = 0; i0 < m; i0 += kPerRound * kDepth) {
+      uint4 v[kDepth];
+#pragma unroll
+      for (int u = 0; u < kDepth; ++u) {
+        const int i = min(i0 + u * kPerRound + grp, m - 1);
+        v[u] = *reinterpret_cast<const uint4*>(k + (int64_t)i * kD + 8 * sub);
+      }
+#pragma unroll
+      for (int u = 0; u < kDepth; ++u) {
+        const uint32_t w4[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+        float a = 0.f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          a = fmaf(qv[2 * e], bf16_lo(w4[e]), a);
+          a = fmaf(qv[2 * e + 1], bf16_hi(w4[e]), a);
+        }
+        a = sum16(a);
+        const int i = i0 + u * kPerRound + grp;
+        if (sub == 0 && i < m) key[i] = score_key(a);
+      }
+    }
   }
   __syncthreads();
-  // bitonic sort: first = higher score, then lower index
-  for (int sz = 2; sz <= L; sz <<= 1) {
+
+  // 2. radix select of the P-th largest key (the keys matching `prefix` on
+  // the bits decided so far always number at least `need`)
+  uint32_t prefix = 0, pmask = 0, need = (uint32_t)P;
+  for (int shift = 24; shift >= 0; shift -= 8) {
+    hist[t] = 0;
+    __syncthreads();
+    for (int i = t; i < m; i += kLabNT) {
+      const uint32_t u = key[i];
+      if ((u & pmask) == prefix) atomicAdd(&hist[(u >> shift) & 255u], 1u);
+    }
+    __syncthreads();
+    const uint32_t c = hist[255 - t];  // thread t: digit 255 - t, counted from the top
+    uint32_t tot;
+    const uint32_t above = block_excl_scan_u32(c, misc, &tot);
+    if (above < need && above + c >= need) {
+      misc[8] = 255u - (uint32_t)t;
+      misc[9] = need - above;
+    }
+    __syncthreads();
+    prefix |= misc[8] << shift;
+    pmask |= 255u << shift;
+    need = misc[9];
+    __syncthreads();
+  }
+  const uint32_t T = prefix;
+
+  // 3. collect: every key above T, and the first `need` keys equal to T in
+  // index order; thread t owns indices [t R, t R + R)
+  {
+    const int R = (m + kLabNT - 1) / kLabNT;
+    const int i0 = t * R, i1 = min(i0 + R, m);
+    uint32_t ngt = 0, neq = 0;
+    for (int i = i0; i < i1; ++i) {
+      const uint32_t u = key[i];
+      ngt += u > T ? 1u : 0u;
+      neq += u == T ? 1u : 0u;
+    }
+    uint32_t tot;
+    const uint32_t pre = block_excl_scan_u32(ngt | (neq << 16), misc, &tot);  // m <= 8192
+    uint32_t gpos = pre & 0xFFFFu, epos = pre >> 16;
+    const uint32_t cgt = (uint32_t)P - need;  // keys above T
+    for (int i = i0; i < i1; ++i) {
+      const uint32_t u = key[i];
+      if (u > T) {
+        ck[gpos] = u;
+        ci[gpos] = i;
+        ++gpos;
+      } else if (u == T) {
+        if (epos < need) {
+          ck[cgt + epos] = u;
+          ci[cgt + epos] = i;
+        }
+        ++epos;
+      }
+    }
+  }
+  int Lc = 1;
+  while (Lc < P) Lc <<= 1;
+  for (int r = P + t; r < Lc; r += kLabNT) {  // padding ranks last
+    ck[r] = 0u;
+    ci[r] = 0x7FFFFFFF;
+  }
+  __syncthreads();
+  for (int sz = 2; sz <= Lc; sz <<= 1) {
     for (int st = sz >> 1; st > 0; st >>= 1) {
-      for (int e = t; e < L / 2; e += kLabNT) {
+      for (int e = t; e < Lc / 2; e += kLabNT) {
         const int lo = 2 * e - (e & (st - 1));
         const int hi = lo + st;
         const bool up = (lo & sz) == 0;  // this half sorts "first" to the front
-        const float ka = key[lo], kb = key[hi];
-        const int ia = ids[lo], ib = ids[hi];
+        const uint32_t ka = ck[lo], kb = ck[hi];
+        const int ia = ci[lo], ib = ci[hi];
         const bool b_first = (kb > ka) || (kb == ka && ib < ia);
         if (b_first == up) {
-          key[lo] = kb; key[hi] = ka;
-          ids[lo] = ib; ids[hi] = ia;
+          ck[lo] = kb; ck[hi] = ka;
+          ci[lo] = ib; ci[hi] = ia;
         }
       }
       __syncthreads();
     }
   }
-  const int P = max(1, (m * pos_permille + 999) / 1000);
+
+  // 4. labels: -1 for keys 0..p, then the ranked positives
+  float* lab = reinterpret_cast<float*>(key);
+  for (int i = t; i < m; i += kLabNT) lab[i] = -1.f;
+  __syncthreads();
+  for (int r = t; r < P; r += kLabNT)
+    lab[ci[r]] = (P == 1) ? s_max : s_max - (s_max - s_min) * (float)r / (float)(P - 1);
+  __syncthreads();
   float* row = S + (int64_t)j * n;
-  for (int r = t; r < m; r += kLabNT) {
-    const float v = (r < P) ? ((P == 1) ? s_max : s_max - (s_max - s_min) * (float)r / (float)(P - 1)) : -1.f;
-    row[ids[r]] = v;
-  }
-  for (int i = m + t; i < n; i += kLabNT) row[i] = 0.f;
+  for (int i = t; i < n; i += kLabNT) row[i] = i < m ? lab[i] : 0.f;
 }
 
 // ------------------------------------------------------------ tiled GEMM
@@ -542,15 +662,18 @@ __global__ void update_kernel(float* __restrict__ W, const float* __restrict__ d
 
 }  // namespace
 
-size_t label_lds_bytes() { return (size_t)(kD + 2 * kMaxLabelKeys) * 4; }
+size_t label_lds_bytes(int n, int pos_permille) {
+  return ((size_t)(n + 3) / 4 * 4 + 2 * (size_t)label_cand_slots(n, pos_permille) + 256 + 16) * 4;
+}
 
 hipError_t launch_hash_labels(const uint16_t* q, const uint16_t* k, const int32_t* q_pos, int J, int n,
                               int pos_permille, float s_max, float s_min, float* S, hipStream_t s) {
   static bool configured = false;
-  const size_t lds = label_lds_bytes();
-  if (!configured) {
+  const size_t lds = label_lds_bytes(n, pos_permille);
+  if (!configured) {  // the largest size any call can need
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&labels_kernel),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+                                       hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       (int)label_lds_bytes(kMaxLabelKeys, 1000));
     if (e != hipSuccess) return e;
     configured = true;
   }

@@ -312,7 +312,8 @@ int hata_stream_read(const void* src, size_t bytes, uint64_t* sink,
  * -1.  labels [J][n] fp32 (device): row j holds those labels for keys
  * 0..q_pos[j] and 0 beyond.  The pages use the top 10% (pos_permille = 100)
  * and labels in [1, 20].  d = 128; 1 <= n <= 8192 (HATA_ERR_UNSUPPORTED
- * above); q_pos is a device int32[J].
+ * above); q_pos is a device int32[J].  q and k 16-byte aligned, labels
+ * 4-byte aligned (HATA_ERR_ALIGN otherwise).
  */
 int hata_hash_labels(const void* q, const void* k, const int32_t* q_pos, int J,
                      int n, int d, int pos_permille, float s_max, float s_min,

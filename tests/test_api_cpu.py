@@ -179,6 +179,8 @@ def test_hash_labels_validation(lib):
     assert call(pm=0) == ESHAPE
     assert call(pm=1001) == ESHAPE
     assert call(k=MIS2) == EALIGN
+    assert call(q=MIS) == EALIGN
+    assert call(k=MIS) == EALIGN
 
 
 def test_hash_train_step_validation(lib):

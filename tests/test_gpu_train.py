@@ -49,6 +49,31 @@ def test_labels_exact_inputs_match_oracle(hata_gpu, n):
     np.testing.assert_allclose(got, ref, rtol=1e-6, atol=1e-6)
 
 
+@pytest.mark.parametrize("n,pm,distinct", [(3000, 1, 0), (3000, 333, 0), (8192, 1000, 0), (2000, 100, 4),
+                                            (5000, 250, 3)])
+def test_labels_fractions_and_heavy_ties_match_oracle(hata_gpu, n, pm, distinct):
+    """Other positive fractions (one per mille up to every key, where the
+    ranking sorts all p + 1 keys) and key rows drawn from only a few distinct
+    rows, so that nearly every query has a run of equal scores at its
+    positive/negative boundary (ties go to the lower key index).  Exact
+    inputs: every score is exact in fp32, so the labels must be equal."""
+    J = 24
+    q, k, pos = _qk(J, n, 9700 + n + pm, exact=True)
+    if distinct:
+        rng = np.random.default_rng(9701 + n)
+        k = k[rng.integers(0, distinct, size=n)]
+    _log(f"labels n={n} permille={pm} distinct={distinct}")
+    S = torch.full((J, n), np.nan, dtype=torch.float32, device="cuda")
+    hata_gpu.hash_labels(bf16_tensor(q), bf16_tensor(k), torch.from_numpy(pos).cuda(), S,
+                         pos_permille=pm, s_max=7.5, s_min=0.5)
+    torch.cuda.synchronize()
+    ref = train.labels(q, k, pos, pos_permille=pm, s_max=7.5, s_min=0.5)
+    got = S.cpu().numpy()
+    np.testing.assert_array_equal(got > 0, ref > 0)
+    np.testing.assert_array_equal(got == -1, ref == -1)
+    np.testing.assert_allclose(got, ref, rtol=1e-6, atol=1e-6)
+
+
 def test_labels_gaussian_inputs_valid(hata_gpu):
     """fp32 scores may order near-ties differently from fp64: every
     disagreement must involve keys whose fp64 scores lie within 1e-4 of the
