@@ -390,14 +390,16 @@ def model_sweep(layers: int = 32, ctxs=(32768, 65536, 131072), reps: int = 10) -
     return res
 
 
-def prefill_bench(N: int = 32768, B: int = 1, Hq: int = 32, Hkv: int = 8, r: int = 128, reps: int = 5) -> dict:
+def prefill_bench(N: int = 32768, B: int = 1, Hq: int = 32, Hkv: int = 8, r: int = 128, reps: int = 5,
+                  paged: bool = True) -> dict:
     """Time hata_prefill on one Llama-3.1-8B-shaped layer (bf16 N(0,1) q/K/V
     and fp32 N(0, 1/128) W_H drawn on the device; parity is in the tests):
     causal attention over an N-token prompt with the prompt keys' codes
     written to the cache.  Algorithmic work: 4 d per visible (query, key)
     pair and query head (the two products), i.e. 2 d Hq N (N + 1) flops, plus
     the encode.  Beside it, the separate bulk encode of the same keys
-    (hata_encode_append), the pass that the fused encode replaces."""
+    (hata_encode_append), the pass that the fused encode replaces, and (paged)
+    hata_prefill_paged on the same data in pools of 256-row pages."""
     import torch
 
     from hash_top_sparse_amd import binding
@@ -435,13 +437,41 @@ def prefill_bench(N: int = 32768, B: int = 1, Hq: int = 32, Hkv: int = 8, r: int
     tf = (flops + enc_flops) / (ms * 1e-3) / 1e12
     log(f"prefill {N} tokens x {Hq}/{Hkv} heads: {ms:.2f} ms ({tf:.0f} TFLOP/s, {tf / 2500:.1%} of bf16 peak); "
         f"separate bulk encode of the keys {enc_ms * 1e3:.0f} us")
+    # the same prompt into K/V/code pools of 256-row pages in shuffled order
+    paged_ms = None
+    if paged:
+        P = 256
+        mp = (N + P - 1) // P
+        num_pages = B * mp
+        bt = torch.randperm(num_pages, generator=g, device=dev).to(torch.int32).view(B, mp)
+        idx = bt.reshape(-1).long()
+
+        def pool(x):
+            c = x.shape[-1]
+            xp = torch.zeros((B, Hkv, mp * P, c), dtype=x.dtype, device=dev)
+            xp[:, :, :N] = x
+            pl = torch.empty((num_pages, Hkv, P, c), dtype=x.dtype, device=dev)
+            pl[idx] = xp.view(B, Hkv, mp, P, c).permute(0, 2, 1, 3, 4).reshape(B * mp, Hkv, P, c)
+            return pl
+
+        Kp, Vp, Cp = pool(K), pool(V), pool(codes)
+        binding.prefill_paged(q, Kp, Vp, W, Cp, bt, seq, N, scale, out)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(reps):
+            binding.prefill_paged(q, Kp, Vp, W, Cp, bt, seq, N, scale, out)
+        e1.record()
+        torch.cuda.synchronize()
+        paged_ms = e0.elapsed_time(e1) / reps
+        log(f"paged prefill ({P}-row pages in shuffled order): {paged_ms:.2f} ms")
+        del Kp, Vp, Cp
     del q, K, V, out
     torch.cuda.empty_cache()
     return {"workload": f"Llama-3.1-8B-shaped layer prefill, B={B}, {Hq}/{Hkv} heads, d=128, r={r}",
             "tokens": B * N, "ms": ms, "tokens_per_s": B * N / (ms * 1e-3),
             "flops": flops + enc_flops, "TFLOPs": tf, "peak_TFLOPs": 2500.0, "frac_of_peak": tf / 2500.0,
             "encode_flops_share": enc_flops / (flops + enc_flops),
-            "separate_bulk_encode_ms": enc_ms}
+            "separate_bulk_encode_ms": enc_ms, "paged_256_row_pages_ms": paged_ms}
 
 
 def paged_bench(config: int = 4, pages=(16, 256), steps: int = 200) -> dict:
@@ -599,7 +629,7 @@ def main() -> int:
     binding.load()
     torch.cuda.set_device(0)
     if args.prefill_run:
-        prefill_bench(reps=1)
+        prefill_bench(reps=1, paged=False)
         log("prefill run done")
         return 0
     if args.train_run:

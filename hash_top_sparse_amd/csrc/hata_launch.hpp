@@ -14,9 +14,14 @@ namespace hata {
 struct PageMap {
   const int32_t* bt = nullptr;
   int max_pages = 0, num_pages = 0, log2P = 0;
-  __device__ __forceinline__ int64_t row(int b, int h, int Hkv, int64_t j) const {
-    int pg = bt[(int64_t)b * max_pages + (int)(j >> log2P)];
-    pg = min(max(pg, 0), num_pages - 1);
+  __device__ __forceinline__ int64_t row(int b, int h, int Hkv, int64_t j) const { return at(page(b, j), h, Hkv, j); }
+  // the pool page holding row j of sequence b (the id clamped into the pool)
+  __device__ __forceinline__ int page(int b, int64_t j) const {
+    const int pg = bt[(int64_t)b * max_pages + (int)(j >> log2P)];
+    return min(max(pg, 0), num_pages - 1);
+  }
+  // pool row of row j of a sequence whose page for j is pg
+  __device__ __forceinline__ int64_t at(int pg, int h, int Hkv, int64_t j) const {
     return (((int64_t)pg * Hkv + h) << log2P) + (j & ((int64_t(1) << log2P) - 1));
   }
 };

@@ -131,20 +131,48 @@ __global__ __launch_bounds__(kNT, 2) void prefill_kernel(PrefillArgs a) {
   // t/16 + 16 i, columns 8 (t % 16) ..; value chunk i is row 4 vkg + i
   const int koff = (t >> 4) * kD + (t & 15) * 8;
   const int voff = 4 * vkg * kD + vc * 8;
-  auto fetch = [&](int tile) {
-    if constexpr (PAGED) {  // every row through the block table (any page size)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int kr = tile * kBK + (t >> 4) + 16 * i, vr = tile * kBK + 4 * vkg + i;
-        kreg[i] = kr < L ? *reinterpret_cast<const uint4*>(a.K + a.pm.row(b, hk, a.Hkv, kr) * kD + (t & 15) * 8)
-                         : make_uint4(0, 0, 0, 0);
-        vreg[i] = vr < L ? *reinterpret_cast<const uint4*>(a.V + a.pm.row(b, hk, a.Hkv, vr) * kD + vc * 8)
-                         : make_uint4(0, 0, 0, 0);
-      }
+  // PAGED: the page ids of the next tile to fetch, loaded one fetch ahead so
+  // that a tile's loads do not wait for the block table (rows clamped below
+  // L).  Pages of >= 64 rows hold whole tiles: one id per tile (tpg), and the
+  // tile is then read like a contiguous one; smaller pages: the ids of this
+  // thread's 4 key rows and 4 value rows.
+  const bool whole = PAGED && a.pm.log2P >= 6;
+  int tpg = 0, kpg[4] = {}, vpg[4] = {};
+  auto load_pages = [&](int tile) {
+    if (whole) {
+      tpg = a.pm.page(b, tile * kBK);
       return;
     }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      kpg[i] = a.pm.page(b, min(tile * kBK + (t >> 4) + 16 * i, L - 1));
+      vpg[i] = a.pm.page(b, min(tile * kBK + 4 * vkg + i, L - 1));
+    }
+  };
+  if constexpr (PAGED) load_pages(0);
+  auto fetch = [&](int tile) {
     const uint16_t* kt = Kh + (int64_t)tile * kBK * kD;
     const uint16_t* vtl = Vh + (int64_t)tile * kBK * kD;
+    if constexpr (PAGED) {
+      if (whole) {
+        const int64_t base = a.pm.at(tpg, hk, a.Hkv, tile * kBK) * kD;
+        kt = a.K + base;
+        vtl = a.V + base;
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int kr = tile * kBK + (t >> 4) + 16 * i, vr = tile * kBK + 4 * vkg + i;
+          kreg[i] = kr < L ? *reinterpret_cast<const uint4*>(a.K + a.pm.at(kpg[i], hk, a.Hkv, kr) * kD +
+                                                             (t & 15) * 8)
+                           : make_uint4(0, 0, 0, 0);
+          vreg[i] = vr < L ? *reinterpret_cast<const uint4*>(a.V + a.pm.at(vpg[i], hk, a.Hkv, vr) * kD + vc * 8)
+                           : make_uint4(0, 0, 0, 0);
+        }
+        if (tile + 1 < ntiles) load_pages(tile + 1);
+        return;
+      }
+      if (tile + 1 < ntiles) load_pages(tile + 1);
+    }
     if (tile * kBK + kBK <= L) {  // a full tile (all but possibly the last)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
