@@ -122,7 +122,7 @@ struct StepArgs {
   float* part;      // [U][kMaxWg][RECP]
   int full_words;
   // paged cache (the PAGED instance): row j of (b, h) is row j % P of page
-  // bt[b * max_pages + j / P] of pools [num_pages][Hkv][P][.], P = 2^log2P >= 256
+  // bt[b * max_pages + j / P] of pools [num_pages][Hkv][P][.], P = 2^log2P >= 16
   const int32_t* bt;
   int max_pages, num_pages, log2P;
 };
@@ -1043,8 +1043,18 @@ hipError_t launch_decode_step(const StepPlan& p, const uint16_t* q, const uint16
   }
 }
 
+template <int G>
+static hipError_t launch_paged_g(const StepPlan& p, const StepArgs& a, hipStream_t s) {
+  switch (p.R) {
+    case 32: return launch_step_gsr<G, false, 32, true>(p, a, s);
+    case 64: return launch_step_gsr<G, false, 64, true>(p, a, s);
+    case 256: return launch_step_gsr<G, false, 256, true>(p, a, s);
+    default: return launch_step_gsr<G, false, 128, true>(p, a, s);
+  }
+}
+
 bool decode_step_paged_fusable(const StepPlan& p, int page_rows) {
-  return p.fused && p.R == 128 && page_rows >= 16 && p.lds_bytes + kMaxPgl * 4 <= 159 * 1024;
+  return p.fused && page_rows >= 16 && p.lds_bytes + kMaxPgl * 4 <= 159 * 1024;
 }
 
 hipError_t launch_decode_step_paged(const StepPlan& p, const uint16_t* q, const uint16_t* K, const uint16_t* V,
@@ -1065,10 +1075,10 @@ hipError_t launch_decode_step_paged(const StepPlan& p, const uint16_t* q, const 
   a.full_words = p.full_words;
   a.bt = pm.bt; a.max_pages = pm.max_pages; a.num_pages = pm.num_pages; a.log2P = pm.log2P;
   switch (p.G) {
-    case 1: return launch_step_gsr<1, false, 128, true>(p, a, s);
-    case 2: return launch_step_gsr<2, false, 128, true>(p, a, s);
-    case 4: return launch_step_gsr<4, false, 128, true>(p, a, s);
-    case 8: return launch_step_gsr<8, false, 128, true>(p, a, s);
+    case 1: return launch_paged_g<1>(p, a, s);
+    case 2: return launch_paged_g<2>(p, a, s);
+    case 4: return launch_paged_g<4>(p, a, s);
+    case 8: return launch_paged_g<8>(p, a, s);
     default: return hipErrorInvalidValue;
   }
 }

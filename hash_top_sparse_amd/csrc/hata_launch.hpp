@@ -84,7 +84,8 @@ hipError_t launch_decode_step(const StepPlan& p, const uint16_t* q, const uint16
                               float* out, int32_t* idx_out, unsigned char* ws, hipStream_t s);
 
 // The fused step over a paged cache (K, V, codes in page pools, pm): plans
-// whose step is fused and r = 128 (any page size of at least 16 rows).
+// whose step is fused, any code width, any page size of at least 16 rows,
+// while the page-id list still fits in LDS beside the step's own.
 bool decode_step_paged_fusable(const StepPlan& p, int page_rows);
 hipError_t launch_decode_step_paged(const StepPlan& p, const uint16_t* q, const uint16_t* K, const uint16_t* V,
                                     const float* W, uint64_t* codes, const PageMap& pm, int Hq, int Hkv,

@@ -258,11 +258,11 @@ int hata_prefill_paged(const void* q, const void* K_pool, const void* V_pool,
  * Same steps and results as hata_decode_step on the gathered contiguous
  * cache: the key row n_b-1 is encoded and its code written through the
  * table, every code row 0..n_b-1 is scored, top-k by (score, index), and
- * the attention gathers the kept K/V rows through the table.  With r = 128
- * and a shape whose step fits on chip, the step runs as hata_decode_step's
- * single kernel (page ids of each workgroup's rows loaded with its first
- * loads); otherwise as separate kernels (row encode, Hamming scan, top-k,
- * gather attention).  page_rows a power of two in [16, 65536]; q, the pools
+ * the attention gathers the kept K/V rows through the table.  When the
+ * step fits on chip (any r), it runs as hata_decode_step's single kernel
+ * (page ids of each workgroup's rows loaded with its first loads);
+ * otherwise as separate kernels (row encode, Hamming scan, top-k, gather
+ * attention).  page_rows a power of two in [16, 65536]; q, the pools
  * 16-byte aligned; idx_out [B][Hkv][k] optional.  ws: hata_workspace_bytes(
  * HATA_OP_DECODE_STEP_PAGED, ...), zeroed once before first use (as for
  * hata_decode_step).

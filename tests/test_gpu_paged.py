@@ -176,3 +176,40 @@ def test_fused_paged_step_full_size_bitwise(hata_gpu, P):
     assert torch.equal(idx, cidx)
     assert torch.equal(out, cout)
     assert torch.equal(_gather(Cp, bt, N), codes)
+
+
+@pytest.mark.slow
+def test_staged_paged_step_equals_fused_contiguous_step(hata_gpu):
+    """A shape whose fused step fits on chip only without the paged step's
+    page-id list (one unit of 8 query heads, 256-bit codes, k = 4096,
+    1,114,112 cached rows: 17,408 per workgroup), so the paged step runs its
+    separate kernels (row encode, Hamming scan, multi-workgroup top-k,
+    gather attention) while the contiguous one is fused: kept sets and codes
+    equal, outputs close."""
+    B, Hq, Hkv, N, k, r, P = 1, 8, 1, 1114112, 4096, 256, 64
+    _log(f"staged paged route N={N} r={r} k={k} P={P}")
+    g = torch.Generator(device="cuda")
+    g.manual_seed(9800)
+    q = torch.randn((B, Hq, 128), generator=g, device="cuda").to(torch.bfloat16)
+    K = torch.randn((B, Hkv, N, 128), generator=g, device="cuda").to(torch.bfloat16)
+    V = torch.randn((B, Hkv, N, 128), generator=g, device="cuda").to(torch.bfloat16)
+    W = torch.randn((Hkv, 128, r), generator=g, device="cuda") / np.sqrt(128.0)
+    codes = torch.zeros((B, Hkv, N, r // 64), dtype=torch.int64, device="cuda")
+    hata_gpu.encode_append(K, W, codes, n_new=N - 1)  # row N-1 is written by the steps
+    seq = torch.full((B,), N, dtype=torch.int32, device="cuda")
+    mp = N // P
+    bt = torch.randperm(mp + 5, generator=g, device="cuda")[:mp].to(torch.int32).view(B, mp)
+    Kp, Vp = _paginate(K, P, bt, mp + 5), _paginate(V, P, bt, mp + 5)
+    Cp = _paginate(codes, P, bt, mp + 5)
+    ws = hata_gpu.alloc_workspace(hata_gpu.OP_DECODE_STEP_PAGED, B, Hq, Hkv, N, k, r=r)
+    out = torch.zeros((B, Hq, 128), dtype=torch.float32, device="cuda")
+    idx = torch.zeros((B, Hkv, k), dtype=torch.int32, device="cuda")
+    hata_gpu.decode_step_paged(q, Kp, Vp, W, Cp, bt, seq, N, k, 0.0883883, out, ws, idx_out=idx)
+    cws = hata_gpu.alloc_workspace(hata_gpu.OP_DECODE_STEP, B, Hq, Hkv, N, k, r=r)
+    cout, cidx = torch.zeros_like(out), torch.zeros_like(idx)
+    hata_gpu.decode_step(q, K, V, W, codes, seq, N, k, 0.0883883, cout, cws, cidx)
+    torch.cuda.synchronize()
+    assert hata_gpu.workspace_check(ws) == 0 and hata_gpu.workspace_check(cws) == 0
+    assert torch.equal(_gather(Cp, bt, N), codes)
+    assert torch.equal(idx, cidx)
+    assert_close(out.cpu().numpy(), cout.cpu().numpy().astype(np.float64), "staged paged vs fused contiguous")
