@@ -534,8 +534,17 @@ __global__ __launch_bounds__(256) void mask_cols_kernel(const float* __restrict_
 // rows of X [rows][cols]: out[r] = sum_c X[r][c] (sums S_j) or columns
 __global__ void row_sums_kernel(const float* __restrict__ X, int rows, int cols, float* __restrict__ out) {
   const int r = blockIdx.x;
-  float a = 0.f;
-  for (int c = threadIdx.x; c < cols; c += 256) a += X[(int64_t)r * cols + c];
+  const float* x = X + (int64_t)r * cols;
+  // eight running sums per thread (columns c + 256 u), so eight loads are in
+  // flight; added in a fixed order
+  float a8[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  int c = threadIdx.x;
+  for (; c + 7 * 256 < cols; c += 8 * 256) {
+#pragma unroll
+    for (int u = 0; u < 8; ++u) a8[u] += x[c + 256 * u];
+  }
+  for (; c < cols; c += 256) a8[0] += x[c];
+  const float a = ((a8[0] + a8[1]) + (a8[2] + a8[3])) + ((a8[4] + a8[5]) + (a8[6] + a8[7]));
   __shared__ float red[256];
   red[threadIdx.x] = a;
   __syncthreads();
