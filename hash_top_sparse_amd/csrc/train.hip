@@ -588,14 +588,18 @@ __global__ void col_sums_finish_kernel(const float* __restrict__ part, int cols,
 // part[3 row] = rs * ||H_row||^2 (for the similarity term),
 // part[3 row + 1] = H_row . P_row and part[3 row + 2] = ||Cb_row||^2 (the
 // balance term; Cb = M Hk for the queries, null for the keys).
-__global__ void dz_kernel(const float* __restrict__ H, const float* __restrict__ P,
-                          const float* __restrict__ Qb, const float* __restrict__ Cb,
-                          const float* __restrict__ rs, int rows, int r,
-                          float eps, float eta, float* __restrict__ dZ, float* __restrict__ part) {
-  const int row = blockIdx.x;
+__global__ __launch_bounds__(256) void dz_kernel(const float* __restrict__ H, const float* __restrict__ P,
+                                                 const float* __restrict__ Qb, const float* __restrict__ Cb,
+                                                 const float* __restrict__ rs, int rows, int r, float eps, float eta,
+                                                 float* __restrict__ dZ, float* __restrict__ part) {
+  // one wave per row (four rows per workgroup); the row's partial sums are
+  // added per lane in column order, then over the wave in a fixed order
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= rows) return;  // the whole wave
   float a1 = 0.f, a2 = 0.f, a3 = 0.f;
   const float w = rs[row];
-  for (int c = threadIdx.x; c < r; c += blockDim.x) {
+  for (int c = lane; c < r; c += 64) {
     const int64_t e = (int64_t)row * r + c;
     const float h = H[e], pp = P[e];
     float g = 2.f * eps * (w * h - pp);
@@ -605,18 +609,20 @@ __global__ void dz_kernel(const float* __restrict__ H, const float* __restrict__
     a2 += h * pp;
     if (Cb) a3 += Cb[e] * Cb[e];
   }
-  __shared__ float red[3][256];
-  red[0][threadIdx.x] = a1;
-  red[1][threadIdx.x] = a2;
-  red[2][threadIdx.x] = a3;
-  __syncthreads();
-  for (int o = blockDim.x / 2; o > 0; o >>= 1) {
-    if ((int)threadIdx.x < o)
-      for (int u = 0; u < 3; ++u) red[u][threadIdx.x] += red[u][threadIdx.x + o];
-    __syncthreads();
+  auto wave_sum = [](float v) {
+    const int s16 = __float_as_int(sum16(v));  // each group of 16 lanes holds its sum
+    return ((__int_as_float(__builtin_amdgcn_readlane(s16, 0)) + __int_as_float(__builtin_amdgcn_readlane(s16, 16))) +
+            __int_as_float(__builtin_amdgcn_readlane(s16, 32))) +
+           __int_as_float(__builtin_amdgcn_readlane(s16, 48));
+  };
+  a1 = wave_sum(a1);
+  a2 = wave_sum(a2);
+  a3 = wave_sum(a3);
+  if (lane == 0) {
+    part[3 * row] = a1;
+    part[3 * row + 1] = a2;
+    part[3 * row + 2] = a3;
   }
-  if (threadIdx.x == 0)
-    for (int u = 0; u < 3; ++u) part[3 * row + u] = red[u][0];
 }
 
 // Final loss terms and the decorrelation factor, one workgroup of 1024
@@ -757,9 +763,9 @@ hipError_t launch_hash_train_step(const TrainPlan& p, const uint16_t* q, const u
   hipLaunchKernelGGL(col_sums_finish_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, part, n, cs);
   HATA_TRY(hipGetLastError());
   // dZ and the per-row loss parts
-  hipLaunchKernelGGL(dz_kernel, dim3(J), dim3(128), 0, s, Hq, SHk, (const float*)nullptr, (const float*)Cm, rs, J, r,
+  hipLaunchKernelGGL(dz_kernel, dim3((unsigned)((J + 3) / 4)), dim3(256), 0, s, Hq, SHk, (const float*)nullptr, (const float*)Cm, rs, J, r,
                      eps, eta, dZq, partq);
-  hipLaunchKernelGGL(dz_kernel, dim3(n), dim3(128), 0, s, Hk, StHq, (const float*)MtC, (const float*)nullptr, cs, n,
+  hipLaunchKernelGGL(dz_kernel, dim3((unsigned)((n + 3) / 4)), dim3(256), 0, s, Hk, StHq, (const float*)MtC, (const float*)nullptr, cs, n,
                      r, eps, eta, dZk, partk);
   HATA_TRY(hipGetLastError());
   // dW = sigma (Q^T dZq + K^T dZk)
