@@ -163,7 +163,7 @@ def read_peak(gib: int = 4, reps: int = 5) -> float:
 
 
 def measure(cfg_id: int, steps: int, warmup: int, dense_steps: int, layers: int, use_graph: bool,
-            with_bulk: bool, with_qk: bool = True, r: int = 128):
+            with_bulk: bool, with_qk: bool = True, r: int = 128, read_rate: float | None = None):
     """Time the fused step (and the dense baseline) on one workload; returns
     (result dict, inputs)."""
     import torch
@@ -303,15 +303,34 @@ def measure(cfg_id: int, steps: int, warmup: int, dense_steps: int, layers: int,
         for i in range(4):
             dstep(i)
         torch.cuda.synchronize()
+        # timed like the fused step: a captured graph of the steps (eagerly
+        # when the fused step is timed eagerly)
+        if use_graph:
+            gd = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(gd):
+                for i in range(dense_steps):
+                    dstep(i)
+            gd.replay()
+            torch.cuda.synchronize()
         ev0.record()
-        for i in range(dense_steps):
-            dstep(i)
+        if use_graph:
+            gd.replay()
+        else:
+            for i in range(dense_steps):
+                dstep(i)
         ev1.record()
         torch.cuda.synchronize()
         d_ms = ev0.elapsed_time(ev1) / dense_steps
         dgb = dense_bytes(B, Hq, Hkv, N) / (d_ms * 1e-3) / 1e9
         dense = {"ms_per_step": d_ms, "GBs": dgb, "frac_of_peak": dgb / PEAK_HBM_GBS,
-                 "speedup_of_hata": d_ms / ms_step}
+                 "speedup_of_hata": d_ms / ms_step,
+                 "timing": "graph of the steps, HIP events" if use_graph else "eager, HIP events"}
+        if read_rate:
+            # a dense pass that moved its bytes at the measured read rate
+            floor_ms = dense_bytes(B, Hq, Hkv, N) / (read_rate * 1e9) * 1e3
+            dense["floor_ms_at_measured_read_rate"] = floor_ms
+            dense["speedup_of_hata_vs_floor"] = floor_ms / ms_step
+            dense["frac_of_measured_read_rate"] = dgb / read_rate
         log(f"dense: {d_ms * 1e3:.1f} us/step, {dgb:.0f} GB/s, hata speedup {d_ms / ms_step:.2f}x")
     res = {"workload": shape.name, "code_bits": r, "ms_per_step": ms_step, "steps_per_s": 1000.0 / ms_step,
            "tokens_per_s": B * 1000.0 / ms_step,
@@ -586,6 +605,102 @@ def train_bench(J: int = 512, n: int = 8192, r: int = 128, steps: int = 20) -> d
             "step_TFLOPs": tf, "frac_of_fp32_peak": tf / 157.3, "loss_after": loss.cpu().tolist()}
 
 
+TRACE_POINTS = ("start", "qcodes", "scanned", "hist", "published", "wait1", "windows", "threshold",
+                "compacted", "attended", "record", "wait2", "end")
+
+
+def phase_trace(cfg_id: int = 4, steps: int = 200, layers: int = 0) -> dict:
+    """Per-phase timeline of the fused step, from the phase-trace build of the
+    library (libhata_trace.so: thread 0 of every workgroup reads the 100 MHz
+    real-time counter at each phase boundary and stores the readings in the
+    workspace, past the plain build's layout).  Eager steps over rotated
+    layer caches as in the headline measurement; after each step the trace
+    area is copied aside on the stream.  Reported per phase boundary: the
+    median over steps of the median and of the latest workgroup's time since
+    the step's first workgroup started, and the median time each workgroup
+    spends in each phase."""
+    import torch
+
+    from hash_top_sparse_amd import binding, synth
+
+    binding.load(binding.TRACE_LIB_PATH)
+    dev = torch.device("cuda:0")
+    shape = synth.CONFIGS[cfg_id]
+    B, Hq, Hkv, N, k = shape.B, shape.Hq, shape.Hkv, shape.N, shape.k
+    U = B * Hkv
+    L = layers or max(2, min(64, int(np.ceil(1.5e9 / step_bytes(B, Hq, Hkv, N, k)))))
+    inp = synth.make_inputs(shape)
+    bf = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+    q0, K0, V0 = bf(inp.q), bf(inp.K), bf(inp.V)
+    W = torch.from_numpy(inp.W).to(dev)
+    seq = torch.from_numpy(inp.seq_lens).to(dev)
+    codes0 = torch.zeros((B, Hkv, N, 2), dtype=torch.int64, device=dev)
+    binding.encode_append(K0, W, codes0, n_new=N)
+    bufs = [(K0.clone() if l else K0, V0.clone() if l else V0, codes0.clone() if l else codes0)
+            for l in range(L)]
+    ws = binding.alloc_workspace(binding.OP_DECODE_STEP, B, Hq, Hkv, N, k, device=dev)
+    # workgroups per unit as the library plans them for these sizes (a
+    # fused step within the LDS limit); the trace area is the workspace's
+    # last ceil(U * Wg * 128 / 256) * 256 bytes
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    Wg = max(1, min(cus // U, 64, -(-N // 256)))
+    assert -(-N // Wg) <= 32768, "the phase trace covers shapes of at most 32768 tokens per workgroup"
+    nbytes = -(-U * Wg * 128 // 256) * 256
+    off = ws.numel() - nbytes
+    out = torch.zeros((B, Hq, 128), dtype=torch.float32, device=dev)
+    rec = torch.zeros((steps, nbytes), dtype=torch.uint8, device=dev)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(2 * steps)]
+    for i in range(16):
+        Kl, Vl, cl = bufs[i % L]
+        binding.decode_step(q0, Kl, Vl, W, cl, seq, N, k, inp.scale, out, ws)
+    torch.cuda.synchronize()
+    for i in range(steps):
+        Kl, Vl, cl = bufs[i % L]
+        evs[2 * i].record()
+        binding.decode_step(q0, Kl, Vl, W, cl, seq, N, k, inp.scale, out, ws)
+        evs[2 * i + 1].record()
+        rec[i].copy_(ws[off:])
+    torch.cuda.synchronize()
+    if binding.workspace_check(ws):
+        raise RuntimeError("workspace error word set during the phase trace")
+    ev_us = np.array([evs[2 * i].elapsed_time(evs[2 * i + 1]) * 1e3 for i in range(steps)])
+    ts = rec.cpu().numpy().view(np.uint64).reshape(steps, -1, 16).astype(np.int64)[:, :U * Wg]
+    nwg = int((ts[0, :, 0] != 0).sum())
+    assert nwg == U * Wg, f"{nwg} workgroups left timestamps, {U * Wg} expected"
+    ts = ts[:, :, :len(TRACE_POINTS)]
+    tick_ns = 10.0  # s_memrealtime runs at 100 MHz
+    t0 = ts[:, :, 0].min(axis=1)[:, None]
+    valid = ts != 0
+    rel = np.where(valid, (ts - t0[:, :, None]) * tick_ns / 1e3, np.nan)  # us since the first start
+    med_rel = np.nanmedian(np.nanmedian(rel, axis=1), axis=0)
+    max_rel = np.nanmedian(np.nanmax(rel, axis=1), axis=0)
+    phases = {}
+    prev = None
+    for j, name in enumerate(TRACE_POINTS):
+        col = rel[:, :, j]
+        if np.isnan(col).all():
+            continue
+        entry = {"median_since_first_start_us": float(med_rel[j]), "latest_since_first_start_us": float(max_rel[j])}
+        if prev is not None:
+            dur = rel[:, :, j] - rel[:, :, prev]
+            entry["median_phase_us"] = float(np.nanmedian(dur))
+            entry["p90_phase_us"] = float(np.nanpercentile(dur, 90))
+        phases[name] = entry
+        prev = j
+    res = {"workload": shape.name, "workgroups": nwg, "units": U, "steps": steps, "layers": L,
+           "kernel_us_hip_events_median": float(np.median(ev_us)),
+           "span_first_start_to_last_end_us_median": float(max_rel[len(TRACE_POINTS) - 1]),
+           "start_spread_us_median": float(max_rel[0]), "phases": phases}
+    log(f"phase trace {shape.name}: {nwg} workgroups, {steps} eager steps, events {np.median(ev_us):.2f} us/step")
+    log(f"{'boundary':>10} {'median':>8} {'latest':>8} {'phase':>8} {'p90':>8}  (us)")
+    for name, e in phases.items():
+        log(f"{name:>10} {e['median_since_first_start_us']:8.2f} {e['latest_since_first_start_us']:8.2f} "
+            f"{e.get('median_phase_us', 0.0):8.2f} {e.get('p90_phase_us', 0.0):8.2f}")
+    del bufs
+    torch.cuda.empty_cache()
+    return res
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -598,19 +713,22 @@ def main() -> int:
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="launch the timed steps eagerly")
-    ap.add_argument("--sweep", action="store_true", help="also time the other workloads (2, 3, 5)")
+    ap.add_argument("--no-sweep", action="store_true",
+                    help="skip the other workloads (32K batch 1, 64K batch 4, 32K MHA batch 8, 4K tiny)")
     ap.add_argument("--no-prefill", action="store_true", help="skip the 32K-token prefill measurement")
     ap.add_argument("--no-paged", action="store_true", help="skip the paged-cache step measurement")
-    ap.add_argument("--train", action="store_true",
-                    help="also time the hash-weight training step (labels + one gradient step, one head)")
-    ap.add_argument("--width-sweep", action="store_true",
-                    help="also time the workload with 32-, 64- and 256-bit codes")
-    ap.add_argument("--model-sweep", action="store_true",
-                    help="also time 32-layer decode (one graph per token) at 32K/64K/128K against dense")
+    ap.add_argument("--no-train", action="store_true",
+                    help="skip the hash-weight training step (labels + one gradient step, one head)")
+    ap.add_argument("--no-width-sweep", action="store_true",
+                    help="skip the workload with 32-, 64- and 256-bit codes")
+    ap.add_argument("--no-model-sweep", action="store_true",
+                    help="skip the 32-layer decode (one graph per token) at 32K/64K/128K against dense")
     ap.add_argument("--prefill-run", action="store_true",
                     help="short run for hardware-counter passes on the prefill: one 32K-token prefill")
     ap.add_argument("--train-run", action="store_true",
                     help="only the training step, 20 calls (for kernel traces)")
+    ap.add_argument("--phase-trace", action="store_true",
+                    help="only the per-phase timeline of the fused step (phase-trace build of the library)")
     ap.add_argument("--pmc-run", action="store_true",
                     help="short run for hardware-counter passes: 32 eager fused steps over the layer "
                          "caches, then one plain device copy of 1 GiB as the byte-counter reference")
@@ -626,8 +744,12 @@ def main() -> int:
     from hash_top_sparse_amd import binding
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
-    binding.load()
     torch.cuda.set_device(0)
+    if args.phase_trace:
+        for c in ((args.config,) if args.config != 4 else (4, 2, 1)):
+            print(json.dumps({"phase_trace": phase_trace(c, steps=200)}), flush=True)
+        return 0
+    binding.load()
     if args.prefill_run:
         prefill_bench(reps=1, paged=False)
         log("prefill run done")
@@ -646,24 +768,29 @@ def main() -> int:
         torch.cuda.synchronize()
         log("pmc run done: reference copy of 1073741824 bytes")
         return 0
+    peak_meas = read_peak()
+    log(f"streaming read of 4 GiB: {peak_meas:.0f} GB/s")
     head, inp = measure(args.config, args.steps, args.warmup, 0 if args.no_dense else args.dense_steps,
-                        args.layers, not args.no_graph, with_bulk=True)
+                        args.layers, not args.no_graph, with_bulk=True, read_rate=peak_meas)
     shape = inp.shape
+    # the other workloads and code widths: graphs of at least 256 steps
+    # (200 eager ones for the spread), whatever --steps is
+    sub_steps = max(256, args.steps // 8)
     sweep = None
-    if args.sweep:
+    if not args.no_sweep:
         sweep = {}
         for c in (2, 3, 5, 1):
             if c == args.config:
                 continue
-            r, _ = measure(c, max(256, args.steps // 8), 16, 0 if args.no_dense else 32, 0,
-                           not args.no_graph, with_bulk=False, with_qk=False)
+            r, _ = measure(c, sub_steps, 16, 0 if args.no_dense else 32, 0,
+                           not args.no_graph, with_bulk=False, with_qk=False, read_rate=peak_meas)
             sweep[str(c)] = r
 
     wsweep = None
-    if args.width_sweep:
+    if not args.no_width_sweep:
         wsweep = {}
         for r in (32, 64, 256):
-            rr, _ = measure(args.config, max(256, args.steps // 4), 16, 0, 0, not args.no_graph,
+            rr, _ = measure(args.config, sub_steps, 16, 0, 0, not args.no_graph,
                             with_bulk=False, with_qk=False, r=r)
             B_, Hkv_, N_ = shape.B, shape.Hkv, shape.N
             # the stored rows: ceil(r/64) words, so 32-bit codes move 8 bytes a row
@@ -673,10 +800,8 @@ def main() -> int:
                               "bytes_per_step": rr["bytes_per_step"], "stored_bytes_per_step": layout}
     pbench = None if args.no_prefill else prefill_bench()
     gbench = None if args.no_paged else paged_bench(args.config)
-    msweep = model_sweep() if args.model_sweep else None
-    tbench = train_bench() if args.train else None
-    peak_meas = read_peak()
-    log(f"streaming read of 4 GiB: {peak_meas:.0f} GB/s")
+    msweep = None if args.no_model_sweep else model_sweep()
+    tbench = None if args.no_train else train_bench()
     cpu = None
     if not args.no_cpu:
         cpu = cpu_baseline(inp, args.cpu_budget)
@@ -684,7 +809,7 @@ def main() -> int:
 
     ms_step = head["ms_per_step"]
     res = {
-        "metric": "decode steps/s and HBM GB/s (% of peak) for hata_decode_step at 128K ctx",
+        "metric": "decode steps/s and HBM GB/s (% of peak) for hata_decode_step at 32K\u2013128K ctx",
         "value": 1000.0 / ms_step,
         "unit": "steps/s",
         "n_gpus": 1,

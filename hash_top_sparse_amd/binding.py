@@ -19,6 +19,7 @@ import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libhata.so")
+TRACE_LIB_PATH = os.path.join(_HERE, "libhata_trace.so")
 
 OP_TOPK = 1
 OP_SPARSE_DECODE = 2
@@ -35,14 +36,17 @@ class HataError(RuntimeError):
         self.status = status
 
 
-def load() -> ctypes.CDLL:
-    """Load libhata.so (built in-tree by hash_top_sparse_amd/build.py)."""
+def load(path: str | None = None) -> ctypes.CDLL:
+    """Load libhata.so (built in-tree by hash_top_sparse_amd/build.py).  The
+    first call fixes the library: `path` may name the phase-trace build
+    (libhata_trace.so) instead, for the phase measurement of bench.py."""
     global _lib
     if _lib is not None:
         return _lib
-    if not os.path.exists(LIB_PATH):
-        raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m hash_top_sparse_amd.build`")
-    L = ctypes.CDLL(LIB_PATH)
+    path = path or LIB_PATH
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with `python -m hash_top_sparse_amd.build`")
+    L = ctypes.CDLL(path)
     P, I, I64, F, SZ = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
     sig = {
         "hata_status_string": ([I], ctypes.c_char_p),
@@ -58,6 +62,7 @@ def load() -> ctypes.CDLL:
         "hata_workspace_bytes": ([I, I, I, I, I, I, I64, I], SZ),
         "hata_workspace_reset": ([P, SZ, P], I),
         "hata_workspace_check": ([P, SZ, ctypes.POINTER(I), P], I),
+        "hata_workspace_set_spin_limit": ([P, SZ, ctypes.c_uint32, P], I),
         "hata_stream_read": ([P, SZ, P, SZ, P], I),
         "hata_hash_labels": ([P, P, P, I, I, I, I, F, F, P, P], I),
         "hata_hash_train_step": ([P, P, P, P, I, I, I, I, F, F, F, F, F, P, P, P, P, SZ, P], I),
@@ -80,6 +85,7 @@ def exported_symbols() -> list[str]:
                         "hata_sparse_decode", "hata_decode_step", "hata_decode_step_qk",
                         "hata_dense_decode",
                         "hata_workspace_bytes", "hata_workspace_reset", "hata_workspace_check",
+                        "hata_workspace_set_spin_limit",
                         "hata_stream_read", "hata_hash_labels", "hata_hash_train_step",
                         "hata_hash_train_workspace_bytes", "hata_prefill", "hata_decode_step_paged",
                         "hata_prefill_paged")
@@ -352,6 +358,10 @@ def hash_train_step(q: torch.Tensor, k: torch.Tensor, q_pos: torch.Tensor, label
 
 def workspace_reset(ws: torch.Tensor, stream=None) -> None:
     _check(load().hata_workspace_reset(_ptr(ws), ws.numel(), _stream(stream)))
+
+
+def workspace_set_spin_limit(ws: torch.Tensor, polls: int, stream=None) -> None:
+    _check(load().hata_workspace_set_spin_limit(_ptr(ws), ws.numel(), int(polls), _stream(stream)))
 
 
 def workspace_check(ws: torch.Tensor, stream=None) -> int:

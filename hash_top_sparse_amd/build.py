@@ -3,6 +3,11 @@
 Every source is compiled on each call (object files go to _build/, then one
 shared library is linked next to this file).  Packed-fp32 instruction
 generation is disabled for all device code.
+
+A second library, libhata_trace.so, is linked from the same objects except
+the fused decode step, which is compiled with HATA_PHASE_TRACE: its kernel
+stores a timestamp per phase and workgroup into the workspace.  It serves
+the phase measurement of bench.py (--phase-trace) only.
 """
 from __future__ import annotations
 
@@ -16,6 +21,8 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libhata.so")
+TRACE_LIB = os.path.join(HERE, "libhata_trace.so")
+TRACED = "decode_step.hip"
 ARCH = "gfx950"
 
 HIP_SOURCES = ["encode.hip", "encode_bulk.hip", "score_select.hip", "attention.hip",
@@ -27,10 +34,10 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", os.path.
 DEVICE_ONLY = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 
 
-def _compile(src: str) -> str:
+def _compile(src: str, trace: bool = False) -> str:
     path = os.path.join(CSRC, src)
-    obj = os.path.join(BUILD, src + ".o")
-    cmd = ["hipcc", *COMMON, "-c", path, "-o", obj]
+    obj = os.path.join(BUILD, src + (".trace.o" if trace else ".o"))
+    cmd = ["hipcc", *COMMON, *(["-DHATA_PHASE_TRACE"] if trace else []), "-c", path, "-o", obj]
     if src.endswith(".hip"):
         cmd[1:1] = DEVICE_ONLY
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -39,20 +46,31 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(BUILD, exist_ok=True)
-    srcs = [s for s in HIP_SOURCES + CPP_SOURCES if os.path.exists(os.path.join(CSRC, s))]
-    with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
-        objs = list(ex.map(_compile, srcs))
-    tmp = LIB + ".tmp%d" % os.getpid()
+def _link(objs: list, lib: str) -> None:
+    tmp = lib + ".tmp%d" % os.getpid()
     # -z defs: an unresolved symbol fails the link instead of the first load
     cmd = ["hipcc", f"--offload-arch={ARCH}", "-shared", "-fPIC", "-Wl,-z,defs", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = False, trace: bool = True) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    srcs = [s for s in HIP_SOURCES + CPP_SOURCES if os.path.exists(os.path.join(CSRC, s))]
+    jobs = [(s, False) for s in srcs] + ([(TRACED, True)] if trace else [])
+    with cf.ThreadPoolExecutor(max_workers=min(8, len(jobs))) as ex:
+        objs = list(ex.map(lambda j: _compile(*j), jobs))
+    plain = objs[:len(srcs)]
+    _link(plain, LIB)
     if verbose:
         print("built", LIB)
+    if trace:
+        traced = [objs[-1] if src == TRACED else o for src, o in zip(srcs, plain)]
+        _link(traced, TRACE_LIB)
+        if verbose:
+            print("built", TRACE_LIB)
     return LIB
 
 

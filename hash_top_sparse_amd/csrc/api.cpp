@@ -277,8 +277,8 @@ static int decode_step_impl(const void* q, const void* K, const void* V, const f
   auto* qc = reinterpret_cast<uint64_t*>(wsb + p.off_qc);
   auto* sc = reinterpret_cast<uint16_t*>(wsb + p.off_scores);
   auto* part = reinterpret_cast<float*>(wsb + p.off_attn);
-  int32_t* idx = idx_out;
-  if (!idx) return fail(HATA_ERR_UNSUPPORTED, "decode_step: this shape needs idx_out");
+  // the kept list goes to idx_out, or to the workspace when it is NULL
+  int32_t* idx = idx_out ? idx_out : reinterpret_cast<int32_t*>(wsb + p.off_idx);
   auto* hist = reinterpret_cast<uint32_t*>(wsb + p.off_topk);  // unit histograms, filled by the scan
   hipError_t e = hata::launch_fill_zero(hist, (size_t)B * Hkv * (G * r + 1) * 4, s);
   if (e == hipSuccess) e = hata::launch_encode_rows(qb, 1, B, Hq, Hkv, 1, W_H, qc, 1, nullptr, 0, s, r);
@@ -551,6 +551,15 @@ int hata_workspace_reset(void* ws, size_t ws_bytes, void* stream) {
   if (int st = pre_launch("workspace_reset")) return st;
   hipError_t e = hata::launch_fill_zero(ws, ws_bytes, reinterpret_cast<hipStream_t>(stream));
   return check_launch(e, "workspace_reset launch");
+}
+
+int hata_workspace_set_spin_limit(void* ws, size_t ws_bytes, uint32_t polls, void* stream) {
+  if (!ws) return fail(HATA_ERR_NULL, "workspace_set_spin_limit: ws is NULL");
+  if (ws_bytes < 8) return fail(HATA_ERR_WORKSPACE, "workspace_set_spin_limit: workspace too small");
+  if (!aligned(ws, 4)) return fail(HATA_ERR_ALIGN, "workspace_set_spin_limit: ws must be 4-byte aligned");
+  if (int st = pre_launch("workspace_set_spin_limit")) return st;
+  hipError_t e = hata::launch_set_word(static_cast<uint32_t*>(ws) + 1, polls, reinterpret_cast<hipStream_t>(stream));
+  return check_launch(e, "workspace_set_spin_limit launch");
 }
 
 int hata_workspace_check(const void* ws, size_t ws_bytes, int* err_out, void* stream) {

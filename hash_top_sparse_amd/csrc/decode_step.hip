@@ -10,11 +10,12 @@
 // workgroups (co-resident: the host keeps units x Wg <= CU count); workgroup
 // w owns tokens [w*chunk, (w+1)*chunk).  When the unit count is a multiple of
 // 8 the block -> unit map gives a unit only blocks whose indices agree mod 8;
-// the dispatcher deals blocks round-robin over the 8 XCDs, so (once a probe
-// launch has confirmed that on the device) a unit's workgroups share one XCD
-// and its exchanges use plain stores that land in that XCD's L2, read back
-// with device-coherent loads; every writer stamps its XCD id into its window
-// header and readers check it.  Otherwise the stores are device-coherent.
+// the dispatcher deals blocks round-robin over the 8 XCDs, so a unit's
+// workgroups usually share one XCD and one L2.  Each workgroup stamps its XCD
+// id into the workspace early in the launch and, before its first exchange,
+// reads the stamps of its unit: when all of them show its own XCD, its
+// exchange stores are plain stores (they land in that L2, where the readers'
+// device-coherent loads find them); otherwise they are device-coherent.
 //
 // Per workgroup:
 //   1. issue the streaming loads of its code-cache rows (16 bytes per token);
@@ -36,13 +37,13 @@
 //      merge a slice of the unit's outputs by log-sum-exp in fixed order.
 // With Wg == 1 steps 4 and 7 need no exchange.
 //
-// Exchanges between workgroups use agent-coherent stores/loads into their
-// own slots plus one monotonically increasing flag per workgroup; there is
-// no same-address read-modify-write (those serialise at the memory side).
-// Every wait is bounded; a timeout sets bit 0 of the workspace error word.
+// Exchanges between workgroups use stores into their own slots plus one
+// monotonically increasing flag per workgroup; there is no same-address
+// read-modify-write (those serialise at the memory side).  Every wait is
+// bounded: a wait that gives up sets bit 0 of the workspace error word and
+// the workgroup writes NaN into the unit's outputs and -2 into its kept
+// indices instead of results built from incomplete data.
 #include <atomic>
-#include <mutex>
-#include <vector>
 
 #include "hata_device.hpp"
 #include "hata_launch.hpp"
@@ -57,13 +58,51 @@ constexpr int kWinWords = kWinBytes / 4;
 constexpr int kWinHdr = 8;         // uint16 header entries
 constexpr int kWinCap = kWinBytes / 2 - kWinHdr;  // histogram bins a window holds
 constexpr int kMaxChunk = 32768;   // tokens per workgroup (uint16 scores in LDS)
-constexpr uint32_t kSpinLimit = 1u << 22;
+constexpr uint32_t kSpinLimit = 1u << 22;  // default bound on the polls of one wait
 // s_getreg operand for HW_REG_XCC_ID (register 20, bits 0..31): the XCD the
 // wave runs on
 constexpr int kXccIdReg = 20 | (31 << 11);
 constexpr int kShortList = 64;     // kept rows staged in LDS per attention batch
 constexpr int kMaxPgl = kMaxChunk / 16 + 8;   // page ids of one chunk (pages of >= 16 rows)
 constexpr int kPglPerThread = (kMaxPgl + kNT - 1) / kNT;
+
+// Phase-trace build (compiled with HATA_PHASE_TRACE, a separate library used
+// only for measurement): thread 0 of every workgroup reads the 100 MHz
+// real-time counter at the phase boundaries listed below and stores the
+// readings at exit.  Marks sit where the kernel already synchronises, so
+// they add no barrier.
+constexpr int kTracePoints = 16;
+enum TracePoint {
+  kTrStart = 0,      // first instruction
+  kTrQcodes = 1,     // query codes built
+  kTrScanned = 2,    // every owned token scored (appended key included)
+  kTrHist = 3,       // cumulative histogram built
+  kTrPublished = 4,  // window and flag stored
+  kTrWait1 = 5,      // every window of the unit published
+  kTrWindows = 6,    // windows read, headers parsed
+  kTrThreshold = 7,  // threshold and this workgroup's tie quota known
+  kTrCompacted = 8,  // kept list built
+  kTrAttended = 9,   // attention over the kept rows done
+  kTrRecord = 10,    // partial record and flag stored
+  kTrWait2 = 11,     // every record of the unit published
+  kTrEnd = 12        // outputs written
+};
+#ifdef HATA_PHASE_TRACE
+#define HATA_MARK(i) \
+  do {                                                        \
+    if (threadIdx.x == 0) tr_ts[i] = __builtin_amdgcn_s_memrealtime(); \
+  } while (0)
+#define HATA_TRACE_STORE()                                                     \
+  do {                                                                         \
+    if (threadIdx.x == 0) {                                                    \
+      uint64_t* tr_dst = a.trace + ((int64_t)unit * a.Wg + w) * kTracePoints;  \
+      for (int tr_i = 0; tr_i < kTracePoints; ++tr_i) tr_dst[tr_i] = tr_ts[tr_i]; \
+    }                                                                          \
+  } while (0)
+#else
+#define HATA_MARK(i) do {} while (0)
+#define HATA_TRACE_STORE() do {} while (0)
+#endif
 
 template <int G, int R = kR, bool PAGED = false>
 struct Cfg {
@@ -114,8 +153,13 @@ struct StepArgs {
   int Hq, Hkv, k;
   float scale;
   int Wg, chunk, xcd_map, U;
-  int xcd_local;    // exchanges stay on one XCD: plain stores (see CohBuf::st16x)
+  // err[0]: error bits; err[1]: bound on the polls of one wait (0: the
+  // default kSpinLimit); err[2]: never written in practice (see `warm`)
   uint32_t* err;
+  uint32_t* stamps; // [U][kMaxWg]: (epoch << 4) | XCD id of each workgroup
+#ifdef HATA_PHASE_TRACE
+  uint64_t* trace;  // [U * Wg][kTracePoints] timestamps (phase-trace build only)
+#endif
   uint32_t* flags;  // [U][kMaxWg]
   uint32_t* win;    // [U][kMaxWg][kWinWords]
   uint32_t* full;   // [U][kMaxWg][full_words]  (only for overflowing windows)
@@ -140,8 +184,11 @@ __device__ __forceinline__ void map_block(const StepArgs& a, int* unit, int* w) 
   }
 }
 
-// Wave 0 waits until every flag of the unit has reached `target`.
-__device__ __forceinline__ void wait_unit(const StepArgs& a, int unit, uint32_t target) {
+// Wave 0 waits until every flag of the unit has reached `target`, for at
+// most `limit` polls.  Returns true in every thread when it did; on a
+// timeout bit 0 of the error word and *failed (LDS, preset to 0) are set.
+__device__ __forceinline__ bool wait_unit(const StepArgs& a, int unit, uint32_t target, uint32_t limit,
+                                          uint32_t* failed) {
   const int lane = threadIdx.x & 63;
   if ((threadIdx.x >> 6) == 0) {
     const CohBuf fb(a.flags + (int64_t)unit * kMaxWg, kMaxWg * 4);
@@ -150,14 +197,18 @@ __device__ __forceinline__ void wait_unit(const StepArgs& a, int unit, uint32_t 
       const uint32_t v = (lane < a.Wg) ? fb.ld4(lane * 4) : target;
       const bool ok = (int32_t)(v - target) >= 0;
       if (__all(ok)) break;
-      if (++it > kSpinLimit) {
-        if (lane == 0) atomicOr(a.err, 1u);
+      if (++it > limit) {
+        if (lane == 0) {
+          atomicOr(a.err, 1u);
+          *failed = 1u;
+        }
         break;
       }
       __builtin_amdgcn_s_sleep(1);
     }
   }
   __syncthreads();
+  return *failed == 0u;
 }
 
 // In-place inclusive scan of hist[0, NB) with 256 threads.  Also records the
@@ -218,6 +269,10 @@ __global__ __launch_bounds__(kNT) void decode_step_kernel(const StepArgs a) {
   uint16_t* sc = reinterpret_cast<uint16_t*>(smem + ((C::o_sel + (a.k + 1) * 4 + 15) / 16 * 16));
 
   const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
+#ifdef HATA_PHASE_TRACE
+  uint64_t tr_ts[kTracePoints] = {};
+#endif
+  HATA_MARK(kTrStart);
   int unit, w;
   map_block(a, &unit, &w);
   const int b = unit / a.Hkv, h = unit - b * a.Hkv;
@@ -350,6 +405,9 @@ __global__ __launch_bounds__(kNT) void decode_step_kernel(const StepArgs a) {
   // keep the loads above ahead of the length read in the issued code
   __builtin_amdgcn_sched_barrier(0);
   const int n_in = a.seq_lens[b];
+  // bound on the polls of one exchange wait (err[1] == 0: the default)
+  const uint32_t spin_w = a.err[1];
+  const uint32_t spin_limit = spin_w ? spin_w : kSpinLimit;
   const bool bad_len = n_in < 1 || (int64_t)n_in > cap;
   const int n = bad_len ? 1 : n_in;
   const int cnt = max(0, min(n, lo + a.chunk) - lo);
@@ -380,6 +438,12 @@ __global__ __launch_bounds__(kNT) void decode_step_kernel(const StepArgs a) {
   }
   __syncthreads();
   project_pack<G, R>(wr, qf, red, qcode, G);
+  HATA_MARK(kTrQcodes);
+  // this workgroup's XCD stamp for the launch ((epoch + 1) << 4 | XCD id;
+  // epochs are even, so a stamp is never 0, the value of a fresh workspace)
+  const uint32_t own_xcc = (uint32_t)__builtin_amdgcn_s_getreg(kXccIdReg) & 0xFu;
+  const uint32_t own_stamp = ((epoch + 1u) << 4) | own_xcc;
+  if (a.Wg > 1 && t == 0) CohBuf(a.stamps + (int64_t)unit * kMaxWg, kMaxWg * 4).st4(w * 4, own_stamp);
   if constexpr (SEP) {
     // Independent query and key encoders (HashAttention summary page,
     // "Approach"): the workgroup that owns the appended row reloads W's
@@ -476,13 +540,29 @@ __global__ __launch_bounds__(kNT) void decode_step_kernel(const StepArgs a) {
       sc[new_li] = (uint16_t)s_new;
     }
   }
+  // the unit's XCD stamps (wave 0, lane = workgroup), read while the
+  // histogram is scanned
+  uint32_t unit_stamp = own_stamp;
+  if (a.Wg > 1 && wv == 0)
+    unit_stamp = CohBuf(a.stamps + (int64_t)unit * kMaxWg, kMaxWg * 4).ld4(min(lane, a.Wg - 1) * 4);
   __syncthreads();
+  HATA_MARK(kTrScanned);
 
   // ---- 4. threshold
   cum_hist<NB>(hist, misc, misc + 8, (uint32_t)cnt, (uint32_t)k);
+  HATA_MARK(kTrHist);
   const int lo_w = (int)misc[0];   // first nonempty bin (NB if none)
   const int hi_w = (int)misc[1];   // last nonempty bin
   const int tk = (int)misc[2];     // own k-th smallest score (NB if cnt < k)
+  // A wait that gave up: the unit's results would rest on incomplete
+  // exchange data, so this workgroup writes NaN into every output of the
+  // unit and -2 into its kept indices (its error bit is already set).
+  auto fail_unit = [&]() {
+    float* o = a.out + ((int64_t)b * a.Hq + (int64_t)h * G) * kD;
+    for (int e = t; e < G * kD; e += kNT) o[e] = __uint_as_float(0x7FC00000u);
+    if (a.idx_out)
+      for (int j = t; j < k; j += kNT) a.idx_out[(int64_t)unit * k + j] = -2;
+  };
   int T;
   uint32_t lt_all, quota, sel_before = 0, take_self;
   if (a.Wg == 1) {
@@ -492,6 +572,14 @@ __global__ __launch_bounds__(kNT) void decode_step_kernel(const StepArgs a) {
     const uint32_t eq_self = hist[T] - lt_all;
     take_self = eq_self < quota ? eq_self : quota;
   } else {
+    // Plain exchange stores only when every workgroup of the unit has
+    // stamped this launch from this XCD (then every reader shares this L2);
+    // the decision is kept in LDS for the partial records of step 7.
+    bool xl = false;
+    if (wv == 0) {
+      xl = __all(unit_stamp == own_stamp) != 0;
+      if (lane == 0) misc[25] = xl ? 1u : 0u;
+    }
     const CohBuf wbuf(a.win + (int64_t)unit * kMaxWg * kWinWords, kMaxWg * kWinBytes);
     // publish the window [wlo, top] of this workgroup's histogram
     const bool has_k = cnt >= k;
@@ -506,8 +594,7 @@ __global__ __launch_bounds__(kNT) void decode_step_kernel(const StepArgs a) {
         e16[2] = has_k ? 1u : 0u; e16[3] = ovf ? 1u : 0u;
         // cumulative count at the window's last stored bin
         e16[4] = (len > 0) ? hist[wlo + min(len, kWinCap) - 1] : 0u; e16[5] = 0;
-        e16[6] = (uint32_t)__builtin_amdgcn_s_getreg(kXccIdReg) & 0xFu;  // this XCD
-        e16[7] = 0;
+        e16[6] = 0; e16[7] = 0;
       } else {
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
@@ -521,7 +608,7 @@ __global__ __launch_bounds__(kNT) void decode_step_kernel(const StepArgs a) {
       u32x4 v;
       v.x = e16[0] | (e16[1] << 16); v.y = e16[2] | (e16[3] << 16);
       v.z = e16[4] | (e16[5] << 16); v.w = e16[6] | (e16[7] << 16);
-      wbuf.st16x(w * kWinBytes + t * 16, v, a.xcd_local);
+      wbuf.st16x(w * kWinBytes + t * 16, v, xl);
     }
     if (ovf) {
       const CohBuf fbuf(a.full + ((int64_t)unit * kMaxWg + w) * a.full_words, a.full_words * 4);
@@ -532,13 +619,18 @@ __global__ __launch_bounds__(kNT) void decode_step_kernel(const StepArgs a) {
           const int s2 = 2 * i + e;
           two[e] = (s2 < NB) ? hist[s2] : (uint32_t)cnt;
         }
-        fbuf.st4x(i * 4, two[0] | (two[1] << 16), a.xcd_local);
+        fbuf.st4x(i * 4, two[0] | (two[1] << 16), xl);
       }
     }
     wait_all_mem();
     __syncthreads();
-    if (t == 0) CohBuf(a.flags + (int64_t)unit * kMaxWg, kMaxWg * 4).st4x(w * 4, epoch + 1, a.xcd_local);
-    wait_unit(a, unit, epoch + 1);
+    if (t == 0) CohBuf(a.flags + (int64_t)unit * kMaxWg, kMaxWg * 4).st4x(w * 4, epoch + 1, xl);
+    HATA_MARK(kTrPublished);
+    if (!wait_unit(a, unit, epoch + 1, spin_limit, misc + 24)) {
+      fail_unit();
+      return;
+    }
+    HATA_MARK(kTrWait1);
 
     // read every window of the unit: Wg*16 chunks of 16 bytes, all in flight
     {
@@ -572,12 +664,6 @@ __global__ __launch_bounds__(kNT) void decode_step_kernel(const StepArgs a) {
           topc = ln > 0 ? (int)(hv.z & 0xFFFFu) : 0;
         }
         reinterpret_cast<int4*>(whdr)[lane] = make_int4(lw, ln, topc, ow ? 1 : 0);
-        if (a.xcd_local) {
-          // the plain-store exchange needs every writer on this XCD
-          const uint32_t own = (uint32_t)__builtin_amdgcn_s_getreg(kXccIdReg) & 0xFu;
-          const uint32_t wx = (lane < a.Wg) ? (hv.w & 0xFFFFu) : own;
-          if (__ballot(wx != own) && lane == 0) atomicOr(a.err, 4u);
-        }
         // T cannot exceed any workgroup's own k-th smallest score
         const int tmin = wave_min_i((lane < a.Wg && hw) ? tw : NB - 1);
         const int glo = min(wave_min_i(lw), tmin);
@@ -586,6 +672,7 @@ __global__ __launch_bounds__(kNT) void decode_step_kernel(const StepArgs a) {
       }
     }
     __syncthreads();
+    HATA_MARK(kTrWindows);
     const int4* hdr4 = reinterpret_cast<const int4*>(whdr);            // [kMaxWg]
     uint32_t* cpart = reinterpret_cast<uint32_t*>(whdr + 4 * kMaxWg);  // [2][4][64]
     const bool any_ow = misc[18] != 0;
@@ -659,6 +746,7 @@ __global__ __launch_bounds__(kNT) void decode_step_kernel(const StepArgs a) {
     take_self = eq_self < left ? eq_self : left;
     sel_before = pre_lt + (pre_eq < quota ? pre_eq : quota);
   }
+  HATA_MARK(kTrThreshold);
 
   // ---- 5. ordered compaction of the kept tokens (index order).  Thread t
   // owns the run of `run` consecutive tokens from t*run and records, per 32
@@ -732,6 +820,7 @@ __global__ __launch_bounds__(kNT) void decode_step_kernel(const StepArgs a) {
   }
   const int m_self = min(k, (int)(tot_lt + min(tot_eq, take_self)));
   __syncthreads();
+  HATA_MARK(kTrCompacted);
 
   // ---- 6. gather-fused attention over the kept rows (G > 1: batches of
   // kShortList rows staged in LDS, the next batch's loads in flight while a
@@ -751,6 +840,7 @@ __global__ __launch_bounds__(kNT) void decode_step_kernel(const StepArgs a) {
                                   reinterpret_cast<uint4*>(kvs));
   }
 
+  HATA_MARK(kTrAttended);
   // kept indices, written once the attention no longer needs the LDS list
   // (coalesced, and no barrier waits on these stores)
   auto write_idx = [&]() {
@@ -769,10 +859,13 @@ __global__ __launch_bounds__(kNT) void decode_step_kernel(const StepArgs a) {
       const float* r = red + g * kRec;
       outp[e] = (r[1] > 0.f) ? r[2 + c] / r[1] : 0.f;
     }
+    HATA_MARK(kTrEnd);
+    HATA_TRACE_STORE();
     return;
   }
 
   // ---- 7. publish this workgroup's record, wait, merge a slice of the outputs
+  const bool xl2 = misc[25] != 0u;  // plain stores (see step 4)
   const CohBuf pbuf(a.part + (int64_t)unit * kMaxWg * C::RECP, kMaxWg * C::RECP * 4);
   for (int c = t; c < C::RECP / 4; c += kNT) {
     float f[4];
@@ -792,12 +885,17 @@ __global__ __launch_bounds__(kNT) void decode_step_kernel(const StepArgs a) {
     u32x4 v4;
     v4.x = __float_as_uint(f[0]); v4.y = __float_as_uint(f[1]);
     v4.z = __float_as_uint(f[2]); v4.w = __float_as_uint(f[3]);
-    pbuf.st16x((w * C::RECP + 4 * c) * 4, v4, a.xcd_local);
+    pbuf.st16x((w * C::RECP + 4 * c) * 4, v4, xl2);
   }
   wait_all_mem();
   __syncthreads();
-  if (t == 0) CohBuf(a.flags + (int64_t)unit * kMaxWg, kMaxWg * 4).st4x(w * 4, epoch + 2, a.xcd_local);
-  wait_unit(a, unit, epoch + 2);
+  if (t == 0) CohBuf(a.flags + (int64_t)unit * kMaxWg, kMaxWg * 4).st4x(w * 4, epoch + 2, xl2);
+  HATA_MARK(kTrRecord);
+  if (!wait_unit(a, unit, epoch + 2, spin_limit, misc + 24)) {
+    fail_unit();
+    return;
+  }
+  HATA_MARK(kTrWait2);
 
   // slice [e0, e1) of the G*128 outputs, a multiple of 4 wide
   const int per_wg = ((G * kD + a.Wg - 1) / a.Wg + 3) / 4 * 4;
@@ -854,62 +952,14 @@ __global__ __launch_bounds__(kNT) void decode_step_kernel(const StepArgs a) {
       if (sub16 == 0) outp[e0 + eo] = (Ls > 0.f) ? A / Ls : 0.f;
     }
   }
-  if (warm == 0x9E3779B9u && k < 0) a.err[1] = warm;  // keeps the exchange-line loads
+  if (warm == 0x9E3779B9u && k < 0) a.err[2] = warm;  // keeps the exchange-line loads
   // keep every flag slot of the unit equal for the next launch (which may
   // use a different number of workgroups per unit)
   if (w == 0 && t >= a.Wg && t < kMaxWg)
     st_agent(a.flags + (int64_t)unit * kMaxWg + t, epoch + 2);
   write_idx();
-}
-
-__global__ void xcc_probe_kernel(uint32_t* out) {
-  if (threadIdx.x == 0) out[blockIdx.x] = (uint32_t)__builtin_amdgcn_s_getreg(kXccIdReg) & 0xFu;
-}
-
-// Whether the workgroups of a launch whose indices agree mod 8 share an XCD
-// (the 8 classes on 8 different XCDs) on the current device, checked once
-// per device with a 2048-workgroup probe launch (not while `user` is being
-// captured: then the answer is "no" for this call only).  The dispatcher
-// deals workgroups round-robin over the XCDs; where the round starts may
-// differ between launches, so only the classes are relied on.
-bool xcd_round_robin(hipStream_t user) {
-  constexpr int kDevs = 64, kBlocks = 2048;
-  static std::mutex mu;
-  static int state[kDevs] = {0};  // 0 unknown, 1 verified, 2 differs
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kDevs) {
-    (void)hipGetLastError();
-    return false;
-  }
-  std::lock_guard<std::mutex> lk(mu);
-  if (state[dev]) return state[dev] == 1;
-  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
-  if (hipStreamIsCapturing(user, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone) {
-    (void)hipGetLastError();
-    return false;
-  }
-  bool ran = false, ok = true;
-  uint32_t* d = nullptr;
-  hipStream_t ps = nullptr;
-  if (hipStreamCreateWithFlags(&ps, hipStreamNonBlocking) == hipSuccess &&
-      hipMalloc(reinterpret_cast<void**>(&d), kBlocks * sizeof(uint32_t)) == hipSuccess) {
-    hipLaunchKernelGGL(xcc_probe_kernel, dim3(kBlocks), dim3(64), 0, ps, d);
-    std::vector<uint32_t> h(kBlocks);
-    if (hipGetLastError() == hipSuccess &&
-        hipMemcpyAsync(h.data(), d, kBlocks * sizeof(uint32_t), hipMemcpyDeviceToHost, ps) == hipSuccess &&
-        hipStreamSynchronize(ps) == hipSuccess) {
-      ran = true;
-      for (int i = 0; i < kBlocks; ++i) ok = ok && h[i] == h[i & 7];
-      for (int i = 0; i < 8; ++i)
-        for (int j = 0; j < i; ++j) ok = ok && h[i] != h[j];
-    }
-  }
-  if (d) (void)hipFree(d);
-  if (ps) (void)hipStreamDestroy(ps);
-  (void)hipGetLastError();
-  if (!ran) return false;  // not cached: tried again on a later call
-  state[dev] = ok ? 1 : 2;
-  return ok;
+  HATA_MARK(kTrEnd);
+  HATA_TRACE_STORE();
 }
 
 }  // namespace
@@ -972,6 +1022,7 @@ StepPlan plan_decode_step(int B, int Hq, int Hkv, int64_t max_len, int k, int nu
     const size_t slots = (size_t)U * kMaxWg;
     p.off_flags = off; off = align(off + slots * 4);
     if (Wg > 1) {
+      p.off_stamps = off; off = align(off + slots * 4);
       p.off_win = off;  off = align(off + slots * kWinWords * 4);
       p.off_full = off; off = align(off + slots * (size_t)p.full_words * 4);
       p.off_part = off; off = align(off + slots * recp * 4);
@@ -980,9 +1031,16 @@ StepPlan plan_decode_step(int B, int Hq, int Hkv, int64_t max_len, int k, int nu
     // staged steps inside hata_decode_step
     p.off_qc = off;     off = align(off + (size_t)B * Hq * ((r + 63) / 64) * 8);
     p.off_scores = off; off = align(off + (size_t)U * max_len * 2);
+    p.off_idx = off;    off = align(off + (size_t)U * k * 4);  // kept list when idx_out is NULL
     p.off_attn = off;   off = align(off + attn_part_floats(B, Hkv, G, k) * 4);
     p.off_topk = off;   off = align(off + topk_scratch_bytes(B, Hkv, max_len, G * r));
   }
+#ifdef HATA_PHASE_TRACE
+  if (p.fused) {
+    p.off_trace = off;
+    off = align(off + (size_t)U * Wg * kTracePoints * 8);
+  }
+#endif
   p.total = off;
   return p;
 }
@@ -1025,8 +1083,11 @@ hipError_t launch_decode_step(const StepPlan& p, const uint16_t* q, const uint16
   a.q = q; a.K = K; a.V = V; a.W = W; a.Wk = Wk ? Wk : W; a.codes = codes; a.seq_lens = seq_lens;
   a.out = out; a.idx_out = idx_out; a.cap = cap; a.Hq = Hq; a.Hkv = Hkv; a.k = k;
   a.scale = scale; a.Wg = p.Wg; a.chunk = p.chunk; a.xcd_map = p.xcd_map; a.U = p.U;
-  a.xcd_local = (p.xcd_map && p.Wg > 1 && xcd_round_robin(s)) ? 1 : 0;
   a.err = reinterpret_cast<uint32_t*>(ws + p.off_err);
+  a.stamps = reinterpret_cast<uint32_t*>(ws + p.off_stamps);
+#ifdef HATA_PHASE_TRACE
+  a.trace = reinterpret_cast<uint64_t*>(ws + p.off_trace);
+#endif
   a.flags = reinterpret_cast<uint32_t*>(ws + p.off_flags);
   a.win = p.Wg > 1 ? reinterpret_cast<uint32_t*>(ws + p.off_win) : nullptr;
   a.full = p.Wg > 1 ? reinterpret_cast<uint32_t*>(ws + p.off_full) : nullptr;
@@ -1066,8 +1127,11 @@ hipError_t launch_decode_step_paged(const StepPlan& p, const uint16_t* q, const 
   a.q = q; a.K = K; a.V = V; a.W = W; a.Wk = W; a.codes = codes; a.seq_lens = seq_lens;
   a.out = out; a.idx_out = idx_out; a.cap = (int64_t)pm.max_pages << pm.log2P; a.Hq = Hq; a.Hkv = Hkv; a.k = k;
   a.scale = scale; a.Wg = p.Wg; a.chunk = p.chunk; a.xcd_map = p.xcd_map; a.U = p.U;
-  a.xcd_local = (p.xcd_map && p.Wg > 1 && xcd_round_robin(s)) ? 1 : 0;
   a.err = reinterpret_cast<uint32_t*>(ws + p.off_err);
+  a.stamps = reinterpret_cast<uint32_t*>(ws + p.off_stamps);
+#ifdef HATA_PHASE_TRACE
+  a.trace = reinterpret_cast<uint64_t*>(ws + p.off_trace);
+#endif
   a.flags = reinterpret_cast<uint32_t*>(ws + p.off_flags);
   a.win = p.Wg > 1 ? reinterpret_cast<uint32_t*>(ws + p.off_win) : nullptr;
   a.full = p.Wg > 1 ? reinterpret_cast<uint32_t*>(ws + p.off_full) : nullptr;

@@ -137,4 +137,14 @@ hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s) {
   return hipGetLastError();
 }
 
+__global__ void set_word_kernel(uint32_t* p, uint32_t v) {
+  if (threadIdx.x == 0) p[0] = v;
+}
+
+// Write one 32-bit word of device memory with a kernel (graph-capturable).
+hipError_t launch_set_word(uint32_t* p, uint32_t v, hipStream_t s) {
+  hipLaunchKernelGGL(set_word_kernel, dim3(1), dim3(64), 0, s, p, v);
+  return hipGetLastError();
+}
+
 }  // namespace hata

@@ -72,8 +72,9 @@ struct StepPlan {
   int G = 0, U = 0, Wg = 1, chunk = 0, xcd_map = 0, R = 128;
   size_t lds_bytes = 0;
   // workspace layout (byte offsets)
-  size_t off_err = 0, off_flags = 0, off_win = 0, off_full = 0, off_part = 0;
-  size_t off_qc = 0, off_scores = 0, off_attn = 0, off_topk = 0;
+  size_t off_err = 0, off_flags = 0, off_stamps = 0, off_win = 0, off_full = 0, off_part = 0;
+  size_t off_qc = 0, off_scores = 0, off_idx = 0, off_attn = 0, off_topk = 0;
+  size_t off_trace = 0;  // phase-trace build only: per-workgroup timestamps at the end
   int full_words = 0;  // 32-bit words per workgroup in the full-histogram area
   size_t total = 0;
 };
@@ -93,6 +94,7 @@ hipError_t launch_decode_step_paged(const StepPlan& p, const uint16_t* q, const 
                                     unsigned char* ws, hipStream_t s);
 
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s);
+hipError_t launch_set_word(uint32_t* p, uint32_t v, hipStream_t s);
 
 // ---------------------------------------------------------------- prefill
 // Causal attention over each sequence's prompt (queries [B][Hq][q_rows][128]

@@ -28,6 +28,8 @@ Recipes (the readings are listed in the repository's design notes):
 """
 from __future__ import annotations
 
+import concurrent.futures as cf
+import os
 from dataclasses import dataclass, field
 
 import numpy as np
@@ -149,13 +151,14 @@ def make_inputs(shape: Shape, cap: int | None = None, seq_lens=None, k: int | No
     V = np.empty((B, Hkv, cap, d), np.uint16)
     needle_pos = np.zeros((B, Hkv, shape.needles), np.int32) if shape.needles else None
 
-    for b in range(B):
+    def draw(b: int) -> None:
+        # sequence b: its own generator, its own slices of q, K, V
         rng = np.random.Generator(np.random.PCG64(shape.seed_base + b))
         if shape.dist == "exact":
             K[b] = _exact_vals(rng, (Hkv, cap, d))
             V[b] = _exact_vals(rng, (Hkv, cap, d))
             q[b] = _exact_vals(rng, (Hq, d))
-            continue
+            return
         # K is drawn in fp32 per head so outliers and needles are applied
         # before the single bf16 rounding.
         for h in range(Hkv):
@@ -178,6 +181,16 @@ def make_inputs(shape: Shape, cap: int | None = None, seq_lens=None, k: int | No
                 K[b, h, pos] = bf16_bits(np.float32(0.9) * qsrc + noise)
                 needle_pos[b, h, :m] = pos
                 needle_pos[b, h, m:] = -1
+
+    # sequences are independent draws: large batches fill on several threads
+    # (the values do not depend on the thread count)
+    workers = min(B, os.cpu_count() or 1, 16)
+    if workers > 1 and B * Hkv * cap * d >= (1 << 24):
+        with cf.ThreadPoolExecutor(max_workers=workers) as ex:
+            list(ex.map(draw, range(B)))
+    else:
+        for b in range(B):
+            draw(b)
     return Inputs(shape=shape, q=q, K=K, V=V, W=W, seq_lens=seq_lens, k=k, scale=scale,
                   needle_pos=needle_pos, outlier_ch=outlier_ch)
 

@@ -41,12 +41,16 @@
  *            every n_b, used only to size launch grids (so calls can be
  *            captured in a HIP graph); it must satisfy 1 <= max_len <= cap.
  *
- * Supported sizes: d = 128, r = 128, G = Hq/Hkv in {1, 2, 4, 8}, 1 <= k <= 4096.
+ * Supported sizes: d = 128; r in {32, 64, 128, 256} (a code of r bits takes
+ * ceil(r/64) 64-bit words; hata_sparse_decode and hata_dense_decode take no
+ * code); G = Hq/Hkv in {1, 2, 4, 8}; 1 <= k <= 4096.
  *
  * Ownership and threading: every pointer is a device pointer unless stated;
  * the caller allocates and owns every buffer, the library never allocates,
- * frees or keeps a pointer after returning, and never synchronises the
- * stream.  `stream` is a hipStream_t passed as void* (NULL = default stream).
+ * frees or keeps a pointer after returning, creates no stream and never
+ * synchronises (hata_workspace_check, a diagnostic, is the one call that
+ * waits for its stream).  `stream` is a hipStream_t passed as void* (NULL =
+ * default stream).
  * Workspaces are sized by hata_workspace_bytes, zeroed once by the caller
  * (hata_workspace_reset), restore their own state at the end of every call
  * and must not be shared by calls that can run concurrently.
@@ -170,7 +174,20 @@ int hata_sparse_decode(const void* q, const void* K, const void* V, int B,
  * out = 0 and idx_out = -1 and its code rows are left unchanged.
  * ws: hata_workspace_bytes(HATA_OP_DECODE_STEP, ...), zeroed once before
  * first use.  Shapes whose per-unit scores do not fit on chip run the same
- * steps as separate kernels inside this call.
+ * steps as separate kernels inside this call (idx_out may still be NULL:
+ * the kept list then lives in the workspace).
+ * The workgroups of one unit exchange histogram windows and partial
+ * attention records through the workspace and wait for each other; they
+ * must all be resident at once, which the launch size ensures on an
+ * otherwise idle device.  Every such wait is bounded (2^22 polls, or the
+ * bound set by hata_workspace_set_spin_limit).  A wait that gives up sets
+ * bit 0 of the workspace error word (hata_workspace_check) and the unit's
+ * results are marked instead of computed from incomplete data: NaN in
+ * out (at least the outputs the timed-out workgroup merges) and -2 in
+ * idx_out.  The workspace must then be reset (hata_workspace_reset) before
+ * its next use.  Kernels of other streams that occupy compute units while
+ * a step runs can delay its workgroups' start; the step then waits for
+ * them, and fails as above only if they do not start within the bound.
  */
 int hata_decode_step(const void* q, const void* K, const void* V,
                      const float* W_H, uint64_t* codes, int B, int Hq, int Hkv,
@@ -349,12 +366,22 @@ size_t hata_workspace_bytes(int op, int B, int Hq, int Hkv, int d, int r,
 int hata_workspace_reset(void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * Testing aid for the bounded waits of hata_decode_step,
+ * hata_decode_step_qk and hata_decode_step_paged: the waits of calls that
+ * use this workspace give up after `polls` polls (0 restores the default of
+ * 2^22).  Written by a kernel on `stream`; hata_workspace_reset also
+ * restores the default.  ws_bytes >= 8.
+ */
+int hata_workspace_set_spin_limit(void* ws, size_t ws_bytes, uint32_t polls,
+                                  void* stream);
+
+/*
  * Synchronise `stream` and read the workspace's device-side error word:
  * *err_out = 0 if no kernel reported a problem since the last reset, else a
- * bit set (1 = a cross-workgroup wait gave up after its spin limit;
- * 4 = workgroups of one hata_decode_step unit ran on different XCDs,
- * against the placement a once-per-device check had shown).
- * Diagnostic only; never needed on the hot path.
+ * bit set (1 = a cross-workgroup wait of a decode step gave up after its
+ * spin limit; the affected units' outputs are then NaN and their idx_out
+ * entries -2, see hata_decode_step).  Diagnostic only; never needed on the
+ * hot path.
  */
 int hata_workspace_check(const void* ws, size_t ws_bytes, int* err_out,
                          void* stream);
