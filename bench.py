@@ -606,7 +606,9 @@ def train_bench(J: int = 512, n: int = 8192, r: int = 128, steps: int = 20) -> d
 
 
 TRACE_POINTS = ("start", "qcodes", "scanned", "hist", "published", "wait1", "windows", "threshold",
-                "compacted", "attended", "record", "wait2", "end")
+                "compacted", "attended", "record", "wait2", "end", "qrows", "fma", "reduced")
+# the boundaries in the order a workgroup passes them (indices into TRACE_POINTS)
+TRACE_ORDER = (0, 13, 14, 15, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12)
 
 
 def phase_trace(cfg_id: int = 4, steps: int = 200, layers: int = 0) -> dict:
@@ -676,7 +678,8 @@ def phase_trace(cfg_id: int = 4, steps: int = 200, layers: int = 0) -> dict:
     max_rel = np.nanmedian(np.nanmax(rel, axis=1), axis=0)
     phases = {}
     prev = None
-    for j, name in enumerate(TRACE_POINTS):
+    for j in TRACE_ORDER:
+        name = TRACE_POINTS[j]
         col = rel[:, :, j]
         if np.isnan(col).all():
             continue
@@ -689,7 +692,7 @@ def phase_trace(cfg_id: int = 4, steps: int = 200, layers: int = 0) -> dict:
         prev = j
     res = {"workload": shape.name, "workgroups": nwg, "units": U, "steps": steps, "layers": L,
            "kernel_us_hip_events_median": float(np.median(ev_us)),
-           "span_first_start_to_last_end_us_median": float(max_rel[len(TRACE_POINTS) - 1]),
+           "span_first_start_to_last_end_us_median": float(max_rel[TRACE_POINTS.index("end")]),
            "start_spread_us_median": float(max_rel[0]), "phases": phases}
     log(f"phase trace {shape.name}: {nwg} workgroups, {steps} eager steps, events {np.median(ev_us):.2f} us/step")
     log(f"{'boundary':>10} {'median':>8} {'latest':>8} {'phase':>8} {'p90':>8}  (us)")

@@ -85,7 +85,10 @@ enum TracePoint {
   kTrAttended = 9,   // attention over the kept rows done
   kTrRecord = 10,    // partial record and flag stored
   kTrWait2 = 11,     // every record of the unit published
-  kTrEnd = 12        // outputs written
+  kTrEnd = 12,       // outputs written
+  kTrQrows = 13,     // query rows staged in LDS
+  kTrFma = 14,       // projection products of thread 0 done (its W_H arrived)
+  kTrRed = 15        // projection partial sums staged
 };
 #ifdef HATA_PHASE_TRACE
 #define HATA_MARK(i) \
@@ -437,7 +440,12 @@ __global__ __launch_bounds__(kNT) void decode_step_kernel(const StepArgs a) {
       if (t + kNT * u < kMaxPgl) pgl[t + kNT * u] = pgv[u];
   }
   __syncthreads();
+  HATA_MARK(kTrQrows);
+#ifdef HATA_PHASE_TRACE
+  project_pack<G, R>(wr, qf, red, qcode, G, &tr_ts[kTrFma]);
+#else
   project_pack<G, R>(wr, qf, red, qcode, G);
+#endif
   HATA_MARK(kTrQcodes);
   // this workgroup's XCD stamp for the launch ((epoch + 1) << 4 | XCD id;
   // epochs are even, so a stamp is never 0, the value of a fresh workspace)
