@@ -58,6 +58,7 @@ def load(path: str | None = None) -> ctypes.CDLL:
         "hata_sparse_decode": ([P, P, P, I, I, I, I, I64, P, I, F, P, P, SZ, P], I),
         "hata_decode_step": ([P, P, P, P, P, I, I, I, I, I, I64, P, I64, I, F, P, P, P, SZ, P], I),
         "hata_decode_step_qk": ([P, P, P, P, P, P, I, I, I, I, I, I64, P, I64, I, F, P, P, P, SZ, P], I),
+        "hata_decode_step_noalloc": ([P, P, P, P, P, I, I, I, I, I, I64, P, I64, I, F, P, P, P], I),
         "hata_dense_decode": ([P, P, P, I, I, I, I, I64, P, I64, F, P, P, SZ, P], I),
         "hata_workspace_bytes": ([I, I, I, I, I, I, I64, I], SZ),
         "hata_workspace_reset": ([P, SZ, P], I),
@@ -83,6 +84,7 @@ def exported_symbols() -> list[str]:
     return [n for n in ("hata_status_string", "hata_last_error_message", "hata_version",
                         "hata_encode_append", "hata_hamming_scores", "hata_topk",
                         "hata_sparse_decode", "hata_decode_step", "hata_decode_step_qk",
+                        "hata_decode_step_noalloc",
                         "hata_dense_decode",
                         "hata_workspace_bytes", "hata_workspace_reset", "hata_workspace_check",
                         "hata_workspace_set_spin_limit",
@@ -292,6 +294,27 @@ def decode_step(q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, W_H: torch.Te
     _check(load().hata_decode_step(_ptr(q), _ptr(K), _ptr(V), _ptr(W_H), _ptr(codes), B, Hq, Hkv,
                                    d, r, cap, _ptr(seq_lens), int(max_len), int(k), float(scale),
                                    _ptr(out), _ptr(idx_out), _ptr(ws), ws.numel(), _stream(stream)))
+
+
+def decode_step_noalloc(q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, W_H: torch.Tensor,
+                        codes: torch.Tensor, seq_lens: torch.Tensor, max_len: int, k: int, scale: float,
+                        out: torch.Tensor, idx_out: torch.Tensor | None = None, stream=None) -> None:
+    """The fused decode step without a workspace argument (see
+    hata_decode_step_noalloc: the library's static scratch serves)."""
+    for t, n in ((q, "q"), (K, "K"), (V, "V")):
+        _need(t, torch.bfloat16, n)
+    _need(W_H, torch.float32, "W_H")
+    _need(codes, torch.int64, "codes")
+    _need(out, torch.float32, "out")
+    _need(seq_lens, torch.int32, "seq_lens")
+    if idx_out is not None:
+        _need(idx_out, torch.int32, "idx_out")
+    B, Hq, d = q.shape
+    _, Hkv, cap, _ = K.shape
+    r = W_H.shape[2]
+    _check(load().hata_decode_step_noalloc(_ptr(q), _ptr(K), _ptr(V), _ptr(W_H), _ptr(codes), B, Hq, Hkv,
+                                           d, r, cap, _ptr(seq_lens), int(max_len), int(k), float(scale),
+                                           _ptr(out), _ptr(idx_out), _stream(stream)))
 
 
 def decode_step_qk(q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, W_Hq: torch.Tensor,

@@ -243,10 +243,12 @@ int hata_stream_read(const void* src, size_t bytes, uint64_t* sink, size_t sink_
   return check_launch(e, "stream_read launch");
 }
 
+// noalloc: ws is ignored and the library's static scratch serves instead
 static int decode_step_impl(const void* q, const void* K, const void* V, const float* W_H,
                             const float* W_Hk, uint64_t* codes, int B, int Hq, int Hkv, int d, int r,
                             int64_t cap, const int32_t* seq_lens, int64_t max_len, int k, float scale,
-                            float* out, int32_t* idx_out, void* ws, size_t ws_bytes, void* stream) {
+                            float* out, int32_t* idx_out, void* ws, size_t ws_bytes, void* stream,
+                            bool noalloc = false) {
   if (!q || !K || !V || !W_H || !W_Hk || !codes || !seq_lens || !out)
     return fail(HATA_ERR_NULL, "decode_step: null pointer");
   int st = check_dims(d, r);
@@ -259,11 +261,29 @@ static int decode_step_impl(const void* q, const void* K, const void* V, const f
   int cus = 0;
   if ((st = current_cus(&cus))) return st;
   const hata::StepPlan p = hata::plan_decode_step(B, Hq, Hkv, max_len, k, cus, r);
-  if (!ws || ws_bytes < p.total)
-    return fail(HATA_ERR_WORKSPACE, "decode_step: workspace of %zu bytes needed, %zu given", p.total, ws_bytes);
-  if ((st = pre_launch("decode_step"))) return st;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  auto* wsb = static_cast<unsigned char*>(ws);
+  unsigned char* wsb = nullptr;
+  if (noalloc) {
+    // the static scratch stands in for the workspace: its flag and stamp
+    // slots are cleared first (a fill kernel), since calls of other sizes
+    // share them
+    if (p.total > hata::kNoAllocScratchBytes)
+      return fail(HATA_ERR_WORKSPACE, "decode_step_noalloc: these sizes need %zu bytes of scratch, above the "
+                  "%zu-byte static scratch; use hata_decode_step with a workspace", p.total,
+                  hata::kNoAllocScratchBytes);
+    if ((st = pre_launch("decode_step_noalloc"))) return st;
+    hipError_t e = hata::noalloc_scratch(&wsb);
+    if (e != hipSuccess) return hip_fail(e, "decode_step_noalloc: hipGetSymbolAddress");
+    if (p.fused) {
+      e = hata::launch_fill_zero(wsb, p.Wg > 1 ? p.off_win : p.total, s);
+      if (e != hipSuccess) return hip_fail(e, "decode_step_noalloc: clearing the scratch flags");
+    }
+  } else {
+    if (!ws || ws_bytes < p.total)
+      return fail(HATA_ERR_WORKSPACE, "decode_step: workspace of %zu bytes needed, %zu given", p.total, ws_bytes);
+    if ((st = pre_launch("decode_step"))) return st;
+    wsb = static_cast<unsigned char*>(ws);
+  }
   const auto* qb = static_cast<const uint16_t*>(q);
   const auto* Kb = static_cast<const uint16_t*>(K);
   const auto* Vb = static_cast<const uint16_t*>(V);
@@ -391,6 +411,13 @@ int hata_decode_step(const void* q, const void* K, const void* V, const float* W
                      size_t ws_bytes, void* stream) {
   return decode_step_impl(q, K, V, W_H, W_H, codes, B, Hq, Hkv, d, r, cap, seq_lens, max_len, k, scale,
                           out, idx_out, ws, ws_bytes, stream);
+}
+
+int hata_decode_step_noalloc(const void* q, const void* K, const void* V, const float* W_H, uint64_t* codes,
+                             int B, int Hq, int Hkv, int d, int r, int64_t cap, const int32_t* seq_lens,
+                             int64_t max_len, int k, float scale, float* out, int32_t* idx_out, void* stream) {
+  return decode_step_impl(q, K, V, W_H, W_H, codes, B, Hq, Hkv, d, r, cap, seq_lens, max_len, k, scale,
+                          out, idx_out, nullptr, 0, stream, true);
 }
 
 int hata_decode_step_qk(const void* q, const void* K, const void* V, const float* W_Hq,

@@ -44,9 +44,16 @@
 // the workgroup writes NaN into the unit's outputs and -2 into its kept
 // indices instead of results built from incomplete data.
 #include <atomic>
+#include <mutex>
 
 #include "hata_device.hpp"
 #include "hata_launch.hpp"
+
+// Scratch of hata_decode_step_noalloc: the decode step's workspace for
+// callers that cannot allocate (zero at load; each device holds its own copy
+// until the process ends).  Host code reaches it only through the address
+// hipGetSymbolAddress returns for the current device (noalloc_scratch).
+static __device__ __align__(256) unsigned char scratch[hata::kNoAllocScratchBytes];
 
 namespace hata {
 
@@ -1153,6 +1160,28 @@ hipError_t launch_decode_step_paged(const StepPlan& p, const uint16_t* q, const 
     case 8: return launch_paged_g<8>(p, a, s);
     default: return hipErrorInvalidValue;
   }
+}
+
+// Device address of `scratch` on the current device, looked up once per
+// device (hipGetSymbolAddress with that device current) and kept.
+hipError_t noalloc_scratch(unsigned char** out) {
+  constexpr int kDevs = 64;
+  static std::mutex mu;
+  static unsigned char* ptrs[kDevs] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kDevs) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lk(mu);
+  if (!ptrs[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    ptrs[dev] = static_cast<unsigned char*>(p);
+  }
+  *out = ptrs[dev];
+  return hipSuccess;
 }
 
 }  // namespace hata

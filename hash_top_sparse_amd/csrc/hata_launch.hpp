@@ -79,6 +79,12 @@ struct StepPlan {
   size_t total = 0;
 };
 StepPlan plan_decode_step(int B, int Hq, int Hkv, int64_t max_len, int k, int num_cus, int r = 128);
+
+// hata_decode_step_noalloc: a static device array of this many bytes per
+// device serves as the step's workspace; noalloc_scratch gives its address
+// on the current device.
+constexpr size_t kNoAllocScratchBytes = (size_t)16 << 20;
+hipError_t noalloc_scratch(unsigned char** out);
 hipError_t launch_decode_step(const StepPlan& p, const uint16_t* q, const uint16_t* K,
                               const uint16_t* V, const float* W, const float* Wk, uint64_t* codes, int B, int Hq,
                               int Hkv, int64_t cap, const int32_t* seq_lens, int k, float scale,

@@ -196,6 +196,30 @@ int hata_decode_step(const void* q, const void* K, const void* V,
                      int32_t* idx_out, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * hata_decode_step for callers that cannot allocate device memory (code
+ * under HIP graph capture, serving loops, harnesses that forbid
+ * hipMalloc): the same step, arguments, layouts and results, with no
+ * workspace argument.  Its workspace is a static device array of the
+ * library (16 MiB per device, held until the process ends; its address is
+ * looked up once per device with hipGetSymbolAddress); the call allocates
+ * nothing.  Each call first clears the array's flag slots with a fill
+ * kernel on `stream`, so calls of different sizes may follow each other.
+ * Every call on one device shares that device's array: calls that can
+ * overlap (other streams, other host threads) race and must be serialised
+ * by the caller.  Sizes whose workspace (hata_workspace_bytes(
+ * HATA_OP_DECODE_STEP, ...)) exceeds 16 MiB are rejected with
+ * HATA_ERR_WORKSPACE before anything is launched.  The bounded waits have
+ * the default bound; a wait that gives up marks the outputs as for
+ * hata_decode_step (the next call clears the flags again).
+ */
+int hata_decode_step_noalloc(const void* q, const void* K, const void* V,
+                             const float* W_H, uint64_t* codes, int B, int Hq,
+                             int Hkv, int d, int r, int64_t cap,
+                             const int32_t* seq_lens, int64_t max_len, int k,
+                             float scale, float* out, int32_t* idx_out,
+                             void* stream);
+
+/*
  * hata_decode_step with independent query and key encoders (HashAttention
  * summary page, "Approach": separate query and key encoders): the G query
  * rows of KV head h are encoded with W_Hq[h] and the appended key row with
