@@ -606,9 +606,10 @@ def train_bench(J: int = 512, n: int = 8192, r: int = 128, steps: int = 20) -> d
 
 
 TRACE_POINTS = ("start", "qcodes", "scanned", "hist", "published", "wait1", "windows", "threshold",
-                "compacted", "attended", "record", "wait2", "end", "qrows", "fma", "reduced")
+                "compacted", "attended", "record", "wait2", "end", "qrows", "", "", "search")
 # the boundaries in the order a workgroup passes them (indices into TRACE_POINTS)
-TRACE_ORDER = (0, 13, 14, 15, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12)
+TRACE_ORDER = (0, 13, 1, 2, 3, 4, 5, 6, 16, 7, 8, 9, 10, 11, 12)
+TRACE_SLOTS = 24  # timestamps stored per workgroup
 
 
 def phase_trace(cfg_id: int = 4, steps: int = 200, layers: int = 0) -> dict:
@@ -643,11 +644,11 @@ def phase_trace(cfg_id: int = 4, steps: int = 200, layers: int = 0) -> dict:
     ws = binding.alloc_workspace(binding.OP_DECODE_STEP, B, Hq, Hkv, N, k, device=dev)
     # workgroups per unit as the library plans them for these sizes (a
     # fused step within the LDS limit); the trace area is the workspace's
-    # last ceil(U * Wg * 128 / 256) * 256 bytes
+    # last ceil(U * Wg * 8 * TRACE_SLOTS / 256) * 256 bytes
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     Wg = max(1, min(cus // U, 64, -(-N // 256)))
     assert -(-N // Wg) <= 32768, "the phase trace covers shapes of at most 32768 tokens per workgroup"
-    nbytes = -(-U * Wg * 128 // 256) * 256
+    nbytes = -(-U * Wg * TRACE_SLOTS * 8 // 256) * 256
     off = ws.numel() - nbytes
     out = torch.zeros((B, Hq, 128), dtype=torch.float32, device=dev)
     rec = torch.zeros((steps, nbytes), dtype=torch.uint8, device=dev)
@@ -666,7 +667,7 @@ def phase_trace(cfg_id: int = 4, steps: int = 200, layers: int = 0) -> dict:
     if binding.workspace_check(ws):
         raise RuntimeError("workspace error word set during the phase trace")
     ev_us = np.array([evs[2 * i].elapsed_time(evs[2 * i + 1]) * 1e3 for i in range(steps)])
-    ts = rec.cpu().numpy().view(np.uint64).reshape(steps, -1, 16).astype(np.int64)[:, :U * Wg]
+    ts = rec.cpu().numpy().view(np.uint64).reshape(steps, -1, TRACE_SLOTS).astype(np.int64)[:, :U * Wg]
     nwg = int((ts[0, :, 0] != 0).sum())
     assert nwg == U * Wg, f"{nwg} workgroups left timestamps, {U * Wg} expected"
     ts = ts[:, :, :len(TRACE_POINTS)]

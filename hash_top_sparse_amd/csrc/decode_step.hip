@@ -65,6 +65,8 @@ constexpr int kWinWords = kWinBytes / 4;
 constexpr int kWinHdr = 8;         // uint16 header entries
 constexpr int kWinCap = kWinBytes / 2 - kWinHdr;  // histogram bins a window holds
 constexpr int kMaxChunk = 32768;   // tokens per workgroup (uint16 scores in LDS)
+constexpr int kStepWgMaxOcc2 = 32; // workgroups per unit when two share a CU
+constexpr size_t kLdsPerCu = 160 * 1024;
 constexpr uint32_t kSpinLimit = 1u << 22;  // default bound on the polls of one wait
 // s_getreg operand for HW_REG_XCC_ID (register 20, bits 0..31): the XCD the
 // wave runs on
@@ -78,7 +80,7 @@ constexpr int kPglPerThread = (kMaxPgl + kNT - 1) / kNT;
 // real-time counter at the phase boundaries listed below and stores the
 // readings at exit.  Marks sit where the kernel already synchronises, so
 // they add no barrier.
-constexpr int kTracePoints = 16;
+constexpr int kTracePoints = 24;
 enum TracePoint {
   kTrStart = 0,      // first instruction
   kTrQcodes = 1,     // query codes built
@@ -94,8 +96,7 @@ enum TracePoint {
   kTrWait2 = 11,     // every record of the unit published
   kTrEnd = 12,       // outputs written
   kTrQrows = 13,     // query rows staged in LDS
-  kTrFma = 14,       // projection products of thread 0 done (its W_H arrived)
-  kTrRed = 15        // projection partial sums staged
+  kTrSearch = 16     // threshold found (before the writers' prefix counts)
 };
 #ifdef HATA_PHASE_TRACE
 #define HATA_MARK(i) \
@@ -130,16 +131,23 @@ struct Cfg {
   static constexpr int RED0 = (kMergeFloats<G> > PROJ) ? kMergeFloats<G> : PROJ;
   static constexpr int RED = (RED0 > (G + 4) * kRec) ? RED0 : (G + 4) * kRec;
   // LDS offsets in bytes
-  static constexpr int o_hist = 0;                               // NBP uint32
+  // score histogram copies: one per wave (fewer same-address LDS atomics;
+  // measured 0.2 us faster at 32K and 128K) when the bins are few, else one
+  static constexpr int HCOPY = (NB <= 1024) ? 4 : 1;
+  static constexpr int o_hist = 0;                               // HCOPY * NBP uint32
   static constexpr int NSTG = (G + 1 + 3) / 4;                   // staging loads per thread
-  static constexpr int o_qf = o_hist + NBP * 4;                  // 4*NSTG rows of 128 float (G+1 used)
+  static constexpr int o_qf = o_hist + HCOPY * NBP * 4;          // 4*NSTG rows of 128 float (G+1 used)
   static constexpr int o_red = o_qf + 4 * NSTG * kD * 4;         // RED float
   static constexpr int o_qcode = o_red + RED * 4;                // (G+1)*W64 uint64
   static constexpr int o_misc = o_qcode + (G + 1) * W64 * 8;     // 64 uint32
   static constexpr int o_whdr = o_misc + 64 * 4;                 // kMaxWg int4 + 2*4*64 uint32
+  // the unit's histogram windows (read after the first exchange, used up by
+  // the threshold) and the attention's staged K/V rows share one area, as
+  // do the partial records staged for the final merge (after the attention)
   static constexpr int o_win = o_whdr + 4 * kMaxWg * 4 + 2048;   // kMaxWg*kWinBytes (also combine staging)
-  static constexpr int o_kvs = o_win + kMaxWg * kWinBytes;       // kShortList K/V rows
-  static constexpr int o_pgl = o_kvs + kShortList * 512;         // paged: kMaxPgl int32 page ids
+  static constexpr int o_kvs = o_win;                            // kShortList K/V rows
+  static constexpr int WKV = (kMaxWg * kWinBytes > kShortList * 512) ? kMaxWg * kWinBytes : kShortList * 512;
+  static constexpr int o_pgl = o_kvs + WKV;                      // paged: kMaxPgl int32 page ids
   static constexpr int o_sel = o_pgl + (PAGED ? kMaxPgl * 4 : 0); // k + 1 int32
   static size_t lds_bytes(int k, int chunk) {
     size_t s = (size_t)o_sel + (size_t)(k + 1) * 4;
@@ -181,17 +189,18 @@ struct StepArgs {
   int max_pages, num_pages, log2P;
 };
 
+// Block -> (unit, workgroup).  xcd_map: blocks agreeing mod 8 form the
+// units of one XCD class (unit = 8 * (slot / Wg) + bid % 8, slot = bid / 8);
+// otherwise unit = bid / Wg.  Branch-free, so the compiler issues every
+// kernel-argument load at once (with a branch here it sank the load of the
+// data pointers below the first argument wait).
 __device__ __forceinline__ void map_block(const StepArgs& a, int* unit, int* w) {
   const int bid = blockIdx.x;
-  if (a.xcd_map) {
-    const int xcd = bid & 7, slot = bid >> 3;
-    const int uix = slot / a.Wg;
-    *w = slot - uix * a.Wg;
-    *unit = uix * 8 + xcd;
-  } else {
-    *unit = bid / a.Wg;
-    *w = bid - *unit * a.Wg;
-  }
+  const int sh = a.xcd_map ? 3 : 0;
+  const int xcd = bid & ((1 << sh) - 1), slot = bid >> sh;
+  const int uix = slot / a.Wg;
+  *w = slot - uix * a.Wg;
+  *unit = (uix << sh) + xcd;
 }
 
 // Wave 0 waits until every flag of the unit has reached `target`, for at
@@ -221,11 +230,12 @@ __device__ __forceinline__ bool wait_unit(const StepArgs& a, int unit, uint32_t 
   return *failed == 0u;
 }
 
-// In-place inclusive scan of hist[0, NB) with 256 threads.  Also records the
+// In-place inclusive scan of hist[0, NB) with 256 threads (the sum of
+// COPIES copies STRIDE words apart, written to the first).  Also records the
 // first bin where the running count becomes > 0, >= cnt and >= k in misc[0],
 // misc[1], misc[2] (each written by the one thread that sees the transition;
 // the caller presets them to NB).  Ends with __syncthreads.
-template <int NB>
+template <int NB, int COPIES = 1, int STRIDE = 0>
 __device__ __forceinline__ void cum_hist(uint32_t* hist, uint32_t* misc, uint32_t* tmp,
                                          uint32_t cnt, uint32_t k) {
   constexpr int BPT = (NB + kNT - 1) / kNT;
@@ -235,7 +245,12 @@ __device__ __forceinline__ void cum_hist(uint32_t* hist, uint32_t* misc, uint32_
 #pragma unroll
   for (int j = 0; j < BPT; ++j) {
     const int s = t * BPT + j;
-    v[j] = (s < NB) ? hist[s] : 0u;
+    uint32_t x = 0u;
+    if (s < NB) {
+#pragma unroll
+      for (int c = 0; c < COPIES; ++c) x += hist[c * STRIDE + s];
+    }
+    v[j] = x;
     loc += v[j];
   }
   uint32_t tot;
@@ -260,8 +275,13 @@ __device__ __forceinline__ void cum_hist(uint32_t* hist, uint32_t* misc, uint32_
 // width in bits (32, 64, 128, 256).
 // PAGED: K, V and codes are page pools addressed through a.bt (separate
 // instance; the contiguous code is unchanged).
+// Instances with G <= 4 and R <= 128 are compiled for two workgroups per CU
+// (at most 256 registers a lane), which the plan uses for many units.
+template <int G, int R>
+constexpr int step_occupancy() { return (G <= 4 && R <= 128) ? 2 : 1; }
+
 template <int G, bool SEP, int R, bool PAGED>
-__global__ __launch_bounds__(kNT) void decode_step_kernel(const StepArgs a) {
+__global__ __launch_bounds__(kNT, (step_occupancy<G, R>())) void decode_step_kernel(const StepArgs a) {
   using C = Cfg<G, R, PAGED>;
   constexpr int W64 = C::W64, W32 = Width<R>::W32;
   constexpr int NB = C::NB;
@@ -414,9 +434,14 @@ __global__ __launch_bounds__(kNT) void decode_step_kernel(const StepArgs a) {
   }
   // keep the loads above ahead of the length read in the issued code
   __builtin_amdgcn_sched_barrier(0);
-  const int n_in = a.seq_lens[b];
+  // The length and the wait bound are read as constants (scalar loads, which
+  // do not queue behind the vector loads above; this kernel never writes
+  // either word).
+  typedef const __attribute__((address_space(4))) int32_t* cint_p;
+  typedef const __attribute__((address_space(4))) uint32_t* cuint_p;
+  const int n_in = *(cint_p)(a.seq_lens + b);
   // bound on the polls of one exchange wait (err[1] == 0: the default)
-  const uint32_t spin_w = a.err[1];
+  const uint32_t spin_w = *(cuint_p)(a.err + 1);
   const uint32_t spin_limit = spin_w ? spin_w : kSpinLimit;
   const bool bad_len = n_in < 1 || (int64_t)n_in > cap;
   const int n = bad_len ? 1 : n_in;
@@ -439,7 +464,7 @@ __global__ __launch_bounds__(kNT) void decode_step_kernel(const StepArgs a) {
     qf[r * kD + 2 * c2] = bf16_lo(v);
     qf[r * kD + 2 * c2 + 1] = bf16_hi(v);
   }
-  for (int i = t; i < C::NBP; i += kNT) hist[i] = 0;
+  for (int i = t; i < C::HCOPY * C::NBP; i += kNT) hist[i] = 0;
   if (t < 64) misc[t] = (t < 3) ? (uint32_t)NB : 0u;
   if constexpr (PAGED) {
 #pragma unroll
@@ -448,11 +473,7 @@ __global__ __launch_bounds__(kNT) void decode_step_kernel(const StepArgs a) {
   }
   __syncthreads();
   HATA_MARK(kTrQrows);
-#ifdef HATA_PHASE_TRACE
-  project_pack<G, R>(wr, qf, red, qcode, G, &tr_ts[kTrFma]);
-#else
   project_pack<G, R>(wr, qf, red, qcode, G);
-#endif
   HATA_MARK(kTrQcodes);
   // this workgroup's XCD stamp for the launch ((epoch + 1) << 4 | XCD id;
   // epochs are even, so a stamp is never 0, the value of a fresh workspace)
@@ -494,7 +515,7 @@ __global__ __launch_bounds__(kNT) void decode_step_kernel(const StepArgs a) {
     code_words<R>(c, cw);
     const uint32_t s = gqa_hamming_w<G, R>(cw, qm);
     sc[li] = (uint16_t)s;
-    atomicAdd(&hist[s], 1u);
+    atomicAdd(&hist[(C::HCOPY > 1 ? wv * C::NBP : 0) + s], 1u);
   };
   constexpr int BATCH = PF * kNT;
   int base = 0;
@@ -564,7 +585,7 @@ __global__ __launch_bounds__(kNT) void decode_step_kernel(const StepArgs a) {
   HATA_MARK(kTrScanned);
 
   // ---- 4. threshold
-  cum_hist<NB>(hist, misc, misc + 8, (uint32_t)cnt, (uint32_t)k);
+  cum_hist<NB, C::HCOPY, C::NBP>(hist, misc, misc + 8, (uint32_t)cnt, (uint32_t)k);
   HATA_MARK(kTrHist);
   const int lo_w = (int)misc[0];   // first nonempty bin (NB if none)
   const int hi_w = (int)misc[1];   // last nonempty bin
@@ -744,6 +765,7 @@ __global__ __launch_bounds__(kNT) void decode_step_kernel(const StepArgs a) {
         break;
       }
     }
+    HATA_MARK(kTrSearch);
     // Every wave (lane = writer) forms the writers' below-T and tie counts
     // and their prefixes itself and takes this workgroup's values by
     // readlane: no LDS round trip and no barrier.
@@ -1011,6 +1033,32 @@ StepPlan plan_decode_step(int B, int Hq, int Hkv, int64_t max_len, int k, int nu
       Wg = (int)need;
       chunk = (max_len + Wg - 1) / Wg;
       chunk = (chunk + kNT - 1) / kNT * kNT;
+    }
+  }
+  // Two workgroups per CU (instances with G <= 4 and r <= 128 are built for
+  // it) when a unit already spans several workgroups, that gives it at most
+  // 32 and the LDS fits: smaller chunks, and one workgroup's waits overlap
+  // the other's work (measured at 64K tokens, batch 4: 23.8 -> 20.2 us per
+  // step).  Not beyond 32 workgroups per unit (at 64 the exchanges cost more
+  // than that gains) and not from one (that adds both exchanges: MHA batch
+  // 8, 40.7 -> 44.8 us).
+  if (p.fused && p.G <= 4 && r <= 128 && Wg > 1) {
+    int Wg2 = 2 * num_cus / (U > 0 ? U : 1);
+    if (Wg2 > kStepWgMaxOcc2) Wg2 = kStepWgMaxOcc2;
+    if (Wg2 > by_tokens) Wg2 = (int)by_tokens;
+    int64_t chunk2 = (max_len + Wg2 - 1) / Wg2;
+    chunk2 = (chunk2 + kNT - 1) / kNT * kNT;
+    if (Wg2 > Wg && chunk2 <= kMaxChunk && (int64_t)U * Wg2 <= 2 * num_cus) {
+      size_t l2 = 0, r2 = 0;
+      switch (p.G) {
+        case 1: cfg_sizes<1>(r, k, (int)chunk2, &l2, &r2); break;
+        case 2: cfg_sizes<2>(r, k, (int)chunk2, &l2, &r2); break;
+        default: cfg_sizes<4>(r, k, (int)chunk2, &l2, &r2); break;
+      }
+      if (l2 <= kLdsPerCu / 2) {
+        Wg = Wg2;
+        chunk = chunk2;
+      }
     }
   }
   p.Wg = Wg;

@@ -250,11 +250,9 @@ __device__ __forceinline__ void load_w_regs(const float* __restrict__ Wh, WRegs<
 // first W registers start while the later ones are still arriving; each
 // accumulator still takes its 16 channels in ascending order.  Ends with
 // __syncthreads.
-// trs (optional, thread 0 only): real-time counter readings after the FMA
-// loop and after the partial sums are staged (phase measurement).
 template <int ROWS, int R = kR>
 __device__ __forceinline__ void project_pack(const WRegs<R>& wr, const float* xs, float* red,
-                                             uint64_t* out, int nrows, uint64_t* trs = nullptr) {
+                                             uint64_t* out, int nrows) {
   constexpr int CPT = Width<R>::CPT, W64 = Width<R>::W64;
   const int t = threadIdx.x, lane = t & 63, wv = t >> 6, cg = t & 31, rg = t >> 5;
   float acc[ROWS][CPT];
@@ -277,7 +275,6 @@ __device__ __forceinline__ void project_pack(const WRegs<R>& wr, const float* xs
       }
     }
   }
-  if (trs && t == 0) trs[0] = __builtin_amdgcn_s_memrealtime();
 #pragma unroll
   for (int r = 0; r < ROWS; ++r) {
     if (r >= nrows) break;
@@ -299,7 +296,6 @@ __device__ __forceinline__ void project_pack(const WRegs<R>& wr, const float* xs
     }
   }
   __syncthreads();
-  if (trs && t == 0) trs[1] = __builtin_amdgcn_s_memrealtime();
   // (row, word) pair p = row * W64 + word goes to wave p % 4
 #pragma unroll
   for (int p = wv; p < ROWS * W64; p += 4) {
