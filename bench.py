@@ -647,6 +647,10 @@ def phase_trace(cfg_id: int = 4, steps: int = 200, layers: int = 0) -> dict:
     # last ceil(U * Wg * 8 * TRACE_SLOTS / 256) * 256 bytes
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     Wg = max(1, min(cus // U, 64, -(-N // 256)))
+    if Hq // Hkv <= 4 and Wg > 1:  # two workgroups per compute unit when that gives more of them
+        Wg2 = min(2 * cus // U, 32, -(-N // 256))
+        if Wg2 > Wg and -(-N // Wg2) <= 32768 and U * Wg2 <= 2 * cus:
+            Wg = Wg2
     assert -(-N // Wg) <= 32768, "the phase trace covers shapes of at most 32768 tokens per workgroup"
     nbytes = -(-U * Wg * TRACE_SLOTS * 8 // 256) * 256
     off = ws.numel() - nbytes

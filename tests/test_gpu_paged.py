@@ -8,6 +8,7 @@ import numpy as np
 import pytest
 import torch
 
+import oracle
 from hash_top_sparse_amd import synth
 from helpers import (Dev, assert_close, check_codes, codes_np, gather_pages as _gather, gpu_build_cache,
                      gpu_query_codes, oracle_units, paginate as _paginate)
@@ -213,3 +214,19 @@ def test_staged_paged_step_equals_fused_contiguous_step(hata_gpu):
     assert torch.equal(_gather(Cp, bt, N), codes)
     assert torch.equal(idx, cidx)
     assert_close(out.cpu().numpy(), cout.cpu().numpy().astype(np.float64), "staged paged vs fused contiguous")
+
+    # and against the oracle, stage by stage on the device's own query codes
+    _log("staged paged route vs oracle")
+    bits = lambda t: t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)  # noqa: E731
+    Kn, Vn, qn = bits(K[0, 0]), bits(V[0, 0]), bits(q[0])
+    Wn = W[0].cpu().numpy()
+    cn = codes_np(codes)[0, 0]
+    check_codes(cn[N - 1:N], Kn[N - 1:N], Wn, False)
+    qc = torch.zeros((B, Hq, 1, r // 64), dtype=torch.int64, device="cuda")
+    hata_gpu.encode_append(q.view(B, Hq, 1, 128), W, qc, n_new=1)
+    torch.cuda.synchronize()
+    S = oracle.hamming_gqa(codes_np(qc)[0, :, 0], cn)
+    ridx = oracle.topk(S, k)
+    np.testing.assert_array_equal(idx.cpu().numpy()[0, 0], ridx)
+    rout = oracle.attention(qn, Kn, Vn, ridx, 0.0883883)
+    assert_close(out.cpu().numpy()[0], rout, "staged paged vs oracle")

@@ -6,7 +6,9 @@ Attention bar (derived from the kernel's arithmetic): the scores, softmax
 statistics and every accumulation are fp32, and the weights are rounded to
 bf16 before the value product (relative error <= 2^-9 each), so per element
 |gpu - ref| <= 1e-4 + 1e-3 |ref| + 2^-8 * sum_j p_j |v_j| (twice the rounding
-bound).  Codes: bit-exact on the exact recipe, the flip allowance (|p| <
+bound).  The error against the decode path's attention bar
+(2e-3 + 1e-3 |ref| per element) is logged: worst ratio and the number of
+elements past it.  Codes: bit-exact on the exact recipe, the flip allowance (|p| <
 1e-4) otherwise.  Rows past each sequence's length are left untouched."""
 from __future__ import annotations
 
@@ -15,7 +17,7 @@ import pytest
 import torch
 
 from hash_top_sparse_amd import synth
-from helpers import bf16_tensor, check_codes, codes_np, gather_pages, paginate
+from helpers import ATOL, RTOL, bf16_tensor, check_codes, codes_np, gather_pages, paginate
 from oracle import prefill as oprefill
 
 pytestmark = pytest.mark.gpu
@@ -31,6 +33,18 @@ def _log(msg):
 
 def _bar(ref, absw):
     return 1e-4 + 1e-3 * np.abs(ref) + PV_ROUND * absw
+
+
+def _check_out(got, ref, absw, what):
+    """The kernel-derived bar (asserted); against the decode path's attention
+    bar 2e-3 + 1e-3 |ref| the worst ratio and the count of elements past it
+    are returned for the log (the bf16 weights can exceed it where a few
+    keys with large |v| carry most of the weight)."""
+    err = np.abs(got - ref)
+    bar = _bar(ref, absw)
+    assert (err <= bar).all(), f"{what}: max err {err.max():.3e}, worst excess {(err - bar).max():.3e}"
+    ratio = err / (ATOL + RTOL * np.abs(ref))
+    return float(ratio.max()), int((ratio > 1).sum()), int(ratio.size)
 
 
 def _inputs(B, Hq, Hkv, q_rows, cap, r, seed, exact=False):
@@ -84,16 +98,16 @@ def test_prefill_matches_oracle(hata_gpu, case):
     ref = oprefill.causal_attention(q, K, V, lens, scale)
     absw = oprefill.abs_weighted_values(q, K, V, lens, scale)
     flips = 0
+    worst, past, total = 0.0, 0, 0
     for b in range(B):
         n = lens[b]
-        err = np.abs(out[b, :, :n] - ref[b, :, :n])
-        bar = _bar(ref[b, :, :n], absw[b, :, :n])
-        assert (err <= bar).all(), f"b={b}: max err {err.max():.3e}, worst excess {(err - bar).max():.3e}"
+        w_, p_, t_ = _check_out(out[b, :, :n], ref[b, :, :n], absw[b, :, :n], f"b={b}")
+        worst, past, total = max(worst, w_), past + p_, total + t_
         assert (out[b, :, n:] == SENT_OUT).all()
         for h in range(Hkv):
             flips += check_codes(codes[b, h, :n], K[b, h, :n], W[h], exact)
             assert (codes[b, h, n:] == np.uint64(SENT_CODE)).all()
-    _log(f"  flips {flips}")
+    _log(f"  flips {flips}; err / (2e-3 + 1e-3|ref|): worst {worst:.3g}, {past} of {total} past 1")
 
 
 def test_prefill_respects_max_len(hata_gpu):
@@ -151,18 +165,20 @@ def test_prefill_full_size_sampled(hata_gpu, Hq, Hkv, N):
     Kb = K.view(torch.int16).cpu().numpy().view(np.uint16)
     Vb = V.view(torch.int16).cpu().numpy().view(np.uint16)
     Wn = W.cpu().numpy()
+    worst, past, total = 0.0, 0, 0
     for h in range(Hq):
         qrows = q[0, h, torch.from_numpy(pos).cuda()].view(torch.int16).cpu().numpy().view(np.uint16)
         ref, absw = oprefill.attention_rows(qrows, pos, Kb[0, h // G], Vb[0, h // G], scale, with_abs=True)
         got = out[0, h, torch.from_numpy(pos).cuda()].cpu().numpy()
-        err = np.abs(got - ref)
-        assert (err <= _bar(ref, absw)).all(), f"head {h}: max err {err.max():.3e}"
+        w_, p_, t_ = _check_out(got, ref, absw, f"head {h}")
+        worst, past, total = max(worst, w_), past + p_, total + t_
     cn = codes_np(codes)
     rows = np.unique(np.concatenate([pos, rng.integers(0, N, size=200)]))
     flips = 0
     for h in range(Hkv):
         flips += check_codes(cn[0, h, rows], Kb[0, h, rows], Wn[h], False)
-    _log(f"  sampled {len(pos)} rows x {Hq} heads, {len(rows)} code rows x {Hkv} heads, flips {flips}")
+    _log(f"  sampled {len(pos)} rows x {Hq} heads, {len(rows)} code rows x {Hkv} heads, flips {flips}, "
+         f"err / (2e-3 + 1e-3|ref|): worst {worst:.3g}, {past} of {total} past 1")
 
 
 PAGED_CASES = [

@@ -11,6 +11,8 @@ from hash_top_sparse_amd import synth
 from helpers import bf16_tensor
 from oracle import train
 
+import train_bounds
+
 pytestmark = pytest.mark.gpu
 
 
@@ -106,6 +108,18 @@ def test_train_step_matches_oracle(hata_gpu, J, n, r):
     _check_step(hata_gpu, q, k, pos, r, 9400 + r + J + n)
 
 
+@pytest.mark.parametrize("terms", [(1e-3, 2e-4, 0.3), (1e-3, 0.0, 0.0), (0.0, 2e-4, 0.0), (0.0, 0.0, 0.3)],
+                         ids=["all", "similarity", "balance", "decorrelation"])
+def test_train_step_full_size_per_term(hata_gpu, terms):
+    """The training workload's full shape (512 sampled queries over 8192
+    keys, 128 hash bits), with all three loss terms and with each term alone
+    (the others' weights zero), so that an error in one term's gradient
+    cannot hide under another's."""
+    J, n, r = 512, 8192, 128
+    q, k, pos = _qk(J, n, 9800)
+    _check_step(hata_gpu, q, k, pos, r, 9801, terms=terms)
+
+
 def test_train_step_unsorted_clustered_positions(hata_gpu):
     """Query positions need not be sorted or distinct: 300 queries (two
     batches of the mask-sum kernels) with runs of equal positions at both
@@ -120,13 +134,19 @@ def test_train_step_unsorted_clustered_positions(hata_gpu):
     _check_step(hata_gpu, q, k, pos, r, 9602)
 
 
-def _check_step(hata_gpu, q, k, pos, r, seed):
+def _check_step(hata_gpu, q, k, pos, r, seed, terms=(1e-3, 2e-4, 0.3)):
+    """One device step against the fp64 oracle.  The gradient and the loss
+    terms must lie within the per-element fp32 error bounds of
+    tests/train_bounds.py (first-order probabilistic rounding analysis of
+    the same evaluation); the hyper-parameters are fp32 values, so that both
+    sides use the same ones."""
     J, n = q.shape[0], k.shape[0]
     rng = np.random.default_rng(seed)
     W0 = (rng.standard_normal((128, r)) / np.sqrt(128.0)).astype(np.float32)
-    S = train.labels(q, k, pos)
-    sigma, eps, eta, lam, lr = 1.5, 1e-3, 2e-4, 0.3, 0.02
-    _log(f"train step J={J} n={n} r={r}")
+    S = train.labels(q, k, pos).astype(np.float32).astype(np.float64)
+    sigma, lr = 1.5, float(np.float32(0.02))
+    eps, eta, lam = (float(np.float32(t)) for t in terms)
+    _log(f"train step J={J} n={n} r={r} eps={eps:g} eta={eta:g} lam={lam:g}")
     W = torch.from_numpy(W0.copy()).cuda()
     grad = torch.zeros_like(W)
     loss = torch.zeros(4, dtype=torch.float32, device="cuda")
@@ -135,17 +155,21 @@ def _check_step(hata_gpu, q, k, pos, r, seed):
                              torch.from_numpy(S.astype(np.float32)).cuda(), W, sigma, eps, eta, lam, lr,
                              loss, ws, grad=grad)
     torch.cuda.synchronize()
-    ref_g = train.grad(q, k, pos, S.astype(np.float32).astype(np.float64), W0, sigma, eps, eta, lam)
-    ref_l = train.loss(q, k, pos, S.astype(np.float32).astype(np.float64), W0, sigma, eps, eta, lam)
-    g = grad.cpu().numpy()
-    scale = np.abs(ref_g).max()
-    np.testing.assert_allclose(g, ref_g, rtol=2e-3, atol=2e-3 * scale)
-    np.testing.assert_allclose(loss.cpu().numpy(), np.array(ref_l), rtol=1e-3)
+    ref_g = train.grad(q, k, pos, S, W0, sigma, eps, eta, lam)
+    ref_l = np.array(train.loss(q, k, pos, S, W0, sigma, eps, eta, lam))
+    g = grad.cpu().numpy().astype(np.float64)
+    gb = train_bounds.grad_bound_prob(q, k, pos, S, W0, sigma, eps, eta, lam)
+    lb = train_bounds.loss_bound_prob(q, k, pos, S, W0, sigma, eps, eta, lam)
+    err = np.abs(g - ref_g)
+    _log(f"  max |err| / bound {float((err / gb).max()):.3g}, max bound / max |g| "
+         f"{float(gb.max() / np.abs(ref_g).max()):.2e}")
+    assert (err <= gb).all(), f"{int((err > gb).sum())} elements outside, worst {(err / gb).max():.3g}x"
+    lerr = np.abs(loss.cpu().numpy().astype(np.float64) - ref_l)
+    assert (lerr <= lb).all(), (lerr, lb)
     # the device forms W - lr * g, lr as fp32, with one fused multiply-add:
     # one fp32 rounding of the updated value, at most half an ulp of it
     # (2^-24 relative); the bound is set at twice that
-    lr32 = float(np.float32(lr))
-    np.testing.assert_allclose(W.cpu().numpy(), W0.astype(np.float64) - lr32 * g.astype(np.float64),
+    np.testing.assert_allclose(W.cpu().numpy(), W0.astype(np.float64) - lr * g,
                                rtol=2.0 ** -23, atol=1e-30)
 
 
