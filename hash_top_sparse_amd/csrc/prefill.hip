@@ -27,9 +27,10 @@
 //                 A and B agree)
 // The workgroup also encodes its own rows [p0, p0 + 128/G): when a tile
 // holding some of them is staged, each wave multiplies the 32-row halves of
-// the tile by 32-column slices of W_H split exactly into three bf16 terms
-// (every product exact, fp32 accumulation), takes the sign with ballots and
-// collects the 32-bit code words in LDS; the rows go to the cache at the end.
+// the tile by 32-column slices of W_H split into two bf16 terms, in the same
+// order of products and accumulations as the bulk encode (so the codes are
+// the same bit for bit), takes the sign with ballots and collects the 32-bit
+// code words in LDS; the rows go to the cache at the end.
 //
 // Blocks are issued heaviest first (the causal work grows with the position)
 // and (sequence, KV head) varies fastest, so with B * Hkv a multiple of 8
@@ -383,21 +384,17 @@ __global__ __launch_bounds__(kNT, 2) void prefill_kernel(PrefillArgs a) {
           for (int i = 0; i < 16; ++i) e[i] = 0.f;
 #pragma unroll 1
           for (int kk = 0; kk < 8; ++kk) {
-            bf16x8 w1, w2, w3;
+            bf16x8 w1, w2;
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
               const float v = Wh[(16 * kk + 8 * half + j) * R + 32 * ct + (lane & 31)];
               const __bf16 a1 = (__bf16)v;
-              const float r1 = v - (float)a1;
-              const __bf16 a2 = (__bf16)r1;
               w1[j] = a1;
-              w2[j] = a2;
-              w3[j] = (__bf16)(r1 - (float)a2);
+              w2[j] = (__bf16)(v - (float)a1);
             }
             const bf16x8 af = *reinterpret_cast<const bf16x8*>(krow + 16 * kk);
             e = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, w1, e, 0, 0, 0);
             e = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, w2, e, 0, 0, 0);
-            e = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, w3, e, 0, 0, 0);
           }
           // element i: lanes 0-31 hold row 8 (i/4) + i%4, lanes 32-63 the
           // row 4 below, at columns 32 ct + lane % 32

@@ -368,28 +368,36 @@ def test_stream_read_reads_every_word(hata_gpu):
 
 
 @pytest.mark.parametrize("dist", ["exact", "gauss"])
-def test_bulk_encode_matches_row_encode(hata_gpu, dist):
+@pytest.mark.parametrize("n", [3000, 20000], ids=["4-tile-workgroups", "16-tile-workgroups"])
+def test_bulk_encode_matches_row_encode(hata_gpu, dist, n):
     """The matrix-core bulk path and the per-row path agree: bit-identical on
-    the exact recipe, within the flip allowance of each other otherwise."""
-    s = _shape(2, 4, 2, 3000, 16, dist=dist, seed=7950)
-    inp = synth.make_inputs(s, cap=3100)
+    the exact recipe, within the flip allowance of each other otherwise.
+    3000 rows run in workgroups of 4 tiles of 128 rows; 20000 rows in
+    workgroups of 16 tiles, the last one ragged (every workgroup's last tile
+    is written from all four waves' words)."""
+    cap = n + 100
+    s = _shape(2, 4, 2, n, 16, dist=dist, seed=7950 + n)
+    inp = synth.make_inputs(s, cap=cap)
     d = Dev(inp)
-    bulk = torch.zeros((2, 2, 3100, 2), dtype=torch.int64, device="cuda")
-    hata_gpu.encode_append(d.K, d.W, bulk, n_new=3000)       # matrix cores
+    bulk = torch.zeros((2, 2, cap, 2), dtype=torch.int64, device="cuda")
+    hata_gpu.encode_append(d.K, d.W, bulk, n_new=n)       # matrix cores
     rows = torch.zeros_like(bulk)
-    for start in range(0, 3000, 500):                      # per-row path, 500 rows at a time
+    step = 500 if n <= 3000 else 511                    # per-row path (below the bulk threshold)
+    for start in range(0, n, step):
         pos = torch.full((2,), start, dtype=torch.int32, device="cuda")
-        hata_gpu.encode_append(d.K, d.W, rows, n_new=min(500, 3000 - start), pos=pos)
+        hata_gpu.encode_append(d.K, d.W, rows, n_new=min(step, n - start), pos=pos)
     torch.cuda.synchronize()
     a, b_ = codes_np(bulk), codes_np(rows)
-    assert (a[:, :, 3000:] == 0).all()
+    assert (a[:, :, n:] == 0).all()
     if dist == "exact":
         np.testing.assert_array_equal(a, b_)
     else:
+        rng = np.random.default_rng(n)
         for b in range(2):
             for h in range(2):
-                check_codes(a[b, h, :3000], inp.K[b, h, :3000], inp.W[h], exact=False)
-                check_codes(b_[b, h, :3000], inp.K[b, h, :3000], inp.W[h], exact=False)
+                sel = np.sort(rng.choice(n, size=min(n, 3000), replace=False))
+                check_codes(a[b, h, sel], inp.K[b, h, sel], inp.W[h], exact=False)
+                check_codes(b_[b, h, sel], inp.K[b, h, sel], inp.W[h], exact=False)
 
 
 # ------------------------------------- separate query and key encoders

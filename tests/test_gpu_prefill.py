@@ -126,8 +126,10 @@ def test_prefill_respects_max_len(hata_gpu):
 
 def test_prefill_equals_separate_encode(hata_gpu):
     """The codes the prefill writes equal those of hata_encode_append on the
-    same keys (the bulk matrix-core path), bit for bit, on Gaussian inputs."""
-    B, Hq, Hkv, n = 1, 8, 2, 1000
+    same keys (the bulk matrix-core path), bit for bit, on Gaussian inputs
+    (both form the same two-term products in the same order; 786,432
+    projections, so a different rounding would show)."""
+    B, Hq, Hkv, n = 1, 8, 2, 3072
     q, K, V, W = _inputs(B, Hq, Hkv, n, n, 128, seed=8950)
     _, codes = _run(hata_gpu, q, K, V, W, [n], n, 0.0883883)
     sep = torch.zeros((B, Hkv, n, 2), dtype=torch.int64, device="cuda")
