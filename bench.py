@@ -612,7 +612,7 @@ TRACE_ORDER = (0, 13, 1, 2, 3, 4, 5, 6, 16, 7, 8, 9, 10, 11, 12)
 TRACE_SLOTS = 24  # timestamps stored per workgroup
 
 
-def phase_trace(cfg_id: int = 4, steps: int = 200, layers: int = 0) -> dict:
+def phase_trace(cfg_id: int = 4, steps: int = 200, layers: int = 0, r: int = 128) -> dict:
     """Per-phase timeline of the fused step, from the phase-trace build of the
     library (libhata_trace.so: thread 0 of every workgroup reads the 100 MHz
     real-time counter at each phase boundary and stores the readings in the
@@ -626,9 +626,13 @@ def phase_trace(cfg_id: int = 4, steps: int = 200, layers: int = 0) -> dict:
 
     from hash_top_sparse_amd import binding, synth
 
+    import dataclasses
+
     binding.load(binding.TRACE_LIB_PATH)
     dev = torch.device("cuda:0")
     shape = synth.CONFIGS[cfg_id]
+    if r != shape.r:
+        shape = dataclasses.replace(shape, r=r, name=f"{shape.name}-r{r}")
     B, Hq, Hkv, N, k = shape.B, shape.Hq, shape.Hkv, shape.N, shape.k
     U = B * Hkv
     L = layers or max(2, min(64, int(np.ceil(1.5e9 / step_bytes(B, Hq, Hkv, N, k)))))
@@ -637,17 +641,17 @@ def phase_trace(cfg_id: int = 4, steps: int = 200, layers: int = 0) -> dict:
     q0, K0, V0 = bf(inp.q), bf(inp.K), bf(inp.V)
     W = torch.from_numpy(inp.W).to(dev)
     seq = torch.from_numpy(inp.seq_lens).to(dev)
-    codes0 = torch.zeros((B, Hkv, N, 2), dtype=torch.int64, device=dev)
+    codes0 = torch.zeros((B, Hkv, N, (r + 63) // 64), dtype=torch.int64, device=dev)
     binding.encode_append(K0, W, codes0, n_new=N)
     bufs = [(K0.clone() if l else K0, V0.clone() if l else V0, codes0.clone() if l else codes0)
             for l in range(L)]
-    ws = binding.alloc_workspace(binding.OP_DECODE_STEP, B, Hq, Hkv, N, k, device=dev)
+    ws = binding.alloc_workspace(binding.OP_DECODE_STEP, B, Hq, Hkv, N, k, device=dev, r=r)
     # workgroups per unit as the library plans them for these sizes (a
     # fused step within the LDS limit); the trace area is the workspace's
     # last ceil(U * Wg * 8 * TRACE_SLOTS / 256) * 256 bytes
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     Wg = max(1, min(cus // U, 64, -(-N // 256)))
-    if Hq // Hkv <= 4 and Wg > 1:  # two workgroups per compute unit when that gives more of them
+    if Hq // Hkv <= 4 and r <= 128 and Wg > 1:  # two workgroups per compute unit when that gives more of them
         Wg2 = min(2 * cus // U, 32, -(-N // 256))
         if Wg2 > Wg and -(-N // Wg2) <= 32768 and U * Wg2 <= 2 * cus:
             Wg = Wg2
@@ -735,6 +739,7 @@ def main() -> int:
                     help="short run for hardware-counter passes on the prefill: one 32K-token prefill")
     ap.add_argument("--train-run", action="store_true",
                     help="only the training step, 20 calls (for kernel traces)")
+    ap.add_argument("--r", type=int, default=128, help="code width for --phase-trace (32, 64, 128, 256)")
     ap.add_argument("--phase-trace", action="store_true",
                     help="only the per-phase timeline of the fused step (phase-trace build of the library)")
     ap.add_argument("--pmc-run", action="store_true",
@@ -754,8 +759,8 @@ def main() -> int:
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
     if args.phase_trace:
-        for c in ((args.config,) if args.config != 4 else (4, 2, 1)):
-            print(json.dumps({"phase_trace": phase_trace(c, steps=200)}), flush=True)
+        for c in ((args.config,) if args.config != 4 or args.r != 128 else (4, 2, 1)):
+            print(json.dumps({"phase_trace": phase_trace(c, steps=200, r=args.r)}), flush=True)
         return 0
     binding.load()
     if args.prefill_run:
