@@ -713,6 +713,33 @@ def phase_trace(cfg_id: int = 4, steps: int = 200, layers: int = 0, r: int = 128
     return res
 
 
+def bulk_run(cfg_id: int = 4, calls: int = 20) -> None:
+    """Short run for counter passes on the bulk encode: `calls` encodes of
+    the workload's whole key cache (every KV head, all N rows) over rotating
+    key tensors, then one plain device copy of 1 GiB as the byte-counter
+    reference."""
+    import torch
+
+    from hash_top_sparse_amd import binding, synth
+
+    shape = synth.CONFIGS[cfg_id]
+    B, Hkv, N = shape.B, shape.Hkv, shape.N
+    g = torch.Generator(device="cuda").manual_seed(5)
+    keys = [torch.randn((B, Hkv, N, 128), generator=g, device="cuda").to(torch.bfloat16) for _ in range(4)]
+    W = torch.randn((Hkv, 128, 128), generator=g, device="cuda") / 128 ** 0.5
+    codes = torch.zeros((B, Hkv, N, 2), dtype=torch.int64, device="cuda")
+    for i in range(calls):
+        binding.encode_append(keys[i % len(keys)], W, codes, n_new=N)
+    torch.cuda.synchronize()
+    src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    src.fill_(1)
+    torch.cuda.synchronize()
+    dst.copy_(src)  # reference: reads and writes exactly 1 GiB
+    torch.cuda.synchronize()
+    log(f"bulk run done: {calls} encodes of {B * Hkv * N} keys; reference copy of 1073741824 bytes")
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -737,6 +764,9 @@ def main() -> int:
                     help="skip the 32-layer decode (one graph per token) at 32K/64K/128K against dense")
     ap.add_argument("--prefill-run", action="store_true",
                     help="short run for hardware-counter passes on the prefill: one 32K-token prefill")
+    ap.add_argument("--bulk-run", action="store_true",
+                    help="short run for hardware-counter passes on the bulk encode (20 encodes of the "
+                         "workload's key cache, then a 1 GiB reference copy)")
     ap.add_argument("--train-run", action="store_true",
                     help="only the training step, 20 calls (for kernel traces)")
     ap.add_argument("--r", type=int, default=128, help="code width for --phase-trace (32, 64, 128, 256)")
@@ -766,6 +796,9 @@ def main() -> int:
     if args.prefill_run:
         prefill_bench(reps=1, paged=False)
         log("prefill run done")
+        return 0
+    if args.bulk_run:
+        bulk_run(args.config)
         return 0
     if args.train_run:
         train_bench(steps=20)
