@@ -226,45 +226,88 @@ __global__ __launch_bounds__(kLabNT) void labels_kernel(const uint16_t* __restri
 // B(k 2 kk + l / 32, col l % 32).  Products with few output tiles and a
 // long k split k over blockIdx.z; each split writes its own partial tile and
 // a second kernel adds the partials in split order (deterministic).
+// Each accessor also reads kVec consecutive elements along its contiguous
+// index with one 16-byte load (vec), allowed when ld is a multiple of kVec
+// (the base pointers are 16-byte aligned).
 struct AccF32 {  // row-major [rows][ld]
   static constexpr bool kColFast = true;
+  static constexpr int kVec = 4;
   const float* p; int ld;
   __device__ float operator()(int r, int c) const { return p[(int64_t)r * ld + c]; }
+  __device__ void vec(int r, int c, float* o) const {  // (r, c .. c + 3)
+    const float4 v = *reinterpret_cast<const float4*>(p + (int64_t)r * ld + c);
+    o[0] = v.x; o[1] = v.y; o[2] = v.z; o[3] = v.w;
+  }
+  __device__ bool vec_ok() const { return (ld & 3) == 0; }
 };
 struct AccF32T {  // element (r, c) of the transpose of a row-major [.][ld]
   static constexpr bool kColFast = false;
+  static constexpr int kVec = 4;
   const float* p; int ld;
   __device__ float operator()(int r, int c) const { return p[(int64_t)c * ld + r]; }
+  __device__ void vec(int r, int c, float* o) const {  // (r .. r + 3, c)
+    const float4 v = *reinterpret_cast<const float4*>(p + (int64_t)c * ld + r);
+    o[0] = v.x; o[1] = v.y; o[2] = v.z; o[3] = v.w;
+  }
+  __device__ bool vec_ok() const { return (ld & 3) == 0; }
 };
 struct AccBf16 {
   static constexpr bool kColFast = true;
+  static constexpr int kVec = 8;
   const uint16_t* p; int ld;
   __device__ float operator()(int r, int c) const { return __uint_as_float((uint32_t)p[(int64_t)r * ld + c] << 16); }
+  __device__ void vec(int r, int c, float* o) const {  // (r, c .. c + 7)
+    const uint4 v = *reinterpret_cast<const uint4*>(p + (int64_t)r * ld + c);
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) { o[2 * i] = bf16_lo(w[i]); o[2 * i + 1] = bf16_hi(w[i]); }
+  }
+  __device__ bool vec_ok() const { return (ld & 7) == 0; }
 };
 struct AccBf16T {
   static constexpr bool kColFast = false;
+  static constexpr int kVec = 8;
   const uint16_t* p; int ld;
   __device__ float operator()(int r, int c) const { return __uint_as_float((uint32_t)p[(int64_t)c * ld + r] << 16); }
+  __device__ void vec(int r, int c, float* o) const {  // (r .. r + 7, c)
+    const uint4 v = *reinterpret_cast<const uint4*>(p + (int64_t)c * ld + r);
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) { o[2 * i] = bf16_lo(w[i]); o[2 * i + 1] = bf16_hi(w[i]); }
+  }
+  __device__ bool vec_ok() const { return (ld & 7) == 0; }
 };
 struct AccGramMinusI {  // (W^T W - I)[r][c] from a precomputed W^T W
   static constexpr bool kColFast = true;
+  static constexpr int kVec = 4;
   const float* p; int ld;
   __device__ float operator()(int r, int c) const { return p[(int64_t)r * ld + c] - (r == c ? 1.f : 0.f); }
+  __device__ void vec(int r, int c, float* o) const {
+    const float4 v = *reinterpret_cast<const float4*>(p + (int64_t)r * ld + c);
+    o[0] = v.x - (r == c ? 1.f : 0.f); o[1] = v.y - (r == c + 1 ? 1.f : 0.f);
+    o[2] = v.z - (r == c + 2 ? 1.f : 0.f); o[3] = v.w - (r == c + 3 ? 1.f : 0.f);
+  }
+  __device__ bool vec_ok() const { return (ld & 3) == 0; }
 };
 
 constexpr int kT = 64, kKS = 32, kLdsRow = kT + 4, kFill = kT * kKS / 256;
 
-// element u of this thread's share of the A tile (rows m0.., k k0..)
-template <bool ColFast>
-__device__ inline void a_slot(int t, int u, int& mm, int& kk) {
-  const int e = t + 256 * u;
-  if constexpr (ColFast) { mm = e / kKS; kk = e % kKS; } else { mm = e % kT; kk = e / kT; }
+// Tile fills in 16-byte pieces: piece q of the A tile (rows m0 .., k k0 ..)
+// or of the B tile (k k0 .., columns n0 ..) covers V = Acc::kVec consecutive
+// elements along the accessor's contiguous index, consecutive pieces walking
+// that index so a wave's loads coalesce.  (mm, kk) / (kk, nn) is the first
+// element; the others follow along k (dk = 1) or along m / n.
+template <class Acc>
+__device__ inline void a_piece(int q, int& mm, int& kk) {
+  constexpr int V = Acc::kVec;
+  if constexpr (Acc::kColFast) { mm = q / (kKS / V); kk = (q % (kKS / V)) * V; }
+  else { kk = q / (kT / V); mm = (q % (kT / V)) * V; }
 }
-// element u of this thread's share of the B tile (k k0.., columns n0..)
-template <bool ColFast>
-__device__ inline void b_slot(int t, int u, int& kk, int& nn) {
-  const int e = t + 256 * u;
-  if constexpr (ColFast) { nn = e % kT; kk = e / kT; } else { nn = e / kKS; kk = e % kKS; }
+template <class Acc>
+__device__ inline void b_piece(int q, int& kk, int& nn) {
+  constexpr int V = Acc::kVec;
+  if constexpr (Acc::kColFast) { kk = q / (kT / V); nn = (q % (kT / V)) * V; }
+  else { nn = q / (kKS / V); kk = (q % (kKS / V)) * V; }
 }
 
 template <class A, class B>
@@ -276,15 +319,45 @@ __global__ __launch_bounds__(256) void gemm_kernel(int M, int N, int K, int kchu
   const int t = threadIdx.x;
   const int m0 = blockIdx.y * kT, n0 = blockIdx.x * kT;
   const int kbeg = blockIdx.z * kchunk, kend = min(K, kbeg + kchunk);
+  // this thread's pieces: A::kVec (B::kVec) elements each, kFill in all
+  constexpr int PA = kFill / A::kVec, PB = kFill / B::kVec;
   float ra[kFill], rb[kFill];
+  const bool va = a.vec_ok(), vb = b.vec_ok();
   auto fetch = [&](int k0) {
 #pragma unroll
-    for (int u = 0; u < kFill; ++u) {
-      int mm, kk, nn, kb;
-      a_slot<A::kColFast>(t, u, mm, kk);
-      ra[u] = (m0 + mm < M && k0 + kk < kend) ? a(m0 + mm, k0 + kk) : 0.f;
-      b_slot<B::kColFast>(t, u, kb, nn);
-      rb[u] = (k0 + kb < kend && n0 + nn < N) ? b(k0 + kb, n0 + nn) : 0.f;
+    for (int u = 0; u < PA; ++u) {
+      int mm, kk;
+      a_piece<A>(t + 256 * u, mm, kk);
+      float* o = ra + u * A::kVec;
+      const int m = m0 + mm, k = k0 + kk;
+      // the piece's last element (along k or along m)
+      const bool full = A::kColFast ? (m < M && k + A::kVec <= kend) : (m + A::kVec <= M && k < kend);
+      if (va && full) {
+        a.vec(m, k, o);
+      } else {
+#pragma unroll
+        for (int i = 0; i < A::kVec; ++i) {
+          const int mi = A::kColFast ? m : m + i, ki = A::kColFast ? k + i : k;
+          o[i] = (mi < M && ki < kend) ? a(mi, ki) : 0.f;
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < PB; ++u) {
+      int kk, nn;
+      b_piece<B>(t + 256 * u, kk, nn);
+      float* o = rb + u * B::kVec;
+      const int k = k0 + kk, n = n0 + nn;
+      const bool full = B::kColFast ? (k < kend && n + B::kVec <= N) : (k + B::kVec <= kend && n < N);
+      if (vb && full) {
+        b.vec(k, n, o);
+      } else {
+#pragma unroll
+        for (int i = 0; i < B::kVec; ++i) {
+          const int ki = B::kColFast ? k : k + i, ni = B::kColFast ? n + i : n;
+          o[i] = (ki < kend && ni < N) ? b(ki, ni) : 0.f;
+        }
+      }
     }
   };
   typedef float f32x16 __attribute__((ext_vector_type(16)));
@@ -295,12 +368,24 @@ __global__ __launch_bounds__(256) void gemm_kernel(int M, int N, int K, int kchu
   if (kbeg < kend) fetch(kbeg);
   for (int k0 = kbeg; k0 < kend; k0 += kKS) {
 #pragma unroll
-    for (int u = 0; u < kFill; ++u) {
-      int mm, kk, nn, kb;
-      a_slot<A::kColFast>(t, u, mm, kk);
-      as[kk][mm] = ra[u];
-      b_slot<B::kColFast>(t, u, kb, nn);
-      bs[kb][nn] = rb[u];
+    for (int u = 0; u < PA; ++u) {
+      int mm, kk;
+      a_piece<A>(t + 256 * u, mm, kk);
+#pragma unroll
+      for (int i = 0; i < A::kVec; ++i) {
+        if constexpr (A::kColFast) as[kk + i][mm] = ra[u * A::kVec + i];
+        else as[kk][mm + i] = ra[u * A::kVec + i];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < PB; ++u) {
+      int kk, nn;
+      b_piece<B>(t + 256 * u, kk, nn);
+#pragma unroll
+      for (int i = 0; i < B::kVec; ++i) {
+        if constexpr (B::kColFast) bs[kk][nn + i] = rb[u * B::kVec + i];
+        else bs[kk + i][nn] = rb[u * B::kVec + i];
+      }
     }
     __syncthreads();
     if (k0 + kKS < kend) fetch(k0 + kKS);
