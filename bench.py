@@ -699,7 +699,18 @@ def phase_trace(cfg_id: int = 4, steps: int = 200, layers: int = 0, r: int = 128
             entry["p90_phase_us"] = float(np.nanpercentile(dur, 90))
         phases[name] = entry
         prev = j
-    res = {"workload": shape.name, "workgroups": nwg, "units": U, "steps": steps, "layers": L,
+    # values the traced build records in slots 20..23 (search rounds, window
+    # base, smallest own k-th score, threshold | kept rows << 16)
+    vals = rec.cpu().numpy().view(np.uint64).reshape(steps, -1, TRACE_SLOTS).astype(np.int64)[:, :U * Wg, 20:24]
+    kept = vals[:, :, 3] >> 16
+    search = {"rounds_median": float(np.median(vals[:, :, 0])), "rounds_max": int(vals[:, :, 0].max()),
+              "window_base_median": float(np.median(vals[:, :, 1])),
+              "min_kth_median": float(np.median(vals[:, :, 2])),
+              "threshold_median": float(np.median(vals[:, :, 3] & 0xFFFF)),
+              "kept_rows_per_workgroup_median": float(np.median(kept)),
+              "kept_rows_per_workgroup_max_median_over_steps": float(np.median(kept.max(axis=1)))}
+    log(f"search: {search}")
+    res = {"workload": shape.name, "workgroups": nwg, "units": U, "steps": steps, "layers": L, "search": search,
            "kernel_us_hip_events_median": float(np.median(ev_us)),
            "span_first_start_to_last_end_us_median": float(max_rel[TRACE_POINTS.index("end")]),
            "start_spread_us_median": float(max_rel[0]), "phases": phases}

@@ -103,6 +103,12 @@ enum TracePoint {
   do {                                                        \
     if (threadIdx.x == 0) tr_ts[i] = __builtin_amdgcn_s_memrealtime(); \
   } while (0)
+// a value recorded in slot i (slots 20..23: search rounds, window base,
+// smallest own k-th score, threshold | kept rows << 16)
+#define HATA_VALUE(i, v) \
+  do {                                                        \
+    if (threadIdx.x == 0) tr_ts[i] = (uint64_t)(v);           \
+  } while (0)
 #define HATA_TRACE_STORE()                                                     \
   do {                                                                         \
     if (threadIdx.x == 0) {                                                    \
@@ -112,6 +118,7 @@ enum TracePoint {
   } while (0)
 #else
 #define HATA_MARK(i) do {} while (0)
+#define HATA_VALUE(i, v) do {} while (0)
 #define HATA_TRACE_STORE() do {} while (0)
 #endif
 
@@ -740,7 +747,10 @@ __global__ __launch_bounds__(kNT, (step_occupancy<G, R>())) void decode_step_ker
     const int glo = (int)misc[16], tmin = (int)misc[17];
     int Tw = tmin;
     const int nper = (a.Wg + 3) / 4;
+    HATA_VALUE(21, glo);
+    HATA_VALUE(22, tmin);
     for (int c0 = glo, rnd = 0; c0 <= tmin; c0 += 64, ++rnd) {
+      HATA_VALUE(20, rnd + 1);
       const int s2 = c0 + lane;
       // writers wv, wv+4, ... in groups of 8 (unused header slots count 0)
       uint32_t part = 0;
@@ -878,6 +888,7 @@ __global__ __launch_bounds__(kNT, (step_occupancy<G, R>())) void decode_step_ker
   }
 
   HATA_MARK(kTrAttended);
+  HATA_VALUE(23, (uint32_t)T | ((uint32_t)m_self << 16));
   // kept indices, written once the attention no longer needs the LDS list
   // (coalesced, and no barrier waits on these stores)
   auto write_idx = [&]() {
