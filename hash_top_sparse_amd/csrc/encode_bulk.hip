@@ -118,37 +118,13 @@ __global__ __launch_bounds__(kNT, 2) void encode_bulk_kernel(
     for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[rt][i] = 0.f;
-    // k-step s: the four row blocks' fragments are read one step ahead, and
-    // the eight products of a step run W1 over the four accumulators, then
-    // W2, so that dependent products are four apart
-    const uint16_t* xrow = xs + (lane & 31) * kXsStride + 8 * (lane >> 5);
-    bf16x8 xf[2][4];
-#pragma unroll
-    for (int rt = 0; rt < 4; ++rt)
-      xf[0][rt] = *reinterpret_cast<const bf16x8*>(xrow + rt * 32 * kXsStride);
-#pragma unroll
-    for (int s = 0; s < 8; ++s) {
-      if (s + 1 < 8) {
-#pragma unroll
-        for (int rt = 0; rt < 4; ++rt)
-          xf[(s + 1) & 1][rt] = *reinterpret_cast<const bf16x8*>(xrow + rt * 32 * kXsStride + 16 * (s + 1));
-      }
-#pragma unroll
-      for (int rt = 0; rt < 4; ++rt)
-        acc[rt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(w1[s], xf[s & 1][rt], acc[rt], 0, 0, 0);
-#pragma unroll
-      for (int rt = 0; rt < 4; ++rt)
-        acc[rt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(w2[s], xf[s & 1][rt], acc[rt], 0, 0, 0);
-    }
-    __syncthreads();  // every wave done reading the tile
-    // sign + pack: accumulator i of lane l is bit 8*(i/4) + 4*(l/32) + i%4
-    // of word wv of row rt*32 + l%32.  The 16 sign bits are shifted into one
-    // word (one alignbit each), spread to their nibbles and inverted: a code
-    // bit is 1 where the sign bit is clear, which is p >= 0 for every p the
-    // accumulation can produce (it starts at +0, and an exact zero sum of
-    // fp32 terms rounds to +0, never -0).
-#pragma unroll
-    for (int rt = 0; rt < 4; ++rt) {
+    // sign + pack of row block rt: accumulator i of lane l is bit
+    // 8*(i/4) + 4*(l/32) + i%4 of word wv of row rt*32 + l%32.  The 16 sign
+    // bits are shifted into one word (one alignbit each), spread to their
+    // nibbles and inverted: a code bit is 1 where the sign bit is clear,
+    // which is p >= 0 for every p the accumulation can produce (it starts at
+    // +0, and an exact zero sum of fp32 terms rounds to +0, never -0).
+    auto pack = [&](int rt) {
       uint32_t neg = 0;
 #pragma unroll
       for (int i = 15; i >= 0; --i) neg = __builtin_amdgcn_alignbit(neg, __float_as_uint(acc[rt][i]), 31);
@@ -156,7 +132,40 @@ __global__ __launch_bounds__(kNT, 2) void encode_bulk_kernel(
       uint32_t part = (~neg & 0x0F0F0F0Fu) << (4 * (lane >> 5));
       part |= __shfl_xor(part, 32);
       if (lane < 32) cw[(j * kTileRows + rt * 32 + lane) * 4 + wv] = part;
+    };
+    // Two halves of two row blocks each: the first half's products, then the
+    // second half's with the first half's packing placed among them (vector
+    // work that the matrix core's latency hides), then the second half's
+    // packing.  Fragments are read one k-step ahead; within a step W1 runs
+    // over the half's two accumulators, then W2.
+    const uint16_t* xrow = xs + (lane & 31) * kXsStride + 8 * (lane >> 5);
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+      bf16x8 xf[2][2];
+#pragma unroll
+      for (int q = 0; q < 2; ++q)
+        xf[0][q] = *reinterpret_cast<const bf16x8*>(xrow + (2 * hf + q) * 32 * kXsStride);
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        if (s + 1 < 8) {
+#pragma unroll
+          for (int q = 0; q < 2; ++q)
+            xf[(s + 1) & 1][q] =
+                *reinterpret_cast<const bf16x8*>(xrow + (2 * hf + q) * 32 * kXsStride + 16 * (s + 1));
+        }
+#pragma unroll
+        for (int q = 0; q < 2; ++q)
+          acc[2 * hf + q] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(w1[s], xf[s & 1][q], acc[2 * hf + q], 0, 0, 0);
+#pragma unroll
+        for (int q = 0; q < 2; ++q)
+          acc[2 * hf + q] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(w2[s], xf[s & 1][q], acc[2 * hf + q], 0, 0, 0);
+        if (hf == 1 && s == 2) pack(0);
+        if (hf == 1 && s == 5) pack(1);
+      }
     }
+    __syncthreads();  // every wave done reading the tile
+    pack(2);
+    pack(3);
   };
   // Every workgroup runs all TILES tiles: tiles past the rows read zeros and
   // their stores are dropped.  The loop unrolls completely (refill is known
