@@ -177,7 +177,6 @@ def measure(cfg_id: int, steps: int, warmup: int, dense_steps: int, layers: int,
     if r != shape.r:
         shape = dataclasses.replace(shape, r=r, name=f"{shape.name}-r{r}")
     B, Hq, Hkv, N, k = shape.B, shape.Hq, shape.Hkv, shape.N, shape.k
-    words = (r + 63) // 64
     per_step = step_bytes(B, Hq, Hkv, N, k, r=r)
     L = layers or max(2, min(64, int(np.ceil(1.5e9 / per_step))))
     log(f"workload {shape.name}: B={B} Hq={Hq} Hkv={Hkv} N={N} k={k}; {L} layer caches")
@@ -188,7 +187,7 @@ def measure(cfg_id: int, steps: int, warmup: int, dense_steps: int, layers: int,
     q0, K0, V0 = bf(inp.q), bf(inp.K), bf(inp.V)
     W = torch.from_numpy(inp.W).to(dev)
     seq = torch.from_numpy(inp.seq_lens).to(dev)
-    codes0 = torch.zeros((B, Hkv, N, words), dtype=torch.int64, device=dev)
+    codes0 = binding.new_codes(B, Hkv, N, r=r, device=dev)
     binding.encode_append(K0, W, codes0, n_new=N)
     torch.cuda.synchronize()
     layer_bufs = []
@@ -431,7 +430,7 @@ def prefill_bench(N: int = 32768, B: int = 1, Hq: int = 32, Hkv: int = 8, r: int
     V = torch.randn((B, Hkv, N, 128), generator=g, device=dev).to(torch.bfloat16)
     W = torch.randn((Hkv, 128, r), generator=g, device=dev) / np.sqrt(128.0)
     out = torch.empty((B, Hq, N, 128), dtype=torch.float32, device=dev)
-    codes = torch.zeros((B, Hkv, N, (r + 63) // 64), dtype=torch.int64, device=dev)
+    codes = binding.new_codes(B, Hkv, N, r=r, device=dev)
     seq = torch.full((B,), N, dtype=torch.int32, device=dev)
     scale = 1.0 / np.sqrt(128.0)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -641,7 +640,7 @@ def phase_trace(cfg_id: int = 4, steps: int = 200, layers: int = 0, r: int = 128
     q0, K0, V0 = bf(inp.q), bf(inp.K), bf(inp.V)
     W = torch.from_numpy(inp.W).to(dev)
     seq = torch.from_numpy(inp.seq_lens).to(dev)
-    codes0 = torch.zeros((B, Hkv, N, (r + 63) // 64), dtype=torch.int64, device=dev)
+    codes0 = binding.new_codes(B, Hkv, N, r=r, device=dev)
     binding.encode_append(K0, W, codes0, n_new=N)
     bufs = [(K0.clone() if l else K0, V0.clone() if l else V0, codes0.clone() if l else codes0)
             for l in range(L)]
@@ -850,8 +849,9 @@ def main() -> int:
             rr, _ = measure(args.config, sub_steps, 16, 0, 0, not args.no_graph,
                             with_bulk=False, with_qk=False, r=r)
             B_, Hkv_, N_ = shape.B, shape.Hkv, shape.N
-            # the stored rows: ceil(r/64) words, so 32-bit codes move 8 bytes a row
-            layout = rr["bytes_per_step"] + B_ * Hkv_ * N_ * (((r + 63) // 64) * 8 - r // 8)
+            # code rows are stored in r/8 bytes (4 at r = 32): the stored bytes
+            # are the formula's
+            layout = rr["bytes_per_step"]
             wsweep[str(r)] = {"ms_per_step": rr["ms_per_step"], "steps_per_s": rr["steps_per_s"],
                               "GBs": rr["GBs"], "frac_of_peak": rr["frac_of_peak"],
                               "bytes_per_step": rr["bytes_per_step"], "stored_bytes_per_step": layout}

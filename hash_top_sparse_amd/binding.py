@@ -6,9 +6,11 @@ pointers plus torch's current stream to the C entry point of the same name,
 and raises HataError on a non-zero status.  Every step of the path runs in
 the library's HIP kernels; there is no fallback.
 
-dtype conventions on the torch side: bf16 arrays are torch.bfloat16, codes
-are torch.int64 holding the uint64 code words, scores are torch.int16 holding
-uint16 values, indices are torch.int32.
+dtype conventions on the torch side: bf16 arrays are torch.bfloat16; a code
+row of r bits is r/32 32-bit words, held as torch.int32 [..., r/32] or, for
+r >= 64, as torch.int64 [..., r/64] (the same bytes; `new_codes` makes the
+int64 form for r >= 64 and the int32 one at r = 32); scores are torch.int16
+holding uint16 values, indices are torch.int32.
 """
 from __future__ import annotations
 
@@ -115,6 +117,32 @@ def _need(t: torch.Tensor, dtype: torch.dtype, name: str) -> None:
         raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
 
 
+def _need_codes(t: torch.Tensor, r: int, name: str) -> None:
+    """A code tensor for r-bit codes: int32 rows of r/32 words, or int64 rows
+    of r/64 words when r >= 64."""
+    if t.dtype == torch.int32:
+        ok = t.shape[-1] == r // 32
+    elif t.dtype == torch.int64:
+        ok = r >= 64 and t.shape[-1] == r // 64
+    else:
+        raise TypeError(f"{name} must be torch.int32 or torch.int64, got {t.dtype}")
+    if not ok:
+        raise ValueError(f"{name}: last dimension {t.shape[-1]} ({t.dtype}) does not hold {r}-bit codes")
+
+
+def code_bits(t: torch.Tensor) -> int:
+    """Code width r of a code tensor (from its last dimension and dtype)."""
+    return t.shape[-1] * (32 if t.dtype == torch.int32 else 64)
+
+
+def new_codes(*shape: int, r: int = 128, device="cuda", fill: int = 0) -> torch.Tensor:
+    """A code tensor [*shape, words] for r-bit codes: int64 words for r >= 64,
+    one int32 word per row at r = 32."""
+    if r >= 64:
+        return torch.full((*shape, r // 64), fill, dtype=torch.int64, device=device)
+    return torch.full((*shape, r // 32), fill, dtype=torch.int32, device=device)
+
+
 def _stream(stream=None):
     s = torch.cuda.current_stream() if stream is None else stream
     return ctypes.c_void_p(s.cuda_stream)
@@ -124,15 +152,15 @@ def _stream(stream=None):
 
 def encode_append(x: torch.Tensor, W_H: torch.Tensor, codes: torch.Tensor, n_new: int,
                   pos: torch.Tensor | None = None, stream=None) -> None:
-    """x bf16 [B,H,x_rows,d]; W_H f32 [Hkv,d,r]; codes int64 [B,H,cap,ceil(r/64)]
-    (r in 32, 64, 128, 256; for r = 32 the high half of each word stays 0)."""
+    """x bf16 [B,H,x_rows,d]; W_H f32 [Hkv,d,r]; codes [B,H,cap,words] holding
+    r-bit code rows (r in 32, 64, 128, 256; see `new_codes`)."""
     _need(x, torch.bfloat16, "x")
     _need(W_H, torch.float32, "W_H")
-    _need(codes, torch.int64, "codes")
     if pos is not None:
         _need(pos, torch.int32, "pos")
     B, H, x_rows, d = x.shape
     Hkv, _, r = W_H.shape
+    _need_codes(codes, r, "codes")
     cap = codes.shape[2]
     _check(load().hata_encode_append(_ptr(x), x_rows, B, H, int(n_new), _ptr(W_H), Hkv, d, r,
                                      _ptr(codes), cap, _ptr(pos), _stream(stream)))
@@ -140,15 +168,17 @@ def encode_append(x: torch.Tensor, W_H: torch.Tensor, codes: torch.Tensor, n_new
 
 def hamming_scores(q_codes: torch.Tensor, k_codes: torch.Tensor, seq_lens: torch.Tensor,
                    max_len: int, scores: torch.Tensor, stream=None, r: int | None = None) -> None:
-    """q_codes int64 [B,Hq,ceil(r/64)]; k_codes int64 [B,Hkv,cap,ceil(r/64)]; scores int16
-    [B,Hkv,cap].  r defaults to 64 bits per code word."""
-    _need(q_codes, torch.int64, "q_codes")
-    _need(k_codes, torch.int64, "k_codes")
+    """q_codes [B,Hq,words]; k_codes [B,Hkv,cap,words] (r-bit code rows, see
+    `new_codes`); scores int16 [B,Hkv,cap].  r defaults to the width the
+    code tensors hold."""
+    r = int(r or code_bits(q_codes))
+    _need_codes(q_codes, r, "q_codes")
+    _need_codes(k_codes, r, "k_codes")
     _need(scores, torch.int16, "scores")
     _need(seq_lens, torch.int32, "seq_lens")
-    B, Hq, words = q_codes.shape
+    B, Hq, _ = q_codes.shape
     _, Hkv, cap, _ = k_codes.shape
-    _check(load().hata_hamming_scores(_ptr(q_codes), _ptr(k_codes), B, Hq, Hkv, int(r or words * 64), cap,
+    _check(load().hata_hamming_scores(_ptr(q_codes), _ptr(k_codes), B, Hq, Hkv, r, cap,
                                       _ptr(seq_lens), int(max_len), _ptr(scores), _stream(stream)))
 
 
@@ -210,11 +240,12 @@ def prefill(q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, W_H: torch.Tensor
             seq_lens: torch.Tensor, max_len: int, scale: float, out: torch.Tensor, stream=None) -> None:
     """Causal prompt attention with the prompt keys' codes written to the cache.
     q bf16 [B,Hq,q_rows,d]; K,V bf16 [B,Hkv,cap,d]; W_H f32 [Hkv,d,r]; codes int64
-    [B,Hkv,cap,ceil(r/64)]; seq_lens int32 [B]; out f32 [B,Hq,q_rows,d]."""
+    [B,Hkv,cap,words] (r-bit code rows, see `new_codes`); seq_lens int32 [B]; out f32
+    [B,Hq,q_rows,d]."""
     for t, n in ((q, "q"), (K, "K"), (V, "V")):
         _need(t, torch.bfloat16, n)
     _need(W_H, torch.float32, "W_H")
-    _need(codes, torch.int64, "codes")
+    _need_codes(codes, W_H.shape[2], "codes")
     _need(seq_lens, torch.int32, "seq_lens")
     _need(out, torch.float32, "out")
     B, Hq, q_rows, d = q.shape
@@ -228,12 +259,12 @@ def decode_step_paged(q: torch.Tensor, K_pool: torch.Tensor, V_pool: torch.Tenso
                       code_pool: torch.Tensor, block_table: torch.Tensor, seq_lens: torch.Tensor, max_len: int,
                       k: int, scale: float, out: torch.Tensor, ws: torch.Tensor, idx_out: torch.Tensor | None = None,
                       stream=None) -> None:
-    """q bf16 [B,Hq,d]; K_pool, V_pool bf16 [pages,Hkv,P,d]; code_pool int64 [pages,Hkv,P,ceil(r/64)];
+    """q bf16 [B,Hq,d]; K_pool, V_pool bf16 [pages,Hkv,P,d]; code_pool [pages,Hkv,P,words] (code rows, see `new_codes`);
     block_table int32 [B,max_pages]; out f32 [B,Hq,d]; idx_out int32 [B,Hkv,k] or None."""
     for t, n in ((q, "q"), (K_pool, "K_pool"), (V_pool, "V_pool")):
         _need(t, torch.bfloat16, n)
     _need(W_H, torch.float32, "W_H")
-    _need(code_pool, torch.int64, "code_pool")
+    _need_codes(code_pool, W_H.shape[2], "code_pool")
     _need(block_table, torch.int32, "block_table")
     _need(seq_lens, torch.int32, "seq_lens")
     _need(out, torch.float32, "out")
@@ -252,11 +283,11 @@ def prefill_paged(q: torch.Tensor, K_pool: torch.Tensor, V_pool: torch.Tensor, W
                   code_pool: torch.Tensor, block_table: torch.Tensor, seq_lens: torch.Tensor, max_len: int,
                   scale: float, out: torch.Tensor, stream=None) -> None:
     """hata_prefill into page pools: q bf16 [B,Hq,q_rows,d]; K_pool, V_pool bf16 [pages,Hkv,P,d];
-    code_pool int64 [pages,Hkv,P,ceil(r/64)]; block_table int32 [B,max_pages]; out f32 [B,Hq,q_rows,d]."""
+    code_pool [pages,Hkv,P,words] (code rows, see `new_codes`); block_table int32 [B,max_pages]; out f32 [B,Hq,q_rows,d]."""
     for t, n in ((q, "q"), (K_pool, "K_pool"), (V_pool, "V_pool")):
         _need(t, torch.bfloat16, n)
     _need(W_H, torch.float32, "W_H")
-    _need(code_pool, torch.int64, "code_pool")
+    _need_codes(code_pool, W_H.shape[2], "code_pool")
     _need(block_table, torch.int32, "block_table")
     _need(seq_lens, torch.int32, "seq_lens")
     _need(out, torch.float32, "out")
@@ -283,7 +314,7 @@ def decode_step(q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, W_H: torch.Te
     for t, n in ((q, "q"), (K, "K"), (V, "V")):
         _need(t, torch.bfloat16, n)
     _need(W_H, torch.float32, "W_H")
-    _need(codes, torch.int64, "codes")
+    _need_codes(codes, W_H.shape[2], "codes")
     _need(out, torch.float32, "out")
     _need(seq_lens, torch.int32, "seq_lens")
     if idx_out is not None:
@@ -304,7 +335,7 @@ def decode_step_noalloc(q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, W_H: 
     for t, n in ((q, "q"), (K, "K"), (V, "V")):
         _need(t, torch.bfloat16, n)
     _need(W_H, torch.float32, "W_H")
-    _need(codes, torch.int64, "codes")
+    _need_codes(codes, W_H.shape[2], "codes")
     _need(out, torch.float32, "out")
     _need(seq_lens, torch.int32, "seq_lens")
     if idx_out is not None:
@@ -327,7 +358,7 @@ def decode_step_qk(q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, W_Hq: torc
         _need(t, torch.bfloat16, n)
     _need(W_Hq, torch.float32, "W_Hq")
     _need(W_Hk, torch.float32, "W_Hk")
-    _need(codes, torch.int64, "codes")
+    _need_codes(codes, W_Hq.shape[2], "codes")
     _need(out, torch.float32, "out")
     _need(seq_lens, torch.int32, "seq_lens")
     if idx_out is not None:

@@ -120,7 +120,7 @@ const char* hata_last_error_message(void) { return g_msg; }
 int hata_version(void) { return 100; }
 
 int hata_encode_append(const void* x, int64_t x_rows, int B, int H, int n_new, const float* W_H,
-                       int Hkv, int d, int r, uint64_t* codes, int64_t cap, const int32_t* pos,
+                       int Hkv, int d, int r, uint32_t* codes, int64_t cap, const int32_t* pos,
                        void* stream) {
   if (!x || !W_H || !codes) return fail(HATA_ERR_NULL, "encode_append: x, W_H and codes are required");
   int st = check_dims(d, r);
@@ -148,7 +148,7 @@ int hata_encode_append(const void* x, int64_t x_rows, int B, int H, int n_new, c
   return check_launch(e, "encode_append launch");
 }
 
-int hata_hamming_scores(const uint64_t* q_codes, const uint64_t* k_codes, int B, int Hq, int Hkv,
+int hata_hamming_scores(const uint32_t* q_codes, const uint32_t* k_codes, int B, int Hq, int Hkv,
                         int r, int64_t cap, const int32_t* seq_lens, int64_t max_len,
                         uint16_t* scores, void* stream) {
   if (!q_codes || !k_codes || !seq_lens || !scores) return fail(HATA_ERR_NULL, "hamming_scores: null pointer");
@@ -245,7 +245,7 @@ int hata_stream_read(const void* src, size_t bytes, uint64_t* sink, size_t sink_
 
 // noalloc: ws is ignored and the library's static scratch serves instead
 static int decode_step_impl(const void* q, const void* K, const void* V, const float* W_H,
-                            const float* W_Hk, uint64_t* codes, int B, int Hq, int Hkv, int d, int r,
+                            const float* W_Hk, uint32_t* codes, int B, int Hq, int Hkv, int d, int r,
                             int64_t cap, const int32_t* seq_lens, int64_t max_len, int k, float scale,
                             float* out, int32_t* idx_out, void* ws, size_t ws_bytes, void* stream,
                             bool noalloc = false) {
@@ -294,7 +294,7 @@ static int decode_step_impl(const void* q, const void* K, const void* V, const f
   }
   // Staged steps: the per-unit scores do not fit on chip at this shape.
   const int G = Hq / Hkv;
-  auto* qc = reinterpret_cast<uint64_t*>(wsb + p.off_qc);
+  auto* qc = reinterpret_cast<uint32_t*>(wsb + p.off_qc);
   auto* sc = reinterpret_cast<uint16_t*>(wsb + p.off_scores);
   auto* part = reinterpret_cast<float*>(wsb + p.off_attn);
   // the kept list goes to idx_out, or to the workspace when it is NULL
@@ -324,7 +324,7 @@ PagedPlan plan_paged(int B, int Hq, int Hkv, int64_t max_len, int k, int r) {
   PagedPlan p;
   const size_t U = (size_t)B * Hkv;
   size_t off = 0;
-  p.qc = off;   off = al(off + (size_t)B * Hq * ((r + 63) / 64) * 8);
+  p.qc = off;   off = al(off + (size_t)B * Hq * ((r + 31) / 32) * 4);
   p.sc = off;   off = al(off + U * (size_t)max_len * 2);
   p.idx = off;  off = al(off + U * (size_t)k * 4);
   p.attn = off; off = al(off + hata::attn_part_floats(B, Hkv, Hq / Hkv, k) * 4);
@@ -335,7 +335,7 @@ PagedPlan plan_paged(int B, int Hq, int Hkv, int64_t max_len, int k, int r) {
 }  // namespace
 
 int hata_decode_step_paged(const void* q, const void* K_pool, const void* V_pool, const float* W_H,
-                           uint64_t* code_pool, const int32_t* block_table, int max_pages, int num_pages,
+                           uint32_t* code_pool, const int32_t* block_table, int max_pages, int num_pages,
                            int page_rows, int B, int Hq, int Hkv, int d, int r, const int32_t* seq_lens,
                            int64_t max_len, int k, float scale, float* out, int32_t* idx_out, void* ws,
                            size_t ws_bytes, void* stream) {
@@ -384,7 +384,7 @@ int hata_decode_step_paged(const void* q, const void* K_pool, const void* V_pool
   const auto* Kb = static_cast<const uint16_t*>(K_pool);
   const auto* Vb = static_cast<const uint16_t*>(V_pool);
   const int G = Hq / Hkv;
-  auto* qc = reinterpret_cast<uint64_t*>(wsb + p.qc);
+  auto* qc = reinterpret_cast<uint32_t*>(wsb + p.qc);
   auto* sc = reinterpret_cast<uint16_t*>(wsb + p.sc);
   int32_t* idx = idx_out ? idx_out : reinterpret_cast<int32_t*>(wsb + p.idx);
   auto* part = reinterpret_cast<float*>(wsb + p.attn);
@@ -405,7 +405,7 @@ int hata_decode_step_paged(const void* q, const void* K_pool, const void* V_pool
   return check_launch(e, "decode_step_paged launch");
 }
 
-int hata_decode_step(const void* q, const void* K, const void* V, const float* W_H, uint64_t* codes,
+int hata_decode_step(const void* q, const void* K, const void* V, const float* W_H, uint32_t* codes,
                      int B, int Hq, int Hkv, int d, int r, int64_t cap, const int32_t* seq_lens,
                      int64_t max_len, int k, float scale, float* out, int32_t* idx_out, void* ws,
                      size_t ws_bytes, void* stream) {
@@ -413,7 +413,7 @@ int hata_decode_step(const void* q, const void* K, const void* V, const float* W
                           out, idx_out, ws, ws_bytes, stream);
 }
 
-int hata_decode_step_noalloc(const void* q, const void* K, const void* V, const float* W_H, uint64_t* codes,
+int hata_decode_step_noalloc(const void* q, const void* K, const void* V, const float* W_H, uint32_t* codes,
                              int B, int Hq, int Hkv, int d, int r, int64_t cap, const int32_t* seq_lens,
                              int64_t max_len, int k, float scale, float* out, int32_t* idx_out, void* stream) {
   return decode_step_impl(q, K, V, W_H, W_H, codes, B, Hq, Hkv, d, r, cap, seq_lens, max_len, k, scale,
@@ -421,7 +421,7 @@ int hata_decode_step_noalloc(const void* q, const void* K, const void* V, const 
 }
 
 int hata_decode_step_qk(const void* q, const void* K, const void* V, const float* W_Hq,
-                        const float* W_Hk, uint64_t* codes, int B, int Hq, int Hkv, int d, int r,
+                        const float* W_Hk, uint32_t* codes, int B, int Hq, int Hkv, int d, int r,
                         int64_t cap, const int32_t* seq_lens, int64_t max_len, int k, float scale,
                         float* out, int32_t* idx_out, void* ws, size_t ws_bytes, void* stream) {
   return decode_step_impl(q, K, V, W_Hq, W_Hk, codes, B, Hq, Hkv, d, r, cap, seq_lens, max_len, k, scale,
@@ -447,7 +447,7 @@ int hata_hash_labels(const void* q, const void* k, const int32_t* q_pos, int J, 
   return check_launch(e, "hash_labels launch");
 }
 
-int hata_prefill(const void* q, const void* K, const void* V, const float* W_H, uint64_t* codes, int B, int Hq,
+int hata_prefill(const void* q, const void* K, const void* V, const float* W_H, uint32_t* codes, int B, int Hq,
                  int Hkv, int d, int r, int64_t q_rows, int64_t cap, const int32_t* seq_lens, int64_t max_len,
                  float scale, float* out, void* stream) {
   if (!q || !K || !V || !W_H || !codes || !seq_lens || !out)
@@ -477,7 +477,7 @@ int hata_prefill(const void* q, const void* K, const void* V, const float* W_H, 
 }
 
 int hata_prefill_paged(const void* q, const void* K_pool, const void* V_pool, const float* W_H,
-                       uint64_t* code_pool, const int32_t* block_table, int max_pages, int num_pages, int page_rows,
+                       uint32_t* code_pool, const int32_t* block_table, int max_pages, int num_pages, int page_rows,
                        int B, int Hq, int Hkv, int d, int r, int64_t q_rows, const int32_t* seq_lens,
                        int64_t max_len, float scale, float* out, void* stream) {
   if (!q || !K_pool || !V_pool || !W_H || !code_pool || !block_table || !seq_lens || !out)

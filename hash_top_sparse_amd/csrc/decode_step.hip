@@ -170,7 +170,7 @@ struct StepArgs {
   const uint16_t* V;
   const float* W;
   const float* Wk;  // key encoder (== W unless a separate one is given)
-  uint64_t* codes;
+  uint32_t* codes;  // rows of W32 32-bit words
   const int32_t* seq_lens;
   float* out;
   int32_t* idx_out;
@@ -390,7 +390,7 @@ __global__ __launch_bounds__(kNT, (step_occupancy<G, R>())) void decode_step_ker
   const int lo = w * a.chunk;
   // the code ring's first PF*256 rows of the chunk, clamped into the cache
   // (rows past the sequence end are loaded and never scored)
-  const uint64_t* cunit = a.codes + row0 * W64;
+  const uint32_t* cunit = a.codes + row0 * W32;
   CodeRow<R> cbuf[PF];
   if constexpr (PAGED) {
     // pages of >= 256 rows: a 256-row batch lies in one page (lo is a
@@ -459,7 +459,7 @@ __global__ __launch_bounds__(kNT, (step_occupancy<G, R>())) void decode_step_ker
   const int64_t krow_at = PAGED ? prow(owns_new ? n - 1 : 0) : row0 + (owns_new ? n - 1 : 0);
   const uint32_t krow = reinterpret_cast<const uint32_t*>(a.K + krow_at * kD)[lane];
   // ring refills: rows lo + li for li < cnt
-  const uint64_t* cbase = cunit + (int64_t)(cnt > 0 ? lo : 0) * W64;
+  const uint32_t* cbase = cunit + (int64_t)(cnt > 0 ? lo : 0) * W32;
 
   // ---- 2. encode the query rows.  Every staging slot is stored (slots past
   // the G query rows are zero), so no load is consumed under a branch.
@@ -571,7 +571,7 @@ __global__ __launch_bounds__(kNT, (step_occupancy<G, R>())) void decode_step_ker
     }
     __syncthreads();
     project_pack<1, R>(wr, qf + G * kD, red, qcode + G * W64, 1);
-    if (t < W64) a.codes[(PAGED ? prow(n - 1) : row0 + n - 1) * W64 + t] = qcode[G * W64 + t];
+    if (t < W32) a.codes[(PAGED ? prow(n - 1) : row0 + n - 1) * W32 + t] = code_word32(qcode + G * W64, t);
     if (t == new_li % kNT) {
       uint32_t cw[W32];
 #pragma unroll
@@ -1103,7 +1103,7 @@ StepPlan plan_decode_step(int B, int Hq, int Hkv, int64_t max_len, int k, int nu
     }
   } else {
     // staged steps inside hata_decode_step
-    p.off_qc = off;     off = align(off + (size_t)B * Hq * ((r + 63) / 64) * 8);
+    p.off_qc = off;     off = align(off + (size_t)B * Hq * ((r + 31) / 32) * 4);
     p.off_scores = off; off = align(off + (size_t)U * max_len * 2);
     p.off_idx = off;    off = align(off + (size_t)U * k * 4);  // kept list when idx_out is NULL
     p.off_attn = off;   off = align(off + attn_part_floats(B, Hkv, G, k) * 4);
@@ -1150,7 +1150,7 @@ static hipError_t launch_step_g(const StepPlan& p, const StepArgs& a, hipStream_
 }
 
 hipError_t launch_decode_step(const StepPlan& p, const uint16_t* q, const uint16_t* K,
-                              const uint16_t* V, const float* W, const float* Wk, uint64_t* codes, int B, int Hq,
+                              const uint16_t* V, const float* W, const float* Wk, uint32_t* codes, int B, int Hq,
                               int Hkv, int64_t cap, const int32_t* seq_lens, int k, float scale,
                               float* out, int32_t* idx_out, unsigned char* ws, hipStream_t s) {
   StepArgs a;
@@ -1193,7 +1193,7 @@ bool decode_step_paged_fusable(const StepPlan& p, int page_rows) {
 }
 
 hipError_t launch_decode_step_paged(const StepPlan& p, const uint16_t* q, const uint16_t* K, const uint16_t* V,
-                                    const float* W, uint64_t* codes, const PageMap& pm, int Hq, int Hkv,
+                                    const float* W, uint32_t* codes, const PageMap& pm, int Hq, int Hkv,
                                     const int32_t* seq_lens, int k, float scale, float* out, int32_t* idx_out,
                                     unsigned char* ws, hipStream_t s) {
   if (!decode_step_paged_fusable(p, 1 << pm.log2P)) return hipErrorInvalidValue;

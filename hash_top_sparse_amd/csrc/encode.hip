@@ -24,9 +24,9 @@ constexpr int kRowsPerBatch = 4;
 template <int R, bool PAGED>
 __global__ __launch_bounds__(kNT) void encode_rows_kernel(
     const uint16_t* __restrict__ x, int64_t x_rows, int H, int Hkv, int n_new,
-    const float* __restrict__ W, uint64_t* __restrict__ codes, int64_t cap,
+    const float* __restrict__ W, uint32_t* __restrict__ codes, int64_t cap,
     const int32_t* __restrict__ pos, int pos_off, int rows_per_block, PageMap pm) {
-  constexpr int W64 = Width<R>::W64;
+  constexpr int W64 = Width<R>::W64, W32 = Width<R>::W32;
   __shared__ __align__(16) float xs[kRowsPerBatch * kD];
   __shared__ __align__(16) float red[4 * kRowsPerBatch * R];
   __shared__ uint64_t cw[kRowsPerBatch * W64];
@@ -69,14 +69,16 @@ __global__ __launch_bounds__(kNT) void encode_rows_kernel(
     __syncthreads();
     const int nr = min(kRowsPerBatch, r_end - r0);
     project_pack<kRowsPerBatch, R>(wr, xs, red, cw, nr);
-    if (t < nr * W64) {
-      const int r = r0 + t / W64;
+    // 32-bit word t % W32 of row t / W32
+    if (t < nr * W32) {
+      const int rr = t / W32, wd = t - rr * W32;
+      const int r = r0 + rr;
       const int g = r / n_new, j = r - g * n_new;
       const int64_t ridx = p_b + j;
       if (ridx >= 0 && ridx < lim) {
         const int64_t head = (int64_t)b * H + (int64_t)hk * G + g;
         const int64_t cr = PAGED ? pm.row(b, hk, Hkv, ridx) : head * cap + ridx;
-        codes[cr * W64 + t % W64] = cw[t];
+        codes[cr * W32 + wd] = code_word32(cw + rr * W64, wd);
       }
     }
   }
@@ -84,7 +86,7 @@ __global__ __launch_bounds__(kNT) void encode_rows_kernel(
 
 template <int R>
 void launch_encode_r(dim3 grid, const uint16_t* x, int64_t x_rows, int H, int Hkv, int n_new, const float* W,
-                     uint64_t* codes, int64_t cap, const int32_t* pos, int pos_off, int rpb, const PageMap* pm,
+                     uint32_t* codes, int64_t cap, const int32_t* pos, int pos_off, int rpb, const PageMap* pm,
                      hipStream_t s) {
   if (pm && pm->bt)
     hipLaunchKernelGGL((encode_rows_kernel<R, true>), grid, dim3(kNT), 0, s, x, x_rows, H, Hkv, n_new, W, codes,
@@ -97,7 +99,7 @@ void launch_encode_r(dim3 grid, const uint16_t* x, int64_t x_rows, int H, int Hk
 }  // namespace
 
 hipError_t launch_encode_rows(const uint16_t* x, int64_t x_rows, int B, int H, int Hkv, int n_new,
-                              const float* W, uint64_t* codes, int64_t cap, const int32_t* pos,
+                              const float* W, uint32_t* codes, int64_t cap, const int32_t* pos,
                               int pos_off, hipStream_t s, int r, const PageMap* pm) {
   if (pm && pm->bt && H != Hkv) return hipErrorInvalidValue;
   const int G = H / Hkv;

@@ -46,7 +46,7 @@ constexpr int kMaxTilesPerWg = 16; // code words of every tile of a workgroup st
 template <int TILES>
 __global__ __launch_bounds__(kNT, 2) void encode_bulk_kernel(
     const uint16_t* __restrict__ x, int64_t x_rows, int H, int Hkv, int n_new,
-    const float* __restrict__ W, uint64_t* __restrict__ codes, int64_t cap,
+    const float* __restrict__ W, uint32_t* __restrict__ codes, int64_t cap,
     const int32_t* __restrict__ pos, int pos_off) {
   static_assert(TILES % 2 == 0 && TILES <= kMaxTilesPerWg, "tiles per workgroup");
   constexpr int tiles_per_wg = TILES;
@@ -88,7 +88,7 @@ __global__ __launch_bounds__(kNT, 2) void encode_bulk_kernel(
   const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint16_t*>(x + (head * x_rows + r_lo) * kD), 0, (int)((r_hi - r_lo) * kD * 2), 0x00020000);
   const __amdgpu_buffer_rsrc_t cr = __builtin_amdgcn_make_buffer_rsrc(
-      codes + (head * cap + r_lo) * 2, 0, (int)((r_hi - r_lo) * 16), 0x00020000);
+      codes + (head * cap + r_lo) * 4, 0, (int)((r_hi - r_lo) * 16), 0x00020000);
 
   // row tile loader: 128 rows x 16 chunks of 16 bytes, 8 chunks per thread
   // (rows before r_lo give negative offsets, i.e. out of range as well)
@@ -192,7 +192,7 @@ __global__ __launch_bounds__(kNT, 2) void encode_bulk_kernel(
 }  // namespace
 
 hipError_t launch_encode_bulk(const uint16_t* x, int64_t x_rows, int B, int H, int Hkv, int n_new,
-                              const float* W, uint64_t* codes, int64_t cap, const int32_t* pos,
+                              const float* W, uint32_t* codes, int64_t cap, const int32_t* pos,
                               int pos_off, hipStream_t s) {
   // the kernel's buffer resources span at most kMaxRows rows (1 GiB of keys);
   // longer runs are encoded in pieces

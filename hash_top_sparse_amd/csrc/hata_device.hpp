@@ -11,13 +11,15 @@ constexpr int kR = 128;      // default code bits
 constexpr int kWords32 = 4;  // 32-bit words per default code
 constexpr int kNT = 256;     // threads per workgroup of the decode kernels
 
-// Code widths: R bits stored in ceil(R/64) 64-bit words per code row, the
-// bits past R zero (R = 32 keeps one 64-bit word).
+// Code widths: a code row of R bits is stored as R/32 32-bit words, bit c in
+// bit c % 32 of word c / 32 (4 bytes at R = 32; for R >= 64 the same bytes as
+// R/64 little-endian 64-bit words).  W64 is the 64-bit word count of the
+// LDS layout the projection writes.
 template <int R>
 struct Width {
   static_assert(R == 32 || R == 64 || R == 128 || R == 256, "code width");
-  static constexpr int W64 = (R + 63) / 64;  // storage words per code row
-  static constexpr int W32 = (R + 31) / 32;  // 32-bit words that hold code bits
+  static constexpr int W64 = (R + 63) / 64;  // 64-bit words per row in LDS (bits past R zero)
+  static constexpr int W32 = (R + 31) / 32;  // 32-bit words per stored code row
   static constexpr int CPT = R / 32;         // projection columns per thread
 };
 
@@ -45,6 +47,7 @@ __device__ __forceinline__ uint2 load_stream8(const uint2* p) {
   const u32x2 v = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
   return make_uint2(v.x, v.y);
 }
+__device__ __forceinline__ uint32_t load_stream4(const uint32_t* p) { return __builtin_nontemporal_load(p); }
 
 // Agent-coherent accesses for data that workgroups of one launch exchange.
 // They compile to global_load/global_store with the device-scope cache bit
@@ -380,33 +383,39 @@ __device__ __forceinline__ uint32_t gqa_hamming(const uint4 c, const QMasks<G>& 
   return gqa_hamming_w<G, kR>(cw, m);
 }
 
-// One code row of R bits as loaded by the scans: 8 bytes (R <= 64), 16 or 32.
+// One code row of R bits as loaded by the scans: 4, 8, 16 or 32 bytes.
 template <int R>
 struct CodeRow {
-  uint4 v[(Width<R>::W64 + 1) / 2];
+  uint4 v[(Width<R>::W32 + 3) / 4];
 };
-// streaming load of code row `row` (R/8 bytes rounded up to 8) from codes
+// streaming load of code row `row` (R/8 bytes) from codes
 template <int R>
-__device__ __forceinline__ CodeRow<R> load_code(const uint64_t* codes, int64_t row) {
+__device__ __forceinline__ CodeRow<R> load_code(const uint32_t* codes, int64_t row) {
   CodeRow<R> c;
-  if constexpr (Width<R>::W64 == 1) {
-    const uint2 v = load_stream8(reinterpret_cast<const uint2*>(codes + row));
+  if constexpr (Width<R>::W32 == 1) {
+    c.v[0] = make_uint4(load_stream4(codes + row), 0u, 0u, 0u);
+  } else if constexpr (Width<R>::W32 == 2) {
+    const uint2 v = load_stream8(reinterpret_cast<const uint2*>(codes + row * 2));
     c.v[0] = make_uint4(v.x, v.y, 0u, 0u);
   } else {
 #pragma unroll
-    for (int i = 0; i < Width<R>::W64 / 2; ++i)
-      c.v[i] = load_stream16(reinterpret_cast<const uint4*>(codes + row * Width<R>::W64) + i);
+    for (int i = 0; i < Width<R>::W32 / 4; ++i)
+      c.v[i] = load_stream16(reinterpret_cast<const uint4*>(codes + row * Width<R>::W32) + i);
   }
   return c;
 }
+// 32-bit word wd of a code row held as 64-bit words (the projection's layout)
+__device__ __forceinline__ uint32_t code_word32(const uint64_t* row64, int wd) {
+  return (uint32_t)(row64[wd >> 1] >> ((wd & 1) * 32));
+}
 template <int R>
 __device__ __forceinline__ void code_words(const CodeRow<R>& c, uint32_t (&cw)[Width<R>::W32]) {
-  if constexpr (Width<R>::W64 == 1) {
+  if constexpr (Width<R>::W32 <= 2) {
     cw[0] = c.v[0].x;
     if constexpr (Width<R>::W32 == 2) cw[1] = c.v[0].y;
   } else {
 #pragma unroll
-    for (int i = 0; i < Width<R>::W64 / 2; ++i) {
+    for (int i = 0; i < Width<R>::W32 / 4; ++i) {
       cw[4 * i] = c.v[i].x; cw[4 * i + 1] = c.v[i].y; cw[4 * i + 2] = c.v[i].z; cw[4 * i + 3] = c.v[i].w;
     }
   }

@@ -30,17 +30,17 @@ struct PageMap {
 // x bf16 [B][H][x_rows][128]; rows p_b + j (j < n_new) -> codes [B][H][cap][2].
 // Row index of (b, j) is (pos ? pos[b] : 0) + pos_off + j.
 hipError_t launch_encode_rows(const uint16_t* x, int64_t x_rows, int B, int H, int Hkv, int n_new,
-                              const float* W, uint64_t* codes, int64_t cap, const int32_t* pos,
+                              const float* W, uint32_t* codes, int64_t cap, const int32_t* pos,
                               int pos_off, hipStream_t s, int r = 128, const PageMap* pm = nullptr);
 // Same contract, matrix-core path for long row runs (prefill).
 hipError_t launch_encode_bulk(const uint16_t* x, int64_t x_rows, int B, int H, int Hkv, int n_new,
-                              const float* W, uint64_t* codes, int64_t cap, const int32_t* pos,
+                              const float* W, uint32_t* codes, int64_t cap, const int32_t* pos,
                               int pos_off, hipStream_t s);
 // Row-run length from which hata_encode_append uses the matrix-core path.
 constexpr int kBulkMinRows = 512;
 
 // ---------------------------------------------------------------- score / select
-hipError_t launch_hamming(const uint64_t* qc, const uint64_t* kc, int B, int Hq, int Hkv,
+hipError_t launch_hamming(const uint32_t* qc, const uint32_t* kc, int B, int Hq, int Hkv,
                           int64_t cap, const int32_t* seq_lens, int64_t max_len, uint16_t* scores,
                           int64_t sstride, hipStream_t s, int r = 128, const PageMap* pm = nullptr,
                           uint32_t* hist = nullptr);
@@ -86,7 +86,7 @@ StepPlan plan_decode_step(int B, int Hq, int Hkv, int64_t max_len, int k, int nu
 constexpr size_t kNoAllocScratchBytes = (size_t)16 << 20;
 hipError_t noalloc_scratch(unsigned char** out);
 hipError_t launch_decode_step(const StepPlan& p, const uint16_t* q, const uint16_t* K,
-                              const uint16_t* V, const float* W, const float* Wk, uint64_t* codes, int B, int Hq,
+                              const uint16_t* V, const float* W, const float* Wk, uint32_t* codes, int B, int Hq,
                               int Hkv, int64_t cap, const int32_t* seq_lens, int k, float scale,
                               float* out, int32_t* idx_out, unsigned char* ws, hipStream_t s);
 
@@ -95,7 +95,7 @@ hipError_t launch_decode_step(const StepPlan& p, const uint16_t* q, const uint16
 // while the page-id list still fits in LDS beside the step's own.
 bool decode_step_paged_fusable(const StepPlan& p, int page_rows);
 hipError_t launch_decode_step_paged(const StepPlan& p, const uint16_t* q, const uint16_t* K, const uint16_t* V,
-                                    const float* W, uint64_t* codes, const PageMap& pm, int Hq, int Hkv,
+                                    const float* W, uint32_t* codes, const PageMap& pm, int Hq, int Hkv,
                                     const int32_t* seq_lens, int k, float scale, float* out, int32_t* idx_out,
                                     unsigned char* ws, hipStream_t s);
 
@@ -106,12 +106,12 @@ hipError_t launch_set_word(uint32_t* p, uint32_t v, hipStream_t s);
 // Causal attention over each sequence's prompt (queries [B][Hq][q_rows][128]
 // at positions 0..n_b-1, keys/values [B][Hkv][cap][128]) into out fp32
 // [B][Hq][q_rows][128], with code rows 0..n_b-1 written to codes
-// [B][Hkv][cap][r/64 rounded up]; n_b = min(seq_lens[b], max_len).
+// [B][Hkv][cap][r/32] 32-bit words; n_b = min(seq_lens[b], max_len).
 // G = Hq / Hkv in {1, 2, 4, 8}, r in {32, 64, 128, 256}.  pm (optional): K, V
 // and codes are page pools addressed through it (cap = max_pages * P).
 int prefill_positions_per_block(int G);
 hipError_t launch_prefill(const uint16_t* q, const uint16_t* K, const uint16_t* V, const float* W,
-                          uint64_t* codes, int B, int Hq, int Hkv, int64_t q_rows, int64_t cap,
+                          uint32_t* codes, int B, int Hq, int Hkv, int64_t q_rows, int64_t cap,
                           const int32_t* seq_lens, int max_len, float scale, float* out, int r,
                           hipStream_t s, const PageMap* pm = nullptr);
 

@@ -61,7 +61,7 @@ struct PrefillArgs {
   const uint16_t* K;
   const uint16_t* V;
   const float* W;
-  uint64_t* codes;
+  uint32_t* codes;  // rows of R/32 32-bit words
   const int32_t* seq_lens;
   float* out;
   int B, Hq, Hkv;
@@ -76,7 +76,6 @@ struct PrefillArgs {
 template <int G, int R, bool PAGED>
 __global__ __launch_bounds__(kNT, 2) void prefill_kernel(PrefillArgs a) {
   constexpr int QP = 128 / G;         // positions per workgroup
-  constexpr int W64 = Width<R>::W64;  // 64-bit words per code row
   constexpr int CT = R / 32;          // 32-column slices of the code
   // two K/V tile buffers (the next tile is stored while the current one is
   // multiplied: one barrier per tile), then the code words
@@ -413,16 +412,14 @@ __global__ __launch_bounds__(kNT, 2) void prefill_kernel(PrefillArgs a) {
   }
   __syncthreads();
 
-  // code rows [p0, pend)
-  uint64_t* crow = a.codes + (((int64_t)b * a.Hkv + hk) * a.cap + p0) * W64;
-  for (int e = t; e < (pend - p0) * W64; e += kNT) {
-    const int row = e / W64, w = e - row * W64;
-    const uint64_t lo = cw[row * CT + 2 * w];
-    const uint64_t hi = (2 * w + 1 < CT) ? cw[row * CT + 2 * w + 1] : 0u;
+  // code rows [p0, pend): CT = R/32 words each
+  uint32_t* crow = a.codes + (((int64_t)b * a.Hkv + hk) * a.cap + p0) * CT;
+  for (int e = t; e < (pend - p0) * CT; e += kNT) {
+    const int row = e / CT, w = e - row * CT;
     if constexpr (PAGED)
-      a.codes[a.pm.row(b, hk, a.Hkv, p0 + row) * W64 + w] = lo | (hi << 32);
+      a.codes[a.pm.row(b, hk, a.Hkv, p0 + row) * CT + w] = cw[e];
     else
-      crow[e] = lo | (hi << 32);
+      crow[e] = cw[e];
   }
 }
 
@@ -468,7 +465,7 @@ hipError_t launch_p(const PrefillArgs& a, int G, int r, hipStream_t s) {
 int prefill_positions_per_block(int G) { return 128 / G; }
 
 hipError_t launch_prefill(const uint16_t* q, const uint16_t* K, const uint16_t* V, const float* W,
-                          uint64_t* codes, int B, int Hq, int Hkv, int64_t q_rows, int64_t cap,
+                          uint32_t* codes, int B, int Hq, int Hkv, int64_t q_rows, int64_t cap,
                           const int32_t* seq_lens, int max_len, float scale, float* out, int r,
                           hipStream_t s, const PageMap* pm) {
   const int G = Hq / Hkv;

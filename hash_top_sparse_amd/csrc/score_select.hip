@@ -19,8 +19,8 @@ constexpr int kHamTPT = 8;  // tokens per thread in the staged Hamming kernel
 // workgroup's score histogram (bins 0..G r) into hist[unit][G r + 1] (for the
 // many-workgroup top-k; hist zeroed beforehand).
 template <int G, int R, bool PAGED, bool HIST>
-__global__ __launch_bounds__(kNT) void hamming_kernel(const uint64_t* __restrict__ qc,
-                                                      const uint64_t* __restrict__ kc, int Hq,
+__global__ __launch_bounds__(kNT) void hamming_kernel(const uint32_t* __restrict__ qc,
+                                                      const uint32_t* __restrict__ kc, int Hq,
                                                       int Hkv, int64_t cap,
                                                       const int32_t* __restrict__ seq_lens,
                                                       uint16_t* __restrict__ scores,
@@ -36,18 +36,18 @@ __global__ __launch_bounds__(kNT) void hamming_kernel(const uint64_t* __restrict
   const int64_t i0 = (int64_t)blockIdx.x * (kNT * kHamTPT);
   if (i0 >= n) return;
 
-  constexpr int W64 = Width<R>::W64, W32 = Width<R>::W32;
+  constexpr int W32 = Width<R>::W32;
   uint32_t qw[G][W32];
 #pragma unroll
   for (int g = 0; g < G; ++g) {
-    const uint64_t* qp = qc + ((int64_t)b * Hq + (int64_t)h * G + g) * W64;
+    const uint32_t* qp = qc + ((int64_t)b * Hq + (int64_t)h * G + g) * W32;
 #pragma unroll
-    for (int w = 0; w < W32; ++w) qw[g][w] = (uint32_t)(qp[w >> 1] >> ((w & 1) * 32));
+    for (int w = 0; w < W32; ++w) qw[g][w] = qp[w];
   }
   QMasks<G, R> m;
   build_qmasks<G, R>(qw, m);
 
-  const uint64_t* src = kc + ((int64_t)b * Hkv + h) * cap * W64;
+  const uint32_t* src = kc + ((int64_t)b * Hkv + h) * cap * W32;
   uint16_t* dst = scores + ((int64_t)b * Hkv + h) * sstride;
   CodeRow<R> c[kHamTPT];
 #pragma unroll
@@ -401,7 +401,7 @@ size_t topk_scratch_bytes(int B, int Hkv, int64_t max_len, int max_score) {
 }
 
 template <int G, int R>
-static void launch_hamming_gr(const uint64_t* qc, const uint64_t* kc, int Hq, int Hkv, int64_t cap,
+static void launch_hamming_gr(const uint32_t* qc, const uint32_t* kc, int Hq, int Hkv, int64_t cap,
                               const int32_t* seq_lens, uint16_t* scores, int64_t sstride, dim3 grid,
                               const PageMap* pm, uint32_t* hist, hipStream_t s) {
   const bool paged = pm && pm->bt;
@@ -421,7 +421,7 @@ static void launch_hamming_gr(const uint64_t* qc, const uint64_t* kc, int Hq, in
 }
 
 template <int R>
-static hipError_t launch_hamming_r(const uint64_t* qc, const uint64_t* kc, int G, int Hq, int Hkv,
+static hipError_t launch_hamming_r(const uint32_t* qc, const uint32_t* kc, int G, int Hq, int Hkv,
                                    int64_t cap, const int32_t* seq_lens, uint16_t* scores, int64_t sstride,
                                    dim3 grid, const PageMap* pm, uint32_t* hist, hipStream_t s) {
   switch (G) {
@@ -434,7 +434,7 @@ static hipError_t launch_hamming_r(const uint64_t* qc, const uint64_t* kc, int G
   return hipGetLastError();
 }
 
-hipError_t launch_hamming(const uint64_t* qc, const uint64_t* kc, int B, int Hq, int Hkv,
+hipError_t launch_hamming(const uint32_t* qc, const uint32_t* kc, int B, int Hq, int Hkv,
                           int64_t cap, const int32_t* seq_lens, int64_t max_len, uint16_t* scores,
                           int64_t sstride, hipStream_t s, int r, const PageMap* pm, uint32_t* hist) {
   const int G = Hq / Hkv;

@@ -19,8 +19,11 @@
  *
  * Conventions fixed here (the notes leave them open):
  *   - bit c of a code is 1 iff the fp32 projection p_c compares >= 0.0f
- *     (so -0.0 gives 1 and NaN gives 0); bit c lives in 64-bit word c/64 at
- *     bit position c%64;
+ *     (so -0.0 gives 1 and NaN gives 0; the matrix-core encode of long row
+ *     runs reads the sign of its fp32 accumulator, the same bit for every
+ *     finite input since that sum never ends at -0.0, unspecified for NaN
+ *     inputs); bit c lives in 32-bit word c/32 at bit position c%32 (for
+ *     r >= 64 equally in 64-bit word c/64 at bit c%64);
  *   - one W_H per KV head, stored [Hkv][d][r] row-major, used for the G query
  *     heads of that KV head and for its keys; query head j uses KV head j/G;
  *   - the kept set is the first min(k, n) tokens in (summed distance, token
@@ -33,7 +36,9 @@
  *   q      bf16   [B][Hq][d]
  *   K, V   bf16   [B][Hkv][cap][d]          (row n_b-1 is the new token)
  *   W_H    fp32   [Hkv][d][r]
- *   codes  uint64 [B][Hkv][cap][r/64]       (16-byte aligned)
+ *   codes  uint32 [B][Hkv][cap][r/32]       (16-byte aligned; bit c of a code
+ *            is bit c % 32 of word c / 32, so for r >= 64 a row is also
+ *            r/64 little-endian 64-bit words)
  *   out    fp32   [B][Hq][d]
  *   idx    int32  [B][Hkv][k]
  *   seq_lens int32 [B] on the device: n_b, the number of valid rows
@@ -42,8 +47,9 @@
  *            captured in a HIP graph); it must satisfy 1 <= max_len <= cap.
  *
  * Supported sizes: d = 128; r in {32, 64, 128, 256} (a code of r bits takes
- * ceil(r/64) 64-bit words; hata_sparse_decode and hata_dense_decode take no
- * code); G = Hq/Hkv in {1, 2, 4, 8}; 1 <= k <= 4096.
+ * r/32 32-bit words, r/8 bytes: 4 at r = 32; hata_sparse_decode and
+ * hata_dense_decode take no code); G = Hq/Hkv in {1, 2, 4, 8};
+ * 1 <= k <= 4096.
  *
  * Ownership and threading: every pointer is a device pointer unless stated;
  * the caller allocates and owns every buffer, the library never allocates,
@@ -106,7 +112,7 @@ int hata_version(void);
  * bit-pack and cache update).
  * x is bf16 [B][H][x_rows][d]; for each (b, h) and j in [0, n_new) the row
  * p_b + j of x is encoded with W_H[h / (H/Hkv)] and written to row p_b + j of
- * codes [B][H][cap][r/64], where p_b = pos ? pos[b] : 0 (pos: device int32[B]).
+ * codes [B][H][cap][r/32], where p_b = pos ? pos[b] : 0 (pos: device int32[B]).
  *   queries:      x = q, H = Hq, x_rows = 1, cap = 1, pos = NULL, n_new = 1
  *   key append:   x = K cache, H = Hkv, x_rows = cap, pos = seq_lens - 1 (device)
  *   prefill bulk: x = K cache, H = Hkv, x_rows = cap, pos = NULL, n_new = n
@@ -116,17 +122,17 @@ int hata_version(void);
  * Requires H % Hkv == 0; codes 16-byte aligned.
  */
 int hata_encode_append(const void* x, int64_t x_rows, int B, int H, int n_new,
-                       const float* W_H, int Hkv, int d, int r, uint64_t* codes,
+                       const float* W_H, int Hkv, int d, int r, uint32_t* codes,
                        int64_t cap, const int32_t* pos, void* stream);
 
 /*
  * Hamming scores with GQA sum (decode-stage steps 3-4):
  * scores[b][h][i] = sum over g in [hG, hG+G) of popcount(q_codes[b][g] XOR
  * k_codes[b][h][i]) for i < n_b; entries i >= n_b are not written.
- * q_codes uint64 [B][Hq][r/64]; k_codes uint64 [B][Hkv][cap][r/64];
+ * q_codes uint32 [B][Hq][r/32]; k_codes uint32 [B][Hkv][cap][r/32];
  * scores uint16 [B][Hkv][cap].  Values lie in [0, G*r].
  */
-int hata_hamming_scores(const uint64_t* q_codes, const uint64_t* k_codes, int B,
+int hata_hamming_scores(const uint32_t* q_codes, const uint32_t* k_codes, int B,
                         int Hq, int Hkv, int r, int64_t cap,
                         const int32_t* seq_lens, int64_t max_len,
                         uint16_t* scores, void* stream);
@@ -190,7 +196,7 @@ int hata_sparse_decode(const void* q, const void* K, const void* V, int B,
  * them, and fails as above only if they do not start within the bound.
  */
 int hata_decode_step(const void* q, const void* K, const void* V,
-                     const float* W_H, uint64_t* codes, int B, int Hq, int Hkv,
+                     const float* W_H, uint32_t* codes, int B, int Hq, int Hkv,
                      int d, int r, int64_t cap, const int32_t* seq_lens,
                      int64_t max_len, int k, float scale, float* out,
                      int32_t* idx_out, void* ws, size_t ws_bytes, void* stream);
@@ -213,7 +219,7 @@ int hata_decode_step(const void* q, const void* K, const void* V,
  * hata_decode_step (the next call clears the flags again).
  */
 int hata_decode_step_noalloc(const void* q, const void* K, const void* V,
-                             const float* W_H, uint64_t* codes, int B, int Hq,
+                             const float* W_H, uint32_t* codes, int B, int Hq,
                              int Hkv, int d, int r, int64_t cap,
                              const int32_t* seq_lens, int64_t max_len, int k,
                              float scale, float* out, int32_t* idx_out,
@@ -230,7 +236,7 @@ int hata_decode_step_noalloc(const void* q, const void* K, const void* V,
  * path only the workgroup that owns the appended row loads W_Hk.
  */
 int hata_decode_step_qk(const void* q, const void* K, const void* V,
-                        const float* W_Hq, const float* W_Hk, uint64_t* codes,
+                        const float* W_Hq, const float* W_Hk, uint32_t* codes,
                         int B, int Hq, int Hkv, int d, int r, int64_t cap,
                         const int32_t* seq_lens, int64_t max_len, int k,
                         float scale, float* out, int32_t* idx_out, void* ws,
@@ -248,7 +254,7 @@ int hata_decode_step_qk(const void* q, const void* K, const void* V,
  * attention has staged, so the prompt keys are read from HBM once.
  * Layouts (device memory): q bf16 [B][Hq][q_rows][d]; K, V bf16
  * [B][Hkv][cap][d] (rows 0..n_b-1 hold the prompt); W_H fp32 [Hkv][d][r];
- * codes uint64 [B][Hkv][cap][ceil(r/64)]; seq_lens int32 [B]; out fp32
+ * codes uint32 [B][Hkv][cap][r/32]; seq_lens int32 [B]; out fp32
  * [B][Hq][q_rows][d].  Rows at positions >= n_b of out and codes are left
  * as they are.  The weights of the value product are rounded to bf16 (as
  * flash attention does); the scores, the softmax statistics and all
@@ -259,7 +265,7 @@ int hata_decode_step_qk(const void* q, const void* K, const void* V,
  * launch failure.
  */
 int hata_prefill(const void* q, const void* K, const void* V,
-                 const float* W_H, uint64_t* codes, int B, int Hq, int Hkv,
+                 const float* W_H, uint32_t* codes, int B, int Hq, int Hkv,
                  int d, int r, int64_t q_rows, int64_t cap,
                  const int32_t* seq_lens, int64_t max_len, float scale,
                  float* out, void* stream);
@@ -269,8 +275,8 @@ int hata_prefill(const void* q, const void* K, const void* V,
  * its code rows written to, pools addressed through a block table, as in
  * hata_decode_step_paged (row j of sequence b lives in page
  * block_table[b * max_pages + j / page_rows]; K_pool, V_pool bf16
- * [num_pages][Hkv][page_rows][d], code_pool uint64
- * [num_pages][Hkv][page_rows][ceil(r/64)]; page ids clamped into
+ * [num_pages][Hkv][page_rows][d], code_pool uint32
+ * [num_pages][Hkv][page_rows][r/32]; page ids clamped into
  * [0, num_pages)).  q and out keep hata_prefill's layouts.  The results are
  * those of hata_prefill on the gathered contiguous cache (bit for bit; the
  * same kernel reads its rows through the table).  page_rows a power of two
@@ -278,7 +284,7 @@ int hata_prefill(const void* q, const void* K, const void* V,
  * as for hata_prefill.  No workspace.
  */
 int hata_prefill_paged(const void* q, const void* K_pool, const void* V_pool,
-                       const float* W_H, uint64_t* code_pool,
+                       const float* W_H, uint32_t* code_pool,
                        const int32_t* block_table, int max_pages,
                        int num_pages, int page_rows, int B, int Hq, int Hkv,
                        int d, int r, int64_t q_rows, const int32_t* seq_lens,
@@ -291,7 +297,7 @@ int hata_prefill_paged(const void* q, const void* K_pool, const void* V_pool,
  * unchanged): row j of sequence b lives in page block_table[b * max_pages +
  * j / page_rows] of three pools that share the table,
  *   K_pool, V_pool bf16 [num_pages][Hkv][page_rows][d]
- *   code_pool uint64    [num_pages][Hkv][page_rows][ceil(r/64)]
+ *   code_pool uint32    [num_pages][Hkv][page_rows][r/32]
  * block_table int32 [B][max_pages] (device); page ids outside
  * [0, num_pages) are clamped into it (reads and writes stay in the pools;
  * the results for such rows are then unspecified).  The logical capacity is
@@ -310,7 +316,7 @@ int hata_prefill_paged(const void* q, const void* K_pool, const void* V_pool,
  */
 int hata_decode_step_paged(const void* q, const void* K_pool,
                            const void* V_pool, const float* W_H,
-                           uint64_t* code_pool, const int32_t* block_table,
+                           uint32_t* code_pool, const int32_t* block_table,
                            int max_pages, int num_pages, int page_rows, int B,
                            int Hq, int Hkv, int d, int r,
                            const int32_t* seq_lens, int64_t max_len, int k,

@@ -28,7 +28,12 @@ def codes_tensor(a: np.ndarray, dev="cuda") -> torch.Tensor:
 
 
 def codes_np(t: torch.Tensor) -> np.ndarray:
-    return t.cpu().numpy().view(np.uint64)
+    """Code rows as the oracle holds them: uint64 words, ceil(r/64) a row (a
+    32-bit code row, held as one int32 word, zero-extended)."""
+    a = t.cpu().numpy()
+    if a.dtype == np.int32:
+        return a.view(np.uint32).astype(np.uint64)
+    return a.view(np.uint64)
 
 
 def scores_np(t: torch.Tensor) -> np.ndarray:

@@ -41,8 +41,7 @@ def test_paged_step_matches_oracle_and_contiguous_step(hata_gpu, case):
     d = Dev(inp)
     codes = gpu_build_cache(hata_gpu, d) if r == 128 else None
     if codes is None:
-        words = (r + 63) // 64
-        codes = torch.zeros((B, Hkv, d.cap, words), dtype=torch.int64, device="cuda")
+        codes = hata_gpu.new_codes(B, Hkv, d.cap, r=r)
         hata_gpu.encode_append(d.K, d.W, codes, n_new=d.cap)
     mp = (d.cap + P - 1) // P
     num_pages = B * mp + spare
@@ -75,10 +74,9 @@ def test_paged_step_matches_oracle_and_contiguous_step(hata_gpu, case):
             check_codes(cn[b, h, n - 1:n], inp.K[b, h, n - 1:n], inp.W[h], dist == "exact")
     qc = gpu_query_codes(hata_gpu, d) if r == 128 else None
     if qc is None:
-        words = (r + 63) // 64
-        qc4 = torch.zeros((B, Hq, 1, words), dtype=torch.int64, device="cuda")
+        qc4 = hata_gpu.new_codes(B, Hq, 1, r=r)
         hata_gpu.encode_append(d.q.view(B, Hq, 1, 128), d.W, qc4, n_new=1)
-        qc = qc4.view(B, Hq, words)
+        qc = qc4.view(B, Hq, qc4.shape[-1])
     _, ridx, rout = oracle_units(inp, codes_np(qc), cn)
     np.testing.assert_array_equal(idx.cpu().numpy(), ridx)
     assert_close(out.cpu().numpy(), rout, "paged vs oracle")

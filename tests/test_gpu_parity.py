@@ -462,8 +462,8 @@ def test_decode_step_qk_staged_shape(hata_gpu, r):
     Wq = torch.randn((Hkv, 128, r), generator=g, device="cuda") / np.sqrt(128.0)
     Wk = torch.randn((Hkv, 128, r), generator=g, device="cuda") / np.sqrt(128.0)
     seq = torch.full((B,), N, dtype=torch.int32, device="cuda")
-    wd = (r + 63) // 64
-    codes = torch.zeros((B, Hkv, N, wd), dtype=torch.int64, device="cuda")
+    codes = hata_gpu.new_codes(B, Hkv, N, r=r)
+    wd = codes.shape[-1]
     hata_gpu.encode_append(K, Wk, codes, n_new=N)
     codes[:, :, N - 1] = 0x1234
     ws = hata_gpu.alloc_workspace(hata_gpu.OP_DECODE_STEP, B, Hq, Hkv, N, k, r=r)
@@ -472,7 +472,7 @@ def test_decode_step_qk_staged_shape(hata_gpu, r):
     _log(f"qk staged shape: 130 units x 32800, r={r}")
     hata_gpu.decode_step_qk(q, K, V, Wq, Wk, codes, seq, N, k, 1.0 / np.sqrt(128.0), out, ws, idx)
     torch.cuda.synchronize()
-    qc = torch.zeros((B, Hq, 1, wd), dtype=torch.int64, device="cuda")
+    qc = hata_gpu.new_codes(B, Hq, 1, r=r)
     hata_gpu.encode_append(q.view(B, Hq, 1, 128), Wq, qc, n_new=1)
     bits = lambda t: t.view(torch.int16).cpu().numpy().view(np.uint16)
     qcn = codes_np(qc.view(B, Hq, wd))
@@ -488,8 +488,9 @@ def test_decode_step_qk_staged_shape(hata_gpu, r):
 
 
 # ------------------------------------------------- other code widths r
-# Codes of r in {32, 64, 256} bits (ceil(r/64) words per row, bits past r
-# zero): every stage against the oracle at that width.
+# Codes of r in {32, 64, 256} bits (r/8 bytes per row: one int32 word at
+# r = 32, r/64 int64 words otherwise): every stage against the oracle at that
+# width.
 
 def _wshape(B, Hq, Hkv, N, k, r, dist="gauss", seed=8100):
     return synth.Shape(f"w-{B}-{Hq}-{Hkv}-{N}-{k}-{r}-{dist}", B=B, Hq=Hq, Hkv=Hkv, N=N, k=k, dist=dist,
@@ -497,16 +498,15 @@ def _wshape(B, Hq, Hkv, N, k, r, dist="gauss", seed=8100):
 
 
 def _wcache(hb, d: Dev, r: int) -> torch.Tensor:
-    codes = torch.zeros((d.B, d.Hkv, d.cap, (r + 63) // 64), dtype=torch.int64, device="cuda")
+    codes = hb.new_codes(d.B, d.Hkv, d.cap, r=r)
     hb.encode_append(d.K, d.W, codes, n_new=d.cap)
     return codes
 
 
 def _wqcodes(hb, d: Dev, r: int) -> torch.Tensor:
-    w = (r + 63) // 64
-    qc = torch.zeros((d.B, d.Hq, 1, w), dtype=torch.int64, device="cuda")
+    qc = hb.new_codes(d.B, d.Hq, 1, r=r)
     hb.encode_append(d.q.view(d.B, d.Hq, 1, 128), d.W, qc, n_new=1)
-    return qc.view(d.B, d.Hq, w)
+    return qc.view(d.B, d.Hq, qc.shape[-1])
 
 
 @pytest.mark.parametrize("r", [32, 64, 256])
@@ -521,8 +521,8 @@ def test_encode_and_hamming_each_width(hata_gpu, r, dist):
     for b in range(2):
         for h in range(2):
             check_codes(cn[b, h], inp.K[b, h], inp.W[h], exact=dist == "exact")
-    if r == 32:
-        assert (cn >> np.uint64(32) == 0).all()  # bits past r stay zero
+    if r == 32:  # 4-byte rows: a row of another width would land in the next head's rows
+        assert codes.dtype == torch.int32 and codes.shape[-1] == 1
     qc = _wqcodes(hata_gpu, d, r)
     sc = torch.zeros((2, 2, d.cap), dtype=torch.int16, device="cuda")
     hata_gpu.hamming_scores(qc, codes, d.seq, d.max_len, sc, r=r)

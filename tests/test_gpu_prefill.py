@@ -27,6 +27,11 @@ SENT_OUT = 7.25
 SENT_CODE = 0x5A5A5A5A5A5A5A5A
 
 
+def _sent(r):
+    """Sentinel code word for r-bit rows (one int32 word at r = 32)."""
+    return SENT_CODE if r >= 64 else 0x5A5A5A5A
+
+
 def _log(msg):
     print(msg, flush=True)
 
@@ -67,9 +72,8 @@ def _run(hb, q, K, V, W, lens, max_len, scale):
     B, Hq, q_rows, d = q.shape
     _, Hkv, cap, _ = K.shape
     r = W.shape[2]
-    words = (r + 63) // 64
     out = torch.full((B, Hq, q_rows, d), SENT_OUT, dtype=torch.float32, device="cuda")
-    codes = torch.full((B, Hkv, cap, words), SENT_CODE, dtype=torch.int64, device="cuda")
+    codes = hb.new_codes(B, Hkv, cap, r=r, fill=_sent(r))
     hb.prefill(bf16_tensor(q), bf16_tensor(K), bf16_tensor(V), torch.from_numpy(W).cuda(), codes,
                torch.from_numpy(np.asarray(lens, np.int32)).cuda(), max_len, scale, out)
     torch.cuda.synchronize()
@@ -106,7 +110,7 @@ def test_prefill_matches_oracle(hata_gpu, case):
         assert (out[b, :, n:] == SENT_OUT).all()
         for h in range(Hkv):
             flips += check_codes(codes[b, h, :n], K[b, h, :n], W[h], exact)
-            assert (codes[b, h, n:] == np.uint64(SENT_CODE)).all()
+            assert (codes[b, h, n:] == np.uint64(_sent(r))).all()
     _log(f"  flips {flips}; err / (2e-3 + 1e-3|ref|): worst {worst:.3g}, {past} of {total} past 1")
 
 
@@ -208,11 +212,9 @@ def test_paged_prefill_equals_contiguous_bitwise(hata_gpu, case):
     num_pages = B * mp + spare
     perm = np.random.default_rng(8701 + P).permutation(num_pages)[:B * mp].astype(np.int32)
     bt = torch.from_numpy(perm.reshape(B, mp)).cuda()
-    words = (r + 63) // 64
     Kp = paginate(bf16_tensor(K), P, bt, num_pages)
     Vp = paginate(bf16_tensor(V), P, bt, num_pages)
-    Cp = paginate(torch.full((B, Hkv, cap, words), SENT_CODE, dtype=torch.int64, device="cuda"), P, bt, num_pages,
-                  fill=SENT_CODE)
+    Cp = paginate(hata_gpu.new_codes(B, Hkv, cap, r=r, fill=_sent(r)), P, bt, num_pages, fill=_sent(r))
     out = torch.full((B, Hq, q_rows, 128), SENT_OUT, dtype=torch.float32, device="cuda")
     hata_gpu.prefill_paged(bf16_tensor(q), Kp, Vp, torch.from_numpy(W).cuda(), Cp, bt,
                            torch.from_numpy(np.asarray(lens, np.int32)).cuda(), max(lens), scale, out)
@@ -224,4 +226,4 @@ def test_paged_prefill_equals_contiguous_bitwise(hata_gpu, case):
     used = set(perm.tolist())
     for pg in range(num_pages):
         if pg not in used:
-            assert (codes_np(Cp[pg]) == np.uint64(SENT_CODE)).all()
+            assert (codes_np(Cp[pg]) == np.uint64(_sent(r))).all()
