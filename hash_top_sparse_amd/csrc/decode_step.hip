@@ -96,6 +96,8 @@ enum TracePoint {
   kTrWait2 = 11,     // every record of the unit published
   kTrEnd = 12,       // outputs written
   kTrQrows = 13,     // query rows staged in LDS
+  kTrSearchLoop = 14,  // search bounds read, first round starts
+  kTrRound1 = 15,    // first search round's partial counts exchanged in LDS
   kTrSearch = 16     // threshold found (before the writers' prefix counts)
 };
 #ifdef HATA_PHASE_TRACE
@@ -145,8 +147,11 @@ struct Cfg {
   static constexpr int NSTG = (G + 1 + 3) / 4;                   // staging loads per thread
   static constexpr int o_qf = o_hist + HCOPY * NBP * 4;          // 4*NSTG rows of 128 float (G+1 used)
   static constexpr int o_red = o_qf + 4 * NSTG * kD * 4;         // RED float
-  static constexpr int o_qcode = o_red + RED * 4;                // (G+1)*W64 uint64
-  static constexpr int o_misc = o_qcode + (G + 1) * W64 * 8;     // 64 uint32
+  static constexpr int o_qcode = (o_red + RED * 4 + 15) / 16 * 16;  // (G+1)*W64 uint64
+  // (rounded up to 16 bytes: with one 64-bit word per code the query codes
+  // end 8 bytes past a 16-byte boundary, and every later area is read with
+  // 16-byte LDS accesses)
+  static constexpr int o_misc = (o_qcode + (G + 1) * W64 * 8 + 15) / 16 * 16;  // 64 uint32
   static constexpr int o_whdr = o_misc + 64 * 4;                 // kMaxWg int4 + 2*4*64 uint32
   // the unit's histogram windows (read after the first exchange, used up by
   // the threshold) and the attention's staged K/V rows share one area, as
@@ -156,6 +161,9 @@ struct Cfg {
   static constexpr int WKV = (kMaxWg * kWinBytes > kShortList * 512) ? kMaxWg * kWinBytes : kShortList * 512;
   static constexpr int o_pgl = o_kvs + WKV;                      // paged: kMaxPgl int32 page ids
   static constexpr int o_sel = o_pgl + (PAGED ? kMaxPgl * 4 : 0); // k + 1 int32
+  static_assert(o_qf % 16 == 0 && o_red % 16 == 0 && o_qcode % 16 == 0 && o_misc % 16 == 0 &&
+                    o_whdr % 16 == 0 && o_win % 16 == 0 && o_pgl % 16 == 0 && o_sel % 16 == 0,
+                "LDS areas start on 16-byte boundaries");
   static size_t lds_bytes(int k, int chunk) {
     size_t s = (size_t)o_sel + (size_t)(k + 1) * 4;
     s = (s + 15) / 16 * 16;
@@ -749,6 +757,7 @@ __global__ __launch_bounds__(kNT, (step_occupancy<G, R>())) void decode_step_ker
     const int nper = (a.Wg + 3) / 4;
     HATA_VALUE(21, glo);
     HATA_VALUE(22, tmin);
+    HATA_MARK(kTrSearchLoop);
     for (int c0 = glo, rnd = 0; c0 <= tmin; c0 += 64, ++rnd) {
       HATA_VALUE(20, rnd + 1);
       const int s2 = c0 + lane;
@@ -768,6 +777,7 @@ __global__ __launch_bounds__(kNT, (step_occupancy<G, R>())) void decode_step_ker
       uint32_t* cp = cpart + (rnd & 1) * 256;
       cp[wv * 64 + lane] = part;
       __syncthreads();
+      if (rnd == 0) HATA_MARK(kTrRound1);
       const uint32_t C = cp[lane] + cp[64 + lane] + cp[128 + lane] + cp[192 + lane];
       const uint64_t hit = __ballot(C >= (uint32_t)k && s2 <= tmin);
       if (hit) {
