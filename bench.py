@@ -605,9 +605,9 @@ def train_bench(J: int = 512, n: int = 8192, r: int = 128, steps: int = 20) -> d
 
 
 TRACE_POINTS = ("start", "qcodes", "scanned", "hist", "published", "wait1", "windows", "threshold",
-                "compacted", "attended", "record", "wait2", "end", "qrows", "search_loop", "round1", "search")
+                "compacted", "attended", "record", "wait2", "end", "qrows", "search_loop", "round1", "search", "gathered", "accumulated")
 # the boundaries in the order a workgroup passes them (indices into TRACE_POINTS)
-TRACE_ORDER = (0, 13, 1, 2, 3, 4, 5, 6, 14, 15, 16, 7, 8, 9, 10, 11, 12)
+TRACE_ORDER = (0, 13, 1, 2, 3, 4, 5, 6, 14, 15, 16, 7, 8, 17, 18, 9, 10, 11, 12)
 TRACE_SLOTS = 24  # timestamps stored per workgroup
 
 

@@ -71,7 +71,6 @@ constexpr uint32_t kSpinLimit = 1u << 22;  // default bound on the polls of one 
 // s_getreg operand for HW_REG_XCC_ID (register 20, bits 0..31): the XCD the
 // wave runs on
 constexpr int kXccIdReg = 20 | (31 << 11);
-constexpr int kShortList = 64;     // kept rows staged in LDS per attention batch
 constexpr int kMaxPgl = kMaxChunk / 16 + 8;   // page ids of one chunk (pages of >= 16 rows)
 constexpr int kPglPerThread = (kMaxPgl + kNT - 1) / kNT;
 
@@ -98,7 +97,9 @@ enum TracePoint {
   kTrQrows = 13,     // query rows staged in LDS
   kTrSearchLoop = 14,  // search bounds read, first round starts
   kTrRound1 = 15,    // first search round's partial counts exchanged in LDS
-  kTrSearch = 16     // threshold found (before the writers' prefix counts)
+  kTrSearch = 16,    // threshold found (before the writers' prefix counts)
+  kTrGathered = 17,  // first batch of kept K/V rows staged (G > 1)
+  kTrAccum = 18      // every kept row accumulated, before the heads' merge (G > 1)
 };
 #ifdef HATA_PHASE_TRACE
 #define HATA_MARK(i) \
@@ -157,8 +158,8 @@ struct Cfg {
   // the threshold) and the attention's staged K/V rows share one area, as
   // do the partial records staged for the final merge (after the attention)
   static constexpr int o_win = o_whdr + 4 * kMaxWg * 4 + 2048;   // kMaxWg*kWinBytes (also combine staging)
-  static constexpr int o_kvs = o_win;                            // kShortList K/V rows
-  static constexpr int WKV = (kMaxWg * kWinBytes > kShortList * 512) ? kMaxWg * kWinBytes : kShortList * 512;
+  static constexpr int o_kvs = o_win;                            // staged K rows and V^T of one batch
+  static constexpr int WKV = (kMaxWg * kWinBytes > kMxLdsBytes) ? kMaxWg * kWinBytes : kMxLdsBytes;
   static constexpr int o_pgl = o_kvs + WKV;                      // paged: kMaxPgl int32 page ids
   static constexpr int o_sel = o_pgl + (PAGED ? kMaxPgl * 4 : 0); // k + 1 int32
   static_assert(o_qf % 16 == 0 && o_red % 16 == 0 && o_qcode % 16 == 0 && o_misc % 16 == 0 &&
@@ -879,22 +880,24 @@ __global__ __launch_bounds__(kNT, (step_occupancy<G, R>())) void decode_step_ker
   __syncthreads();
   HATA_MARK(kTrCompacted);
 
-  // ---- 6. gather-fused attention over the kept rows (G > 1: batches of
-  // kShortList rows staged in LDS, the next batch's loads in flight while a
-  // batch is used, waves assigned to heads; G = 1: rows gathered straight
-  // into registers, three steps of 64 rows in flight)
+  // ---- 6. gather-fused attention over the kept rows (G > 1: batches of 64
+  // rows staged in LDS, the next batch's loads in flight while a batch is
+  // used, logits and weighted values on the matrix cores; G = 1: rows
+  // gathered straight into registers, three steps of 64 rows in flight)
   if constexpr (PAGED) {
     const PagedRows map{pgl, (w * a.chunk) >> a.log2P, a.log2P, a.Hkv, h, kMaxPgl - 1};
     if constexpr (G == 1)
       attend_rows_g1<4, 3>(qf, sel, m_self, n, a.K, a.V, a.scale, red, map);
     else
-      attend_heads<G, kShortList>(qf, sel, m_self, n, a.K, a.V, a.scale, red, reinterpret_cast<uint4*>(kvs), map);
+      attend_heads_mx<G>(qf, sel, m_self, n, a.K, a.V, a.scale, red, reinterpret_cast<uint16_t*>(kvs), map);
   } else {
     if constexpr (G == 1)
       attend_rows_g1<4, 3>(qf, sel, m_self, n, a.K + row0 * kD, a.V + row0 * kD, a.scale, red);
     else
-      attend_heads<G, kShortList>(qf, sel, m_self, n, a.K + row0 * kD, a.V + row0 * kD, a.scale, red,
-                                  reinterpret_cast<uint4*>(kvs));
+      attend_heads_mx<G>(qf, sel, m_self, n, a.K + row0 * kD, a.V + row0 * kD, a.scale, red,
+                         reinterpret_cast<uint16_t*>(kvs), SameRows(), [&](int i) {
+                           if (i == 0) HATA_MARK(kTrGathered); else HATA_MARK(kTrAccum);
+                         });
   }
 
   HATA_MARK(kTrAttended);

@@ -608,7 +608,7 @@ __device__ __forceinline__ void finish_heads(const SoftmaxState<(G >= 4) ? G / 4
 // NPF steps stay in flight in a register ring (NPF*UN*512 bytes per group).
 // Row ids past the list are clamped to its last row, so every load is issued
 // unconditionally (the compiler can count them exactly) and the extra rows
-// are masked out of the softmax.  Same output as attend_heads<1, ...>.
+// are masked out of the softmax.
 // Row map of the gather: cache row of a kept token (the identity for a
 // contiguous cache).
 struct SameRows {
@@ -668,29 +668,51 @@ __device__ __forceinline__ void attend_rows_g1(const float* qf, const int32_t* s
   finish_heads<1>(st, red);
 }
 
-// Attention over the kept rows with waves assigned to heads.  Rows are taken
-// in batches of MAXR: a batch's K/V rows are staged in LDS by the whole
-// workgroup (16-byte loads, MAXR*32/256 per thread), and the next batch's
-// loads are issued into registers before the current batch is used, so they
-// are in flight meanwhile.  For G >= 4 wave wv owns heads
-// [wv*G/4, (wv+1)*G/4) over every row, and for G < 4 the 4/G waves of a head
-// split the rows.  Within a wave the 4 groups of 16 lanes take rows in turn
-// (8 channels per lane); the online-softmax state runs over all batches.
-// Each wave merges only its own heads (permlane swaps), so no cross-wave
-// merge is needed for G >= 4.  kvs: LDS of MAXR * 512 bytes.  Writes
-// red[g*kRec + {M, L, A[128]}] (red holds at least (G + 4) * kRec floats);
-// ends with __syncthreads.
-template <int G, int MAXR, class Map = SameRows>
-__device__ __forceinline__ void attend_heads(const float* qf, const int32_t* sel, int m, int n,
-                                             const uint16_t* K, const uint16_t* V, float scale,
-                                             float* red, uint4* kvs, const Map& map = Map()) {
-  constexpr int HPW = (G >= 4) ? G / 4 : 1;  // heads per wave
-  constexpr int WPH = (G >= 4) ? 1 : 4 / G;  // waves per head
-  constexpr int LPT = MAXR * 32 / kNT;       // staging loads per thread and batch
-  const int t = threadIdx.x, lane = t & 63, wv = t >> 6, rg = lane >> 4, sub = lane & 15;
-  // row id of staging slot i of batch r0 (clamped into the list) and the load
+// No-op phase marker (the phase-trace build passes one that records times).
+struct NoMark {
+  __device__ __forceinline__ void operator()(int) const {}
+};
+
+// Attention over the kept rows on the matrix cores (G = 2, 4, 8 query heads
+// per KV head; 256 threads).  Rows are taken in batches of 64 and staged in
+// LDS as they come from HBM (K then V, 16-byte pieces), in 528-byte rows so
+// that the 16 rows of a logit tile fall on distinct bank groups; rows past
+// the list are staged as zeros, and the next batch's loads are in flight
+// while a batch is used.  Per batch every wave forms the whole logit tile
+// S^T = K Q^T with v_mfma_f32_16x16x32_bf16 (keys as M in 16-key tiles,
+// heads as N, the 128 channels in 4 steps of 32), so the four waves hold
+// identical logits and the same running max without exchanging them.  Wave w
+// then accumulates O^T = V^T P^T for channels [32 w, 32 w + 32) over steps
+// of 32 keys, with the weights split into two bf16 terms P = hi + lo
+// (lo = bf16(P - hi)): both contractions run on the matrix cores and the
+// split leaves a relative error of at most 2^-16 in each weight.  q and K
+// are bf16, so the logits' products are exact and only their fp32 summation
+// order differs from a plain dot product.  The k index of the V^T P^T
+// product runs over the keys in the order the S^T accumulators hold them
+// (lane group h4 holds keys 4 h4 .. 4 h4 + 3 of each 16-key tile); the V^T
+// operand is gathered in that order with 2-byte LDS reads.  Tiles past the
+// batch are skipped by uniform branches.  Writes red[g*kRec + {M, L, A[128]}]
+// (M: running max of the scaled logits, L: sum of the weights, A: weighted
+// V relative to M); ends with __syncthreads.  kvl: LDS of kMxLdsBytes.
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef unsigned short u16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+constexpr int kMxRows = 64;                    // kept rows per batch
+constexpr int kMxRow = 2 * kD + 8;             // uint16 per staged row (K, V, 16 bytes of padding)
+constexpr int kMxLdsBytes = kMxRows * kMxRow * 2;
+
+template <int G, class Map = SameRows, class Mark = NoMark>
+__device__ __forceinline__ void attend_heads_mx(const float* qf, const int32_t* sel, int m, int n,
+                                                const uint16_t* K, const uint16_t* V, float scale,
+                                                float* red, uint16_t* kvl, const Map& map = Map(),
+                                                const Mark& mark = Mark()) {
+  static_assert(G >= 2 && G <= 16, "heads are the N index of a 16-wide tile");
+  constexpr int LPT = kMxRows * 32 / kNT;  // 16-byte staging loads per thread and batch
+  const int t = threadIdx.x, lane = t & 63, wv = t >> 6, h4 = lane >> 4, l16 = lane & 15;
+  // staging slot i of thread t: piece c = t + 256 i, row c >> 5, 16-byte
+  // part c & 31 (parts 0..15: K channels 8 p .. 8 p + 7; 16..31: V)
   auto gather = [&](int r0, uint4 (&v)[LPT]) {
-    const int mb = min(MAXR, m - r0);
+    const int mb = min(kMxRows, m - r0);
     int tokv[LPT];
 #pragma unroll
     for (int i = 0; i < LPT; ++i) tokv[i] = sel[r0 + max(min((t >> 5) + 8 * i, mb - 1), 0)];
@@ -705,47 +727,145 @@ __device__ __forceinline__ void attend_heads(const float* qf, const int32_t* sel
       }
     }
   };
-  const int hg = wv / WPH, part = wv - hg * WPH;
-  const int g0 = hg * HPW;
-  float qreg[HPW][8];
+  // B operand of S^T = K Q^T: head l16 (zero past G), channels 32 kk + 8 h4 + j
+  // (every lane reads a valid row, the select follows the loads: a
+  // conditional load here would be a branch and a wait per element)
+  bf16x8_t qb[4];
+  {
+    const float* qrow = qf + min(l16, G - 1) * kD + 8 * h4;
+    const bool keep = l16 < G;
+    float4 qv[8];
 #pragma unroll
-  for (int i = 0; i < HPW; ++i)
+    for (int kk = 0; kk < 4; ++kk) {
+      qv[2 * kk] = *reinterpret_cast<const float4*>(qrow + 32 * kk);
+      qv[2 * kk + 1] = *reinterpret_cast<const float4*>(qrow + 32 * kk + 4);
+    }
 #pragma unroll
-    for (int c = 0; c < 8; ++c) qreg[i][c] = qf[(g0 + i) * kD + sub * 8 + c];
-  SoftmaxState<HPW> st;
-  st.init();
-  constexpr int UN = 4;
-  const int stride = 4 * WPH;
+    for (int kk = 0; kk < 4; ++kk) {
+      const float f[8] = {qv[2 * kk].x, qv[2 * kk].y, qv[2 * kk].z, qv[2 * kk].w,
+                          qv[2 * kk + 1].x, qv[2 * kk + 1].y, qv[2 * kk + 1].z, qv[2 * kk + 1].w};
+#pragma unroll
+      for (int j = 0; j < 8; ++j) qb[kk][j] = (__bf16)(keep ? f[j] : 0.f);
+    }
+  }
+  float m_run = -INFINITY, l_run = 0.f;
+  f32x4_t o[2];
+#pragma unroll
+  for (int c2 = 0; c2 < 2; ++c2) o[c2] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   uint4 pv[LPT];
   gather(0, pv);
-  for (int r0 = 0; r0 < m; r0 += MAXR) {
-    const int mb = min(MAXR, m - r0);
+  for (int r0 = 0; r0 < m; r0 += kMxRows) {
+    const int mb = min(kMxRows, m - r0);
     if (r0 > 0) __syncthreads();  // the previous batch is no longer read
 #pragma unroll
     for (int i = 0; i < LPT; ++i) {
       const int c = t + i * kNT;
-      if ((c >> 5) < mb) kvs[c] = pv[i];
+      *reinterpret_cast<uint4*>(kvl + (c >> 5) * kMxRow + (c & 31) * 8) = pv[i];
     }
-    if (r0 + MAXR < m) gather(r0 + MAXR, pv);  // in flight while this batch is used
+    if (r0 + kMxRows < m) gather(r0 + kMxRows, pv);  // in flight while this batch is used
     __syncthreads();
-    for (int rr = part * 4 + rg; rr < mb; rr += stride * UN) {
-      uint4 kv[UN], vv[UN];
-      bool valid[UN];
+    if (r0 == 0) mark(0);
+    // V^T operands (A of O^T = V^T P^T) for channel tiles 2 wv + c2 and key
+    // steps ps, read before the logits so that both LDS round trips overlap:
+    // k index 8 h4 + j is key 32 ps + 4 h4 + j (j < 4) or 32 ps + 16 + 4 h4 + j - 4
+    bf16x8_t va[2][2];
+    auto load_va = [&](int ps) {
 #pragma unroll
-      for (int u = 0; u < UN; ++u) {
-        const int r = rr + u * stride;
-        valid[u] = r < mb;
-        kv[u] = make_uint4(0, 0, 0, 0);
-        vv[u] = make_uint4(0, 0, 0, 0);
-        if (valid[u]) {
-          kv[u] = kvs[r * 32 + sub];
-          vv[u] = kvs[r * 32 + 16 + sub];
+      for (int c2 = 0; c2 < 2; ++c2) {
+        const uint16_t* vcol = kvl + kD + 32 * wv + 16 * c2 + l16;
+        u16x8_t a16;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) a16[j] = vcol[(32 * ps + 16 * (j >> 2) + 4 * h4 + (j & 3)) * kMxRow];
+        va[ps][c2] = __builtin_bit_cast(bf16x8_t, a16);
+      }
+    };
+    load_va(0);
+    if (mb > 32) load_va(1);
+    // logits: s[kt][i] is key 16 kt + 4 h4 + i of the batch for head l16
+    // (channels in two independent accumulations, added at the end)
+    f32x4_t s[4];
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) {
+      s[kt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      if (16 * kt < mb) {
+        const uint16_t* krow = kvl + (16 * kt + l16) * kMxRow + 8 * h4;
+        bf16x8_t ka[4];
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) ka[kk] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(krow + 32 * kk));
+        f32x4_t s2 = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        s[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[0], qb[0], s[kt], 0, 0, 0);
+        s2 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[2], qb[2], s2, 0, 0, 0);
+        s[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[1], qb[1], s[kt], 0, 0, 0);
+        s2 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[3], qb[3], s2, 0, 0, 0);
+        s[kt] += s2;
+      }
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) {
+      if (16 * kt < mb) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const bool ok = 16 * kt + 4 * h4 + i < mb;
+          s[kt][i] = ok ? s[kt][i] * scale : -INFINITY;
+          mx = fmaxf(mx, s[kt][i]);
         }
       }
-      attend_block<HPW, UN>(st, qreg, kv, vv, valid, scale);
+    }
+    mx = pair32_max(pair16_max(mx));  // over the batch's keys, per head
+    const float m_new = fmaxf(m_run, mx);
+    // exp(-inf) = 0 when m_run was -inf
+    const float alpha = (m_new == -INFINITY) ? 1.f : __expf(m_run - m_new);
+    l_run *= alpha;
+#pragma unroll
+    for (int c2 = 0; c2 < 2; ++c2) o[c2] *= alpha;
+    m_run = m_new;
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) {
+      if (16 * kt < mb) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float p = (16 * kt + 4 * h4 + i < mb) ? __expf(s[kt][i] - m_new) : 0.f;
+          s[kt][i] = p;
+          l_run += p;
+        }
+      } else {
+        s[kt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      }
+    }
+    // O^T += V^T P^T over steps of 32 keys (tiles 2 ps and 2 ps + 1), the
+    // weights taken in the V^T operand's key order
+#pragma unroll
+    for (int ps = 0; ps < 2; ++ps) {
+      if (32 * ps < mb) {
+        bf16x8_t hi, lo;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const float p = s[2 * ps + (j >> 2)][j & 3];
+          const __bf16 ph = (__bf16)p;
+          hi[j] = ph;
+          lo[j] = (__bf16)(p - (float)ph);
+        }
+#pragma unroll
+        for (int c2 = 0; c2 < 2; ++c2) {
+          o[c2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[ps][c2], hi, o[c2], 0, 0, 0);
+          o[c2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[ps][c2], lo, o[c2], 0, 0, 0);
+        }
+      }
     }
   }
-  finish_heads<G>(st, red);
+  mark(1);
+  const float L = pair32_sum(pair16_sum(l_run));
+  if (l16 < G) {
+    float* r = red + l16 * kRec;
+    // accumulator i of channel tile 2 wv + c2 holds channel 32 wv + 16 c2 + 4 h4 + i
+#pragma unroll
+    for (int c2 = 0; c2 < 2; ++c2)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) r[2 + 32 * wv + 16 * c2 + 4 * h4 + i] = o[c2][i];
+    if (wv == 0 && h4 == 0) { r[0] = m_run; r[1] = L; }
+  }
+  __syncthreads();
 }
 
 }  // namespace hata
