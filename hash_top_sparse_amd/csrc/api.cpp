@@ -275,7 +275,7 @@ static int decode_step_impl(const void* q, const void* K, const void* V, const f
     hipError_t e = hata::noalloc_scratch(&wsb);
     if (e != hipSuccess) return hip_fail(e, "decode_step_noalloc: hipGetSymbolAddress");
     if (p.fused) {
-      e = hata::launch_fill_zero(wsb, p.Wg > 1 ? p.off_win : p.total, s);
+      e = hata::launch_fill_zero(wsb, p.off_win, s);
       if (e != hipSuccess) return hip_fail(e, "decode_step_noalloc: clearing the scratch flags");
     }
   } else {

@@ -1105,12 +1105,18 @@ StepPlan plan_decode_step(int B, int Hq, int Hkv, int64_t max_len, int k, int nu
   }
   size_t off = 0;
   p.off_err = off;   off = align(off + 256);
+  // The exchange area (flags, stamps and histogram windows of every unit's
+  // kMaxWg workgroup slots) sits at offsets that depend on the unit count
+  // only and is reserved whether or not this call runs the fused step, so a
+  // call that runs the separate kernels never writes over the flags that a
+  // later fused step with the same B and Hkv reads its epoch from.
+  const size_t slots = (size_t)U * kMaxWg;
+  p.off_flags = off;  off = align(off + slots * 4);
+  p.off_stamps = off; off = align(off + slots * 4);
+  p.off_win = off;    off = align(off + slots * kWinWords * 4);
+  p.off_xend = off;
   if (p.fused) {
-    const size_t slots = (size_t)U * kMaxWg;
-    p.off_flags = off; off = align(off + slots * 4);
     if (Wg > 1) {
-      p.off_stamps = off; off = align(off + slots * 4);
-      p.off_win = off;  off = align(off + slots * kWinWords * 4);
       p.off_full = off; off = align(off + slots * (size_t)p.full_words * 4);
       p.off_part = off; off = align(off + slots * recp * 4);
     }

@@ -75,6 +75,7 @@ struct StepPlan {
   size_t off_err = 0, off_flags = 0, off_stamps = 0, off_win = 0, off_full = 0, off_part = 0;
   size_t off_qc = 0, off_scores = 0, off_idx = 0, off_attn = 0, off_topk = 0;
   size_t off_trace = 0;  // phase-trace build only: per-workgroup timestamps at the end
+  size_t off_xend = 0;   // end of the exchange area (error words, flags, stamps, windows)
   int full_words = 0;  // 32-bit words per workgroup in the full-histogram area
   size_t total = 0;
 };

@@ -179,7 +179,12 @@ int hata_sparse_decode(const void* q, const void* K, const void* V, int B,
  * A sequence whose length (read on the device) lies outside [1, cap] gets
  * out = 0 and idx_out = -1 and its code rows are left unchanged.
  * ws: hata_workspace_bytes(HATA_OP_DECODE_STEP, ...), zeroed once before
- * first use.  Shapes whose per-unit scores do not fit on chip run the same
+ * first use.  A workspace serves the B and Hkv it was zeroed for, at any
+ * Hq, r, max_len and k within its size (calls that run the separate
+ * kernels leave the fused step's flags alone); before a call with another
+ * B or Hkv it must be zeroed again, since the per-unit exchange slots then
+ * sit at other offsets.
+ * Shapes whose per-unit scores do not fit on chip run the same
  * steps as separate kernels inside this call (idx_out may still be NULL:
  * the kept list then lives in the workspace).
  * The workgroups of one unit exchange histogram windows and partial

@@ -114,3 +114,42 @@ def test_staged_step_without_idx_out(hata_gpu):
     ix = idx.cpu().numpy()
     assert ((ix >= 0) & (ix < N - 5)).all()
     assert (np.diff(ix, axis=-1) > 0).all()
+
+
+def test_fused_after_staged_on_one_workspace(hata_gpu):
+    """One workspace, the same B and Hkv, three calls: a fused step (100
+    units of 60,000 tokens: two workgroups per unit), a call whose longer
+    context (70,000 tokens) runs the separate kernels, then the fused step
+    again.  The separate kernels' buffers lie past the fused step's exchange
+    area, so the third call reads the flags the first one left and equals it
+    bit for bit."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    U = min(100, cus // 2 - 2)
+    n_fused, n_staged, k = 60000, 70000, 64
+    _log(f"fused after staged: {U} units, {n_fused} / {n_staged} tokens")
+    g = torch.Generator(device="cuda").manual_seed(9420)
+    q = torch.randn((1, U, 128), generator=g, device="cuda").to(torch.bfloat16)
+    K = torch.randn((1, U, n_staged, 128), generator=g, device="cuda").to(torch.bfloat16)
+    V = torch.randn((1, U, n_staged, 128), generator=g, device="cuda").to(torch.bfloat16)
+    W = torch.randn((U, 128, 128), generator=g, device="cuda") * (1.0 / 128) ** 0.5
+    codes = hata_gpu.new_codes(1, U, n_staged, r=128)
+    hata_gpu.encode_append(K, W, codes, n_new=n_staged)
+    ws_bytes = max(hata_gpu.workspace_bytes(hata_gpu.OP_DECODE_STEP, 1, U, U, n, k) for n in (n_fused, n_staged))
+    ws = torch.zeros(ws_bytes, dtype=torch.uint8, device="cuda")
+    assert hata_gpu.workspace_bytes(hata_gpu.OP_DECODE_STEP, 1, U, U, n_staged, k) > \
+        hata_gpu.workspace_bytes(hata_gpu.OP_DECODE_STEP, 1, U, U, n_fused, k)  # the staged layout
+    scale = 1.0 / 128 ** 0.5
+    seq_f = torch.tensor([n_fused], dtype=torch.int32, device="cuda")
+    seq_s = torch.tensor([n_staged], dtype=torch.int32, device="cuda")
+    outs, idxs = [], []
+    for seq, n in ((seq_f, n_fused), (seq_s, n_staged), (seq_f, n_fused)):
+        out = torch.zeros((1, U, 128), dtype=torch.float32, device="cuda")
+        idx = torch.full((1, U, k), -9, dtype=torch.int32, device="cuda")
+        hata_gpu.decode_step(q, K, V, W, codes, seq, n, k, scale, out, ws, idx)
+        torch.cuda.synchronize()
+        assert hata_gpu.workspace_check(ws) == 0
+        outs.append(out.cpu().numpy())
+        idxs.append(idx.cpu().numpy())
+    np.testing.assert_array_equal(idxs[2], idxs[0])
+    np.testing.assert_array_equal(outs[2], outs[0])
+    assert (idxs[1] >= 0).all()
