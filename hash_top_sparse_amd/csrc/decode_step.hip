@@ -168,8 +168,9 @@ struct Cfg {
   static size_t lds_bytes(int k, int chunk) {
     size_t s = (size_t)o_sel + (size_t)(k + 1) * 4;
     s = (s + 15) / 16 * 16;
-    // scores, padded to a multiple of 8 slabs of 256 tokens
-    return s + (size_t)((chunk + 8 * kNT - 1) / (8 * kNT) * (8 * kNT)) * 2;
+    // scores, padded to a multiple of 8 slabs of 256 tokens, with 8 spare
+    // slots after every 128 tokens (sc_slot)
+    return s + (size_t)((chunk + 8 * kNT - 1) / (8 * kNT) * (8 * kNT)) * 2 * 17 / 16;
   }
 };
 
@@ -313,6 +314,13 @@ __global__ __launch_bounds__(kNT, (step_occupancy<G, R>())) void decode_step_ker
   unsigned char* kvs = smem + C::o_kvs;
   int32_t* sel = reinterpret_cast<int32_t*>(smem + C::o_sel);
   uint16_t* sc = reinterpret_cast<uint16_t*>(smem + ((C::o_sel + (a.k + 1) * 4 + 15) / 16 * 16));
+  // LDS slot of token li's score: 8 spare slots after every 128 tokens, so
+  // that the compaction's 16-byte reads (thread t reading its run of
+  // consecutive tokens from t * run on) fall on distinct bank groups for
+  // runs of 32 tokens and more as well (unpadded, runs of 128 tokens put 8
+  // consecutive lanes on one bank group); 8-token groups stay contiguous
+  // and 16-byte aligned
+  const auto sc_slot = [](int li) { return li + ((li >> 7) << 3); };
 
   const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
 #ifdef HATA_PHASE_TRACE
@@ -530,7 +538,7 @@ __global__ __launch_bounds__(kNT, (step_occupancy<G, R>())) void decode_step_ker
     uint32_t cw[W32];
     code_words<R>(c, cw);
     const uint32_t s = gqa_hamming_w<G, R>(cw, qm);
-    sc[li] = (uint16_t)s;
+    sc[sc_slot(li)] = (uint16_t)s;
     atomicAdd(&hist[(C::HCOPY > 1 ? wv * C::NBP : 0) + s], 1u);
   };
   constexpr int BATCH = PF * kNT;
@@ -585,11 +593,11 @@ __global__ __launch_bounds__(kNT, (step_occupancy<G, R>())) void decode_step_ker
       uint32_t cw[W32];
 #pragma unroll
       for (int wd = 0; wd < W32; ++wd) cw[wd] = (uint32_t)(qcode[G * W64 + (wd >> 1)] >> ((wd & 1) * 32));
-      const uint32_t s_old = sc[new_li];
+      const uint32_t s_old = sc[sc_slot(new_li)];
       const uint32_t s_new = gqa_hamming_w<G, R>(cw, qm);
       atomicSub(&hist[s_old], 1u);
       atomicAdd(&hist[s_new], 1u);
-      sc[new_li] = (uint16_t)s_new;
+      sc[sc_slot(new_li)] = (uint16_t)s_new;
     }
   }
   // the unit's XCD stamps (wave 0, lane = workgroup), read while the
@@ -819,23 +827,43 @@ __global__ __launch_bounds__(kNT, (step_occupancy<G, R>())) void decode_step_ker
   const int run = per8 * 8;
   const int i_begin = t * run;  // the padded score area covers 256 * run tokens
   const int nvalid = max(0, min(cnt - i_begin, run));
-  const uint32_t Tu = (uint32_t)T;
+  // Masks of 8 tokens at once from packed 16-bit arithmetic (scores and T
+  // are below 2^15): the sign bit of s - T (resp. s - T - 1) in each 16-bit
+  // half says s < T (resp. s <= T); a byte permute with its sign-extension
+  // selectors turns the 4 sign bits of two words into 4 bytes of 0x00 or
+  // 0xFF, one bit of each byte is kept at its token's position (token q of
+  // the 8 at bit 7 - q), and a multiply by 0x01010101 adds the 4 bytes of
+  // two such words into the top byte: token q at bit 31 - q.
+  typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+  const u16x2 tv0 = {(unsigned short)T, (unsigned short)T};
+  const u16x2 tv1 = {(unsigned short)(T + 1), (unsigned short)(T + 1)};
+  auto byte_mask = [](const uint32_t (&d)[4]) {
+    // selectors 8..11: 0xFF where bit 15 / 31 of the second operand, then
+    // bit 15 / 31 of the first operand, is set
+    const uint32_t a = __builtin_amdgcn_perm(d[1], d[0], 0x0B0A0908u);  // tokens 0..3
+    const uint32_t b = __builtin_amdgcn_perm(d[3], d[2], 0x0B0A0908u);  // tokens 4..7
+    const uint32_t x = (a & 0x10204080u) | (b & 0x01020408u);
+    return (x * 0x01010101u) >> 24;
+  };
   uint32_t mlt[kRunWords], meq[kRunWords];
 #pragma unroll
   for (int wi = 0; wi < kRunWords; ++wi) {
-    uint32_t ml = 0, me = 0;
+    uint32_t ml = 0, mle = 0;
     if (wi * 4 < per8) {
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
         if (wi * 4 + c < per8) {
-          const uint4 v = *reinterpret_cast<const uint4*>(sc + i_begin + wi * 32 + c * 8);
+          const uint4 v = *reinterpret_cast<const uint4*>(sc + sc_slot(i_begin + wi * 32 + c * 8));
           const uint32_t wds[4] = {v.x, v.y, v.z, v.w};
+          uint32_t dl[4], de[4];
 #pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const uint32_t s2 = (wds[e >> 1] >> ((e & 1) * 16)) & 0xFFFFu;
-            ml = ml + ml + (s2 < Tu ? 1u : 0u);
-            me = me + me + (s2 == Tu ? 1u : 0u);
+          for (int q = 0; q < 4; ++q) {
+            const u16x2 s2 = __builtin_bit_cast(u16x2, wds[q]);
+            dl[q] = __builtin_bit_cast(uint32_t, (u16x2)(s2 - tv0));
+            de[q] = __builtin_bit_cast(uint32_t, (u16x2)(s2 - tv1));
           }
+          ml = (ml << 8) | byte_mask(dl);
+          mle = (mle << 8) | byte_mask(de);
         }
       }
       // left-align (token p at bit 31-p) and drop tokens past cnt
@@ -843,10 +871,10 @@ __global__ __launch_bounds__(kNT, (step_occupancy<G, R>())) void decode_step_ker
       const int nv = max(0, min(32, nvalid - wi * 32));
       const uint32_t keep = nv == 0 ? 0u : (~0u << (32 - nv));
       ml = (ml << (32 - ntok)) & keep;
-      me = (me << (32 - ntok)) & keep;
+      mle = (mle << (32 - ntok)) & keep;
     }
     mlt[wi] = ml;
-    meq[wi] = me;
+    meq[wi] = mle & ~ml;
   }
   uint32_t own_pk = 0;
 #pragma unroll
