@@ -228,6 +228,11 @@ STEP_CASES = [
     (2, 4, 2, 1000, 5, "exact", [1000, 999]),     # G = 2, tiny k
     (8, 32, 32, 2048, 128, "gauss", None),        # 256 units, one workgroup each
     (1, 4, 4, 30000, 40, "gauss", None),          # G = 1 over many workgroups, most keep no row
+    # workgroups keeping more than one attention batch (64 rows) of the
+    # matrix-core path, for each G it serves
+    (1, 8, 1, 4096, 1024, "exact", None),         # G = 8, many ties: up to 256 kept rows a workgroup
+    (1, 2, 1, 4096, 1024, "exact", None),         # G = 2, the same
+    (64, 32, 8, 1024, 300, "gauss", None),        # 512 units of one workgroup, G = 4: 300 kept rows each
 ]
 
 
