@@ -338,7 +338,10 @@ __global__ __launch_bounds__(kNT, (step_occupancy<G, R>())) void decode_step_ker
   // the id into the pool)
   auto prow = [&](int r) -> int64_t {
     const int pg = min(r >> a.log2P, a.max_pages - 1);
-    const int pid = min(max(a.bt[(int64_t)b * a.max_pages + pg], 0), a.num_pages - 1);
+    // read as a constant (a scalar load, counted apart from the vector
+    // loads, so using it does not wait for W_H and the code ring)
+    typedef const __attribute__((address_space(4))) int32_t* cbt_p;
+    const int pid = min(max(*(cbt_p)(a.bt + (int64_t)b * a.max_pages + pg), 0), a.num_pages - 1);
     return (((int64_t)pid * a.Hkv + h) << a.log2P) + (r & ((1 << a.log2P) - 1));
   };
   int32_t* pgl = reinterpret_cast<int32_t*>(smem + C::o_pgl);  // PAGED: the chunk's page ids
@@ -349,22 +352,35 @@ __global__ __launch_bounds__(kNT, (step_occupancy<G, R>())) void decode_step_ker
   // every wave (a chunk has at most 128 batches), so a ring refill takes its
   // id with a readlane instead of a scalar load, whose wait would also drain
   // the scan's LDS atomics
+  // The block-table words are loaded here, every load unconditional with its
+  // index clamped into the table, and clamped into the pool only after the
+  // query rows and W_H have been requested (below): a load whose value is
+  // used at once, or under a branch, is followed by a wait for every load
+  // before it, which with one wait per page id put eight round trips in
+  // front of the code stream.
   int bpid0 = 0, bpid1 = 0;
+  int npg = 0;
   if constexpr (PAGED) {
-    auto pid_of = [&](int r) {
-      const int pg = min(r >> a.log2P, a.max_pages - 1);
-      return min(max(a.bt[(int64_t)b * a.max_pages + pg], 0), a.num_pages - 1);
-    };
+    const int32_t* btb = a.bt + (int64_t)b * a.max_pages;
     const int fp = (w * a.chunk) >> a.log2P;
-    const int npg = ((w * a.chunk + a.chunk - 1) >> a.log2P) - fp + 1;
+    npg = ((w * a.chunk + a.chunk - 1) >> a.log2P) - fp + 1;
 #pragma unroll
-    for (int u = 0; u < kPglPerThread; ++u)
-      if (t + kNT * u < npg) pgv[u] = pid_of((fp + t + kNT * u) << a.log2P);
-    if (a.log2P >= 8) {
-      bpid0 = pid_of(w * a.chunk + lane * kNT);
-      bpid1 = pid_of(w * a.chunk + (lane + 64) * kNT);
-    }
+    for (int u = 0; u < kPglPerThread; ++u) pgv[u] = btb[min(fp + t + kNT * u, a.max_pages - 1)];
+    // pages of >= 256 rows: the batch ids (otherwise never used)
+    bpid0 = btb[min((w * a.chunk + lane * kNT) >> a.log2P, a.max_pages - 1)];
+    bpid1 = btb[min((w * a.chunk + (lane + 64) * kNT) >> a.log2P, a.max_pages - 1)];
   }
+  // PAGED: the ids of the chunk's pages lane and 64 + lane, in every wave
+  // (the code ring's first PF batches of 256 rows lie in the first 128
+  // pages for pages of >= 16 rows)
+  int ppid0 = 0, ppid1 = 0;
+  if constexpr (PAGED) {
+    const int32_t* btb = a.bt + (int64_t)b * a.max_pages;
+    const int fp = (w * a.chunk) >> a.log2P;
+    ppid0 = btb[min(fp + lane, a.max_pages - 1)];
+    ppid1 = btb[min(fp + 64 + lane, a.max_pages - 1)];
+  }
+  auto clamp_pid = [&](int v) { return min(max(v, 0), a.num_pages - 1); };
   // PAGED: physical row of the chunk's row lo + i for a uniform, 256-aligned
   // i < 32768 + BATCH (batch i / 256 of the chunk)
   auto prow_batch = [&](int lo_, int i) -> int64_t {
@@ -410,25 +426,24 @@ __global__ __launch_bounds__(kNT, (step_occupancy<G, R>())) void decode_step_ker
   const uint32_t* cunit = a.codes + row0 * W32;
   CodeRow<R> cbuf[PF];
   if constexpr (PAGED) {
-    // pages of >= 256 rows: a 256-row batch lies in one page (lo is a
-    // multiple of 256), one uniform page id per batch; smaller pages: each
-    // lane's own page id.  Batches past the table load its last full batch
-    // (never scored).
-    if (a.log2P >= 8) {
+    // the page of row lo + j*256 + t, i.e. the chunk's page pi =
+    // (row >> log2P) - (lo >> log2P) < 128, taken from lane pi % 64 of
+    // ppid0 / ppid1 by a wave-local permute: one path for every page size,
+    // with no branch and no load whose value is used at once, so the wait
+    // for these ids (loaded ahead of the query rows and W_H) does not also
+    // wait for those.  Rows past the cache are clamped to its last row
+    // (loaded, never scored).
+    bpid0 = clamp_pid(bpid0);
+    bpid1 = clamp_pid(bpid1);
+    const int fp = lo >> a.log2P;
 #pragma unroll
-      for (int j = 0; j < PF; ++j) {
-        const int rb = (int)min((int64_t)lo + j * kNT, cap - kNT);
-        cbuf[j] = load_code<R>(a.codes, prow(rb) + t);
-      }
-    } else {
-      // (cap need not be a multiple of 256 here: clamp each row, not the batch)
-#pragma unroll
-      for (int j = 0; j < PF; ++j) {
-        const int r = (int)min((int64_t)lo + j * kNT + t, cap - 1);
-        const int pg = min(r >> a.log2P, a.max_pages - 1);
-        const int pid = min(max(a.bt[(int64_t)b * a.max_pages + pg], 0), a.num_pages - 1);
-        cbuf[j] = load_code<R>(a.codes, (((int64_t)pid * a.Hkv + h) << a.log2P) + (r & ((1 << a.log2P) - 1)));
-      }
+    for (int j = 0; j < PF; ++j) {
+      const int r = (int)min((int64_t)lo + j * kNT + t, cap - 1);
+      const int pi = min(max((r >> a.log2P) - fp, 0), 127);
+      const int v0 = __builtin_amdgcn_ds_bpermute((pi & 63) << 2, ppid0);
+      const int v1 = __builtin_amdgcn_ds_bpermute((pi & 63) << 2, ppid1);
+      const int pid = clamp_pid(pi < 64 ? v0 : v1);
+      cbuf[j] = load_code<R>(a.codes, (((int64_t)pid * a.Hkv + h) << a.log2P) + (r & ((1 << a.log2P) - 1)));
     }
   } else {
 #pragma unroll
@@ -493,7 +508,7 @@ __global__ __launch_bounds__(kNT, (step_occupancy<G, R>())) void decode_step_ker
   if constexpr (PAGED) {
 #pragma unroll
     for (int u = 0; u < kPglPerThread; ++u)
-      if (t + kNT * u < kMaxPgl) pgl[t + kNT * u] = pgv[u];
+      if (t + kNT * u < kMaxPgl) pgl[t + kNT * u] = (t + kNT * u < npg) ? clamp_pid(pgv[u]) : 0;
   }
   __syncthreads();
   HATA_MARK(kTrQrows);
