@@ -162,6 +162,55 @@ def read_peak(gib: int = 4, reps: int = 5) -> float:
     return best
 
 
+def code_stream_alone(layer_bufs, L: int, n: int) -> dict | None:
+    """The code cache read on its own: the library's plain streaming kernel
+    (one workgroup of 256 threads per CU, 16 loads of 16 bytes in flight per
+    thread, as many workgroups as the fused step launches at 128K) over each
+    layer's code cache in the same rotation as the step, timed as a captured
+    graph of n launches; and the same kernel over only the first 16 bytes per
+    thread of each cache (one load per thread), which times the launch and
+    the first access.  A bound for the step's scan phase, which cannot end
+    before its code rows have arrived."""
+    import torch
+
+    from hash_top_sparse_amd import binding
+
+    if n <= 0:
+        return None
+    sink = torch.zeros(1024, dtype=torch.int64, device="cuda")
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    first = min(cus, 1024) * 256 * 16
+    out = {}
+    for name, nbytes in (("whole", None), ("one_load_per_thread", first)):
+        views = []
+        for i in range(L):
+            c = layer_bufs[i][2].view(-1).view(torch.uint8)
+            views.append(c if nbytes is None else c[: min(nbytes, c.numel())])
+        for i in range(4):
+            binding.stream_read(views[i % L], sink)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(n):
+                binding.stream_read(views[i % L], sink)
+        g.replay()
+        torch.cuda.synchronize()
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ev0.record()
+        g.replay()
+        ev1.record()
+        torch.cuda.synchronize()
+        ms = ev0.elapsed_time(ev1) / n
+        out[name] = {"ms_per_launch": ms, "bytes": int(views[0].numel()),
+                     "GBs": views[0].numel() / (ms * 1e-3) / 1e9}
+        del g
+    log(f"code cache read alone: {out['whole']['ms_per_launch'] * 1e3:.2f} us "
+        f"({out['whole']['bytes'] / 1e6:.1f} MB); one load per thread: "
+        f"{out['one_load_per_thread']['ms_per_launch'] * 1e3:.2f} us")
+    out["timing"] = "graph of the launches, HIP events"
+    return out
+
+
 def measure(cfg_id: int, steps: int, warmup: int, dense_steps: int, layers: int, use_graph: bool,
             with_bulk: bool, with_qk: bool = True, r: int = 128, read_rate: float | None = None):
     """Time the fused step (and the dense baseline) on one workload; returns
@@ -287,6 +336,7 @@ def measure(cfg_id: int, steps: int, warmup: int, dense_steps: int, layers: int,
     err = binding.workspace_check(ws)
     if err:
         raise RuntimeError(f"workspace error word {err}: a cross-workgroup wait timed out")
+    stream = code_stream_alone(layer_bufs, L, min(steps, 1024) if use_graph else 0) if use_graph else None
     achieved = per_step / (ms_step * 1e-3) / 1e9
     log(f"fused step: {ms_step * 1e3:.2f} us/step, {achieved:.0f} GB/s ({achieved / PEAK_HBM_GBS:.1%})")
 
@@ -335,7 +385,7 @@ def measure(cfg_id: int, steps: int, warmup: int, dense_steps: int, layers: int,
            "tokens_per_s": B * 1000.0 / ms_step,
            "GBs": achieved, "frac_of_peak": achieved / PEAK_HBM_GBS, "bytes_per_step": per_step,
            "layers": L, "eager_step_spread": spread, "separate_key_encoder": qk, "dense": dense,
-           "bulk_encode": bulk}
+           "bulk_encode": bulk, "code_stream_alone": stream}
     del layer_bufs
     torch.cuda.empty_cache()
     return res, inp
@@ -892,6 +942,7 @@ def main() -> int:
         "tokens_per_s": head["tokens_per_s"],
         "eager_step_spread": head["eager_step_spread"],
         "separate_key_encoder": head["separate_key_encoder"],
+        "code_stream_alone": head["code_stream_alone"],
         "cpu_baseline": cpu,
         "dense_baseline": head["dense"],
         "bulk_encode": head["bulk_encode"],
