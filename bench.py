@@ -137,6 +137,27 @@ def cpu_baseline(inp, budget_s: float) -> dict:
             "cpu_model": cpu_model}
 
 
+# Device-side delay put ahead of the start event of a timed graph replay
+# (torch's spin kernel, about 1 ms): the host has finished submitting the
+# graph's launches when the start event is reached, so the time the host
+# takes to submit them is not counted as time of the kernels.
+GRAPH_LEAD_CYCLES = 2_000_000
+
+
+def replay_ms(g, n: int) -> float:
+    """Milliseconds per launch of one replay of graph `g` holding `n`
+    launches, by HIP events on the replay stream."""
+    import torch
+
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda._sleep(GRAPH_LEAD_CYCLES)
+    ev0.record()
+    g.replay()
+    ev1.record()
+    torch.cuda.synchronize()
+    return ev0.elapsed_time(ev1) / n
+
+
 def read_peak(gib: int = 4, reps: int = 5) -> float:
     """HBM read rate (GB/s) of the library's streaming-read kernel over a
     `gib` GiB buffer: best of `reps` passes, HIP events on the launch stream."""
@@ -195,12 +216,7 @@ def code_stream_alone(layer_bufs, L: int, n: int) -> dict | None:
                 binding.stream_read(views[i % L], sink)
         g.replay()
         torch.cuda.synchronize()
-        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        ev0.record()
-        g.replay()
-        ev1.record()
-        torch.cuda.synchronize()
-        ms = ev0.elapsed_time(ev1) / n
+        ms = replay_ms(g, n)
         out[name] = {"ms_per_launch": ms, "bytes": int(views[0].numel()),
                      "GBs": views[0].numel() / (ms * 1e-3) / 1e9}
         del g
@@ -280,6 +296,7 @@ def measure(cfg_id: int, steps: int, warmup: int, dense_steps: int, layers: int,
             step(i)
         ev1.record()
         torch.cuda.synchronize()
+        ms_step = ev0.elapsed_time(ev1) / steps
     else:
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
@@ -288,11 +305,7 @@ def measure(cfg_id: int, steps: int, warmup: int, dense_steps: int, layers: int,
         torch.cuda.synchronize()
         g.replay()
         torch.cuda.synchronize()
-        ev0.record()
-        g.replay()
-        ev1.record()
-        torch.cuda.synchronize()
-    ms_step = ev0.elapsed_time(ev1) / steps
+        ms_step = replay_ms(g, steps)
     # spread of single eagerly launched steps (launch gap included), events
     # around each step on the launch stream
     nsp = min(200, steps)
@@ -325,11 +338,7 @@ def measure(cfg_id: int, steps: int, warmup: int, dense_steps: int, layers: int,
                 step_qk(i)
         gq.replay()
         torch.cuda.synchronize()
-        ev0.record()
-        gq.replay()
-        ev1.record()
-        torch.cuda.synchronize()
-        qk_ms = ev0.elapsed_time(ev1) / nqk
+        qk_ms = replay_ms(gq, nqk)
         del gq
         qk = {"ms_per_step": qk_ms, "steps_per_s": 1000.0 / qk_ms}
         log(f"fused step, separate key encoder: {qk_ms * 1e3:.2f} us/step")
@@ -361,15 +370,15 @@ def measure(cfg_id: int, steps: int, warmup: int, dense_steps: int, layers: int,
                     dstep(i)
             gd.replay()
             torch.cuda.synchronize()
-        ev0.record()
         if use_graph:
-            gd.replay()
+            d_ms = replay_ms(gd, dense_steps)
         else:
+            ev0.record()
             for i in range(dense_steps):
                 dstep(i)
-        ev1.record()
-        torch.cuda.synchronize()
-        d_ms = ev0.elapsed_time(ev1) / dense_steps
+            ev1.record()
+            torch.cuda.synchronize()
+            d_ms = ev0.elapsed_time(ev1) / dense_steps
         dgb = dense_bytes(B, Hq, Hkv, N) / (d_ms * 1e-3) / 1e9
         dense = {"ms_per_step": d_ms, "GBs": dgb, "frac_of_peak": dgb / PEAK_HBM_GBS,
                  "speedup_of_hata": d_ms / ms_step,

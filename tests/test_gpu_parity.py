@@ -266,6 +266,61 @@ def test_decode_step_matches_oracle(hata_gpu, case):
     assert_close(out.cpu().numpy(), ref_out)
 
 
+@pytest.mark.parametrize("G", [1, 4])
+@pytest.mark.parametrize("pattern", ["clusters", "all-tied"])
+def test_decode_step_concentrated_kept_rows(hata_gpu, G, pattern):
+    """A unit of 64 workgroups of 512 tokens whose kept rows are concentrated
+    in a few workgroups (some hold more than 256 tokens at or below the
+    threshold, others none).  "clusters": 450 tokens of workgroup 0 and 200
+    of workgroup 5 get codes within two bits of the bitwise majority of the
+    unit's query codes (k = 512); "all-tied": every cached row has one code,
+    so every score ties and the lowest-index rule decides (k = 300)."""
+    N = 32768
+    k = 512 if pattern == "clusters" else 300
+    s = _shape(1, G, 1, N, k, seed=7950 + G)
+    inp = synth.make_inputs(s)
+    d = Dev(inp)
+    _log(f"concentrated kept rows, G={G} {pattern}")
+    qc = codes_np(gpu_query_codes(hata_gpu, d))[0]  # [G, 2] uint64
+    rng = np.random.default_rng(7960 + G)
+    cn = np.zeros((1, 1, N, 2), np.uint64)
+    if pattern == "clusters":
+        cn[0, 0] = rng.integers(0, 2 ** 64, size=(N, 2), dtype=np.uint64)
+        bits = np.unpackbits(qc.view(np.uint8).reshape(G, 16), axis=1, bitorder="little").astype(np.int32)
+        maj = (2 * bits.sum(axis=0) > G) | ((2 * bits.sum(axis=0) == G) & (bits[0] == 1))
+        maj_words = np.packbits(maj.astype(np.uint8), bitorder="little").view(np.uint64)
+        rows = np.r_[10:460, 5 * 512 + 20:5 * 512 + 220]
+        for j in rows:
+            c = maj_words.copy()
+            for bpos in rng.choice(128, size=int(rng.integers(0, 3)), replace=False):
+                c[bpos // 64] ^= np.uint64(1) << np.uint64(bpos % 64)
+            cn[0, 0, j] = c
+    else:
+        cn[0, 0, :] = rng.integers(0, 2 ** 64, size=2, dtype=np.uint64)
+    codes = codes_tensor(cn)
+    ws = hata_gpu.alloc_workspace(hata_gpu.OP_DECODE_STEP, 1, G, 1, N, k)
+    out = torch.full((1, G, 128), np.nan, dtype=torch.float32, device="cuda")
+    idx = torch.full((1, 1, k), -9, dtype=torch.int32, device="cuda")
+    hata_gpu.decode_step(d.q, d.K, d.V, d.W, codes, d.seq, N, k, inp.scale, out, ws, idx)
+    torch.cuda.synchronize()
+    assert hata_gpu.workspace_check(ws) == 0
+    cg = codes_np(codes)
+    np.testing.assert_array_equal(cg[0, 0, :N - 1], cn[0, 0, :N - 1])
+    qc3 = qc.reshape(1, G, 2)
+    scores, ref_idx, ref_out = oracle_units(inp, qc3, cg)
+    S = scores[(0, 0)]
+    T = int(np.sort(S, kind="stable")[k - 1])
+    per_wg = np.bincount(np.arange(N) // 512, weights=(S <= T), minlength=64)
+    _log(f"  T={T}, workgroups with more than 256 tokens at or below T: {int((per_wg > 256).sum())}, "
+         f"with at most 256: {int((per_wg <= 256).sum())}")
+    if pattern == "clusters":
+        assert per_wg[0] > 256 and (per_wg <= 256).any()
+    else:
+        assert (per_wg > 256).all()
+    np.testing.assert_array_equal(idx.cpu().numpy(), ref_idx)
+    assert_close(out.cpu().numpy(), ref_out)
+
+
 @pytest.mark.parametrize("B,Hq,Hkv,N,k", [(3, 32, 8, 4096, 256), (3, 4, 1, 3000, 64)])
 def test_decode_step_invalid_lengths(hata_gpu, B, Hq, Hkv, N, k):
     """A sequence whose device-side length lies outside [1, cap] gets a zero
