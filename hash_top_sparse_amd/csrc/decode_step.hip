@@ -558,18 +558,44 @@ __global__ __launch_bounds__(kNT, (step_occupancy<G, R>())) void decode_step_ker
   };
   constexpr int BATCH = PF * kNT;
   int base = 0;
-  for (; base + 2 * BATCH <= cnt; base += BATCH) {  // this batch and the next are full
+  // one full batch whose successor is full as well: score each ring slot and
+  // refill it with the row BATCH tokens ahead
+  auto scan_batch = [&](int b0) {
 #pragma unroll
     for (int j = 0; j < PF; ++j) {
-      const int li = base + j * kNT + t;
+      const int li = b0 + j * kNT + t;
       score_one(cbuf[j], li);
       if constexpr (PAGED)
-        cbuf[j] = load_code<R>(a.codes, a.log2P >= 8 ? prow_batch(lo, base + j * kNT + BATCH) + t
-                                                     : prow_lane(lo, base + j * kNT + BATCH));
+        cbuf[j] = load_code<R>(a.codes, a.log2P >= 8 ? prow_batch(lo, b0 + j * kNT + BATCH) + t
+                                                     : prow_lane(lo, b0 + j * kNT + BATCH));
       else
         cbuf[j] = load_code<R>(cbase, li + BATCH);
     }
+  };
+  // The appended key row is encoded by the one workgroup that owns it (the
+  // other workgroups never wait for it).  Projected after the scan, it made
+  // that workgroup the unit's last to publish its window, about one encode
+  // later than the rest; so when the chunk spans at least two ring batches
+  // it is projected right after the first batch, while the refills of the
+  // second are in flight (its row was requested before them).
+  auto encode_key = [&]() {
+    if (t < 64) {
+      qf[G * kD + 2 * lane] = bf16_lo(krow);
+      qf[G * kD + 2 * lane + 1] = bf16_hi(krow);
+    }
+    __syncthreads();
+    project_pack<1, R>(wr, qf + G * kD, red, qcode + G * W64, 1);
+  };
+  bool key_encoded = false;
+  if (base + 2 * BATCH <= cnt) {  // this batch and the next are full
+    scan_batch(base);
+    base += BATCH;
+    if (owns_new) {
+      encode_key();
+      key_encoded = true;
+    }
   }
+  for (; base + 2 * BATCH <= cnt; base += BATCH) scan_batch(base);
   if (base + BATCH <= cnt) {  // a full batch, the next one partial or empty
 #pragma unroll
     for (int j = 0; j < PF; ++j) {
@@ -593,16 +619,9 @@ __global__ __launch_bounds__(kNT, (step_occupancy<G, R>())) void decode_step_ker
     }
   }
   if (owns_new) {
-    // The appended key row, encoded by the one workgroup that owns it once
-    // its scan is done (its load has long arrived; the other workgroups never
-    // wait for it); its code goes to the cache and its score replaces the
-    // one computed from the stale cache row.
-    if (t < 64) {
-      qf[G * kD + 2 * lane] = bf16_lo(krow);
-      qf[G * kD + 2 * lane + 1] = bf16_hi(krow);
-    }
-    __syncthreads();
-    project_pack<1, R>(wr, qf + G * kD, red, qcode + G * W64, 1);
+    // the key's code goes to the cache and its score replaces the one
+    // computed from the stale cache row
+    if (!key_encoded) encode_key();
     if (t < W32) a.codes[(PAGED ? prow(n - 1) : row0 + n - 1) * W32 + t] = code_word32(qcode + G * W64, t);
     if (t == new_li % kNT) {
       uint32_t cw[W32];

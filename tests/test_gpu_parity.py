@@ -233,6 +233,9 @@ STEP_CASES = [
     (1, 8, 1, 4096, 1024, "exact", None),         # G = 8, many ties: up to 256 kept rows a workgroup
     (1, 2, 1, 4096, 1024, "exact", None),         # G = 2, the same
     (64, 32, 8, 1024, 300, "gauss", None),        # 512 units of one workgroup, G = 4: 300 kept rows each
+    # chunks of more than two ring batches, the appended row inside a middle
+    # workgroup's chunk (its key is encoded between the first two batches)
+    (2, 4, 1, 270000, 512, "gauss", [270000, 123457]),
 ]
 
 
