@@ -102,6 +102,9 @@ FUSED_CASES = [
     (1, 32, 8, 20000, [20000], 512, 16, 3),        # 16-row pages: page ids per lane
     (2, 8, 8, 5000, [5000, 777], 64, 32, 2),
     (2, 64, 8, 3000, [3000, 1], 128, 64, 1),
+    # chunks of more than two ring batches, the appended row inside a middle
+    # workgroup's chunk
+    (2, 4, 1, 270000, [270000, 123457], 512, 256, 3),
 ]
 
 
