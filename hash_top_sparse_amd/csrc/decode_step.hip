@@ -884,20 +884,44 @@ __global__ __launch_bounds__(kNT, (step_occupancy<G, R>())) void decode_step_ker
   for (int wi = 0; wi < kRunWords; ++wi) {
     uint32_t ml = 0, mle = 0;
     if (wi * 4 < per8) {
+      auto masks8 = [&](const uint4 v) {  // the 8 tokens of one 16-byte score read
+        const uint32_t wds[4] = {v.x, v.y, v.z, v.w};
+        uint32_t dl[4], de[4];
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        if (wi * 4 + c < per8) {
-          const uint4 v = *reinterpret_cast<const uint4*>(sc + sc_slot(i_begin + wi * 32 + c * 8));
-          const uint32_t wds[4] = {v.x, v.y, v.z, v.w};
-          uint32_t dl[4], de[4];
+        for (int q = 0; q < 4; ++q) {
+          const u16x2 s2 = __builtin_bit_cast(u16x2, wds[q]);
+          dl[q] = __builtin_bit_cast(uint32_t, (u16x2)(s2 - tv0));
+          de[q] = __builtin_bit_cast(uint32_t, (u16x2)(s2 - tv1));
+        }
+        ml = (ml << 8) | byte_mask(dl);
+        mle = (mle << 8) | byte_mask(de);
+      };
+      if (G == 1 && wi * 4 + 4 <= per8) {
+        // One query head per KV head, a full word: its four reads are issued
+        // together (runs of 32 tokens and more, i.e. chunks of 8192 tokens
+        // and more, which occur with one workgroup per unit).  Measured on
+        // this instance only; the others keep one read at a time.
+        uint4 v4[4];
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const u16x2 s2 = __builtin_bit_cast(u16x2, wds[q]);
-            dl[q] = __builtin_bit_cast(uint32_t, (u16x2)(s2 - tv0));
-            de[q] = __builtin_bit_cast(uint32_t, (u16x2)(s2 - tv1));
+        for (int c = 0; c < 4; ++c) v4[c] = *reinterpret_cast<const uint4*>(sc + sc_slot(i_begin + wi * 32 + c * 8));
+#pragma unroll
+        for (int c = 0; c < 4; ++c) masks8(v4[c]);
+      } else {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          if (wi * 4 + c < per8) {
+            const uint4 v = *reinterpret_cast<const uint4*>(sc + sc_slot(i_begin + wi * 32 + c * 8));
+            const uint32_t wds[4] = {v.x, v.y, v.z, v.w};
+            uint32_t dl[4], de[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const u16x2 s2 = __builtin_bit_cast(u16x2, wds[q]);
+              dl[q] = __builtin_bit_cast(uint32_t, (u16x2)(s2 - tv0));
+              de[q] = __builtin_bit_cast(uint32_t, (u16x2)(s2 - tv1));
+            }
+            ml = (ml << 8) | byte_mask(dl);
+            mle = (mle << 8) | byte_mask(de);
           }
-          ml = (ml << 8) | byte_mask(dl);
-          mle = (mle << 8) | byte_mask(de);
         }
       }
       // left-align (token p at bit 31-p) and drop tokens past cnt

@@ -236,6 +236,9 @@ STEP_CASES = [
     # chunks of more than two ring batches, the appended row inside a middle
     # workgroup's chunk (its key is encoded between the first two batches)
     (2, 4, 1, 270000, 512, "gauss", [270000, 123457]),
+    # one query head per KV head, chunks of 9472 tokens: a full 32-token mask
+    # word per thread and a partial one
+    (1, 2, 2, 600000, 256, "gauss", None),
 ]
 
 
