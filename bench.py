@@ -619,9 +619,10 @@ def train_bench(J: int = 512, n: int = 8192, r: int = 128, steps: int = 20) -> d
     """Time the hash-weight training step for one head (synthetic bf16 N(0,1)
     Q/K drawn on the device, J sampled queries at random positions of an
     n-key sequence): the label kernel and one gradient step, HIP events over
-    `steps` calls each.  FLOP count of the step: the two projections, the
-    two J x n x r label-weighted pair products, the two gradient products
-    and the W^T W terms (the causal-mask sums, O((n + J) r) adds, are not
+    `steps` eager calls each, and the step again as a captured graph of
+    `steps` steps.  FLOP count of the step: the two projections, the two
+    J x n x r label-weighted pair products, the two gradient products and
+    the W^T W terms (the causal-mask sums, O((n + J) r) adds, are not
     counted)."""
     import torch
 
@@ -654,13 +655,25 @@ def train_bench(J: int = 512, n: int = 8192, r: int = 128, steps: int = 20) -> d
         binding.hash_train_step(q, k, pos, S, W, 1.0, 1e-3, 1e-4, 0.1, 1e-3, loss, ws)
     e1.record()
     torch.cuda.synchronize()
-    st_ms = e0.elapsed_time(e1) / steps
+    st_eager_ms = e0.elapsed_time(e1) / steps
+    # the same steps from a captured graph, like the decode step (each replay
+    # continues the training: every step updates W in place)
+    gtr = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(gtr):
+        for _ in range(steps):
+            binding.hash_train_step(q, k, pos, S, W, 1.0, 1e-3, 1e-4, 0.1, 1e-3, loss, ws)
+    gtr.replay()
+    torch.cuda.synchronize()
+    st_ms = replay_ms(gtr, steps)
+    del gtr
     flops = 4.0 * J * n * r + 4.0 * (J + n) * 128 * r + 4.0 * 128 * r * r
     tf = flops / (st_ms * 1e-3) / 1e12
     log(f"hash training, J={J} n={n} r={r}: labels {lab_ms * 1e3:.1f} us, step {st_ms * 1e3:.1f} us "
-        f"({tf:.2f} TFLOP/s fp32)")
-    return {"J": J, "n": n, "r": r, "labels_ms": lab_ms, "step_ms": st_ms, "step_flops": flops,
-            "step_TFLOPs": tf, "frac_of_fp32_peak": tf / 157.3, "loss_after": loss.cpu().tolist()}
+        f"from a graph, {st_eager_ms * 1e3:.1f} us eager ({tf:.2f} TFLOP/s fp32)")
+    return {"J": J, "n": n, "r": r, "labels_ms": lab_ms, "step_ms": st_ms, "step_ms_eager": st_eager_ms,
+            "timing": "graph of the steps, HIP events (step_ms); eager launches (step_ms_eager)",
+            "step_flops": flops, "step_TFLOPs": tf, "frac_of_fp32_peak": tf / 157.3,
+            "loss_after": loss.cpu().tolist()}
 
 
 TRACE_POINTS = ("start", "qcodes", "scanned", "hist", "published", "wait1", "windows", "threshold",
