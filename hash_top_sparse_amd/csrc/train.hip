@@ -449,11 +449,13 @@ __global__ void splitk_reduce_kernel(const float* __restrict__ part, int splits,
 }  // namespace
 
 // number of k splits for an M x N x K product: aim at about four
-// workgroups per compute unit, each split at least 128 deep
+// workgroups per compute unit, each split at least 128 deep, or one k step
+// (32) deep for products of k <= 512 (W^T W, W A, Q^T dZq: few output
+// tiles, so otherwise a handful of workgroups would walk k alone)
 int train_gemm_splits(int M, int N, int K) {
   const int tiles = ((M + kT - 1) / kT) * ((N + kT - 1) / kT);
   const int want = (1024 + tiles - 1) / tiles;
-  const int s = std::min(want, K / 128);
+  const int s = std::min(want, K / (K <= 512 ? kKS : 128));
   return std::max(s, 1);
 }
 
