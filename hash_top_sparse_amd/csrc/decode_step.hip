@@ -573,11 +573,11 @@ __global__ __launch_bounds__(kNT, (step_occupancy<G, R>())) void decode_step_ker
     }
   };
   // The appended key row is encoded by the one workgroup that owns it (the
-  // other workgroups never wait for it).  Projected after the scan, it made
-  // that workgroup the unit's last to publish its window, about one encode
-  // later than the rest; so when the chunk spans at least two ring batches
-  // it is projected right after the first batch, while the refills of the
-  // second are in flight (its row was requested before them).
+  // other workgroups never wait for it).  When the chunk spans at least two
+  // ring batches it is projected right after the first batch, while the
+  // refills of the second are in flight (its row was requested before
+  // them), instead of adding one encode to that workgroup's path between
+  // its scan and its window.
   auto encode_key = [&]() {
     if (t < 64) {
       qf[G * kD + 2 * lane] = bf16_lo(krow);
