@@ -474,6 +474,9 @@ QK_CASES = [
     (8, 32, 32, 2048, 128, "gauss", None),        # one workgroup per unit: every workgroup owns its row
     (1, 4, 1, 4096, 256, "exact", None),          # exact recipe: codes bit-exact
     (2, 8, 2, 3000, 64, "gauss", [3000, 1]),      # ragged, n = 1 (the new key is the only token)
+    # chunks of more than two ring batches: the key, inside a middle
+    # workgroup's chunk, is projected with W_Hk between the first two batches
+    (2, 4, 1, 270000, 256, "gauss", [270000, 200000]),
 ]
 
 
