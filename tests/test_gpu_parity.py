@@ -609,6 +609,7 @@ WIDTH_STEP_CASES = [
     (8, 32, 32, 2048, 128, "gauss"),     # one workgroup per unit
     (1, 16, 2, 20000, 100, "gauss"),     # G = 8
     (1, 4, 1, 4096, 256, "exact"),       # exact recipe, many ties
+    (1, 4, 1, 270000, 256, "gauss"),     # chunks of more than two ring batches (key encoded between them)
 ]
 
 
